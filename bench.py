@@ -1,0 +1,181 @@
+#!/usr/bin/env python3
+"""Throughput of the direct-convolution library on one MI355X.
+
+Headline workload (one step): single-channel fp32 filtering of an 8192x8192
+image, once with a 3x3, once with a 5x5 and once with a 7x7 filter (three
+launches, each on its own input/output buffers so no launch finds the previous
+one's data in cache). `value` is the step's algorithmic HBM bytes (x, y and w
+once per launch) over its time, in GB/s.
+
+Also reported, each timed on its own: the fp32 32->32 3x3 layer at 1280x720,
+the fused 1280x720 upscaling chain (ms per frame) and the fp16 NHWC 64->64
+layer of 8x256x256, with GFLOP/s and fractions of peak.
+
+Peaks: HBM 8.0 TB/s; fp32 FMA on the vector ALUs without packed-FP32
+instructions 78.6 TFLOP/s (256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz; the
+kernels are built with packed FP32 off, which halves the 157.3 TFLOP/s figure
+that counts packed FMAs); dense fp16 MFMA 2.5 PFLOP/s.
+
+cpu_baseline: the fp64 CPU oracle on the host cores, one full headline step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "conv GFLOP/s and HBM GB/s as % of MI355X peak; ms per 1280x720 frame"
+HBM_PEAK_GBS = 8000.0
+FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12     # 78.64, plain v_fma_f32
+FP32_PACKED_PEAK_TFLOPS = 157.3
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+class Case:
+    """One kernel launch of a workload: callable, counted work, kernel name."""
+
+    def __init__(self, name, launch, flops, nbytes, kernel, bound_peak=None):
+        self.name, self.launch, self.flops, self.bytes, self.kernel = name, launch, flops, nbytes, kernel
+
+
+def _single_large_cases(torch, isa, synth, stream):
+    cases = []
+    for R in (3, 5, 7):
+        x, w = synth.large_image(R)
+        xd = torch.from_numpy(x).cuda()
+        wd = torch.from_numpy(w).cuda()
+        yd = torch.empty_like(xd)
+        plan = isa.Plan(isa.make_desc(1, 1, 8192, 8192, 1, R, R))
+        info = plan.info()
+
+        def launch(plan=plan, xd=xd, wd=wd, yd=yd):
+            isa.conv2d_forward(plan.handle, xd.data_ptr(), wd.data_ptr(), None, yd.data_ptr(), stream)
+
+        c = Case("8192x8192 %dx%d" % (R, R), launch, info["flops"], info["bytes"], info["kernel"])
+        c.keep = (plan, xd, wd, yd)
+        c.R = R
+        cases.append(c)
+    return cases
+
+
+def _time_cases(torch, cases, steps, warmup, stream_obj):
+    """Warmup, then `steps` steps of all cases with an event pair around every
+    launch, all on the stream the library launches on."""
+    for _ in range(warmup):
+        for c in cases:
+            c.launch()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cases]
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream_obj)
+    for s in range(steps):
+        for i, c in enumerate(cases):
+            ev[s][i][0].record(stream_obj)
+            c.launch()
+            ev[s][i][1].record(stream_obj)
+    t1.record(stream_obj)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    per = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps for i in range(len(cases))]
+    return total_ms / steps, per, wall
+
+
+def _roofline(c, ms):
+    """Roofline entry of one launch: bound by HBM or by the fp32 ALUs."""
+    sec = ms / 1e3
+    ai = c.flops / c.bytes
+    ridge = FP32_VALU_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai > ridge:
+        ach = c.flops / sec / 1e12
+        return {"bound": "alu", "achieved": round(ach, 3), "peak": round(FP32_VALU_PEAK_TFLOPS, 2),
+                "unit": "TFLOP/s", "frac": round(ach / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
+                "peak_packed_fp32": FP32_PACKED_PEAK_TFLOPS}
+    ach = c.bytes / sec / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+
+
+def _cpu_baseline(synth, oracle):
+    """The oracle on one full headline step (3x3, 5x5 and 7x7 over 8192x8192)."""
+    import numpy as np
+    total_bytes, secs = 0.0, 0.0
+    for R in (3, 5, 7):
+        x, w = synth.large_image(R)
+        xd = x.astype(np.float64)
+        wd = w.astype(np.float64)
+        t = time.perf_counter()
+        oracle.conv2d(xd, wd)
+        secs += time.perf_counter() - t
+        total_bytes += 4.0 * (2 * 8192 * 8192 + R * R)
+        del xd
+    return {"value": round(total_bytes / secs / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": round(secs, 2),
+            "sample": "one full step: 8192x8192 fp32 image with 3x3, 5x5 and 7x7 filters, fp64 oracle "
+                      "with error scale (compute only, input widening not timed)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import image_stencil_amd as isa
+    import synth
+
+    isa.load()
+    torch.cuda.init()
+    stream_obj = torch.cuda.current_stream()
+    stream = stream_obj.cuda_stream
+
+    cases = _single_large_cases(torch, isa, synth, stream)
+    ms_step, per, wall = _time_cases(torch, cases, args.steps, args.warmup, stream_obj)
+    step_bytes = sum(c.bytes for c in cases)
+    step_flops = sum(c.flops for c in cases)
+    value = step_bytes / (ms_step / 1e3) / 1e9
+    kernels = []
+    for c, ms in zip(cases, per):
+        kernels.append({"case": c.name, "kernel": c.kernel, "ms": round(ms, 4),
+                        "gflops": round(c.flops / ms / 1e6, 1), "gbs": round(c.bytes / ms / 1e6, 1),
+                        "roofline": _roofline(c, ms)})
+    dom = max(range(len(cases)), key=lambda i: per[i])
+    roof = dict(_roofline(cases[dom], per[dom]))
+    roof["kernel"] = cases[dom].kernel + " (%s)" % cases[dom].name
+    roof["launch_ms"] = round(per[dom], 4)
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "single-channel fp32 filtering, 8192x8192 image, 3x3 + 5x5 + 7x7 filters "
+                                  "(one launch each per step)",
+                      "image": [8192, 8192], "filters": [3, 5, 7], "parallelism": "none (1 GPU)"},
+           "gflops": round(step_flops / ms_step / 1e6, 1), "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+           "roofline": roof, "kernels": kernels, "wall_s_timed": round(wall, 3)}
+    for c in cases:
+        c.keep = None
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        import oracle
+        out["cpu_baseline"] = _cpu_baseline(synth, oracle)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

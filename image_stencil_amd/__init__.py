@@ -1,0 +1,197 @@
+"""Python binding of libimgstencil: direct 2D convolution with small filters on gfx950.
+
+The functions with the C names (conv2d_create, conv2d_forward, conv2d_destroy,
+conv2d_get_plan_info, conv_chain_workspace_size, conv_chain_forward,
+conv_chain_kernel_name, is_lds_tile_bytes, is_swizzle_col) marshal arguments to
+the C ABI of include/imgstencil.h and nothing else. conv2d() and conv_chain()
+are conveniences on torch tensors: torch only allocates device memory and
+supplies the current HIP stream.
+"""
+import ctypes
+
+from . import _abi
+from ._abi import (IS_F16, IS_F32, IS_NCHW, IS_NHWC, IS_CHAIN_AUTO, IS_CHAIN_FUSED, IS_CHAIN_UNFUSED,
+                   ImgStencilError, conv2d_desc, conv_chain_desc, conv2d_plan_info)
+
+__all__ = ["conv2d_create", "conv2d_forward", "conv2d_destroy", "conv2d_get_plan_info",
+           "conv_chain_workspace_size", "conv_chain_forward", "conv_chain_kernel_name",
+           "is_lds_tile_bytes", "is_swizzle_col", "is_version", "make_desc", "make_chain_desc",
+           "conv2d", "conv_chain", "Plan", "ImgStencilError"]
+
+
+def load():
+    return _abi.load()
+
+
+def make_desc(n, c, h, w, k, r, s, dtype="f32", relu=False):
+    """conv2d_desc for a same-padded stride-1 layer; f32 is NCHW, f16 is NHWC."""
+    d = conv2d_desc()
+    d.n, d.c, d.h, d.w, d.k, d.r, d.s = n, c, h, w, k, r, s
+    d.pad_h, d.pad_w = (r - 1) // 2, (s - 1) // 2
+    d.stride_h = d.stride_w = 1
+    if dtype == "f32":
+        d.in_dtype = d.out_dtype = IS_F32
+        d.layout = IS_NCHW
+    elif dtype == "f16":
+        d.in_dtype = d.out_dtype = IS_F16
+        d.layout = IS_NHWC
+    else:
+        raise ValueError("dtype must be 'f32' (NCHW) or 'f16' (NHWC)")
+    d.relu = int(bool(relu))
+    return d
+
+
+def conv2d_create(desc):
+    """Returns an opaque plan handle (int); raises ImgStencilError on a bad desc."""
+    plan = ctypes.c_void_p()
+    _abi.check(load().conv2d_create(ctypes.byref(desc), ctypes.byref(plan)), "conv2d_create")
+    return plan.value
+
+
+def conv2d_forward(plan, x_ptr, w_ptr, bias_ptr, y_ptr, stream):
+    """Raw pointers (ints, bias may be 0/None) and a hipStream_t (int)."""
+    _abi.check(load().conv2d_forward(plan, x_ptr, w_ptr, bias_ptr or None, y_ptr, stream or None),
+               "conv2d_forward")
+
+
+def conv2d_destroy(plan):
+    load().conv2d_destroy(plan)
+
+
+def conv2d_get_plan_info(plan):
+    info = conv2d_plan_info()
+    _abi.check(load().conv2d_get_plan_info(plan, ctypes.byref(info)), "conv2d_get_plan_info")
+    return {"kernel": info.kernel.decode(), "grid": (info.grid_x, info.grid_y, info.grid_z),
+            "block": info.block, "lds_bytes": info.lds_bytes, "tile": (info.tile_w, info.tile_h),
+            "flops": info.flops, "bytes": info.bytes}
+
+
+def make_chain_desc(n, h, w, layers, depth_to_space=1, mode=IS_CHAIN_AUTO):
+    """layers: sequence of (c, k, r, relu) (square filters)."""
+    d = conv_chain_desc()
+    d.n, d.h, d.w = n, h, w
+    if not 1 <= len(layers) <= _abi.IS_MAX_CHAIN:
+        raise ValueError("1 to %d layers" % _abi.IS_MAX_CHAIN)
+    d.n_layers = len(layers)
+    for i, (c, k, r, relu) in enumerate(layers):
+        L = d.layer[i]
+        L.c, L.k, L.r, L.s, L.relu = c, k, r, r, int(bool(relu))
+    d.depth_to_space = depth_to_space
+    d.dtype = IS_F32
+    d.mode = mode
+    return d
+
+
+def conv_chain_workspace_size(desc):
+    n = ctypes.c_size_t()
+    _abi.check(load().conv_chain_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+               "conv_chain_workspace_size")
+    return n.value
+
+
+def conv_chain_kernel_name(desc):
+    buf = ctypes.create_string_buffer(64)
+    _abi.check(load().conv_chain_kernel_name(ctypes.byref(desc), buf, 64), "conv_chain_kernel_name")
+    return buf.value.decode()
+
+
+def conv_chain_forward(desc, x_ptr, w_ptrs, b_ptrs, y_ptr, ws_ptr, ws_bytes, stream):
+    n = desc.n_layers
+    W = (ctypes.c_void_p * n)(*w_ptrs)
+    B = (ctypes.c_void_p * n)(*[p or None for p in b_ptrs]) if b_ptrs is not None else None
+    _abi.check(load().conv_chain_forward(ctypes.byref(desc), x_ptr, W, B, y_ptr, ws_ptr or None,
+                                         ws_bytes, stream or None), "conv_chain_forward")
+
+
+def is_lds_tile_bytes(tile_w, tile_h, r, s, channels, elem_bytes):
+    return load().is_lds_tile_bytes(tile_w, tile_h, r, s, channels, elem_bytes)
+
+
+def is_swizzle_col(y, x, nx, elem_bytes, chunk_bytes):
+    return load().is_swizzle_col(y, x, nx, elem_bytes, chunk_bytes)
+
+
+def is_version():
+    return load().is_version()
+
+
+# ---------------------------------------------------------------- torch helpers
+class Plan:
+    """Owns a conv2d plan; forward() launches on torch's current stream."""
+
+    def __init__(self, desc):
+        self.desc = desc
+        self.handle = conv2d_create(desc)
+
+    def info(self):
+        return conv2d_get_plan_info(self.handle)
+
+    def forward(self, x, w, b, y, stream=None):
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        conv2d_forward(self.handle, x.data_ptr(), w.data_ptr(), b.data_ptr() if b is not None else None,
+                       y.data_ptr(), stream)
+        return y
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            conv2d_destroy(h)
+            self.handle = None
+
+
+def _check_dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s" % (name, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def conv2d(x, w, b=None, relu=False):
+    """y = act(conv(x, w) + b). fp32: x is N,C,H,W. fp16: x is N,H,W,C. w is K,C,R,S."""
+    import torch
+    f16 = x.dtype == torch.float16
+    _check_dev(x, x.dtype, "x")
+    _check_dev(w, x.dtype, "w")
+    if b is not None:
+        _check_dev(b, torch.float32, "b")
+    K, C, R, S = w.shape
+    if f16:
+        N, H, W, Cx = x.shape
+        y = torch.empty((N, H, W, K), dtype=x.dtype, device=x.device)
+    else:
+        N, Cx, H, W = x.shape
+        y = torch.empty((N, K, H, W), dtype=x.dtype, device=x.device)
+    if Cx != C:
+        raise ValueError("channel mismatch")
+    p = Plan(make_desc(N, C, H, W, K, R, S, "f16" if f16 else "f32", relu))
+    return p.forward(x, w, b, y)
+
+
+def conv_chain(x, layers, depth_to_space=1, mode=IS_CHAIN_AUTO):
+    """layers: list of (w, b, relu) device tensors (fp32, NCHW). Returns the chain output."""
+    import torch
+    _check_dev(x, torch.float32, "x")
+    N, C, H, W = x.shape
+    spec = []
+    for (w, b, relu) in layers:
+        _check_dev(w, torch.float32, "w")
+        if b is not None:
+            _check_dev(b, torch.float32, "b")
+        spec.append((w.shape[1], w.shape[0], w.shape[2], relu))
+    d = make_chain_desc(N, H, W, spec, depth_to_space, mode)
+    if depth_to_space == 2:
+        y = torch.empty((N, 1, 2 * H, 2 * W), dtype=torch.float32, device=x.device)
+    else:
+        y = torch.empty((N, spec[-1][1], H, W), dtype=torch.float32, device=x.device)
+    ws_bytes = conv_chain_workspace_size(d)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device) if ws_bytes else None
+    conv_chain_forward(d, x.data_ptr(), [w.data_ptr() for (w, _, _) in layers],
+                       [b.data_ptr() if b is not None else None for (_, b, _) in layers],
+                       y.data_ptr(), ws.data_ptr() if ws is not None else None, ws_bytes,
+                       torch.cuda.current_stream().cuda_stream)
+    return y

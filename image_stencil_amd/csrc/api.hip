@@ -1,0 +1,306 @@
+// api.hip -- the C ABI: descriptor validation, kernel choice and launch.
+#include <new>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+struct conv2d_plan_s {
+  is::Plan p;
+};
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+is_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return IS_OK;
+  g_last_hip_error = (int)e;
+  return IS_ERR_HIP;
+}
+
+bool log_enabled() {
+  static const int on = [] {
+    const char *v = getenv("IMGSTENCIL_LOG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+size_t elem_size(is_dtype t) { return t == IS_F16 ? 2 : 4; }
+
+is_status validate(const conv2d_desc *d) {
+  if (!d) return IS_ERR_INVALID_ARG;
+  if (d->n < 0 || d->h < 0 || d->w < 0 || d->c < 1 || d->k < 1 || d->r < 1 || d->s < 1)
+    return IS_ERR_INVALID_ARG;
+  if (d->stride_h != 1 || d->stride_w != 1) return IS_ERR_INVALID_ARG;
+  if ((d->r % 2) == 0 || (d->s % 2) == 0) return IS_ERR_UNSUPPORTED;
+  if (d->pad_h != (d->r - 1) / 2 || d->pad_w != (d->s - 1) / 2) return IS_ERR_INVALID_ARG;
+  if (d->r > 31 || d->s > 31) return IS_ERR_UNSUPPORTED;
+  if (d->relu != 0 && d->relu != 1) return IS_ERR_INVALID_ARG;
+  const bool f32 = d->in_dtype == IS_F32 && d->out_dtype == IS_F32 && d->layout == IS_NCHW;
+  const bool f16 = d->in_dtype == IS_F16 && d->out_dtype == IS_F16 && d->layout == IS_NHWC;
+  if (!f32 && !f16) return IS_ERR_UNSUPPORTED;
+  // Element counts must stay addressable with 64-bit offsets and 32-bit grids.
+  const double in_elems = (double)d->n * d->c * d->h * d->w;
+  const double out_elems = (double)d->n * d->k * d->h * d->w;
+  if (in_elems > 4.0e12 || out_elems > 4.0e12) return IS_ERR_UNSUPPORTED;
+  return IS_OK;
+}
+
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return na && nb && a0 < b0 + nb && b0 < a0 + na;
+}
+
+void fill_info(const is::Plan &p, conv2d_plan_info *info) {
+  memset(info, 0, sizeof(*info));
+  snprintf(info->kernel, sizeof(info->kernel), "%s", p.name);
+  info->grid_x = p.grid_x;
+  info->grid_y = p.grid_y;
+  info->grid_z = p.grid_z;
+  info->block = p.block;
+  info->lds_bytes = p.lds;
+  info->tile_w = p.tile_w;
+  info->tile_h = p.tile_h;
+  const conv2d_desc &d = p.d;
+  info->flops = 2.0 * d.n * d.k * d.c * d.r * d.s * (double)d.h * d.w;
+  const double es = (double)elem_size(d.in_dtype);
+  info->bytes = es * ((double)d.n * d.c * d.h * d.w + (double)d.n * d.k * d.h * d.w +
+                      (double)d.k * d.c * d.r * d.s) +
+                4.0 * d.k;
+}
+
+is_status make_plan(const conv2d_desc *d, is::Plan &p) {
+  const is_status st = validate(d);
+  if (st != IS_OK) return st;
+  memset(&p, 0, sizeof(p));
+  p.d = *d;
+  if (!is::configure_single(p)) is::configure_generic(p);
+  if (log_enabled())
+    fprintf(stderr, "[imgstencil] n=%d c=%d h=%d w=%d k=%d r=%d s=%d -> %s grid=%d block=%d lds=%d\n",
+            d->n, d->c, d->h, d->w, d->k, d->r, d->s, p.name, p.grid_x, p.block, p.lds);
+  return IS_OK;
+}
+
+is_status run_plan(const is::Plan &p, const void *x, const void *w, const float *bias, void *y,
+                   hipStream_t stream) {
+  const conv2d_desc &d = p.d;
+  if (!x || !w || !y) return IS_ERR_INVALID_ARG;
+  if (misaligned(x) || misaligned(w) || misaligned(y) || (bias && misaligned(bias)))
+    return IS_ERR_MISALIGNED;
+  const size_t es = elem_size(d.in_dtype);
+  const size_t xb = es * (size_t)d.n * d.c * d.h * d.w;
+  const size_t yb = es * (size_t)d.n * d.k * d.h * d.w;
+  if (overlap(x, xb, y, yb)) return IS_ERR_INVALID_ARG;
+  if (xb == 0 || yb == 0) return IS_OK;   // empty image: nothing to compute
+  hipError_t e;
+  switch (p.kid) {
+    case is::kSingleChannel:
+      e = is::launch_single(p, static_cast<const float *>(x), static_cast<const float *>(w), bias,
+                            static_cast<float *>(y), stream);
+      break;
+    default:
+      e = is::launch_generic(p, x, w, bias, y, stream);
+      break;
+  }
+  return hip_status(e);
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Checks a chain descriptor and returns the conv2d_desc of each layer.
+is_status chain_layers(const conv_chain_desc *d, conv2d_desc *ld) {
+  if (!d) return IS_ERR_INVALID_ARG;
+  if (d->n_layers < 1 || d->n_layers > IS_MAX_CHAIN || d->n < 0 || d->h < 0 || d->w < 0)
+    return IS_ERR_INVALID_ARG;
+  if (d->dtype != IS_F32) return IS_ERR_UNSUPPORTED;
+  if (d->depth_to_space != 1 && d->depth_to_space != 2) return IS_ERR_UNSUPPORTED;
+  if (d->mode != IS_CHAIN_AUTO && d->mode != IS_CHAIN_FUSED && d->mode != IS_CHAIN_UNFUSED)
+    return IS_ERR_INVALID_ARG;
+  for (int l = 0; l < d->n_layers; ++l) {
+    const conv_layer_desc &L = d->layer[l];
+    if (l > 0 && L.c != d->layer[l - 1].k) return IS_ERR_INVALID_ARG;
+    conv2d_desc &c = ld[l];
+    memset(&c, 0, sizeof(c));
+    c.n = d->n; c.c = L.c; c.h = d->h; c.w = d->w;
+    c.k = L.k; c.r = L.r; c.s = L.s;
+    c.pad_h = (L.r - 1) / 2; c.pad_w = (L.s - 1) / 2;
+    c.stride_h = c.stride_w = 1;
+    c.in_dtype = c.out_dtype = IS_F32;
+    c.layout = IS_NCHW;
+    c.relu = L.relu;
+    const is_status st = validate(&c);
+    if (st != IS_OK) return st;
+  }
+  if (d->depth_to_space == 2 && d->layer[d->n_layers - 1].k != 4) return IS_ERR_UNSUPPORTED;
+  return IS_OK;
+}
+
+bool chain_fusable(const conv_chain_desc *, const conv2d_desc *) { return false; }
+
+size_t chain_buffer_bytes(const conv_chain_desc *d) {
+  size_t m = 0;
+  for (int l = 0; l < d->n_layers; ++l) {
+    const size_t b = 4 * (size_t)d->n * d->layer[l].k * d->h * d->w;
+    if (b > m) m = b;
+  }
+  return align256(m);
+}
+
+is_status chain_workspace(const conv_chain_desc *d, const conv2d_desc *ld, size_t *bytes) {
+  if (d->mode != IS_CHAIN_UNFUSED && chain_fusable(d, ld)) {
+    *bytes = 0;
+    return IS_OK;
+  }
+  if (d->mode == IS_CHAIN_FUSED) return IS_ERR_UNSUPPORTED;
+  // Ping-pong buffers for the intermediates; a single layer without
+  // depth-to-space writes straight to y.
+  const int need = (d->n_layers == 1 && d->depth_to_space == 1) ? 0 : (d->n_layers == 1 ? 1 : 2);
+  *bytes = need * chain_buffer_bytes(d);
+  return IS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+is_status conv_chain_workspace_size(const conv_chain_desc *d, size_t *bytes) {
+  if (!bytes) return IS_ERR_INVALID_ARG;
+  conv2d_desc ld[IS_MAX_CHAIN];
+  const is_status st = chain_layers(d, ld);
+  if (st != IS_OK) return st;
+  return chain_workspace(d, ld, bytes);
+}
+
+is_status conv_chain_kernel_name(const conv_chain_desc *d, char *name, size_t len) {
+  if (!name || len == 0) return IS_ERR_INVALID_ARG;
+  conv2d_desc ld[IS_MAX_CHAIN];
+  const is_status st = chain_layers(d, ld);
+  if (st != IS_OK) return st;
+  size_t ws = 0;
+  const is_status st2 = chain_workspace(d, ld, &ws);
+  if (st2 != IS_OK) return st2;
+  const bool fused = d->mode != IS_CHAIN_UNFUSED && chain_fusable(d, ld);
+  snprintf(name, len, "%s", fused ? "is_k3_chain" : "layer_by_layer");
+  return IS_OK;
+}
+
+is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void *const *w,
+                             const float *const *b, void *y, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  try {
+    conv2d_desc ld[IS_MAX_CHAIN];
+    is_status st = chain_layers(d, ld);
+    if (st != IS_OK) return st;
+    if (!x || !w || !y) return IS_ERR_INVALID_ARG;
+    for (int l = 0; l < d->n_layers; ++l) {
+      if (!w[l]) return IS_ERR_INVALID_ARG;
+      if (misaligned(w[l]) || (b && b[l] && misaligned(b[l]))) return IS_ERR_MISALIGNED;
+    }
+    if (misaligned(x) || misaligned(y)) return IS_ERR_MISALIGNED;
+    const size_t xb = 4 * (size_t)d->n * d->layer[0].c * d->h * d->w;
+    const size_t yb = 4 * (size_t)d->n * d->layer[d->n_layers - 1].k * d->h * d->w;
+    if (overlap(x, xb, y, yb)) return IS_ERR_INVALID_ARG;
+    size_t need = 0;
+    st = chain_workspace(d, ld, &need);
+    if (st != IS_OK) return st;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return IS_ERR_WORKSPACE;
+    if (need > 0 && misaligned(workspace)) return IS_ERR_MISALIGNED;
+    if (need > 0 && (overlap(workspace, need, x, xb) || overlap(workspace, need, y, yb)))
+      return IS_ERR_INVALID_ARG;
+    if (xb == 0 || yb == 0) return IS_OK;
+
+    const size_t half = chain_buffer_bytes(d);
+    char *ws = static_cast<char *>(workspace);
+    const void *src = x;
+    for (int l = 0; l < d->n_layers; ++l) {
+      const bool last = l == d->n_layers - 1;
+      void *dst = (last && d->depth_to_space == 1) ? y : (void *)(ws + (l % 2) * half);
+      is::Plan p;
+      st = make_plan(&ld[l], p);
+      if (st != IS_OK) return st;
+      st = run_plan(p, src, w[l], b ? b[l] : nullptr, dst, stream);
+      if (st != IS_OK) return st;
+      src = dst;
+    }
+    if (d->depth_to_space == 2)
+      return hip_status(is::launch_depth_to_space2(static_cast<const float *>(src),
+                                                   static_cast<float *>(y), d->n, d->h, d->w,
+                                                   stream));
+    return IS_OK;
+  } catch (...) {
+    return IS_ERR_INVALID_ARG;
+  }
+}
+
+
+is_status conv2d_create(const conv2d_desc *d, conv2d_plan *out) {
+  if (!out) return IS_ERR_INVALID_ARG;
+  *out = nullptr;
+  try {
+    is::Plan p;
+    const is_status st = make_plan(d, p);
+    if (st != IS_OK) return st;
+    conv2d_plan_s *h = new (std::nothrow) conv2d_plan_s;
+    if (!h) return IS_ERR_NO_MEMORY;
+    h->p = p;
+    *out = h;
+    return IS_OK;
+  } catch (...) {
+    return IS_ERR_NO_MEMORY;
+  }
+}
+
+is_status conv2d_forward(conv2d_plan plan, const void *x, const void *w, const float *bias, void *y,
+                         hipStream_t stream) {
+  if (!plan) return IS_ERR_INVALID_ARG;
+  try {
+    return run_plan(plan->p, x, w, bias, y, stream);
+  } catch (...) {
+    return IS_ERR_INVALID_ARG;
+  }
+}
+
+void conv2d_destroy(conv2d_plan plan) { delete plan; }
+
+is_status conv2d_get_plan_info(conv2d_plan plan, conv2d_plan_info *info) {
+  if (!plan || !info) return IS_ERR_INVALID_ARG;
+  fill_info(plan->p, info);
+  return IS_OK;
+}
+
+size_t is_lds_tile_bytes(int tile_w, int tile_h, int r, int s, int channels, int elem_bytes) {
+  if (tile_w <= 0 || tile_h <= 0 || r <= 0 || s <= 0 || channels <= 0 || elem_bytes <= 0) return 0;
+  return (size_t)(tile_w + s - 1) * (size_t)(tile_h + r - 1) * (size_t)channels * (size_t)elem_bytes;
+}
+
+int is_swizzle_col(int y, int x, int nx, int elem_bytes, int chunk_bytes) {
+  auto pow2 = [](int v) { return v > 0 && (v & (v - 1)) == 0; };
+  if (y < 0 || x < 0 || x >= nx || !pow2(nx) || !pow2(elem_bytes) || !pow2(chunk_bytes)) return -1;
+  if (chunk_bytes < elem_bytes || chunk_bytes > nx * elem_bytes || nx * elem_bytes < 32) return -1;
+  return is::swizzle_col(y, x, nx, elem_bytes, chunk_bytes);
+}
+
+const char *is_status_str(is_status st) {
+  switch (st) {
+    case IS_OK: return "ok";
+    case IS_ERR_INVALID_ARG: return "invalid argument";
+    case IS_ERR_UNSUPPORTED: return "unsupported";
+    case IS_ERR_MISALIGNED: return "tensor base not 16-byte aligned";
+    case IS_ERR_HIP: return "HIP runtime error";
+    case IS_ERR_NO_MEMORY: return "out of host memory";
+    case IS_ERR_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+int is_last_hip_error(void) { return g_last_hip_error; }
+
+int is_version(void) { return IS_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// common.hpp -- device helpers shared by the gfx950 convolution kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace is {
+
+constexpr int kWave = 64;   // CDNA wavefront width
+
+// Word 3 of a raw (unswizzled, stride 0) gfx9 buffer resource: 32-bit data
+// format so that range checking is in bytes against num_records.
+constexpr int kBufferFlags = 0x00020000;
+
+// GFX9 DPP wavefront shifts: every lane reads the register of its neighbour
+// inside the whole 64-lane wave (row_mask and bank_mask all on). A lane whose
+// source lies outside the wave keeps `old` (bound_ctrl off).
+constexpr int kDppWaveShl1 = 0x130;   // lane l reads lane l+1
+constexpr int kDppWaveShr1 = 0x138;   // lane l reads lane l-1
+
+__device__ __forceinline__ float from_prev_lane(float src, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
+                                                    kDppWaveShr1, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float from_next_lane(float src, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
+                                                    kDppWaveShl1, 0xf, 0xf, false));
+}
+
+// Workgroups are dealt to the 8 XCDs of the chip round-robin in launch order,
+// and each XCD has its own L2. Renumber launch index b so that XCD k receives
+// the contiguous logical range [k*T/8, (k+1)*T/8) of the first 8*floor(T/8)
+// tiles; neighbouring tiles then share an L2 and their halo rows/columns hit
+// there. The last T mod 8 tiles keep their own index. A bijection on [0, T).
+__device__ __forceinline__ int xcd_remap(int b, int T) {
+  const int per = T >> 3;
+  if (b >= (per << 3)) return b;
+  return (b & 7) * per + (b >> 3);
+}
+
+// XOR swizzle of a column index inside an LDS array T a[][nx] whose rows are
+// nx * elem_bytes bytes (a power of two >= 32), permuting chunks of chunk_bytes:
+// chunk index i = (y*nx + x)*eb/cb, row-of-chunks yc = i / (nx*eb/cb),
+// column-of-chunks xc = i mod (nx*eb/cb), swizzled chunk xc ^ yc, then back to an
+// element column keeping the element's offset inside its chunk. Used for the
+// NHWC fp16 tiles; a bijection on x for every fixed y.
+__host__ __device__ constexpr int swizzle_col(int y, int x, int nx, int eb, int cb) {
+  const int per_chunk = cb / eb;                  // elements per chunk
+  const int chunks_per_row = (nx * eb) / cb;      // chunks in one swizzle row
+  const long long i_chunk = ((long long)y * nx + x) * eb / cb;
+  const long long y_chunk = i_chunk / chunks_per_row;
+  const long long x_chunk = i_chunk % chunks_per_row;
+  const long long x_chunk_swz = y_chunk ^ x_chunk;
+  return (int)((x_chunk_swz * per_chunk) % nx) + x % per_chunk;
+}
+
+}  // namespace is

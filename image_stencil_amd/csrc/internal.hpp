@@ -1,0 +1,43 @@
+// internal.hpp -- plan structure and kernel launchers behind the C ABI.
+#pragma once
+
+#include "../../include/imgstencil.h"
+
+namespace is {
+
+enum KernelId {
+  kGenericNchwF32 = 0,   // one thread per output, any shape (fallback)
+  kGenericNhwcF16 = 1,   // one thread per output, any shape (fallback)
+  kSingleChannel = 2,    // C = K = 1, fp32 NCHW, r, s <= 7
+  kMultiChannel = 3,     // fp32 NCHW register-blocked, C, K multiples of the block
+  kMfmaNhwcF16 = 4       // fp16 NHWC implicit GEMM on MFMA
+};
+
+struct Plan {
+  conv2d_desc d;
+  KernelId kid;
+  const char *name;
+  int grid_x, grid_y, grid_z;
+  int block;
+  int lds;
+  int tile_w, tile_h;
+  // Kernel-specific geometry.
+  int nseg, nstrip, ntiles;   // column segments, row strips, total tiles
+  int strip_rows;             // output rows per strip
+  int vec;                    // 1 = 16-byte vector path
+};
+
+// Each kernel family fills the launch geometry of a plan it accepts and
+// launches it. configure_* return false when the family cannot run the desc.
+bool configure_generic(Plan &p);
+hipError_t launch_generic(const Plan &p, const void *x, const void *w, const float *b, void *y,
+                          hipStream_t s);
+
+bool configure_single(Plan &p);
+hipError_t launch_single(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                         hipStream_t s);
+
+// out[n,0,2i+dy,2j+dx] = z[n,2*dy+dx,i,j] for z of N x 4 x H x W fp32.
+hipError_t launch_depth_to_space2(const float *z, float *out, int N, int H, int W, hipStream_t s);
+
+}  // namespace is

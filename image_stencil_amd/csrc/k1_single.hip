@@ -1,0 +1,243 @@
+// k1_single.hip -- single-channel fp32 filtering (C = K = 1, NCHW), r, s in {1,3,5,7}.
+//
+// The "special case" kernel of "Optimizing Memory Efficiency for Convolution
+// Kernels on Kepler GPUs" (arXiv 1705.10591), sections "thread layout" (3.1) and
+// "memory access schedule" with its Algorithm 1, rebuilt for a CDNA wave64:
+//  * a wave owns a strip of 256 columns x `strip_rows` rows (the page's H x W
+//    image block; its best block was 256 wide) and sweeps it top to bottom, one
+//    input row per step, so every input pixel is fetched from HBM once plus a
+//    thin halo (the page's communication-optimal global reads);
+//  * each lane keeps 4 contiguous columns, read and written as one 16-byte
+//    access (the page's n pixels per thread, with n matched to the access width);
+//  * horizontal sharing: the page stages each row in shared memory so that
+//    neighbours can read each other's pixels. Inside one wave the same exchange
+//    is a DPP wavefront shift of registers (no LDS traffic, no barrier); only
+//    lanes 0 and 63 fetch the 16-byte halo outside the wave's 256 columns;
+//  * vertical sharing stays in registers as on the page: a ring of r rolling
+//    output rows, each input row adding its contribution to the r output rows
+//    it touches; the oldest row is complete after its last filter row and is
+//    stored, then recycled;
+//  * the filter sits in scalar registers (wave-uniform operand of every FMA),
+//    the analogue of the page's constant-memory broadcast;
+//  * the next rows are prefetched U steps ahead into registers (the page's
+//    prefetch that overlaps global loads with the FMAs).
+#include "common.hpp"
+#include "internal.hpp"
+
+#include <limits.h>
+
+namespace is {
+namespace {
+
+constexpr int kSegCols = 4 * kWave;   // 256 output columns per wave
+
+template <int R>
+struct Unroll {   // rows per unrolled step: a multiple of R (ring slots are static)
+  static constexpr int value = R == 1 ? 4 : (R == 3 ? 6 : R);
+};
+
+struct Row4 {
+  float v[4];
+};
+
+// Buffer resource of one image row: loads past num_records return 0 and stores
+// past it are dropped, which gives the zero padding of columns >= W (and of
+// whole rows outside the image, whose num_records is 0) without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float *base, int t, int H, int W) {
+  const bool in = t >= 0 && t < H;
+  const float *p = in ? base + (size_t)t * (size_t)W : base;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, in ? W * 4 : 0,
+                                           kBufferFlags);
+}
+
+// Load one input row into `m` (this lane's 4 columns) and `h` (lane 0: the 4
+// columns left of the segment; lane 63: the 4 columns right of it). Byte
+// offsets are 32-bit; offsets outside the row (negative ones included, as
+// unsigned values) read as 0.
+template <bool VEC, int Q>
+__device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, int off_m, int off_h, Row4 &m,
+                                         Row4 &h) {
+  if constexpr (VEC) {
+    const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off_m, 0, 0));
+    m.v[0] = a.x; m.v[1] = a.y; m.v[2] = a.z; m.v[3] = a.w;
+    if constexpr (Q > 0) {
+      const float4 b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off_h, 0, 0));
+      h.v[0] = b.x; h.v[1] = b.y; h.v[2] = b.z; h.v[3] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m.v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off_m + 4 * i, 0, 0));
+    if constexpr (Q > 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        h.v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off_h + 4 * i, 0, 0));
+    }
+  }
+}
+
+template <int R, int S, bool VEC, bool RELU>
+__global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ x,
+                                                     const float *__restrict__ w,
+                                                     const float *__restrict__ bias,
+                                                     float *__restrict__ y, int H, int W,
+                                                     int strip_rows, int nseg, int nstrip,
+                                                     int ntiles) {
+  constexpr int P = (R - 1) / 2, Q = (S - 1) / 2;
+  constexpr int U = Unroll<R>::value;
+  constexpr int NW = 4 + 2 * Q;   // window: 4 own columns plus Q each side
+
+  const int lane = threadIdx.x;
+  const int tile = xcd_remap(blockIdx.x, ntiles);
+  const int seg = tile % nseg;
+  const int strip = (tile / nseg) % nstrip;
+  const int n = tile / (nseg * nstrip);
+  const int x0 = seg * kSegCols;
+  const int col = x0 + 4 * lane;
+  const int y0 = strip * strip_rows;
+  const int rows_out = min(strip_rows, H - y0);
+  const int NT = rows_out + 2 * P;   // input rows y0-P .. y0+rows_out-1+P
+
+  const size_t plane = (size_t)H * (size_t)W;
+  const float *xp = x + (size_t)n * plane;
+  float *yp = y + (size_t)n * plane;
+
+  // Byte offsets inside a row. Lanes other than 0 and 63 aim their halo load
+  // past any row so that it reads nothing.
+  const int off_m = 4 * col;
+  const int off_h = lane == 0 ? 4 * (x0 - 4) : (lane == kWave - 1 ? 4 * (x0 + kSegCols) : INT_MIN);
+
+  float wr[R * S];
+#pragma unroll
+  for (int i = 0; i < R * S; ++i) wr[i] = w[i];
+  const float bv = bias ? bias[0] : 0.f;
+
+  Row4 pf[U], ph[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) load_row<VEC, Q>(row_rsrc(xp, y0 - P + i, H, W), off_m, off_h, pf[i], ph[i]);
+
+  // acc[slot]: ring of the R output rows that the current input row touches;
+  // output row o (relative ro = o - y0) lives in slot (ro + 2P) mod R.
+  float acc[R][4];
+#pragma unroll
+  for (int s = 0; s < R; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[s][i] = 0.f;
+
+  for (int rb = 0; rb < NT; rb += U) {
+#pragma unroll
+    for (int p = 0; p < U; ++p) {
+      const int r = rb + p;
+      if (r < NT) {
+        const Row4 c = pf[p];
+        const Row4 h = ph[p];
+
+        float win[NW];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) win[Q + i] = c.v[i];
+#pragma unroll
+        for (int q = 1; q <= Q; ++q) {
+          win[Q - q] = from_prev_lane(c.v[4 - q], h.v[4 - q]);
+          win[Q + 3 + q] = from_next_lane(c.v[q - 1], h.v[q - 1]);
+        }
+
+        // Input row r feeds relative output rows r-2P+j, j = 0..R-1, with
+        // filter row R-1-j. j = R-1 is the first contribution to output row r:
+        // it starts that slot with a product instead of clearing it.
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const int slot = (p + j) % R;
+          const int u = R - 1 - j;
+#pragma unroll
+          for (int v = 0; v < S; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[slot][i] = (j == R - 1 && v == 0)
+                                 ? wr[u * S + v] * win[i + v]
+                                 : __builtin_fmaf(wr[u * S + v], win[i + v], acc[slot][i]);
+        }
+
+        const int ro = r - 2 * P;   // output row completed by this input row (slot p mod R)
+        if (ro >= 0) {
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[i] = acc[p % R][i] + bv;
+            if constexpr (RELU) o[i] = fmaxf(o[i], 0.f);
+          }
+          const __amdgpu_buffer_rsrc_t rs_o = row_rsrc(yp, y0 + ro, H, W);
+          if constexpr (VEC) {
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
+                                   make_float4(o[0], o[1], o[2], o[3])),
+                rs_o, off_m, 0, 0);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, o[i]), rs_o,
+                                                    off_m + 4 * i, 0, 0);
+          }
+        }
+        // Prefetch U rows ahead into the registers this row has just released.
+        if (r + U < NT) load_row<VEC, Q>(row_rsrc(xp, y0 - P + r + U, H, W), off_m, off_h, pf[p], ph[p]);
+      }
+    }
+  }
+}
+
+using K1Fn = void (*)(const float *, const float *, const float *, float *, int, int, int, int, int,
+                      int);
+
+template <bool VEC, bool RELU>
+K1Fn pick(int r, int s) {
+#define IS_K1_CASE(RR, SS) \
+  if (r == RR && s == SS) return is_k1_single<RR, SS, VEC, RELU>;
+#define IS_K1_ROW(RR) IS_K1_CASE(RR, 1) IS_K1_CASE(RR, 3) IS_K1_CASE(RR, 5) IS_K1_CASE(RR, 7)
+  IS_K1_ROW(1) IS_K1_ROW(3) IS_K1_ROW(5) IS_K1_ROW(7)
+#undef IS_K1_ROW
+#undef IS_K1_CASE
+  return nullptr;
+}
+
+}  // namespace
+
+bool configure_single(Plan &p) {
+  const conv2d_desc &d = p.d;
+  if (d.c != 1 || d.k != 1 || d.layout != IS_NCHW || d.in_dtype != IS_F32) return false;
+  if (d.r > 7 || d.s > 7) return false;
+  if (pick<true, false>(d.r, d.s) == nullptr) return false;
+  const int nseg = (d.w + kSegCols - 1) / kSegCols;
+  // Tall strips keep the vertical halo small ((rows + r - 1) / rows re-read);
+  // shorter ones only where the image would otherwise fill too few waves.
+  int rows = 128;
+  while (rows > 8 && (long long)nseg * ((d.h + rows - 1) / rows) * d.n < 2048) rows >>= 1;
+  const int nstrip = (d.h + rows - 1) / rows;
+  p.kid = kSingleChannel;
+  p.name = "is_k1_single";
+  p.nseg = nseg;
+  p.nstrip = nstrip;
+  p.strip_rows = rows;
+  p.ntiles = nseg * nstrip * d.n;
+  p.grid_x = p.ntiles;
+  p.grid_y = 1;
+  p.grid_z = 1;
+  p.block = kWave;
+  p.lds = 0;
+  p.tile_w = kSegCols;
+  p.tile_h = rows;
+  p.vec = (d.w % 4 == 0) ? 1 : 0;
+  return true;
+}
+
+hipError_t launch_single(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                         hipStream_t s) {
+  const bool relu = p.d.relu != 0;
+  const K1Fn fn = p.vec ? (relu ? pick<true, true>(p.d.r, p.d.s) : pick<true, false>(p.d.r, p.d.s))
+                        : (relu ? pick<false, true>(p.d.r, p.d.s) : pick<false, false>(p.d.r, p.d.s));
+  if (!fn) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, p.d.h, p.d.w,
+                     p.strip_rows, p.nseg, p.nstrip, p.ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace is

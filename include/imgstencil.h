@@ -1,0 +1,189 @@
+/*
+ * imgstencil.h -- C ABI of the MI355X (gfx950) direct 2D convolution library.
+ *
+ * The operation (every entry point below computes it, or a chain of it):
+ *
+ *   y[n,k,i,j] = act( sum_{c,u,v} w[k,c,u,v] * x[n,c,i+u-(R-1)/2,j+v-(S-1)/2] + b[k] )
+ *
+ * with x read as zero outside the HxW image (same-size output, stride 1,
+ * centred window, no filter flip) and act = ReLU or identity. This is the
+ * per-output-pixel loop nest of "Optimizing convolution kernels - CNNs in
+ * Vulkan Part 2/3" (StreamHPC), section "Where we left off": loops over output
+ * channel, input channel, kernel row and kernel column; input pixel = output
+ * pixel + kernel offset - kernel size / 2; bias added to the finished sum; ReLU
+ * by the apply_relu switch of its "Vectorization" section. The single-channel
+ * case is the "special case" (one input channel) of "Optimizing Memory
+ * Efficiency for Convolution Kernels on Kepler GPUs" (arXiv 1705.10591) and the
+ * multi-channel case its "general case".
+ *
+ * Conventions for every entry point:
+ *  - Tensors are caller-owned DEVICE memory, dense and contiguous, with the
+ *    base address aligned to 16 bytes (else IS_ERR_MISALIGNED). The library
+ *    never allocates device memory on a forward call and keeps no pointer
+ *    after the call returns.
+ *  - Weights are K,C,R,S (row-major, contiguous) in the input dtype. Bias is
+ *    K fp32 values or NULL (no bias).
+ *  - Accumulation is always fp32. fp16 outputs are rounded to nearest even.
+ *  - Calls only enqueue work on the given stream (0 = the null stream): no host
+ *    synchronisation, no allocation. Launch errors return IS_ERR_HIP and
+ *    is_last_hip_error() gives the hipError_t. Faults inside a kernel surface
+ *    at the caller's next synchronisation.
+ *  - No exception crosses this boundary; every function returns a status.
+ *  - Input and output must not overlap (IS_ERR_INVALID_ARG when x and y
+ *    ranges intersect).
+ */
+#ifndef IMGSTENCIL_H
+#define IMGSTENCIL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IS_VERSION 1
+#define IS_MAX_CHAIN 8
+
+typedef enum {
+  IS_OK = 0,
+  IS_ERR_INVALID_ARG = 1,   /* null pointer, bad size, overlap, bad padding/stride */
+  IS_ERR_UNSUPPORTED = 2,   /* valid request this library does not implement (even filters, ...) */
+  IS_ERR_MISALIGNED = 3,    /* a tensor base address is not 16-byte aligned */
+  IS_ERR_HIP = 4,           /* the HIP runtime reported an error at launch */
+  IS_ERR_NO_MEMORY = 5,     /* host allocation of a plan failed */
+  IS_ERR_WORKSPACE = 6      /* workspace missing or smaller than required */
+} is_status;
+
+typedef enum { IS_F32 = 0, IS_F16 = 1 } is_dtype;
+typedef enum { IS_NCHW = 0, IS_NHWC = 1 } is_layout;
+
+/* One convolution layer.
+ *  n, c, h, w : input batch, channels, height, width (h, w may be 0: empty, no work)
+ *  k, r, s    : output channels, filter height, filter width (r and s odd, >= 1)
+ *  pad_h/pad_w: must equal (r-1)/2 and (s-1)/2 (same-size zero padding)
+ *  stride_h/w : must be 1
+ *  in_dtype / out_dtype: (IS_F32, IS_F32) with layout IS_NCHW, or
+ *                        (IS_F16, IS_F16) with layout IS_NHWC
+ *  layout     : memory order of x and y: NCHW (x[n][c][i][j]) or NHWC (x[n][i][j][c])
+ *  relu       : 0 = identity, 1 = ReLU after the bias                              */
+typedef struct {
+  int n, c, h, w;
+  int k, r, s;
+  int pad_h, pad_w;
+  int stride_h, stride_w;
+  is_dtype in_dtype, out_dtype;
+  is_layout layout;
+  int relu;
+} conv2d_desc;
+
+typedef struct conv2d_plan_s *conv2d_plan;
+
+/* What a plan will launch (read-only, for tests and measurement). */
+typedef struct {
+  char kernel[64];        /* device kernel family name, e.g. "is_k1_single" */
+  int grid_x, grid_y, grid_z;
+  int block;              /* threads per workgroup */
+  int lds_bytes;          /* LDS per workgroup */
+  int tile_w, tile_h;     /* output pixels per wave or workgroup tile */
+  double flops;           /* algorithmic: 2*N*K*C*R*S*H*W */
+  double bytes;           /* algorithmic: x + y + w + b, each once */
+} conv2d_plan_info;
+
+/* Validate a descriptor and choose a kernel, a tile and a grid. Host only: runs
+ * without a GPU. On success *out receives a plan that the caller releases with
+ * conv2d_destroy. A plan is immutable and may be used from several threads and
+ * streams at once. Errors: IS_ERR_INVALID_ARG (null, negative sizes, c or k < 1,
+ * wrong padding, stride != 1), IS_ERR_UNSUPPORTED (even r or s, dtype/layout
+ * pair not listed above, r or s > 31), IS_ERR_NO_MEMORY. */
+is_status conv2d_create(const conv2d_desc *d, conv2d_plan *out);
+
+/* Enqueue y = act(conv(x, w) + bias) on `stream`.
+ *  x: input in the plan's layout and dtype, N*C*H*W elements
+ *  w: K*C*R*S weights in the input dtype
+ *  bias: K fp32 values, or NULL
+ *  y: output in the plan's layout and dtype, N*K*H*W elements (written in full)
+ * Errors: IS_ERR_INVALID_ARG (null plan/x/w/y, x and y overlap),
+ * IS_ERR_MISALIGNED, IS_ERR_HIP. */
+is_status conv2d_forward(conv2d_plan plan, const void *x, const void *w,
+                         const float *bias, void *y, hipStream_t stream);
+
+/* Release a plan (NULL is ignored). */
+void conv2d_destroy(conv2d_plan plan);
+
+/* Describe what a plan launches. */
+is_status conv2d_get_plan_info(conv2d_plan plan, conv2d_plan_info *info);
+
+/* A chain of layers applied one after another, each reading the previous
+ * layer's output: z_0 = x, z_l = act_l(conv_l(z_{l-1}) + b_l), and finally an
+ * optional depth-to-space by `depth_to_space` = 2 that turns the last layer's
+ * 4 channels of HxW into one channel of 2Hx2W with
+ * out[n,0,2i+dy,2j+dx] = z[n,2*dy+dx,i,j]. This is the neural upscaling
+ * network of the same StreamHPC page (introduction; layer table of "Reducing
+ * memory traffic"), and the fused evaluation follows the warp-sized overlapped
+ * tiles with loop fusion of "Model-Based Warp Overlapped Tiling for Image
+ * Processing Programs on GPUs" (arXiv 1909.07190, abstract).
+ *  Layer l reads layer[l].c channels (layer[0].c = input channels, layer[l].c
+ *  = layer[l-1].k), has layer[l].k outputs, odd r == s, and ReLU if relu != 0.
+ *  dtype: IS_F32 only (NCHW). */
+typedef struct { int c, k, r, s, relu; } conv_layer_desc;
+
+typedef enum {
+  IS_CHAIN_AUTO = 0,     /* fused when a fused kernel exists for the chain, else layer by layer */
+  IS_CHAIN_FUSED = 1,    /* fused only (IS_ERR_UNSUPPORTED if no fused kernel fits) */
+  IS_CHAIN_UNFUSED = 2   /* one conv2d launch per layer through the workspace */
+} is_chain_mode;
+
+typedef struct {
+  int n, h, w, n_layers;
+  conv_layer_desc layer[IS_MAX_CHAIN];
+  int depth_to_space;    /* 1 = none, 2 = x2 on the last layer (needs its k == 4) */
+  is_dtype dtype;
+  is_chain_mode mode;
+} conv_chain_desc;
+
+/* Device bytes of workspace conv_chain_forward needs for this chain and mode
+ * (0 for the fused kernel; two intermediate tensors for layer by layer). */
+is_status conv_chain_workspace_size(const conv_chain_desc *d, size_t *bytes);
+
+/* Enqueue the chain on `stream`.
+ *  x: N x layer[0].c x H x W fp32 input
+ *  w[l], b[l]: host arrays of n_layers device pointers (b[l] may be NULL)
+ *  y: N x layer[last].k x H x W, or N x 1 x 2H x 2W with depth_to_space = 2
+ *  workspace: device memory of at least conv_chain_workspace_size bytes, or
+ *             NULL when that size is 0
+ * Errors: as conv2d_forward, plus IS_ERR_WORKSPACE and IS_ERR_UNSUPPORTED. */
+is_status conv_chain_forward(const conv_chain_desc *d, const void *x,
+                             const void *const *w, const float *const *b,
+                             void *y, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Name of the kernel family conv_chain_forward launches for this chain
+ * ("is_k3_chain" when fused), copied into name[0..len-1]. */
+is_status conv_chain_kernel_name(const conv_chain_desc *d, char *name, size_t len);
+
+/* LDS bytes of an input tile that covers tile_w x tile_h outputs of a filter
+ * r x s over `channels` channels of `elem_bytes` each: the tile plus its halo,
+ * (tile_w + s - 1) * (tile_h + r - 1) * channels * elem_bytes. The sizing rule
+ * of the shared-memory table in "Some notes on workgroup sizes" (StreamHPC
+ * page). Returns 0 for non-positive arguments. */
+size_t is_lds_tile_bytes(int tile_w, int tile_h, int r, int s, int channels, int elem_bytes);
+
+/* XOR swizzle of an LDS index, the formula of "CUDA shared memory swizzling"
+ * (section on the swizzling formula): for an array T a[][nx] with
+ * nx * elem_bytes a power of two >= 32 and chunks of chunk_bytes (a power of
+ * two, elem_bytes <= chunk_bytes <= nx * elem_bytes), element [y][x] is stored
+ * at column x_swz of row y. The same function the device code uses.
+ * Returns -1 for arguments outside those rules. */
+int is_swizzle_col(int y, int x, int nx, int elem_bytes, int chunk_bytes);
+
+const char *is_status_str(is_status st);
+int is_last_hip_error(void);   /* hipError_t of this thread's most recent IS_ERR_HIP */
+int is_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IMGSTENCIL_H */

@@ -41,6 +41,8 @@ def load_library(path):
     lib.oracle_conv2d_points.restype = ctypes.c_int
     lib.oracle_depth_to_space.argtypes = [i64, i64, i64, i64, _f64p, _f64p]
     lib.oracle_depth_to_space.restype = ctypes.c_int
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ctypes.c_int
     return lib
 
 
@@ -52,6 +54,11 @@ def _load():
             _build.build()
         _lib = load_library(_LIB_PATH)
     return _lib
+
+
+def threads():
+    """Host threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
 
 
 def _f64(a):

@@ -31,6 +31,9 @@
 #include <stdint.h>
 #include <stddef.h>
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_OK 0
 #define ORACLE_EINVAL 1
@@ -149,4 +152,13 @@ int oracle_depth_to_space(int64_t N, int64_t H, int64_t W, int64_t f,
             out[(size_t)((n * Ho + (f * i + dy)) * Wo + (f * j + dx))] =
                 z[idx_nchw(n, f * dy + dx, i, j, C, H, W)];
   return ORACLE_OK;
+}
+
+/* Threads the parallel loops above use (1 without OpenMP). */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

@@ -1,0 +1,121 @@
+"""GPU parity of single-channel filtering (C = K = 1, fp32 NCHW) against the oracle.
+
+Every call goes through the C ABI (conv2d_create / conv2d_forward) on the
+current HIP stream. Full comparisons at sizes the oracle finishes in seconds
+(several 256-column wave segments and 128-row strips, ragged tails, widths that
+are not multiples of 4); at 8192x8192 the comparison covers sampled rows and
+columns chosen on strip and segment boundaries.
+"""
+import numpy as np
+import pytest
+
+import image_stencil_amd as isa
+import oracle
+import synth
+from gpu_util import dev, host, say
+from tolerance import TAU_F32, check
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, w, b=None, relu=False, expect="is_k1_single"):
+    import torch
+    N, C, H, W = x.shape
+    K, _, R, S = w.shape
+    plan = isa.Plan(isa.make_desc(N, C, H, W, K, R, S, "f32", relu))
+    assert plan.info()["kernel"] == expect
+    xd, wd = dev(x), dev(w)
+    bd = dev(b) if b is not None else None
+    y = torch.full((N, K, H, W), float("nan"), dtype=torch.float32, device="cuda")
+    plan.forward(xd, wd, bd, y)
+    return host(y)
+
+
+def test_small_image_3x3():
+    """256x256 image, 3x3 normal(0,1) filter, seed 0, no bias: every output."""
+    x, w = synth.small_image_3x3(seed=0)
+    say("small image 3x3 256x256")
+    y = _run(x, w)
+    ref, m = oracle.conv2d(x, w)
+    ratio = check(y, ref, m, TAU_F32, "256x256 3x3")
+    say("max err/bound", ratio)
+
+
+SHAPES = [(1, 1), (7, 3), (3, 260), (255, 257), (300, 700), (129, 1024), (1000, 260), (2, 1536)]
+FILTERS = [(1, 1), (3, 3), (5, 5), (7, 7), (3, 7), (7, 1), (1, 5), (5, 3)]
+
+
+@pytest.mark.parametrize("H,W", SHAPES)
+@pytest.mark.parametrize("R,S", FILTERS)
+def test_ragged_shapes(H, W, R, S):
+    x, _ = synth.single_channel(H, W, R, N=2, seed=H * 31 + W)
+    w = np.random.default_rng(R * 10 + S).standard_normal((1, 1, R, S)).astype(np.float32)
+    say("single", H, W, R, S)
+    y = _run(x, w)
+    ref, m = oracle.conv2d(x, w)
+    check(y, ref, m, TAU_F32, "single %dx%d R=%d S=%d" % (H, W, R, S))
+
+
+@pytest.mark.parametrize("relu", [False, True])
+def test_bias_and_relu(relu):
+    x, w = synth.single_channel(300, 516, 5, N=1, seed=3)
+    x = x - np.float32(0.5)
+    b = np.array([0.125], np.float32)
+    say("bias relu", relu)
+    y = _run(x, w, b, relu)
+    ref, m = oracle.conv2d(x, w, b, relu)
+    check(y, ref, m, TAU_F32, "bias relu=%s" % relu)
+
+
+def test_delta_filters_bit_exact():
+    """A one-hot filter copies the shifted image: exact on the GPU too, since every
+    product is by 1.0 or 0.0 and sums with zeros are exact."""
+    x, _ = synth.single_channel(261, 520, 7, N=1, seed=5)
+    for (R, S) in ((7, 7), (3, 5), (1, 1)):
+        for u0 in range(R):
+            for v0 in range(S):
+                w = np.zeros((1, 1, R, S), np.float32)
+                w[0, 0, u0, v0] = 1.0
+                y = _run(x, w)
+                ref, _ = oracle.conv2d(x, w)
+                np.testing.assert_array_equal(y.astype(np.float64), ref, err_msg="delta %d,%d" % (u0, v0))
+
+
+def test_empty_image_launches_nothing():
+    import torch
+    plan = isa.Plan(isa.make_desc(1, 1, 0, 16, 1, 3, 3))
+    x = torch.zeros(16, device="cuda")
+    w = torch.zeros(9, device="cuda")
+    y = torch.zeros(16, device="cuda")
+    plan.forward(x, w, None, y)
+    torch.cuda.synchronize()
+
+
+def _boundary_rows(H, strip):
+    rows = {0, 1, 2, 3, H - 4, H - 3, H - 2, H - 1}
+    for s in range(strip, H, strip * 7):
+        rows |= {s - 3, s - 1, s, s + 2}
+    rng = np.random.default_rng(1)
+    rows |= set(int(r) for r in rng.integers(0, H, 12))
+    return sorted(r for r in rows if 0 <= r < H)
+
+
+@pytest.mark.parametrize("R", [3, 5, 7])
+def test_large_image_sampled(R):
+    """8192x8192 with an RxR normal(0, 1/(R*R)) filter: the launch the benchmark
+    times, checked on whole rows and columns around strip and segment edges."""
+    x, w = synth.large_image(R)
+    say("large image", R)
+    plan = isa.Plan(isa.make_desc(1, 1, 8192, 8192, 1, R, R))
+    strip = plan.info()["tile"][1]
+    y = _run(x, w)
+    assert np.isfinite(y).all()
+    rows = _boundary_rows(8192, strip)
+    cols = [0, 1, 2, 255, 256, 257, 4095, 4096, 8189, 8190, 8191]
+    pts = [(0, 0, i, j) for i in rows for j in range(8192)]
+    pts += [(0, 0, i, j) for j in cols for i in range(8192)]
+    pts = np.array(pts, np.int64)
+    ref, m = oracle.conv2d_points(x, w, None, False, pts)
+    got = y[pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]]
+    ratio = check(got, ref, m, TAU_F32, "8192^2 R=%d" % R)
+    say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))

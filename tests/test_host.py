@@ -1,0 +1,229 @@
+"""Host-side checks of the C ABI and the analytic models (no GPU needed).
+
+The library is loaded but no kernel is launched: descriptor validation, plan
+choice, the LDS sizing rule and the swizzle index map are pure host code.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import image_stencil_amd as isa
+from image_stencil_amd import _abi, traffic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M):
+            if m.group(1) not in ("if", "typedef", "defined"):
+                names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_abi.LIB_PATH)
+    declared = _declared_functions()
+    assert {"conv2d_create", "conv2d_forward", "conv_chain_forward"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), "symbol %s declared in include/ but not exported" % name
+    # and the binding declares a signature for each
+    assert declared == {s[0] for s in _abi.SIGNATURES}
+
+
+def test_version():
+    assert isa.is_version() == 1
+
+
+def _status(desc):
+    plan = ctypes.c_void_p()
+    st = _abi.load().conv2d_create(ctypes.byref(desc), ctypes.byref(plan))
+    if st == 0:
+        _abi.load().conv2d_destroy(plan)
+    return st
+
+
+def test_create_validation():
+    ok = isa.make_desc(1, 1, 64, 64, 1, 3, 3)
+    assert _status(ok) == _abi.IS_OK
+    bad = isa.make_desc(1, 1, 64, 64, 1, 4, 3)
+    assert _status(bad) == _abi.IS_ERR_UNSUPPORTED          # even filter
+    d = isa.make_desc(1, 1, 64, 64, 1, 3, 3)
+    d.pad_h = 0
+    assert _status(d) == _abi.IS_ERR_INVALID_ARG           # not same padding
+    d = isa.make_desc(1, 1, 64, 64, 1, 3, 3)
+    d.stride_w = 2
+    assert _status(d) == _abi.IS_ERR_INVALID_ARG
+    d = isa.make_desc(1, 0, 64, 64, 1, 3, 3)
+    assert _status(d) == _abi.IS_ERR_INVALID_ARG           # no channels
+    d = isa.make_desc(-1, 1, 64, 64, 1, 3, 3)
+    assert _status(d) == _abi.IS_ERR_INVALID_ARG
+    d = isa.make_desc(1, 4, 8, 8, 4, 3, 3)
+    d.layout = _abi.IS_NHWC                                 # fp32 NHWC not offered
+    assert _status(d) == _abi.IS_ERR_UNSUPPORTED
+    d = isa.make_desc(1, 4, 8, 8, 4, 3, 3, dtype="f16")
+    assert _status(d) == _abi.IS_OK
+    d.out_dtype = _abi.IS_F32
+    assert _status(d) == _abi.IS_ERR_UNSUPPORTED
+    d = isa.make_desc(1, 1, 0, 0, 1, 3, 3)                  # empty image is valid
+    assert _status(d) == _abi.IS_OK
+    assert _abi.load().conv2d_create(None, None) == _abi.IS_ERR_INVALID_ARG
+
+
+def test_forward_argument_errors_need_no_gpu():
+    """Null and misaligned pointers are rejected before any launch."""
+    p = isa.Plan(isa.make_desc(1, 1, 64, 64, 1, 3, 3))
+    lib = _abi.load()
+    assert lib.conv2d_forward(p.handle, None, 16, None, 4096 * 16, None) == _abi.IS_ERR_INVALID_ARG
+    assert lib.conv2d_forward(p.handle, 0x1004, 0x2000, None, 0x100000, None) == _abi.IS_ERR_MISALIGNED
+    # x and y overlapping
+    assert lib.conv2d_forward(p.handle, 0x10000, 0x200, None, 0x10000 + 64, None) == _abi.IS_ERR_INVALID_ARG
+    assert lib.conv2d_forward(None, 0x1000, 0x2000, None, 0x100000, None) == _abi.IS_ERR_INVALID_ARG
+
+
+def test_plan_choice_and_counts():
+    for R in (3, 5, 7):
+        p = isa.Plan(isa.make_desc(1, 1, 8192, 8192, 1, R, R))
+        info = p.info()
+        assert info["kernel"] == "is_k1_single"
+        assert info["flops"] == 2 * R * R * 8192 * 8192
+        assert info["flops"] == traffic.conv_flops(1, 1, 8192, 8192, 1, R, R)
+        assert info["bytes"] == traffic.conv_bytes(1, 1, 8192, 8192, 1, R, R)
+        gx = info["grid"][0]
+        assert gx == 32 * (8192 // info["tile"][1])
+    # counts quoted for the workloads: 1.21/3.36/6.58 GFLOP and 536.9 MB for 8192^2
+    assert round(traffic.conv_flops(1, 1, 8192, 8192, 1, 3, 3) / 1e9, 2) == 1.21
+    assert round(traffic.conv_flops(1, 1, 8192, 8192, 1, 7, 7) / 1e9, 2) == 6.58
+    assert round(traffic.conv_flops(1, 32, 720, 1280, 32, 3, 3) / 1e9, 2) == 16.99
+    chain = [(1, 32, 5), (32, 32, 3), (32, 32, 3), (32, 4, 3)]
+    assert round(traffic.chain_flops(1, 720, 1280, chain) / 1e9, 2) == 37.57
+    assert round(traffic.conv_flops(8, 64, 256, 256, 64, 3, 3) / 1e9, 2) == 38.65
+    # wide filters fall back to the one-thread-per-output kernel
+    info = isa.Plan(isa.make_desc(1, 1, 64, 64, 1, 9, 9)).info()
+    assert info["kernel"] == "is_k0_generic_nchw_f32"
+
+
+def test_lds_tile_rule_matches_vulkan_table():
+    """(tile_w + s - 1)(tile_h + r - 1) * channels * bytes reproduces the page's table."""
+    for wx, wy, kb in _read_golden("vulkan_lds_tile_table.txt"):
+        b = isa.is_lds_tile_bytes(int(wx), int(wy), 3, 3, 64, 2)
+        assert b == float(kb) * 1024, (wx, wy, kb, b)
+    assert isa.is_lds_tile_bytes(0, 8, 3, 3, 64, 2) == 0
+
+
+def test_naive_traffic_model_matches_vulkan_table():
+    rows = _read_golden("vulkan_naive_traffic_table.txt")
+    total_in, total_reads = 0.0, 0.0
+    for row in rows:
+        if row[0] == "total":
+            assert total_in == float(row[1]) and total_reads == float(row[2])
+            continue
+        _, cin, cin_p, cout, cout_p, kern, in_mb, reads_mb = row
+        size, reads = traffic.naive_input_reads(720, 1280, int(cin_p), int(cout_p))
+        # the page prints the input size rounded to MB (exact for layers 2-4)
+        assert abs(size / traffic.MIB - float(in_mb)) < 0.5
+        assert reads / traffic.MIB == pytest.approx(float(in_mb) * int(cout_p), abs=0.5 * int(cout_p))
+        assert float(reads_mb) == float(in_mb) * int(cout_p)
+        total_in += float(in_mb)
+        total_reads += float(reads_mb)
+
+
+def test_kepler_paper_formulas():
+    # registers for n contiguous outputs of a KxK filter, K*(K+n-1): 3x3, n=2 -> 12
+    assert traffic.special_case_registers(3, 2) == 12
+    assert traffic.special_case_registers(5, 1) == 25
+    # one thread owning W_T contiguous outputs reads (W_T+K-1)*K*C instead of W_T*K*K*C;
+    # the ratio is (W_T+K-1)/(W_T*K)
+    for wt, k, c in ((4, 3, 32), (8, 5, 16), (1, 3, 1)):
+        a = traffic.shared_reads(wt, k, c, True)
+        b = traffic.shared_reads(wt, k, c, False)
+        assert a / b == pytest.approx((wt + k - 1) / (wt * k))
+
+
+# ------------------------------------------------------------- LDS swizzle map
+def _passes(words, banks=32):
+    """Passes a warp access needs: the largest number of distinct words in one bank."""
+    per_bank = {}
+    for w in words:
+        per_bank.setdefault(w % banks, set()).add(w)
+    return max(len(v) for v in per_bank.values())
+
+
+def test_swizzle_is_a_bijection_per_row():
+    for nx, eb, cb in ((16, 4, 4), (32, 4, 4), (8, 4, 16), (64, 2, 16), (32, 2, 8), (128, 2, 16), (16, 8, 8)):
+        for y in range(0, 70):
+            cols = [isa.is_swizzle_col(y, x, nx, eb, cb) for x in range(nx)]
+            assert sorted(cols) == list(range(nx)), (nx, eb, cb, y)
+            # elements keep their offset inside a chunk
+            per = cb // eb
+            assert all(c % per == x % per for x, c in enumerate(cols))
+
+
+def test_swizzle_spreads_columns_over_rows():
+    """Property 3 of the page: for a fixed column, consecutive rows land in as many
+    distinct swizzled columns as there are chunks in a row."""
+    for nx, eb, cb in ((32, 4, 4), (16, 4, 4), (64, 2, 16)):
+        chunks = nx * eb // cb
+        per = cb // eb
+        for x in range(nx):
+            got = {isa.is_swizzle_col(y, x, nx, eb, cb) // per for y in range(chunks)}
+            assert len(got) == chunks
+
+
+def test_swizzle_rejects_bad_arguments():
+    assert isa.is_swizzle_col(0, 0, 12, 4, 4) == -1      # nx not a power of two
+    assert isa.is_swizzle_col(0, 0, 4, 4, 4) == -1       # row of 16 bytes < 32
+    assert isa.is_swizzle_col(0, 16, 16, 4, 4) == -1     # x out of range
+    assert isa.is_swizzle_col(0, 0, 16, 4, 2) == -1      # chunk smaller than element
+
+
+def test_swizzle_worked_example():
+    """The 32x16 and 32x32 float examples of the swizzling page (see the fixture)."""
+    for rows, cols, eb, layout, access, passes in _read_golden("swizzle_32x16_example.txt"):
+        rows, cols, eb, passes = int(rows), int(cols), int(eb), int(passes)
+
+        def word(y, x):
+            xs = isa.is_swizzle_col(y, x, cols, eb, eb) if layout == "swizzled" else x
+            return y * cols + xs
+
+        if access == "write":       # 32 consecutive values: rows 0.. of the array
+            words = [word(t // cols, t % cols) for t in range(32)]
+            got = _passes(words)
+        else:                       # worst column over all columns
+            got = max(_passes([word(y, x) for y in range(rows)]) for x in range(cols))
+        assert got == passes, (rows, cols, layout, access, got, passes)
+
+
+def test_chain_descriptor_checks():
+    d = isa.make_chain_desc(1, 16, 16, [(1, 8, 5, True), (8, 4, 3, False)], depth_to_space=2)
+    ws = isa.conv_chain_workspace_size(d)
+    assert ws >= 2 * 4 * 8 * 16 * 16
+    assert isa.conv_chain_kernel_name(d) in ("layer_by_layer", "is_k3_chain")
+    bad = isa.make_chain_desc(1, 16, 16, [(1, 8, 5, True), (7, 4, 3, False)])
+    with pytest.raises(isa.ImgStencilError):
+        isa.conv_chain_workspace_size(bad)
+    bad = isa.make_chain_desc(1, 16, 16, [(1, 8, 5, True), (8, 3, 3, False)], depth_to_space=2)
+    with pytest.raises(isa.ImgStencilError):
+        isa.conv_chain_workspace_size(bad)
+    one = isa.make_chain_desc(1, 16, 16, [(1, 4, 3, False)], depth_to_space=1,
+                              mode=isa.IS_CHAIN_UNFUSED)
+    assert isa.conv_chain_workspace_size(one) == 0
