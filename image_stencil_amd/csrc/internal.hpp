@@ -37,6 +37,10 @@ bool configure_single(Plan &p);
 hipError_t launch_single(const Plan &p, const float *x, const float *w, const float *b, float *y,
                          hipStream_t s);
 
+bool configure_multi(Plan &p);
+hipError_t launch_multi(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                        hipStream_t s);
+
 // out[n,0,2i+dy,2j+dx] = z[n,2*dy+dx,i,j] for z of N x 4 x H x W fp32.
 hipError_t launch_depth_to_space2(const float *z, float *out, int N, int H, int W, hipStream_t s);
 

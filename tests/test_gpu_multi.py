@@ -1,0 +1,91 @@
+"""GPU parity of multi-channel fp32 NCHW layers against the oracle.
+
+Calls go through the C ABI. Shapes span several 64x16 tiles with ragged edges,
+channel counts that fill one or several LDS slabs, every output-channel group
+size, and the full 1x32x720x1280 layer (sampled rows, all columns and
+channels).
+"""
+import numpy as np
+import pytest
+
+import image_stencil_amd as isa
+import oracle
+import synth
+from gpu_util import dev, host, say
+from tolerance import TAU_F32, check
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, w, b, relu, expect=None):
+    import torch
+    N, C, H, W = x.shape
+    K, _, R, S = w.shape
+    plan = isa.Plan(isa.make_desc(N, C, H, W, K, R, S, "f32", relu))
+    if expect:
+        assert plan.info()["kernel"] == expect
+    y = torch.full((N, K, H, W), float("nan"), dtype=torch.float32, device="cuda")
+    plan.forward(dev(x), dev(w), dev(b) if b is not None else None, y)
+    return host(y)
+
+
+CASES = [
+    # N, C, K, H, W, R, relu, kernel
+    (1, 32, 32, 50, 200, 3, True, "is_k2_multi"),
+    (2, 8, 16, 37, 132, 3, False, "is_k2_multi"),
+    (1, 4, 8, 17, 68, 3, True, "is_k2_multi"),
+    (1, 4, 4, 33, 64, 3, False, "is_k2_multi"),
+    (1, 1, 32, 40, 136, 5, True, "is_k2_multi"),
+    (1, 8, 32, 21, 72, 5, False, "is_k2_multi"),
+    (1, 1, 32, 19, 68, 3, True, "is_k2_multi"),
+    (1, 12, 32, 16, 64, 1, False, "is_k2_multi"),
+    (1, 32, 4, 45, 140, 3, False, "is_k2_multi"),
+    (3, 3, 8, 9, 20, 3, True, "is_k0_generic_nchw_f32"),
+    (1, 5, 6, 11, 30, 5, False, "is_k0_generic_nchw_f32"),
+    (1, 8, 8, 10, 13, 3, True, "is_k0_generic_nchw_f32"),
+]
+
+
+@pytest.mark.parametrize("N,C,K,H,W,R,relu,kernel", CASES)
+def test_multichannel_shapes(N, C, K, H, W, R, relu, kernel):
+    x, w, b = synth.cnn_layer_f32(N=N, C=C, K=K, H=H, W=W, R=R, seed=C * 7 + K)
+    say("multi", N, C, K, H, W, R, relu)
+    y = _run(x, w, b, relu, kernel)
+    ref, m = oracle.conv2d(x, w, b, relu)
+    ratio = check(y, ref, m, TAU_F32, "multi N%d C%d K%d %dx%d R%d" % (N, C, K, H, W, R))
+    say("max err/bound %.3g" % ratio)
+
+
+def test_no_bias():
+    x, w, _ = synth.cnn_layer_f32(N=1, C=8, K=8, H=20, W=64, seed=2)
+    y = _run(x, w, None, False, "is_k2_multi")
+    ref, m = oracle.conv2d(x, w, None, False)
+    check(y, ref, m, TAU_F32, "no bias")
+
+
+def test_delta_weights_bit_exact():
+    """One-hot weights per output channel copy a shifted input channel exactly."""
+    x, _, _ = synth.cnn_layer_f32(N=1, C=8, K=8, H=33, W=136, seed=3)
+    w = np.zeros((8, 8, 3, 3), np.float32)
+    rng = np.random.default_rng(4)
+    for k in range(8):
+        w[k, rng.integers(0, 8), rng.integers(0, 3), rng.integers(0, 3)] = 1.0
+    y = _run(x, w, None, False, "is_k2_multi")
+    ref, _ = oracle.conv2d(x, w)
+    np.testing.assert_array_equal(y.astype(np.float64), ref)
+
+
+def test_cnn_layer_720p_sampled():
+    """1x32x720x1280 -> 32, 3x3, bias, ReLU: rows on tile edges and random rows,
+    every column and output channel."""
+    x, w, b = synth.cnn_layer_f32()
+    say("cnn layer 720p")
+    y = _run(x, w, b, True, "is_k2_multi")
+    assert np.isfinite(y).all()
+    rows = sorted({0, 1, 15, 16, 17, 31, 32, 47, 359, 360, 703, 704, 718, 719} |
+                  set(int(r) for r in np.random.default_rng(5).integers(0, 720, 6)))
+    pts = np.array([(0, k, i, j) for k in range(32) for i in rows for j in range(1280)], np.int64)
+    ref, m = oracle.conv2d_points(x, w, b, True, pts)
+    got = y[pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]]
+    ratio = check(got, ref, m, TAU_F32, "720p layer")
+    say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))
