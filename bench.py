@@ -100,6 +100,41 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup):
                             "roofline": _roofline(c, ms)}
     for c in cases:
         c.keep = None
+
+    # Upscaling chain on a 1280x720 frame: fused kernel and layer by layer.
+    x, layers = synth.chain_f32()
+    spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
+    flops = sum(2.0 * 720 * 1280 * k * c * r * r for (c, k, r, _) in spec)
+    nbytes = 4.0 * (720 * 1280 * 5) + sum(4.0 * (k * c * r * r + k) for (c, k, r, _) in spec)
+    wl = [(torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()) for (w, b, _) in layers]
+    for mode_name, mode in (("fused", isa.IS_CHAIN_FUSED), ("unfused", isa.IS_CHAIN_UNFUSED)):
+        d = isa.make_chain_desc(1, 720, 1280, spec, 2, mode)
+        kname = isa.conv_chain_kernel_name(d)
+        ws_bytes = isa.conv_chain_workspace_size(d)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        ccases = []
+        for _ in range(16):
+            xd = torch.from_numpy(x).cuda()
+            yd = torch.empty((1, 1, 1440, 2560), dtype=torch.float32, device="cuda")
+
+            def launch(d=d, xd=xd, yd=yd, ws=ws, ws_bytes=ws_bytes):
+                isa.conv_chain_forward(d, xd.data_ptr(), [w.data_ptr() for (w, _) in wl],
+                                       [b.data_ptr() for (_, b) in wl], yd.data_ptr(),
+                                       ws.data_ptr() if ws_bytes else None, ws_bytes, stream)
+
+            c = Case("upscaling chain 1280x720 (%s)" % mode_name, launch, flops, nbytes, kname)
+            c.keep = (xd, yd)
+            ccases.append(c)
+        _, per, _ = _time_cases(torch, ccases, steps, warmup, stream_obj)
+        ms = sum(per) / len(per)
+        out["upscale_chain_" + mode_name] = {
+            "workload": ccases[0].name + ": 5x5 1->32, 3x3 32->32 x2, 3x3 32->4, depth-to-space x2",
+            "kernel": kname, "ms_per_frame": round(ms, 4), "gflops": round(flops / ms / 1e6, 1),
+            "frac_fp32_valu": round(flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
+            "frac_fp32_packed_peak": round(flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4)}
+        for c in ccases:
+            c.keep = None
+        del ws
     return out
 
 

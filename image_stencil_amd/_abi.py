@@ -71,6 +71,14 @@ def load():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libimgstencil.so is not built (%s); run __graft_entry__.build() "
                                "or python image_stencil_amd/build.py" % LIB_PATH)
+        # Let torch load its HIP runtime first when it is installed: the library
+        # then binds to that same libamdhip64.so.7, so that device pointers and
+        # streams coming from torch are valid in it. Loaded first, the library
+        # would pull in the system runtime, and torch would have to share it.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         for name, res, args in SIGNATURES:
             fn = getattr(lib, name)

@@ -145,7 +145,7 @@ is_status chain_layers(const conv_chain_desc *d, conv2d_desc *ld) {
   return IS_OK;
 }
 
-bool chain_fusable(const conv_chain_desc *, const conv2d_desc *) { return false; }
+bool chain_fusable(const conv_chain_desc *d, const conv2d_desc *) { return is::chain_fused_supported(d); }
 
 size_t chain_buffer_bytes(const conv_chain_desc *d) {
   size_t m = 0;
@@ -218,6 +218,11 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void
     if (need > 0 && (overlap(workspace, need, x, xb) || overlap(workspace, need, y, yb)))
       return IS_ERR_INVALID_ARG;
     if (xb == 0 || yb == 0) return IS_OK;
+
+    if (need == 0 && d->mode != IS_CHAIN_UNFUSED && chain_fusable(d, ld))
+      return hip_status(is::launch_chain_fused(d, static_cast<const float *>(x),
+                                               reinterpret_cast<const float *const *>(w), b,
+                                               static_cast<float *>(y), stream));
 
     const size_t half = chain_buffer_bytes(d);
     char *ws = static_cast<char *>(workspace);

@@ -55,4 +55,15 @@ __host__ __device__ constexpr int swizzle_col(int y, int x, int nx, int eb, int 
   return (int)((x_chunk_swz * per_chunk) % nx) + x % per_chunk;
 }
 
+// Launch and report this launch's error. hipGetLastError() is per-thread state
+// that earlier calls of the host program (not ours) may have left set; it is
+// cleared first so that only a failure of this launch is returned.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned lds, hipStream_t s,
+                         Args &&...args) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<KArgs>(args)...);
+  return hipGetLastError();
+}
+
 }  // namespace is

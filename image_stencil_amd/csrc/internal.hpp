@@ -41,6 +41,11 @@ bool configure_multi(Plan &p);
 hipError_t launch_multi(const Plan &p, const float *x, const float *w, const float *b, float *y,
                         hipStream_t s);
 
+// The fused upscaling chain (1->32 5x5, 32->32 3x3 twice, 32->4 3x3, depth-to-space x2).
+bool chain_fused_supported(const conv_chain_desc *d);
+hipError_t launch_chain_fused(const conv_chain_desc *d, const float *x, const float *const *w,
+                              const float *const *b, float *y, hipStream_t s);
+
 // out[n,0,2i+dy,2j+dx] = z[n,2*dy+dx,i,j] for z of N x 4 x H x W fp32.
 hipError_t launch_depth_to_space2(const float *z, float *out, int N, int H, int W, hipStream_t s);
 

@@ -93,16 +93,13 @@ bool configure_generic(Plan &p) {
 hipError_t launch_generic(const Plan &p, const void *x, const void *w, const float *b, void *y,
                           hipStream_t s) {
   const conv2d_desc &d = p.d;
-  if (p.kid == kGenericNchwF32) {
-    hipLaunchKernelGGL(is_k0_generic_nchw_f32, dim3(p.grid_x), dim3(p.block), 0, s,
-                       static_cast<const float *>(x), static_cast<const float *>(w), b,
-                       static_cast<float *>(y), d.n, d.c, d.h, d.w, d.k, d.r, d.s, d.relu);
-  } else {
-    hipLaunchKernelGGL(is_k0_generic_nhwc_f16, dim3(p.grid_x), dim3(p.block), 0, s,
+  if (p.kid == kGenericNchwF32)
+    return launch_kernel(is_k0_generic_nchw_f32, dim3(p.grid_x), dim3(p.block), 0, s,
+                         static_cast<const float *>(x), static_cast<const float *>(w), b,
+                         static_cast<float *>(y), d.n, d.c, d.h, d.w, d.k, d.r, d.s, d.relu);
+  return launch_kernel(is_k0_generic_nhwc_f16, dim3(p.grid_x), dim3(p.block), 0, s,
                        static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(w), b,
                        static_cast<_Float16 *>(y), d.n, d.c, d.h, d.w, d.k, d.r, d.s, d.relu);
-  }
-  return hipGetLastError();
 }
 
 }  // namespace is

@@ -235,9 +235,8 @@ hipError_t launch_single(const Plan &p, const float *x, const float *w, const fl
   const K1Fn fn = p.vec ? (relu ? pick<true, true>(p.d.r, p.d.s) : pick<true, false>(p.d.r, p.d.s))
                         : (relu ? pick<false, true>(p.d.r, p.d.s) : pick<false, false>(p.d.r, p.d.s));
   if (!fn) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, p.d.h, p.d.w,
+  return launch_kernel(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, p.d.h, p.d.w,
                      p.strip_rows, p.nseg, p.nstrip, p.ntiles);
-  return hipGetLastError();
 }
 
 }  // namespace is

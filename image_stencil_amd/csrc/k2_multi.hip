@@ -283,9 +283,8 @@ hipError_t launch_multi(const Plan &p, const float *x, const float *w, const flo
   const int ft = p.strip_rows, cs = p.vec;
   const K2Fn fn = d.relu ? pick<true>(d.r, ft, cs) : pick<false>(d.r, ft, cs);
   if (!fn) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, d.c, d.h, d.w, d.k, p.nseg,
+  return launch_kernel(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, d.c, d.h, d.w, d.k, p.nseg,
                      p.nstrip, d.k / ft, p.ntiles);
-  return hipGetLastError();
 }
 
 }  // namespace is

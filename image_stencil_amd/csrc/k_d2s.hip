@@ -35,8 +35,7 @@ hipError_t launch_depth_to_space2(const float *z, float *out, int N, int H, int 
   if (total == 0) return hipSuccess;
   long long blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(is_d2s2_f32, dim3((unsigned)blocks), dim3(256), 0, s, z, out, N, H, W);
-  return hipGetLastError();
+  return launch_kernel(is_d2s2_f32, dim3((unsigned)blocks), dim3(256), 0, s, z, out, N, H, W);
 }
 
 }  // namespace is

@@ -1,0 +1,99 @@
+"""GPU parity of the conv chain (fused kernel and layer-by-layer) against the oracle.
+
+The upscaling chain: 5x5 1->32 + ReLU, 3x3 32->32 + ReLU (twice), 3x3 32->4,
+depth-to-space x2. The oracle chains its fp64 layers and propagates the error
+scale m_l = conv(|w_l|, m_{l-1}) + |b_l|; both GPU paths must stay within
+1e-5 * m of it. Small frames cover many row blocks, partial strips and image
+borders; the 1280x720 frame is checked on sampled windows.
+"""
+import numpy as np
+import pytest
+
+import image_stencil_amd as isa
+import oracle
+import synth
+from gpu_util import dev, host, say
+from tolerance import TAU_F32, check
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_chain(x, layers, mode, d2s=2):
+    import torch
+    dl = [(dev(w), dev(b), relu) for (w, b, relu) in layers]
+    y = isa.conv_chain(dev(x), dl, depth_to_space=d2s, mode=mode)
+    return host(y)
+
+
+def _spec(layers):
+    return [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
+
+
+@pytest.mark.parametrize("N,H,W", [(1, 37, 120), (2, 20, 60), (1, 1, 4), (1, 70, 200), (1, 9, 56), (1, 130, 116)])
+@pytest.mark.parametrize("mode", ["fused", "unfused"])
+def test_upscale_chain_small(N, H, W, mode):
+    x, layers = synth.chain_f32(N=N, H=H, W=W, seed=H + W)
+    m_ = isa.IS_CHAIN_FUSED if mode == "fused" else isa.IS_CHAIN_UNFUSED
+    d = isa.make_chain_desc(N, H, W, _spec(layers), 2, m_)
+    assert isa.conv_chain_kernel_name(d) == ("is_k3_chain" if mode == "fused" else "layer_by_layer")
+    say("chain", mode, N, H, W)
+    y = _gpu_chain(x, layers, m_)
+    ref, m = oracle.chain(x, layers, d2s=2)
+    assert y.shape == ref.shape == (N, 1, 2 * H, 2 * W)
+    ratio = check(y, ref, m, TAU_F32, "chain %s %dx%dx%d" % (mode, N, H, W))
+    say("max err/bound %.3g" % ratio)
+
+
+def test_fused_matches_unfused():
+    x, layers = synth.chain_f32(N=1, H=90, W=340, seed=9)
+    yf = _gpu_chain(x, layers, isa.IS_CHAIN_FUSED)
+    yu = _gpu_chain(x, layers, isa.IS_CHAIN_UNFUSED)
+    ref, m = oracle.chain(x, layers, d2s=2)
+    check(yf, ref, m, TAU_F32, "fused")
+    check(yu, ref, m, TAU_F32, "unfused")
+    # the two GPU paths agree to twice the tolerance of each against the oracle
+    assert np.all(np.abs(yf.astype(np.float64) - yu) <= 2 * TAU_F32 * m)
+
+
+def test_relu_flags_and_no_bias():
+    x, layers = synth.chain_f32(N=1, H=24, W=64, seed=10)
+    layers = [(w, None if i == 2 else b, (i % 2 == 0)) for i, (w, b, _) in enumerate(layers)]
+    import torch
+    dl = [(dev(w), dev(b) if b is not None else None, relu) for (w, b, relu) in layers]
+    y = host(isa.conv_chain(dev(x), dl, depth_to_space=2, mode=isa.IS_CHAIN_FUSED))
+    ref, m = oracle.chain(x, layers, d2s=2)
+    check(y, ref, m, TAU_F32, "relu flags")
+
+
+def test_other_chains_run_layer_by_layer():
+    spec = ((3, 8, 3, True), (8, 4, 5, False))
+    x, layers = synth.chain_f32(N=1, H=21, W=40, spec=spec, seed=11)
+    d = isa.make_chain_desc(1, 21, 40, _spec(layers), 1, isa.IS_CHAIN_AUTO)
+    assert isa.conv_chain_kernel_name(d) == "layer_by_layer"
+    with pytest.raises(isa.ImgStencilError):
+        isa.conv_chain_workspace_size(isa.make_chain_desc(1, 21, 40, _spec(layers), 1, isa.IS_CHAIN_FUSED))
+    y = _gpu_chain(x, layers, isa.IS_CHAIN_AUTO, d2s=1)
+    ref, m = oracle.chain(x, layers, d2s=1)
+    check(y, ref, m, TAU_F32, "2-layer chain")
+
+
+def test_upscale_chain_720p_sampled():
+    """The 1280x720 frame through the fused kernel, checked on windows at the
+    frame corners and edges, on strip and block boundaries, and inside."""
+    x, layers = synth.chain_f32()
+    d = isa.make_chain_desc(1, 720, 1280, _spec(layers), 2, isa.IS_CHAIN_AUTO)
+    assert isa.conv_chain_kernel_name(d) == "is_k3_chain"
+    say("chain 720p")
+    y = _gpu_chain(x, layers, isa.IS_CHAIN_AUTO)
+    assert y.shape == (1, 1, 1440, 2560) and np.isfinite(y).all()
+    wins = [(0, 12, 0, 64), (708, 720, 1216, 1280), (0, 8, 1240, 1280), (712, 720, 0, 40),
+            (60, 76, 100, 124), (64, 72, 44, 76), (132, 140, 552, 568), (350, 366, 600, 680),
+            (203, 207, 1100, 1180)]
+    worst = 0.0
+    for (i0, i1, j0, j1) in wins:
+        z, m = oracle.chain_window(x, layers, i0, i1, j0, j1)
+        ref = oracle.depth_to_space(z, 2)
+        mm = oracle.depth_to_space(m, 2)
+        got = y[:, :, 2 * i0:2 * i1, 2 * j0:2 * j1]
+        worst = max(worst, check(got, ref, mm, TAU_F32, "720p window %s" % ((i0, i1, j0, j1),)))
+    say("max err/bound %.3g" % worst)
