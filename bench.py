@@ -101,6 +101,36 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup):
     for c in cases:
         c.keep = None
 
+    # fp16 NHWC layer on the matrix cores.
+    x, w, b = synth.cnn_layer_f16_nhwc()
+    plan = isa.Plan(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16", False))
+    info = plan.info()
+    wd, bd = torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
+    mcases = []
+    for _ in range(4):
+        xd = torch.from_numpy(x).cuda()
+        yd = torch.empty((8, 256, 256, 64), dtype=torch.float16, device="cuda")
+
+        def launch(xd=xd, yd=yd):
+            isa.conv2d_forward(plan.handle, xd.data_ptr(), wd.data_ptr(), bd.data_ptr(), yd.data_ptr(), stream)
+
+        c = Case("fp16 NHWC layer 8x256x256x64 -> 64, 3x3", launch, info["flops"], info["bytes"], info["kernel"])
+        c.keep = (xd, yd)
+        mcases.append(c)
+    _, per, _ = _time_cases(torch, mcases, steps, warmup, stream_obj)
+    ms = sum(per) / len(per)
+    c = mcases[0]
+    ach = c.flops / ms / 1e9
+    out["mfma_layer_f16"] = {"workload": c.name + ", fp32 accumulate, fp16 out", "kernel": c.kernel,
+                             "ms": round(ms, 4), "gflops": round(c.flops / ms / 1e6, 1),
+                             "gbs": round(c.bytes / ms / 1e6, 1),
+                             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
+                                          "unit": "TFLOP/s", "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4),
+                                          "hbm_frac": round(c.bytes / ms / 1e6 / HBM_PEAK_GBS, 4)}}
+    for c in mcases:
+        c.keep = None
+    del plan
+
     # Upscaling chain on a 1280x720 frame: fused kernel and layer by layer.
     x, layers = synth.chain_f32()
     spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]

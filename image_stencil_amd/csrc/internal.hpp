@@ -41,6 +41,10 @@ bool configure_multi(Plan &p);
 hipError_t launch_multi(const Plan &p, const float *x, const float *w, const float *b, float *y,
                         hipStream_t s);
 
+bool configure_mfma(Plan &p);
+hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
+                       hipStream_t s);
+
 // The fused upscaling chain (1->32 5x5, 32->32 3x3 twice, 32->4 3x3, depth-to-space x2).
 bool chain_fused_supported(const conv_chain_desc *d);
 hipError_t launch_chain_fused(const conv_chain_desc *d, const float *x, const float *const *w,

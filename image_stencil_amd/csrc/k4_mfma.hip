@@ -1,0 +1,303 @@
+// k4_mfma.hip -- fp16 NHWC 3x3 layer with 64 input and 64 output channels as an
+// implicit GEMM on the gfx950 matrix cores, fp32 accumulation, fp16 output.
+//
+// For output pixel p and output channel o the layer is
+//   y[p][o] = b[o] + sum_k W[o][k] * X[k][p],  k = (tap t = 3u + v, channel c),
+// a dense contraction of length 9 * 64 = 576 (the "blocked GEMM" view of a
+// convolution that "Optimizing Memory Efficiency for Convolution Kernels on
+// Kepler GPUs" contrasts with its direct method; here the wide-channel layer
+// really is that contraction, so it runs on MFMA). Design:
+//  * persistent workgroups of 4 waves, one per CU; each loops over 8 x 32 pixel
+//    tiles of an image, tiles of one XCD being neighbours so halo re-reads hit
+//    that XCD's L2;
+//  * the input tile with its 1-pixel halo (10 x 34 pixels x 128 bytes) streams
+//    HBM -> LDS by buffer_load ... lds, double-buffered against the MFMAs;
+//    pixels outside the image read as 0 through the buffer range check;
+//  * LDS holds each pixel's 64 channels as eight 16-byte chunks, permuted by the
+//    XOR swizzle of "CUDA shared memory swizzling" (its formula, with 16-byte
+//    elements and chunks) over rows of SWZ bytes, so that 16 lanes reading the
+//    same chunk of 16 consecutive pixels hit distinct banks;
+//  * wave w owns output channels 32*(w&1) .. +32 (two 16-row A blocks) for the
+//    tile rows 4*(w>>1) .. +4; its 36 weight fragments (all 576 k) stay in
+//    registers for the whole kernel;
+//  * v_mfma_f32_16x16x32_f16: A = 16 output channels x 32 k (weights), B = 32 k
+//    x 16 pixels (one 16-byte LDS read per lane), D = 4 consecutive output
+//    channels of one pixel per lane, so the epilogue writes 8-byte fp16 vectors
+//    into the NHWC output after adding the fp32 bias and rounding to nearest even.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace is {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
+typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
+
+constexpr int kC = 64;                       // input channels
+constexpr int kK = 64;                       // output channels
+constexpr int kTR = 8, kTC = 32;             // output tile: rows x columns
+constexpr int kIR = kTR + 2, kIC = kTC + 2;  // input tile with halo
+constexpr int kChunks = kIR * kIC * 8;       // 16-byte chunks per input tile
+constexpr int kThreads = 256;
+constexpr int kRounds = (kChunks + kThreads - 1) / kThreads;   // DMA rounds per wave
+constexpr int kBufChunks = kRounds * kThreads;                 // chunks per LDS buffer
+constexpr int kWVec = kK * 9 * 8;            // weight vectors [o][t][c/8] of 8 halves
+constexpr unsigned kOob = 0xFFFFFFF0u;
+
+static_assert(kWVec <= 2 * kBufChunks, "weights are staged in the tile buffers");
+
+constexpr int kRowSlots = kIC * 8;           // 16-byte slots per input tile row
+
+// Slot of chunk c (0..7) of column cx inside one input-tile row. Each tile row
+// is its own swizzled array: rows of SWZ bytes (one pixel for 128, a pixel pair
+// for 256) whose 16-byte chunks are permuted by XOR with the row index, the
+// formula of "CUDA shared memory swizzling" with 16-byte elements and chunks.
+// SWZ = 0 keeps the plain layout. Row-local keys keep the permutation the same
+// in every tile row, so a row step is a constant offset.
+template <int SWZ>
+__device__ __forceinline__ int slot_in_row(int cx, int c) {
+  if constexpr (SWZ == 0) {
+    return cx * 8 + c;
+  } else {
+    constexpr int NX = SWZ / 16;           // chunks per swizzle row
+    constexpr int PPR = NX / 8;            // pixels per swizzle row
+    const int y = cx / PPR;
+    const int x = (cx % PPR) * 8 + c;
+    return y * NX + swizzle_col(y, x, NX, 16, 16);
+  }
+}
+
+// Inverse: column and chunk stored at slot si of a tile row. The XOR swizzle is
+// an involution inside each swizzle row, so the same map undoes it.
+template <int SWZ>
+__device__ __forceinline__ void chunk_at(int si, int &cx, int &c) {
+  if constexpr (SWZ == 0) {
+    cx = si >> 3;
+    c = si & 7;
+  } else {
+    constexpr int NX = SWZ / 16;
+    constexpr int PPR = NX / 8;
+    const int y = si / NX;
+    const int x = swizzle_col(y, si % NX, NX, 16, 16);
+    cx = y * PPR + x / 8;
+    c = x % 8;
+  }
+}
+
+struct MfmaArgs {
+  const _Float16 *x;
+  const _Float16 *w;
+  const float *bias;
+  _Float16 *y;
+  int N, H, W, relu;
+  int tiles_x, tiles_y, ntiles;
+};
+
+template <int SWZ>
+__global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
+  __shared__ uint4v lds[2 * kBufChunks];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n16 = lane & 15;     // pixel (B, D) or output channel (A) inside a 16-block
+  const int g = lane >> 4;       // k group of 8 (A, B) or channel group of 4 (D)
+  const int oh = wave & 1;       // output-channel half
+  const int mh = wave >> 1;      // tile-row half
+
+  // ---- Weights: stage KCRS into LDS as [o][t][c/8] vectors of 8 channels,
+  // then every lane keeps its 36 A fragments (2 channel blocks x 18 k steps).
+  {
+    _Float16 *wl = reinterpret_cast<_Float16 *>(lds);
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(a.w), (short)0, kK * kC * 9 * 2, kBufferFlags);
+    // 8 consecutive KCRS halves per 16-byte load; element e = o*576 + c*9 + t.
+    for (int v = tid; v < kK * kC * 9 / 8; v += kThreads) {
+      const uint4v q = __builtin_amdgcn_raw_buffer_load_b128(rw, v * 16, 0, 0);
+      const _Float16 *h = reinterpret_cast<const _Float16 *>(&q);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = v * 8 + j;
+        const int o = e / 576, r = e % 576, c = r / 9, t = r % 9;
+        wl[(o * 9 + t) * 64 + c] = h[j];
+      }
+    }
+  }
+  __syncthreads();
+  half8 wa[2][18];
+#pragma unroll
+  for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const int o = 32 * oh + 16 * ob + n16;
+      const int t = ks >> 1, h = ks & 1;
+      wa[ob][ks] = __builtin_bit_cast(half8, lds[(o * 9 + t) * 8 + h * 4 + g]);
+    }
+  float bias[2][4];
+#pragma unroll
+  for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias[ob][i] = a.bias ? a.bias[32 * oh + 16 * ob + 4 * g + i] : 0.f;
+  __syncthreads();
+
+  // ---- Tile schedule: XCD x (= blockIdx mod 8) walks its own contiguous range.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int per_xcd = (a.ntiles + 7) / 8;
+  const int lo = xcd * per_xcd;
+  const int hi = min(a.ntiles, lo + per_xcd);
+  const int step = G >> 3;
+  int tile = lo + (blockIdx.x >> 3);
+
+  const size_t img = (size_t)a.H * a.W * kC;   // halves per image
+  auto tile_origin = [&](int tl, int &n, int &y0, int &x0) {
+    const int tx = tl % a.tiles_x;
+    const int ty = (tl / a.tiles_x) % a.tiles_y;
+    n = tl / (a.tiles_x * a.tiles_y);
+    y0 = ty * kTR;
+    x0 = tx * kTC;
+  };
+  auto issue = [&](int tl, uint4v *buf) {
+    int n, y0, x0;
+    tile_origin(tl, n, y0, x0);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<_Float16 *>(a.x + (size_t)n * img), (short)0, (int)(img * 2), kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int s = (j * 4 + wave) * 64 + lane;
+      const int ry = s / kRowSlots;
+      int cx, c;
+      chunk_at<SWZ>(s - ry * kRowSlots, cx, c);
+      const int gy = y0 - 1 + ry;
+      const int gx = x0 - 1 + cx;
+      const bool in = s < kChunks && gy >= 0 && gy < a.H && gx >= 0 && gx < a.W;
+      const unsigned off = in ? (unsigned)((((size_t)gy * a.W + gx) * kC + c * 8) * 2) : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void *)(buf + (j * 4 + wave) * 64), 16, off, 0, 0, 0);
+    }
+  };
+
+  // Byte offsets (inside a tile buffer) of this lane's B reads for filter column
+  // v, channel half h and 16-pixel column block cb, at tile row 4*mh; the row
+  // (pb/2 + u) adds a constant multiple of a tile row.
+  int boff[3][2][2];
+#pragma unroll
+  for (int v = 0; v < 3; ++v)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        boff[v][h][cb] = ((4 * mh) * kRowSlots + slot_in_row<SWZ>(16 * cb + n16 + v, 4 * h + g)) * 16;
+
+  auto compute_store = [&](int tl, const uint4v *buf) {
+    float4v acc[8][2];
+#pragma unroll
+    for (int pb = 0; pb < 8; ++pb)
+#pragma unroll
+      for (int ob = 0; ob < 2; ++ob) acc[pb][ob] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const int t = ks >> 1, h = ks & 1;
+      const int u = t / 3, v = t % 3;
+#pragma unroll
+      for (int pb = 0; pb < 8; ++pb) {
+        const char *p = reinterpret_cast<const char *>(buf) + boff[v][h][pb & 1] +
+                        ((pb >> 1) + u) * kRowSlots * 16;
+        const half8 b = *reinterpret_cast<const half8 *>(p);
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+          acc[pb][ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[ob][ks], b, acc[pb][ob], 0, 0, 0);
+      }
+    }
+    int n, y0, x0;
+    tile_origin(tl, n, y0, x0);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        a.y + (size_t)n * img, (short)0, (int)(img * 2), kBufferFlags);
+#pragma unroll
+    for (int pb = 0; pb < 8; ++pb) {
+      const int gy = y0 + 4 * mh + (pb >> 1);
+      const int gx = x0 + 16 * (pb & 1) + n16;
+      const bool in = gy < a.H && gx < a.W;
+#pragma unroll
+      for (int ob = 0; ob < 2; ++ob) {
+        _Float16 hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float o = acc[pb][ob][i] + bias[ob][i];
+          if (a.relu) o = fmaxf(o, 0.f);
+          hv[i] = (_Float16)o;
+        }
+        const int oc = 32 * oh + 16 * ob + 4 * g;
+        const unsigned off = in ? (unsigned)((((size_t)gy * a.W + gx) * kK + oc) * 2) : kOob;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, hv), ry, off, 0, 0);
+      }
+    }
+  };
+
+  if (tile < hi) issue(tile, lds);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int cur = 0;
+  while (tile < hi) {
+    const int next = tile + step;
+    if (next < hi) issue(next, lds + (cur ^ 1) * kBufChunks);
+    compute_store(tile, lds + cur * kBufChunks);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    tile = next;
+    cur ^= 1;
+  }
+}
+
+}  // namespace
+
+bool configure_mfma(Plan &p) {
+  const conv2d_desc &d = p.d;
+  if (d.layout != IS_NHWC || d.in_dtype != IS_F16 || d.out_dtype != IS_F16) return false;
+  if (d.c != kC || d.k != kK || d.r != 3 || d.s != 3) return false;
+  if (2.0 * d.h * (double)d.w * kC >= 4.0e9) return false;   // 32-bit offsets per image
+  const long long tiles = (long long)((d.w + kTC - 1) / kTC) * ((d.h + kTR - 1) / kTR) * d.n;
+  if (tiles > (1LL << 31) - 1) return false;
+  p.kid = kMfmaNhwcF16;
+  p.name = "is_k4_mfma";
+  p.nseg = (d.w + kTC - 1) / kTC;
+  p.nstrip = (d.h + kTR - 1) / kTR;
+  p.ntiles = (int)tiles;
+  // Persistent: one workgroup per CU (its LDS and registers fill the CU),
+  // 8 XCDs x 32 CUs; fewer when there are fewer tiles (kept a multiple of 8).
+  int g = 256;
+  while (g > 8 && g / 2 >= p.ntiles) g /= 2;
+  p.grid_x = g;
+  p.grid_y = p.grid_z = 1;
+  p.block = kThreads;
+  p.lds = 2 * kBufChunks * 16;
+  p.tile_w = kTC;
+  p.tile_h = kTR;
+  p.vec = 256;   // swizzle row bytes
+  return true;
+}
+
+hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
+                       hipStream_t s) {
+  MfmaArgs a;
+  a.x = x;
+  a.w = w;
+  a.bias = b;
+  a.y = y;
+  a.N = p.d.n;
+  a.H = p.d.h;
+  a.W = p.d.w;
+  a.relu = p.d.relu;
+  a.tiles_x = p.nseg;
+  a.tiles_y = p.nstrip;
+  a.ntiles = p.ntiles;
+  switch (p.vec) {
+    case 0: return launch_kernel(is_k4_mfma<0>, dim3(p.grid_x), dim3(p.block), 0, s, a);
+    case 128: return launch_kernel(is_k4_mfma<128>, dim3(p.grid_x), dim3(p.block), 0, s, a);
+    default: return launch_kernel(is_k4_mfma<256>, dim3(p.grid_x), dim3(p.block), 0, s, a);
+  }
+}
+
+}  // namespace is

@@ -1,0 +1,84 @@
+"""GPU parity of the fp16 NHWC layer (MFMA implicit GEMM) against the oracle.
+
+fp16 inputs and weights, fp32 bias and accumulation, fp16 output rounded to
+nearest even: |y - y_ref| <= 2e-3 * m per element, m = sum |w*x| + |b|. The
+oracle consumes the same fp16 values, widened exactly. Shapes cover exact and
+ragged 8x32 tiles, single pixels, batches, and the full 8x256x256x64 layer on
+whole sampled rows.
+"""
+import numpy as np
+import pytest
+
+import image_stencil_amd as isa
+import oracle
+import synth
+from gpu_util import dev, host, say
+from tolerance import TAU_F16, check
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, w, b, relu, expect=None):
+    import torch
+    N, H, W, C = x.shape
+    K, _, R, S = w.shape
+    plan = isa.Plan(isa.make_desc(N, C, H, W, K, R, S, "f16", relu))
+    if expect:
+        assert plan.info()["kernel"] == expect
+    y = torch.full((N, H, W, K), float("nan"), dtype=torch.float16, device="cuda")
+    plan.forward(dev(x), dev(w), dev(b) if b is not None else None, y)
+    return host(y)
+
+
+@pytest.mark.parametrize("N,H,W", [(1, 8, 32), (2, 20, 40), (1, 1, 1), (1, 9, 33), (3, 17, 70), (1, 64, 64)])
+@pytest.mark.parametrize("relu", [False, True])
+def test_mfma_layer_shapes(N, H, W, relu):
+    x, w, b = synth.cnn_layer_f16_nhwc(N=N, H=H, W=W, seed=N * 100 + H + W)
+    say("mfma", N, H, W, relu)
+    y = _run(x, w, b, relu, "is_k4_mfma")
+    ref, m = oracle.conv2d(x, w, b, relu, "NHWC")
+    ratio = check(y, ref, m, TAU_F16, "mfma %dx%dx%d" % (N, H, W))
+    say("max err/bound %.3g" % ratio)
+
+
+def test_mfma_no_bias():
+    x, w, _ = synth.cnn_layer_f16_nhwc(N=1, H=16, W=40, seed=5)
+    y = _run(x, w, None, False, "is_k4_mfma")
+    ref, m = oracle.conv2d(x, w, None, False, "NHWC")
+    check(y, ref, m, TAU_F16, "mfma no bias")
+
+
+def test_mfma_delta_weights_exact():
+    """One-hot weights copy one shifted input channel: every product is exact and
+    the fp16 input survives the fp32 sum and the rounding back to fp16."""
+    x, _, _ = synth.cnn_layer_f16_nhwc(N=1, H=19, W=45, seed=6)
+    w = np.zeros((64, 64, 3, 3), np.float16)
+    rng = np.random.default_rng(7)
+    for k in range(64):
+        w[k, rng.integers(0, 64), rng.integers(0, 3), rng.integers(0, 3)] = 1.0
+    y = _run(x, w, None, False, "is_k4_mfma")
+    ref, _ = oracle.conv2d(x, w, None, False, "NHWC")
+    np.testing.assert_array_equal(y.astype(np.float64), ref)
+
+
+def test_f16_other_channel_counts_use_generic_kernel():
+    x, w, b = synth.cnn_layer_f16_nhwc(N=1, C=16, K=8, H=12, W=20, seed=8)
+    y = _run(x, w, b, True, "is_k0_generic_nhwc_f16")
+    ref, m = oracle.conv2d(x, w, b, True, "NHWC")
+    check(y, ref, m, TAU_F16, "generic f16")
+
+
+def test_mfma_layer_8x256x256_sampled():
+    """8 x 256 x 256 x 64 -> 64: rows on tile edges in every image, all columns
+    and channels."""
+    x, w, b = synth.cnn_layer_f16_nhwc()
+    say("mfma full layer")
+    y = _run(x, w, b, False, "is_k4_mfma")
+    assert np.isfinite(y.astype(np.float32)).all()
+    rows = [0, 7, 8, 127, 128, 248, 255]
+    pts = np.array([(n, k, i, j) for n in range(8) for i in rows[n % 3::3] + [rows[n % 7]]
+                    for j in range(256) for k in range(64)], np.int64)
+    ref, m = oracle.conv2d_points(x, w, b, False, pts, "NHWC")
+    got = y[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
+    ratio = check(got, ref, m, TAU_F16, "8x256x256 layer")
+    say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))
