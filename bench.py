@@ -210,6 +210,26 @@ def _roofline(c, ms):
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
 
 
+def _copy_reference(torch, stream_obj, mib=256, reps=5):
+    """A plain device-to-device copy of `mib` MiB (torch copy_): the achievable
+    streaming rate on this machine, and the known-size kernel that scales the
+    FETCH_SIZE / WRITE_SIZE counters of a profiling run."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream_obj)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(stream_obj)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"bytes_per_copy": 2 * n * 4, "ms": round(ms, 4), "gbs": round(2 * n * 4 / ms / 1e6, 1)}
+
+
 def _cpu_baseline(synth, oracle):
     """The oracle on one full headline step (3x3, 5x5 and 7x7 over 8192x8192)."""
     import numpy as np
@@ -281,6 +301,7 @@ def main():
         out["secondary"] = _secondary(torch, isa, synth, stream, stream_obj, args.steps, args.warmup)
         torch.cuda.empty_cache()
 
+    out["copy_reference"] = _copy_reference(torch, stream_obj)
     if not args.no_cpu_baseline:
         import oracle
         out["cpu_baseline"] = _cpu_baseline(synth, oracle)

@@ -1,7 +1,7 @@
 // internal.hpp -- plan structure and kernel launchers behind the C ABI.
 #pragma once
 
-#include "../../include/imgstencil.h"
+#include "imgstencil.h"
 
 namespace is {
 

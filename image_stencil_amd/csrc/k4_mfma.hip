@@ -7,10 +7,10 @@
 // convolution that "Optimizing Memory Efficiency for Convolution Kernels on
 // Kepler GPUs" contrasts with its direct method; here the wide-channel layer
 // really is that contraction, so it runs on MFMA). Design:
-//  * persistent workgroups of 4 waves, one per CU; each loops over 8 x 32 pixel
+//  * persistent workgroups of 4 waves, one per CU; each loops over 16 x 32 pixel
 //    tiles of an image, tiles of one XCD being neighbours so halo re-reads hit
 //    that XCD's L2;
-//  * the input tile with its 1-pixel halo (10 x 34 pixels x 128 bytes) streams
+//  * the input tile with its 1-pixel halo (18 x 34 pixels x 128 bytes) streams
 //    HBM -> LDS by buffer_load ... lds, double-buffered against the MFMAs;
 //    pixels outside the image read as 0 through the buffer range check;
 //  * LDS holds each pixel's 64 channels as eight 16-byte chunks, permuted by the
@@ -18,12 +18,13 @@
 //    elements and chunks) over rows of SWZ bytes, so that 16 lanes reading the
 //    same chunk of 16 consecutive pixels hit distinct banks;
 //  * wave w owns output channels 32*(w&1) .. +32 (two 16-row A blocks) for the
-//    tile rows 4*(w>>1) .. +4; its 36 weight fragments (all 576 k) stay in
+//    tile rows 8*(w>>1) .. +8; its 36 weight fragments (all 576 k) stay in
 //    registers for the whole kernel;
 //  * v_mfma_f32_16x16x32_f16: A = 16 output channels x 32 k (weights), B = 32 k
 //    x 16 pixels (one 16-byte LDS read per lane), D = 4 consecutive output
-//    channels of one pixel per lane, so the epilogue writes 8-byte fp16 vectors
-//    into the NHWC output after adding the fp32 bias and rounding to nearest even.
+//    channels of one pixel per lane; the epilogue adds the fp32 bias, rounds to
+//    fp16 (nearest even) and restages the tile through LDS so that the NHWC
+//    output leaves as whole 128-byte pixels.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -37,7 +38,7 @@ typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
 
 constexpr int kC = 64;                       // input channels
 constexpr int kK = 64;                       // output channels
-constexpr int kTR = 8, kTC = 32;             // output tile: rows x columns
+constexpr int kTR = 16, kTC = 32;            // output tile: rows x columns
 constexpr int kIR = kTR + 2, kIC = kTC + 2;  // input tile with halo
 constexpr int kChunks = kIR * kIC * 8;       // 16-byte chunks per input tile
 constexpr int kThreads = 256;
@@ -45,8 +46,15 @@ constexpr int kRounds = (kChunks + kThreads - 1) / kThreads;   // DMA rounds per
 constexpr int kBufChunks = kRounds * kThreads;                 // chunks per LDS buffer
 constexpr int kWVec = kK * 9 * 8;            // weight vectors [o][t][c/8] of 8 halves
 constexpr unsigned kOob = 0xFFFFFFF0u;
+constexpr int kPB = 16;                      // 16-pixel blocks per wave: 8 rows x 2 column blocks
+constexpr int kStores = kTR * kTC * 8 / kThreads;   // 16-byte output stores per thread per tile
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= kStores (bits 3:0 and 15:14),
+// expcnt and lgkmcnt not waited for (all ones).
+constexpr int kWaitDmaNotStores = (kStores & 0xF) | ((kStores >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+static_assert(kStores < 64, "vmcnt field");
 
-static_assert(kWVec <= 2 * kBufChunks, "weights are staged in the tile buffers");
+static_assert(kK * (kC * 9 * 2 + 16) <= 2 * kBufChunks * 16, "weights are staged in the tile buffers");
+static_assert(kTR * kTC * 8 <= kBufChunks, "the output tile is staged in one tile buffer");
 
 constexpr int kRowSlots = kIC * 8;           // 16-byte slots per input tile row
 
@@ -105,36 +113,41 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   const int n16 = lane & 15;     // pixel (B, D) or output channel (A) inside a 16-block
   const int g = lane >> 4;       // k group of 8 (A, B) or channel group of 4 (D)
   const int oh = wave & 1;       // output-channel half
-  const int mh = wave >> 1;      // tile-row half
+  const int mh = wave >> 1;      // tile-row half: rows 8*mh .. 8*mh+7
 
-  // ---- Weights: stage KCRS into LDS as [o][t][c/8] vectors of 8 channels,
-  // then every lane keeps its 36 A fragments (2 channel blocks x 18 k steps).
+  // ---- Weights: copy the KCRS tensor into LDS with 16-byte loads, each output
+  // channel's 576 halves on a row of 1168 bytes (16 bytes of padding spread
+  // the 16 channels a fragment read touches over distinct banks); then every
+  // lane gathers its 36 A fragments (2 channel blocks x 18 k steps): fragment
+  // (ob, ks) holds channels 32h + 8g .. +8 of tap t = ks/2 for output channel
+  // 32*oh + 16*ob + n16, i.e. 8 halves 9 apart in the channel's row.
+  constexpr int kWRow = kC * 9 * 2 + 16;   // bytes per padded weight row
   {
-    _Float16 *wl = reinterpret_cast<_Float16 *>(lds);
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(a.w), (short)0, kK * kC * 9 * 2, kBufferFlags);
-    // 8 consecutive KCRS halves per 16-byte load; element e = o*576 + c*9 + t.
-    for (int v = tid; v < kK * kC * 9 / 8; v += kThreads) {
-      const uint4v q = __builtin_amdgcn_raw_buffer_load_b128(rw, v * 16, 0, 0);
-      const _Float16 *h = reinterpret_cast<const _Float16 *>(&q);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int e = v * 8 + j;
-        const int o = e / 576, r = e % 576, c = r / 9, t = r % 9;
-        wl[(o * 9 + t) * 64 + c] = h[j];
-      }
+    constexpr int kVecRow = kC * 9 * 2 / 16;   // 72 vectors per output channel
+    for (int v = tid; v < kK * kVecRow; v += kThreads) {
+      const int o = v / kVecRow, r = v - o * kVecRow;
+      *reinterpret_cast<uint4v *>(reinterpret_cast<char *>(lds) + o * kWRow + r * 16) =
+          __builtin_amdgcn_raw_buffer_load_b128(rw, v * 16, 0, 0);
     }
   }
   __syncthreads();
   half8 wa[2][18];
+  {
+    const char *wl = reinterpret_cast<const char *>(lds);
 #pragma unroll
-  for (int ob = 0; ob < 2; ++ob)
+    for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const int o = 32 * oh + 16 * ob + n16;
-      const int t = ks >> 1, h = ks & 1;
-      wa[ob][ks] = __builtin_bit_cast(half8, lds[(o * 9 + t) * 8 + h * 4 + g]);
-    }
+      for (int ks = 0; ks < 18; ++ks) {
+        const int o = 32 * oh + 16 * ob + n16;
+        const int t = ks >> 1, h = ks & 1;
+        const _Float16 *src =
+            reinterpret_cast<const _Float16 *>(wl + o * kWRow) + (32 * h + 8 * g) * 9 + t;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wa[ob][ks][j] = src[9 * j];
+      }
+  }
   float bias[2][4];
 #pragma unroll
   for (int ob = 0; ob < 2; ++ob)
@@ -189,37 +202,54 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
-        boff[v][h][cb] = ((4 * mh) * kRowSlots + slot_in_row<SWZ>(16 * cb + n16 + v, 4 * h + g)) * 16;
+        boff[v][h][cb] = ((8 * mh) * kRowSlots + slot_in_row<SWZ>(16 * cb + n16 + v, 4 * h + g)) * 16;
 
   auto compute_store = [&](int tl, const uint4v *buf) {
-    float4v acc[8][2];
+    float4v acc[kPB][2];
 #pragma unroll
-    for (int pb = 0; pb < 8; ++pb)
+    for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
       for (int ob = 0; ob < 2; ++ob) acc[pb][ob] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
+    // One 16-byte LDS read per lane gives the B fragment of a 16-pixel block;
+    // it feeds the MFMAs of both output-channel blocks. The 18 x kPB (k step,
+    // pixel block) pairs run as one unrolled sequence whose B read is issued
+    // kAhead pairs early into a ring of registers; scheduling barriers between
+    // pairs keep the compiler from hoisting more reads than the ring holds.
+    constexpr int kSteps = 18 * kPB;
+    constexpr int kAhead = 8;
+    auto read_b = [&](int i) -> half8 {
+      const int ks = i / kPB, pb = i % kPB;
       const int t = ks >> 1, h = ks & 1;
       const int u = t / 3, v = t % 3;
+      const char *p = reinterpret_cast<const char *>(buf) + boff[v][h][pb & 1] +
+                      ((pb >> 1) + u) * kRowSlots * 16;
+      return *reinterpret_cast<const half8 *>(p);
+    };
+    half8 ring[kAhead];
 #pragma unroll
-      for (int pb = 0; pb < 8; ++pb) {
-        const char *p = reinterpret_cast<const char *>(buf) + boff[v][h][pb & 1] +
-                        ((pb >> 1) + u) * kRowSlots * 16;
-        const half8 b = *reinterpret_cast<const half8 *>(p);
+    for (int i = 0; i < kAhead; ++i) ring[i] = read_b(i);
 #pragma unroll
-        for (int ob = 0; ob < 2; ++ob)
-          acc[pb][ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[ob][ks], b, acc[pb][ob], 0, 0, 0);
-      }
+    for (int i = 0; i < kSteps; ++i) {
+      const half8 b = ring[i % kAhead];
+      if (i + kAhead < kSteps) ring[i % kAhead] = read_b(i + kAhead);
+      const int ks = i / kPB, pb = i % kPB;
+#pragma unroll
+      for (int ob = 0; ob < 2; ++ob)
+        acc[pb][ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[ob][ks], b, acc[pb][ob], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    int n, y0, x0;
-    tile_origin(tl, n, y0, x0);
-    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-        a.y + (size_t)n * img, (short)0, (int)(img * 2), kBufferFlags);
+
+    // Epilogue: bias, optional ReLU, fp16 round to nearest even; the 16 x 32 x 64
+    // output tile is staged in this tile's LDS buffer (no longer read) as NHWC
+    // pixels of eight 16-byte chunks, XOR-swizzled by bits 1..3 of the pixel
+    // index so that 16 lanes writing one chunk of 16 pixels hit distinct banks,
+    // then copied out as whole 128-byte pixels: 32 consecutive pixels of a tile
+    // row are 4 KB of contiguous NHWC output per instruction.
+    __syncthreads();
+    char *stage = reinterpret_cast<char *>(const_cast<uint4v *>(buf));
 #pragma unroll
-    for (int pb = 0; pb < 8; ++pb) {
-      const int gy = y0 + 4 * mh + (pb >> 1);
-      const int gx = x0 + 16 * (pb & 1) + n16;
-      const bool in = gy < a.H && gx < a.W;
+    for (int pb = 0; pb < kPB; ++pb) {
+      const int p = (8 * mh + (pb >> 1)) * kTC + 16 * (pb & 1) + n16;   // tile pixel
 #pragma unroll
       for (int ob = 0; ob < 2; ++ob) {
         _Float16 hv[4];
@@ -229,10 +259,25 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
           if (a.relu) o = fmaxf(o, 0.f);
           hv[i] = (_Float16)o;
         }
-        const int oc = 32 * oh + 16 * ob + 4 * g;
-        const unsigned off = in ? (unsigned)((((size_t)gy * a.W + gx) * kK + oc) * 2) : kOob;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, hv), ry, off, 0, 0);
+        const int chunk = 4 * oh + 2 * ob + (g >> 1);   // 16-byte chunk of channels
+        const int sw = chunk ^ ((p >> 1) & 7);
+        *reinterpret_cast<uint2v *>(stage + p * 128 + sw * 16 + (g & 1) * 8) = __builtin_bit_cast(uint2v, hv);
       }
+    }
+    __syncthreads();
+    int n, y0, x0;
+    tile_origin(tl, n, y0, x0);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        a.y + (size_t)n * img, (short)0, (int)(img * 2), kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < kStores; ++j) {
+      const int q = j * kThreads + tid;
+      const int p = q >> 3, chunk = q & 7;
+      const uint4v v = *reinterpret_cast<const uint4v *>(stage + p * 128 + ((chunk ^ ((p >> 1) & 7)) * 16));
+      const int gy = y0 + p / kTC, gx = x0 + p % kTC;
+      const unsigned off =
+          (gy < a.H && gx < a.W) ? (unsigned)((((size_t)gy * a.W + gx) * kK + chunk * 8) * 2) : kOob;
+      __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
     }
   };
 
@@ -244,7 +289,10 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     const int next = tile + step;
     if (next < hi) issue(next, lds + (cur ^ 1) * kBufChunks);
     compute_store(tile, lds + cur * kBufChunks);
-    __builtin_amdgcn_s_waitcnt(0);
+    // Wait for the next tile's DMA but not for this tile's output stores:
+    // vector-memory operations retire in issue order on gfx9, and the stores
+    // (kStores per thread) were issued after the DMA.
+    __builtin_amdgcn_s_waitcnt(kWaitDmaNotStores);
     __syncthreads();
     tile = next;
     cur ^= 1;
