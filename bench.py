@@ -33,6 +33,118 @@ FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12     # 78.64, plain v_fma
 FP32_PACKED_PEAK_TFLOPS = 157.3
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 
+# HBM traffic per launch from the FETCH_SIZE / WRITE_SIZE counters (two
+# rocprofv3 --pmc runs of this script, summarised by --pmc-summary into
+# TRAFFIC_FILE). Each figure is tied to a digest of the kernel's sources: once a
+# source changes, the case reports traffic null until the counters are re-taken.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+TRAFFIC_KERNELS = {   # bench case -> (kernel as the profiler names it, its source files)
+    "8192x8192 3x3": ("is_k1_single<3, 3, true, false>", ("k1_single.hip",)),
+    "8192x8192 5x5": ("is_k1_single<5, 5, true, false>", ("k1_single.hip",)),
+    "8192x8192 7x7": ("is_k1_single<7, 7, true, false>", ("k1_single.hip",)),
+    "fp32 layer 1x32x720x1280 -> 32, 3x3": ("is_k2_multi<3, 32, 4, true>", ("k2_multi.hip",)),
+    "fp16 NHWC layer 8x256x256x64 -> 64, 3x3": ("is_k4_mfma<256>", ("k4_mfma.hip",)),
+    "upscaling chain 1280x720 (fused)": ("is_k3_chain", ("k3_chain.hip",)),
+}
+# The known-size dispatch: torch's elementwise negation of 256 MiB of fp32
+# (run by _copy_reference), which reads 256 MiB and writes 256 MiB.
+CALIB_KERNEL = "neg_kernel"
+CALIB_BYTES = 256 << 20
+
+
+def _source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in tuple(files) + ("common.hpp",):
+        with open(os.path.join(ROOT, "image_stencil_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _short_kernel(name):
+    import re
+    name = name.replace("void ", "").replace("is::(anonymous namespace)::", "")
+    m = re.match(r"([^(<]+(<[^>]*>)?)", name)
+    return m.group(1).strip() if m else name
+
+
+def _counter_means(d, counter):
+    """Mean per dispatch of one counter, by kernel, over every counter CSV under d."""
+    import csv
+    import glob
+    per = {}   # (kernel, dispatch) -> summed value
+    full = {}
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = _short_kernel(r["Kernel_Name"])
+                full[k] = r["Kernel_Name"]
+                key = (k, f, r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    acc = {}
+    for (k, _, _), v in per.items():
+        acc.setdefault(k, []).append(v)
+    return {k: (sum(v) / len(v), len(v), full[k]) for k, v in acc.items()}
+
+
+def pmc_summary(fetch_dir, write_dir):
+    """Markdown summary of two counter runs: per-dispatch FETCH_SIZE and
+    WRITE_SIZE of each bench case's kernel, scaled by the known-size dispatch."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+
+    def calib(tab):
+        hits = [v for k, v in tab.items() if CALIB_KERNEL in v[2]]
+        if len(hits) != 1:
+            raise SystemExit("expected one calibration kernel (%s), found %d" % (CALIB_KERNEL, len(hits)))
+        return hits[0]
+
+    cf, cw = calib(fetch), calib(write)
+    sf = CALIB_BYTES / (cf[0] * 1024.0)
+    sw = CALIB_BYTES / (cw[0] * 1024.0)
+    lines = ["# HBM traffic per launch from the FETCH_SIZE and WRITE_SIZE counters", "",
+             "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o run -- \\" % fetch_dir,
+             "    python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o run -- \\" % write_dir,
+             "    python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "python3 bench.py --pmc-summary %s %s > profiles/hbm_traffic_counters.md" % (fetch_dir, write_dir),
+             "```", "",
+             "Counters are in KiB per dispatch, averaged over the dispatches of each kernel. The scale",
+             "factors make the known-size dispatch (torch's negation of 256 MiB of fp32: 256 MiB read,",
+             "256 MiB written) read its true size: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f." % (sf, sw), "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|---|",
+             "| `%s` (calibration) | %d | %.1f | %.1f |" % (_short_kernel(cf[2])[:60], cf[1], cf[0], cw[0]), "",
+             "Machine-read by bench.py (traffic = scaled fetch + scaled write bytes per launch; the digest",
+             "is that of the kernel's sources when the counters were taken):", "",
+             "| case | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic bytes | source digest |",
+             "|---|---|---|---|---|---|---|"]
+    for case, (kern, files) in TRAFFIC_KERNELS.items():
+        if kern not in fetch or kern not in write:
+            continue
+        f, n, _ = fetch[kern]
+        w_, _, _ = write[kern]
+        t = f * 1024.0 * sf + w_ * 1024.0 * sw
+        lines.append("| %s | `%s` | %d | %.1f | %.1f | %.0f | %s |" % (case, kern, n, f, w_, t, _source_digest(files)))
+    return "\n".join(lines) + "\n"
+
+
+def _traffic(case):
+    """Counter-derived HBM bytes per launch of a bench case, or None when absent
+    or taken with other kernel sources than the current ones."""
+    if case not in TRAFFIC_KERNELS or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            cols = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cols) == 7 and cols[0] == case:
+                if cols[6] != _source_digest(TRAFFIC_KERNELS[case][1]):
+                    return None
+                return float(cols[5])
+    return None
+
 
 class Case:
     """One kernel launch of a workload: callable, counted work, kernel name."""
@@ -126,7 +238,8 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup):
                              "gbs": round(c.bytes / ms / 1e6, 1),
                              "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                                           "unit": "TFLOP/s", "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4),
-                                          "hbm_frac": round(c.bytes / ms / 1e6 / HBM_PEAK_GBS, 4)}}
+                                          "hbm_frac": round(c.bytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                          "traffic": _traffic(c.name)}}
     for c in mcases:
         c.keep = None
     del plan
@@ -161,7 +274,8 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup):
             "workload": ccases[0].name + ": 5x5 1->32, 3x3 32->32 x2, 3x3 32->4, depth-to-space x2",
             "kernel": kname, "ms_per_frame": round(ms, 4), "gflops": round(flops / ms / 1e6, 1),
             "frac_fp32_valu": round(flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
-            "frac_fp32_packed_peak": round(flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4)}
+            "frac_fp32_packed_peak": round(flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
+            "roofline": _roofline(ccases[0], ms)}
         for c in ccases:
             c.keep = None
         del ws
@@ -203,31 +317,36 @@ def _roofline(c, ms):
     if ai > ridge:
         ach = c.flops / sec / 1e12
         return {"bound": "alu", "achieved": round(ach, 3), "peak": round(FP32_VALU_PEAK_TFLOPS, 2),
-                "unit": "TFLOP/s", "frac": round(ach / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / FP32_VALU_PEAK_TFLOPS, 4), "traffic": _traffic(c.name),
                 "peak_packed_fp32": FP32_PACKED_PEAK_TFLOPS}
     ach = c.bytes / sec / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": _traffic(c.name)}
 
 
 def _copy_reference(torch, stream_obj, mib=256, reps=5):
-    """A plain device-to-device copy of `mib` MiB (torch copy_): the achievable
-    streaming rate on this machine, and the known-size kernel that scales the
-    FETCH_SIZE / WRITE_SIZE counters of a profiling run."""
+    """Two plain streaming references over `mib` MiB: a device-to-device copy
+    (torch copy_, the runtime's copy kernel) and torch's elementwise negation
+    (reads and writes each fp32 element once). The second has a kernel name of
+    its own, which makes it the known-size dispatch that scales the FETCH_SIZE /
+    WRITE_SIZE counters of a profiling run of this script."""
     n = mib * (1 << 20) // 4
     a = torch.ones(n, device="cuda")
     b = torch.empty_like(a)
-    for _ in range(2):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream_obj)
-    for _ in range(reps):
-        b.copy_(a)
-    e1.record(stream_obj)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    return {"bytes_per_copy": 2 * n * 4, "ms": round(ms, 4), "gbs": round(2 * n * 4 / ms / 1e6, 1)}
+    out = {"bytes_per_launch": 2 * n * 4}
+    for name, fn in (("copy", lambda: b.copy_(a)), ("neg_kernel", lambda: torch.neg(a, out=b))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream_obj)
+        for _ in range(reps):
+            fn()
+        e1.record(stream_obj)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "gbs": round(2 * n * 4 / ms / 1e6, 1)}
+    return out
 
 
 def _cpu_baseline(synth, oracle):
@@ -256,7 +375,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
+                         "of this script and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        sys.stdout.write(pmc_summary(*args.pmc_summary))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
