@@ -107,9 +107,9 @@ def pmc_summary(fetch_dir, write_dir):
     lines = ["# HBM traffic per launch from the FETCH_SIZE and WRITE_SIZE counters", "",
              "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
              "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o run -- \\" % fetch_dir,
-             "    python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "    python3 bench.py --steps 2 --warmup 1 --min-warm-s 0 --no-cpu-baseline",
              "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o run -- \\" % write_dir,
-             "    python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "    python3 bench.py --steps 2 --warmup 1 --min-warm-s 0 --no-cpu-baseline",
              "python3 bench.py --pmc-summary %s %s > profiles/hbm_traffic_counters.md" % (fetch_dir, write_dir),
              "```", "",
              "Counters are in KiB per dispatch, averaged over the dispatches of each kernel. The scale",
@@ -282,12 +282,22 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup):
     return out
 
 
+MIN_WARM_S = 0.3
+
+
 def _time_cases(torch, cases, steps, warmup, stream_obj):
     """Warmup, then `steps` steps of all cases with an event pair around every
-    launch, all on the stream the library launches on."""
-    for _ in range(warmup):
+    launch, all on the stream the library launches on. The warmup runs at least
+    `warmup` steps and at least MIN_WARM_S seconds: the ALU-bound launches
+    measured up to 25% slower while the clock was still ramping after a short
+    warmup."""
+    t0w, n = time.perf_counter(), 0
+    while n < warmup or time.perf_counter() - t0w < MIN_WARM_S:
         for c in cases:
             c.launch()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cases]
           for _ in range(steps)]
@@ -349,23 +359,27 @@ def _copy_reference(torch, stream_obj, mib=256, reps=5):
     return out
 
 
-def _cpu_baseline(synth, oracle):
-    """The oracle on one full headline step (3x3, 5x5 and 7x7 over 8192x8192)."""
+def _cpu_baseline(synth, oracle, min_s=10.0):
+    """The oracle on full headline steps (3x3, 5x5 and 7x7 over 8192x8192),
+    repeated until at least `min_s` seconds of oracle compute have run."""
     import numpy as np
-    total_bytes, secs = 0.0, 0.0
+    data = []
     for R in (3, 5, 7):
         x, w = synth.large_image(R)
-        xd = x.astype(np.float64)
-        wd = w.astype(np.float64)
-        t = time.perf_counter()
-        oracle.conv2d(xd, wd)
-        secs += time.perf_counter() - t
-        total_bytes += 4.0 * (2 * 8192 * 8192 + R * R)
-        del xd
+        data.append((R, x.astype(np.float64), w.astype(np.float64)))
+        del x
+    total_bytes, secs, reps = 0.0, 0.0, 0
+    while reps == 0 or secs < min_s:
+        for R, xd, wd in data:
+            t = time.perf_counter()
+            oracle.conv2d(xd, wd)
+            secs += time.perf_counter() - t
+            total_bytes += 4.0 * (2 * 8192 * 8192 + R * R)
+        reps += 1
     return {"value": round(total_bytes / secs / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
-            "kind": "oracle", "seconds": round(secs, 2),
-            "sample": "one full step: 8192x8192 fp32 image with 3x3, 5x5 and 7x7 filters, fp64 oracle "
-                      "with error scale (compute only, input widening not timed)"}
+            "kind": "oracle", "seconds": round(secs, 2), "steps": reps,
+            "sample": "%d full steps: 8192x8192 fp32 image with 3x3, 5x5 and 7x7 filters, fp64 oracle "
+                      "with error scale (compute only; input widening not timed)" % reps}
 
 
 def main():
@@ -373,12 +387,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--min-warm-s", type=float, default=0.3,
+                    help="least warmup time per timed group, seconds (default %(default)s)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script and exit (no GPU needed)")
     args = ap.parse_args()
+    globals()["MIN_WARM_S"] = args.min_warm_s
     if args.pmc_summary:
         sys.stdout.write(pmc_summary(*args.pmc_summary))
         return
