@@ -131,6 +131,33 @@ def pmc_summary(fetch_dir, write_dir):
     return "\n".join(lines) + "\n"
 
 
+def stats_summary(trace_dir):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of this script:
+    calls and durations per kernel, with the bench case each kernel times."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True))
+    if not files:
+        raise SystemExit("no kernel_stats.csv under %s" % trace_dir)
+    cases = {k: c for c, (k, _) in TRAFFIC_KERNELS.items()}
+    lines = ["# Kernel durations of the bench workloads (rocprofv3 kernel trace)", "",
+             "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d %s -o run -- \\" % trace_dir,
+             "    python3 bench.py --no-cpu-baseline",
+             "python3 bench.py --stats-summary %s > profiles/kernel_durations_bench_workloads.md" % trace_dir,
+             "```", "",
+             "Durations in microseconds over every dispatch of the run (warmup included). The bench's",
+             "own per-launch event timings of the same run are printed in its JSON line.", "",
+             "| kernel | bench case | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            k = _short_kernel(r["Name"])
+            lines.append("| `%s` | %s | %s | %.1f | %.1f | %.1f |" % (
+                k[:70], cases.get(k, ""), r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    return "\n".join(lines) + "\n"
+
+
 def _traffic(case):
     """Counter-derived HBM bytes per launch of a bench case, or None when absent
     or taken with other kernel sources than the current ones."""
@@ -394,10 +421,16 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script and exit (no GPU needed)")
+    ap.add_argument("--stats-summary", metavar="TRACE_DIR",
+                    help="print the kernel-duration summary of a rocprofv3 --kernel-trace --stats run of "
+                         "this script and exit (no GPU needed)")
     args = ap.parse_args()
     globals()["MIN_WARM_S"] = args.min_warm_s
     if args.pmc_summary:
         sys.stdout.write(pmc_summary(*args.pmc_summary))
+        return
+    if args.stats_summary:
+        sys.stdout.write(stats_summary(args.stats_summary))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
