@@ -18,13 +18,19 @@
 //    elements and chunks) over rows of SWZ bytes, so that 16 lanes reading the
 //    same chunk of 16 consecutive pixels hit distinct banks;
 //  * wave w owns output channels 32*(w&1) .. +32 (two 16-row A blocks) for the
-//    tile rows 8*(w>>1) .. +8; its 36 weight fragments (all 576 k) stay in
-//    registers for the whole kernel;
+//    16 columns 16*(w>>1) .. +16 of all 16 tile rows; its 36 weight fragments
+//    (all 576 k) stay in registers for the whole kernel;
 //  * v_mfma_f32_16x16x32_f16: A = 16 output channels x 32 k (weights), B = 32 k
 //    x 16 pixels (one 16-byte LDS read per lane), D = 4 consecutive output
-//    channels of one pixel per lane; the epilogue adds the fp32 bias, rounds to
-//    fp16 (nearest even) and restages the tile through LDS so that the NHWC
-//    output leaves as whole 128-byte pixels.
+//    channels of one pixel per lane;
+//  * rolling rows, as in the single-channel kernel: the B fragment of input
+//    row i (tap column v, channel half h) is read once and feeds the output rows
+//    i, i-1 and i-2 through filter rows 0, 1 and 2, so a wave reads 18 x 6
+//    fragments per tile instead of 16 x 18 (LDS read bandwidth, not the matrix
+//    cores, bounded the one-read-per-tap order);
+//  * the epilogue adds the fp32 bias, rounds to fp16 (nearest even) and
+//    restages the tile through LDS so that the NHWC output leaves as whole
+//    128-byte pixels.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -46,7 +52,7 @@ constexpr int kRounds = (kChunks + kThreads - 1) / kThreads;   // DMA rounds per
 constexpr int kBufChunks = kRounds * kThreads;                 // chunks per LDS buffer
 constexpr int kWVec = kK * 9 * 8;            // weight vectors [o][t][c/8] of 8 halves
 constexpr unsigned kOob = 0xFFFFFFF0u;
-constexpr int kPB = 16;                      // 16-pixel blocks per wave: 8 rows x 2 column blocks
+constexpr int kPB = kTR;                     // 16-pixel blocks per wave: one per tile row
 constexpr int kStores = kTR * kTC * 8 / kThreads;   // 16-byte output stores per thread per tile
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= kStores (bits 3:0 and 15:14),
 // expcnt and lgkmcnt not waited for (all ones).
@@ -113,7 +119,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   const int n16 = lane & 15;     // pixel (B, D) or output channel (A) inside a 16-block
   const int g = lane >> 4;       // k group of 8 (A, B) or channel group of 4 (D)
   const int oh = wave & 1;       // output-channel half
-  const int mh = wave >> 1;      // tile-row half: rows 8*mh .. 8*mh+7
+  const int ch = wave >> 1;      // tile-column half: columns 16*ch .. 16*ch+15
 
   // ---- Weights: copy the KCRS tensor into LDS with 16-byte loads, each output
   // channel's 576 halves on a row of 1168 bytes (16 bytes of padding spread
@@ -126,10 +132,19 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(a.w), (short)0, kK * kC * 9 * 2, kBufferFlags);
     constexpr int kVecRow = kC * 9 * 2 / 16;   // 72 vectors per output channel
-    for (int v = tid; v < kK * kVecRow; v += kThreads) {
+    constexpr int kVecPerThread = kK * kVecRow / kThreads;
+    static_assert(kVecPerThread * kThreads == kK * kVecRow, "whole vectors per thread");
+    // All loads first, then the LDS writes: a load-write loop would wait for
+    // each load in turn, 18 round trips to L2 before the first tile.
+    uint4v t[kVecPerThread];
+#pragma unroll
+    for (int j = 0; j < kVecPerThread; ++j)
+      t[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, (j * kThreads + tid) * 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kVecPerThread; ++j) {
+      const int v = j * kThreads + tid;
       const int o = v / kVecRow, r = v - o * kVecRow;
-      *reinterpret_cast<uint4v *>(reinterpret_cast<char *>(lds) + o * kWRow + r * 16) =
-          __builtin_amdgcn_raw_buffer_load_b128(rw, v * 16, 0, 0);
+      *reinterpret_cast<uint4v *>(reinterpret_cast<char *>(lds) + o * kWRow + r * 16) = t[j];
     }
   }
   __syncthreads();
@@ -193,16 +208,12 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   };
 
   // Byte offsets (inside a tile buffer) of this lane's B reads for filter column
-  // v, channel half h and 16-pixel column block cb, at tile row 4*mh; the row
-  // (pb/2 + u) adds a constant multiple of a tile row.
-  int boff[3][2][2];
+  // v and channel half h at input-tile row 0; row i adds i tile rows.
+  int boff[3][2];
 #pragma unroll
   for (int v = 0; v < 3; ++v)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        boff[v][h][cb] = ((8 * mh) * kRowSlots + slot_in_row<SWZ>(16 * cb + n16 + v, 4 * h + g)) * 16;
+    for (int h = 0; h < 2; ++h) boff[v][h] = slot_in_row<SWZ>(16 * ch + n16 + v, 4 * h + g) * 16;
 
   auto compute_store = [&](int tl, const uint4v *buf) {
     float4v acc[kPB][2];
@@ -210,32 +221,37 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
       for (int ob = 0; ob < 2; ++ob) acc[pb][ob] = float4v{0.f, 0.f, 0.f, 0.f};
-    // One 16-byte LDS read per lane gives the B fragment of a 16-pixel block;
-    // it feeds the MFMAs of both output-channel blocks. The 18 x kPB (k step,
-    // pixel block) pairs run as one unrolled sequence whose B read is issued
-    // kAhead pairs early into a ring of registers; scheduling barriers between
-    // pairs keep the compiler from hoisting more reads than the ring holds.
-    constexpr int kSteps = 18 * kPB;
+    // Reads go in (input row i, tap column v, channel half h) order; read i
+    // feeds output rows i - u, u = 0..2 (those inside the tile), with the A
+    // fragment of k step 2(3u + v) + h, for both output-channel blocks. Each read
+    // is issued kAhead reads early into a ring of registers; scheduling
+    // barriers between reads keep the compiler from hoisting more reads than
+    // the ring holds.
+    constexpr int kReads = kIR * 6;
     constexpr int kAhead = 8;
-    auto read_b = [&](int i) -> half8 {
-      const int ks = i / kPB, pb = i % kPB;
-      const int t = ks >> 1, h = ks & 1;
-      const int u = t / 3, v = t % 3;
-      const char *p = reinterpret_cast<const char *>(buf) + boff[v][h][pb & 1] +
-                      ((pb >> 1) + u) * kRowSlots * 16;
+    auto read_b = [&](int q) -> half8 {
+      const int i = q / 6, v = (q % 6) >> 1, h = q & 1;
+      const char *p = reinterpret_cast<const char *>(buf) + boff[v][h] + i * kRowSlots * 16;
       return *reinterpret_cast<const half8 *>(p);
     };
     half8 ring[kAhead];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) ring[i] = read_b(i);
+    for (int q = 0; q < kAhead; ++q) ring[q] = read_b(q);
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-      const half8 b = ring[i % kAhead];
-      if (i + kAhead < kSteps) ring[i % kAhead] = read_b(i + kAhead);
-      const int ks = i / kPB, pb = i % kPB;
+    for (int q = 0; q < kReads; ++q) {
+      const half8 b = ring[q % kAhead];
+      if (q + kAhead < kReads) ring[q % kAhead] = read_b(q + kAhead);
+      const int i = q / 6, v = (q % 6) >> 1, h = q & 1;
 #pragma unroll
-      for (int ob = 0; ob < 2; ++ob)
-        acc[pb][ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[ob][ks], b, acc[pb][ob], 0, 0, 0);
+      for (int u = 0; u < 3; ++u) {
+        const int o = i - u;
+        if (o >= 0 && o < kTR) {
+          const int ks = 2 * (3 * u + v) + h;
+#pragma unroll
+          for (int ob = 0; ob < 2; ++ob)
+            acc[o][ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[ob][ks], b, acc[o][ob], 0, 0, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -249,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     char *stage = reinterpret_cast<char *>(const_cast<uint4v *>(buf));
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb) {
-      const int p = (8 * mh + (pb >> 1)) * kTC + 16 * (pb & 1) + n16;   // tile pixel
+      const int p = pb * kTC + 16 * ch + n16;   // tile pixel
 #pragma unroll
       for (int ob = 0; ob < 2; ++ob) {
         _Float16 hv[4];
@@ -323,7 +339,7 @@ bool configure_mfma(Plan &p) {
   p.lds = 2 * kBufChunks * 16;
   p.tile_w = kTC;
   p.tile_h = kTR;
-  p.vec = 256;   // swizzle row bytes
+  p.vec = 128;   // swizzle row bytes (fewest SQ_LDS_BANK_CONFLICT cycles of 0, 128, 256)
   return true;
 }
 
