@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace is {
 
 constexpr int kWave = 64;   // CDNA wavefront width
@@ -58,6 +60,19 @@ __host__ __device__ constexpr int swizzle_col(int y, int x, int nx, int eb, int 
 // Launch and report this launch's error. hipGetLastError() is per-thread state
 // that earlier calls of the host program (not ours) may have left set; it is
 // cleared first so that only a failure of this launch is returned.
+// Calls f(std::integral_constant<int, 0>{}), ..., f(<N-1>) in order: a loop
+// whose index is a compile-time constant in every step, for bodies too large
+// for the unroller's size limit (a partially unrolled loop would index
+// register arrays dynamically).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <typename... KArgs, typename... Args>
 hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned lds, hipStream_t s,
                          Args &&...args) {

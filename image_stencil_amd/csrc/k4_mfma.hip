@@ -28,9 +28,10 @@
 //    i, i-1 and i-2 through filter rows 0, 1 and 2, so a wave reads 18 x 6
 //    fragments per tile instead of 16 x 18 (LDS read bandwidth, not the matrix
 //    cores, bounded the one-read-per-tap order);
-//  * the epilogue adds the fp32 bias, rounds to fp16 (nearest even) and
-//    restages the tile through LDS so that the NHWC output leaves as whole
-//    128-byte pixels.
+//  * an output row is final once input row +2 has been read: it gets the fp32
+//    bias, the optional ReLU and fp16 rounding (nearest even) and is stored
+//    from the accumulators inside the MFMA loop, so stores overlap the matrix
+//    work and the tile needs no epilogue phase.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -53,14 +54,13 @@ constexpr int kBufChunks = kRounds * kThreads;                 // chunks per LDS
 constexpr int kWVec = kK * 9 * 8;            // weight vectors [o][t][c/8] of 8 halves
 constexpr unsigned kOob = 0xFFFFFFF0u;
 constexpr int kPB = kTR;                     // 16-pixel blocks per wave: one per tile row
-constexpr int kStores = kTR * kTC * 8 / kThreads;   // 16-byte output stores per thread per tile
+constexpr int kStores = kTR * 2;             // 8-byte output stores per thread per tile
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= kStores (bits 3:0 and 15:14),
 // expcnt and lgkmcnt not waited for (all ones).
 constexpr int kWaitDmaNotStores = (kStores & 0xF) | ((kStores >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 static_assert(kStores < 64, "vmcnt field");
 
 static_assert(kK * (kC * 9 * 2 + 16) <= 2 * kBufChunks * 16, "weights are staged in the tile buffers");
-static_assert(kTR * kTC * 8 <= kBufChunks, "the output tile is staged in one tile buffer");
 
 constexpr int kRowSlots = kIC * 8;           // 16-byte slots per input tile row
 
@@ -216,6 +216,17 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     for (int h = 0; h < 2; ++h) boff[v][h] = slot_in_row<SWZ>(16 * ch + n16 + v, 4 * h + g) * 16;
 
   auto compute_store = [&](int tl, const uint4v *buf) {
+    int n, y0, x0;
+    tile_origin(tl, n, y0, x0);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        a.y + (size_t)n * img, (short)0, (int)(img * 2), kBufferFlags);
+    // Byte offset of this lane's 4 output channels in its output column (32-bit
+    // offsets: the plan keeps an image under 4 GB), or an out-of-range offset
+    // when the column is outside the image; row gy adds gy * W * 128 bytes.
+    const int gx = x0 + 16 * ch + n16;
+    const bool col_in = gx < a.W;
+    const unsigned col_off = (unsigned)(gx * kK + 32 * oh + 4 * g) * 2u;
+    const unsigned row_bytes = (unsigned)a.W * kK * 2u;
     float4v acc[kPB][2];
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb)
@@ -237,11 +248,11 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     half8 ring[kAhead];
 #pragma unroll
     for (int q = 0; q < kAhead; ++q) ring[q] = read_b(q);
-#pragma unroll
-    for (int q = 0; q < kReads; ++q) {
+    static_for<kReads>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
       const half8 b = ring[q % kAhead];
-      if (q + kAhead < kReads) ring[q % kAhead] = read_b(q + kAhead);
-      const int i = q / 6, v = (q % 6) >> 1, h = q & 1;
+      if constexpr (q + kAhead < kReads) ring[q % kAhead] = read_b(q + kAhead);
+      constexpr int i = q / 6, v = (q % 6) >> 1, h = q & 1;
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
         const int o = i - u;
@@ -252,49 +263,31 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
             acc[o][ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[ob][ks], b, acc[o][ob], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // Epilogue: bias, optional ReLU, fp16 round to nearest even; the 16 x 32 x 64
-    // output tile is staged in this tile's LDS buffer (no longer read) as NHWC
-    // pixels of eight 16-byte chunks, XOR-swizzled by bits 1..3 of the pixel
-    // index so that 16 lanes writing one chunk of 16 pixels hit distinct banks,
-    // then copied out as whole 128-byte pixels: 32 consecutive pixels of a tile
-    // row are 4 KB of contiguous NHWC output per instruction.
-    __syncthreads();
-    char *stage = reinterpret_cast<char *>(const_cast<uint4v *>(buf));
+      // The last read of input row i completes output row i - 2: add the bias,
+      // apply the ReLU, round to fp16 (nearest even) and store it straight from
+      // the accumulators, so that the output leaves while the matrix cores keep
+      // working. Each lane writes 4 channels (8 bytes) of one pixel; the four
+      // lanes of a pixel and the other waves fill its 128-byte line in L2 before
+      // it is written back.
+      if constexpr (v == 2 && h == 1 && i >= 2) {
+        constexpr int o = i - 2;
+        const int gy = y0 + o;
 #pragma unroll
-    for (int pb = 0; pb < kPB; ++pb) {
-      const int p = pb * kTC + 16 * ch + n16;   // tile pixel
+        for (int ob = 0; ob < 2; ++ob) {
+          _Float16 hv[4];
 #pragma unroll
-      for (int ob = 0; ob < 2; ++ob) {
-        _Float16 hv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float o = acc[pb][ob][i] + bias[ob][i];
-          if (a.relu) o = fmaxf(o, 0.f);
-          hv[i] = (_Float16)o;
+          for (int e = 0; e < 4; ++e) {
+            float r = acc[o][ob][e] + bias[ob][e];
+            if (a.relu) r = fmaxf(r, 0.f);
+            hv[e] = (_Float16)r;
+          }
+          const unsigned off =
+              (gy < a.H && col_in) ? (unsigned)gy * row_bytes + col_off + 32u * ob : kOob;
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, hv), ry, off, 0, 0);
         }
-        const int chunk = 4 * oh + 2 * ob + (g >> 1);   // 16-byte chunk of channels
-        const int sw = chunk ^ ((p >> 1) & 7);
-        *reinterpret_cast<uint2v *>(stage + p * 128 + sw * 16 + (g & 1) * 8) = __builtin_bit_cast(uint2v, hv);
       }
-    }
-    __syncthreads();
-    int n, y0, x0;
-    tile_origin(tl, n, y0, x0);
-    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-        a.y + (size_t)n * img, (short)0, (int)(img * 2), kBufferFlags);
-#pragma unroll
-    for (int j = 0; j < kStores; ++j) {
-      const int q = j * kThreads + tid;
-      const int p = q >> 3, chunk = q & 7;
-      const uint4v v = *reinterpret_cast<const uint4v *>(stage + p * 128 + ((chunk ^ ((p >> 1) & 7)) * 16));
-      const int gy = y0 + p / kTC, gx = x0 + p % kTC;
-      const unsigned off =
-          (gy < a.H && gx < a.W) ? (unsigned)((((size_t)gy * a.W + gx) * kK + chunk * 8) * 2) : kOob;
-      __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   if (tile < hi) issue(tile, lds);
