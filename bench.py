@@ -8,15 +8,16 @@ one's data in cache). `value` is the step's algorithmic HBM bytes (x, y and w
 once per launch) over its time, in GB/s.
 
 Also reported, each timed on its own: the fp32 32->32 3x3 layer at 1280x720,
-the fused 1280x720 upscaling chain (ms per frame) and the fp16 NHWC 64->64
-layer of 8x256x256, with GFLOP/s and fractions of peak.
+the 1280x720 upscaling chain fused and layer by layer (ms per frame) and the
+fp16 NHWC 64->64 layer of 8x256x256, with GFLOP/s and fractions of peak.
 
 Peaks: HBM 8.0 TB/s; fp32 FMA on the vector ALUs without packed-FP32
 instructions 78.6 TFLOP/s (256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz; the
 kernels are built with packed FP32 off, which halves the 157.3 TFLOP/s figure
-that counts packed FMAs); dense fp16 MFMA 2.5 PFLOP/s.
+that counts packed FMAs); dense fp32 MFMA 157.3 TFLOP/s (the 32->32 fp32
+layers run there); dense fp16 MFMA 2.5 PFLOP/s.
 
-cpu_baseline: the fp64 CPU oracle on the host cores, one full headline step.
+cpu_baseline: the fp64 CPU oracle on the host cores, full headline steps.
 """
 import argparse
 import json
@@ -31,6 +32,8 @@ METRIC = "conv GFLOP/s and HBM GB/s as % of MI355X peak; ms per 1280x720 frame"
 HBM_PEAK_GBS = 8000.0
 FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12     # 78.64, plain v_fma_f32
 FP32_PACKED_PEAK_TFLOPS = 157.3
+FP32_MFMA_PEAK_TFLOPS = 157.3    # dense fp32 matrix cores (v_mfma_f32_16x16x4_f32)
+MFMA_F32_KERNELS = ("is_k5_mfma_f32",)
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 
 # HBM traffic per launch from the FETCH_SIZE / WRITE_SIZE counters (two
@@ -42,7 +45,7 @@ TRAFFIC_KERNELS = {   # bench case -> (kernel as the profiler names it, its sour
     "8192x8192 3x3": ("is_k1_single<3, 3, true, false>", ("k1_single.hip",)),
     "8192x8192 5x5": ("is_k1_single<5, 5, true, false>", ("k1_single.hip",)),
     "8192x8192 7x7": ("is_k1_single<7, 7, true, false>", ("k1_single.hip",)),
-    "fp32 layer 1x32x720x1280 -> 32, 3x3": ("is_k2_multi<3, 32, 4, true>", ("k2_multi.hip",)),
+    "fp32 layer 1x32x720x1280 -> 32, 3x3": ("is_k5_mfma_f32", ("k5_mfma_f32.hip",)),
     "fp16 NHWC layer 8x256x256x64 -> 64, 3x3": ("is_k4_mfma<256>", ("k4_mfma.hip",)),
     "upscaling chain 1280x720 (fused)": ("is_k3_chain", ("k3_chain.hip",)),
 }
@@ -302,7 +305,9 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup):
             "kernel": kname, "ms_per_frame": round(ms, 4), "gflops": round(flops / ms / 1e6, 1),
             "frac_fp32_valu": round(flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
             "frac_fp32_packed_peak": round(flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
-            "roofline": _roofline(ccases[0], ms)}
+            # layer by layer, the two 32 -> 32 layers (90% of the FLOPs) run on
+            # the fp32 matrix cores; the fused kernel is all vector ALU
+            "roofline": _roofline(ccases[0], ms, mfma_f32=(mode_name == "unfused"))}
         for c in ccases:
             c.keep = None
         del ws
@@ -346,10 +351,15 @@ def _time_cases(torch, cases, steps, warmup, stream_obj):
     return total_ms / steps, per, wall
 
 
-def _roofline(c, ms):
-    """Roofline entry of one launch: bound by HBM or by the fp32 ALUs."""
+def _roofline(c, ms, mfma_f32=False):
+    """Roofline entry of one launch: bound by HBM, by the fp32 vector ALUs, or
+    (mfma_f32: the dominant work runs on the fp32 matrix cores) by those."""
     sec = ms / 1e3
     ai = c.flops / c.bytes
+    if mfma_f32 or c.kernel in MFMA_F32_KERNELS:
+        ach = c.flops / sec / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 3), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": _traffic(c.name), "dtype": "f32"}
     ridge = FP32_VALU_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if ai > ridge:
         ach = c.flops / sec / 1e12

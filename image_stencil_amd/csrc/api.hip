@@ -80,7 +80,8 @@ is_status make_plan(const conv2d_desc *d, is::Plan &p) {
   if (st != IS_OK) return st;
   memset(&p, 0, sizeof(p));
   p.d = *d;
-  if (!is::configure_single(p) && !is::configure_multi(p) && !is::configure_mfma(p))
+  if (!is::configure_single(p) && !is::configure_mfma_f32(p) && !is::configure_multi(p) &&
+      !is::configure_mfma(p))
     is::configure_generic(p);
   if (log_enabled())
     fprintf(stderr, "[imgstencil] n=%d c=%d h=%d w=%d k=%d r=%d s=%d -> %s grid=%d block=%d lds=%d\n",
@@ -108,6 +109,10 @@ is_status run_plan(const is::Plan &p, const void *x, const void *w, const float 
     case is::kMultiChannel:
       e = is::launch_multi(p, static_cast<const float *>(x), static_cast<const float *>(w), bias,
                            static_cast<float *>(y), stream);
+      break;
+    case is::kMfmaNchwF32:
+      e = is::launch_mfma_f32(p, static_cast<const float *>(x), static_cast<const float *>(w), bias,
+                              static_cast<float *>(y), stream);
       break;
     case is::kMfmaNhwcF16:
       e = is::launch_mfma(p, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(w), bias,

@@ -10,7 +10,8 @@ enum KernelId {
   kGenericNhwcF16 = 1,   // one thread per output, any shape (fallback)
   kSingleChannel = 2,    // C = K = 1, fp32 NCHW, r, s <= 7
   kMultiChannel = 3,     // fp32 NCHW register-blocked, C, K multiples of the block
-  kMfmaNhwcF16 = 4       // fp16 NHWC implicit GEMM on MFMA
+  kMfmaNhwcF16 = 4,      // fp16 NHWC implicit GEMM on MFMA
+  kMfmaNchwF32 = 5       // fp32 NCHW 32 -> 32 3x3 implicit GEMM on the fp32 MFMA
 };
 
 struct Plan {
@@ -44,6 +45,10 @@ hipError_t launch_multi(const Plan &p, const float *x, const float *w, const flo
 bool configure_mfma(Plan &p);
 hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
                        hipStream_t s);
+
+bool configure_mfma_f32(Plan &p);
+hipError_t launch_mfma_f32(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                           hipStream_t s);
 
 // The fused upscaling chain (1->32 5x5, 32->32 3x3 twice, 32->4 3x3, depth-to-space x2).
 bool chain_fused_supported(const conv_chain_desc *d);

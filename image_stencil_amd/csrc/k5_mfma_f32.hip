@@ -1,0 +1,249 @@
+// k5_mfma_f32.hip -- fp32 NCHW 3x3 layer with 32 input and 32 output channels
+// as an implicit GEMM on the gfx950 fp32 matrix cores, with bias and ReLU.
+//
+// The layer y[o][p] = b[o] + sum_k W[o][k] X[k][p] over k = (tap t = 3u + v,
+// channel c) is a dense contraction of length 9 * 32 = 288 (the "blocked GEMM"
+// view of a convolution that "Optimizing Memory Efficiency for Convolution
+// Kernels on Kepler GPUs" sets against its direct method). At 32 channels the
+// direct fp32 kernel is bound by the vector ALUs; v_mfma_f32_16x16x4_f32 does
+// the same fp32 products and sums at twice that ceiling (157.3 vs 78.6 TFLOP/s
+// without packed FP32). Design, shared with the fp16 NHWC kernel:
+//  * persistent workgroups of 4 waves, one per CU, looping over 16 x 32 pixel
+//    tiles; tiles of one XCD are neighbours so halo re-reads hit its L2;
+//  * the input tile with its 1-pixel halo (32 channels x 18 rows x 34 columns)
+//    streams HBM -> LDS by 4-byte buffer_load ... lds, double-buffered against
+//    the MFMAs; pixels outside the image read as 0 through the range check;
+//  * LDS keeps the NCHW order with a channel-plane pitch of 624 floats (612
+//    used), an odd multiple of 16 banks: the 16 lanes of one channel read 16
+//    consecutive floats, and the two channels of a 32-lane half land on
+//    disjoint bank halves;
+//  * wave w computes output channels 16*(w&1) .. +16 for columns 16*(w>>1) ..
+//    +16 of all 16 tile rows; its 72 weight fragments (all 288 k) stay in
+//    registers;
+//  * MFMA operands: A = 16 pixels x 4 channels of one tap (one LDS float per
+//    lane), B = 4 channels x 16 output channels (weights), D = 4 consecutive
+//    pixels of one output channel per lane, stored as one 16-byte NCHW vector;
+//  * rolling rows: the A fragment of input row i (tap column v, channel quad)
+//    is read once and feeds output rows i, i-1 and i-2 through filter rows 0, 1
+//    and 2; an output row is final after input row +2 and is stored from the
+//    accumulators inside the loop (bias, optional ReLU).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace is {
+namespace {
+
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 32;                        // input channels
+constexpr int kK = 32;                        // output channels
+constexpr int kTR = 16, kTC = 32;             // output tile: rows x columns
+constexpr int kIR = kTR + 2, kIC = kTC + 2;   // input tile with halo
+constexpr int kPlane = 624;                   // LDS floats per channel plane (kIR * kIC = 612 used)
+constexpr int kBufFloats = kC * kPlane;       // floats per LDS tile buffer
+constexpr int kThreads = 256;
+constexpr int kRounds = kBufFloats / kThreads;   // 4-byte DMA rounds per thread and tile
+constexpr int kCQ = kC / 4;                   // channel quads (k steps per tap)
+constexpr int kKS = 9 * kCQ;                  // k steps of 4
+constexpr int kStores = kTR;                  // 16-byte output stores per thread per tile
+constexpr unsigned kOob = 0xFFFFFFF0u;
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= kStores (bits 3:0 and 15:14),
+// expcnt and lgkmcnt not waited for (all ones).
+constexpr int kWaitDmaNotStores = (kStores & 0xF) | ((kStores >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+static_assert(kRounds * kThreads == kBufFloats, "whole DMA rounds");
+static_assert(kIR * kIC <= kPlane && kPlane % 32 == 16, "plane pitch: 16 banks apart");
+static_assert(kStores < 64, "vmcnt field");
+
+struct MfmaF32Args {
+  const float *x;
+  const float *w;
+  const float *bias;
+  float *y;
+  int N, H, W, relu;
+  int tiles_x, tiles_y, ntiles;
+};
+
+__global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
+  __shared__ float lds[2 * kBufFloats];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n16 = lane & 15;   // pixel of A, output channel of B and D
+  const int g = lane >> 4;     // channel of A and B inside a quad; pixel group of D
+  const int ob = wave & 1;     // output channels 16*ob .. +16
+  const int ch = wave >> 1;    // tile columns 16*ch .. +16
+
+  // ---- Weights: fragment (t, cq) of this lane is W[16ob + n16][4cq + g][t].
+  float wb[kKS];
+  {
+    const float *wp = a.w + ((size_t)(16 * ob + n16) * kC + g) * 9;
+#pragma unroll
+    for (int t = 0; t < 9; ++t)
+#pragma unroll
+      for (int cq = 0; cq < kCQ; ++cq) wb[t * kCQ + cq] = wp[cq * 4 * 9 + t];
+  }
+  const float bv = a.bias ? a.bias[16 * ob + n16] : 0.f;
+
+  // ---- Tile schedule: XCD x (= blockIdx mod 8) walks its own contiguous range.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int per_xcd = (a.ntiles + 7) / 8;
+  const int lo = xcd * per_xcd;
+  const int hi = min(a.ntiles, lo + per_xcd);
+  const int step = G >> 3;
+  int tile = lo + (blockIdx.x >> 3);
+
+  const int H = a.H, W = a.W;
+  const size_t plane = (size_t)H * W;
+  auto tile_origin = [&](int tl, int &n, int &y0, int &x0) {
+    const int tx = tl % a.tiles_x;
+    const int ty = (tl / a.tiles_x) % a.tiles_y;
+    n = tl / (a.tiles_x * a.tiles_y);
+    y0 = ty * kTR;
+    x0 = tx * kTC;
+  };
+  // LDS float s of a buffer holds channel s / kPlane, tile row r / kIC and
+  // column r % kIC of r = s % kPlane (image row y0-1+row, column x0-1+col);
+  // the plane padding and pixels outside the image are loaded as 0.
+  auto issue = [&](int tl, float *buf) {
+    int n, y0, x0;
+    tile_origin(tl, n, y0, x0);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.x + (size_t)n * kC * plane), (short)0, (int)(kC * plane * 4), kBufferFlags);
+#pragma unroll 2
+    for (int j = 0; j < kRounds; ++j) {
+      const int s = (j * 4 + wave) * 64 + lane;
+      const int c = s / kPlane;
+      const int r = s - c * kPlane;
+      const int row = r / kIC;
+      const int col = r - row * kIC;
+      const int gy = y0 - 1 + row, gx = x0 - 1 + col;
+      const bool in = r < kIR * kIC && gy >= 0 && gy < H && gx >= 0 && gx < W;
+      const unsigned off = in ? (unsigned)(((size_t)c * plane + (size_t)gy * W + gx) * 4) : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void *)(buf + (j * 4 + wave) * 64), 4, off, 0, 0, 0);
+    }
+  };
+
+  // Float offset (inside a buffer) of this lane's A reads for tap column v at
+  // tile row 0: channel g of the quad, column 16*ch + n16 + v.
+  const int aoff = g * kPlane + 16 * ch + n16;
+
+  auto compute_store = [&](int tl, const float *buf) {
+    int n, y0, x0;
+    tile_origin(tl, n, y0, x0);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        a.y + (size_t)n * kK * plane, (short)0, (int)(kK * plane * 4), kBufferFlags);
+    // This lane's output: channel 16*ob + n16, columns x0 + 16*ch + 4g .. +4.
+    const int gx = x0 + 16 * ch + 4 * g;
+    const bool col_in = gx < W;
+    const unsigned col_off = (unsigned)(((size_t)(16 * ob + n16) * plane + gx) * 4);
+    float4v acc[kTR];
+#pragma unroll
+    for (int o = 0; o < kTR; ++o) acc[o] = float4v{0.f, 0.f, 0.f, 0.f};
+    // Reads in (input row i, tap column v, channel quad cq) order, each issued
+    // kAhead reads early into a ring of registers.
+    constexpr int kReads = kIR * 3 * kCQ;
+    constexpr int kAhead = 16;
+    auto read_a = [&](int q) -> float {
+      const int i = q / (3 * kCQ), v = (q / kCQ) % 3, cq = q % kCQ;
+      return buf[aoff + cq * 4 * kPlane + i * kIC + v];
+    };
+    float ring[kAhead];
+#pragma unroll
+    for (int q = 0; q < kAhead; ++q) ring[q] = read_a(q);
+    static_for<kReads>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
+      const float av = ring[q % kAhead];
+      if constexpr (q + kAhead < kReads) ring[q % kAhead] = read_a(q + kAhead);
+      constexpr int i = q / (3 * kCQ), v = (q / kCQ) % 3, cq = q % kCQ;
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int o = i - u;
+        if (o >= 0 && o < kTR)
+          acc[o] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wb[(3 * u + v) * kCQ + cq], acc[o], 0, 0, 0);
+      }
+      if constexpr (v == 2 && cq == kCQ - 1 && i >= 2) {
+        constexpr int o = i - 2;
+        const int gy = y0 + o;
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          r[e] = acc[o][e] + bv;
+          if (a.relu) r[e] = fmaxf(r[e], 0.f);
+        }
+        const unsigned off = (gy < H && col_in) ? col_off + (unsigned)gy * (unsigned)W * 4u : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4v, float4v{r[0], r[1], r[2], r[3]}),
+                                               ry, off, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  if (tile < hi) issue(tile, lds);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int cur = 0;
+  while (tile < hi) {
+    const int next = tile + step;
+    if (next < hi) issue(next, lds + (cur ^ 1) * kBufFloats);
+    compute_store(tile, lds + cur * kBufFloats);
+    // Wait for the next tile's DMA but not for this tile's output stores:
+    // vector-memory operations retire in issue order on gfx9, and the stores
+    // (kStores per thread) were issued after the DMA.
+    __builtin_amdgcn_s_waitcnt(kWaitDmaNotStores);
+    __syncthreads();
+    tile = next;
+    cur ^= 1;
+  }
+}
+
+}  // namespace
+
+bool configure_mfma_f32(Plan &p) {
+  const conv2d_desc &d = p.d;
+  if (d.layout != IS_NCHW || d.in_dtype != IS_F32 || d.out_dtype != IS_F32) return false;
+  if (d.c != kC || d.k != kK || d.r != 3 || d.s != 3) return false;
+  if (d.w % 4 != 0) return false;   // 16-byte output vectors
+  // 32-bit buffer offsets inside one image of the input and of the output.
+  if (4.0 * kC * (double)d.h * d.w >= 2.0e9) return false;
+  const long long tiles = (long long)((d.w + kTC - 1) / kTC) * ((d.h + kTR - 1) / kTR) * d.n;
+  if (tiles > (1LL << 31) - 1) return false;
+  p.kid = kMfmaNchwF32;
+  p.name = "is_k5_mfma_f32";
+  p.nseg = (d.w + kTC - 1) / kTC;
+  p.nstrip = (d.h + kTR - 1) / kTR;
+  p.ntiles = (int)tiles;
+  // Persistent: one workgroup per CU (its LDS fills the CU), 8 XCDs x 32 CUs;
+  // fewer when there are fewer tiles (kept a multiple of 8).
+  int g = 256;
+  while (g > 8 && g / 2 >= p.ntiles) g /= 2;
+  p.grid_x = g;
+  p.grid_y = p.grid_z = 1;
+  p.block = kThreads;
+  p.lds = 2 * kBufFloats * 4;
+  p.tile_w = kTC;
+  p.tile_h = kTR;
+  return true;
+}
+
+hipError_t launch_mfma_f32(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                           hipStream_t s) {
+  MfmaF32Args a;
+  a.x = x;
+  a.w = w;
+  a.bias = b;
+  a.y = y;
+  a.N = p.d.n;
+  a.H = p.d.h;
+  a.W = p.d.w;
+  a.relu = p.d.relu;
+  a.tiles_x = p.nseg;
+  a.tiles_y = p.nstrip;
+  a.ntiles = p.ntiles;
+  return launch_kernel(is_k5_mfma_f32, dim3(p.grid_x), dim3(p.block), 0, s, a);
+}
+
+}  // namespace is

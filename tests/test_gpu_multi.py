@@ -1,9 +1,10 @@
 """GPU parity of multi-channel fp32 NCHW layers against the oracle.
 
-Calls go through the C ABI. Shapes span several 64x16 tiles with ragged edges,
-channel counts that fill one or several LDS slabs, every output-channel group
-size, and the full 1x32x720x1280 layer (sampled rows, all columns and
-channels).
+Calls go through the C ABI. Shapes span several tiles with ragged edges (64x16
+for the register-blocked kernel, 32x16 for the fp32 MFMA kernel that takes the
+32 -> 32 3x3 layers), channel counts that fill one or several LDS slabs, every
+output-channel group size, and the full 1x32x720x1280 layer (sampled rows, all
+columns and channels).
 """
 import numpy as np
 import pytest
@@ -31,7 +32,13 @@ def _run(x, w, b, relu, expect=None):
 
 CASES = [
     # N, C, K, H, W, R, relu, kernel
-    (1, 32, 32, 50, 200, 3, True, "is_k2_multi"),
+    (1, 32, 32, 50, 200, 3, True, "is_k5_mfma_f32"),
+    (2, 32, 32, 37, 132, 3, False, "is_k5_mfma_f32"),
+    (3, 32, 32, 19, 68, 3, True, "is_k5_mfma_f32"),
+    (1, 32, 32, 16, 32, 3, False, "is_k5_mfma_f32"),
+    (1, 32, 32, 1, 4, 3, True, "is_k5_mfma_f32"),
+    (1, 32, 32, 33, 260, 3, False, "is_k5_mfma_f32"),
+    (1, 32, 32, 9, 30, 3, False, "is_k0_generic_nchw_f32"),
     (2, 8, 16, 37, 132, 3, False, "is_k2_multi"),
     (1, 4, 8, 17, 68, 3, True, "is_k2_multi"),
     (1, 4, 4, 33, 64, 3, False, "is_k2_multi"),
@@ -75,12 +82,29 @@ def test_delta_weights_bit_exact():
     np.testing.assert_array_equal(y.astype(np.float64), ref)
 
 
+def test_mfma_f32_no_bias_and_delta_weights():
+    """The fp32 MFMA kernel without bias, and with one-hot weights (each output
+    channel copies one shifted input channel): products by 0 and 1 and their
+    sums are exact, so the result must be too."""
+    x, w, _ = synth.cnn_layer_f32(N=1, C=32, K=32, H=35, W=72, seed=6)
+    y = _run(x, w, None, False, "is_k5_mfma_f32")
+    ref, m = oracle.conv2d(x, w, None, False)
+    check(y, ref, m, TAU_F32, "mfma f32 no bias")
+    wd = np.zeros((32, 32, 3, 3), np.float32)
+    rng = np.random.default_rng(7)
+    for k in range(32):
+        wd[k, rng.integers(0, 32), rng.integers(0, 3), rng.integers(0, 3)] = 1.0
+    y = _run(x, wd, None, False, "is_k5_mfma_f32")
+    ref, _ = oracle.conv2d(x, wd)
+    np.testing.assert_array_equal(y.astype(np.float64), ref)
+
+
 def test_cnn_layer_720p_sampled():
     """1x32x720x1280 -> 32, 3x3, bias, ReLU: rows on tile edges and random rows,
     every column and output channel."""
     x, w, b = synth.cnn_layer_f32()
     say("cnn layer 720p")
-    y = _run(x, w, b, True, "is_k2_multi")
+    y = _run(x, w, b, True, "is_k5_mfma_f32")
     assert np.isfinite(y).all()
     rows = sorted({0, 1, 15, 16, 17, 31, 32, 47, 359, 360, 703, 704, 718, 719} |
                   set(int(r) for r in np.random.default_rng(5).integers(0, 720, 6)))

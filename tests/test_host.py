@@ -117,6 +117,10 @@ def test_plan_choice_and_counts():
     chain = [(1, 32, 5), (32, 32, 3), (32, 32, 3), (32, 4, 3)]
     assert round(traffic.chain_flops(1, 720, 1280, chain) / 1e9, 2) == 37.57
     assert round(traffic.conv_flops(8, 64, 256, 256, 64, 3, 3) / 1e9, 2) == 38.65
+    # the 32 -> 32 3x3 fp32 layer runs on the fp32 matrix cores
+    info = isa.Plan(isa.make_desc(1, 32, 720, 1280, 32, 3, 3, "f32", True)).info()
+    assert info["kernel"] == "is_k5_mfma_f32"
+    assert info["tile"] == (32, 16) and info["lds_bytes"] == 2 * 32 * 624 * 4
     # wide filters fall back to the one-thread-per-output kernel
     info = isa.Plan(isa.make_desc(1, 1, 64, 64, 1, 9, 9)).info()
     assert info["kernel"] == "is_k0_generic_nchw_f32"
