@@ -16,13 +16,15 @@
 //    top of each block: each intermediate layer keeps a ring of its last six
 //    output rows (all 32 channels, fp32) in LDS, which is all that the next
 //    layer's 3x3 window needs for four new rows;
-//  * the 8 waves each own 4 output channels of a layer; a lane holds 4
-//    contiguous pixels x 4 channels of one row, reads one 16-byte LDS vector per
-//    input channel and filter row and takes its left/right neighbours by DPP
-//    row shifts, as in the multi-channel kernel;
-//  * weights of the wave's channels are read with uniform buffer loads into
-//    registers (16-byte aligned vectors; the second wave on each SIMD hides
-//    their latency);
+//  * the two 32 -> 32 layers (90% of the FLOPs) run on the fp32 matrix cores
+//    (v_mfma_f32_16x16x4_f32, as in the fp32 MFMA layer kernel): each wave owns
+//    16 output channels of one of the four step rows, reads one LDS float per
+//    lane per (tap, channel quad, 16-column block) and keeps the weights of both
+//    layers in registers;
+//  * the 5x5 1 -> 32 layer and the 3x3 32 -> 4 layer stay on the vector ALUs:
+//    a lane holds 4 contiguous pixels x 4 channels of one row, reads one
+//    16-byte LDS vector per input channel and filter row and takes its
+//    left/right neighbours by DPP row shifts, as in the multi-channel kernel;
 //  * only the input frame is read from HBM and only the depth-to-space output
 //    is written: two 16-byte stores per lane and output row pair.
 #include "common.hpp"
@@ -53,6 +55,14 @@ __device__ __forceinline__ float row_next(float src, float old) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), kDppRowShl1,
                                                     0xf, 0xf, false));
 }
+
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// Intermediate rings hold, per row slot and channel, the 64 window columns as
+// 16 float4 vectors; odd channels are stored rotated by 4 vectors (16 floats)
+// so that the two channels read by one 32-lane half of an MFMA operand load
+// land on disjoint halves of the 32 LDS banks. Vector lc of channel c:
+__device__ __forceinline__ int rot4(int c, int lc) { return (lc + 4 * (c & 1)) & 15; }
 
 struct ChainArgs {
   const float *x;
@@ -98,7 +108,7 @@ __device__ __forceinline__ void window3(const float4 *src, const int (&slot)[3],
                                         float (&win)[3][6]) {
 #pragma unroll
   for (int u = 0; u < 3; ++u) {
-    const float4 o = src[(slot[u] * kCh + c) * kG + lc];
+    const float4 o = src[(slot[u] * kCh + c) * kG + rot4(c, lc)];
     win[u][1] = o.x; win[u][2] = o.y; win[u][3] = o.z; win[u][4] = o.w;
     win[u][0] = row_prev(o.w, 0.f);
     win[u][5] = row_next(o.x, 0.f);
@@ -131,8 +141,6 @@ __global__ __launch_bounds__(kThreads) void is_k3_chain(ChainArgs a) {
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (size_t)n * HW, (unsigned)(HW * 4));
   const __amdgpu_buffer_rsrc_t ry = rsrc(a.y + (size_t)n * 4 * HW, (unsigned)(4 * HW * 4));
   const __attribute__((address_space(4))) float *w0c = (const __attribute__((address_space(4))) float *)a.w[0];
-  const __amdgpu_buffer_rsrc_t rw1 = rsrc(a.w[1], 32 * 32 * 9 * 4);
-  const __amdgpu_buffer_rsrc_t rw2 = rsrc(a.w[2], 32 * 32 * 9 * 4);
   const __amdgpu_buffer_rsrc_t rw3 = rsrc(a.w[3], 4 * 32 * 9 * 4);
 
   // Byte offset of input vector q (row slot q/kInG of a 4- or 8-row batch
@@ -147,6 +155,22 @@ __global__ __launch_bounds__(kThreads) void is_k3_chain(ChainArgs a) {
 
   // Input rows t0+1 .. t0+8 before the first step.
   for (int q = tid; q < 8 * kInG; q += kThreads) in_ring[q] = ld4(rx, in_off(t0 + 1, q));
+
+  // MFMA layers: lane (g4, n16) holds, for filter tap t and channel quad cq,
+  // the weight of output channel 16*mob + n16 and input channel 4*cq + g4.
+  const int mob = wave & 1, mrow = wave >> 1;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  float wm[2][9 * (kCh / 4)];
+  float bm[2];
+#pragma unroll
+  for (int l = 0; l < 2; ++l) {
+    const float *wp = a.w[l + 1] + ((size_t)(16 * mob + n16) * kCh + g4) * 9;
+#pragma unroll
+    for (int tp = 0; tp < 9; ++tp)
+#pragma unroll
+      for (int cq = 0; cq < kCh / 4; ++cq) wm[l][tp * (kCh / 4) + cq] = wp[cq * 4 * 9 + tp];
+    bm[l] = a.b[l + 1] ? a.b[l + 1][16 * mob + n16] : 0.f;
+  }
 
   const int gcol = xw + 4 * lc;                 // first image column of the lane's pixels
   const bool col_in = gcol >= 0 && gcol < W;
@@ -211,64 +235,72 @@ __global__ __launch_bounds__(kThreads) void is_k3_chain(ChainArgs a) {
           if (relu) o[p] = fmaxf(o[p], 0.f);
           if (!keep) o[p] = 0.f;
         }
-        dst[(f0 + f) * kG + lc] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[(f0 + f) * kG + rot4(f0 + f, lc)] = make_float4(o[0], o[1], o[2], o[3]);
       }
     }
     __syncthreads();
 
-    // ---- Layers 2 and 3: 3x3, 32 -> 32 (rows t+2.. and t+1..), skipped while
-    // their inputs are still warming up.
+    // ---- Layers 2 and 3: 3x3, 32 -> 32 (rows t+2.. and t+1..) on the fp32
+    // matrix cores, skipped while their inputs are still warming up. Wave w
+    // computes output channels 16*(w&1) .. +16 of step row w>>1 for the four
+    // 16-column blocks of the window: A = 16 pixels x 4 channels of one tap
+    // (one LDS float per lane), B = 4 channels x 16 output channels (weights in
+    // registers), D = 4 consecutive pixels of one output channel per lane,
+    // written back to the next ring as one float4. The window's edge columns
+    // read a neighbouring column of the same ring row instead of 0; they only
+    // reach window columns 0..2 and 61..63 of the last layer, outside the kept
+    // 4..59.
     for (int l = 1; l <= 2; ++l) {
       if (k >= 1) {
-        const float4 *src = ring[l - 1];
-        const __amdgpu_buffer_rsrc_t rw = l == 1 ? rw1 : rw2;
-        const float *bias = a.b[l];
-        const int row = t + 3 - l + lr;
-        int slot[3];
+        const float *src = reinterpret_cast<const float *>(ring[l - 1]);
+        const float *wl = wm[l - 1];
+        const int row = t + 3 - l + mrow;
+        float4v acc[4];
 #pragma unroll
-        for (int u = 0; u < 3; ++u) slot[u] = (row - 1 + u - t0) % kRing;
-        float acc[4][4];
+        for (int cb = 0; cb < 4; ++cb) acc[cb] = float4v{0.f, 0.f, 0.f, 0.f};
+        // Float offset of the lane's A element for filter row u, tap column v
+        // and column block cb (channel quad 0); quad cq adds 4 * kWin * cq.
+        int aoff[3][3][4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int u = 0; u < 3; ++u) {
+          const int base = ((row - 1 + u - t0) % kRing * kCh + g4) * kWin;
 #pragma unroll
-          for (int p = 0; p < 4; ++p) acc[f][p] = 0.f;
-
-        // Input channels in groups of 4 so that each channel's tap offset inside
-        // its 16-byte vectors is a constant after unrolling.
-        for (int c4 = 0; c4 < kCh; c4 += 4) {
+          for (int v = 0; v < 3; ++v)
 #pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const int c = c4 + cc;
-            float tap[4][9];
-#pragma unroll
-            for (int f = 0; f < 4; ++f) load_taps9(rw, taps_base(f0 + f, c), cc, tap[f]);
-            float win[3][6];
-            window3(src, slot, c, lc, win);
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-#pragma unroll
-              for (int u = 0; u < 3; ++u)
-#pragma unroll
-                for (int v = 0; v < 3; ++v)
-#pragma unroll
-                  for (int p = 0; p < 4; ++p)
-                    acc[f][p] = __builtin_fmaf(tap[f][u * 3 + v], win[u][p + v], acc[f][p]);
-          }
+            for (int cb = 0; cb < 4; ++cb) aoff[u][v][cb] = base + ((16 * cb + n16 + v - 1 + 16 * (g4 & 1)) & 63);
         }
-        const bool keep = col_in && row >= 0 && row < H;
-        const bool relu = (a.relu_mask >> l) & 1;
-        float4 *dst = ring[l] + ((row - t0) % kRing) * kCh * kG;
+        constexpr int kSteps = 9 * (kCh / 4) * 4;   // (tap, channel quad, column block)
+        constexpr int kAhead = 16;
+        auto read_a = [&](int q) -> float {
+          const int tq = q / 4, cb = q % 4, tp = tq / 8, cq = tq % 8;
+          return src[aoff[tp / 3][tp % 3][cb] + cq * 4 * kWin];
+        };
+        float ra[kAhead];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const float bb = bias ? bias[f0 + f] : 0.f;
+        for (int q = 0; q < kAhead; ++q) ra[q] = read_a(q);
+        static_for<kSteps>([&](auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value;
+          const float av = ra[q % kAhead];
+          if constexpr (q + kAhead < kSteps) ra[q % kAhead] = read_a(q + kAhead);
+          constexpr int tq = q / 4, cb = q % 4;
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wl[tq], acc[cb], 0, 0, 0);
+        });
+        const bool row_in = row >= 0 && row < H;
+        const bool relu = (a.relu_mask >> l) & 1;
+        const int c = 16 * mob + n16;
+        float4 *dst = ring[l] + ((row - t0) % kRing) * kCh * kG + c * kG;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const int gc = xw + 16 * cb + 4 * g4;   // image column of the lane's first pixel
+          const bool keep = row_in && gc >= 0 && gc < W;
           float o[4];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            o[p] = acc[f][p] + bb;
-            if (relu) o[p] = fmaxf(o[p], 0.f);
-            if (!keep) o[p] = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            o[e] = acc[cb][e] + bm[l - 1];
+            if (relu) o[e] = fmaxf(o[e], 0.f);
+            if (!keep) o[e] = 0.f;
           }
-          dst[(f0 + f) * kG + lc] = make_float4(o[0], o[1], o[2], o[3]);
+          dst[rot4(c, 4 * cb + g4)] = make_float4(o[0], o[1], o[2], o[3]);
         }
       }
       __syncthreads();
