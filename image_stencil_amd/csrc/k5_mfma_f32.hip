@@ -8,17 +8,20 @@
 // direct fp32 kernel is bound by the vector ALUs; v_mfma_f32_16x16x4_f32 does
 // the same fp32 products and sums at twice that ceiling (157.3 vs 78.6 TFLOP/s
 // without packed FP32). Design, shared with the fp16 NHWC kernel:
-//  * persistent workgroups of 4 waves, one per CU, looping over 16 x 32 pixel
-//    tiles; tiles of one XCD are neighbours so halo re-reads hit its L2;
-//  * the input tile with its 1-pixel halo (32 channels x 18 rows x 34 columns)
-//    streams HBM -> LDS by 4-byte buffer_load ... lds, double-buffered against
-//    the MFMAs; pixels outside the image read as 0 through the range check;
-//  * LDS keeps the NCHW order with a channel-plane pitch of 624 floats (612
-//    used), an odd multiple of 16 banks: the 16 lanes of one channel read 16
-//    consecutive floats, and the two channels of a 32-lane half land on
-//    disjoint bank halves;
+//  * persistent workgroups of 4 waves, one per CU, looping over 12 x 32 pixel
+//    tiles (2400 on a 1280x720 frame: 10 rounds of 256 CUs with 6% idle,
+//    where 16-row tiles left 12% idle); tiles of one XCD are neighbours so halo
+//    re-reads hit its L2;
+//  * the input tile with its halo (32 channels x 14 rows x 40 columns, aligned
+//    16-byte chunks) streams HBM -> LDS by 16-byte buffer_load ... lds,
+//    double-buffered against the MFMAs; pixels outside the image read as 0
+//    through the range check;
+//  * LDS keeps the NCHW order; the channel-plane pitch of 560 floats is an odd
+//    multiple of 16 banks: the 16 lanes of one channel read 16 consecutive
+//    floats, and the two channels of a 32-lane half land on disjoint bank
+//    halves;
 //  * wave w computes output channels 16*(w&1) .. +16 for columns 16*(w>>1) ..
-//    +16 of all 16 tile rows; its 72 weight fragments (all 288 k) stay in
+//    +16 of all 12 tile rows; its 72 weight fragments (all 288 k) stay in
 //    registers;
 //  * MFMA operands: A = 16 pixels x 4 channels of one tap (one LDS float per
 //    lane), B = 4 channels x 16 output channels (weights), D = 4 consecutive
@@ -38,21 +41,40 @@ typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 32;                        // input channels
 constexpr int kK = 32;                        // output channels
-constexpr int kTR = 16, kTC = 32;             // output tile: rows x columns
-constexpr int kIR = kTR + 2, kIC = kTC + 2;   // input tile with halo
-constexpr int kPlane = 624;                   // LDS floats per channel plane (kIR * kIC = 612 used)
-constexpr int kBufFloats = kC * kPlane;       // floats per LDS tile buffer
+constexpr int kTR = 12, kTC = 32;             // output tile: rows x columns
+constexpr int kIR = kTR + 2;                  // input rows with halo
+// An input row is loaded as 10 aligned 16-byte chunks, image columns x0-4 ..
+// x0+35, of which x0-1 .. x0+32 are used (LDS column 3 holds x0-1).
+constexpr int kChunksRow = 10;
+constexpr int kIC = 4 * kChunksRow;           // LDS floats per input row
+constexpr int kPlane = kIR * kIC;             // LDS floats per channel plane (560)
+constexpr int kChunks = kC * kIR * kChunksRow;   // 16-byte chunks per input tile
 constexpr int kThreads = 256;
-constexpr int kRounds = kBufFloats / kThreads;   // 4-byte DMA rounds per thread and tile
+constexpr int kRounds = (kChunks + kThreads - 1) / kThreads;   // 16-byte DMA rounds per thread and tile
+constexpr int kBufFloats = kRounds * kThreads * 4;   // floats per LDS tile buffer (whole rounds)
 constexpr int kCQ = kC / 4;                   // channel quads (k steps per tap)
 constexpr int kKS = 9 * kCQ;                  // k steps of 4
-constexpr int kStores = kTR;                  // 16-byte output stores per thread per tile
+constexpr int kReadSteps = kIR * 3 * kCQ;     // A reads per wave and tile
+// The next tile's DMA rounds are issued during the first kIssueSteps read
+// steps (round j at step j * kIssueSteps / kRounds), so that the last one has
+// the rest of the tile's MFMAs to arrive.
+constexpr int kIssueSteps = kReadSteps * 3 / 5;
+// Output stores issued after the last DMA round of a tile: row o is stored at
+// read step (o + 2) * 3 * kCQ + 3 * kCQ - 1.
+constexpr int stores_after_last_round() {
+  const int q_last = ((kRounds - 1) * kIssueSteps) / kRounds;
+  int n = 0;
+  for (int o = 0; o < kTR; ++o)
+    if ((o + 2) * 3 * kCQ + 3 * kCQ - 1 >= q_last) ++n;
+  return n;
+}
+constexpr int kStores = stores_after_last_round();
 constexpr unsigned kOob = 0xFFFFFFF0u;
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= kStores (bits 3:0 and 15:14),
 // expcnt and lgkmcnt not waited for (all ones).
 constexpr int kWaitDmaNotStores = (kStores & 0xF) | ((kStores >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-static_assert(kRounds * kThreads == kBufFloats, "whole DMA rounds");
-static_assert(kIR * kIC <= kPlane && kPlane % 32 == 16, "plane pitch: 16 banks apart");
+static_assert(kPlane % 32 == 16, "plane pitch: 16 banks apart");
+static_assert(kC * kPlane <= kBufFloats, "the tile fits its buffer");
 static_assert(kStores < 64, "vmcnt field");
 
 struct MfmaF32Args {
@@ -104,34 +126,53 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
     y0 = ty * kTR;
     x0 = tx * kTC;
   };
-  // LDS float s of a buffer holds channel s / kPlane, tile row r / kIC and
-  // column r % kIC of r = s % kPlane (image row y0-1+row, column x0-1+col);
-  // the plane padding and pixels outside the image are loaded as 0.
-  auto issue = [&](int tl, float *buf) {
-    int n, y0, x0;
-    tile_origin(tl, n, y0, x0);
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(a.x + (size_t)n * kC * plane), (short)0, (int)(kC * plane * 4), kBufferFlags);
-#pragma unroll 2
-    for (int j = 0; j < kRounds; ++j) {
-      const int s = (j * 4 + wave) * 64 + lane;
-      const int c = s / kPlane;
-      const int r = s - c * kPlane;
-      const int row = r / kIC;
-      const int col = r - row * kIC;
-      const int gy = y0 - 1 + row, gx = x0 - 1 + col;
-      const bool in = r < kIR * kIC && gy >= 0 && gy < H && gx >= 0 && gx < W;
-      const unsigned off = in ? (unsigned)(((size_t)c * plane + (size_t)gy * W + gx) * 4) : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (__attribute__((address_space(3))) void *)(buf + (j * 4 + wave) * 64), 4, off, 0, 0, 0);
-    }
+  // LDS chunk s of a buffer holds channel s / (kIR * kChunksRow), tile row
+  // r / kChunksRow and chunk r % kChunksRow of r = s % (kIR * kChunksRow)
+  // (image row y0-1+row, columns x0-4+4*chunk .. +4); chunks outside the image
+  // are loaded as 0 (W is a multiple of 4, so a chunk is wholly in or out), and
+  // so are the chunks of the last round past the tile. One DMA round j moves
+  // chunks (4j + wave) * 64 + lane.
+  struct Dma {
+    __amdgpu_buffer_rsrc_t rx;
+    int y0, x0;
+    bool any;   // false: no tile to load, every round reads nothing
+  };
+  auto dma_for = [&](int tl) -> Dma {
+    Dma d;
+    int n;
+    d.any = tl < hi;
+    tile_origin(d.any ? tl : 0, n, d.y0, d.x0);
+    d.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.x + (size_t)n * kC * plane), (short)0,
+                                             (int)(kC * plane * 4), kBufferFlags);
+    return d;
+  };
+  // Branch-free and in 32-bit arithmetic (the plan keeps an image's input under
+  // 2 GB): the rounds sit between the MFMAs, where a divergent branch would
+  // break the instruction stream.
+  const int plane_i = H * W;
+  auto issue_round = [&](const Dma &d, float *buf, int j) {
+    constexpr unsigned kPerPlane = kIR * kChunksRow;
+    const unsigned s = (unsigned)((j * 4 + wave) * 64 + lane);
+    const unsigned c = s / kPerPlane;
+    const unsigned r = s - c * kPerPlane;
+    const unsigned row = r / kChunksRow;
+    const unsigned k = r - row * kChunksRow;
+    const int gy = d.y0 - 1 + (int)row, gx = d.x0 - 4 + 4 * (int)k;
+    const bool in = d.any & (s < (unsigned)kChunks) & ((unsigned)gy < (unsigned)H) & ((unsigned)gx < (unsigned)W);
+    const unsigned off = in ? (unsigned)((int)c * plane_i + gy * W + gx) * 4u : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        d.rx, (__attribute__((address_space(3))) void *)(buf + (j * 4 + wave) * 64 * 4), 16, off, 0, 0, 0);
   };
 
   // Float offset (inside a buffer) of this lane's A reads for tap column v at
-  // tile row 0: channel g of the quad, column 16*ch + n16 + v.
-  const int aoff = g * kPlane + 16 * ch + n16;
+  // tile row 0: channel g of the quad, image column x0 - 1 + 16*ch + n16 + v
+  // (LDS column 3 holds x0 - 1).
+  const int aoff = g * kPlane + 3 + 16 * ch + n16;
 
-  auto compute_store = [&](int tl, const float *buf) {
+  // The next tile's DMA rounds are spread over the first 3/5 of the MFMA
+  // loop, between the reads: spread to the very end, the last round's latency
+  // would be exposed at every tile boundary.
+  auto compute_store = [&](int tl, const float *buf, const Dma &dn, float *nbuf) {
     int n, y0, x0;
     tile_origin(tl, n, y0, x0);
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
@@ -145,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
     for (int o = 0; o < kTR; ++o) acc[o] = float4v{0.f, 0.f, 0.f, 0.f};
     // Reads in (input row i, tap column v, channel quad cq) order, each issued
     // kAhead reads early into a ring of registers.
-    constexpr int kReads = kIR * 3 * kCQ;
+    constexpr int kReads = kReadSteps;
     constexpr int kAhead = 16;
     auto read_a = [&](int q) -> float {
       const int i = q / (3 * kCQ), v = (q / kCQ) % 3, cq = q % kCQ;
@@ -156,6 +197,16 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
     for (int q = 0; q < kAhead; ++q) ring[q] = read_a(q);
     static_for<kReads>([&](auto qc) __attribute__((always_inline)) {
       constexpr int q = decltype(qc)::value;
+      // rounds issued at this step: j with j * kIssueSteps / kRounds == q
+      constexpr int j0 = q < kIssueSteps ? (q * kRounds + kIssueSteps - 1) / kIssueSteps : kRounds;
+      constexpr int j1 = q < kIssueSteps ? ((q + 1) * kRounds + kIssueSteps - 1) / kIssueSteps : kRounds;
+      if constexpr (j1 > j0) {
+#pragma unroll
+        for (int j = j0; j < j1; ++j) issue_round(dn, nbuf, j);
+        // keeps the round ahead of this step's store (the tile-end wait counts
+        // the stores issued after the last round)
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const float av = ring[q % kAhead];
       if constexpr (q + kAhead < kReads) ring[q % kAhead] = read_a(q + kAhead);
       constexpr int i = q / (3 * kCQ), v = (q / kCQ) % 3, cq = q % kCQ;
@@ -182,17 +233,18 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
     });
   };
 
-  if (tile < hi) issue(tile, lds);
+  {
+    const Dma d0 = dma_for(tile);
+    for (int j = 0; j < kRounds; ++j) issue_round(d0, lds, j);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int cur = 0;
   while (tile < hi) {
     const int next = tile + step;
-    if (next < hi) issue(next, lds + (cur ^ 1) * kBufFloats);
-    compute_store(tile, lds + cur * kBufFloats);
-    // Wait for the next tile's DMA but not for this tile's output stores:
-    // vector-memory operations retire in issue order on gfx9, and the stores
-    // (kStores per thread) were issued after the DMA.
+    compute_store(tile, lds + cur * kBufFloats, dma_for(next), lds + (cur ^ 1) * kBufFloats);
+    // Wait for the next tile's DMA but not for the output stores issued after
+    // its last round: vector-memory operations retire in issue order on gfx9.
     __builtin_amdgcn_s_waitcnt(kWaitDmaNotStores);
     __syncthreads();
     tile = next;
