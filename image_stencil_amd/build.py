@@ -56,6 +56,16 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # Every symbol of the library's own namespace must be defined in it: the
+    # host pass can drop a kernel's launch stub (a struct declared inside a
+    # template kernel did) and leave an undefined reference that only fails
+    # when the library is loaded.
+    nm = subprocess.run(["nm", "-u", "-C", tmp], capture_output=True, text=True)
+    if nm.returncode == 0:
+        missing = [l.strip() for l in nm.stdout.splitlines() if "is::" in l]
+        if missing:
+            os.remove(tmp)
+            raise RuntimeError("libimgstencil.so has undefined symbols of its own:\n  " + "\n  ".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

@@ -51,10 +51,21 @@ constexpr int kChunks = kIR * kIC * 8;       // 16-byte chunks per input tile
 constexpr int kThreads = 256;
 constexpr int kRounds = (kChunks + kThreads - 1) / kThreads;   // DMA rounds per wave
 constexpr int kBufChunks = kRounds * kThreads;                 // chunks per LDS buffer
-constexpr int kWVec = kK * 9 * 8;            // weight vectors [o][t][c/8] of 8 halves
 constexpr unsigned kOob = 0xFFFFFFF0u;
 constexpr int kPB = kTR;                     // 16-pixel blocks per wave: one per tile row
-constexpr int kStores = kTR * 2;             // 8-byte output stores per thread per tile
+constexpr int kReadSteps = (kTR + 2) * 6;    // B reads per wave and tile
+// The next tile's DMA rounds are issued during the first kIssueSteps read
+// steps; output stores issued after the last round: output row o is stored
+// (two 8-byte stores) at read step 6 * (o + 2) + 5.
+constexpr int kIssueSteps = kReadSteps * 3 / 5;
+constexpr int stores_after_last_round() {
+  const int q_last = ((kRounds - 1) * kIssueSteps) / kRounds;
+  int n = 0;
+  for (int o = 0; o < kTR; ++o)
+    if (6 * (o + 2) + 5 >= q_last) n += 2;
+  return n;
+}
+constexpr int kStores = stores_after_last_round();
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= kStores (bits 3:0 and 15:14),
 // expcnt and lgkmcnt not waited for (all ones).
 constexpr int kWaitDmaNotStores = (kStores & 0xF) | ((kStores >> 4) << 14) | (0x7 << 4) | (0xF << 8);
@@ -107,6 +118,13 @@ struct MfmaArgs {
   _Float16 *y;
   int N, H, W, relu;
   int tiles_x, tiles_y, ntiles;
+};
+
+// The DMA source of one tile: the image's buffer resource and the tile origin.
+struct TileDma {
+  __amdgpu_buffer_rsrc_t rx;
+  int y0, x0;
+  bool any;   // false: no tile to load, every round reads nothing
 };
 
 template <int SWZ>
@@ -187,24 +205,30 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     y0 = ty * kTR;
     x0 = tx * kTC;
   };
-  auto issue = [&](int tl, uint4v *buf) {
-    int n, y0, x0;
-    tile_origin(tl, n, y0, x0);
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<_Float16 *>(a.x + (size_t)n * img), (short)0, (int)(img * 2), kBufferFlags);
-#pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-      const int s = (j * 4 + wave) * 64 + lane;
-      const int ry = s / kRowSlots;
-      int cx, c;
-      chunk_at<SWZ>(s - ry * kRowSlots, cx, c);
-      const int gy = y0 - 1 + ry;
-      const int gx = x0 - 1 + cx;
-      const bool in = s < kChunks && gy >= 0 && gy < a.H && gx >= 0 && gx < a.W;
-      const unsigned off = in ? (unsigned)((((size_t)gy * a.W + gx) * kC + c * 8) * 2) : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (__attribute__((address_space(3))) void *)(buf + (j * 4 + wave) * 64), 16, off, 0, 0, 0);
-    }
+  // DMA of one tile, in rounds: round j moves LDS slots (4j + wave) * 64 + lane
+  // of a buffer. Offsets are branch-free 32-bit arithmetic (the plan keeps an
+  // image under 4 GB): the rounds of the next tile sit between the MFMAs,
+  // where a divergent branch would break the instruction stream.
+  auto dma_for = [&](int tl) -> TileDma {
+    TileDma d;
+    int n;
+    d.any = tl < hi;
+    tile_origin(d.any ? tl : 0, n, d.y0, d.x0);
+    d.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(a.x + (size_t)n * img), (short)0,
+                                             (int)(img * 2), kBufferFlags);
+    return d;
+  };
+  auto issue_round = [&](const TileDma &d, uint4v *buf, int j) {
+    const unsigned s = (unsigned)((j * 4 + wave) * 64 + lane);
+    const unsigned ry = s / kRowSlots;
+    int cx, c;
+    chunk_at<SWZ>((int)(s - ry * kRowSlots), cx, c);
+    const int gy = d.y0 - 1 + (int)ry;
+    const int gx = d.x0 - 1 + cx;
+    const bool in = d.any & (s < (unsigned)kChunks) & ((unsigned)gy < (unsigned)a.H) & ((unsigned)gx < (unsigned)a.W);
+    const unsigned off = in ? (unsigned)(((gy * a.W + gx) * kC + c * 8) * 2) : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        d.rx, (__attribute__((address_space(3))) void *)(buf + (j * 4 + wave) * 64), 16, off, 0, 0, 0);
   };
 
   // Byte offsets (inside a tile buffer) of this lane's B reads for filter column
@@ -215,7 +239,11 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) boff[v][h] = slot_in_row<SWZ>(16 * ch + n16 + v, 4 * h + g) * 16;
 
-  auto compute_store = [&](int tl, const uint4v *buf) {
+  // The next tile's DMA rounds are issued between the reads of the first 3/5
+  // of the MFMA loop (round j at read step j * kIssueSteps / kRounds): issued
+  // in a burst before the loop they delay its first MFMAs, and spread to the
+  // very end the last round's latency is exposed at the tile boundary.
+  auto compute_store = [&](int tl, const uint4v *buf, const TileDma &dn, uint4v *nbuf) {
     int n, y0, x0;
     tile_origin(tl, n, y0, x0);
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
@@ -238,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     // is issued kAhead reads early into a ring of registers; scheduling
     // barriers between reads keep the compiler from hoisting more reads than
     // the ring holds.
-    constexpr int kReads = kIR * 6;
+    constexpr int kReads = kReadSteps;
     constexpr int kAhead = 8;
     auto read_b = [&](int q) -> half8 {
       const int i = q / 6, v = (q % 6) >> 1, h = q & 1;
@@ -250,6 +278,16 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     for (int q = 0; q < kAhead; ++q) ring[q] = read_b(q);
     static_for<kReads>([&](auto qc) __attribute__((always_inline)) {
       constexpr int q = decltype(qc)::value;
+      // rounds issued at this step: j with j * kIssueSteps / kRounds == q
+      constexpr int j0 = q < kIssueSteps ? (q * kRounds + kIssueSteps - 1) / kIssueSteps : kRounds;
+      constexpr int j1 = q < kIssueSteps ? ((q + 1) * kRounds + kIssueSteps - 1) / kIssueSteps : kRounds;
+      if constexpr (j1 > j0) {
+#pragma unroll
+        for (int j = j0; j < j1; ++j) issue_round(dn, nbuf, j);
+        // keeps the rounds ahead of this step's stores (the tile-end wait
+        // counts the stores issued after the last round)
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const half8 b = ring[q % kAhead];
       if constexpr (q + kAhead < kReads) ring[q % kAhead] = read_b(q + kAhead);
       constexpr int i = q / 6, v = (q % 6) >> 1, h = q & 1;
@@ -282,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
             hv[e] = (_Float16)r;
           }
           const unsigned off =
-              (gy < a.H && col_in) ? (unsigned)gy * row_bytes + col_off + 32u * ob : kOob;
+              ((gy < a.H) & col_in) ? (unsigned)gy * row_bytes + col_off + 32u * ob : kOob;
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, hv), ry, off, 0, 0);
         }
       }
@@ -290,17 +328,19 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     });
   };
 
-  if (tile < hi) issue(tile, lds);
+  {
+    const TileDma d0 = dma_for(tile);
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) issue_round(d0, lds, j);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int cur = 0;
   while (tile < hi) {
     const int next = tile + step;
-    if (next < hi) issue(next, lds + (cur ^ 1) * kBufChunks);
-    compute_store(tile, lds + cur * kBufChunks);
-    // Wait for the next tile's DMA but not for this tile's output stores:
-    // vector-memory operations retire in issue order on gfx9, and the stores
-    // (kStores per thread) were issued after the DMA.
+    compute_store(tile, lds + cur * kBufChunks, dma_for(next), lds + (cur ^ 1) * kBufChunks);
+    // Wait for the next tile's DMA but not for the output stores issued after
+    // its last round: vector-memory operations retire in issue order on gfx9.
     __builtin_amdgcn_s_waitcnt(kWaitDmaNotStores);
     __syncthreads();
     tile = next;

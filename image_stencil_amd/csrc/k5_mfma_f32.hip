@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
           r[e] = acc[o][e] + bv;
           if (a.relu) r[e] = fmaxf(r[e], 0.f);
         }
-        const unsigned off = (gy < H && col_in) ? col_off + (unsigned)gy * (unsigned)W * 4u : kOob;
+        const unsigned off = ((gy < H) & col_in) ? col_off + (unsigned)gy * (unsigned)W * 4u : kOob;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4v, float4v{r[0], r[1], r[2], r[3]}),
                                                ry, off, 0, 0);
       }
