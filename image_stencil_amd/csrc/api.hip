@@ -166,17 +166,37 @@ size_t chain_buffer_bytes(const conv_chain_desc *d) {
   return align256(m);
 }
 
+// Workspace of the layer-by-layer path: ping-pong buffers for the
+// intermediates; a single layer without depth-to-space writes straight to y.
+size_t unfused_bytes(const conv_chain_desc *d) {
+  const int need = (d->n_layers == 1 && d->depth_to_space == 1) ? 0 : (d->n_layers == 1 ? 1 : 2);
+  return need * chain_buffer_bytes(d);
+}
+
+// Workspace that conv_chain_forward wants for the chain and mode: none for the
+// fused kernel; IS_CHAIN_AUTO asks for the layer-by-layer workspace, which
+// enables the faster path (on MI355X the layer-by-layer chain, with its
+// 32 -> 32 layers on the fp32 MFMA kernel, beats the fused kernel, whose
+// overlapped windows recompute about a quarter of the work).
 is_status chain_workspace(const conv_chain_desc *d, const conv2d_desc *ld, size_t *bytes) {
-  if (d->mode != IS_CHAIN_UNFUSED && chain_fusable(d, ld)) {
+  if (d->mode == IS_CHAIN_FUSED) {
+    if (!chain_fusable(d, ld)) return IS_ERR_UNSUPPORTED;
     *bytes = 0;
     return IS_OK;
   }
-  if (d->mode == IS_CHAIN_FUSED) return IS_ERR_UNSUPPORTED;
-  // Ping-pong buffers for the intermediates; a single layer without
-  // depth-to-space writes straight to y.
-  const int need = (d->n_layers == 1 && d->depth_to_space == 1) ? 0 : (d->n_layers == 1 ? 1 : 2);
-  *bytes = need * chain_buffer_bytes(d);
+  *bytes = unfused_bytes(d);
   return IS_OK;
+}
+
+// Whether conv_chain_forward runs the fused kernel: always in IS_CHAIN_FUSED;
+// in IS_CHAIN_AUTO when the workspace falls short of the layer-by-layer need
+// and the chain has a fused kernel.
+bool runs_fused(const conv_chain_desc *d, const conv2d_desc *ld, const void *workspace,
+                size_t workspace_bytes) {
+  if (d->mode == IS_CHAIN_FUSED) return true;
+  if (d->mode == IS_CHAIN_UNFUSED || !chain_fusable(d, ld)) return false;
+  const size_t need = unfused_bytes(d);
+  return need > 0 && (!workspace || workspace_bytes < need);
 }
 
 }  // namespace
@@ -199,7 +219,8 @@ is_status conv_chain_kernel_name(const conv_chain_desc *d, char *name, size_t le
   size_t ws = 0;
   const is_status st2 = chain_workspace(d, ld, &ws);
   if (st2 != IS_OK) return st2;
-  const bool fused = d->mode != IS_CHAIN_UNFUSED && chain_fusable(d, ld);
+  // the path taken when the caller passes the workspace reported above
+  const bool fused = d->mode == IS_CHAIN_FUSED;
   snprintf(name, len, "%s", fused ? "is_k3_chain" : "layer_by_layer");
   return IS_OK;
 }
@@ -223,13 +244,15 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void
     size_t need = 0;
     st = chain_workspace(d, ld, &need);
     if (st != IS_OK) return st;
+    const bool fused = runs_fused(d, ld, workspace, workspace_bytes);
+    if (fused) need = 0;
     if (need > 0 && (!workspace || workspace_bytes < need)) return IS_ERR_WORKSPACE;
     if (need > 0 && misaligned(workspace)) return IS_ERR_MISALIGNED;
     if (need > 0 && (overlap(workspace, need, x, xb) || overlap(workspace, need, y, yb)))
       return IS_ERR_INVALID_ARG;
     if (xb == 0 || yb == 0) return IS_OK;
 
-    if (need == 0 && d->mode != IS_CHAIN_UNFUSED && chain_fusable(d, ld))
+    if (fused)
       return hip_status(is::launch_chain_fused(d, static_cast<const float *>(x),
                                                reinterpret_cast<const float *const *>(w), b,
                                                static_cast<float *>(y), stream));

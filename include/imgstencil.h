@@ -130,7 +130,8 @@ is_status conv2d_get_plan_info(conv2d_plan plan, conv2d_plan_info *info);
 typedef struct { int c, k, r, s, relu; } conv_layer_desc;
 
 typedef enum {
-  IS_CHAIN_AUTO = 0,     /* fused when a fused kernel exists for the chain, else layer by layer */
+  IS_CHAIN_AUTO = 0,     /* layer by layer when the workspace allows it (the faster path on
+                            MI355X), else the fused kernel if the chain has one */
   IS_CHAIN_FUSED = 1,    /* fused only (IS_ERR_UNSUPPORTED if no fused kernel fits) */
   IS_CHAIN_UNFUSED = 2   /* one conv2d launch per layer through the workspace */
 } is_chain_mode;
@@ -143,8 +144,10 @@ typedef struct {
   is_chain_mode mode;
 } conv_chain_desc;
 
-/* Device bytes of workspace conv_chain_forward needs for this chain and mode
- * (0 for the fused kernel; two intermediate tensors for layer by layer). */
+/* Device bytes of workspace conv_chain_forward wants for this chain and mode:
+ * 0 for IS_CHAIN_FUSED; the two intermediate tensors of the layer-by-layer
+ * path for IS_CHAIN_UNFUSED and IS_CHAIN_AUTO (with less, AUTO runs the fused
+ * kernel when the chain has one, and fails with IS_ERR_WORKSPACE otherwise). */
 is_status conv_chain_workspace_size(const conv_chain_desc *d, size_t *bytes);
 
 /* Enqueue the chain on `stream`.
@@ -159,8 +162,9 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x,
                              void *y, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
-/* Name of the kernel family conv_chain_forward launches for this chain
- * ("is_k3_chain" when fused), copied into name[0..len-1]. */
+/* Name of the kernel family conv_chain_forward launches for this chain when
+ * given the workspace conv_chain_workspace_size reports ("is_k3_chain" when
+ * fused, "layer_by_layer" otherwise), copied into name[0..len-1]. */
 is_status conv_chain_kernel_name(const conv_chain_desc *d, char *name, size_t len);
 
 /* LDS bytes of an input tile that covers tile_w x tile_h outputs of a filter

@@ -77,14 +77,35 @@ def test_other_chains_run_layer_by_layer():
     check(y, ref, m, TAU_F32, "2-layer chain")
 
 
+def test_auto_mode_uses_workspace_when_given():
+    """AUTO runs layer by layer with the workspace it reports and falls back to
+    the fused kernel without one; both match the oracle."""
+    import torch
+    x, layers = synth.chain_f32(N=1, H=30, W=72, seed=12)
+    d = isa.make_chain_desc(1, 30, 72, _spec(layers), 2, isa.IS_CHAIN_AUTO)
+    ws = isa.conv_chain_workspace_size(d)
+    assert ws >= 2 * 4 * 32 * 30 * 72
+    assert isa.conv_chain_kernel_name(d) == "layer_by_layer"
+    ref, m = oracle.chain(x, layers, d2s=2)
+    xd = dev(x)
+    wl = [(dev(w), dev(b)) for (w, b, _) in layers]
+    for ws_given in (ws, 0):
+        y = torch.full((1, 1, 60, 144), float("nan"), dtype=torch.float32, device="cuda")
+        buf = torch.empty(max(ws_given, 1), dtype=torch.uint8, device="cuda")
+        isa.conv_chain_forward(d, xd.data_ptr(), [w.data_ptr() for (w, _) in wl], [b.data_ptr() for (_, b) in wl],
+                               y.data_ptr(), buf.data_ptr() if ws_given else None, ws_given,
+                               torch.cuda.current_stream().cuda_stream)
+        check(host(y), ref, m, TAU_F32, "auto, workspace %d" % ws_given)
+
+
 def test_upscale_chain_720p_sampled():
     """The 1280x720 frame through the fused kernel, checked on windows at the
     frame corners and edges, on strip and block boundaries, and inside."""
     x, layers = synth.chain_f32()
-    d = isa.make_chain_desc(1, 720, 1280, _spec(layers), 2, isa.IS_CHAIN_AUTO)
+    d = isa.make_chain_desc(1, 720, 1280, _spec(layers), 2, isa.IS_CHAIN_FUSED)
     assert isa.conv_chain_kernel_name(d) == "is_k3_chain"
     say("chain 720p")
-    y = _gpu_chain(x, layers, isa.IS_CHAIN_AUTO)
+    y = _gpu_chain(x, layers, isa.IS_CHAIN_FUSED)
     assert y.shape == (1, 1, 1440, 2560) and np.isfinite(y).all()
     wins = [(0, 12, 0, 64), (708, 720, 1216, 1280), (0, 8, 1240, 1280), (712, 720, 0, 40),
             (60, 76, 100, 124), (64, 72, 44, 76), (132, 140, 552, 568), (350, 366, 600, 680),

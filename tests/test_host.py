@@ -231,3 +231,11 @@ def test_chain_descriptor_checks():
     one = isa.make_chain_desc(1, 16, 16, [(1, 4, 3, False)], depth_to_space=1,
                               mode=isa.IS_CHAIN_UNFUSED)
     assert isa.conv_chain_workspace_size(one) == 0
+    # the upscaling chain: AUTO asks for the layer-by-layer workspace, FUSED for none
+    spec = [(1, 32, 5, True), (32, 32, 3, True), (32, 32, 3, True), (32, 4, 3, False)]
+    auto = isa.make_chain_desc(1, 720, 1280, spec, 2, isa.IS_CHAIN_AUTO)
+    assert isa.conv_chain_workspace_size(auto) == 2 * 4 * 32 * 720 * 1280
+    assert isa.conv_chain_kernel_name(auto) == "layer_by_layer"
+    fused = isa.make_chain_desc(1, 720, 1280, spec, 2, isa.IS_CHAIN_FUSED)
+    assert isa.conv_chain_workspace_size(fused) == 0
+    assert isa.conv_chain_kernel_name(fused) == "is_k3_chain"
