@@ -7,7 +7,7 @@
 // convolution that "Optimizing Memory Efficiency for Convolution Kernels on
 // Kepler GPUs" contrasts with its direct method; here the wide-channel layer
 // really is that contraction, so it runs on MFMA). Design:
-//  * persistent workgroups of 4 waves, one per CU; each loops over 16 x 32 pixel
+//  * persistent workgroups, one per CU; each loops over 16 x 32 pixel
 //    tiles of an image, tiles of one XCD being neighbours so halo re-reads hit
 //    that XCD's L2;
 //  * the input tile with its 1-pixel halo (18 x 34 pixels x 128 bytes) streams
@@ -17,23 +17,28 @@
 //    XOR swizzle of "CUDA shared memory swizzling" (its formula, with 16-byte
 //    elements and chunks) over rows of SWZ bytes, so that 16 lanes reading the
 //    same chunk of 16 consecutive pixels hit distinct banks;
-//  * wave w owns output channels 32*(w&1) .. +32 (two 16-row A blocks) for the
-//    16 columns 16*(w>>1) .. +16 of all 16 tile rows; its 36 weight fragments
-//    (all 576 k) stay in registers for the whole kernel;
+//  * 8 waves, 2 per SIMD: wave w owns the 16 output channels 16*(w%4) .. +16
+//    (one A block) for the 16 columns 16*(w/4) .. +16 of all 16 tile rows; its
+//    18 weight fragments (all 576 k) stay in registers. Two waves per SIMD
+//    let one wave's MFMAs run while the other waits for its LDS reads (a
+//    build with 2 A blocks per wave and 4 waves is kept behind OB_PER_WAVE);
 //  * v_mfma_f32_16x16x32_f16: A = 16 output channels x 32 k (weights), B = 32 k
 //    x 16 pixels (one 16-byte LDS read per lane), D = 4 consecutive output
 //    channels of one pixel per lane;
 //  * rolling rows, as in the single-channel kernel: the B fragment of input
 //    row i (tap column v, channel half h) is read once and feeds the output rows
 //    i, i-1 and i-2 through filter rows 0, 1 and 2, so a wave reads 18 x 6
-//    fragments per tile instead of 16 x 18 (LDS read bandwidth, not the matrix
-//    cores, bounded the one-read-per-tap order);
+//    fragments per tile instead of 16 x 18;
 //  * an output row is final once input row +2 has been read: it gets the fp32
 //    bias, the optional ReLU and fp16 rounding (nearest even) and is stored
 //    from the accumulators inside the MFMA loop, so stores overlap the matrix
 //    work and the tile needs no epilogue phase.
 #include "common.hpp"
 #include "internal.hpp"
+
+#ifndef OB_PER_WAVE
+#define OB_PER_WAVE 1
+#endif
 
 namespace is {
 namespace {
@@ -48,8 +53,15 @@ constexpr int kK = 64;                       // output channels
 constexpr int kTR = 16, kTC = 32;            // output tile: rows x columns
 constexpr int kIR = kTR + 2, kIC = kTC + 2;  // input tile with halo
 constexpr int kChunks = kIR * kIC * 8;       // 16-byte chunks per input tile
-constexpr int kThreads = 256;
-constexpr int kRounds = (kChunks + kThreads - 1) / kThreads;   // DMA rounds per wave
+// Output-channel blocks of 16 per wave. With 1, each wave holds 16 output
+// channels (72 weight VGPRs, 64 accumulators) and the workgroup has 8 waves,
+// 2 per SIMD, so one wave's MFMAs run while the other waits for its LDS reads;
+// with 2, a B read feeds twice the MFMAs but each SIMD has a single wave.
+constexpr int kOB = OB_PER_WAVE;
+constexpr int kGroups = kK / (16 * kOB);     // output-channel groups
+constexpr int kWaves = kGroups * 2;          // x 2 tile-column halves
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRounds = (kChunks + kThreads - 1) / kThreads;   // DMA rounds per thread
 constexpr int kBufChunks = kRounds * kThreads;                 // chunks per LDS buffer
 constexpr unsigned kOob = 0xFFFFFFF0u;
 constexpr int kPB = kTR;                     // 16-pixel blocks per wave: one per tile row
@@ -62,7 +74,7 @@ constexpr int stores_after_last_round() {
   const int q_last = ((kRounds - 1) * kIssueSteps) / kRounds;
   int n = 0;
   for (int o = 0; o < kTR; ++o)
-    if (6 * (o + 2) + 5 >= q_last) n += 2;
+    if (6 * (o + 2) + 5 >= q_last) n += kOB;
   return n;
 }
 constexpr int kStores = stores_after_last_round();
@@ -136,15 +148,15 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   const int lane = tid & 63;
   const int n16 = lane & 15;     // pixel (B, D) or output channel (A) inside a 16-block
   const int g = lane >> 4;       // k group of 8 (A, B) or channel group of 4 (D)
-  const int oh = wave & 1;       // output-channel half
-  const int ch = wave >> 1;      // tile-column half: columns 16*ch .. 16*ch+15
+  const int og = wave % kGroups;  // output channels 16*kOB*og .. +16*kOB
+  const int ch = wave / kGroups;  // tile-column half: columns 16*ch .. 16*ch+15
 
   // ---- Weights: copy the KCRS tensor into LDS with 16-byte loads, each output
   // channel's 576 halves on a row of 1168 bytes (16 bytes of padding spread
   // the 16 channels a fragment read touches over distinct banks); then every
   // lane gathers its 36 A fragments (2 channel blocks x 18 k steps): fragment
   // (ob, ks) holds channels 32h + 8g .. +8 of tap t = ks/2 for output channel
-  // 32*oh + 16*ob + n16, i.e. 8 halves 9 apart in the channel's row.
+  // 16*(kOB*og + ob) + n16, i.e. 8 halves 9 apart in the channel's row.
   constexpr int kWRow = kC * 9 * 2 + 16;   // bytes per padded weight row
   {
     const __amdgpu_buffer_rsrc_t rw =
@@ -166,14 +178,14 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     }
   }
   __syncthreads();
-  half8 wa[2][18];
+  half8 wa[kOB][18];
   {
     const char *wl = reinterpret_cast<const char *>(lds);
 #pragma unroll
-    for (int ob = 0; ob < 2; ++ob)
+    for (int ob = 0; ob < kOB; ++ob)
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        const int o = 32 * oh + 16 * ob + n16;
+        const int o = 16 * (kOB * og + ob) + n16;
         const int t = ks >> 1, h = ks & 1;
         const _Float16 *src =
             reinterpret_cast<const _Float16 *>(wl + o * kWRow) + (32 * h + 8 * g) * 9 + t;
@@ -181,11 +193,11 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
         for (int j = 0; j < 8; ++j) wa[ob][ks][j] = src[9 * j];
       }
   }
-  float bias[2][4];
+  float bias[kOB][4];
 #pragma unroll
-  for (int ob = 0; ob < 2; ++ob)
+  for (int ob = 0; ob < kOB; ++ob)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bias[ob][i] = a.bias ? a.bias[32 * oh + 16 * ob + 4 * g + i] : 0.f;
+    for (int i = 0; i < 4; ++i) bias[ob][i] = a.bias ? a.bias[16 * (kOB * og + ob) + 4 * g + i] : 0.f;
   __syncthreads();
 
   // ---- Tile schedule: XCD x (= blockIdx mod 8) walks its own contiguous range.
@@ -219,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     return d;
   };
   auto issue_round = [&](const TileDma &d, uint4v *buf, int j) {
-    const unsigned s = (unsigned)((j * 4 + wave) * 64 + lane);
+    const unsigned s = (unsigned)((j * kWaves + wave) * 64 + lane);
     const unsigned ry = s / kRowSlots;
     int cx, c;
     chunk_at<SWZ>((int)(s - ry * kRowSlots), cx, c);
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     const bool in = d.any & (s < (unsigned)kChunks) & ((unsigned)gy < (unsigned)a.H) & ((unsigned)gx < (unsigned)a.W);
     const unsigned off = in ? (unsigned)(((gy * a.W + gx) * kC + c * 8) * 2) : kOob;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        d.rx, (__attribute__((address_space(3))) void *)(buf + (j * 4 + wave) * 64), 16, off, 0, 0, 0);
+        d.rx, (__attribute__((address_space(3))) void *)(buf + (j * kWaves + wave) * 64), 16, off, 0, 0, 0);
   };
 
   // Byte offsets (inside a tile buffer) of this lane's B reads for filter column
@@ -253,13 +265,13 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     // when the column is outside the image; row gy adds gy * W * 128 bytes.
     const int gx = x0 + 16 * ch + n16;
     const bool col_in = gx < a.W;
-    const unsigned col_off = (unsigned)(gx * kK + 32 * oh + 4 * g) * 2u;
+    const unsigned col_off = (unsigned)(gx * kK + 16 * kOB * og + 4 * g) * 2u;
     const unsigned row_bytes = (unsigned)a.W * kK * 2u;
-    float4v acc[kPB][2];
+    float4v acc[kPB][kOB];
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb)
 #pragma unroll
-      for (int ob = 0; ob < 2; ++ob) acc[pb][ob] = float4v{0.f, 0.f, 0.f, 0.f};
+      for (int ob = 0; ob < kOB; ++ob) acc[pb][ob] = float4v{0.f, 0.f, 0.f, 0.f};
     // Reads go in (input row i, tap column v, channel half h) order; read i
     // feeds output rows i - u, u = 0..2 (those inside the tile), with the A
     // fragment of k step 2(3u + v) + h, for both output-channel blocks. Each read
@@ -297,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
         if (o >= 0 && o < kTR) {
           const int ks = 2 * (3 * u + v) + h;
 #pragma unroll
-          for (int ob = 0; ob < 2; ++ob)
+          for (int ob = 0; ob < kOB; ++ob)
             acc[o][ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[ob][ks], b, acc[o][ob], 0, 0, 0);
         }
       }
@@ -311,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
         constexpr int o = i - 2;
         const int gy = y0 + o;
 #pragma unroll
-        for (int ob = 0; ob < 2; ++ob) {
+        for (int ob = 0; ob < kOB; ++ob) {
           _Float16 hv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
