@@ -161,6 +161,71 @@ def stats_summary(trace_dir):
     return "\n".join(lines) + "\n"
 
 
+LDS_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS")
+
+
+def lds_study(torch, isa, synth, stream, stream_obj, steps, warmup):
+    """The LDS-staged kernels for a counter run of their bank conflicts: the fp16
+    layer under each swizzle of its input tile (IMGSTENCIL_K4_SWIZZLE, read at
+    plan creation; the kernel is instantiated per swizzle, so the profiler sees
+    is_k4_mfma<0>, <128> and <256>), the fp32 layer and the fused chain."""
+    out = []
+    x, w, b = synth.cnn_layer_f16_nhwc()
+    xd, wd, bd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
+    yd = torch.empty((8, 256, 256, 64), dtype=torch.float16, device="cuda")
+    for swz in (0, 128, 256):
+        os.environ["IMGSTENCIL_K4_SWIZZLE"] = str(swz)
+        plan = isa.Plan(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16", False))
+        del os.environ["IMGSTENCIL_K4_SWIZZLE"]
+        c = Case("fp16 layer, swizzle %d" % swz,
+                 lambda plan=plan: isa.conv2d_forward(plan.handle, xd.data_ptr(), wd.data_ptr(), bd.data_ptr(),
+                                                      yd.data_ptr(), stream),
+                 0, 1, plan.info()["kernel"])
+        _, per, _ = _time_cases(torch, [c], steps, warmup, stream_obj)
+        out.append({"case": c.name, "swizzle_row_bytes": swz, "ms": round(per[0], 4)})
+    x, w, b = synth.cnn_layer_f32()
+    c = _layer_cases(torch, isa, stream, x, w, b, True, 1, "fp32 layer")[0]
+    _, per, _ = _time_cases(torch, [c], steps, warmup, stream_obj)
+    out.append({"case": c.name, "kernel": c.kernel, "ms": round(per[0], 4)})
+    x, layers = synth.chain_f32()
+    spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
+    d = isa.make_chain_desc(1, 720, 1280, spec, 2, isa.IS_CHAIN_FUSED)
+    xd = torch.from_numpy(x).cuda()
+    wl = [(torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()) for (w, b, _) in layers]
+    yc = torch.empty((1, 1, 1440, 2560), dtype=torch.float32, device="cuda")
+    c = Case("fused chain", lambda: isa.conv_chain_forward(d, xd.data_ptr(), [w.data_ptr() for (w, _) in wl],
+                                                           [b.data_ptr() for (_, b) in wl], yc.data_ptr(), None, 0,
+                                                           stream), 0, 1, "is_k3_chain")
+    _, per, _ = _time_cases(torch, [c], steps, warmup, stream_obj)
+    out.append({"case": c.name, "kernel": c.kernel, "ms": round(per[0], 4)})
+    return out
+
+
+def pmc_lds_summary(pmc_dir):
+    """Markdown summary of a counter run of --lds-study: LDS counters per dispatch
+    of each LDS-staged kernel."""
+    tabs = {c: _counter_means(pmc_dir, c) for c in LDS_COUNTERS}
+    kernels = [k for k in sorted(tabs[LDS_COUNTERS[0]]) if k.startswith("is_k")]
+    lines = ["# LDS bank conflicts of the LDS-staged kernels", "",
+             "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
+             "rocprofv3 --pmc %s --output-format csv -d %s -o run -- \\" % (" ".join(LDS_COUNTERS), pmc_dir),
+             "    python3 bench.py --lds-study --steps 2 --warmup 1 --min-warm-s 0",
+             "python3 bench.py --pmc-lds-summary %s > profiles/lds_bank_conflicts.md" % pmc_dir,
+             "```", "",
+             "Counter values per dispatch (cycles or instructions summed over the chip), averaged over the",
+             "dispatches of each kernel. The fp16 layer runs once per swizzle of its input tile (row bytes",
+             "0 = plain, 128, 256; the plan picks 128). conflict share = SQ_LDS_BANK_CONFLICT /",
+             "SQ_LDS_IDX_ACTIVE.", "",
+             "| kernel | dispatches | " + " | ".join(LDS_COUNTERS) + " | conflict share |",
+             "|---|---|" + "---|" * len(LDS_COUNTERS) + "---|"]
+    for k in kernels:
+        vals = [tabs[c].get(k, (0.0, 0, ""))[0] for c in LDS_COUNTERS]
+        share = vals[0] / vals[1] if vals[1] else 0.0
+        lines.append("| `%s` | %d | %s | %.3f |" % (k, tabs[LDS_COUNTERS[0]][k][1],
+                                                    " | ".join("%.0f" % v for v in vals), share))
+    return "\n".join(lines) + "\n"
+
+
 def _traffic(case):
     """Counter-derived HBM bytes per launch of a bench case, or None when absent
     or taken with other kernel sources than the current ones."""
@@ -434,6 +499,11 @@ def main():
     ap.add_argument("--stats-summary", metavar="TRACE_DIR",
                     help="print the kernel-duration summary of a rocprofv3 --kernel-trace --stats run of "
                          "this script and exit (no GPU needed)")
+    ap.add_argument("--lds-study", action="store_true",
+                    help="time only the LDS-staged kernels (fp16 layer under each swizzle, fp32 layer, fused "
+                         "chain), for a counter run of their bank conflicts")
+    ap.add_argument("--pmc-lds-summary", metavar="PMC_DIR",
+                    help="print the LDS counter summary of a rocprofv3 --pmc run of --lds-study and exit")
     args = ap.parse_args()
     globals()["MIN_WARM_S"] = args.min_warm_s
     if args.pmc_summary:
@@ -441,6 +511,9 @@ def main():
         return
     if args.stats_summary:
         sys.stdout.write(stats_summary(args.stats_summary))
+        return
+    if args.pmc_lds_summary:
+        sys.stdout.write(pmc_lds_summary(args.pmc_lds_summary))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -455,6 +528,11 @@ def main():
     torch.cuda.init()
     stream_obj = torch.cuda.current_stream()
     stream = stream_obj.cuda_stream
+
+    if args.lds_study:
+        print(json.dumps({"study": "lds", "results": lds_study(torch, isa, synth, stream, stream_obj, args.steps,
+                                                                args.warmup)}), flush=True)
+        return
 
     cases = _single_large_cases(torch, isa, synth, stream)
     ms_step, per, wall = _time_cases(torch, cases, args.steps, args.warmup, stream_obj)

@@ -36,6 +36,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <stdlib.h>
+
 #ifndef OB_PER_WAVE
 #define OB_PER_WAVE 1
 #endif
@@ -384,7 +386,14 @@ bool configure_mfma(Plan &p) {
   p.lds = 2 * kBufChunks * 16;
   p.tile_w = kTC;
   p.tile_h = kTR;
-  p.vec = 128;   // swizzle row bytes (fewest SQ_LDS_BANK_CONFLICT cycles of 0, 128, 256)
+  // Swizzle row bytes: 128 gives the fewest SQ_LDS_BANK_CONFLICT cycles of 0,
+  // 128 and 256. IMGSTENCIL_K4_SWIZZLE=0|128|256 overrides it (read when the
+  // plan is created) so that the three layouts can be measured.
+  p.vec = 128;
+  if (const char *e = getenv("IMGSTENCIL_K4_SWIZZLE")) {
+    const int v = atoi(e);
+    if (v == 0 || v == 128 || v == 256) p.vec = v;
+  }
   return true;
 }
 
