@@ -98,18 +98,22 @@ def test_auto_mode_uses_workspace_when_given():
         check(host(y), ref, m, TAU_F32, "auto, workspace %d" % ws_given)
 
 
-def test_upscale_chain_720p_sampled():
-    """The 1280x720 frame through the fused kernel, checked on windows at the
-    frame corners and edges, on strip and block boundaries, and inside."""
+@pytest.mark.parametrize("mode", ["fused", "auto"])
+def test_upscale_chain_720p_sampled(mode):
+    """The 1280x720 frame through the fused kernel, and through AUTO with its
+    workspace (layer by layer, the 32 -> 32 layers on the fp32 MFMA kernel),
+    checked on windows at the frame corners and edges, on strip, block and tile
+    boundaries, and inside."""
     x, layers = synth.chain_f32()
-    d = isa.make_chain_desc(1, 720, 1280, _spec(layers), 2, isa.IS_CHAIN_FUSED)
-    assert isa.conv_chain_kernel_name(d) == "is_k3_chain"
-    say("chain 720p")
-    y = _gpu_chain(x, layers, isa.IS_CHAIN_FUSED)
+    m_ = isa.IS_CHAIN_FUSED if mode == "fused" else isa.IS_CHAIN_AUTO
+    d = isa.make_chain_desc(1, 720, 1280, _spec(layers), 2, m_)
+    assert isa.conv_chain_kernel_name(d) == ("is_k3_chain" if mode == "fused" else "layer_by_layer")
+    say("chain 720p", mode)
+    y = _gpu_chain(x, layers, m_)
     assert y.shape == (1, 1, 1440, 2560) and np.isfinite(y).all()
     wins = [(0, 12, 0, 64), (708, 720, 1216, 1280), (0, 8, 1240, 1280), (712, 720, 0, 40),
             (60, 76, 100, 124), (64, 72, 44, 76), (132, 140, 552, 568), (350, 366, 600, 680),
-            (203, 207, 1100, 1180)]
+            (203, 207, 1100, 1180), (10, 14, 28, 36), (346, 350, 632, 644)]
     worst = 0.0
     for (i0, i1, j0, j1) in wins:
         z, m = oracle.chain_window(x, layers, i0, i1, j0, j1)
