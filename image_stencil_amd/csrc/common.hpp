@@ -30,6 +30,18 @@ __device__ __forceinline__ float from_next_lane(float src, float old) {
                                                     kDppWaveShl1, 0xf, 0xf, false));
 }
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations
+// (lgkmcnt 0) but not for its vector-memory operations, so that loads into
+// another LDS buffer stay in flight across it (__syncthreads() waits for
+// those too). The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Workgroups are dealt to the 8 XCDs of the chip round-robin in launch order,
 // and each XCD has its own L2. Renumber launch index b so that XCD k receives
 // the contiguous logical range [k*T/8, (k+1)*T/8) of the first 8*floor(T/8)

@@ -3,8 +3,9 @@
 fp16 inputs and weights, fp32 bias and accumulation, fp16 output rounded to
 nearest even: |y - y_ref| <= 2e-3 * m per element, m = sum |w*x| + |b|. The
 oracle consumes the same fp16 values, widened exactly. Shapes cover exact and
-ragged 8x32 tiles, single pixels, batches, and the full 8x256x256x64 layer on
-whole sampled rows.
+ragged 64-row x 32-column units (and the 4-row stages inside them), single
+pixels, batches, more units than workgroups, and the full 8x256x256x64 layer
+on whole sampled rows.
 """
 import numpy as np
 import pytest
@@ -30,7 +31,8 @@ def _run(x, w, b, relu, expect=None):
     return host(y)
 
 
-@pytest.mark.parametrize("N,H,W", [(1, 8, 32), (2, 20, 40), (1, 1, 1), (1, 9, 33), (3, 17, 70), (1, 64, 64)])
+@pytest.mark.parametrize("N,H,W", [(1, 8, 32), (2, 20, 40), (1, 1, 1), (1, 9, 33), (3, 17, 70), (1, 64, 64),
+                                   (1, 130, 96), (2, 65, 33), (1, 66, 31)])
 @pytest.mark.parametrize("relu", [False, True])
 def test_mfma_layer_shapes(N, H, W, relu):
     x, w, b = synth.cnn_layer_f16_nhwc(N=N, H=H, W=W, seed=N * 100 + H + W)
@@ -81,4 +83,20 @@ def test_mfma_layer_8x256x256_sampled():
     ref, m = oracle.conv2d_points(x, w, b, False, pts, "NHWC")
     got = y[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
     ratio = check(got, ref, m, TAU_F16, "8x256x256 layer")
+    say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))
+
+
+def test_mfma_layer_more_units_than_workgroups():
+    """3 x 700 x 260: 3 * 11 * 9 = 297 units on 256 workgroups, so some
+    workgroups run two units back to back; rows on unit and stage edges."""
+    x, w, b = synth.cnn_layer_f16_nhwc(N=3, H=700, W=260, seed=11)
+    say("mfma 3x700x260")
+    y = _run(x, w, b, True, "is_k4_mfma")
+    assert np.isfinite(y.astype(np.float32)).all()
+    rows = [0, 1, 3, 4, 62, 63, 64, 65, 127, 128, 639, 640, 698, 699]
+    cols = list(range(0, 260, 7)) + [31, 32, 255, 256, 259]
+    pts = np.array([(n, k, i, j) for n in range(3) for i in rows for j in cols for k in range(0, 64, 5)], np.int64)
+    ref, m = oracle.conv2d_points(x, w, b, True, pts, "NHWC")
+    got = y[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
+    ratio = check(got, ref, m, TAU_F16, "3x700x260 layer")
     say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))
