@@ -18,8 +18,8 @@
 //    stages, 5 stages (20 rows) ahead of the stage being read: no tile-sized
 //    double buffer that must be complete at a tile boundary. A row is 32
 //    pixels x 128 bytes, with its two halo pixels stored after them; each wave
-//    moves half a row per stage plus one halo pixel (an 8-lane DMA). Pixels
-//    outside the image read as 0 through the buffer range check;
+//    moves half a row per stage plus the row's halo pixels. Pixels outside the
+//    image read as 0 through the buffer range check;
 //  * LDS holds each pixel's 64 channels as eight 16-byte chunks, permuted by the
 //    XOR swizzle of "CUDA shared memory swizzling" (its formula, with 16-byte
 //    elements and chunks) over rows of SWZ bytes, so that 16 lanes reading the
@@ -80,11 +80,13 @@ constexpr int kNonTemporal = 2;
 static_assert(kWaves == 2 * kS, "each wave moves half of one row of a stage");
 static_assert(kS * kOutRowBytes == kWaves * 2 * 1024, "each wave stores two 1 KB pieces of a stage");
 
-// Weights are staged once, in ring slots 2.. and the staging area, while the
-// DMA of the unit's first two stages fills slots 0 and 1.
+// Weights are staged once, in ring slots kPreStages.. and the staging area,
+// while the DMA of the first unit's first kPreStages stages fills the slots
+// before them.
+constexpr int kPreStages = 3;
 constexpr int kWRow = kC * 9 * 2 + 16;        // bytes per padded weight row
-constexpr int kWStage = 2 * kStageBytes;
-static_assert(kWStage + kK * kWRow <= kLdsBytes, "weights fit beside the first two stages");
+constexpr int kWStage = kPreStages * kStageBytes;
+static_assert(kWStage + kK * kWRow <= kLdsBytes, "weights fit beside the first stages");
 
 // ---- VMEM operations of one wave, in program order, per unit:
 //   prologue: DMA of stages 0 .. kD-1 (3 operations each, nothing in between);
@@ -184,15 +186,19 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   const unsigned pix_row_bytes = (unsigned)a.W * kC * 2u;
 
   // ---- DMA of one stage: wave w moves row w/2 of the stage, pixels
-  // 16*(w%2) .. +16 (two 1 KB operations, 64 slots each) and one halo pixel
-  // (left for even w, right for odd; 8 lanes). Offsets are branch-free 32-bit
-  // arithmetic (the plan keeps an image under 4 GB).
+  // 16*(w%2) .. +16 (two 1 KB operations, 64 slots each), and the row's two
+  // halo pixels (one 4-byte-per-lane operation: 64 x 4 bytes = both 128-byte
+  // pixels, the whole halo part of the row). Both waves of a row load its halo:
+  // they write the same bytes to the same place, which keeps every wave's
+  // operation count equal and the instruction stream free of branches.
+  // Offsets are branch-free 32-bit arithmetic (the plan keeps an image under
+  // 4 GB).
   const int drow = wave >> 1;
   const int dhalf = wave & 1;
   int dpx[2], dc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) chunk_at<SWZ>(128 * dhalf + 64 * j + lane, dpx[j], dc[j]);
-  const int hpx = dhalf ? kTC : -1;
+  const int hpx = (lane >> 5) ? kTC : -1;   // halo DMA: lanes 0-31 left pixel, 32-63 right
   // Stores: wave w copies row w/2 of a stage's staged rows, pixels
   // 16*(w%2) + 8j + lane/8 (j = 0, 1), chunk lane%8: whole 128-byte lines.
   const int sr = wave >> 1;
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
       q.scol[j] = sx < a.W ? (unsigned)((sx * kK + sc * 8) * 2) : kOob;
     }
     const int hx = q.x0 + hpx;
-    q.hcol = ((unsigned)hx < (unsigned)a.W) ? (unsigned)((hx * kC + (lane & 7) * 8) * 2) : kOob;
+    q.hcol = ((unsigned)hx < (unsigned)a.W) ? (unsigned)(hx * kC * 2 + 4 * (lane & 31)) : kOob;
     return q;
   };
   auto issue_stage = [&](const UnitGeo &q, int t) {
@@ -233,21 +239,22 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
           q.rx, (__attribute__((address_space(3))) void *)(dst + (128 * dhalf + 64 * j) * 16), 16, off, 0, 0,
           kNonTemporal);
     }
-    if (lane < 8) {
+    {
       const unsigned off = (row_in & (q.hcol != kOob)) ? roff + q.hcol : kOob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          q.rx, (__attribute__((address_space(3))) void *)(dst + (kHaloSlot + 8 * dhalf) * 16), 16, off, 0, 0,
-          kNonTemporal);
+          q.rx, (__attribute__((address_space(3))) void *)(dst + kHaloSlot * 16), 4, off, 0, 0, kNonTemporal);
     }
   };
 
-  // ---- Weights and bias: loads first, then the DMA of the first unit's first
-  // two stages, then the LDS transposition, so that the DMA latency overlaps
-  // it. Each output channel's 576 halves go on a row of 1168 bytes (16 bytes
-  // of padding spread the 16 channels a fragment read touches over distinct
-  // banks); every lane then gathers its 18 A fragments: fragment ks holds
-  // channels 32h + 8g .. +8 of tap t = ks/2 (h = ks%2) for output channel
-  // 16*og + n16, i.e. 8 halves 9 apart in the channel's row.
+  // ---- Weights and bias: coalesced loads first, then the DMA of the first
+  // unit's first kPreStages stages, then the weights' trip through LDS, so
+  // that the DMA latency overlaps it. Each output channel's 576 halves go on
+  // a row of 1168 bytes (16 bytes of padding put the rows of 8 consecutive
+  // channels on distinct banks). Fragment ks = 2t + h of lane (n16, g) holds
+  // channels c0 .. c0+8 (c0 = 32h + 8g) of tap t for output channel
+  // o = 16*og + n16: halves 9jj + t (jj = 0..7) of the 72 halves
+  // w[o][c0 .. c0+8][0..3][0..3], 144 contiguous bytes of o's row, read as 9
+  // 16-byte vectors per channel half and sorted in registers.
   UnitGeo geo = unit_geo(unit);
   half8 wa[18];
   float4v bias;
@@ -266,8 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j)
       t[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, (j * kThreads + tid) * 16, 0, 0);
-    issue_stage(geo, 0);
-    issue_stage(geo, 1);
+#pragma unroll
+    for (int st = 0; st < kPreStages; ++st) issue_stage(geo, st);
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j) {
       const int v = j * kThreads + tid;
@@ -278,16 +285,22 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   lds_barrier();
   {
     const int o = 16 * og + n16;
+    half8 raw[2][9];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 9; ++j)
+        raw[h][j] = *reinterpret_cast<const half8 *>(lds + kWStage + o * kWRow + (32 * h + 8 * g) * 18 + 16 * j);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
       const int t = ks >> 1, h = ks & 1;
-      const _Float16 *src =
-          reinterpret_cast<const _Float16 *>(lds + kWStage + o * kWRow) + (32 * h + 8 * g) * 9 + t;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) wa[ks][j] = src[9 * j];
+      for (int jj = 0; jj < 8; ++jj) wa[ks][jj] = raw[h][(9 * jj + t) / 8][(9 * jj + t) % 8];
     }
   }
   lds_barrier();   // the weights' LDS is ring space from here on
+#pragma unroll
+  for (int st = kPreStages; st < kD; ++st) issue_stage(geo, st);
 
   // Byte offsets (inside a row) of this lane's B reads for filter column v and
   // channel half h: pixel 16*ch + n16 + v - 1 of the row, chunk 4h + g.
@@ -310,10 +323,8 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   const int soff_r = kRingBytes + sr * kOutRowBytes + spx * 128 + ((sc ^ (spx & 7)) * 16);
 
   while (true) {
-    // ---- Unit prologue: stages 2 .. kD-1 join the first two in flight; the
-    // first two must have landed before the first read.
-#pragma unroll
-    for (int t = 2; t < kD; ++t) issue_stage(geo, t);
+    // ---- Unit prologue: stages 0 .. kD-1 are in flight; the first two must
+    // have landed before the first read.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(vm_after(1, -1)));
     lds_barrier();
 
@@ -397,12 +408,12 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
 
     unit += step;
     if (unit >= hi) break;
-    // The next unit's first two stages go out now; its first barrier comes
-    // after this unit's last staging reads (they wait for LDS) and its ring
-    // slots were freed by this unit's last barrier.
+    // The next unit's first kD stages go out now: their ring slots were freed
+    // by this unit's last barrier, and the next unit's first barrier comes
+    // after this unit's last staging reads.
     geo = unit_geo(unit);
-    issue_stage(geo, 0);
-    issue_stage(geo, 1);
+#pragma unroll
+    for (int t = 0; t < kD; ++t) issue_stage(geo, t);
   }
 }
 
