@@ -122,6 +122,9 @@ class Plan:
     def __init__(self, desc):
         self.desc = desc
         self.handle = conv2d_create(desc)
+        # Bound now: at interpreter exit the module's globals may already be
+        # gone when __del__ runs.
+        self._destroy = load().conv2d_destroy
 
     def info(self):
         return conv2d_get_plan_info(self.handle)
@@ -136,8 +139,9 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
-            conv2d_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h and destroy is not None:
+            destroy(h)
             self.handle = None
 
 

@@ -7,7 +7,7 @@
 // Kernels on Kepler GPUs" sets against its direct method). At 32 channels the
 // direct fp32 kernel is bound by the vector ALUs; v_mfma_f32_16x16x4_f32 does
 // the same fp32 products and sums at twice that ceiling (157.3 vs 78.6 TFLOP/s
-// without packed FP32). Design, shared with the fp16 NHWC kernel:
+// without packed FP32). Design:
 //  * persistent workgroups of 4 waves, one per CU, looping over 12 x 32 pixel
 //    tiles (2400 on a 1280x720 frame: 10 rounds of 256 CUs with 6% idle,
 //    where 16-row tiles left 12% idle); tiles of one XCD are neighbours so halo
