@@ -56,11 +56,17 @@ CALIB_BYTES = 256 << 20
 
 
 def _source_digest(files):
+    """Digest of the code of a kernel's sources: comments and whitespace are
+    dropped first, so that an edit of the comments keeps the counters valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in tuple(files) + ("common.hpp",):
-        with open(os.path.join(ROOT, "image_stencil_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "image_stencil_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
