@@ -8,20 +8,20 @@
 // direct fp32 kernel is bound by the vector ALUs; v_mfma_f32_16x16x4_f32 does
 // the same fp32 products and sums at twice that ceiling (157.3 vs 78.6 TFLOP/s
 // without packed FP32). Design:
-//  * persistent workgroups of 4 waves, one per CU, looping over 12 x 32 pixel
-//    tiles (2400 on a 1280x720 frame: 10 rounds of 256 CUs with 6% idle,
-//    where 16-row tiles left 12% idle); tiles of one XCD are neighbours so halo
-//    re-reads hit its L2;
-//  * the input tile with its halo (32 channels x 14 rows x 40 columns, aligned
+//  * persistent workgroups of 4 waves, one per CU, looping over 13 x 32 pixel
+//    tiles (2240 on a 1280x720 frame: 9 rounds of 256 CUs, the last 75% full;
+//    12-row tiles needed 10 rounds, 120 rows per CU against 117); tiles of one
+//    XCD are neighbours so halo re-reads hit its L2;
+//  * the input tile with its halo (32 channels x 15 rows x 40 columns, aligned
 //    16-byte chunks) streams HBM -> LDS by 16-byte buffer_load ... lds,
 //    double-buffered against the MFMAs; pixels outside the image read as 0
 //    through the range check;
-//  * LDS keeps the NCHW order; the channel-plane pitch of 560 floats is an odd
-//    multiple of 16 banks: the 16 lanes of one channel read 16 consecutive
-//    floats, and the two channels of a 32-lane half land on disjoint bank
-//    halves;
+//  * LDS keeps the NCHW order; the channel-plane pitch of 624 floats (600 used)
+//    is an odd multiple of 16 banks: the 16 lanes of one channel read 16
+//    consecutive floats, and the two channels of a 32-lane half land on
+//    disjoint bank halves; the two tile buffers fill the 160 KB of LDS;
 //  * wave w computes output channels 16*(w&1) .. +16 for columns 16*(w>>1) ..
-//    +16 of all 12 tile rows; its 72 weight fragments (all 288 k) stay in
+//    +16 of all 13 tile rows; its 72 weight fragments (all 288 k) stay in
 //    registers;
 //  * MFMA operands: A = 16 pixels x 4 channels of one tap (one LDS float per
 //    lane), B = 4 channels x 16 output channels (weights), D = 4 consecutive
@@ -41,14 +41,15 @@ typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 32;                        // input channels
 constexpr int kK = 32;                        // output channels
-constexpr int kTR = 12, kTC = 32;             // output tile: rows x columns
+constexpr int kTR = 13, kTC = 32;             // output tile: rows x columns
 constexpr int kIR = kTR + 2;                  // input rows with halo
 // An input row is loaded as 10 aligned 16-byte chunks, image columns x0-4 ..
 // x0+35, of which x0-1 .. x0+32 are used (LDS column 3 holds x0-1).
 constexpr int kChunksRow = 10;
 constexpr int kIC = 4 * kChunksRow;           // LDS floats per input row
-constexpr int kPlane = kIR * kIC;             // LDS floats per channel plane (560)
-constexpr int kChunks = kC * kIR * kChunksRow;   // 16-byte chunks per input tile
+constexpr int kPlaneChunks = 156;             // 16-byte slots per channel plane, 150 used
+constexpr int kPlane = 4 * kPlaneChunks;      // LDS floats per channel plane (624)
+constexpr int kChunks = kC * kPlaneChunks;    // 16-byte slots per input tile, padding included
 constexpr int kThreads = 256;
 constexpr int kRounds = (kChunks + kThreads - 1) / kThreads;   // 16-byte DMA rounds per thread and tile
 constexpr int kBufFloats = kRounds * kThreads * 4;   // floats per LDS tile buffer (whole rounds)
@@ -74,6 +75,7 @@ constexpr unsigned kOob = 0xFFFFFFF0u;
 // expcnt and lgkmcnt not waited for (all ones).
 constexpr int kWaitDmaNotStores = (kStores & 0xF) | ((kStores >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 static_assert(kPlane % 32 == 16, "plane pitch: 16 banks apart");
+static_assert(kIR * kChunksRow <= kPlaneChunks, "the tile rows fit the plane");
 static_assert(kC * kPlane <= kBufFloats, "the tile fits its buffer");
 static_assert(kStores < 64, "vmcnt field");
 
@@ -97,17 +99,6 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
   const int ob = wave & 1;     // output channels 16*ob .. +16
   const int ch = wave >> 1;    // tile columns 16*ch .. +16
 
-  // ---- Weights: fragment (t, cq) of this lane is W[16ob + n16][4cq + g][t].
-  float wb[kKS];
-  {
-    const float *wp = a.w + ((size_t)(16 * ob + n16) * kC + g) * 9;
-#pragma unroll
-    for (int t = 0; t < 9; ++t)
-#pragma unroll
-      for (int cq = 0; cq < kCQ; ++cq) wb[t * kCQ + cq] = wp[cq * 4 * 9 + t];
-  }
-  const float bv = a.bias ? a.bias[16 * ob + n16] : 0.f;
-
   // ---- Tile schedule: XCD x (= blockIdx mod 8) walks its own contiguous range.
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7;
@@ -126,12 +117,12 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
     y0 = ty * kTR;
     x0 = tx * kTC;
   };
-  // LDS chunk s of a buffer holds channel s / (kIR * kChunksRow), tile row
-  // r / kChunksRow and chunk r % kChunksRow of r = s % (kIR * kChunksRow)
-  // (image row y0-1+row, columns x0-4+4*chunk .. +4); chunks outside the image
-  // are loaded as 0 (W is a multiple of 4, so a chunk is wholly in or out), and
-  // so are the chunks of the last round past the tile. One DMA round j moves
-  // chunks (4j + wave) * 64 + lane.
+  // LDS chunk s of a buffer holds channel s / kPlaneChunks, tile row
+  // r / kChunksRow and chunk r % kChunksRow of r = s % kPlaneChunks (image row
+  // y0-1+row, columns x0-4+4*chunk .. +4); chunks outside the image are loaded
+  // as 0 (W is a multiple of 4, so a chunk is wholly in or out), and so are the
+  // plane padding and the chunks of the last round past the tile. One DMA
+  // round j moves chunks (4j + wave) * 64 + lane.
   struct Dma {
     __amdgpu_buffer_rsrc_t rx;
     int y0, x0;
@@ -151,18 +142,63 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
   // break the instruction stream.
   const int plane_i = H * W;
   auto issue_round = [&](const Dma &d, float *buf, int j) {
-    constexpr unsigned kPerPlane = kIR * kChunksRow;
     const unsigned s = (unsigned)((j * 4 + wave) * 64 + lane);
-    const unsigned c = s / kPerPlane;
-    const unsigned r = s - c * kPerPlane;
+    const unsigned c = s / kPlaneChunks;
+    const unsigned r = s - c * kPlaneChunks;
     const unsigned row = r / kChunksRow;
     const unsigned k = r - row * kChunksRow;
     const int gy = d.y0 - 1 + (int)row, gx = d.x0 - 4 + 4 * (int)k;
-    const bool in = d.any & (s < (unsigned)kChunks) & ((unsigned)gy < (unsigned)H) & ((unsigned)gx < (unsigned)W);
+    const bool in = d.any & (s < (unsigned)kChunks) & (row < (unsigned)kIR) & ((unsigned)gy < (unsigned)H) &
+                    ((unsigned)gx < (unsigned)W);
     const unsigned off = in ? (unsigned)((int)c * plane_i + gy * W + gx) * 4u : kOob;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         d.rx, (__attribute__((address_space(3))) void *)(buf + (j * 4 + wave) * 64 * 4), 16, off, 0, 0, 0);
   };
+
+  // ---- Weights: coalesced 16-byte loads of the KCRS tensor, then the first
+  // tile's DMA, then the weights through the second tile buffer (rows of 292
+  // floats) while that DMA is in flight. Fragment (t, cq) of this lane is
+  // W[16ob + n16][4cq + g][t].
+  float wb[kKS];
+  float bv;
+  {
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.w), (short)0, kK * kC * 9 * 4, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.bias), (short)0, a.bias ? kK * 4 : 0, kBufferFlags);
+    constexpr int kVecRow = kC * 9 / 4;        // 72 vectors per output channel
+    constexpr int kVecPerThread = kK * kVecRow / kThreads;
+    static_assert(kVecPerThread * kThreads == kK * kVecRow, "whole vectors per thread");
+    constexpr int kWPitch = kC * 9 + 4;        // 16-byte aligned rows
+    static_assert(kK * kWPitch <= kBufFloats, "the weights fit one tile buffer");
+    uint4v t[kVecPerThread];
+#pragma unroll
+    for (int j = 0; j < kVecPerThread; ++j)
+      t[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, (j * kThreads + tid) * 16, 0, 0);
+    {
+      const Dma d0 = dma_for(tile);
+#pragma unroll
+      for (int j = 0; j < kRounds; ++j) issue_round(d0, lds, j);
+    }
+    // The bias after the DMA: it is first used after the wait for that DMA.
+    bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (16 * ob + n16) * 4, 0, 0));
+    float *wl = lds + kBufFloats;
+    // Whole 16-byte vectors: this compiler narrows a 16-byte buffer load whose
+    // elements are taken apart one by one to a single dword.
+#pragma unroll
+    for (int j = 0; j < kVecPerThread; ++j) {
+      const int v = j * kThreads + tid;
+      const int o = v / kVecRow, r = v - o * kVecRow;
+      *reinterpret_cast<uint4v *>(wl + o * kWPitch + 4 * r) = t[j];
+    }
+    lds_barrier();
+    const float *wp = wl + (16 * ob + n16) * kWPitch + g * 9;
+#pragma unroll
+    for (int tp = 0; tp < 9; ++tp)
+#pragma unroll
+      for (int cq = 0; cq < kCQ; ++cq) wb[tp * kCQ + cq] = wp[cq * 4 * 9 + tp];
+    lds_barrier();   // the second buffer takes the next tile's DMA from here on
+  }
 
   // Float offset (inside a buffer) of this lane's A reads for tap column v at
   // tile row 0: channel g of the quad, image column x0 - 1 + 16*ch + n16 + v
@@ -233,10 +269,6 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
     });
   };
 
-  {
-    const Dma d0 = dma_for(tile);
-    for (int j = 0; j < kRounds; ++j) issue_round(d0, lds, j);
-  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int cur = 0;

@@ -120,7 +120,7 @@ def test_plan_choice_and_counts():
     # the 32 -> 32 3x3 fp32 layer runs on the fp32 matrix cores
     info = isa.Plan(isa.make_desc(1, 32, 720, 1280, 32, 3, 3, "f32", True)).info()
     assert info["kernel"] == "is_k5_mfma_f32"
-    assert info["tile"] == (32, 12) and info["lds_bytes"] == 2 * 18 * 256 * 16
+    assert info["tile"] == (32, 13) and info["lds_bytes"] == 2 * 20 * 256 * 16
     # wide filters fall back to the one-thread-per-output kernel
     info = isa.Plan(isa.make_desc(1, 1, 64, 64, 1, 9, 9)).info()
     assert info["kernel"] == "is_k0_generic_nchw_f32"
