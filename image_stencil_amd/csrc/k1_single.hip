@@ -153,7 +153,15 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
   // stores and their waits form one straight sequence per U rows, and the
   // wait before each row covers that row's loads only, not the U-1 prefetched
   // after it.
-  for (int rb = 0; rb < NT; rb += U) {
+  //
+  // The first block of U rows and, when it is whole, the last one are
+  // compiled separately so that they skip the products for output rows outside
+  // the strip (rows above it in the first block, below it in the last), which
+  // no store would keep: 2P rows' worth of FMAs at each end, 8.6% of the
+  // 7x7 strip's work.
+  auto block = [&](int rb, auto first_c, auto last_c) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
 #pragma unroll
     for (int p = 0; p < U; ++p) {
       const int r = rb + p;
@@ -174,6 +182,9 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
       // it starts that slot with a product instead of clearing it.
 #pragma unroll
       for (int j = 0; j < R; ++j) {
+        // Output row r-2P+j: above the strip when FIRST and p + j < 2P, below
+        // it when LAST (r = NT-U+p) and p + j >= U.
+        if ((FIRST && p + j < 2 * P) || (LAST && p + j >= U)) continue;
         const int slot = (p + j) % R;
         const int u = R - 1 - j;
 #pragma unroll
@@ -211,7 +222,16 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
       __builtin_amdgcn_sched_barrier(0);
       load_row<VEC, Q>(row_rsrc(xp, y0 - P + r + U, 0, in_hi, W), off_m, off_h, pf[p], ph[p]);
     }
-  }
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  const int nb = (NT + U - 1) / U;
+  const int rb_last = (nb - 1) * U;
+  const bool last_whole = nb >= 2 && NT - rb_last == U;
+  block(0, yes{}, no{});
+  const int rb_end = last_whole ? rb_last : nb * U;
+  for (int rb = U; rb < rb_end; rb += U) block(rb, no{}, no{});
+  if (last_whole) block(rb_last, no{}, yes{});
 }
 
 using K1Fn = void (*)(const float *, const float *, const float *, float *, int, int, int, int, int,
