@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
 
       // Input row r feeds relative output rows r-2P+j, j = 0..R-1, with
       // filter row R-1-j. j = R-1 is the first contribution to output row r:
-      // it starts that slot with a product instead of clearing it.
+      // it starts that slot with product + bias instead of clearing it.
 #pragma unroll
       for (int j = 0; j < R; ++j) {
         // Output row r-2P+j: above the strip when FIRST and p + j < 2P, below
@@ -192,16 +192,16 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             acc[slot][i] = (j == R - 1 && v == 0)
-                               ? wr[u * S + v] * win[i + v]
+                               ? __builtin_fmaf(wr[u * S + v], win[i + v], bv)
                                : __builtin_fmaf(wr[u * S + v], win[i + v], acc[slot][i]);
       }
 
-      // Output row r-2P (slot p mod R) is complete; it is stored only when it
-      // lies inside the strip.
+      // Output row r-2P (slot p mod R) is complete (the bias entered with its
+      // first product); it is stored only when it lies inside the strip.
       float o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        o[i] = acc[p % R][i] + bv;
+        o[i] = acc[p % R][i];
         if constexpr (RELU) o[i] = fmaxf(o[i], 0.f);
       }
       const __amdgpu_buffer_rsrc_t rs_o = row_rsrc(yp, y0 + r - 2 * P, y0, y0 + rows_out, W);
