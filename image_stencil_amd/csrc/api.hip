@@ -266,6 +266,11 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void
       is::Plan p;
       st = make_plan(&ld[l], p);
       if (st != IS_OK) return st;
+      // The last layer writes the depth-to-space output itself when its kernel can.
+      if (last && d->depth_to_space == 2 && is::multi_d2s_supported(p))
+        return hip_status(is::launch_multi_d2s(p, static_cast<const float *>(src),
+                                               static_cast<const float *>(w[l]), b ? b[l] : nullptr,
+                                               static_cast<float *>(y), stream));
       st = run_plan(p, src, w[l], b ? b[l] : nullptr, dst, stream);
       if (st != IS_OK) return st;
       src = dst;

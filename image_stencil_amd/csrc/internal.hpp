@@ -41,6 +41,11 @@ hipError_t launch_single(const Plan &p, const float *x, const float *w, const fl
 bool configure_multi(Plan &p);
 hipError_t launch_multi(const Plan &p, const float *x, const float *w, const float *b, float *y,
                         hipStream_t s);
+// The multi-channel layer with 4 output channels followed by a 2x depth-to-space
+// (y: N x 1 x 2H x 2W), in one launch.
+bool multi_d2s_supported(const Plan &p);
+hipError_t launch_multi_d2s(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                            hipStream_t s);
 
 bool configure_mfma(Plan &p);
 hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,

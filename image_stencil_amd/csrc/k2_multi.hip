@@ -68,7 +68,10 @@ __device__ __forceinline__ void issue_slab(__amdgpu_buffer_rsrc_t rs, float4 *bu
   }
 }
 
-template <int R, int FT, int CS, bool RELU>
+// D2S: the layer has 4 output channels and its output goes through a 2x
+// depth-to-space, out[n][0][2i+dy][2j+dx] = z[n][2dy+dx][i][j] (y is then
+// N x 1 x 2H x 2W), done in the epilogue instead of a pass of its own.
+template <int R, int FT, int CS, bool RELU, bool D2S>
 __global__ __launch_bounds__(kThreads) void is_k2_multi(const float *__restrict__ x,
                                                         const float *__restrict__ w,
                                                         const float *__restrict__ bias,
@@ -206,6 +209,39 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi(const float *__restrict_
   const int oy = y0 + row0;
   const int ox = x0 + 4 * lc;
   const bool in = oy < H && ox < W;
+  if constexpr (D2S) {
+    static_assert(FT == 4, "depth-to-space takes 4 channels");
+    // This lane's 4 columns of the 4 channels become 8 columns of output rows
+    // 2*oy (channels 0, 1 interleaved) and 2*oy + 1 (channels 2, 3): two
+    // 16-byte stores per row; W % 4 == 0 keeps them whole.
+    float o[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const float b = bias ? bias[f] : 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        o[f][p] = acc[f][p] + b;
+        if constexpr (RELU) o[f][p] = fmaxf(o[f][p], 0.f);
+      }
+    }
+    float *yn = y + (size_t)n * 4 * HW;
+    const __amdgpu_buffer_rsrc_t rs_o =
+        __builtin_amdgcn_make_buffer_rsrc(yn, (short)0, (int)(4 * HW * 4), kBufferFlags);
+#pragma unroll
+    for (int dy = 0; dy < 2; ++dy) {
+      const int c0 = 2 * dy;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned off =
+            in ? (unsigned)((((size_t)(2 * oy + dy) * (2 * W)) + 2 * ox + 4 * h) * 4) : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
+                               make_float4(o[c0][2 * h], o[c0 + 1][2 * h], o[c0][2 * h + 1], o[c0 + 1][2 * h + 1])),
+            rs_o, off, 0, 0);
+      }
+    }
+    return;
+  }
   float *yn = y + ((size_t)n * K + (size_t)kg * FT) * HW;
   const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
       yn, (short)0, (int)(FT * HW * 4), kBufferFlags);
@@ -231,10 +267,17 @@ using K2Fn = void (*)(const float *, const float *, const float *, float *, int,
 template <bool RELU>
 K2Fn pick(int r, int ft, int cs) {
 #define IS_K2_CASE(RR, FF, CC) \
-  if (r == RR && ft == FF && cs == CC) return is_k2_multi<RR, FF, CC, RELU>;
+  if (r == RR && ft == FF && cs == CC) return is_k2_multi<RR, FF, CC, RELU, false>;
   IS_K2_CASE(3, 32, 4) IS_K2_CASE(3, 16, 4) IS_K2_CASE(3, 8, 4) IS_K2_CASE(3, 4, 4)
   IS_K2_CASE(5, 32, 1) IS_K2_CASE(5, 32, 4) IS_K2_CASE(3, 32, 1) IS_K2_CASE(1, 32, 4)
 #undef IS_K2_CASE
+  return nullptr;
+}
+
+// With the depth-to-space epilogue: the 3x3 layer with 4 output channels.
+template <bool RELU>
+K2Fn pick_d2s(int r, int ft, int cs) {
+  if (r == 3 && ft == 4 && cs == 4) return is_k2_multi<3, 4, 4, RELU, true>;
   return nullptr;
 }
 
@@ -275,6 +318,20 @@ bool configure_multi(Plan &p) {
   p.tile_w = kTW;
   p.tile_h = kTH;
   return true;
+}
+
+bool multi_d2s_supported(const Plan &p) {
+  return p.kid == kMultiChannel && p.d.k == 4 && pick_d2s<false>(p.d.r, p.strip_rows, p.vec) != nullptr;
+}
+
+hipError_t launch_multi_d2s(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                            hipStream_t s) {
+  const conv2d_desc &d = p.d;
+  if (!multi_d2s_supported(p)) return hipErrorInvalidValue;
+  const int ft = p.strip_rows, cs = p.vec;
+  const K2Fn fn = d.relu ? pick_d2s<true>(d.r, ft, cs) : pick_d2s<false>(d.r, ft, cs);
+  return launch_kernel(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, d.c, d.h, d.w, d.k, p.nseg,
+                       p.nstrip, d.k / ft, p.ntiles);
 }
 
 hipError_t launch_multi(const Plan &p, const float *x, const float *w, const float *b, float *y,

@@ -77,6 +77,18 @@ def test_other_chains_run_layer_by_layer():
     check(y, ref, m, TAU_F32, "2-layer chain")
 
 
+def test_unfused_depth_to_space_pass_when_widths_are_ragged():
+    """W = 30 (not a multiple of 4): the last layer runs on the fallback kernel
+    and the depth-to-space is its own pass; W = 32 takes the 4-channel layer
+    with the depth-to-space epilogue. Both against the oracle."""
+    for W in (30, 32):
+        x, layers = synth.chain_f32(N=1, H=13, W=W, seed=12)
+        say("chain unfused", W)
+        y = _gpu_chain(x, layers, isa.IS_CHAIN_UNFUSED)
+        ref, m = oracle.chain(x, layers, d2s=2)
+        check(y, ref, m, TAU_F32, "unfused chain W=%d" % W)
+
+
 def test_auto_mode_uses_workspace_when_given():
     """AUTO runs layer by layer with the workspace it reports and falls back to
     the fused kernel without one; both match the oracle."""
