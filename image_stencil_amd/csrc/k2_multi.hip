@@ -142,16 +142,27 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi(const float *__restrict_
   // keep the compiler from hoisting all of them at once, which would exhaust
   // the scalar registers.
   auto compute = [&](const float4 *bf, int c0) {
+    // The next channel's LDS vectors are read before this channel's FMAs and
+    // turned into its window after them, so that the LDS latency is hidden.
+    float4 raw_o[2][R], raw_h[2][R];
+    auto read_raw = [&](int c, int b) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int base = (c * G::LH + row0 + u) * kG;
+        raw_o[b][u] = bf[base + own_g];
+        if constexpr (P > 0) raw_h[b][u] = bf[base + halo_g];
+      }
+    };
+    read_raw(0, 0);
 #pragma unroll
     for (int c = 0; c < CS; ++c) {
       float win[R][4 + 2 * P];
 #pragma unroll
       for (int u = 0; u < R; ++u) {
-        const int base = (c * G::LH + row0 + u) * kG;
-        const float4 o4 = bf[base + own_g];
+        const float4 o4 = raw_o[c & 1][u];
         win[u][P + 0] = o4.x; win[u][P + 1] = o4.y; win[u][P + 2] = o4.z; win[u][P + 3] = o4.w;
         if constexpr (P > 0) {
-          const float4 h4 = bf[base + halo_g];
+          const float4 h4 = raw_h[c & 1][u];
           const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
           const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
@@ -161,6 +172,7 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi(const float *__restrict_
           }
         }
       }
+      if (c + 1 < CS) read_raw(c + 1, (c + 1) & 1);
       constexpr int D = 2;   // prefetch distance in output channels
       float wt[D + 1][R * R];
       auto load_taps = [&](float *dst, int f) {
@@ -270,6 +282,7 @@ K2Fn pick(int r, int ft, int cs) {
   if (r == RR && ft == FF && cs == CC) return is_k2_multi<RR, FF, CC, RELU, false>;
   IS_K2_CASE(3, 32, 4) IS_K2_CASE(3, 16, 4) IS_K2_CASE(3, 8, 4) IS_K2_CASE(3, 4, 4)
   IS_K2_CASE(5, 32, 1) IS_K2_CASE(5, 32, 4) IS_K2_CASE(3, 32, 1) IS_K2_CASE(1, 32, 4)
+  IS_K2_CASE(5, 16, 1) IS_K2_CASE(3, 16, 1)
 #undef IS_K2_CASE
   return nullptr;
 }
@@ -288,9 +301,13 @@ bool configure_multi(Plan &p) {
   if (d.layout != IS_NCHW || d.in_dtype != IS_F32 || d.r != d.s) return false;
   if (d.w % 4 != 0) return false;
   const int cs = (d.c % 4 == 0) ? 4 : 1;
+  // Output channels per workgroup: as many as divide K, up to 32. With one
+  // input channel there is a single slab, so a workgroup loads, computes and
+  // stores in sequence; 16 channels give twice the workgroups to overlap those
+  // phases (the 1 -> 32 5x5 layer of a 1280x720 frame: 35.5 against 38.5 us).
   int ft = 0;
   for (int f : {32, 16, 8, 4})
-    if (d.k % f == 0) {
+    if (d.k % f == 0 && !(d.c == 1 && f == 32 && d.k % 16 == 0 && pick<false>(d.r, 16, cs))) {
       ft = f;
       break;
     }
