@@ -13,6 +13,13 @@ The conv chain is the composition of single layers followed by depth-to-space
 (chain of the upscaling network described in the same page's introduction and
 its "Reducing memory traffic" table), with the error scale propagated layer by
 layer as m_l = conv(|w_l|, m_{l-1}) + |b_l|.
+
+The fp16-storage chain (the same page's "Reducing memory traffic" step, which
+stores the data and the weights as fp16) reads every layer's input as the
+previous layer's output rounded to fp16, nearest even (numpy's float64 ->
+float16 conversion), computes each layer exactly in float64 on those values and
+rounds its output the same way; the network input and the weights are fp16
+values, the biases are given as fp32.
 """
 import ctypes
 import os
@@ -195,3 +202,70 @@ def chain_window(x, layers, i0, i1, j0, j1):
         z = np.where(outside[None, None], 0.0, z)
         m = np.where(outside[None, None], 0.0, m)
     return z, m
+
+
+def _to_f16(a):
+    """Round float64 values to fp16, nearest even, and widen back (exactly)."""
+    return np.asarray(a, np.float64).astype(np.float16).astype(np.float64)
+
+
+def _nhwc_to_nchw(a):
+    return np.ascontiguousarray(np.transpose(a, (0, 3, 1, 2)))
+
+
+def _nchw_to_nhwc(a):
+    return np.ascontiguousarray(np.transpose(a, (0, 2, 3, 1)))
+
+
+def chain_f16(x, layers, d2s=1):
+    """fp16-storage chain on NHWC input, then depth-to-space by d2s (1 = none).
+
+    x: N,H,W,C0 fp16 values; layers: sequence of (w, b, relu) with w K,C,R,R
+    fp16 values and b fp32 or None. z_0 = x, z_l = f16(act(conv(z_{l-1}) + b)).
+    Returns (out, m) in float64, NHWC: (N,H,W,K_last) or (N, d2s*H, d2s*W, 1).
+    """
+    z = _nhwc_to_nchw(_f64(x))
+    m = np.abs(z)
+    for w, b, relu in layers:
+        w = _f64(w)
+        b = None if b is None else _f64(b)
+        z, _ = conv2d(z, w, b, relu)
+        z = _to_f16(z)
+        m, _ = conv2d(m, np.abs(w), None if b is None else np.abs(b), False)
+    if d2s > 1:
+        z = depth_to_space(z, d2s)
+        m = depth_to_space(m, d2s)
+    return _nchw_to_nhwc(z), _nchw_to_nhwc(m)
+
+
+def chain_f16_window(x, layers, i0, i1, j0, j1):
+    """fp16-storage chain output (before depth-to-space, NHWC) on rows [i0,i1) x
+    cols [j0,j1) only: as chain_window, with every layer's output rounded to fp16
+    inside the image and zero outside it. Same result as
+    chain_f16(x, layers)[0][:, i0:i1, j0:j1, :]."""
+    x = _nhwc_to_nchw(_f64(x))
+    N, _, H, W = x.shape
+    radii = []
+    for w, _, _ in layers:
+        R, S = w.shape[2], w.shape[3]
+        if R != S:
+            raise ValueError("chain_f16_window assumes square filters")
+        radii.append((R - 1) // 2)
+    halo = sum(radii)
+    z = _zero_crop(x, i0 - halo, i1 + halo, j0 - halo, j1 + halo)
+    m = np.abs(z)
+    for (w, b, relu), p in zip(layers, radii):
+        w = _f64(w)
+        b = None if b is None else _f64(b)
+        zf, _ = conv2d(z, w, b, relu)
+        mf, _ = conv2d(m, np.abs(w), None if b is None else np.abs(b), False)
+        hh, ww = zf.shape[2], zf.shape[3]
+        z = _to_f16(zf[:, :, p:hh - p, p:ww - p])
+        m = mf[:, :, p:hh - p, p:ww - p]
+        halo -= p
+        rows = np.arange(i0 - halo, i1 + halo)
+        cols = np.arange(j0 - halo, j1 + halo)
+        outside = ((rows < 0) | (rows >= H))[:, None] | ((cols < 0) | (cols >= W))[None, :]
+        z = np.where(outside[None, None], 0.0, z)
+        m = np.where(outside[None, None], 0.0, m)
+    return _nchw_to_nhwc(z), _nchw_to_nhwc(m)

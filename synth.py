@@ -94,3 +94,22 @@ def cnn_layer_f16_nhwc(N=8, C=64, K=64, H=256, W=256, R=3, seed=0):
     w = _normal(rng, (K, C, R, R), np.sqrt(2.0 / (C * R * R))).astype(np.float16)
     b = _normal(rng, (K,), 0.01)
     return x, w, b
+
+
+# The pages' upscaling network (StreamHPC CNN page, "Reducing memory traffic"
+# table): 1 -> 64 (5x5), 64 -> 64, 64 -> 32, 32 -> 9 (3x3); ReLU after the
+# first three layers.
+PAGES_NET = ((1, 64, 5, True), (64, 64, 3, True), (64, 32, 3, True), (32, 9, 3, False))
+
+
+def chain_f16_nhwc(N=1, H=720, W=1280, spec=PAGES_NET, seed=0):
+    """fp16-storage chain: x (N,H,W,C0) fp16 U[0,1) and layers [(w, b, relu)]
+    with w (K,C,R,R) fp16 He-normal and b fp32 normal(0, 0.01)."""
+    rng = np.random.default_rng(seed)
+    x = _uniform01(rng, (N, H, W, spec[0][0])).astype(np.float16)
+    layers = []
+    for (c, k, r, relu) in spec:
+        w = _normal(rng, (k, c, r, r), np.sqrt(2.0 / (c * r * r))).astype(np.float16)
+        b = _normal(rng, (k,), 0.01)
+        layers.append((w, b, relu))
+    return x, layers
