@@ -46,7 +46,7 @@ TRAFFIC_KERNELS = {   # bench case -> (kernel as the profiler names it, its sour
     "8192x8192 5x5": ("is_k1_single<5, 5, true, false>", ("k1_single.hip",)),
     "8192x8192 7x7": ("is_k1_single<7, 7, true, false>", ("k1_single.hip",)),
     "fp32 layer 1x32x720x1280 -> 32, 3x3": ("is_k5_mfma_f32", ("k5_mfma_f32.hip",)),
-    "fp16 NHWC layer 8x256x256x64 -> 64, 3x3": ("is_k4_mfma<128>", ("k4_mfma.hip",)),
+    "fp16 NHWC layer 8x256x256x64 -> 64, 3x3": ("is_k4_mfma<128, 64, 64>", ("k4_mfma.hip",)),
     "upscaling chain 1280x720 (fused)": ("is_k3_chain", ("k3_chain.hip",)),
 }
 # The known-size dispatch: torch's elementwise negation of 256 MiB of fp32
@@ -174,7 +174,7 @@ def lds_study(torch, isa, synth, stream, stream_obj, steps, warmup):
     """The LDS-staged kernels for a counter run of their bank conflicts: the fp16
     layer under each swizzle of its input tile (IMGSTENCIL_K4_SWIZZLE, read at
     plan creation; the kernel is instantiated per swizzle, so the profiler sees
-    is_k4_mfma<0>, <128> and <256>), the fp32 layer and the fused chain."""
+    is_k4_mfma<0, 64, 64>, <128, 64, 64> and <256, 64, 64>), the fp32 layer and the fused chain."""
     out = []
     x, w, b = synth.cnn_layer_f16_nhwc()
     xd, wd, bd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()

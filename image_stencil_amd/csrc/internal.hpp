@@ -26,6 +26,7 @@ struct Plan {
   int nseg, nstrip, ntiles;   // column segments, row strips, total tiles
   int strip_rows;             // output rows per strip
   int vec;                    // 1 = 16-byte vector path
+  int kvalid;                 // fp16 MFMA layer: output channels with weights (the rest are 0)
 };
 
 // Each kernel family fills the launch geometry of a plan it accepts and

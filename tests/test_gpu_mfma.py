@@ -100,3 +100,32 @@ def test_mfma_layer_more_units_than_workgroups():
     got = y[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
     ratio = check(got, ref, m, TAU_F16, "3x700x260 layer")
     say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))
+
+
+@pytest.mark.parametrize("C,K", [(64, 32), (32, 32), (32, 16)])
+@pytest.mark.parametrize("N,H,W", [(1, 8, 32), (2, 37, 70), (1, 66, 130), (1, 1, 1), (1, 40, 257)])
+def test_mfma_other_channel_counts(C, K, N, H, W):
+    """The upscaling network's other fp16 layers (64 -> 32, 32 -> 32, 32 -> 16):
+    wider units (64 and 128 pixels), shorter ones for 16 outputs, ragged edges."""
+    x, w, b = synth.cnn_layer_f16_nhwc(N=N, C=C, K=K, H=H, W=W, seed=C + K + H + W)
+    say("mfma", C, K, N, H, W)
+    y = _run(x, w, b, True, "is_k4_mfma")
+    ref, m = oracle.conv2d(x, w, b, True, "NHWC")
+    check(y, ref, m, TAU_F16, "mfma %d->%d %dx%dx%d" % (C, K, N, H, W))
+
+
+@pytest.mark.parametrize("C,K", [(64, 32), (32, 16)])
+def test_mfma_other_channel_counts_1280x720_sampled(C, K):
+    """Two 1280x720 frames (more units than workgroups): rows on unit and
+    stage edges, columns on unit edges, every channel."""
+    x, w, b = synth.cnn_layer_f16_nhwc(N=2, C=C, K=K, H=720, W=1280, seed=C * 3 + K)
+    say("mfma 2x720x1280", C, K)
+    y = _run(x, w, b, True, "is_k4_mfma")
+    assert np.isfinite(y.astype(np.float32)).all()
+    rows = [0, 1, 3, 4, 31, 32, 33, 63, 64, 65, 703, 704, 719]
+    cols = list(range(0, 1280, 13)) + [63, 64, 127, 128, 1279]
+    pts = np.array([(n, k, i, j) for n in range(2) for i in rows for j in cols for k in range(K)], np.int64)
+    ref, m = oracle.conv2d_points(x, w, b, True, pts, "NHWC")
+    got = y[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
+    ratio = check(got, ref, m, TAU_F16, "2x720x1280 %d->%d" % (C, K))
+    say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))
