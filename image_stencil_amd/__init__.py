@@ -66,8 +66,9 @@ def conv2d_get_plan_info(plan):
             "flops": info.flops, "bytes": info.bytes}
 
 
-def make_chain_desc(n, h, w, layers, depth_to_space=1, mode=IS_CHAIN_AUTO):
-    """layers: sequence of (c, k, r, relu) (square filters)."""
+def make_chain_desc(n, h, w, layers, depth_to_space=1, mode=IS_CHAIN_AUTO, dtype="f32"):
+    """layers: sequence of (c, k, r, relu) (square filters); dtype "f32" (NCHW)
+    or "f16" (NHWC, fp16 storage between layers)."""
     d = conv_chain_desc()
     d.n, d.h, d.w = n, h, w
     if not 1 <= len(layers) <= _abi.IS_MAX_CHAIN:
@@ -77,7 +78,7 @@ def make_chain_desc(n, h, w, layers, depth_to_space=1, mode=IS_CHAIN_AUTO):
         L = d.layer[i]
         L.c, L.k, L.r, L.s, L.relu = c, k, r, r, int(bool(relu))
     d.depth_to_space = depth_to_space
-    d.dtype = IS_F32
+    d.dtype = {"f32": IS_F32, "f16": IS_F16}[dtype]
     d.mode = mode
     return d
 
@@ -177,21 +178,28 @@ def conv2d(x, w, b=None, relu=False):
 
 
 def conv_chain(x, layers, depth_to_space=1, mode=IS_CHAIN_AUTO):
-    """layers: list of (w, b, relu) device tensors (fp32, NCHW). Returns the chain output."""
+    """layers: list of (w, b, relu) device tensors. x fp32 NCHW with fp32 weights,
+    or x fp16 NHWC with fp16 weights (fp32 biases). Returns the chain output."""
     import torch
-    _check_dev(x, torch.float32, "x")
-    N, C, H, W = x.shape
+    f16 = x.dtype == torch.float16
+    _check_dev(x, torch.float16 if f16 else torch.float32, "x")
+    if f16:
+        N, H, W, C = x.shape
+    else:
+        N, C, H, W = x.shape
     spec = []
     for (w, b, relu) in layers:
-        _check_dev(w, torch.float32, "w")
+        _check_dev(w, torch.float16 if f16 else torch.float32, "w")
         if b is not None:
             _check_dev(b, torch.float32, "b")
         spec.append((w.shape[1], w.shape[0], w.shape[2], relu))
-    d = make_chain_desc(N, H, W, spec, depth_to_space, mode)
-    if depth_to_space == 2:
-        y = torch.empty((N, 1, 2 * H, 2 * W), dtype=torch.float32, device=x.device)
+    d = make_chain_desc(N, H, W, spec, depth_to_space, mode, "f16" if f16 else "f32")
+    f = depth_to_space
+    if f16:
+        shape = (N, f * H, f * W, 1) if f > 1 else (N, H, W, spec[-1][1])
     else:
-        y = torch.empty((N, spec[-1][1], H, W), dtype=torch.float32, device=x.device)
+        shape = (N, 1, f * H, f * W) if f > 1 else (N, spec[-1][1], H, W)
+    y = torch.empty(shape, dtype=x.dtype, device=x.device)
     ws_bytes = conv_chain_workspace_size(d)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device) if ws_bytes else None
     conv_chain_forward(d, x.data_ptr(), [w.data_ptr() for (w, _, _) in layers],

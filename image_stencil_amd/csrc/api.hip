@@ -81,7 +81,7 @@ is_status make_plan(const conv2d_desc *d, is::Plan &p) {
   memset(&p, 0, sizeof(p));
   p.d = *d;
   if (!is::configure_single(p) && !is::configure_mfma_f32(p) && !is::configure_multi(p) &&
-      !is::configure_mfma(p))
+      !is::configure_mfma(p) && !is::configure_head_f16(p))
     is::configure_generic(p);
   if (log_enabled())
     fprintf(stderr, "[imgstencil] n=%d c=%d h=%d w=%d k=%d r=%d s=%d -> %s grid=%d block=%d lds=%d\n",
@@ -118,6 +118,10 @@ is_status run_plan(const is::Plan &p, const void *x, const void *w, const float 
       e = is::launch_mfma(p, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(w), bias,
                           static_cast<_Float16 *>(y), stream);
       break;
+    case is::kHeadNhwcF16:
+      e = is::launch_head_f16(p, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(w), bias,
+                              static_cast<_Float16 *>(y), stream);
+      break;
     default:
       e = is::launch_generic(p, x, w, bias, y, stream);
       break;
@@ -132,8 +136,8 @@ is_status chain_layers(const conv_chain_desc *d, conv2d_desc *ld) {
   if (!d) return IS_ERR_INVALID_ARG;
   if (d->n_layers < 1 || d->n_layers > IS_MAX_CHAIN || d->n < 0 || d->h < 0 || d->w < 0)
     return IS_ERR_INVALID_ARG;
-  if (d->dtype != IS_F32) return IS_ERR_UNSUPPORTED;
-  if (d->depth_to_space != 1 && d->depth_to_space != 2) return IS_ERR_UNSUPPORTED;
+  if (d->dtype != IS_F32 && d->dtype != IS_F16) return IS_ERR_UNSUPPORTED;
+  if (d->depth_to_space < 1 || d->depth_to_space > 3) return IS_ERR_UNSUPPORTED;
   if (d->mode != IS_CHAIN_AUTO && d->mode != IS_CHAIN_FUSED && d->mode != IS_CHAIN_UNFUSED)
     return IS_ERR_INVALID_ARG;
   for (int l = 0; l < d->n_layers; ++l) {
@@ -145,22 +149,41 @@ is_status chain_layers(const conv_chain_desc *d, conv2d_desc *ld) {
     c.k = L.k; c.r = L.r; c.s = L.s;
     c.pad_h = (L.r - 1) / 2; c.pad_w = (L.s - 1) / 2;
     c.stride_h = c.stride_w = 1;
-    c.in_dtype = c.out_dtype = IS_F32;
-    c.layout = IS_NCHW;
+    c.in_dtype = c.out_dtype = d->dtype;
+    c.layout = d->dtype == IS_F16 ? IS_NHWC : IS_NCHW;
     c.relu = L.relu;
     const is_status st = validate(&c);
     if (st != IS_OK) return st;
   }
-  if (d->depth_to_space == 2 && d->layer[d->n_layers - 1].k != 4) return IS_ERR_UNSUPPORTED;
+  const int f = d->depth_to_space;
+  if (f > 1 && d->layer[d->n_layers - 1].k != f * f) return IS_ERR_UNSUPPORTED;
   return IS_OK;
 }
 
-bool chain_fusable(const conv_chain_desc *d, const conv2d_desc *) { return is::chain_fused_supported(d); }
+bool chain_fusable(const conv_chain_desc *d, const conv2d_desc *) {
+  return d->dtype == IS_F32 && is::chain_fused_supported(d);
+}
 
-size_t chain_buffer_bytes(const conv_chain_desc *d) {
+// fp16 chains: a last layer of fewer than 16 output channels followed by
+// depth-to-space runs on the MFMA kernel as 16 channels with zero weights past
+// its own (kvalid), into the workspace, when that kernel takes (C, 16).
+bool pad_last_f16(const conv_chain_desc *d, const conv2d_desc &last) {
+  if (d->dtype != IS_F16 || d->depth_to_space == 1 || last.k >= 16) return false;
+  conv2d_desc c = last;
+  c.k = 16;
+  is::Plan p;
+  memset(&p, 0, sizeof(p));
+  p.d = c;
+  return is::configure_mfma(p);
+}
+
+size_t chain_buffer_bytes(const conv_chain_desc *d, const conv2d_desc *ld) {
+  const size_t es = d->dtype == IS_F16 ? 2 : 4;
+  const int last = d->n_layers - 1;
   size_t m = 0;
   for (int l = 0; l < d->n_layers; ++l) {
-    const size_t b = 4 * (size_t)d->n * d->layer[l].k * d->h * d->w;
+    const int k = (l == last && pad_last_f16(d, ld[last])) ? 16 : d->layer[l].k;
+    const size_t b = es * (size_t)d->n * k * d->h * d->w;
     if (b > m) m = b;
   }
   return align256(m);
@@ -168,9 +191,9 @@ size_t chain_buffer_bytes(const conv_chain_desc *d) {
 
 // Workspace of the layer-by-layer path: ping-pong buffers for the
 // intermediates; a single layer without depth-to-space writes straight to y.
-size_t unfused_bytes(const conv_chain_desc *d) {
+size_t unfused_bytes(const conv_chain_desc *d, const conv2d_desc *ld) {
   const int need = (d->n_layers == 1 && d->depth_to_space == 1) ? 0 : (d->n_layers == 1 ? 1 : 2);
-  return need * chain_buffer_bytes(d);
+  return need * chain_buffer_bytes(d, ld);
 }
 
 // Workspace that conv_chain_forward wants for the chain and mode: none for the
@@ -184,7 +207,7 @@ is_status chain_workspace(const conv_chain_desc *d, const conv2d_desc *ld, size_
     *bytes = 0;
     return IS_OK;
   }
-  *bytes = unfused_bytes(d);
+  *bytes = unfused_bytes(d, ld);
   return IS_OK;
 }
 
@@ -195,7 +218,7 @@ bool runs_fused(const conv_chain_desc *d, const conv2d_desc *ld, const void *wor
                 size_t workspace_bytes) {
   if (d->mode == IS_CHAIN_FUSED) return true;
   if (d->mode == IS_CHAIN_UNFUSED || !chain_fusable(d, ld)) return false;
-  const size_t need = unfused_bytes(d);
+  const size_t need = unfused_bytes(d, ld);
   return need > 0 && (!workspace || workspace_bytes < need);
 }
 
@@ -238,8 +261,9 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void
       if (misaligned(w[l]) || (b && b[l] && misaligned(b[l]))) return IS_ERR_MISALIGNED;
     }
     if (misaligned(x) || misaligned(y)) return IS_ERR_MISALIGNED;
-    const size_t xb = 4 * (size_t)d->n * d->layer[0].c * d->h * d->w;
-    const size_t yb = 4 * (size_t)d->n * d->layer[d->n_layers - 1].k * d->h * d->w;
+    const size_t es = d->dtype == IS_F16 ? 2 : 4;
+    const size_t xb = es * (size_t)d->n * d->layer[0].c * d->h * d->w;
+    const size_t yb = es * (size_t)d->n * d->layer[d->n_layers - 1].k * d->h * d->w;
     if (overlap(x, xb, y, yb)) return IS_ERR_INVALID_ARG;
     size_t need = 0;
     st = chain_workspace(d, ld, &need);
@@ -257,14 +281,22 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void
                                                reinterpret_cast<const float *const *>(w), b,
                                                static_cast<float *>(y), stream));
 
-    const size_t half = chain_buffer_bytes(d);
+    const size_t half = chain_buffer_bytes(d, ld);
     char *ws = static_cast<char *>(workspace);
     const void *src = x;
     for (int l = 0; l < d->n_layers; ++l) {
       const bool last = l == d->n_layers - 1;
       void *dst = (last && d->depth_to_space == 1) ? y : (void *)(ws + (l % 2) * half);
       is::Plan p;
-      st = make_plan(&ld[l], p);
+      const bool padded = last && pad_last_f16(d, ld[l]);
+      if (padded) {
+        conv2d_desc c = ld[l];
+        c.k = 16;
+        st = make_plan(&c, p);
+        p.kvalid = ld[l].k;
+      } else {
+        st = make_plan(&ld[l], p);
+      }
       if (st != IS_OK) return st;
       // The last layer writes the depth-to-space output itself when its kernel can.
       if (last && d->depth_to_space == 2 && is::multi_d2s_supported(p))
@@ -275,10 +307,17 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void
       if (st != IS_OK) return st;
       src = dst;
     }
-    if (d->depth_to_space == 2)
-      return hip_status(is::launch_depth_to_space2(static_cast<const float *>(src),
-                                                   static_cast<float *>(y), d->n, d->h, d->w,
-                                                   stream));
+    const int f = d->depth_to_space;
+    if (f > 1 && d->dtype == IS_F16) {
+      const int k = d->layer[d->n_layers - 1].k;
+      const int zc = pad_last_f16(d, ld[d->n_layers - 1]) ? 16 : k;
+      return hip_status(is::launch_depth_to_space_f16(static_cast<const _Float16 *>(src),
+                                                      static_cast<_Float16 *>(y), d->n, d->h, d->w, f, zc,
+                                                      stream));
+    }
+    if (f > 1)
+      return hip_status(is::launch_depth_to_space(static_cast<const float *>(src), static_cast<float *>(y),
+                                                  d->n, d->h, d->w, f, stream));
     return IS_OK;
   } catch (...) {
     return IS_ERR_INVALID_ARG;

@@ -11,7 +11,8 @@ enum KernelId {
   kSingleChannel = 2,    // C = K = 1, fp32 NCHW, r, s <= 7
   kMultiChannel = 3,     // fp32 NCHW register-blocked, C, K multiples of the block
   kMfmaNhwcF16 = 4,      // fp16 NHWC implicit GEMM on MFMA
-  kMfmaNchwF32 = 5       // fp32 NCHW 32 -> 32 3x3 implicit GEMM on the fp32 MFMA
+  kMfmaNchwF32 = 5,      // fp32 NCHW 32 -> 32 3x3 implicit GEMM on the fp32 MFMA
+  kHeadNhwcF16 = 6       // fp16 NHWC first layer, 1 -> K, one MFMA k step over the taps
 };
 
 struct Plan {
@@ -52,6 +53,10 @@ bool configure_mfma(Plan &p);
 hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
                        hipStream_t s);
 
+bool configure_head_f16(Plan &p);
+hipError_t launch_head_f16(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
+                           hipStream_t s);
+
 bool configure_mfma_f32(Plan &p);
 hipError_t launch_mfma_f32(const Plan &p, const float *x, const float *w, const float *b, float *y,
                            hipStream_t s);
@@ -61,7 +66,11 @@ bool chain_fused_supported(const conv_chain_desc *d);
 hipError_t launch_chain_fused(const conv_chain_desc *d, const float *x, const float *const *w,
                               const float *const *b, float *y, hipStream_t s);
 
-// out[n,0,2i+dy,2j+dx] = z[n,2*dy+dx,i,j] for z of N x 4 x H x W fp32.
-hipError_t launch_depth_to_space2(const float *z, float *out, int N, int H, int W, hipStream_t s);
+// out[n,0,f*i+dy,f*j+dx] = z[n,f*dy+dx,i,j] for z of N x f*f x H x W fp32.
+hipError_t launch_depth_to_space(const float *z, float *out, int N, int H, int W, int f, hipStream_t s);
+// The same for NHWC fp16: z is N x H x W x zc (channels f*dy+dx among zc >= f*f),
+// out is N x f*H x f*W x 1.
+hipError_t launch_depth_to_space_f16(const _Float16 *z, _Float16 *out, int N, int H, int W, int f, int zc,
+                                     hipStream_t s);
 
 }  // namespace is

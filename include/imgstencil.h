@@ -117,16 +117,20 @@ is_status conv2d_get_plan_info(conv2d_plan plan, conv2d_plan_info *info);
 
 /* A chain of layers applied one after another, each reading the previous
  * layer's output: z_0 = x, z_l = act_l(conv_l(z_{l-1}) + b_l), and finally an
- * optional depth-to-space by `depth_to_space` = 2 that turns the last layer's
- * 4 channels of HxW into one channel of 2Hx2W with
- * out[n,0,2i+dy,2j+dx] = z[n,2*dy+dx,i,j]. This is the neural upscaling
+ * optional depth-to-space by f = `depth_to_space` (2 or 3) that turns the last
+ * layer's f*f channels of HxW into one channel of fHxfW with
+ * out[n,0,f*i+dy,f*j+dx] = z[n,f*dy+dx,i,j]. This is the neural upscaling
  * network of the same StreamHPC page (introduction; layer table of "Reducing
- * memory traffic"), and the fused evaluation follows the warp-sized overlapped
- * tiles with loop fusion of "Model-Based Warp Overlapped Tiling for Image
- * Processing Programs on GPUs" (arXiv 1909.07190, abstract).
+ * memory traffic": 1 -> 64 5x5, 64 -> 64, 64 -> 32, 32 -> 9 3x3, whose 9
+ * output channels are taken as a 3x3 sub-pixel upscale), and the fused
+ * evaluation follows the warp-sized overlapped tiles with loop fusion of
+ * "Model-Based Warp Overlapped Tiling for Image Processing Programs on GPUs"
+ * (arXiv 1909.07190, abstract).
  *  Layer l reads layer[l].c channels (layer[0].c = input channels, layer[l].c
  *  = layer[l-1].k), has layer[l].k outputs, odd r == s, and ReLU if relu != 0.
- *  dtype: IS_F32 only (NCHW). */
+ *  dtype: IS_F32 (NCHW tensors, fp32 weights and biases) or IS_F16 (NHWC
+ *  tensors, fp16 weights, fp32 biases; every layer's output is stored as fp16,
+ *  the page's "Reducing memory traffic" step; layer by layer only). */
 typedef struct { int c, k, r, s, relu; } conv_layer_desc;
 
 typedef enum {
@@ -139,7 +143,7 @@ typedef enum {
 typedef struct {
   int n, h, w, n_layers;
   conv_layer_desc layer[IS_MAX_CHAIN];
-  int depth_to_space;    /* 1 = none, 2 = x2 on the last layer (needs its k == 4) */
+  int depth_to_space;    /* 1 = none, f = 2 or 3: x f on the last layer (needs its k == f*f) */
   is_dtype dtype;
   is_chain_mode mode;
 } conv_chain_desc;
@@ -151,9 +155,10 @@ typedef struct {
 is_status conv_chain_workspace_size(const conv_chain_desc *d, size_t *bytes);
 
 /* Enqueue the chain on `stream`.
- *  x: N x layer[0].c x H x W fp32 input
+ *  x: N x layer[0].c x H x W fp32 input (IS_F16: N x H x W x layer[0].c fp16)
  *  w[l], b[l]: host arrays of n_layers device pointers (b[l] may be NULL)
- *  y: N x layer[last].k x H x W, or N x 1 x 2H x 2W with depth_to_space = 2
+ *  y: N x layer[last].k x H x W, or N x 1 x fH x fW with depth_to_space = f
+ *     (IS_F16: N x H x W x layer[last].k, or N x fH x fW x 1)
  *  workspace: device memory of at least conv_chain_workspace_size bytes, or
  *             NULL when that size is 0
  * Errors: as conv2d_forward, plus IS_ERR_WORKSPACE and IS_ERR_UNSUPPORTED. */

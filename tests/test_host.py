@@ -239,3 +239,34 @@ def test_chain_descriptor_checks():
     fused = isa.make_chain_desc(1, 720, 1280, spec, 2, isa.IS_CHAIN_FUSED)
     assert isa.conv_chain_workspace_size(fused) == 0
     assert isa.conv_chain_kernel_name(fused) == "is_k3_chain"
+
+
+def test_f16_chain_descriptor_checks():
+    """The pages' net in fp16 storage: two ping-pong buffers of the widest
+    layer (64 channels, 2 bytes), depth-to-space by 3 of the 9 channels, and
+    layer by layer only."""
+    spec = [(1, 64, 5, True), (64, 64, 3, True), (64, 32, 3, True), (32, 9, 3, False)]
+    d = isa.make_chain_desc(1, 720, 1280, spec, 3, isa.IS_CHAIN_AUTO, "f16")
+    assert isa.conv_chain_workspace_size(d) == 2 * 2 * 64 * 720 * 1280
+    assert isa.conv_chain_kernel_name(d) == "layer_by_layer"
+    assert round(traffic.chain_flops(1, 720, 1280, [t[:3] for t in spec]) / 1e9, 2) == 109.65
+    for mode in (isa.IS_CHAIN_FUSED,):
+        with pytest.raises(isa.ImgStencilError):
+            isa.conv_chain_workspace_size(isa.make_chain_desc(1, 720, 1280, spec, 3, mode, "f16"))
+    with pytest.raises(isa.ImgStencilError):       # 9 channels do not make a 2x2 block
+        isa.conv_chain_workspace_size(isa.make_chain_desc(1, 720, 1280, spec, 2, isa.IS_CHAIN_AUTO, "f16"))
+    with pytest.raises(isa.ImgStencilError):       # factors 1 to 3 only
+        isa.conv_chain_workspace_size(isa.make_chain_desc(1, 8, 8, [(1, 16, 3, False)], 4,
+                                                          isa.IS_CHAIN_AUTO, "f16"))
+    # a 32 -> 4 last layer before depth-to-space runs as 16 channels (4 of them
+    # real) in the workspace; a 2 -> 4 one keeps its 4 channels
+    def ws_f16(spec, f):
+        return isa.conv_chain_workspace_size(isa.make_chain_desc(1, 10, 10, spec, f, isa.IS_CHAIN_AUTO, "f16"))
+    assert ws_f16([(1, 32, 3, True), (32, 4, 3, False)], 2) == 2 * 6400
+    assert ws_f16([(1, 2, 3, True), (2, 4, 3, False)], 2) == 2 * 1024
+    # the first layer (one input channel) has its own fp16 kernel
+    for k, r in ((64, 5), (32, 3), (16, 5)):
+        info = isa.Plan(isa.make_desc(1, 1, 720, 1280, k, r, r, "f16", True)).info()
+        assert info["kernel"] == "is_k6_head_f16"
+        assert info["tile"] == (64, 16)
+    assert isa.Plan(isa.make_desc(1, 1, 72, 128, 8, 3, 3, "f16", True)).info()["kernel"] != "is_k6_head_f16"
