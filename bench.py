@@ -72,6 +72,21 @@ def _source_digest(files):
 
 def _short_kernel(name):
     import re
+    if name.startswith("_ZN"):
+        # Left mangled by the tracer (c++filt does not take the _Float16
+        # mangling either): the innermost name and its integer template
+        # arguments are enough here.
+        i, parts = 3, []
+        while i < len(name) and name[i].isdigit():
+            j = i
+            while name[j].isdigit():
+                j += 1
+            n = int(name[i:j])
+            parts.append(name[j:j + n])
+            i = j + n
+        targs = re.findall(r"Li(-?\d+)E", name[i:name.find("EE", i) + 1]) if name[i:i + 1] == "I" else []
+        if parts:
+            return parts[-1] + ("<%s>" % ", ".join(targs) if targs else "")
     name = name.replace("void ", "").replace("is::(anonymous namespace)::", "")
     m = re.match(r"([^(<]+(<[^>]*>)?)", name)
     return m.group(1).strip() if m else name
@@ -98,6 +113,22 @@ def _counter_means(d, counter):
     return {k: (sum(v) / len(v), len(v), full[k]) for k, v in acc.items()}
 
 
+# Arguments of the bench runs under the profiler: the counter and trace runs of
+# the bench workloads leave out the pages' net (its 64 -> 64 layer runs the same
+# kernel instance as the fp16 layer workload and would mix into that row); the
+# net has a kernel-trace run of its own.
+PROFILE_ARGS = "--no-cpu-baseline --secondary fp32_layer,fp16_layer,upscale_chain"
+PMC_ARGS = "--steps 2 --warmup 1 --min-warm-s 0 " + PROFILE_ARGS
+NET_PROFILE_ARGS = "--no-cpu-baseline --secondary pages_net"
+NET_KERNELS = {
+    "is_k6_head_f16<5, 64>": "layer 1: 1 -> 64, 5x5",
+    "is_k4_mfma<128, 64, 64>": "layer 2: 64 -> 64, 3x3",
+    "is_k4_mfma<128, 64, 32>": "layer 3: 64 -> 32, 3x3",
+    "is_k4_mfma<128, 32, 16>": "layer 4: 32 -> 9 (as 16), 3x3",
+    "is_d2s_nhwc_f16<3>": "depth-to-space x3",
+}
+
+
 def pmc_summary(fetch_dir, write_dir):
     """Markdown summary of two counter runs: per-dispatch FETCH_SIZE and
     WRITE_SIZE of each bench case's kernel, scaled by the known-size dispatch."""
@@ -116,9 +147,9 @@ def pmc_summary(fetch_dir, write_dir):
     lines = ["# HBM traffic per launch from the FETCH_SIZE and WRITE_SIZE counters", "",
              "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
              "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o run -- \\" % fetch_dir,
-             "    python3 bench.py --steps 2 --warmup 1 --min-warm-s 0 --no-cpu-baseline",
+             "    python3 bench.py " + PMC_ARGS,
              "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o run -- \\" % write_dir,
-             "    python3 bench.py --steps 2 --warmup 1 --min-warm-s 0 --no-cpu-baseline",
+             "    python3 bench.py " + PMC_ARGS,
              "python3 bench.py --pmc-summary %s %s > profiles/hbm_traffic_counters.md" % (fetch_dir, write_dir),
              "```", "",
              "Counters are in KiB per dispatch, averaged over the dispatches of each kernel. The scale",
@@ -140,24 +171,30 @@ def pmc_summary(fetch_dir, write_dir):
     return "\n".join(lines) + "\n"
 
 
-def stats_summary(trace_dir):
+def stats_summary(trace_dir, net=False):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run of this script:
-    calls and durations per kernel, with the bench case each kernel times."""
+    calls and durations per kernel, with the bench case each kernel times (net:
+    the run of the pages' net, with the layer each kernel runs)."""
     import csv
     import glob
     files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True))
     if not files:
         raise SystemExit("no kernel_stats.csv under %s" % trace_dir)
-    cases = {k: c for c, (k, _) in TRAFFIC_KERNELS.items()}
-    lines = ["# Kernel durations of the bench workloads (rocprofv3 kernel trace)", "",
+    cases = dict(NET_KERNELS) if net else {k: c for c, (k, _) in TRAFFIC_KERNELS.items()}
+    title = ("Kernel durations of the pages' fp16 net per 1280x720 frame" if net
+             else "Kernel durations of the bench workloads")
+    out_file = "pages_net_f16_kernels.md" if net else "kernel_durations_bench_workloads.md"
+    lines = ["# %s (rocprofv3 kernel trace)" % title, "",
              "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
              "rocprofv3 --kernel-trace --stats --output-format csv -d %s -o run -- \\" % trace_dir,
-             "    python3 bench.py --no-cpu-baseline",
-             "python3 bench.py --stats-summary %s > profiles/kernel_durations_bench_workloads.md" % trace_dir,
+             "    python3 bench.py " + (NET_PROFILE_ARGS if net else PROFILE_ARGS),
+             "python3 bench.py --%s %s > profiles/%s" % ("net-stats-summary" if net else "stats-summary",
+                                                        trace_dir, out_file),
              "```", "",
              "Durations in microseconds over every dispatch of the run (warmup included). The bench's",
              "own per-launch event timings of the same run are printed in its JSON line.", "",
-             "| kernel | bench case | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+             "| kernel | %s | calls | avg us | min us | max us |" % ("layer" if net else "bench case"),
+             "|---|---|---|---|---|---|"]
     with open(files[0]) as fh:
         for r in csv.DictReader(fh):
             k = _short_kernel(r["Name"])
@@ -298,88 +335,130 @@ def _layer_cases(torch, isa, stream, x, w, b, relu, sets, label):
     return cases
 
 
-def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup):
-    """Other workloads, each timed on its own (not part of the headline step)."""
+SECONDARY_GROUPS = ("fp32_layer", "fp16_layer", "upscale_chain", "pages_net")
+
+
+def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECONDARY_GROUPS):
+    """Other workloads, each timed on its own (not part of the headline step); `groups` names
+    which of SECONDARY_GROUPS to run."""
     out = {}
-    x, w, b = synth.cnn_layer_f32()
-    cases = _layer_cases(torch, isa, stream, x, w, b, True, 4, "fp32 layer 1x32x720x1280 -> 32, 3x3")
-    ms_step, per, _ = _time_cases(torch, cases, steps, warmup, stream_obj)
-    ms = sum(per) / len(per)
-    c = cases[0]
-    out["cnn_layer_f32"] = {"workload": c.name + ", bias, ReLU", "kernel": c.kernel, "ms_per_frame": round(ms, 4),
-                            "gflops": round(c.flops / ms / 1e6, 1),
-                            "frac_fp32_valu": round(c.flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
-                            "frac_fp32_packed_peak": round(c.flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
-                            "roofline": _roofline(c, ms)}
-    for c in cases:
-        c.keep = None
+    if "fp32_layer" in groups:
+        x, w, b = synth.cnn_layer_f32()
+        cases = _layer_cases(torch, isa, stream, x, w, b, True, 4, "fp32 layer 1x32x720x1280 -> 32, 3x3")
+        ms_step, per, _ = _time_cases(torch, cases, steps, warmup, stream_obj)
+        ms = sum(per) / len(per)
+        c = cases[0]
+        out["cnn_layer_f32"] = {"workload": c.name + ", bias, ReLU", "kernel": c.kernel, "ms_per_frame": round(ms, 4),
+                                "gflops": round(c.flops / ms / 1e6, 1),
+                                "frac_fp32_valu": round(c.flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
+                                "frac_fp32_packed_peak": round(c.flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
+                                "roofline": _roofline(c, ms)}
+        for c in cases:
+            c.keep = None
 
-    # fp16 NHWC layer on the matrix cores.
-    x, w, b = synth.cnn_layer_f16_nhwc()
-    plan = isa.Plan(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16", False))
-    info = plan.info()
-    wd, bd = torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
-    mcases = []
-    for _ in range(4):
-        xd = torch.from_numpy(x).cuda()
-        yd = torch.empty((8, 256, 256, 64), dtype=torch.float16, device="cuda")
+    if "fp16_layer" in groups:
+        # fp16 NHWC layer on the matrix cores.
+        x, w, b = synth.cnn_layer_f16_nhwc()
+        plan = isa.Plan(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16", False))
+        info = plan.info()
+        wd, bd = torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
+        mcases = []
+        for _ in range(4):
+            xd = torch.from_numpy(x).cuda()
+            yd = torch.empty((8, 256, 256, 64), dtype=torch.float16, device="cuda")
 
-        def launch(xd=xd, yd=yd):
-            isa.conv2d_forward(plan.handle, xd.data_ptr(), wd.data_ptr(), bd.data_ptr(), yd.data_ptr(), stream)
+            def launch(xd=xd, yd=yd):
+                isa.conv2d_forward(plan.handle, xd.data_ptr(), wd.data_ptr(), bd.data_ptr(), yd.data_ptr(), stream)
 
-        c = Case("fp16 NHWC layer 8x256x256x64 -> 64, 3x3", launch, info["flops"], info["bytes"], info["kernel"])
-        c.keep = (xd, yd)
-        mcases.append(c)
-    _, per, _ = _time_cases(torch, mcases, steps, warmup, stream_obj)
-    ms = sum(per) / len(per)
-    c = mcases[0]
-    ach = c.flops / ms / 1e9
-    out["mfma_layer_f16"] = {"workload": c.name + ", fp32 accumulate, fp16 out", "kernel": c.kernel,
-                             "ms": round(ms, 4), "gflops": round(c.flops / ms / 1e6, 1),
-                             "gbs": round(c.bytes / ms / 1e6, 1),
-                             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
-                                          "unit": "TFLOP/s", "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4),
-                                          "hbm_frac": round(c.bytes / ms / 1e6 / HBM_PEAK_GBS, 4),
-                                          "traffic": _traffic(c.name)}}
-    for c in mcases:
-        c.keep = None
-    del plan
+            c = Case("fp16 NHWC layer 8x256x256x64 -> 64, 3x3", launch, info["flops"], info["bytes"], info["kernel"])
+            c.keep = (xd, yd)
+            mcases.append(c)
+        _, per, _ = _time_cases(torch, mcases, steps, warmup, stream_obj)
+        ms = sum(per) / len(per)
+        c = mcases[0]
+        ach = c.flops / ms / 1e9
+        out["mfma_layer_f16"] = {"workload": c.name + ", fp32 accumulate, fp16 out", "kernel": c.kernel,
+                                 "ms": round(ms, 4), "gflops": round(c.flops / ms / 1e6, 1),
+                                 "gbs": round(c.bytes / ms / 1e6, 1),
+                                 "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
+                                              "unit": "TFLOP/s", "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4),
+                                              "hbm_frac": round(c.bytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                              "traffic": _traffic(c.name)}}
+        for c in mcases:
+            c.keep = None
+        del plan
 
-    # Upscaling chain on a 1280x720 frame: fused kernel and layer by layer.
-    x, layers = synth.chain_f32()
-    spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
-    flops = sum(2.0 * 720 * 1280 * k * c * r * r for (c, k, r, _) in spec)
-    nbytes = 4.0 * (720 * 1280 * 5) + sum(4.0 * (k * c * r * r + k) for (c, k, r, _) in spec)
-    wl = [(torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()) for (w, b, _) in layers]
-    for mode_name, mode in (("fused", isa.IS_CHAIN_FUSED), ("unfused", isa.IS_CHAIN_UNFUSED)):
-        d = isa.make_chain_desc(1, 720, 1280, spec, 2, mode)
-        kname = isa.conv_chain_kernel_name(d)
+    if "upscale_chain" in groups:
+        # Upscaling chain on a 1280x720 frame: fused kernel and layer by layer.
+        x, layers = synth.chain_f32()
+        spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
+        flops = sum(2.0 * 720 * 1280 * k * c * r * r for (c, k, r, _) in spec)
+        nbytes = 4.0 * (720 * 1280 * 5) + sum(4.0 * (k * c * r * r + k) for (c, k, r, _) in spec)
+        wl = [(torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()) for (w, b, _) in layers]
+        for mode_name, mode in (("fused", isa.IS_CHAIN_FUSED), ("unfused", isa.IS_CHAIN_UNFUSED)):
+            d = isa.make_chain_desc(1, 720, 1280, spec, 2, mode)
+            kname = isa.conv_chain_kernel_name(d)
+            ws_bytes = isa.conv_chain_workspace_size(d)
+            ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+            ccases = []
+            for _ in range(16):
+                xd = torch.from_numpy(x).cuda()
+                yd = torch.empty((1, 1, 1440, 2560), dtype=torch.float32, device="cuda")
+
+                def launch(d=d, xd=xd, yd=yd, ws=ws, ws_bytes=ws_bytes):
+                    isa.conv_chain_forward(d, xd.data_ptr(), [w.data_ptr() for (w, _) in wl],
+                                           [b.data_ptr() for (_, b) in wl], yd.data_ptr(),
+                                           ws.data_ptr() if ws_bytes else None, ws_bytes, stream)
+
+                c = Case("upscaling chain 1280x720 (%s)" % mode_name, launch, flops, nbytes, kname)
+                c.keep = (xd, yd)
+                ccases.append(c)
+            _, per, _ = _time_cases(torch, ccases, steps, warmup, stream_obj)
+            ms = sum(per) / len(per)
+            out["upscale_chain_" + mode_name] = {
+                "workload": ccases[0].name + ": 5x5 1->32, 3x3 32->32 x2, 3x3 32->4, depth-to-space x2",
+                "kernel": kname, "ms_per_frame": round(ms, 4), "gflops": round(flops / ms / 1e6, 1),
+                "frac_fp32_valu": round(flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
+                "frac_fp32_packed_peak": round(flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
+                # both paths run the two 32 -> 32 layers (90% of the FLOPs) on the
+                # fp32 matrix cores
+                "roofline": _roofline(ccases[0], ms, mfma_f32=True)}
+            for c in ccases:
+                c.keep = None
+            del ws
+
+    if "pages_net" in groups:
+        # The pages' own net in fp16 storage, layer by layer on the matrix cores.
+        x, layers = synth.chain_f16_nhwc()
+        spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
+        flops = sum(2.0 * 720 * 1280 * k * c * r * r for (c, k, r, _) in spec)
+        nbytes = 2.0 * 720 * 1280 * (1 + 9) + sum(2.0 * k * c * r * r + 4.0 * k for (c, k, r, _) in spec)
+        wl = [(torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()) for (w, b, _) in layers]
+        d = isa.make_chain_desc(1, 720, 1280, spec, 3, isa.IS_CHAIN_AUTO, "f16")
         ws_bytes = isa.conv_chain_workspace_size(d)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-        ccases = []
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        ncases = []
         for _ in range(16):
             xd = torch.from_numpy(x).cuda()
-            yd = torch.empty((1, 1, 1440, 2560), dtype=torch.float32, device="cuda")
+            yd = torch.empty((1, 2160, 3840, 1), dtype=torch.float16, device="cuda")
 
-            def launch(d=d, xd=xd, yd=yd, ws=ws, ws_bytes=ws_bytes):
+            def launch(xd=xd, yd=yd):
                 isa.conv_chain_forward(d, xd.data_ptr(), [w.data_ptr() for (w, _) in wl],
-                                       [b.data_ptr() for (_, b) in wl], yd.data_ptr(),
-                                       ws.data_ptr() if ws_bytes else None, ws_bytes, stream)
+                                       [b.data_ptr() for (_, b) in wl], yd.data_ptr(), ws.data_ptr(), ws_bytes, stream)
 
-            c = Case("upscaling chain 1280x720 (%s)" % mode_name, launch, flops, nbytes, kname)
+            c = Case("pages' net fp16 1280x720", launch, flops, nbytes, "layer_by_layer")
             c.keep = (xd, yd)
-            ccases.append(c)
-        _, per, _ = _time_cases(torch, ccases, steps, warmup, stream_obj)
+            ncases.append(c)
+        _, per, _ = _time_cases(torch, ncases, steps, warmup, stream_obj)
         ms = sum(per) / len(per)
-        out["upscale_chain_" + mode_name] = {
-            "workload": ccases[0].name + ": 5x5 1->32, 3x3 32->32 x2, 3x3 32->4, depth-to-space x2",
-            "kernel": kname, "ms_per_frame": round(ms, 4), "gflops": round(flops / ms / 1e6, 1),
-            "frac_fp32_valu": round(flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
-            "frac_fp32_packed_peak": round(flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
-            # both paths run the two 32 -> 32 layers (90% of the FLOPs) on the
-            # fp32 matrix cores
-            "roofline": _roofline(ccases[0], ms, mfma_f32=True)}
-        for c in ccases:
+        ach = flops / ms / 1e9
+        out["pages_net_f16"] = {
+            "workload": ncases[0].name + ": 5x5 1->64, 3x3 64->64, 64->32, 32->9, depth-to-space x3, "
+                        "fp16 storage, fp32 accumulate",
+            "kernel": "layer_by_layer", "ms_per_frame": round(ms, 4), "gflops": round(flops / ms / 1e6, 1),
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None}}
+        for c in ncases:
             c.keep = None
         del ws
     return out
@@ -499,12 +578,18 @@ def main():
                     help="least warmup time per timed group, seconds (default %(default)s)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--secondary", default=",".join(SECONDARY_GROUPS),
+                    help="comma-separated secondary workloads to run (default: all of %(default)s); "
+                         "the counter runs keep the pages' net apart, because its 64 -> 64 layer runs the "
+                         "same kernel as the fp16 layer workload")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script and exit (no GPU needed)")
     ap.add_argument("--stats-summary", metavar="TRACE_DIR",
                     help="print the kernel-duration summary of a rocprofv3 --kernel-trace --stats run of "
                          "this script and exit (no GPU needed)")
+    ap.add_argument("--net-stats-summary", metavar="TRACE_DIR",
+                    help="as --stats-summary, for a kernel-trace run of the pages' net alone")
     ap.add_argument("--lds-study", action="store_true",
                     help="time only the LDS-staged kernels (fp16 layer under each swizzle, fp32 layer, fused "
                          "chain), for a counter run of their bank conflicts")
@@ -517,6 +602,9 @@ def main():
         return
     if args.stats_summary:
         sys.stdout.write(stats_summary(args.stats_summary))
+        return
+    if args.net_stats_summary:
+        sys.stdout.write(stats_summary(args.net_stats_summary, net=True))
         return
     if args.pmc_lds_summary:
         sys.stdout.write(pmc_lds_summary(args.pmc_lds_summary))
@@ -567,7 +655,11 @@ def main():
         c.keep = None
     torch.cuda.empty_cache()
     if not args.headline_only:
-        out["secondary"] = _secondary(torch, isa, synth, stream, stream_obj, args.steps, args.warmup)
+        groups = tuple(g for g in args.secondary.split(",") if g)
+        for g in groups:
+            if g not in SECONDARY_GROUPS:
+                raise SystemExit("unknown secondary workload %r (choose from %s)" % (g, ", ".join(SECONDARY_GROUPS)))
+        out["secondary"] = _secondary(torch, isa, synth, stream, stream_obj, args.steps, args.warmup, groups)
         torch.cuda.empty_cache()
 
     out["copy_reference"] = _copy_reference(torch, stream_obj)

@@ -268,5 +268,5 @@ def test_f16_chain_descriptor_checks():
     for k, r in ((64, 5), (32, 3), (16, 5)):
         info = isa.Plan(isa.make_desc(1, 1, 720, 1280, k, r, r, "f16", True)).info()
         assert info["kernel"] == "is_k6_head_f16"
-        assert info["tile"] == (64, 16)
+        assert info["tile"] == (64, 32)
     assert isa.Plan(isa.make_desc(1, 1, 72, 128, 8, 3, 3, "f16", True)).info()["kernel"] != "is_k6_head_f16"
