@@ -16,15 +16,16 @@ from ._abi import (IS_F16, IS_F32, IS_NCHW, IS_NHWC, IS_CHAIN_AUTO, IS_CHAIN_FUS
 __all__ = ["conv2d_create", "conv2d_forward", "conv2d_destroy", "conv2d_get_plan_info",
            "conv_chain_workspace_size", "conv_chain_forward", "conv_chain_kernel_name",
            "is_lds_tile_bytes", "is_swizzle_col", "is_version", "make_desc", "make_chain_desc",
-           "conv2d", "conv_chain", "Plan", "ImgStencilError"]
+           "conv2d", "conv2d_separable", "conv_chain", "Plan", "ImgStencilError"]
 
 
 def load():
     return _abi.load()
 
 
-def make_desc(n, c, h, w, k, r, s, dtype="f32", relu=False):
-    """conv2d_desc for a same-padded stride-1 layer; f32 is NCHW, f16 is NHWC."""
+def make_desc(n, c, h, w, k, r, s, dtype="f32", relu=False, separable=False):
+    """conv2d_desc for a same-padded stride-1 layer; f32 is NCHW, f16 is NHWC.
+    separable: the filter is given as R column taps then S row taps."""
     d = conv2d_desc()
     d.n, d.c, d.h, d.w, d.k, d.r, d.s = n, c, h, w, k, r, s
     d.pad_h, d.pad_w = (r - 1) // 2, (s - 1) // 2
@@ -38,6 +39,7 @@ def make_desc(n, c, h, w, k, r, s, dtype="f32", relu=False):
     else:
         raise ValueError("dtype must be 'f32' (NCHW) or 'f16' (NHWC)")
     d.relu = int(bool(relu))
+    d.separable = int(bool(separable))
     return d
 
 
@@ -174,6 +176,23 @@ def conv2d(x, w, b=None, relu=False):
     if Cx != C:
         raise ValueError("channel mismatch")
     p = Plan(make_desc(N, C, H, W, K, R, S, "f16" if f16 else "f32", relu))
+    return p.forward(x, w, b, y)
+
+
+def conv2d_separable(x, col, row, b=None, relu=False):
+    """Single-channel fp32 filtering with the separable filter w[i][j] =
+    col[i] * row[j]: x N,1,H,W; col R taps, row S taps (device tensors)."""
+    import torch
+    _check_dev(x, torch.float32, "x")
+    _check_dev(col, torch.float32, "col")
+    _check_dev(row, torch.float32, "row")
+    if b is not None:
+        _check_dev(b, torch.float32, "b")
+    N, C, H, W = x.shape
+    R, S = col.numel(), row.numel()
+    w = torch.cat([col.reshape(-1), row.reshape(-1)])
+    y = torch.empty((N, 1, H, W), dtype=x.dtype, device=x.device)
+    p = Plan(make_desc(N, C, H, W, 1, R, S, "f32", relu, separable=True))
     return p.forward(x, w, b, y)
 
 

@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "IS_OK", 1: "IS_ERR_INVALID_ARG", 2: "IS_ERR_UNSUPPORTED", 3:
 class conv2d_desc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in
                 ("n", "c", "h", "w", "k", "r", "s", "pad_h", "pad_w", "stride_h", "stride_w",
-                 "in_dtype", "out_dtype", "layout", "relu")]
+                 "in_dtype", "out_dtype", "layout", "relu", "separable")]
 
 
 class conv2d_plan_info(ctypes.Structure):

@@ -40,9 +40,13 @@ is_status validate(const conv2d_desc *d) {
   if (d->pad_h != (d->r - 1) / 2 || d->pad_w != (d->s - 1) / 2) return IS_ERR_INVALID_ARG;
   if (d->r > 31 || d->s > 31) return IS_ERR_UNSUPPORTED;
   if (d->relu != 0 && d->relu != 1) return IS_ERR_INVALID_ARG;
+  if (d->separable != 0 && d->separable != 1) return IS_ERR_INVALID_ARG;
   const bool f32 = d->in_dtype == IS_F32 && d->out_dtype == IS_F32 && d->layout == IS_NCHW;
   const bool f16 = d->in_dtype == IS_F16 && d->out_dtype == IS_F16 && d->layout == IS_NHWC;
   if (!f32 && !f16) return IS_ERR_UNSUPPORTED;
+  // Separable filters: the single-channel fp32 kernel only.
+  if (d->separable && (!f32 || d->c != 1 || d->k != 1 || d->r != d->s || d->r < 3 || d->r > 7))
+    return IS_ERR_UNSUPPORTED;
   // Element counts must stay addressable with 64-bit offsets and 32-bit grids.
   const double in_elems = (double)d->n * d->c * d->h * d->w;
   const double out_elems = (double)d->n * d->k * d->h * d->w;
@@ -68,10 +72,11 @@ void fill_info(const is::Plan &p, conv2d_plan_info *info) {
   info->tile_w = p.tile_w;
   info->tile_h = p.tile_h;
   const conv2d_desc &d = p.d;
-  info->flops = 2.0 * d.n * d.k * d.c * d.r * d.s * (double)d.h * d.w;
+  const double taps = d.separable ? (double)(d.r + d.s) : (double)d.r * d.s;
+  info->flops = 2.0 * d.n * d.k * d.c * taps * (double)d.h * d.w;
   const double es = (double)elem_size(d.in_dtype);
   info->bytes = es * ((double)d.n * d.c * d.h * d.w + (double)d.n * d.k * d.h * d.w +
-                      (double)d.k * d.c * d.r * d.s) +
+                      (double)d.k * d.c * taps) +
                 4.0 * d.k;
 }
 
@@ -80,9 +85,13 @@ is_status make_plan(const conv2d_desc *d, is::Plan &p) {
   if (st != IS_OK) return st;
   memset(&p, 0, sizeof(p));
   p.d = *d;
-  if (!is::configure_single(p) && !is::configure_mfma_f32(p) && !is::configure_multi(p) &&
-      !is::configure_mfma(p) && !is::configure_head_f16(p))
+  if (d->separable) {
+    // Only the single-channel kernel evaluates separable filters.
+    if (!is::configure_single(p)) return IS_ERR_UNSUPPORTED;
+  } else if (!is::configure_single(p) && !is::configure_mfma_f32(p) && !is::configure_multi(p) &&
+             !is::configure_mfma(p) && !is::configure_head_f16(p)) {
     is::configure_generic(p);
+  }
   if (log_enabled())
     fprintf(stderr, "[imgstencil] n=%d c=%d h=%d w=%d k=%d r=%d s=%d -> %s grid=%d block=%d lds=%d\n",
             d->n, d->c, d->h, d->w, d->k, d->r, d->s, p.name, p.grid_x, p.block, p.lds);

@@ -20,7 +20,11 @@
 //  * the filter sits in scalar registers (wave-uniform operand of every FMA),
 //    the analogue of the page's constant-memory broadcast;
 //  * the next rows are prefetched U steps ahead into registers (the page's
-//    prefetch that overlaps global loads with the FMAs).
+//    prefetch that overlaps global loads with the FMAs);
+//  * separable filters w[u][v] = col[u] * row[v] (SEP): each input row is
+//    filtered once along the row (S FMAs per pixel) and that row result enters
+//    the R rolling output rows with the column taps (R FMAs), R + S FMAs per
+//    pixel instead of R * S.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -90,7 +94,7 @@ __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, int off_m, i
     h.v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off_h + 4 * i, 0, 0));
 }
 
-template <int R, int S, bool VEC, bool RELU>
+template <int R, int S, bool VEC, bool RELU, bool SEP>
 __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ x,
                                                      const float *__restrict__ w,
                                                      const float *__restrict__ bias,
@@ -121,9 +125,11 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
   const int off_m = 4 * col;
   const int off_h = lane == 0 ? 4 * (x0 - Q) : (lane == kWave - 1 ? 4 * (x0 + kSegCols) : INT_MIN);
 
-  float wr[R * S];
+  // Taps: R*S filter values, or (SEP) R column taps then S row taps.
+  constexpr int NTAPS = SEP ? R + S : R * S;
+  float wr[NTAPS];
 #pragma unroll
-  for (int i = 0; i < R * S; ++i) wr[i] = w[i];
+  for (int i = 0; i < NTAPS; ++i) wr[i] = w[i];
   const float bv = bias ? bias[0] : 0.f;
 
   // Input rows this strip needs: y0-P .. y0+rows_out-1+P, clipped to the image.
@@ -177,6 +183,17 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
         win[Q + 3 + q] = from_next_lane(c.v[q - 1], h.v[q - 1]);
       }
 
+      // SEP: the row pass of this input row, once for all R output rows.
+      float hrow[4];
+      if constexpr (SEP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hrow[i] = wr[R] * win[i];
+#pragma unroll
+          for (int v = 1; v < S; ++v) hrow[i] = __builtin_fmaf(wr[R + v], win[i + v], hrow[i]);
+        }
+      }
+
       // Input row r feeds relative output rows r-2P+j, j = 0..R-1, with
       // filter row R-1-j. j = R-1 is the first contribution to output row r:
       // it starts that slot with product + bias instead of clearing it.
@@ -187,6 +204,13 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
         if ((FIRST && p + j < 2 * P) || (LAST && p + j >= U)) continue;
         const int slot = (p + j) % R;
         const int u = R - 1 - j;
+        if constexpr (SEP) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[slot][i] = j == R - 1 ? __builtin_fmaf(wr[u], hrow[i], bv)
+                                      : __builtin_fmaf(wr[u], hrow[i], acc[slot][i]);
+          continue;
+        }
 #pragma unroll
         for (int v = 0; v < S; ++v)
 #pragma unroll
@@ -240,12 +264,27 @@ using K1Fn = void (*)(const float *, const float *, const float *, float *, int,
 template <bool VEC, bool RELU>
 K1Fn pick(int r, int s) {
 #define IS_K1_CASE(RR, SS) \
-  if (r == RR && s == SS) return is_k1_single<RR, SS, VEC, RELU>;
+  if (r == RR && s == SS) return is_k1_single<RR, SS, VEC, RELU, false>;
 #define IS_K1_ROW(RR) IS_K1_CASE(RR, 1) IS_K1_CASE(RR, 3) IS_K1_CASE(RR, 5) IS_K1_CASE(RR, 7)
   IS_K1_ROW(1) IS_K1_ROW(3) IS_K1_ROW(5) IS_K1_ROW(7)
 #undef IS_K1_ROW
 #undef IS_K1_CASE
   return nullptr;
+}
+
+// Separable filters, square sizes.
+template <bool VEC, bool RELU>
+K1Fn pick_sep(int r, int s) {
+  if (r != s) return nullptr;
+  if (r == 3) return is_k1_single<3, 3, VEC, RELU, true>;
+  if (r == 5) return is_k1_single<5, 5, VEC, RELU, true>;
+  if (r == 7) return is_k1_single<7, 7, VEC, RELU, true>;
+  return nullptr;
+}
+
+template <bool VEC, bool RELU>
+K1Fn pick_any(const conv2d_desc &d) {
+  return d.separable ? pick_sep<VEC, RELU>(d.r, d.s) : pick<VEC, RELU>(d.r, d.s);
 }
 
 }  // namespace
@@ -254,7 +293,7 @@ bool configure_single(Plan &p) {
   const conv2d_desc &d = p.d;
   if (d.c != 1 || d.k != 1 || d.layout != IS_NCHW || d.in_dtype != IS_F32) return false;
   if (d.r > 7 || d.s > 7) return false;
-  if (pick<true, false>(d.r, d.s) == nullptr) return false;
+  if (pick_any<true, false>(d) == nullptr) return false;
   const int nseg = (d.w + kSegCols - 1) / kSegCols;
   // Strip height: a wave keeps about one prefetch window of rows in flight, so
   // the bytes in flight per CU grow with the number of resident waves. 64 rows
@@ -266,7 +305,7 @@ bool configure_single(Plan &p) {
   while (rows > 8 && (long long)nseg * ((d.h + rows - 1) / rows) * d.n < 4096) rows >>= 1;
   const int nstrip = (d.h + rows - 1) / rows;
   p.kid = kSingleChannel;
-  p.name = "is_k1_single";
+  p.name = d.separable ? "is_k1_single_separable" : "is_k1_single";
   p.nseg = nseg;
   p.nstrip = nstrip;
   p.strip_rows = rows;
@@ -285,8 +324,8 @@ bool configure_single(Plan &p) {
 hipError_t launch_single(const Plan &p, const float *x, const float *w, const float *b, float *y,
                          hipStream_t s) {
   const bool relu = p.d.relu != 0;
-  const K1Fn fn = p.vec ? (relu ? pick<true, true>(p.d.r, p.d.s) : pick<true, false>(p.d.r, p.d.s))
-                        : (relu ? pick<false, true>(p.d.r, p.d.s) : pick<false, false>(p.d.r, p.d.s));
+  const K1Fn fn = p.vec ? (relu ? pick_any<true, true>(p.d) : pick_any<true, false>(p.d))
+                        : (relu ? pick_any<false, true>(p.d) : pick_any<false, false>(p.d));
   if (!fn) return hipErrorInvalidValue;
   return launch_kernel(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, p.d.h, p.d.w,
                      p.strip_rows, p.nseg, p.nstrip, p.ntiles);

@@ -280,9 +280,16 @@ template <bool RELU>
 K2Fn pick(int r, int ft, int cs) {
 #define IS_K2_CASE(RR, FF, CC) \
   if (r == RR && ft == FF && cs == CC) return is_k2_multi<RR, FF, CC, RELU, false>;
+  // multi-channel layers (slabs of 4 channels)
   IS_K2_CASE(3, 32, 4) IS_K2_CASE(3, 16, 4) IS_K2_CASE(3, 8, 4) IS_K2_CASE(3, 4, 4)
-  IS_K2_CASE(5, 32, 1) IS_K2_CASE(5, 32, 4) IS_K2_CASE(3, 32, 1) IS_K2_CASE(1, 32, 4)
-  IS_K2_CASE(5, 16, 1) IS_K2_CASE(3, 16, 1)
+  IS_K2_CASE(5, 32, 4) IS_K2_CASE(1, 32, 4) IS_K2_CASE(1, 16, 4) IS_K2_CASE(1, 8, 4)
+  IS_K2_CASE(1, 4, 4)
+  // one input channel and F filters (the page's special case with F > 1)
+  IS_K2_CASE(5, 32, 1) IS_K2_CASE(3, 32, 1) IS_K2_CASE(1, 32, 1)
+  IS_K2_CASE(5, 16, 1) IS_K2_CASE(3, 16, 1) IS_K2_CASE(1, 16, 1)
+  IS_K2_CASE(5, 8, 1) IS_K2_CASE(3, 8, 1) IS_K2_CASE(1, 8, 1)
+  IS_K2_CASE(5, 4, 1) IS_K2_CASE(3, 4, 1) IS_K2_CASE(1, 4, 1)
+  IS_K2_CASE(5, 2, 1) IS_K2_CASE(3, 2, 1) IS_K2_CASE(1, 2, 1)
 #undef IS_K2_CASE
   return nullptr;
 }
@@ -306,7 +313,7 @@ bool configure_multi(Plan &p) {
   // stores in sequence; 16 channels give twice the workgroups to overlap those
   // phases (the 1 -> 32 5x5 layer of a 1280x720 frame: 35.5 against 38.5 us).
   int ft = 0;
-  for (int f : {32, 16, 8, 4})
+  for (int f : {32, 16, 8, 4, 2})
     if (d.k % f == 0 && !(d.c == 1 && f == 32 && d.k % 16 == 0 && pick<false>(d.r, 16, cs))) {
       ft = f;
       break;

@@ -67,7 +67,15 @@ typedef enum { IS_NCHW = 0, IS_NHWC = 1 } is_layout;
  *  in_dtype / out_dtype: (IS_F32, IS_F32) with layout IS_NCHW, or
  *                        (IS_F16, IS_F16) with layout IS_NHWC
  *  layout     : memory order of x and y: NCHW (x[n][c][i][j]) or NHWC (x[n][i][j][c])
- *  relu       : 0 = identity, 1 = ReLU after the bias                              */
+ *  relu       : 0 = identity, 1 = ReLU after the bias
+ *  separable  : 0 = a full R x S filter per (k, c); 1 = a separable filter, the
+ *               outer product w[i][j] = col[i] * row[j] of a column filter of R
+ *               taps and a row filter of S taps, evaluated as a row pass and a
+ *               column pass ("Optimizing Memory Efficiency for Convolution
+ *               Kernels on Kepler GPUs", arXiv 1705.10591, special case of one
+ *               channel): single channel only (c = k = 1, fp32 NCHW, r = s in
+ *               {3, 5, 7}); w then holds the R column taps followed by the S
+ *               row taps. Other shapes: IS_ERR_UNSUPPORTED.                     */
 typedef struct {
   int n, c, h, w;
   int k, r, s;
@@ -76,6 +84,7 @@ typedef struct {
   is_dtype in_dtype, out_dtype;
   is_layout layout;
   int relu;
+  int separable;
 } conv2d_desc;
 
 typedef struct conv2d_plan_s *conv2d_plan;
@@ -87,7 +96,7 @@ typedef struct {
   int block;              /* threads per workgroup */
   int lds_bytes;          /* LDS per workgroup */
   int tile_w, tile_h;     /* output pixels per wave or workgroup tile */
-  double flops;           /* algorithmic: 2*N*K*C*R*S*H*W */
+  double flops;           /* algorithmic: 2*N*K*C*R*S*H*W (separable: 2*N*(R+S)*H*W) */
   double bytes;           /* algorithmic: x + y + w + b, each once */
 } conv2d_plan_info;
 
@@ -101,7 +110,8 @@ is_status conv2d_create(const conv2d_desc *d, conv2d_plan *out);
 
 /* Enqueue y = act(conv(x, w) + bias) on `stream`.
  *  x: input in the plan's layout and dtype, N*C*H*W elements
- *  w: K*C*R*S weights in the input dtype
+ *  w: K*C*R*S weights in the input dtype (separable plans: R + S fp32 values,
+ *     the column taps then the row taps)
  *  bias: K fp32 values, or NULL
  *  y: output in the plan's layout and dtype, N*K*H*W elements (written in full)
  * Errors: IS_ERR_INVALID_ARG (null plan/x/w/y, x and y overlap),

@@ -111,6 +111,15 @@ def conv2d(x, w, b=None, relu=False, layout="NCHW", lib=None):
     return y, m
 
 
+def conv2d_separable(x, col, row, b=None, relu=False):
+    """Single-channel filtering with a separable filter: by definition the
+    filter is the outer product w[i][j] = col[i] * row[j] (R column taps, S row
+    taps), applied as any other filter. x: N,1,H,W; returns (y, m) float64."""
+    col, row = _f64(col).reshape(-1), _f64(row).reshape(-1)
+    w = (col[:, None] * row[None, :])[None, None]
+    return conv2d(x, w, b, relu)
+
+
 def conv2d_points(x, w, b, relu, pts, layout="NCHW"):
     """y and m at selected outputs; pts is an (npts, 4) int array of (n, k, i, j)."""
     x, w = _f64(x), _f64(w)

@@ -217,6 +217,32 @@ def test_swizzle_worked_example():
         assert got == passes, (rows, cols, layout, access, got, passes)
 
 
+def test_separable_and_special_case_plans():
+    """Separable filters: single channel fp32 only, square 3/5/7; counted work
+    2 (R + S) per pixel. One channel with F filters and 1x1 layers go to the
+    register-blocked kernel when F (or K) is even."""
+    d = isa.make_desc(1, 1, 8192, 8192, 1, 7, 7, separable=True)
+    info = isa.Plan(d).info()
+    assert info["kernel"] == "is_k1_single_separable"
+    assert info["flops"] == 2 * 14 * 8192 * 8192
+    assert info["bytes"] == 4 * (2 * 8192 * 8192 + 14) + 4
+    for bad in (isa.make_desc(1, 2, 64, 64, 1, 3, 3, separable=True),
+                isa.make_desc(1, 1, 64, 64, 2, 3, 3, separable=True),
+                isa.make_desc(1, 1, 64, 64, 1, 3, 5, separable=True),
+                isa.make_desc(1, 1, 64, 64, 1, 9, 9, separable=True),
+                isa.make_desc(1, 1, 64, 64, 1, 1, 1, separable=True),
+                isa.make_desc(1, 1, 64, 64, 1, 3, 3, "f16", separable=True)):
+        with pytest.raises(isa.ImgStencilError):
+            isa.Plan(bad)
+    weird = isa.make_desc(1, 1, 64, 64, 1, 3, 3)
+    weird.separable = 2
+    with pytest.raises(isa.ImgStencilError):
+        isa.Plan(weird)
+    for (c, k, r) in ((1, 4, 3), (1, 8, 5), (1, 2, 1), (1, 6, 3), (8, 16, 1), (3, 4, 1)):
+        assert isa.Plan(isa.make_desc(1, c, 64, 128, k, r, r)).info()["kernel"] == "is_k2_multi", (c, k, r)
+    assert isa.Plan(isa.make_desc(1, 1, 64, 128, 3, 3, 3)).info()["kernel"] == "is_k0_generic_nchw_f32"
+
+
 def test_chain_descriptor_checks():
     d = isa.make_chain_desc(1, 16, 16, [(1, 8, 5, True), (8, 4, 3, False)], depth_to_space=2)
     ws = isa.conv_chain_workspace_size(d)

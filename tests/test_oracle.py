@@ -22,6 +22,22 @@ def test_oracle_pin(pin):
     pin(_conv)
 
 
+def test_separable_entry_is_row_then_column_pass():
+    """conv2d_separable(x, col, row) equals a horizontal 1D pass with `row`
+    followed by a vertical 1D pass with `col` (zero padding in each), for
+    non-square sizes too, so that swapping the two tap vectors fails."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((2, 1, 13, 17))
+    for R, S in ((3, 3), (5, 5), (7, 7), (3, 7), (7, 1)):
+        col, row = rng.standard_normal(R), rng.standard_normal(S)
+        b = rng.standard_normal(1)
+        y, m = oracle.conv2d_separable(x, col, row, b, False)
+        want = oracle_pins._corr1d_cols(oracle_pins._corr1d_rows(x, row), col) + b[0]
+        assert np.all(np.abs(y - want) <= oracle_pins.TIGHT * m + 1e-300), (R, S)
+        y_relu, _ = oracle.conv2d_separable(x, col, row, b, True)
+        np.testing.assert_array_equal(y_relu, np.maximum(y, 0.0))
+
+
 def test_points_match_full():
     x, w, b = synth.cnn_layer_f32(N=2, C=3, K=5, H=9, W=14, R=3, seed=11)
     y, m = oracle.conv2d(x, w, b, True)
