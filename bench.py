@@ -42,12 +42,14 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0
 # source changes, the case reports traffic null until the counters are re-taken.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 TRAFFIC_KERNELS = {   # bench case -> (kernel as the profiler names it, its source files)
-    "8192x8192 3x3": ("is_k1_single<3, 3, true, false>", ("k1_single.hip",)),
-    "8192x8192 5x5": ("is_k1_single<5, 5, true, false>", ("k1_single.hip",)),
-    "8192x8192 7x7": ("is_k1_single<7, 7, true, false>", ("k1_single.hip",)),
+    "8192x8192 3x3": ("is_k1_single<3, 3, true, false, false>", ("k1_single.hip",)),
+    "8192x8192 5x5": ("is_k1_single<5, 5, true, false, false>", ("k1_single.hip",)),
+    "8192x8192 7x7": ("is_k1_single<7, 7, true, false, false>", ("k1_single.hip",)),
     "fp32 layer 1x32x720x1280 -> 32, 3x3": ("is_k5_mfma_f32", ("k5_mfma_f32.hip",)),
     "fp16 NHWC layer 8x256x256x64 -> 64, 3x3": ("is_k4_mfma<128, 64, 64>", ("k4_mfma.hip",)),
     "upscaling chain 1280x720 (fused)": ("is_k3_chain", ("k3_chain.hip",)),
+    "separable 7x7 filter, 8192x8192 fp32": ("is_k1_single<7, 7, true, false, true>", ("k1_single.hip",)),
+    "1 channel -> 8 filters 3x3, 4096x4096 fp32": ("is_k2_multi<3, 8, 1, false, false>", ("k2_multi.hip",)),
 }
 # The known-size dispatch: torch's elementwise negation of 256 MiB of fp32
 # (run by _copy_reference), which reads 256 MiB and writes 256 MiB.
@@ -117,7 +119,7 @@ def _counter_means(d, counter):
 # the bench workloads leave out the pages' net (its 64 -> 64 layer runs the same
 # kernel instance as the fp16 layer workload and would mix into that row); the
 # net has a kernel-trace run of its own.
-PROFILE_ARGS = "--no-cpu-baseline --secondary fp32_layer,fp16_layer,upscale_chain"
+PROFILE_ARGS = "--no-cpu-baseline --secondary fp32_layer,fp16_layer,upscale_chain,special_cases"
 PMC_ARGS = "--steps 2 --warmup 1 --min-warm-s 0 " + PROFILE_ARGS
 NET_PROFILE_ARGS = "--no-cpu-baseline --secondary pages_net"
 NET_KERNELS = {
@@ -335,7 +337,7 @@ def _layer_cases(torch, isa, stream, x, w, b, relu, sets, label):
     return cases
 
 
-SECONDARY_GROUPS = ("fp32_layer", "fp16_layer", "upscale_chain", "pages_net")
+SECONDARY_GROUPS = ("fp32_layer", "fp16_layer", "upscale_chain", "pages_net", "special_cases")
 
 
 def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECONDARY_GROUPS):
@@ -461,6 +463,40 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
         for c in ncases:
             c.keep = None
         del ws
+
+    if "special_cases" in groups:
+        import numpy as np
+        # The single-channel special case beyond one filter: a separable 7x7
+        # filter (row pass + column pass) and 8 filters on one channel; both
+        # are bound by HBM. Two buffer sets each, so that no launch reads the
+        # previous one's data from the last-level cache.
+        specs = [("separable_7x7_8192", "separable 7x7 filter, 8192x8192 fp32", (1, 1, 8192, 8192, 1, 7, 7), True),
+                 ("one_channel_8_filters_3x3_4096", "1 channel -> 8 filters 3x3, 4096x4096 fp32",
+                  (1, 1, 4096, 4096, 8, 3, 3), False)]
+        for key, name, (n_, c_, h_, w_, k_, r_, s_), sep in specs:
+            plan = isa.Plan(isa.make_desc(n_, c_, h_, w_, k_, r_, s_, "f32", False, separable=sep))
+            info = plan.info()
+            rng = np.random.default_rng(0)
+            wv = (rng.standard_normal(r_ + s_ if sep else k_ * c_ * r_ * s_) / r_).astype(np.float32)
+            wd = torch.from_numpy(wv).cuda()
+            scases = []
+            for _ in range(2):
+                xd = torch.rand((n_, c_, h_, w_), device="cuda")
+                yd = torch.empty((n_, k_, h_, w_), device="cuda")
+
+                def launch(plan=plan, xd=xd, yd=yd, wd=wd):
+                    isa.conv2d_forward(plan.handle, xd.data_ptr(), wd.data_ptr(), None, yd.data_ptr(), stream)
+
+                c = Case(name, launch, info["flops"], info["bytes"], info["kernel"])
+                c.keep = (xd, yd)
+                scases.append(c)
+            _, per, _ = _time_cases(torch, scases, steps, warmup, stream_obj)
+            ms = sum(per) / len(per)
+            out[key] = {"workload": name, "kernel": info["kernel"], "ms": round(ms, 4),
+                        "gflops": round(info["flops"] / ms / 1e6, 1), "roofline": _roofline(scases[0], ms)}
+            for c in scases:
+                c.keep = None
+            del plan
     return out
 
 
