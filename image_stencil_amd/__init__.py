@@ -1,7 +1,8 @@
 """Python binding of libimgstencil: direct 2D convolution with small filters on gfx950.
 
 The functions with the C names (conv2d_create, conv2d_forward, conv2d_destroy,
-conv2d_get_plan_info, conv_chain_workspace_size, conv_chain_forward,
+conv2d_get_plan_info, conv2d_list_variants, conv2d_create_variant,
+conv2d_autotune, conv_chain_workspace_size, conv_chain_forward,
 conv_chain_kernel_name, is_lds_tile_bytes, is_swizzle_col) marshal arguments to
 the C ABI of include/imgstencil.h and nothing else. conv2d() and conv_chain()
 are conveniences on torch tensors: torch only allocates device memory and
@@ -11,9 +12,10 @@ import ctypes
 
 from . import _abi
 from ._abi import (IS_F16, IS_F32, IS_NCHW, IS_NHWC, IS_CHAIN_AUTO, IS_CHAIN_FUSED, IS_CHAIN_UNFUSED,
-                   ImgStencilError, conv2d_desc, conv_chain_desc, conv2d_plan_info)
+                   ImgStencilError, conv2d_desc, conv_chain_desc, conv2d_plan_info, conv2d_variant)
 
 __all__ = ["conv2d_create", "conv2d_forward", "conv2d_destroy", "conv2d_get_plan_info",
+           "conv2d_list_variants", "conv2d_create_variant", "conv2d_autotune",
            "conv_chain_workspace_size", "conv_chain_forward", "conv_chain_kernel_name",
            "is_lds_tile_bytes", "is_swizzle_col", "is_version", "make_desc", "make_chain_desc",
            "conv2d", "conv2d_separable", "conv_chain", "Plan", "ImgStencilError"]
@@ -58,6 +60,36 @@ def conv2d_forward(plan, x_ptr, w_ptr, bias_ptr, y_ptr, stream):
 
 def conv2d_destroy(plan):
     load().conv2d_destroy(plan)
+
+
+def _variants(arr, n):
+    return [{"kernel": arr[i].kernel.decode(), "param": arr[i].param, "is_default": bool(arr[i].is_default),
+             "ms": arr[i].ms} for i in range(n)]
+
+
+def conv2d_list_variants(desc):
+    """Every kernel configuration that can run desc, the default first (dicts)."""
+    n = ctypes.c_int()
+    arr = (conv2d_variant * 32)()
+    _abi.check(load().conv2d_list_variants(ctypes.byref(desc), arr, 32, ctypes.byref(n)), "conv2d_list_variants")
+    return _variants(arr, min(n.value, 32))
+
+
+def conv2d_create_variant(desc, index):
+    plan = ctypes.c_void_p()
+    _abi.check(load().conv2d_create_variant(ctypes.byref(desc), index, ctypes.byref(plan)),
+               "conv2d_create_variant")
+    return plan.value
+
+
+def conv2d_autotune(plan, x_ptr, w_ptr, bias_ptr, y_ptr, stream, reps=10):
+    """Time every variant on these buffers, keep the fastest in the plan, and
+    return the measured variants (dicts with ms)."""
+    n = ctypes.c_int()
+    arr = (conv2d_variant * 32)()
+    _abi.check(load().conv2d_autotune(plan, x_ptr, w_ptr, bias_ptr or None, y_ptr, stream or None, reps, arr, 32,
+                                      ctypes.byref(n)), "conv2d_autotune")
+    return _variants(arr, min(n.value, 32))
 
 
 def conv2d_get_plan_info(plan):
@@ -120,11 +152,12 @@ def is_version():
 
 # ---------------------------------------------------------------- torch helpers
 class Plan:
-    """Owns a conv2d plan; forward() launches on torch's current stream."""
+    """Owns a conv2d plan; forward() launches on torch's current stream.
+    variant: index into conv2d_list_variants(desc) (None: the default)."""
 
-    def __init__(self, desc):
+    def __init__(self, desc, variant=None):
         self.desc = desc
-        self.handle = conv2d_create(desc)
+        self.handle = conv2d_create(desc) if variant is None else conv2d_create_variant(desc, variant)
         # Bound now: at interpreter exit the module's globals may already be
         # gone when __del__ runs.
         self._destroy = load().conv2d_destroy
@@ -139,6 +172,15 @@ class Plan:
         conv2d_forward(self.handle, x.data_ptr(), w.data_ptr(), b.data_ptr() if b is not None else None,
                        y.data_ptr(), stream)
         return y
+
+    def autotune(self, x, w, b, y, reps=10, stream=None):
+        """Time every variant on these tensors and keep the fastest (y is
+        overwritten with its result); returns the measured variants."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        return conv2d_autotune(self.handle, x.data_ptr(), w.data_ptr(), b.data_ptr() if b is not None else None,
+                               y.data_ptr(), stream, reps)
 
     def __del__(self):
         h = getattr(self, "handle", None)

@@ -33,6 +33,11 @@ class conv2d_plan_info(ctypes.Structure):
                 ("bytes", ctypes.c_double)]
 
 
+class conv2d_variant(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char * 64), ("param", ctypes.c_int), ("is_default", ctypes.c_int),
+                ("ms", ctypes.c_float)]
+
+
 class conv_layer_desc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in ("c", "k", "r", "s", "relu")]
 
@@ -50,6 +55,12 @@ SIGNATURES = [
     ("conv2d_forward", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     ("conv2d_destroy", None, [_vp]),
     ("conv2d_get_plan_info", ctypes.c_int, [_vp, ctypes.POINTER(conv2d_plan_info)]),
+    ("conv2d_list_variants", ctypes.c_int, [ctypes.POINTER(conv2d_desc), ctypes.POINTER(conv2d_variant),
+                                            ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
+    ("conv2d_create_variant", ctypes.c_int, [ctypes.POINTER(conv2d_desc), ctypes.c_int, ctypes.POINTER(_vp)]),
+    ("conv2d_autotune", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
+                                       ctypes.POINTER(conv2d_variant), ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_int)]),
     ("conv_chain_workspace_size", ctypes.c_int, [ctypes.POINTER(conv_chain_desc), ctypes.POINTER(ctypes.c_size_t)]),
     ("conv_chain_forward", ctypes.c_int, [ctypes.POINTER(conv_chain_desc), _vp, ctypes.POINTER(_vp),
                                           ctypes.POINTER(_vp), _vp, _vp, ctypes.c_size_t, _vp]),

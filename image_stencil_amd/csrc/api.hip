@@ -98,6 +98,77 @@ is_status make_plan(const conv2d_desc *d, is::Plan &p) {
   return IS_OK;
 }
 
+// ---- Tile variants (runtime tuning) ----------------------------------------
+//
+// A variant is a kernel family and its tuning parameter as the ABI reports it:
+// strip rows (single channel), output channels per workgroup (multi-channel),
+// LDS swizzle row bytes with 0 = none (fp16 MFMA), 0 for the others.
+struct Variant {
+  is::KernelId kid;
+  int param;
+};
+
+int public_param(const is::Plan &p) {
+  switch (p.kid) {
+    case is::kSingleChannel:
+    case is::kMultiChannel: return p.strip_rows;
+    case is::kMfmaNhwcF16: return p.vec;
+    default: return 0;
+  }
+}
+
+bool configure_variant(is::Plan &p, const conv2d_desc &d, const Variant &v) {
+  memset(&p, 0, sizeof(p));
+  p.d = d;
+  switch (v.kid) {
+    case is::kSingleChannel: return is::configure_single(p, v.param);
+    case is::kMultiChannel: return !d.separable && is::configure_multi(p, v.param);
+    case is::kMfmaNhwcF16: return !d.separable && is::configure_mfma(p, v.param == 0 ? -1 : v.param);
+    case is::kMfmaNchwF32: return !d.separable && is::configure_mfma_f32(p);
+    case is::kHeadNhwcF16: return !d.separable && is::configure_head_f16(p);
+    default:
+      if (d.separable) return false;
+      is::configure_generic(p);
+      return true;
+  }
+}
+
+// Every configuration that can run the (validated) descriptor, the default
+// plan's first, each once. The one-thread-per-output fallback is listed only
+// when no other kernel takes the shape (it is never the faster one, and on
+// large layers one timing of it would take longer than all the others).
+int collect_variants(const conv2d_desc &d, const is::Plan &def, Variant *out, int max) {
+  int n = 0;
+  auto add = [&](const is::Plan &p) {
+    const Variant v{p.kid, public_param(p)};
+    for (int i = 0; i < n; ++i)
+      if (out[i].kid == v.kid && out[i].param == v.param) return;
+    if (n < max) out[n++] = v;
+  };
+  add(def);
+  is::Plan p;
+  const Variant tries[] = {
+      {is::kSingleChannel, 16}, {is::kSingleChannel, 32}, {is::kSingleChannel, 64}, {is::kSingleChannel, 128},
+      {is::kMfmaNchwF32, 0},
+      {is::kMultiChannel, 32}, {is::kMultiChannel, 16}, {is::kMultiChannel, 8}, {is::kMultiChannel, 4},
+      {is::kMultiChannel, 2},
+      {is::kMfmaNhwcF16, 128}, {is::kMfmaNhwcF16, 0}, {is::kMfmaNhwcF16, 256},
+      {is::kHeadNhwcF16, 0}};
+  for (const Variant &v : tries)
+    if (configure_variant(p, d, v)) add(p);
+  return n;
+}
+
+constexpr int kMaxVariants = 32;
+
+void fill_variant(const is::Plan &p, bool is_default, float ms, conv2d_variant *out) {
+  memset(out, 0, sizeof(*out));
+  snprintf(out->kernel, sizeof(out->kernel), "%s", p.name);
+  out->param = public_param(p);
+  out->is_default = is_default ? 1 : 0;
+  out->ms = ms;
+}
+
 is_status run_plan(const is::Plan &p, const void *x, const void *w, const float *bias, void *y,
                    hipStream_t stream) {
   const conv2d_desc &d = p.d;
@@ -362,6 +433,100 @@ is_status conv2d_forward(conv2d_plan plan, const void *x, const void *w, const f
 }
 
 void conv2d_destroy(conv2d_plan plan) { delete plan; }
+
+is_status conv2d_list_variants(const conv2d_desc *d, conv2d_variant *out, int max, int *count) {
+  if (!count || max < 0 || (max > 0 && !out)) return IS_ERR_INVALID_ARG;
+  try {
+    is::Plan def;
+    const is_status st = make_plan(d, def);
+    if (st != IS_OK) return st;
+    Variant v[kMaxVariants];
+    const int n = collect_variants(*d, def, v, kMaxVariants);
+    *count = n;
+    for (int i = 0; i < n && i < max; ++i) {
+      is::Plan p;
+      configure_variant(p, *d, v[i]);
+      fill_variant(p, i == 0, 0.f, &out[i]);
+    }
+    return IS_OK;
+  } catch (...) {
+    return IS_ERR_NO_MEMORY;
+  }
+}
+
+is_status conv2d_create_variant(const conv2d_desc *d, int index, conv2d_plan *out) {
+  if (!out) return IS_ERR_INVALID_ARG;
+  *out = nullptr;
+  try {
+    is::Plan def;
+    const is_status st = make_plan(d, def);
+    if (st != IS_OK) return st;
+    Variant v[kMaxVariants];
+    const int n = collect_variants(*d, def, v, kMaxVariants);
+    if (index < 0 || index >= n) return IS_ERR_INVALID_ARG;
+    conv2d_plan_s *h = new (std::nothrow) conv2d_plan_s;
+    if (!h) return IS_ERR_NO_MEMORY;
+    configure_variant(h->p, *d, v[index]);
+    *out = h;
+    return IS_OK;
+  } catch (...) {
+    return IS_ERR_NO_MEMORY;
+  }
+}
+
+is_status conv2d_autotune(conv2d_plan plan, const void *x, const void *w, const float *bias, void *y,
+                          hipStream_t stream, int reps, conv2d_variant *out, int max, int *count) {
+  if (!plan || reps < 1 || max < 0 || (max > 0 && !out)) return IS_ERR_INVALID_ARG;
+  try {
+    const conv2d_desc d = plan->p.d;
+    is::Plan def;
+    is_status st = make_plan(&d, def);
+    if (st != IS_OK) return st;
+    Variant v[kMaxVariants];
+    const int n = collect_variants(d, def, v, kMaxVariants);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+      if (e0) (void)hipEventDestroy(e0);
+      return hip_status(hipErrorOutOfMemory);
+    }
+    int best = -1;
+    float best_ms = 0.f;
+    is::Plan best_plan;
+    for (int i = 0; i < n && st == IS_OK; ++i) {
+      is::Plan p;
+      configure_variant(p, d, v[i]);
+      st = run_plan(p, x, w, bias, y, stream);   // warm-up; also checks the arguments
+      if (st != IS_OK) break;
+      hipError_t e = hipEventRecord(e0, stream);
+      for (int r = 0; r < reps && st == IS_OK; ++r) st = run_plan(p, x, w, bias, y, stream);
+      if (st != IS_OK) break;
+      if (e == hipSuccess) e = hipEventRecord(e1, stream);
+      if (e == hipSuccess) e = hipEventSynchronize(e1);
+      float ms = 0.f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+      if (e != hipSuccess) {
+        st = hip_status(e);
+        break;
+      }
+      ms /= (float)reps;
+      if (i < max) fill_variant(p, i == 0, ms, &out[i]);
+      if (best < 0 || ms < best_ms) {
+        best = i;
+        best_ms = ms;
+        best_plan = p;
+      }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != IS_OK) return st;
+    if (count) *count = n;
+    plan->p = best_plan;
+    // y ends up holding the chosen variant's result.
+    return run_plan(plan->p, x, w, bias, y, stream);
+  } catch (...) {
+    return IS_ERR_NO_MEMORY;
+  }
+}
 
 is_status conv2d_get_plan_info(conv2d_plan plan, conv2d_plan_info *info) {
   if (!plan || !info) return IS_ERR_INVALID_ARG;

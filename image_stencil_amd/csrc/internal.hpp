@@ -32,15 +32,19 @@ struct Plan {
 
 // Each kernel family fills the launch geometry of a plan it accepts and
 // launches it. configure_* return false when the family cannot run the desc.
+// `param` selects one of the family's tile variants (0: the default choice):
+// strip rows for the single-channel kernel, output channels per workgroup for
+// the multi-channel kernel, LDS swizzle row bytes for the fp16 MFMA kernel;
+// a family without variants ignores it.
 bool configure_generic(Plan &p);
 hipError_t launch_generic(const Plan &p, const void *x, const void *w, const float *b, void *y,
                           hipStream_t s);
 
-bool configure_single(Plan &p);
+bool configure_single(Plan &p, int param = 0);
 hipError_t launch_single(const Plan &p, const float *x, const float *w, const float *b, float *y,
                          hipStream_t s);
 
-bool configure_multi(Plan &p);
+bool configure_multi(Plan &p, int param = 0);
 hipError_t launch_multi(const Plan &p, const float *x, const float *w, const float *b, float *y,
                         hipStream_t s);
 // The multi-channel layer with 4 output channels followed by a 2x depth-to-space
@@ -49,7 +53,7 @@ bool multi_d2s_supported(const Plan &p);
 hipError_t launch_multi_d2s(const Plan &p, const float *x, const float *w, const float *b, float *y,
                             hipStream_t s);
 
-bool configure_mfma(Plan &p);
+bool configure_mfma(Plan &p, int param = 0);
 hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
                        hipStream_t s);
 

@@ -289,7 +289,7 @@ K1Fn pick_any(const conv2d_desc &d) {
 
 }  // namespace
 
-bool configure_single(Plan &p) {
+bool configure_single(Plan &p, int param) {
   const conv2d_desc &d = p.d;
   if (d.c != 1 || d.k != 1 || d.layout != IS_NCHW || d.in_dtype != IS_F32) return false;
   if (d.r > 7 || d.s > 7) return false;
@@ -303,6 +303,10 @@ bool configure_single(Plan &p) {
   // measured slower (128 rows: -15% on the 3x3), shorter ones no faster.
   int rows = 64;
   while (rows > 8 && (long long)nseg * ((d.h + rows - 1) / rows) * d.n < 4096) rows >>= 1;
+  if (param != 0) {   // a tuning variant: 8 to 256 rows
+    if (param < 8 || param > 256) return false;
+    rows = param;
+  }
   const int nstrip = (d.h + rows - 1) / rows;
   p.kid = kSingleChannel;
   p.name = d.separable ? "is_k1_single_separable" : "is_k1_single";

@@ -303,7 +303,7 @@ K2Fn pick_d2s(int r, int ft, int cs) {
 
 }  // namespace
 
-bool configure_multi(Plan &p) {
+bool configure_multi(Plan &p, int param) {
   const conv2d_desc &d = p.d;
   if (d.layout != IS_NCHW || d.in_dtype != IS_F32 || d.r != d.s) return false;
   if (d.w % 4 != 0) return false;
@@ -318,6 +318,10 @@ bool configure_multi(Plan &p) {
       ft = f;
       break;
     }
+  if (param != 0) {   // a tuning variant: that many output channels per workgroup
+    if (d.k % param != 0) return false;
+    ft = param;
+  }
   if (ft == 0 || pick<false>(d.r, ft, cs) == nullptr) return false;
   // One slab's bytes and each image's bytes must stay below 4 GB for the
   // 32-bit buffer offsets.

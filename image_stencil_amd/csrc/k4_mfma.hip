@@ -495,7 +495,7 @@ void fill_geometry(Plan &p) {
 
 }  // namespace
 
-bool configure_mfma(Plan &p) {
+bool configure_mfma(Plan &p, int param) {
   const conv2d_desc &d = p.d;
   if (d.layout != IS_NHWC || d.in_dtype != IS_F16 || d.out_dtype != IS_F16) return false;
   if (!shape_supported(d.c, d.k) || d.r != 3 || d.s != 3) return false;
@@ -528,6 +528,11 @@ bool configure_mfma(Plan &p) {
       const int v = atoi(e);
       if (v == 0 || v == 128 || v == 256) p.vec = v;
     }
+  if (param != 0) {   // a tuning variant: swizzle row bytes (-1 = none); 64 -> 64 only has all three
+    const int v = param < 0 ? 0 : param;
+    if (v != 128 && !(d.c == 64 && d.k == 64 && (v == 0 || v == 256))) return false;
+    p.vec = v;
+  }
   return true;
 }
 

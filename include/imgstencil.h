@@ -125,6 +125,54 @@ void conv2d_destroy(conv2d_plan plan);
 /* Describe what a plan launches. */
 is_status conv2d_get_plan_info(conv2d_plan plan, conv2d_plan_info *info);
 
+/* Runtime tile tuning. "Optimizing Memory Efficiency for Convolution Kernels on
+ * Kepler GPUs" (arXiv 1705.10591, the results of its special-case kernel)
+ * picks its block size by a design-space search, and "Optimizing convolution
+ * kernels - CNNs in Vulkan Part 2/3" (section "Some notes on workgroup sizes")
+ * its workgroup shape by measurement, proposing that an implementation
+ * benchmark configurations at run time. Here a descriptor has a list of
+ * variants, every kernel configuration that can run it, and conv2d_autotune
+ * times them all on the caller's buffers and keeps the fastest. The search is
+ * an entry point of its own rather than part of conv2d_create, which runs on
+ * the host without a GPU.
+ *  kernel     : kernel family, as in conv2d_plan_info
+ *  param      : the family's tuning parameter: output rows per strip
+ *               (is_k1_single, is_k1_single_separable), output channels per
+ *               workgroup (is_k2_multi), LDS swizzle row bytes, 0 = none
+ *               (is_k4_mfma); 0 for the others
+ *  is_default : 1 for the variant conv2d_create chooses (always index 0)
+ *  ms         : time per launch measured by conv2d_autotune (0 otherwise)     */
+typedef struct {
+  char kernel[64];
+  int param;
+  int is_default;
+  float ms;
+} conv2d_variant;
+
+/* List the variants of a descriptor, the default first. Host only (no GPU).
+ * *count receives the number of variants; the first min(max, *count) are
+ * written to out (out may be NULL when max is 0). Errors: those of
+ * conv2d_create, IS_ERR_INVALID_ARG (null count, max < 0). */
+is_status conv2d_list_variants(const conv2d_desc *d, conv2d_variant *out, int max, int *count);
+
+/* conv2d_create for variant `index` of conv2d_list_variants. Errors: those of
+ * conv2d_create, IS_ERR_INVALID_ARG (index out of range). */
+is_status conv2d_create_variant(const conv2d_desc *d, int index, conv2d_plan *out);
+
+/* Time every variant of the plan's descriptor on these buffers (one warm-up
+ * launch, then `reps` launches between two HIP events on `stream`) and make
+ * the plan use the fastest. Arguments as for conv2d_forward; y is overwritten
+ * and, when the call returns IS_OK, holds the chosen variant's result (its
+ * last launch is enqueued on `stream`). Unlike conv2d_forward this call
+ * synchronises with the stream's work (hipEventSynchronize) and creates two
+ * events; it allocates no device memory. It changes the plan: do not call it
+ * while another thread uses the same plan, nor inside a stream capture.
+ * out/max/count: as for conv2d_list_variants, with the measured times (count
+ * may be NULL). Errors: those of conv2d_forward, IS_ERR_INVALID_ARG
+ * (reps < 1); on error the plan is unchanged. */
+is_status conv2d_autotune(conv2d_plan plan, const void *x, const void *w, const float *bias, void *y,
+                          hipStream_t stream, int reps, conv2d_variant *out, int max, int *count);
+
 /* A chain of layers applied one after another, each reading the previous
  * layer's output: z_0 = x, z_l = act_l(conv_l(z_{l-1}) + b_l), and finally an
  * optional depth-to-space by f = `depth_to_space` (2 or 3) that turns the last

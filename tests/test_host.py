@@ -243,6 +243,44 @@ def test_separable_and_special_case_plans():
     assert isa.Plan(isa.make_desc(1, 1, 64, 128, 3, 3, 3)).info()["kernel"] == "is_k0_generic_nchw_f32"
 
 
+def test_tile_variants():
+    """The tuning variants of a descriptor: the default plan first, then every
+    other configuration that takes the shape; the fallback only when nothing
+    else does. Each index creates a plan with that kernel and parameter."""
+    def names(d):
+        return [(v["kernel"], v["param"], v["is_default"]) for v in isa.conv2d_list_variants(d)]
+    assert names(isa.make_desc(1, 1, 8192, 8192, 1, 3, 3)) == [
+        ("is_k1_single", 64, True), ("is_k1_single", 16, False), ("is_k1_single", 32, False),
+        ("is_k1_single", 128, False)]
+    assert names(isa.make_desc(1, 32, 720, 1280, 32, 3, 3, "f32", True)) == [
+        ("is_k5_mfma_f32", 0, True), ("is_k2_multi", 32, False), ("is_k2_multi", 16, False),
+        ("is_k2_multi", 8, False), ("is_k2_multi", 4, False)]
+    assert names(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16")) == [
+        ("is_k4_mfma", 128, True), ("is_k4_mfma", 0, False), ("is_k4_mfma", 256, False)]
+    assert names(isa.make_desc(1, 64, 72, 128, 32, 3, 3, "f16")) == [("is_k4_mfma", 128, True)]
+    assert names(isa.make_desc(1, 1, 720, 1280, 64, 5, 5, "f16", True)) == [("is_k6_head_f16", 0, True)]
+    assert names(isa.make_desc(1, 3, 16, 30, 5, 3, 3)) == [("is_k0_generic_nchw_f32", 0, True)]
+    sep = names(isa.make_desc(1, 1, 512, 512, 1, 7, 7, separable=True))
+    assert {k for (k, _, _) in sep} == {"is_k1_single_separable"} and len(sep) == 5
+    d = isa.make_desc(1, 1, 4096, 4096, 8, 3, 3)
+    vs = isa.conv2d_list_variants(d)
+    assert [(v["kernel"], v["param"]) for v in vs] == [("is_k2_multi", 8), ("is_k2_multi", 4), ("is_k2_multi", 2)]
+    for i, v in enumerate(vs):
+        p = isa.Plan(d, variant=i)
+        info = p.info()
+        assert info["kernel"] == v["kernel"]
+        assert info["grid"][0] == 64 * 256 * (8 // v["param"])   # 64x16 tiles x channel groups
+    with pytest.raises(isa.ImgStencilError):
+        isa.Plan(d, variant=len(vs))
+    with pytest.raises(isa.ImgStencilError):
+        isa.Plan(d, variant=-1)
+    # Tuning rejects reps < 1 before touching the GPU.
+    p = isa.Plan(d)
+    n = ctypes.c_int()
+    assert isa.load().conv2d_autotune(p.handle, 0x1000, 0x2000, None, 0x100000, None, 0, None, 0,
+                                      ctypes.byref(n)) == _abi.IS_ERR_INVALID_ARG
+
+
 def test_chain_descriptor_checks():
     d = isa.make_chain_desc(1, 16, 16, [(1, 8, 5, True), (8, 4, 3, False)], depth_to_space=2)
     ws = isa.conv_chain_workspace_size(d)
