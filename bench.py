@@ -50,6 +50,7 @@ TRAFFIC_KERNELS = {   # bench case -> (kernel as the profiler names it, its sour
     "upscaling chain 1280x720 (fused)": ("is_k3_chain", ("k3_chain.hip",)),
     "separable 7x7 filter, 8192x8192 fp32": ("is_k1_single<7, 7, true, false, true>", ("k1_single.hip",)),
     "1 channel -> 8 filters 3x3, 4096x4096 fp32": ("is_k2_multi<3, 8, 1, false, false>", ("k2_multi.hip",)),
+    "stencil pipeline 3x3 x3, 8192x8192 fp32 (auto)": ("is_k7_fused_stencil<3, 3, 3>", ("k7_fused_stencil.hip",)),
 }
 # The known-size dispatch: torch's elementwise negation of 256 MiB of fp32
 # (run by _copy_reference), which reads 256 MiB and writes 256 MiB.
@@ -497,6 +498,43 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
             for c in scases:
                 c.keep = None
             del plan
+
+        # A stencil pipeline of three 3x3 filters (ReLU after each) on 8192^2:
+        # the model's grouping (one fused launch) against one launch per filter.
+        H = W = 8192
+        rs = (3, 3, 3)
+        flops = sum(2.0 * r * r * H * W for r in rs)
+        nbytes = 8.0 * H * W + sum(4.0 * (r * r + 1) for r in rs)
+        wl = [(torch.randn((1, 1, r, r), device="cuda") / r, torch.zeros(1, device="cuda")) for r in rs]
+        res = {}
+        for mode, mname in ((isa.IS_CHAIN_AUTO, "auto"), (isa.IS_CHAIN_UNFUSED, "unfused")):
+            d = isa.make_chain_desc(1, H, W, [(1, 1, r, True) for r in rs], 1, mode)
+            ws_bytes = isa.conv_chain_workspace_size(d)
+            ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+            pcases = []
+            for _ in range(2):
+                xd = torch.rand((1, 1, H, W), device="cuda")
+                yd = torch.empty((1, 1, H, W), device="cuda")
+
+                def launch(d=d, xd=xd, yd=yd, ws=ws, ws_bytes=ws_bytes):
+                    isa.conv_chain_forward(d, xd.data_ptr(), [w.data_ptr() for (w, _) in wl],
+                                           [b.data_ptr() for (_, b) in wl], yd.data_ptr(),
+                                           ws.data_ptr() if ws_bytes else None, ws_bytes, stream)
+
+                c = Case("stencil pipeline 3x3 x3, 8192x8192 fp32 (%s)" % mname, launch, flops, nbytes,
+                         isa.conv_chain_kernel_name(d))
+                c.keep = (xd, yd)
+                pcases.append(c)
+            _, per, _ = _time_cases(torch, pcases, steps, warmup, stream_obj)
+            res[mname] = (sum(per) / len(per), pcases[0], isa.conv_chain_groups(d))
+            for c in pcases:
+                c.keep = None
+            del ws
+        ms, c0, groups = res["auto"]
+        out["stencil_pipeline_3x3x3_8192"] = {
+            "workload": "three 3x3 filters with ReLU, 8192x8192 fp32", "kernel": c0.kernel,
+            "groups": groups, "ms": round(ms, 4), "ms_one_launch_per_filter": round(res["unfused"][0], 4),
+            "gflops": round(flops / ms / 1e6, 1), "roofline": _roofline(c0, ms)}
     return out
 
 

@@ -3,7 +3,7 @@
 The functions with the C names (conv2d_create, conv2d_forward, conv2d_destroy,
 conv2d_get_plan_info, conv2d_list_variants, conv2d_create_variant,
 conv2d_autotune, conv_chain_workspace_size, conv_chain_forward,
-conv_chain_kernel_name, is_lds_tile_bytes, is_swizzle_col) marshal arguments to
+conv_chain_kernel_name, conv_chain_groups, is_lds_tile_bytes, is_swizzle_col) marshal arguments to
 the C ABI of include/imgstencil.h and nothing else. conv2d() and conv_chain()
 are conveniences on torch tensors: torch only allocates device memory and
 supplies the current HIP stream.
@@ -16,7 +16,7 @@ from ._abi import (IS_F16, IS_F32, IS_NCHW, IS_NHWC, IS_CHAIN_AUTO, IS_CHAIN_FUS
 
 __all__ = ["conv2d_create", "conv2d_forward", "conv2d_destroy", "conv2d_get_plan_info",
            "conv2d_list_variants", "conv2d_create_variant", "conv2d_autotune",
-           "conv_chain_workspace_size", "conv_chain_forward", "conv_chain_kernel_name",
+           "conv_chain_workspace_size", "conv_chain_forward", "conv_chain_kernel_name", "conv_chain_groups",
            "is_lds_tile_bytes", "is_swizzle_col", "is_version", "make_desc", "make_chain_desc",
            "conv2d", "conv2d_separable", "conv_chain", "Plan", "ImgStencilError"]
 
@@ -128,6 +128,15 @@ def conv_chain_kernel_name(desc):
     buf = ctypes.create_string_buffer(64)
     _abi.check(load().conv_chain_kernel_name(ctypes.byref(desc), buf, 64), "conv_chain_kernel_name")
     return buf.value.decode()
+
+
+def conv_chain_groups(desc):
+    """Launch groups of the chain, as sizes in layers."""
+    n = ctypes.c_int()
+    arr = (ctypes.c_int * _abi.IS_MAX_CHAIN)()
+    _abi.check(load().conv_chain_groups(ctypes.byref(desc), arr, _abi.IS_MAX_CHAIN, ctypes.byref(n)),
+               "conv_chain_groups")
+    return [arr[i] for i in range(n.value)]
 
 
 def conv_chain_forward(desc, x_ptr, w_ptrs, b_ptrs, y_ptr, ws_ptr, ws_bytes, stream):

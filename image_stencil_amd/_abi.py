@@ -65,6 +65,8 @@ SIGNATURES = [
     ("conv_chain_forward", ctypes.c_int, [ctypes.POINTER(conv_chain_desc), _vp, ctypes.POINTER(_vp),
                                           ctypes.POINTER(_vp), _vp, _vp, ctypes.c_size_t, _vp]),
     ("conv_chain_kernel_name", ctypes.c_int, [ctypes.POINTER(conv_chain_desc), ctypes.c_char_p, ctypes.c_size_t]),
+    ("conv_chain_groups", ctypes.c_int, [ctypes.POINTER(conv_chain_desc), ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_int)]),
     ("is_lds_tile_bytes", ctypes.c_size_t, [ctypes.c_int] * 6),
     ("is_swizzle_col", ctypes.c_int, [ctypes.c_int] * 5),
     ("is_status_str", ctypes.c_char_p, [ctypes.c_int]),

@@ -1,4 +1,5 @@
 // api.hip -- the C ABI: descriptor validation, kernel choice and launch.
+#include <algorithm>
 #include <new>
 #include <stdio.h>
 #include <stdlib.h>
@@ -276,12 +277,103 @@ size_t unfused_bytes(const conv_chain_desc *d, const conv2d_desc *ld) {
   return need * chain_buffer_bytes(d, ld);
 }
 
+// ---- Stencil pipelines: chains of single-channel layers --------------------
+//
+// A chain whose layers all map one channel to one (fp32, no depth-to-space) is
+// an image-processing stencil pipeline. Its layers run in groups of 1 to 3
+// consecutive layers, each group one launch: a single layer on the
+// single-channel kernel, 2 or 3 layers on the fused kernel (warp-overlapped
+// tiles, no intermediate image in HBM). IS_CHAIN_AUTO picks the grouping with
+// a roofline model of each launch (the model of "Model-Based Warp Overlapped
+// Tiling for Image Processing Programs on GPUs", arXiv 1909.07190, reduced to
+// its trade-off: fusion saves the intermediate images' HBM traffic and a
+// launch, and pays for the recomputed overlap columns and rows).
+bool stencil_chain(const conv_chain_desc *d) {
+  if (d->dtype != IS_F32 || d->depth_to_space != 1) return false;
+  for (int l = 0; l < d->n_layers; ++l)
+    if (d->layer[l].c != 1 || d->layer[l].k != 1) return false;
+  return true;
+}
+
+// Rates measured on MI355X: the single-channel kernel streams 5.6 TB/s, the
+// vector FMA loops reach about 80% of the 78.6 TFLOP/s fp32 peak, and a
+// launch with its ramp costs a few microseconds.
+constexpr double kModelHbm = 5.6e12;
+constexpr double kModelAlu = 0.8 * 78.6e12;
+constexpr double kModelLaunch = 3.0e-6;
+
+// Estimated seconds of one launch of layers [first, first + count).
+double model_group_seconds(const conv_chain_desc *d, int first, int count) {
+  const double px = (double)d->n * d->h * d->w;
+  if (count == 1) {
+    const double r = d->layer[first].r, s = d->layer[first].s;
+    return std::max(8.0 * px / kModelHbm, 2.0 * r * s * px / kModelAlu) + kModelLaunch;
+  }
+  const is::FusedStencilGeo g = is::fused_stencil_geometry(d, first, count);
+  int ps = 0;
+  for (int l = 0; l < count; ++l) ps += (d->layer[first + l].r - 1) / 2;
+  // Every stage runs on the whole 256-column window and on the strip's
+  // rows plus ps above and below.
+  const double hf = 256.0 / g.step;
+  const double vf = (g.strip_rows + 2.0 * ps) / g.strip_rows;
+  double flops = 0.0;
+  for (int l = 0; l < count; ++l) flops += 2.0 * d->layer[first + l].r * d->layer[first + l].s * px * hf * vf;
+  const double bytes = 4.0 * px * hf * vf + 4.0 * px;
+  return std::max(bytes / kModelHbm, flops / kModelAlu) + kModelLaunch;
+}
+
+// Sizes of the launch groups of a stencil chain, in order; returns their
+// number, 0 when the mode cannot be met (IS_CHAIN_FUSED with no fused kernel
+// for the whole chain).
+int stencil_groups(const conv_chain_desc *d, int *size) {
+  const int L = d->n_layers;
+  if (d->mode == IS_CHAIN_UNFUSED) {
+    for (int l = 0; l < L; ++l) size[l] = 1;
+    return L;
+  }
+  if (d->mode == IS_CHAIN_FUSED) {
+    if (L == 1 || !is::fused_stencil_geometry(d, 0, L).ok) return 0;
+    size[0] = L;
+    return 1;
+  }
+  double best[IS_MAX_CHAIN + 1];
+  int choice[IS_MAX_CHAIN + 1];
+  best[0] = 0.0;
+  for (int i = 1; i <= L; ++i) {
+    best[i] = -1.0;
+    choice[i] = 1;
+    for (int c = 1; c <= 3 && c <= i; ++c) {
+      const int first = i - c;
+      if (c > 1 && !is::fused_stencil_geometry(d, first, c).ok) continue;
+      const double v = best[first] + model_group_seconds(d, first, c);
+      if (best[i] < 0.0 || v < best[i]) {
+        best[i] = v;
+        choice[i] = c;
+      }
+    }
+  }
+  int rev[IS_MAX_CHAIN], n = 0;
+  for (int i = L; i > 0; i -= choice[i]) rev[n++] = choice[i];
+  for (int g = 0; g < n; ++g) size[g] = rev[n - 1 - g];
+  return n;
+}
+
+// Intermediate images a grouping needs in the workspace (ping-pong).
+int stencil_buffers(int groups) { return groups <= 1 ? 0 : (groups == 2 ? 1 : 2); }
+
 // Workspace that conv_chain_forward wants for the chain and mode: none for the
 // fused kernel; IS_CHAIN_AUTO asks for the layer-by-layer workspace, which
 // enables the faster path (on MI355X the layer-by-layer chain, with its
 // 32 -> 32 layers on the fp32 MFMA kernel, beats the fused kernel, whose
 // overlapped windows recompute about a quarter of the work).
 is_status chain_workspace(const conv_chain_desc *d, const conv2d_desc *ld, size_t *bytes) {
+  if (stencil_chain(d)) {
+    int size[IS_MAX_CHAIN];
+    const int groups = stencil_groups(d, size);
+    if (groups == 0) return IS_ERR_UNSUPPORTED;
+    *bytes = stencil_buffers(groups) * chain_buffer_bytes(d, ld);
+    return IS_OK;
+  }
   if (d->mode == IS_CHAIN_FUSED) {
     if (!chain_fusable(d, ld)) return IS_ERR_UNSUPPORTED;
     *bytes = 0;
@@ -296,6 +388,7 @@ is_status chain_workspace(const conv_chain_desc *d, const conv2d_desc *ld, size_
 // and the chain has a fused kernel.
 bool runs_fused(const conv_chain_desc *d, const conv2d_desc *ld, const void *workspace,
                 size_t workspace_bytes) {
+  if (stencil_chain(d)) return false;   // grouped launches, see stencil_groups
   if (d->mode == IS_CHAIN_FUSED) return true;
   if (d->mode == IS_CHAIN_UNFUSED || !chain_fusable(d, ld)) return false;
   const size_t need = unfused_bytes(d, ld);
@@ -323,8 +416,52 @@ is_status conv_chain_kernel_name(const conv_chain_desc *d, char *name, size_t le
   const is_status st2 = chain_workspace(d, ld, &ws);
   if (st2 != IS_OK) return st2;
   // the path taken when the caller passes the workspace reported above
+  if (stencil_chain(d)) {
+    int size[IS_MAX_CHAIN];
+    const int groups = stencil_groups(d, size);
+    bool all_single = true;
+    for (int g = 0; g < groups; ++g) all_single = all_single && size[g] == 1;
+    if (all_single) {
+      snprintf(name, len, "%s", "layer_by_layer");
+    } else if (groups == 1) {
+      snprintf(name, len, "%s", "is_k7_fused_stencil");
+    } else {
+      char buf[64] = "fused_groups:";
+      for (int g = 0; g < groups; ++g) {
+        char part[8];
+        snprintf(part, sizeof(part), g ? "+%d" : "%d", size[g]);
+        strncat(buf, part, sizeof(buf) - strlen(buf) - 1);
+      }
+      snprintf(name, len, "%s", buf);
+    }
+    return IS_OK;
+  }
   const bool fused = d->mode == IS_CHAIN_FUSED;
   snprintf(name, len, "%s", fused ? "is_k3_chain" : "layer_by_layer");
+  return IS_OK;
+}
+
+is_status conv_chain_groups(const conv_chain_desc *d, int *sizes, int max, int *count) {
+  if (!count || max < 0 || (max > 0 && !sizes)) return IS_ERR_INVALID_ARG;
+  conv2d_desc ld[IS_MAX_CHAIN];
+  const is_status st = chain_layers(d, ld);
+  if (st != IS_OK) return st;
+  size_t ws = 0;
+  const is_status st2 = chain_workspace(d, ld, &ws);
+  if (st2 != IS_OK) return st2;
+  int size[IS_MAX_CHAIN];
+  int groups;
+  if (stencil_chain(d)) {
+    groups = stencil_groups(d, size);
+  } else if (d->mode == IS_CHAIN_FUSED) {
+    groups = 1;
+    size[0] = d->n_layers;
+  } else {
+    groups = d->n_layers;
+    for (int l = 0; l < groups; ++l) size[l] = 1;
+  }
+  *count = groups;
+  for (int g = 0; g < groups && g < max; ++g) sizes[g] = size[g];
   return IS_OK;
 }
 
@@ -348,6 +485,17 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void
     size_t need = 0;
     st = chain_workspace(d, ld, &need);
     if (st != IS_OK) return st;
+    const bool stencil = stencil_chain(d);
+    int gsize[IS_MAX_CHAIN];
+    int groups = stencil ? stencil_groups(d, gsize) : 0;
+    // IS_CHAIN_AUTO without the workspace: one fused launch when it covers
+    // the whole stencil chain.
+    if (stencil && need > 0 && (!workspace || workspace_bytes < need) && d->mode == IS_CHAIN_AUTO &&
+        is::fused_stencil_geometry(d, 0, d->n_layers).ok) {
+      groups = 1;
+      gsize[0] = d->n_layers;
+      need = 0;
+    }
     const bool fused = runs_fused(d, ld, workspace, workspace_bytes);
     if (fused) need = 0;
     if (need > 0 && (!workspace || workspace_bytes < need)) return IS_ERR_WORKSPACE;
@@ -363,6 +511,23 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void
 
     const size_t half = chain_buffer_bytes(d, ld);
     char *ws = static_cast<char *>(workspace);
+    if (stencil) {
+      const float *gsrc = static_cast<const float *>(x);
+      const float *const *wf = reinterpret_cast<const float *const *>(w);
+      for (int g = 0, first = 0; g < groups; first += gsize[g], ++g) {
+        float *dst = g == groups - 1 ? static_cast<float *>(y) : reinterpret_cast<float *>(ws + (g % 2) * half);
+        if (gsize[g] == 1) {
+          is::Plan p;
+          st = make_plan(&ld[first], p);
+          if (st == IS_OK) st = run_plan(p, gsrc, w[first], b ? b[first] : nullptr, dst, stream);
+        } else {
+          st = hip_status(is::launch_fused_stencil(d, first, gsize[g], gsrc, wf, b, dst, stream));
+        }
+        if (st != IS_OK) return st;
+        gsrc = dst;
+      }
+      return IS_OK;
+    }
     const void *src = x;
     for (int l = 0; l < d->n_layers; ++l) {
       const bool last = l == d->n_layers - 1;

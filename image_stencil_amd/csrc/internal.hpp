@@ -70,6 +70,19 @@ bool chain_fused_supported(const conv_chain_desc *d);
 hipError_t launch_chain_fused(const conv_chain_desc *d, const float *x, const float *const *w,
                               const float *const *b, float *y, hipStream_t s);
 
+// Two or three consecutive single-channel layers (1 -> 1, r = s in {3, 5},
+// fp32 NCHW, W % 4 == 0) of a chain, fused in one pass: layers
+// [first, first + count) of d, reading x and writing y (N x 1 x H x W).
+struct FusedStencilGeo {
+  bool ok;
+  int lanes_off, step;        // overlap lanes per side; output columns per window
+  int nseg, nstrip, ntiles;   // windows per row, strips, waves
+  int strip_rows;
+};
+FusedStencilGeo fused_stencil_geometry(const conv_chain_desc *d, int first, int count);
+hipError_t launch_fused_stencil(const conv_chain_desc *d, int first, int count, const float *x,
+                                const float *const *w, const float *const *b, float *y, hipStream_t s);
+
 // out[n,0,f*i+dy,f*j+dx] = z[n,f*dy+dx,i,j] for z of N x f*f x H x W fp32.
 hipError_t launch_depth_to_space(const float *z, float *out, int N, int H, int W, int f, hipStream_t s);
 // The same for NHWC fp16: z is N x H x W x zc (channels f*dy+dx among zc >= f*f),

@@ -188,7 +188,16 @@ is_status conv2d_autotune(conv2d_plan plan, const void *x, const void *w, const 
  *  = layer[l-1].k), has layer[l].k outputs, odd r == s, and ReLU if relu != 0.
  *  dtype: IS_F32 (NCHW tensors, fp32 weights and biases) or IS_F16 (NHWC
  *  tensors, fp16 weights, fp32 biases; every layer's output is stored as fp16,
- *  the page's "Reducing memory traffic" step; layer by layer only). */
+ *  the page's "Reducing memory traffic" step; layer by layer only).
+ * Stencil pipelines: a fp32 chain whose layers all map one channel to one
+ * (c = k = 1) and has no depth-to-space is an image-processing pipeline of
+ * filters, the programs of the same arXiv 1909.07190. It runs in groups of 1
+ * to 3 consecutive layers, one launch each: 2 or 3 layers with r = s in
+ * {3, 5} and W % 4 == 0 can be fused into one pass over warp-overlapped
+ * tiles that keeps the intermediate images on chip. IS_CHAIN_AUTO chooses the
+ * groups with a roofline model of each launch (conv_chain_groups reports
+ * them), IS_CHAIN_FUSED asks for one group of the whole chain, and
+ * IS_CHAIN_UNFUSED for one launch per layer. */
 typedef struct { int c, k, r, s, relu; } conv_layer_desc;
 
 typedef enum {
@@ -209,8 +218,19 @@ typedef struct {
 /* Device bytes of workspace conv_chain_forward wants for this chain and mode:
  * 0 for IS_CHAIN_FUSED; the two intermediate tensors of the layer-by-layer
  * path for IS_CHAIN_UNFUSED and IS_CHAIN_AUTO (with less, AUTO runs the fused
- * kernel when the chain has one, and fails with IS_ERR_WORKSPACE otherwise). */
+ * kernel when the chain has one, and fails with IS_ERR_WORKSPACE otherwise).
+ * Stencil pipelines: one intermediate image per group boundary, at most two
+ * (none for a single group); with less, AUTO runs the whole chain as one
+ * fused group when it can. */
 is_status conv_chain_workspace_size(const conv_chain_desc *d, size_t *bytes);
+
+/* The launch groups of the chain in order, as sizes in layers (host only):
+ * *count receives their number and the first min(max, *count) sizes are
+ * written to sizes. Stencil pipelines: the grouping of the mode (AUTO: the
+ * model's choice, for the workspace conv_chain_workspace_size reports); other
+ * chains: one group (IS_CHAIN_FUSED) or one per layer. Errors: those of
+ * conv_chain_workspace_size, IS_ERR_INVALID_ARG (null count, max < 0). */
+is_status conv_chain_groups(const conv_chain_desc *d, int *sizes, int max, int *count);
 
 /* Enqueue the chain on `stream`.
  *  x: N x layer[0].c x H x W fp32 input (IS_F16: N x H x W x layer[0].c fp16)

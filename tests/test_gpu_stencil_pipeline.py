@@ -1,0 +1,104 @@
+"""GPU parity of stencil pipelines (chains of single-channel filters) against
+the oracle's chain, fused and unfused.
+
+Fused groups evaluate 2 or 3 filters in one pass over warp-overlapped tiles;
+their intermediate images never reach HBM, and each filter still sees zero
+padding outside the image. The oracle composes the filters one by one
+(oracle.chain), with the error scale propagated through the layers; the
+intermediate results stay fp32 on the GPU, so the fp32 bound applies.
+"""
+import numpy as np
+import pytest
+
+import image_stencil_amd as isa
+import oracle
+from gpu_util import dev, host, say
+from tolerance import TAU_F32, check
+
+pytestmark = pytest.mark.gpu
+
+
+def _pipeline(N, H, W, spec, seed):
+    """spec: [(r, relu, with_bias)] -> x, layers [(w, b, relu)]"""
+    rng = np.random.default_rng(seed)
+    x = rng.random((N, 1, H, W), dtype=np.float32)
+    layers = []
+    for (r, relu, with_bias) in spec:
+        w = (rng.standard_normal((1, 1, r, r)) / r).astype(np.float32)
+        b = rng.standard_normal(1).astype(np.float32) * 0.1 if with_bias else None
+        layers.append((w, b, relu))
+    return x, layers
+
+
+def _run(x, layers, mode, expect=None):
+    N, _, H, W = x.shape
+    spec = [(1, 1, w.shape[2], relu) for (w, b, relu) in layers]
+    d = isa.make_chain_desc(N, H, W, spec, 1, mode)
+    if expect is not None:
+        assert isa.conv_chain_groups(d) == expect, isa.conv_chain_groups(d)
+    dl = [(dev(w), dev(b) if b is not None else None, relu) for (w, b, relu) in layers]
+    return host(isa.conv_chain(dev(x), dl, 1, mode))
+
+
+SHAPES = [
+    # N, H, W, [(r, relu, bias)], groups under AUTO
+    (1, 300, 700, [(3, False, False), (3, False, False)], [2]),
+    (2, 129, 500, [(3, True, True), (5, False, True)], [2]),
+    (1, 257, 1000, [(5, True, True), (3, True, True), (5, False, False)], [3]),
+    (1, 70, 244, [(3, False, True), (3, True, False), (3, False, True)], [3]),
+    (1, 1, 4, [(3, False, True), (5, False, True)], [2]),
+    (1, 5, 8, [(5, True, True), (5, True, True), (5, False, True)], [3]),
+    (1, 64, 248, [(5, False, False), (5, False, False)], [2]),
+    (1, 131, 260, [(3, True, True)] * 7, None),
+]
+
+
+@pytest.mark.parametrize("N,H,W,spec,groups", SHAPES)
+def test_pipeline_matches_oracle(N, H, W, spec, groups):
+    x, layers = _pipeline(N, H, W, spec, seed=H + W)
+    ref, m = oracle.chain(x, layers)
+    for mode in (isa.IS_CHAIN_AUTO, isa.IS_CHAIN_UNFUSED):
+        say("pipeline", N, H, W, [r for (r, _, _) in spec], mode)
+        y = _run(x, layers, mode, groups if mode == isa.IS_CHAIN_AUTO else [1] * len(spec))
+        ratio = check(y, ref, m, TAU_F32, "pipeline %dx%dx%d mode %d" % (N, H, W, mode))
+        say("max err/bound %.3g" % ratio)
+
+
+def test_fused_delta_filters_bit_exact():
+    """Unit-impulse filters: the pipeline is a pure shift with zero fill, which
+    the fused kernel must reproduce exactly (products by 0 and 1, sums with 0)."""
+    rng = np.random.default_rng(3)
+    x = rng.random((1, 1, 90, 520), dtype=np.float32)
+    layers = []
+    for (r, i, j) in ((3, 0, 2), (5, 4, 1), (3, 1, 1)):
+        w = np.zeros((1, 1, r, r), np.float32)
+        w[0, 0, i, j] = 1.0
+        layers.append((w, None, False))
+    y = _run(x, layers, isa.IS_CHAIN_FUSED, [3])
+    ref, _ = oracle.chain(x, layers)
+    np.testing.assert_array_equal(y.astype(np.float64), ref)
+
+
+def test_auto_without_workspace_runs_one_fused_group():
+    import torch
+    x, layers = _pipeline(1, 100, 400, [(3, True, True)] * 3, seed=4)
+    d = isa.make_chain_desc(1, 100, 400, [(1, 1, 3, True)] * 3, 1, isa.IS_CHAIN_AUTO)
+    y = torch.full((1, 1, 100, 400), float("nan"), device="cuda")
+    dl = [(dev(w), dev(b)) for (w, b, _) in layers]
+    isa.conv_chain_forward(d, dev(x).data_ptr(), [w.data_ptr() for (w, _) in dl], [b.data_ptr() for (_, b) in dl],
+                           y.data_ptr(), None, 0, torch.cuda.current_stream().cuda_stream)
+    ref, m = oracle.chain(x, layers)
+    check(host(y), ref, m, TAU_F32, "auto without workspace")
+
+
+def test_pipeline_8192_sampled():
+    """Two 3x3 filters on 8192^2 (the fused group the bench times): rows around
+    strip edges and random rows, every column."""
+    x, layers = _pipeline(1, 8192, 8192, [(3, True, True), (3, False, True)], seed=5)
+    say("pipeline 8192^2")
+    y = _run(x, layers, isa.IS_CHAIN_AUTO, [2])
+    rows = sorted({0, 1, 2, 62, 63, 64, 65, 4095, 4096, 8189, 8190, 8191} |
+                  set(int(r) for r in np.random.default_rng(6).integers(0, 8192, 8)))
+    for i in rows:
+        ref, m = oracle.chain_window(x, layers, i, i + 1, 0, 8192)
+        check(y[:, :, i:i + 1, :], ref, m, TAU_F32, "8192^2 row %d" % i)

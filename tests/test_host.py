@@ -281,6 +281,43 @@ def test_tile_variants():
                                       ctypes.byref(n)) == _abi.IS_ERR_INVALID_ARG
 
 
+def _stencil(h, w, rs, mode=None, n=1):
+    mode = isa.IS_CHAIN_AUTO if mode is None else mode
+    return isa.make_chain_desc(n, h, w, [(1, 1, r, False) for r in rs], 1, mode)
+
+
+def test_stencil_pipeline_grouping():
+    """Chains of single-channel filters: the model fuses layers when the saved
+    intermediate traffic outweighs the recomputed overlap; 7x7 layers and
+    widths that are not a multiple of 4 are never fused; groups hold at most
+    3 layers; the workspace holds one image per group boundary, at most two."""
+    img = 4 * 8192 * 8192
+    cases = [
+        ((8192, 8192, [3, 3]), None, [2], "is_k7_fused_stencil", 0),
+        ((8192, 8192, [3, 3]), isa.IS_CHAIN_UNFUSED, [1, 1], "layer_by_layer", img),
+        ((8192, 8192, [3, 3]), isa.IS_CHAIN_FUSED, [2], "is_k7_fused_stencil", 0),
+        ((8192, 8192, [5, 5, 5]), None, [3], "is_k7_fused_stencil", 0),
+        ((8192, 8192, [3] * 7), None, [3, 3, 1], "fused_groups:3+3+1", 2 * img),
+        ((8192, 8192, [7, 7]), None, [1, 1], "layer_by_layer", img),
+        ((8192, 8192, [5, 3, 7, 3, 3]), None, [2, 1, 2], "fused_groups:2+1+2", 2 * img),
+        ((8192, 8190, [3, 3]), None, [1, 1], "layer_by_layer", 4 * 8192 * 8190),
+        ((16, 16, [3, 3]), None, [2], "is_k7_fused_stencil", 0),
+        ((8192, 8192, [3]), None, [1], "layer_by_layer", 0),
+    ]
+    for (h, w, rs), mode, groups, name, ws in cases:
+        d = _stencil(h, w, rs, mode)
+        assert isa.conv_chain_groups(d) == groups, (h, w, rs, mode)
+        assert isa.conv_chain_kernel_name(d) == name, (h, w, rs, mode)
+        assert isa.conv_chain_workspace_size(d) == ws, (h, w, rs, mode)
+    for rs in ([3, 3, 3, 3], [7, 3], [3]):
+        with pytest.raises(isa.ImgStencilError):
+            isa.conv_chain_groups(_stencil(64, 64, rs, isa.IS_CHAIN_FUSED))
+    # the upscaling chain is not a stencil pipeline: layer by layer, or its own fused kernel
+    spec = [(1, 32, 5, True), (32, 32, 3, True), (32, 32, 3, True), (32, 4, 3, False)]
+    assert isa.conv_chain_groups(isa.make_chain_desc(1, 720, 1280, spec, 2, isa.IS_CHAIN_AUTO)) == [1, 1, 1, 1]
+    assert isa.conv_chain_groups(isa.make_chain_desc(1, 720, 1280, spec, 2, isa.IS_CHAIN_FUSED)) == [4]
+
+
 def test_chain_descriptor_checks():
     d = isa.make_chain_desc(1, 16, 16, [(1, 8, 5, True), (8, 4, 3, False)], depth_to_space=2)
     ws = isa.conv_chain_workspace_size(d)
