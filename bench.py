@@ -272,6 +272,66 @@ def pmc_lds_summary(pmc_dir):
     return "\n".join(lines) + "\n"
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_FMA_F32",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def _case_flops():
+    """Algorithmic FLOPs of each counted bench case (2 per multiply-add of the
+    definition; separable filters: R + S products per pixel)."""
+    from image_stencil_amd import traffic
+    chain = [(1, 32, 5), (32, 32, 3), (32, 32, 3), (32, 4, 3)]
+    out = {"8192x8192 %dx%d" % (r, r): traffic.conv_flops(1, 1, 8192, 8192, 1, r, r) for r in (3, 5, 7)}
+    out["fp32 layer 1x32x720x1280 -> 32, 3x3"] = traffic.conv_flops(1, 32, 720, 1280, 32, 3, 3)
+    out["fp16 NHWC layer 8x256x256x64 -> 64, 3x3"] = traffic.conv_flops(8, 64, 256, 256, 64, 3, 3)
+    out["upscaling chain 1280x720 (fused)"] = traffic.chain_flops(1, 720, 1280, chain)
+    out["separable 7x7 filter, 8192x8192 fp32"] = 2.0 * 14 * 8192 * 8192
+    out["1 channel -> 8 filters 3x3, 4096x4096 fp32"] = traffic.conv_flops(1, 1, 4096, 4096, 8, 3, 3)
+    out["stencil pipeline 3x3 x3, 8192x8192 fp32 (auto)"] = 3 * traffic.conv_flops(1, 1, 8192, 8192, 1, 3, 3)
+    return out
+
+
+def pmc_mfma_summary(pmc_dir):
+    """Markdown summary of a counter run of the arithmetic counters: the FLOPs
+    the kernels' instructions perform (MFMA ops in units of 512 FLOPs, fp32
+    vector FMAs at 128 FLOPs per wave instruction) against the algorithmic
+    FLOPs, and the matrix cores' busy share."""
+    tabs = {c: _counter_means(pmc_dir, c) for c in MFMA_COUNTERS}
+    flops = _case_flops()
+    lines = ["# Arithmetic counters of the bench workloads (rocprofv3 --pmc)", "",
+             "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
+             "rocprofv3 --pmc %s --output-format csv -d %s -o run -- \\" % (" ".join(MFMA_COUNTERS), pmc_dir),
+             "    python3 bench.py " + PMC_ARGS,
+             "python3 bench.py --pmc-mfma-summary %s > profiles/arithmetic_counters.md" % pmc_dir,
+             "```", "",
+             "Per dispatch, averaged over the dispatches of each kernel. counted GFLOP = 512 x",
+             "(SQ_INSTS_VALU_MFMA_MOPS_F16 + SQ_INSTS_VALU_MFMA_MOPS_F32) + 128 x SQ_INSTS_VALU_FMA_F32 (a",
+             "wave's fp32 FMA: 64 lanes x 2 FLOPs; lanes masked off still count). The ratio to the",
+             "algorithmic FLOPs shows work the kernel does beyond the definition (zero-padded MFMA operands,",
+             "overlapped tiles, border taps of out-of-image rows) or FLOPs done elsewhere (bias, ReLU are not",
+             "FMAs). MFMA busy share = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 256 CUs x 4",
+             "SIMDs): GRBM_GUI_ACTIVE is read as the sum of the 8 XCDs' own counters (each XCD has its",
+             "GRBM); so read, the shares of the fp16 and fp32 MFMA kernels equal their measured fractions",
+             "of the MFMA peak.", "",
+             "| case | kernel | dispatches | MFMA f16 GFLOP | MFMA f32 GFLOP | vector FMA GFLOP | "
+             "counted / algorithmic | MFMA busy share |",
+             "|---|---|---|---|---|---|---|---|"]
+    for case, (kern, _) in TRAFFIC_KERNELS.items():
+        if kern not in tabs[MFMA_COUNTERS[0]]:
+            continue
+        v = {c: tabs[c].get(kern, (0.0, 0, ""))[0] for c in MFMA_COUNTERS}
+        f16 = 512.0 * v["SQ_INSTS_VALU_MFMA_MOPS_F16"] / 1e9
+        f32 = 512.0 * v["SQ_INSTS_VALU_MFMA_MOPS_F32"] / 1e9
+        fma = 128.0 * v["SQ_INSTS_VALU_FMA_F32"] / 1e9
+        alg = flops.get(case, 0.0) / 1e9
+        ratio = (f16 + f32 + fma) / alg if alg else 0.0
+        gui = v["GRBM_GUI_ACTIVE"]
+        busy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui / 8.0 * 256 * 4) if gui else 0.0
+        lines.append("| %s | `%s` | %d | %.2f | %.2f | %.2f | %.3f | %.3f |" % (
+            case, kern, tabs[MFMA_COUNTERS[0]][kern][1], f16, f32, fma, ratio, busy))
+    return "\n".join(lines) + "\n"
+
+
 def _traffic(case):
     """Counter-derived HBM bytes per launch of a bench case, or None when absent
     or taken with other kernel sources than the current ones."""
@@ -662,6 +722,8 @@ def main():
     ap.add_argument("--stats-summary", metavar="TRACE_DIR",
                     help="print the kernel-duration summary of a rocprofv3 --kernel-trace --stats run of "
                          "this script and exit (no GPU needed)")
+    ap.add_argument("--pmc-mfma-summary", metavar="PMC_DIR",
+                    help="print the arithmetic-counter summary of a rocprofv3 --pmc run and exit")
     ap.add_argument("--net-stats-summary", metavar="TRACE_DIR",
                     help="as --stats-summary, for a kernel-trace run of the pages' net alone")
     ap.add_argument("--lds-study", action="store_true",
@@ -676,6 +738,9 @@ def main():
         return
     if args.stats_summary:
         sys.stdout.write(stats_summary(args.stats_summary))
+        return
+    if args.pmc_mfma_summary:
+        sys.stdout.write(pmc_mfma_summary(args.pmc_mfma_summary))
         return
     if args.net_stats_summary:
         sys.stdout.write(stats_summary(args.net_stats_summary, net=True))
