@@ -544,6 +544,10 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void
       }
       if (st != IS_OK) return st;
       // The last layer writes the depth-to-space output itself when its kernel can.
+      if (last && padded && d->depth_to_space == 3 && is::mfma_d2s3_supported(p))
+        return hip_status(is::launch_mfma_d2s3(p, static_cast<const _Float16 *>(src),
+                                               static_cast<const _Float16 *>(w[l]), b ? b[l] : nullptr,
+                                               static_cast<_Float16 *>(y), stream));
       if (last && d->depth_to_space == 2 && is::multi_d2s_supported(p))
         return hip_status(is::launch_multi_d2s(p, static_cast<const float *>(src),
                                                static_cast<const float *>(w[l]), b ? b[l] : nullptr,

@@ -57,6 +57,12 @@ bool configure_mfma(Plan &p, int param = 0);
 hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
                        hipStream_t s);
 
+// The (32 -> 16) layer whose first 9 channels go through a 3x3 depth-to-space
+// (y: N x 3H x 3W fp16), in one launch: the last layer of the pages' net.
+bool mfma_d2s3_supported(const Plan &p);
+hipError_t launch_mfma_d2s3(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
+                            hipStream_t s);
+
 bool configure_head_f16(Plan &p);
 hipError_t launch_head_f16(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
                            hipStream_t s);

@@ -55,6 +55,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
+typedef unsigned int uint3v __attribute__((ext_vector_type(3)));
 
 constexpr unsigned kOob = 0xFFFFFFF0u;
 // Cache policy of the input DMA and the output stores: non-temporal (gfx950 nt
@@ -196,9 +197,13 @@ struct UnitGeo {
   unsigned scol[2];
 };
 
-template <int SWZ, int C, int K>
+// D2S = 3: the layer's first 9 channels go through a 3x3 depth-to-space on
+// the way out (y is N x 3H x 3W fp16, out[3i+dy][3j+dx] = z[i][j][3dy+dx]),
+// in place of the staged rows' 16-channel pixel lines; 16 output channels only.
+template <int SWZ, int C, int K, int D2S = 0>
 __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   using G = K4Cfg<C, K>;
+  static_assert(D2S == 0 || (D2S == 3 && K == 16), "depth-to-space by 3 of the first 9 of 16 channels");
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -250,6 +255,18 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     spx[j] = byte / (2 * K);
     sc[j] = (byte % (2 * K)) / 16;
   }
+  // D2S: a stage's 4 staged rows make 12 output-row segments (row, dy) of
+  // 3 x TC fp16 values; wave w stores segments 2w and 2w + 1 (waves 6 and 7
+  // have none and store out of range, which keeps every wave's operation
+  // count at 2 per stage), 12 bytes per lane: pixels 2 lane, 2 lane + 1,
+  // channels 3 dy .. 3 dy + 2 of each.
+  int drow_s[2], ddy[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int seg = 2 * wave + j;
+    drow_s[j] = seg < 3 * G::S ? seg / 3 : 0;
+    ddy[j] = seg < 3 * G::S ? seg % 3 : -1;
+  }
 
   auto unit_geo = [&](int u) -> UnitGeo {
     UnitGeo q;
@@ -260,8 +277,13 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     q.x0 = tx * G::TC;
     q.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(a.x + (size_t)n * img_in), (short)0,
                                              (int)(img_in * 2), kBufferFlags);
-    q.ry = __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)n * img_out, (short)0, (int)(img_out * 2),
-                                             kBufferFlags);
+    if constexpr (D2S) {
+      q.ry = __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)n * 9 * a.H * a.W, (short)0,
+                                               (int)((size_t)18 * a.H * a.W), kBufferFlags);
+    } else {
+      q.ry = __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)n * img_out, (short)0, (int)(img_out * 2),
+                                               kBufferFlags);
+    }
 #pragma unroll
     for (int j = 0; j < G::MAIN_OPS; ++j) {
       const int gx = q.x0 + dpx[j];
@@ -269,8 +291,13 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int sx = q.x0 + spx[j];
-      q.scol[j] = sx < a.W ? (unsigned)((sx * K + sc[j] * 8) * 2) : kOob;
+      if constexpr (D2S) {
+        const int sx = q.x0 + 2 * lane;   // W is even: sx < W covers sx + 1
+        q.scol[j] = (ddy[j] >= 0 && sx < a.W) ? (unsigned)(6 * sx) : kOob;
+      } else {
+        const int sx = q.x0 + spx[j];
+        q.scol[j] = sx < a.W ? (unsigned)((sx * K + sc[j] * 8) * 2) : kOob;
+      }
     }
     const int hx = q.x0 + hpx;
     q.hcol = (hside < 2 && (unsigned)hx < (unsigned)a.W)
@@ -382,6 +409,18 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     soff_r[j] = G::RING_BYTES + sr * G::OUT_ROW_BYTES + spx[j] * 2 * K + ((sc[j] ^ (spx[j] & (G::KPP - 1))) * 16);
+  // D2S: staging offsets of the 6 values a lane stores per segment.
+  int doff[2][6];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < 6; ++e) {
+      const int px = 2 * lane + e / 3;
+      const int c = 3 * (ddy[j] < 0 ? 0 : ddy[j]) + e % 3;
+      doff[j][e] = G::RING_BYTES + drow_s[j] * G::OUT_ROW_BYTES + px * 2 * K +
+                   (((c >> 3) ^ (px & (G::KPP - 1))) * 16) + (c & 7) * 2;
+    }
+  const unsigned out3_row_bytes = (unsigned)a.W * 6u;   // D2S output row: 3W fp16
 
   while (true) {
     // ---- Unit prologue: stages 0 .. D-1 are in flight; the first two must
@@ -398,18 +437,38 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     // and then to HBM (output row t*S + sr - 2 of the unit).
     auto read_staged = [&](int t, uint4v (&sv)[2]) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        sv[j] = *reinterpret_cast<const uint4v *>(lds + soff_r[j] + (t & 1) * G::S * G::OUT_ROW_BYTES);
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (D2S) {
+          const char *base = lds + (t & 1) * G::S * G::OUT_ROW_BYTES;
+          unsigned hw[6];
+#pragma unroll
+          for (int e = 0; e < 6; ++e) hw[e] = *reinterpret_cast<const unsigned short *>(base + doff[j][e]);
+          sv[j] = uint4v{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16), 0u};
+        } else {
+          sv[j] = *reinterpret_cast<const uint4v *>(lds + soff_r[j] + (t & 1) * G::S * G::OUT_ROW_BYTES);
+        }
+      }
     };
     auto store_stage = [&](int t, const uint4v (&sv)[2]) {
-      const int o = t * G::S + sr - 2;
-      const int gy = geo.y0 + o;
-      const bool row_out = (o >= 0) & (o < G::UR) & (gy < a.H);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const unsigned off =
-            (row_out & (geo.scol[j] != kOob)) ? (unsigned)gy * out_row_bytes + geo.scol[j] : kOob;
-        __builtin_amdgcn_raw_buffer_store_b128(sv[j], geo.ry, off, 0, kNonTemporal);
+        if constexpr (D2S) {
+          const int o = t * G::S + drow_s[j] - 2;
+          const int gy = geo.y0 + o;
+          const bool row_out = (o >= 0) & (o < G::UR) & (gy < a.H);
+          const unsigned off = (row_out & (geo.scol[j] != kOob))
+                                   ? (unsigned)(3 * gy + ddy[j]) * out3_row_bytes + geo.scol[j]
+                                   : kOob;
+          const uint3v v3 = {sv[j].x, sv[j].y, sv[j].z};
+          __builtin_amdgcn_raw_buffer_store_b96(v3, geo.ry, off, 0, kNonTemporal);
+        } else {
+          const int o = t * G::S + sr - 2;
+          const int gy = geo.y0 + o;
+          const bool row_out = (o >= 0) & (o < G::UR) & (gy < a.H);
+          const unsigned off =
+              (row_out & (geo.scol[j] != kOob)) ? (unsigned)gy * out_row_bytes + geo.scol[j] : kOob;
+          __builtin_amdgcn_raw_buffer_store_b128(sv[j], geo.ry, off, 0, kNonTemporal);
+        }
       }
     };
 
@@ -534,6 +593,31 @@ bool configure_mfma(Plan &p, int param) {
     p.vec = v;
   }
   return true;
+}
+
+bool mfma_d2s3_supported(const Plan &p) {
+  const conv2d_desc &d = p.d;
+  return p.kid == kMfmaNhwcF16 && d.c == 32 && d.k == 16 && p.vec == 128 && p.kvalid == 9 && d.w % 2 == 0 &&
+         18.0 * d.h * (double)d.w < 2.0e9;
+}
+
+hipError_t launch_mfma_d2s3(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
+                            hipStream_t s) {
+  if (!mfma_d2s3_supported(p)) return hipErrorInvalidValue;
+  MfmaArgs a;
+  a.x = x;
+  a.w = w;
+  a.bias = b;
+  a.y = y;
+  a.N = p.d.n;
+  a.H = p.d.h;
+  a.W = p.d.w;
+  a.relu = p.d.relu;
+  a.kvalid = p.kvalid;
+  a.units_x = p.nseg;
+  a.units_y = p.nstrip;
+  a.nunits = p.ntiles;
+  return launch_kernel(is_k4_mfma<128, 32, 16, 3>, dim3(p.grid_x), dim3(p.block), 0, s, a);
 }
 
 hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,

@@ -47,7 +47,8 @@ def _chain(x, layers, d2s, mode=isa.IS_CHAIN_AUTO):
     return host(isa.conv_chain(dev(x), dl, depth_to_space=d2s, mode=mode))
 
 
-@pytest.mark.parametrize("N,H,W", [(1, 37, 70), (2, 20, 130), (1, 1, 1), (1, 66, 200)])
+@pytest.mark.parametrize("N,H,W", [(1, 37, 70), (2, 20, 130), (1, 1, 1), (1, 66, 200), (1, 19, 77), (2, 35, 258),
+                                   (1, 70, 2)])
 def test_pages_net_small_frames(N, H, W):
     x, layers = synth.chain_f16_nhwc(N=N, H=H, W=W, seed=N * 1000 + H + W)
     spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
