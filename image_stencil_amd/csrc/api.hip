@@ -89,8 +89,8 @@ is_status make_plan(const conv2d_desc *d, is::Plan &p) {
   if (d->separable) {
     // Only the single-channel kernel evaluates separable filters.
     if (!is::configure_single(p)) return IS_ERR_UNSUPPORTED;
-  } else if (!is::configure_single(p) && !is::configure_mfma_f32(p) && !is::configure_multi(p) &&
-             !is::configure_mfma(p) && !is::configure_head_f16(p)) {
+  } else if (!is::configure_single(p) && !is::configure_mfma_f32(p) && !is::configure_pointwise(p) &&
+             !is::configure_multi(p) && !is::configure_mfma(p) && !is::configure_head_f16(p)) {
     is::configure_generic(p);
   }
   if (log_enabled())
@@ -112,7 +112,8 @@ struct Variant {
 int public_param(const is::Plan &p) {
   switch (p.kid) {
     case is::kSingleChannel:
-    case is::kMultiChannel: return p.strip_rows;
+    case is::kMultiChannel:
+    case is::kPointwise: return p.strip_rows;
     case is::kMfmaNhwcF16: return p.vec;
     default: return 0;
   }
@@ -126,6 +127,7 @@ bool configure_variant(is::Plan &p, const conv2d_desc &d, const Variant &v) {
     case is::kMultiChannel: return !d.separable && is::configure_multi(p, v.param);
     case is::kMfmaNhwcF16: return !d.separable && is::configure_mfma(p, v.param == 0 ? -1 : v.param);
     case is::kMfmaNchwF32: return !d.separable && is::configure_mfma_f32(p);
+    case is::kPointwise: return is::configure_pointwise(p, v.param);
     case is::kHeadNhwcF16: return !d.separable && is::configure_head_f16(p);
     default:
       if (d.separable) return false;
@@ -151,6 +153,7 @@ int collect_variants(const conv2d_desc &d, const is::Plan &def, Variant *out, in
   const Variant tries[] = {
       {is::kSingleChannel, 16}, {is::kSingleChannel, 32}, {is::kSingleChannel, 64}, {is::kSingleChannel, 128},
       {is::kMfmaNchwF32, 0},
+      {is::kPointwise, 32}, {is::kPointwise, 16}, {is::kPointwise, 8}, {is::kPointwise, 4},
       {is::kMultiChannel, 32}, {is::kMultiChannel, 16}, {is::kMultiChannel, 8}, {is::kMultiChannel, 4},
       {is::kMultiChannel, 2},
       {is::kMfmaNhwcF16, 128}, {is::kMfmaNhwcF16, 0}, {is::kMfmaNhwcF16, 256},
@@ -198,6 +201,10 @@ is_status run_plan(const is::Plan &p, const void *x, const void *w, const float 
     case is::kMfmaNhwcF16:
       e = is::launch_mfma(p, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(w), bias,
                           static_cast<_Float16 *>(y), stream);
+      break;
+    case is::kPointwise:
+      e = is::launch_pointwise(p, static_cast<const float *>(x), static_cast<const float *>(w), bias,
+                               static_cast<float *>(y), stream);
       break;
     case is::kHeadNhwcF16:
       e = is::launch_head_f16(p, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(w), bias,

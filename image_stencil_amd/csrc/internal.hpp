@@ -12,7 +12,8 @@ enum KernelId {
   kMultiChannel = 3,     // fp32 NCHW register-blocked, C, K multiples of the block
   kMfmaNhwcF16 = 4,      // fp16 NHWC implicit GEMM on MFMA
   kMfmaNchwF32 = 5,      // fp32 NCHW 32 -> 32 3x3 implicit GEMM on the fp32 MFMA
-  kHeadNhwcF16 = 6       // fp16 NHWC first layer, 1 -> K, one MFMA k step over the taps
+  kHeadNhwcF16 = 6,      // fp16 NHWC first layer, 1 -> K, one MFMA k step over the taps
+  kPointwise = 7         // fp32 NCHW 1x1 filters over several channels
 };
 
 struct Plan {
@@ -66,6 +67,10 @@ hipError_t launch_mfma_d2s3(const Plan &p, const _Float16 *x, const _Float16 *w,
 bool configure_head_f16(Plan &p);
 hipError_t launch_head_f16(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
                            hipStream_t s);
+
+bool configure_pointwise(Plan &p, int param = 0);
+hipError_t launch_pointwise(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                            hipStream_t s);
 
 bool configure_mfma_f32(Plan &p);
 hipError_t launch_mfma_f32(const Plan &p, const float *x, const float *w, const float *b, float *y,

@@ -8,6 +8,7 @@ against the eager result bit for bit (same kernels, same inputs, same order of
 operations). The stream test runs one plan on two default-priority streams
 concurrently and compares each with its eager result.
 """
+import numpy as np
 import pytest
 
 import image_stencil_amd as isa
@@ -94,6 +95,49 @@ def test_chain_in_a_graph():
                                torch.cuda.current_stream().cuda_stream)
 
     say("graph chain")
+    _check_replays(launch, y)
+
+
+def _chain_graph_case(x, layers, d, out_shape, out_dtype):
+    import torch
+    ws_bytes = isa.conv_chain_workspace_size(d)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    xd = dev(x)
+    wl = [(dev(w), dev(b) if b is not None else None) for (w, b, _) in layers]
+    y = torch.empty(out_shape, dtype=out_dtype, device="cuda")
+
+    def launch():
+        isa.conv_chain_forward(d, xd.data_ptr(), [w.data_ptr() for (w, _) in wl],
+                               [b.data_ptr() if b is not None else None for (_, b) in wl], y.data_ptr(),
+                               ws.data_ptr() if ws_bytes else None, ws_bytes,
+                               torch.cuda.current_stream().cuda_stream)
+
+    return launch, y
+
+
+def test_fp16_net_in_a_graph():
+    """The pages' net in fp16 storage (first-layer kernel, three MFMA layers,
+    depth-to-space in the last one's stores)."""
+    import torch
+    x, layers = synth.chain_f16_nhwc(N=1, H=48, W=96, seed=10)
+    spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
+    d = isa.make_chain_desc(1, 48, 96, spec, 3, isa.IS_CHAIN_AUTO, "f16")
+    launch, y = _chain_graph_case(x, layers, d, (1, 144, 288, 1), torch.float16)
+    say("graph fp16 net")
+    _check_replays(launch, y)
+
+
+def test_stencil_pipeline_in_a_graph():
+    """A stencil pipeline in two launch groups (fused 3+3 layers)."""
+    import torch
+    rng = np.random.default_rng(11)
+    x = rng.random((1, 1, 200, 512), dtype=np.float32)
+    layers = [((rng.standard_normal((1, 1, 3, 3)) / 3).astype(np.float32), np.zeros(1, np.float32), True)
+              for _ in range(6)]
+    d = isa.make_chain_desc(1, 200, 512, [(1, 1, 3, True)] * 6, 1, isa.IS_CHAIN_AUTO)
+    assert len(isa.conv_chain_groups(d)) >= 2
+    launch, y = _chain_graph_case(x, layers, d, (1, 1, 200, 512), torch.float32)
+    say("graph stencil pipeline", isa.conv_chain_groups(d))
     _check_replays(launch, y)
 
 

@@ -45,7 +45,7 @@ CASES = [
     (1, 1, 32, 40, 136, 5, True, "is_k2_multi"),
     (1, 8, 32, 21, 72, 5, False, "is_k2_multi"),
     (1, 1, 32, 19, 68, 3, True, "is_k2_multi"),
-    (1, 12, 32, 16, 64, 1, False, "is_k2_multi"),
+    (1, 12, 32, 16, 64, 1, False, "is_k8_pointwise"),
     (1, 32, 4, 45, 140, 3, False, "is_k2_multi"),
     (3, 3, 8, 9, 20, 3, True, "is_k2_multi"),
     # one input channel, F filters (F = 2 .. 12; 1x1, 3x3, 5x5)
@@ -56,11 +56,15 @@ CASES = [
     (1, 1, 6, 16, 64, 5, False, "is_k2_multi"),
     (1, 1, 16, 21, 72, 1, True, "is_k2_multi"),
     (1, 1, 3, 21, 72, 3, False, "is_k0_generic_nchw_f32"),
-    # 1x1 filters over several channels
-    (1, 8, 16, 21, 72, 1, False, "is_k2_multi"),
-    (2, 16, 8, 33, 132, 1, True, "is_k2_multi"),
-    (1, 4, 4, 9, 64, 1, False, "is_k2_multi"),
-    (1, 3, 4, 17, 68, 1, True, "is_k2_multi"),
+    # 1x1 filters over several channels: the pointwise kernel (planes of whole
+    # 16-byte vectors, ragged last workgroup), else the fallback
+    (1, 8, 16, 21, 72, 1, False, "is_k8_pointwise"),
+    (2, 16, 8, 33, 132, 1, True, "is_k8_pointwise"),
+    (1, 4, 4, 9, 64, 1, False, "is_k8_pointwise"),
+    (1, 3, 4, 17, 68, 1, True, "is_k8_pointwise"),
+    (3, 64, 32, 37, 140, 1, True, "is_k8_pointwise"),
+    (1, 5, 12, 1, 4, 1, False, "is_k8_pointwise"),
+    (1, 8, 16, 9, 30, 1, False, "is_k0_generic_nchw_f32"),
     (1, 5, 6, 11, 30, 5, False, "is_k0_generic_nchw_f32"),
     (1, 8, 8, 10, 13, 3, True, "is_k0_generic_nchw_f32"),
 ]

@@ -37,6 +37,10 @@ def _case(name):
         x, w, b = synth.cnn_layer_f32(N=2, C=1, K=8, H=40, W=136, R=5, seed=5)
         d = isa.make_desc(2, 1, 40, 136, 8, 5, 5, "f32", False)
         return d, x, w, b, False, "NCHW", w, oracle.conv2d(x, w, b, False)
+    if name == "pointwise_8to16":
+        x, w, b = synth.cnn_layer_f32(N=2, C=8, K=16, H=33, W=132, R=1, seed=7)
+        d = isa.make_desc(2, 8, 33, 132, 16, 1, 1, "f32", True)
+        return d, x, w, b, True, "NCHW", w, oracle.conv2d(x, w, b, True)
     if name == "fp16_64to64":
         x, w, b = synth.cnn_layer_f16_nhwc(N=2, C=64, K=64, H=37, W=70, seed=6)
         d = isa.make_desc(2, 64, 37, 70, 64, 3, 3, "f16", False)
@@ -56,7 +60,7 @@ def _run(plan, x, wk, b, d):
     return host(y), (xd, wd, bd, y)
 
 
-CASES = ["single_3x3", "separable_5x5", "fp32_32to32", "one_channel_8_filters", "fp16_64to64"]
+CASES = ["single_3x3", "separable_5x5", "fp32_32to32", "one_channel_8_filters", "pointwise_8to16", "fp16_64to64"]
 
 
 @pytest.mark.parametrize("name", CASES)

@@ -238,8 +238,19 @@ def test_separable_and_special_case_plans():
     weird.separable = 2
     with pytest.raises(isa.ImgStencilError):
         isa.Plan(weird)
-    for (c, k, r) in ((1, 4, 3), (1, 8, 5), (1, 2, 1), (1, 6, 3), (8, 16, 1), (3, 4, 1)):
+    for (c, k, r) in ((1, 4, 3), (1, 8, 5), (1, 2, 1), (1, 6, 3)):
         assert isa.Plan(isa.make_desc(1, c, 64, 128, k, r, r)).info()["kernel"] == "is_k2_multi", (c, k, r)
+    # 1x1 layers over several channels: the pointwise kernel when the planes
+    # are whole 16-byte vectors (with the register-blocked kernel among the
+    # tuning variants), else the multi-channel or fallback kernel
+    for (c, k) in ((8, 16), (3, 4), (32, 32), (512, 8)):
+        assert isa.Plan(isa.make_desc(1, c, 64, 128, k, 1, 1)).info()["kernel"] == "is_k8_pointwise", (c, k)
+    vs = [(v["kernel"], v["param"]) for v in isa.conv2d_list_variants(isa.make_desc(1, 8, 64, 128, 16, 1, 1))]
+    assert vs == [("is_k8_pointwise", 16), ("is_k8_pointwise", 8), ("is_k8_pointwise", 4),
+                  ("is_k2_multi", 16), ("is_k2_multi", 8), ("is_k2_multi", 4)]
+    # staged weights over 48 KB even at 4 channels per workgroup
+    assert isa.Plan(isa.make_desc(1, 4000, 64, 128, 8, 1, 1)).info()["kernel"] == "is_k2_multi"
+    assert isa.Plan(isa.make_desc(1, 8, 9, 30, 16, 1, 1)).info()["kernel"] == "is_k0_generic_nchw_f32"
     assert isa.Plan(isa.make_desc(1, 1, 64, 128, 3, 3, 3)).info()["kernel"] == "is_k0_generic_nchw_f32"
 
 
