@@ -173,9 +173,9 @@ void fill_variant(const is::Plan &p, bool is_default, float ms, conv2d_variant *
   out->ms = ms;
 }
 
-is_status run_plan(const is::Plan &p, const void *x, const void *w, const float *bias, void *y,
-                   hipStream_t stream) {
-  const conv2d_desc &d = p.d;
+// The argument checks of a forward call (no GPU involved).
+is_status check_forward_args(const conv2d_desc &d, const void *x, const void *w, const float *bias,
+                             const void *y) {
   if (!x || !w || !y) return IS_ERR_INVALID_ARG;
   if (misaligned(x) || misaligned(w) || misaligned(y) || (bias && misaligned(bias)))
     return IS_ERR_MISALIGNED;
@@ -183,6 +183,17 @@ is_status run_plan(const is::Plan &p, const void *x, const void *w, const float 
   const size_t xb = es * (size_t)d.n * d.c * d.h * d.w;
   const size_t yb = es * (size_t)d.n * d.k * d.h * d.w;
   if (overlap(x, xb, y, yb)) return IS_ERR_INVALID_ARG;
+  return IS_OK;
+}
+
+is_status run_plan(const is::Plan &p, const void *x, const void *w, const float *bias, void *y,
+                   hipStream_t stream) {
+  const conv2d_desc &d = p.d;
+  const is_status chk = check_forward_args(d, x, w, bias, y);
+  if (chk != IS_OK) return chk;
+  const size_t es = elem_size(d.in_dtype);
+  const size_t xb = es * (size_t)d.n * d.c * d.h * d.w;
+  const size_t yb = es * (size_t)d.n * d.k * d.h * d.w;
   if (xb == 0 || yb == 0) return IS_OK;   // empty image: nothing to compute
   hipError_t e;
   switch (p.kid) {
@@ -657,6 +668,8 @@ is_status conv2d_autotune(conv2d_plan plan, const void *x, const void *w, const 
     const conv2d_desc d = plan->p.d;
     is::Plan def;
     is_status st = make_plan(&d, def);
+    if (st != IS_OK) return st;
+    st = check_forward_args(d, x, w, bias, y);   // before any HIP call
     if (st != IS_OK) return st;
     Variant v[kMaxVariants];
     const int n = collect_variants(d, def, v, kMaxVariants);

@@ -285,11 +285,20 @@ def test_tile_variants():
         isa.Plan(d, variant=len(vs))
     with pytest.raises(isa.ImgStencilError):
         isa.Plan(d, variant=-1)
-    # Tuning rejects reps < 1 before touching the GPU.
+    # Tuning checks its arguments before touching the GPU.
     p = isa.Plan(d)
     n = ctypes.c_int()
-    assert isa.load().conv2d_autotune(p.handle, 0x1000, 0x2000, None, 0x100000, None, 0, None, 0,
-                                      ctypes.byref(n)) == _abi.IS_ERR_INVALID_ARG
+    lib = isa.load()
+    assert lib.conv2d_autotune(p.handle, 0x1000, 0x2000, None, 0x100000000, None, 0, None, 0,
+                               ctypes.byref(n)) == _abi.IS_ERR_INVALID_ARG          # reps < 1
+    assert lib.conv2d_autotune(p.handle, 0x1004, 0x2000, None, 0x100000000, None, 3, None, 0,
+                               ctypes.byref(n)) == _abi.IS_ERR_MISALIGNED
+    assert lib.conv2d_autotune(p.handle, None, 0x2000, None, 0x100000000, None, 3, None, 0,
+                               ctypes.byref(n)) == _abi.IS_ERR_INVALID_ARG          # null x
+    assert lib.conv2d_autotune(p.handle, 0x1000, 0x2000, None, 0x1000, None, 3, None, 0,
+                               ctypes.byref(n)) == _abi.IS_ERR_INVALID_ARG          # x and y overlap
+    assert lib.conv2d_autotune(None, 0x1000, 0x2000, None, 0x100000000, None, 3, None, 0,
+                               ctypes.byref(n)) == _abi.IS_ERR_INVALID_ARG          # null plan
 
 
 def _stencil(h, w, rs, mode=None, n=1):
