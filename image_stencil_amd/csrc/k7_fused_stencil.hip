@@ -32,6 +32,10 @@ namespace {
 constexpr int kCols = 4 * kWave;   // window columns per wave
 constexpr int kPF = 4;             // steps per unrolled block = rows prefetched ahead
 constexpr unsigned kOob = 0xFFFFFFF0u;
+// Output stores are non-temporal (the image is written once; measured 3-4%
+// faster). Input loads keep the default policy: neighbouring windows and
+// strips re-read the overlap rows and columns.
+constexpr int kNonTemporal = 2;
 
 struct FusedArgs {
   const float *x;
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(kWave) void is_k7_fused_stencil(FusedArgs a) {
       __builtin_amdgcn_raw_buffer_store_b128(
           __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
                              make_float4(res[0], res[1], res[2], res[3])),
-          rs_o, off_st, 0, 0);
+          rs_o, off_st, 0, kNonTemporal);
       __builtin_amdgcn_sched_barrier(0);
       const float4 v = __builtin_bit_cast(
           float4, __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(xp, t + kPF, 0, a.H, a.W), off, 0, 0));
