@@ -526,6 +526,32 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
 
     if "special_cases" in groups:
         import numpy as np
+        # The 256x256 3x3 image: its 0.52 MB move in well under a microsecond
+        # at the HBM rate, so a launch is bound by launch latency and the
+        # single wave per strip; reported as time per launch (back to back).
+        x, w = synth.small_image_3x3()
+        plan = isa.Plan(isa.make_desc(1, 1, 256, 256, 1, 3, 3))
+        info = plan.info()
+        wd = torch.from_numpy(w).cuda()
+        tcases = []
+        for _ in range(4):
+            xd = torch.from_numpy(x).cuda()
+            yd = torch.empty((1, 1, 256, 256), device="cuda")
+
+            def launch(plan=plan, xd=xd, yd=yd):
+                isa.conv2d_forward(plan.handle, xd.data_ptr(), wd.data_ptr(), None, yd.data_ptr(), stream)
+
+            c = Case("256x256 3x3", launch, info["flops"], info["bytes"], info["kernel"])
+            c.keep = (xd, yd)
+            tcases.append(c)
+        _, per, _ = _time_cases(torch, tcases, steps, warmup, stream_obj)
+        ms = sum(per) / len(per)
+        out["small_image_3x3_256"] = {"workload": "single-channel fp32 256x256 3x3", "kernel": info["kernel"],
+                                      "us": round(ms * 1e3, 2), "gbs": round(info["bytes"] / ms / 1e6, 1),
+                                      "frac_hbm": round(info["bytes"] / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        for c in tcases:
+            c.keep = None
+        del plan
         # The single-channel special case beyond one filter: a separable 7x7
         # filter (row pass + column pass) and 8 filters on one channel; both
         # are bound by HBM. Two buffer sets each, so that no launch reads the
