@@ -67,7 +67,7 @@ constexpr int kLdsMax = 160 * 1024;
 constexpr int kMaxMainOps = 4;   // 16-byte DMA operations per row half, at most
 
 // Geometry of the layer with C input and K output channels.
-template <int C, int K>
+template <int C, int K, int URX = 0>
 struct K4Cfg {
   static constexpr int NH = C / 32;             // k steps (32 channels) per tap
   static constexpr int CPP = C / 8;             // 16-byte chunks per input pixel
@@ -75,7 +75,7 @@ struct K4Cfg {
   static constexpr int NOB = K / 16;            // 16-channel output blocks
   static constexpr int NCB = kWaves / NOB;      // 16-pixel column blocks of a unit
   static constexpr int TC = 16 * NCB;           // unit width (output pixels)
-  static constexpr int UR = K == 16 ? 32 : 64;  // unit height (output rows)
+  static constexpr int UR = URX ? URX : (K == 16 ? 32 : 64);   // unit height (output rows)
   static constexpr int IN_ROWS = UR + 2;        // input rows of a unit, halo included
   static constexpr int S = 4;                   // input rows per stage
   static constexpr int STAGES = (IN_ROWS + S - 1) / S;
@@ -200,9 +200,10 @@ struct UnitGeo {
 // D2S = 3: the layer's first 9 channels go through a 3x3 depth-to-space on
 // the way out (y is N x 3H x 3W fp16, out[3i+dy][3j+dx] = z[i][j][3dy+dx]),
 // in place of the staged rows' 16-channel pixel lines; 16 output channels only.
-template <int SWZ, int C, int K, int D2S = 0>
+// URX: unit height other than the default 64 rows (60 divides a 720-row frame).
+template <int SWZ, int C, int K, int D2S = 0, int URX = 0>
 __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
-  using G = K4Cfg<C, K>;
+  using G = K4Cfg<C, K, URX>;
   static_assert(D2S == 0 || (D2S == 3 && K == 16), "depth-to-space by 3 of the first 9 of 16 channels");
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
 
@@ -542,9 +543,9 @@ bool shape_supported(int c, int k) {
   return (c == 64 && (k == 64 || k == 32)) || (c == 32 && (k == 32 || k == 16));
 }
 
-template <int C, int K>
+template <int C, int K, int URX = 0>
 void fill_geometry(Plan &p) {
-  using G = K4Cfg<C, K>;
+  using G = K4Cfg<C, K, URX>;
   p.nseg = (p.d.w + G::TC - 1) / G::TC;
   p.nstrip = (p.d.h + G::UR - 1) / G::UR;
   p.lds = G::LDS_BYTES;
@@ -560,10 +561,21 @@ bool configure_mfma(Plan &p, int param) {
   if (!shape_supported(d.c, d.k) || d.r != 3 || d.s != 3) return false;
   if (2.0 * d.h * (double)d.w * d.c >= 4.0e9 || 2.0 * d.h * (double)d.w * d.k >= 4.0e9)
     return false;   // 32-bit offsets per image
-  if (d.c == 64 && d.k == 64) fill_geometry<64, 64>(p);
-  else if (d.c == 64) fill_geometry<64, 32>(p);
-  else if (d.k == 32) fill_geometry<32, 32>(p);
-  else fill_geometry<32, 16>(p);
+  // Unit height: 64 rows, or 60 when that computes fewer rows past the
+  // image's last one (a 720-row frame: 12 units of 60 rows against 12 of 64,
+  // a twelfth of them below the image), for the 64-channel inputs.
+  const bool ur60 = (d.h + 59) / 60 * 60 < (d.h + 63) / 64 * 64;
+  if (d.c == 64 && d.k == 64) {
+    if (ur60) fill_geometry<64, 64, 60>(p);
+    else fill_geometry<64, 64>(p);
+  } else if (d.c == 64) {
+    if (ur60) fill_geometry<64, 32, 60>(p);
+    else fill_geometry<64, 32>(p);
+  } else if (d.k == 32) {
+    fill_geometry<32, 32>(p);
+  } else {
+    fill_geometry<32, 16>(p);
+  }
   const long long units = (long long)p.nseg * p.nstrip * d.n;
   if (units > (1LL << 31) - 1) return false;
   p.kid = kMfmaNhwcF16;
@@ -591,6 +603,16 @@ bool configure_mfma(Plan &p, int param) {
     const int v = param < 0 ? 0 : param;
     if (v != 128 && !(d.c == 64 && d.k == 64 && (v == 0 || v == 256))) return false;
     p.vec = v;
+  }
+  // The 60-row units are built with the 128-byte swizzle only.
+  if (p.vec != 128 && p.tile_h == 60) {
+    if (d.c == 64 && d.k == 64) fill_geometry<64, 64>(p);
+    else fill_geometry<64, 32>(p);
+    const long long u64 = (long long)p.nseg * p.nstrip * d.n;
+    p.ntiles = (int)u64;
+    int g2 = 256;
+    while (g2 > 8 && g2 / 2 >= p.ntiles) g2 /= 2;
+    p.grid_x = g2;
   }
   return true;
 }
@@ -637,13 +659,17 @@ hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, cons
   a.nunits = p.ntiles;
   const dim3 grid(p.grid_x), block(p.block);
   if (p.d.c == 64 && p.d.k == 64) {
+    if (p.tile_h == 60) return launch_kernel(is_k4_mfma<128, 64, 64, 0, 60>, grid, block, 0, s, a);
     switch (p.vec) {
       case 0: return launch_kernel(is_k4_mfma<0, 64, 64>, grid, block, 0, s, a);
       case 128: return launch_kernel(is_k4_mfma<128, 64, 64>, grid, block, 0, s, a);
       default: return launch_kernel(is_k4_mfma<256, 64, 64>, grid, block, 0, s, a);
     }
   }
-  if (p.d.c == 64 && p.d.k == 32) return launch_kernel(is_k4_mfma<128, 64, 32>, grid, block, 0, s, a);
+  if (p.d.c == 64 && p.d.k == 32) {
+    if (p.tile_h == 60) return launch_kernel(is_k4_mfma<128, 64, 32, 0, 60>, grid, block, 0, s, a);
+    return launch_kernel(is_k4_mfma<128, 64, 32>, grid, block, 0, s, a);
+  }
   if (p.d.c == 32 && p.d.k == 32) return launch_kernel(is_k4_mfma<128, 32, 32>, grid, block, 0, s, a);
   if (p.d.c == 32 && p.d.k == 16) return launch_kernel(is_k4_mfma<128, 32, 16>, grid, block, 0, s, a);
   return hipErrorInvalidValue;

@@ -269,6 +269,13 @@ def test_tile_variants():
     assert names(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16")) == [
         ("is_k4_mfma", 128, True), ("is_k4_mfma", 0, False), ("is_k4_mfma", 256, False)]
     assert names(isa.make_desc(1, 64, 72, 128, 32, 3, 3, "f16")) == [("is_k4_mfma", 128, True)]
+    # fp16 MFMA units are 64 rows, or 60 where that computes fewer rows (720)
+    for (h, c, k, th) in ((256, 64, 64, 64), (720, 64, 64, 60), (720, 64, 32, 60), (720, 32, 16, 32),
+                          (1080, 64, 64, 60), (64, 64, 64, 64)):
+        assert isa.Plan(isa.make_desc(1, c, h, 1280, k, 3, 3, "f16")).info()["tile"][1] == th, (h, c, k)
+    # other swizzles keep 64-row units
+    d720 = isa.make_desc(1, 64, 720, 1280, 64, 3, 3, "f16")
+    assert [isa.Plan(d720, variant=i).info()["tile"][1] for i in range(3)] == [60, 64, 64]
     assert names(isa.make_desc(1, 1, 720, 1280, 64, 5, 5, "f16", True)) == [("is_k6_head_f16", 0, True)]
     assert names(isa.make_desc(1, 3, 16, 30, 5, 3, 3)) == [("is_k0_generic_nchw_f32", 0, True)]
     sep = names(isa.make_desc(1, 1, 512, 512, 1, 7, 7, separable=True))
