@@ -346,6 +346,12 @@ def _traffic(case):
     return None
 
 
+def _spread(cases):
+    """Median and minimum launch time over every launch of a workload's buffer sets."""
+    meds = sorted(c.median_ms for c in cases)
+    return {"median_ms": round(meds[len(meds) // 2], 4), "min_ms": round(min(c.min_ms for c in cases), 4)}
+
+
 class Case:
     """One kernel launch of a workload: callable, counted work, kernel name."""
 
@@ -411,6 +417,7 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
         ms = sum(per) / len(per)
         c = cases[0]
         out["cnn_layer_f32"] = {"workload": c.name + ", bias, ReLU", "kernel": c.kernel, "ms_per_frame": round(ms, 4),
+                                **_spread(cases),
                                 "gflops": round(c.flops / ms / 1e6, 1),
                                 "frac_fp32_valu": round(c.flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
                                 "frac_fp32_packed_peak": round(c.flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
@@ -440,7 +447,7 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
         c = mcases[0]
         ach = c.flops / ms / 1e9
         out["mfma_layer_f16"] = {"workload": c.name + ", fp32 accumulate, fp16 out", "kernel": c.kernel,
-                                 "ms": round(ms, 4), "gflops": round(c.flops / ms / 1e6, 1),
+                                 "ms": round(ms, 4), **_spread(mcases), "gflops": round(c.flops / ms / 1e6, 1),
                                  "gbs": round(c.bytes / ms / 1e6, 1),
                                  "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                                               "unit": "TFLOP/s", "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4),
@@ -479,7 +486,7 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
             ms = sum(per) / len(per)
             out["upscale_chain_" + mode_name] = {
                 "workload": ccases[0].name + ": 5x5 1->32, 3x3 32->32 x2, 3x3 32->4, depth-to-space x2",
-                "kernel": kname, "ms_per_frame": round(ms, 4), "gflops": round(flops / ms / 1e6, 1),
+                "kernel": kname, "ms_per_frame": round(ms, 4), **_spread(ccases), "gflops": round(flops / ms / 1e6, 1),
                 "frac_fp32_valu": round(flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
                 "frac_fp32_packed_peak": round(flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
                 # both paths run the two 32 -> 32 layers (90% of the FLOPs) on the
@@ -517,7 +524,8 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
         out["pages_net_f16"] = {
             "workload": ncases[0].name + ": 5x5 1->64, 3x3 64->64, 64->32, 32->9, depth-to-space x3, "
                         "fp16 storage, fp32 accumulate",
-            "kernel": "layer_by_layer", "ms_per_frame": round(ms, 4), "gflops": round(flops / ms / 1e6, 1),
+            "kernel": "layer_by_layer", "ms_per_frame": round(ms, 4), **_spread(ncases),
+            "gflops": round(flops / ms / 1e6, 1),
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None}}
         for c in ncases:
@@ -656,7 +664,12 @@ def _time_cases(torch, cases, steps, warmup, stream_obj):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
-    per = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps for i in range(len(cases))]
+    times = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)] for i in range(len(cases))]
+    per = [sum(t) / steps for t in times]
+    for c, t in zip(cases, times):   # median and minimum per launch, for the report
+        st = sorted(t)
+        c.median_ms = st[len(st) // 2] if len(st) % 2 else 0.5 * (st[len(st) // 2 - 1] + st[len(st) // 2])
+        c.min_ms = st[0]
     return total_ms / steps, per, wall
 
 
@@ -800,6 +813,7 @@ def main():
     kernels = []
     for c, ms in zip(cases, per):
         kernels.append({"case": c.name, "kernel": c.kernel, "ms": round(ms, 4),
+                        "median_ms": round(c.median_ms, 4), "min_ms": round(c.min_ms, 4),
                         "gflops": round(c.flops / ms / 1e6, 1), "gbs": round(c.bytes / ms / 1e6, 1),
                         "roofline": _roofline(c, ms)})
     dom = max(range(len(cases)), key=lambda i: per[i])
