@@ -313,11 +313,14 @@ bool stencil_chain(const conv_chain_desc *d) {
   return true;
 }
 
-// Rates measured on MI355X: the single-channel kernel streams 5.6 TB/s, the
-// vector FMA loops reach about 80% of the 78.6 TFLOP/s fp32 peak, and a
-// launch with its ramp costs a few microseconds.
+// Rates measured on MI355X: the single-channel kernel streams 5.6 TB/s and its
+// FMA loop reaches about 80% of the 78.6 TFLOP/s fp32 vector peak; the fused
+// kernel's loops reach 65-71% (more live registers per wave, and with a 5x5
+// or 7x7 filter among 5x5 or 3x3 ones the taps overflow the scalar registers);
+// a launch with its ramp costs a few microseconds.
 constexpr double kModelHbm = 5.6e12;
 constexpr double kModelAlu = 0.8 * 78.6e12;
+constexpr double kModelAluFused = 0.65 * 78.6e12;
 constexpr double kModelLaunch = 3.0e-6;
 
 // Estimated seconds of one launch of layers [first, first + count).
@@ -337,7 +340,7 @@ double model_group_seconds(const conv_chain_desc *d, int first, int count) {
   double flops = 0.0;
   for (int l = 0; l < count; ++l) flops += 2.0 * d->layer[first + l].r * d->layer[first + l].s * px * hf * vf;
   const double bytes = 4.0 * px * hf * vf + 4.0 * px;
-  return std::max(bytes / kModelHbm, flops / kModelAlu) + kModelLaunch;
+  return std::max(bytes / kModelHbm, flops / kModelAluFused) + kModelLaunch;
 }
 
 // Sizes of the launch groups of a stencil chain, in order; returns their

@@ -81,8 +81,8 @@ bool chain_fused_supported(const conv_chain_desc *d);
 hipError_t launch_chain_fused(const conv_chain_desc *d, const float *x, const float *const *w,
                               const float *const *b, float *y, hipStream_t s);
 
-// Two or three consecutive single-channel layers (1 -> 1, r = s in {3, 5},
-// fp32 NCHW, W % 4 == 0) of a chain, fused in one pass: layers
+// Two or three consecutive single-channel layers (1 -> 1, r = s in {3, 5, 7}
+// with at most one 7, fp32 NCHW, W % 4 == 0) of a chain, fused in one pass: layers
 // [first, first + count) of d, reading x and writing y (N x 1 x H x W).
 struct FusedStencilGeo {
   bool ok;

@@ -213,6 +213,10 @@ K7Fn pick(const int *r, int count) {
   IS_K7_2(3, 3) IS_K7_2(3, 5) IS_K7_2(5, 3) IS_K7_2(5, 5)
   IS_K7_3(3, 3, 3) IS_K7_3(3, 3, 5) IS_K7_3(3, 5, 3) IS_K7_3(5, 3, 3)
   IS_K7_3(3, 5, 5) IS_K7_3(5, 3, 5) IS_K7_3(5, 5, 3) IS_K7_3(5, 5, 5)
+  // one 7x7 filter in the group (two would need more scalar registers than
+  // the taps of a wave can hold)
+  IS_K7_2(7, 3) IS_K7_2(3, 7) IS_K7_2(7, 5) IS_K7_2(5, 7)
+  IS_K7_3(7, 3, 3) IS_K7_3(3, 7, 3) IS_K7_3(3, 3, 7)
 #undef IS_K7_2
 #undef IS_K7_3
   return nullptr;

@@ -50,6 +50,10 @@ SHAPES = [
     (1, 5, 8, [(5, True, True), (5, True, True), (5, False, True)], [3]),
     (1, 64, 248, [(5, False, False), (5, False, False)], [2]),
     (1, 131, 260, [(3, True, True)] * 7, None),
+    # one 7x7 filter in a fused group
+    (1, 150, 300, [(7, True, True), (3, False, True)], None),
+    (1, 77, 516, [(3, False, True), (3, True, False), (7, False, True)], None),
+    (2, 40, 128, [(5, True, True), (7, False, False)], None),
 ]
 
 
@@ -62,6 +66,17 @@ def test_pipeline_matches_oracle(N, H, W, spec, groups):
         y = _run(x, layers, mode, groups if mode == isa.IS_CHAIN_AUTO else [1] * len(spec))
         ratio = check(y, ref, m, TAU_F32, "pipeline %dx%dx%d mode %d" % (N, H, W, mode))
         say("max err/bound %.3g" % ratio)
+
+
+@pytest.mark.parametrize("rs", [(7, 3), (3, 7), (7, 5), (5, 7), (7, 3, 3), (3, 7, 3), (3, 3, 7)])
+def test_fused_groups_with_a_7x7_filter(rs):
+    """Every fused group that holds a 7x7 filter, forced with IS_CHAIN_FUSED."""
+    spec = [(r, i % 2 == 0, True) for i, r in enumerate(rs)]
+    x, layers = _pipeline(1, 70, 264, spec, seed=sum(rs))
+    ref, m = oracle.chain(x, layers)
+    say("fused group", rs)
+    y = _run(x, layers, isa.IS_CHAIN_FUSED, [len(rs)])
+    check(y, ref, m, TAU_F32, "fused group %s" % (rs,))
 
 
 def test_fused_delta_filters_bit_exact():

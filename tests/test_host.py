@@ -327,6 +327,9 @@ def test_stencil_pipeline_grouping():
         ((8192, 8192, [3] * 7), None, [3, 3, 1], "fused_groups:3+3+1", 2 * img),
         ((8192, 8192, [7, 7]), None, [1, 1], "layer_by_layer", img),
         ((8192, 8192, [5, 3, 7, 3, 3]), None, [2, 1, 2], "fused_groups:2+1+2", 2 * img),
+        ((8192, 8192, [7, 3]), None, [2], "is_k7_fused_stencil", 0),
+        ((8192, 8192, [7, 5]), None, [1, 1], "layer_by_layer", img),
+        ((8192, 8192, [7, 3, 7, 3]), None, [1, 3], "fused_groups:1+3", img),
         ((8192, 8190, [3, 3]), None, [1, 1], "layer_by_layer", 4 * 8192 * 8190),
         ((16, 16, [3, 3]), None, [2], "is_k7_fused_stencil", 0),
         ((8192, 8192, [3]), None, [1], "layer_by_layer", 0),
@@ -336,9 +339,11 @@ def test_stencil_pipeline_grouping():
         assert isa.conv_chain_groups(d) == groups, (h, w, rs, mode)
         assert isa.conv_chain_kernel_name(d) == name, (h, w, rs, mode)
         assert isa.conv_chain_workspace_size(d) == ws, (h, w, rs, mode)
-    for rs in ([3, 3, 3, 3], [7, 3], [3]):
+    for rs in ([3, 3, 3, 3], [7, 7], [7, 3, 7], [3]):
         with pytest.raises(isa.ImgStencilError):
             isa.conv_chain_groups(_stencil(64, 64, rs, isa.IS_CHAIN_FUSED))
+    for rs in ([7, 3], [3, 7], [7, 5], [3, 3, 7]):
+        assert isa.conv_chain_groups(_stencil(64, 64, rs, isa.IS_CHAIN_FUSED)) == [len(rs)]
     # the upscaling chain is not a stencil pipeline: layer by layer, or its own fused kernel
     spec = [(1, 32, 5, True), (32, 32, 3, True), (32, 32, 3, True), (32, 4, 3, False)]
     assert isa.conv_chain_groups(isa.make_chain_desc(1, 720, 1280, spec, 2, isa.IS_CHAIN_AUTO)) == [1, 1, 1, 1]
