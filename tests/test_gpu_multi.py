@@ -64,6 +64,9 @@ CASES = [
     (1, 3, 4, 17, 68, 1, True, "is_k8_pointwise"),
     (3, 64, 32, 37, 140, 1, True, "is_k8_pointwise"),
     (1, 5, 12, 1, 4, 1, False, "is_k8_pointwise"),
+    (1, 2, 4, 13, 20, 1, True, "is_k8_pointwise"),
+    (1, 384, 32, 9, 64, 1, False, "is_k8_pointwise"),   # staged weights exactly 48 KB
+    (1, 385, 32, 5, 64, 1, False, "is_k8_pointwise"),   # 16 channels per workgroup instead
     (1, 8, 16, 9, 30, 1, False, "is_k0_generic_nchw_f32"),
     (1, 5, 6, 11, 30, 5, False, "is_k0_generic_nchw_f32"),
     (1, 8, 8, 10, 13, 3, True, "is_k0_generic_nchw_f32"),
