@@ -21,11 +21,13 @@
  *    base address aligned to 16 bytes (else IS_ERR_MISALIGNED). The library
  *    never allocates device memory on a forward call and keeps no pointer
  *    after the call returns.
- *  - Weights are K,C,R,S (row-major, contiguous) in the input dtype. Bias is
- *    K fp32 values or NULL (no bias).
+ *  - Weights are K,C,R,S (row-major, contiguous) in the input dtype (a
+ *    separable filter: its R column taps then its S row taps). Bias is K fp32
+ *    values or NULL (no bias).
  *  - Accumulation is always fp32. fp16 outputs are rounded to nearest even.
  *  - Calls only enqueue work on the given stream (0 = the null stream): no host
- *    synchronisation, no allocation. Launch errors return IS_ERR_HIP and
+ *    synchronisation, no allocation. The one exception is conv2d_autotune,
+ *    which times on the stream and waits for it. Launch errors return IS_ERR_HIP and
  *    is_last_hip_error() gives the hipError_t. Faults inside a kernel surface
  *    at the caller's next synchronisation.
  *  - No exception crosses this boundary; every function returns a status.
