@@ -91,3 +91,38 @@ def test_random_shape(i, kind, N, C, K, H, W, R, S, relu, bias):
     got = host(y)
     check(got, ref, m, TAU_F16 if f16 else TAU_F32,
           "random %d %s (%s)" % (i, kind, plan.info()["kernel"]))
+
+
+def _draw_pipelines(n=24, seed=4321):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        L = int(rng.integers(1, 7))
+        rs = [int(rng.choice([1, 3, 3, 5, 5, 7])) for _ in range(L)]
+        N = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 90))
+        W = int(rng.integers(1, 80)) * 4 if rng.random() < 0.8 else int(rng.integers(1, 300))
+        out.append((i, N, H, W, tuple(rs)))
+    return out
+
+
+PIPES = _draw_pipelines()
+
+
+@pytest.mark.parametrize("i,N,H,W,rs", PIPES, ids=[str(p[0]) for p in PIPES])
+def test_random_pipeline(i, N, H, W, rs):
+    """Chains of single-channel filters under the model's grouping."""
+    rng = np.random.default_rng(2000 + i)
+    x = rng.random((N, 1, H, W), dtype=np.float32)
+    layers = []
+    for r in rs:
+        w = (rng.standard_normal((1, 1, r, r)) / r).astype(np.float32)
+        b = (rng.standard_normal(1) * 0.1).astype(np.float32) if rng.random() < 0.6 else None
+        layers.append((w, b, bool(rng.random() < 0.5)))
+    d = isa.make_chain_desc(N, H, W, [(1, 1, r, relu) for r, (_, _, relu) in zip(rs, layers)], 1, isa.IS_CHAIN_AUTO)
+    groups = isa.conv_chain_groups(d)
+    say("pipeline", i, N, H, W, rs, groups)
+    dl = [(dev(w), dev(b) if b is not None else None, relu) for (w, b, relu) in layers]
+    y = host(isa.conv_chain(dev(x), dl, 1, isa.IS_CHAIN_AUTO))
+    ref, m = oracle.chain(x, layers)
+    check(y, ref, m, TAU_F32, "pipeline %d %s groups %s" % (i, rs, groups))
