@@ -12,6 +12,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libimgstencil.so")
+# Debug variant for the tests: every LDS-staging kernel first fills its LDS
+# with NaN (IMGSTENCIL_LDS_POISON), so that reading LDS that was never written
+# shows up in the results. Never loaded by the binding.
+LIB_LDS_POISON = os.path.join(HERE, "libimgstencil_ldspoison.so")
 ROOT = os.path.dirname(HERE)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -26,19 +30,33 @@ def sources():
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every csrc/*.hip to an object in parallel, then link the library."""
-    objdir = os.path.join(HERE, "_build")
-    os.makedirs(objdir, exist_ok=True)
-    procs, objs = [], []
-    for src in sources():
-        obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        objs.append(obj)
-        cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
-        if len([p for _, p in procs if p.poll() is None]) >= jobs:
-            procs[0][1].wait()
+    """Build the library and its LDS-poison debug variant; returns the library's path."""
+    variants = [(LIB, "_build", []), (LIB_LDS_POISON, "_build_ldspoison", ["-DIMGSTENCIL_LDS_POISON"])]
+    _compile_and_link(variants, verbose, jobs)
+    return LIB
+
+
+def _compile_and_link(variants, verbose, jobs):
+    """Compile every csrc/*.hip of every variant to objects in parallel, then
+    link each variant's library."""
+    procs, objs = [], {}
+    running = []
+    for lib, objname, defines in variants:
+        objdir = os.path.join(HERE, objname)
+        os.makedirs(objdir, exist_ok=True)
+        objs[lib] = []
+        for src in sources():
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            objs[lib].append(obj)
+            cmd = [HIPCC] + FLAGS + defines + ["-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            p = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+            procs.append((src, p))
+            running.append(p)
+            while len([q for q in running if q.poll() is None]) >= jobs:
+                running[0].wait()
+                running = [q for q in running if q.poll() is None]
     failed = []
     for src, p in procs:
         out, _ = p.communicate()
@@ -51,7 +69,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    for lib, _, _ in variants:
+        _link(lib, objs[lib], verbose)
+
+
+def _link(lib, objs, verbose):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -65,9 +88,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         missing = [l.strip() for l in nm.stdout.splitlines() if "is::" in l]
         if missing:
             os.remove(tmp)
-            raise RuntimeError("libimgstencil.so has undefined symbols of its own:\n  " + "\n  ".join(missing))
-    os.replace(tmp, LIB)
-    return LIB
+            raise RuntimeError("%s has undefined symbols of its own:\n  %s" % (os.path.basename(lib),
+                                                                              "\n  ".join(missing)))
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -30,6 +30,22 @@ __device__ __forceinline__ float from_next_lane(float src, float old) {
                                                     kDppWaveShl1, 0xf, 0xf, false));
 }
 
+// Debug builds (-DIMGSTENCIL_LDS_POISON) fill a kernel's LDS with a pattern
+// that is NaN both as fp32 and as each fp16 half before the kernel stages
+// anything, so that a read of LDS that was never written (a missing wait or
+// barrier, an unwritten halo) turns into NaN in the output, which the parity
+// tests reject. Release builds compile it to nothing.
+__device__ __forceinline__ void lds_poison(void *lds, int bytes) {
+#ifdef IMGSTENCIL_LDS_POISON
+  unsigned *p = static_cast<unsigned *>(lds);
+  for (int i = threadIdx.x; i < bytes / 4; i += blockDim.x) p[i] = 0x7FC07FC0u;
+  __syncthreads();
+#else
+  (void)lds;
+  (void)bytes;
+#endif
+}
+
 // Workgroup barrier for LDS data only: waits for this wave's LDS operations
 // (lgkmcnt 0) but not for its vector-memory operations, so that loads into
 // another LDS buffer stay in flight across it (__syncthreads() waits for

@@ -81,6 +81,8 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi(const float *__restrict_
   constexpr int P = G::P;
   __shared__ float4 buf0[G::PADV4];
   __shared__ float4 buf1[G::PADV4];
+  lds_poison(buf0, sizeof(buf0));
+  lds_poison(buf1, sizeof(buf1));
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;

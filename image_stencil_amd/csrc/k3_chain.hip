@@ -119,6 +119,9 @@ __global__ __launch_bounds__(kThreads) void is_k3_chain(ChainArgs a) {
   __shared__ float4 in_ring[kInRing * kInG];
   __shared__ float4 ring[3][kRing * kCh * kG];
   __shared__ float l4buf[4 * kRows * kWin];
+  lds_poison(in_ring, sizeof(in_ring));
+  lds_poison(ring, sizeof(ring));
+  lds_poison(l4buf, sizeof(l4buf));
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform

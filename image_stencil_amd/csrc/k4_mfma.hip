@@ -206,6 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   using G = K4Cfg<C, K, URX>;
   static_assert(D2S == 0 || (D2S == 3 && K == 16), "depth-to-space by 3 of the first 9 of 16 channels");
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+  lds_poison(lds, sizeof(lds));
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -90,6 +90,7 @@ struct MfmaF32Args {
 
 __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
   __shared__ float lds[2 * kBufFloats];
+  lds_poison(lds, sizeof(lds));
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

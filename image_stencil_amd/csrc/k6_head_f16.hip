@@ -105,6 +105,7 @@ __global__ __launch_bounds__(kThreads) void is_k6_head_f16(HeadArgs a) {
   // (branch-free: a conditional write would leave the compiler unsure
   // which prefetch loads are still in flight).
   __shared__ _Float16 tile[2][G::SLOTS];
+  lds_poison(tile, sizeof(tile));
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -34,6 +34,7 @@ __global__ __launch_bounds__(kThreads) void is_k8_pointwise(const float *__restr
                                                            int C, int HW, int K) {
   extern __shared__ float4 wt4[];      // [C][KB / 4]: channel c's KB weights
   float *wt = reinterpret_cast<float *>(wt4);
+  lds_poison(wt4, C * KB * 4);
   const int tid = threadIdx.x;
   const int kg = blockIdx.y;
   const int n = blockIdx.z;
