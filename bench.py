@@ -562,9 +562,14 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
         del plan
         # The single-channel special case beyond one filter: a separable 7x7
         # filter (row pass + column pass) and 8 filters on one channel; both
-        # are bound by HBM. Two buffer sets each, so that no launch reads the
-        # previous one's data from the last-level cache.
-        specs = [("separable_7x7_8192", "separable 7x7 filter, 8192x8192 fp32", (1, 1, 8192, 8192, 1, 7, 7), True),
+        # are bound by HBM. A 1x1 filter (one multiply per pixel) on the same
+        # kernel is the copy rate that its load and store streams reach with
+        # no filter work: the practical ceiling of the 3x3/5x5 filters. Two
+        # buffer sets each, so that no launch reads the previous one's data
+        # from the last-level cache.
+        specs = [("filter_1x1_8192", "1x1 filter (copy bound of the single-channel kernel), 8192x8192 fp32",
+                  (1, 1, 8192, 8192, 1, 1, 1), False),
+                 ("separable_7x7_8192", "separable 7x7 filter, 8192x8192 fp32", (1, 1, 8192, 8192, 1, 7, 7), True),
                  ("one_channel_8_filters_3x3_4096", "1 channel -> 8 filters 3x3, 4096x4096 fp32",
                   (1, 1, 4096, 4096, 8, 3, 3), False)]
         for key, name, (n_, c_, h_, w_, k_, r_, s_), sep in specs:

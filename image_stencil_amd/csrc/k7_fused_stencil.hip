@@ -49,6 +49,16 @@ struct FusedArgs {
   int lanes_off;                   // a
 };
 
+// The neighbour lane's value, 0 for the lane at the wave's edge (a DPP wave
+// shift with bound control: the lane without a source reads zero, so no
+// register has to hold a zero "old" value).
+__device__ __forceinline__ float prev_lane_or_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kDppWaveShr1, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float next_lane_or_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kDppWaveShl1, 0xf, 0xf, true));
+}
+
 template <int R>
 struct Ring {
   float acc[R > 0 ? R : 1][4];
@@ -63,17 +73,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float *base, in
 }
 
 // One stage on one input row (this lane's 4 columns): add the row to the R
-// rolling output rows, hand out the oldest (now complete) one and rotate.
+// rolling output rows, hand out the oldest (now complete) one and rotate. A
+// recycled slot starts at the stage's bias, so a finished row already holds
+// bias + sum of products.
 template <int R>
-__device__ __forceinline__ void stage_row(Ring<R> &g, const float *wt, const float (&in)[4], float (&out)[4]) {
+__device__ __forceinline__ void stage_row(Ring<R> &g, const float *wt, float bias, const float (&in)[4],
+                                          float (&out)[4]) {
   constexpr int Q = (R - 1) / 2;
   float win[4 + 2 * Q];
 #pragma unroll
   for (int i = 0; i < 4; ++i) win[Q + i] = in[i];
 #pragma unroll
   for (int q = 1; q <= Q; ++q) {
-    win[Q - q] = from_prev_lane(in[4 - q], 0.f);
-    win[Q + 3 + q] = from_next_lane(in[q - 1], 0.f);
+    win[Q - q] = prev_lane_or_zero(in[4 - q]);
+    win[Q + 3 + q] = next_lane_or_zero(in[q - 1]);
   }
   // Ring slot j holds output row (input row - Q + j): it takes filter row R-1-j.
 #pragma unroll
@@ -89,17 +102,22 @@ __device__ __forceinline__ void stage_row(Ring<R> &g, const float *wt, const flo
 #pragma unroll
     for (int i = 0; i < 4; ++i) g.acc[j][i] = g.acc[j + 1][i];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) g.acc[R - 1][i] = 0.f;
+  for (int i = 0; i < 4; ++i) g.acc[R - 1][i] = bias;
 }
 
-// Bias, ReLU and the zero padding of an intermediate row.
-__device__ __forceinline__ void finish_row(float (&v)[4], float b, bool relu, bool keep) {
+// ReLU and the zero padding of a finished row in one clamp per value: the
+// median of (v, lo, hi) is max(v, 0) for lo = 0, hi = +inf (ReLU), v for
+// lo = -inf, hi = +inf (none), and 0 for lo = hi = 0 (a row or column outside
+// the image, which the next stage must read as zero).
+struct Clamp {
+  float lo, hi;
+};
+__device__ __forceinline__ Clamp row_clamp(bool relu, bool keep) {
+  return Clamp{keep ? (relu ? 0.f : -__builtin_inff()) : 0.f, keep ? __builtin_inff() : 0.f};
+}
+__device__ __forceinline__ void finish_row(float (&v)[4], Clamp c) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float o = v[i] + b;
-    if (relu) o = fmaxf(o, 0.f);
-    v[i] = keep ? o : 0.f;
-  }
+  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_fmed3f(v[i], c.lo, c.hi);
 }
 
 template <int R>
@@ -149,12 +167,16 @@ __global__ __launch_bounds__(kWave) void is_k7_fused_stencil(FusedArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < R1; ++j) g1.acc[j][i] = 0.f;
+    for (int j = 0; j < R1; ++j) g1.acc[j][i] = b1;
 #pragma unroll
-    for (int j = 0; j < R2; ++j) g2.acc[j][i] = 0.f;
+    for (int j = 0; j < R2; ++j) g2.acc[j][i] = b2;
 #pragma unroll
-    for (int j = 0; j < (R3 > 0 ? R3 : 1); ++j) g3.acc[j][i] = 0.f;
+    for (int j = 0; j < (R3 > 0 ? R3 : 1); ++j) g3.acc[j][i] = b3;
   }
+  // The last stage's row is stored only inside the strip, so its clamp is
+  // fixed; the inner stages' depend on the row (rows above or below the
+  // image are zero padding for the next stage).
+  const Clamp c_last = row_clamp(R3 > 0 ? relu3 : relu2, true);
 
   float pf[kPF][4];
 #pragma unroll
@@ -174,21 +196,21 @@ __global__ __launch_bounds__(kWave) void is_k7_fused_stencil(FusedArgs a) {
       const int t = t0 + kb + p;
       float in[4] = {pf[p][0], pf[p][1], pf[p][2], pf[p][3]};
       float o1[4], o2[4], o3[4];
-      stage_row<R1>(g1, w1, in, o1);
+      stage_row<R1>(g1, w1, b1, in, o1);
       const int e1 = t - P1;
-      finish_row(o1, b1, relu1, col_in && e1 >= 0 && e1 < a.H);
-      stage_row<R2>(g2, w2, o1, o2);
+      finish_row(o1, row_clamp(relu1, col_in && e1 >= 0 && e1 < a.H));
+      stage_row<R2>(g2, w2, b2, o1, o2);
       const int e2 = e1 - P2;
       float *res = o2;
       int eL = e2;
       if constexpr (R3 > 0) {
-        finish_row(o2, b2, relu2, col_in && e2 >= 0 && e2 < a.H);
-        stage_row<R3>(g3, w3, o2, o3);
+        finish_row(o2, row_clamp(relu2, col_in && e2 >= 0 && e2 < a.H));
+        stage_row<R3>(g3, w3, b3, o2, o3);
         eL = e2 - P3;
-        finish_row(o3, b3, relu3, true);
+        finish_row(o3, c_last);
         res = o3;
       } else {
-        finish_row(o2, b2, relu2, true);
+        finish_row(o2, c_last);
       }
       const __amdgpu_buffer_rsrc_t rs_o = row_rsrc(yp, eL, y0, y0 + rows_out, a.W);
       __builtin_amdgcn_raw_buffer_store_b128(
