@@ -96,10 +96,14 @@ def _short_kernel(name):
 
 
 def _counter_means(d, counter):
-    """Mean per dispatch of one counter, by kernel, over every counter CSV under d."""
+    """Mean per dispatch of one counter, by kernel, over every counter CSV under d.
+    A kernel instance launched at several sizes (the 3x3 filter on the 8192x8192
+    image and on the 256x256 one) keeps only its largest launches, which are the
+    bench case the figure belongs to."""
     import csv
     import glob
-    per = {}   # (kernel, dispatch) -> summed value
+    per = {}   # (kernel, file, dispatch) -> summed value
+    grid = {}
     full = {}
     for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         with open(f) as fh:
@@ -110,10 +114,16 @@ def _counter_means(d, counter):
                 full[k] = r["Kernel_Name"]
                 key = (k, f, r["Dispatch_Id"])
                 per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+                grid[key] = int(r["Grid_Size"])
     acc = {}
-    for (k, _, _), v in per.items():
-        acc.setdefault(k, []).append(v)
-    return {k: (sum(v) / len(v), len(v), full[k]) for k, v in acc.items()}
+    for key, v in per.items():
+        acc.setdefault(key[0], []).append((grid[key], v))
+    out = {}
+    for k, gv in acc.items():
+        top = max(g for g, _ in gv)
+        vals = [v for g, v in gv if g == top]
+        out[k] = (sum(vals) / len(vals), len(vals), full[k])
+    return out
 
 
 # Arguments of the bench runs under the profiler: the counter and trace runs of
@@ -179,13 +189,26 @@ def stats_summary(trace_dir, net=False):
     the run of the pages' net, with the layer each kernel runs)."""
     import csv
     import glob
-    files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True))
+    files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
     if not files:
-        raise SystemExit("no kernel_stats.csv under %s" % trace_dir)
+        raise SystemExit("no kernel_trace.csv under %s" % trace_dir)
     cases = dict(NET_KERNELS) if net else {k: c for c, (k, _) in TRAFFIC_KERNELS.items()}
     title = ("Kernel durations of the pages' fp16 net per 1280x720 frame" if net
              else "Kernel durations of the bench workloads")
     out_file = "pages_net_f16_kernels.md" if net else "kernel_durations_bench_workloads.md"
+    # Dispatches grouped by kernel and launch size (workgroups x threads), so
+    # that one instance run on two workloads gives two rows; the bench case is
+    # named on the largest launch of its kernel.
+    groups = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            k = _short_kernel(r["Kernel_Name"])
+            g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            groups.setdefault((k, g), []).append(ns)
+    top = {}
+    for (k, g) in groups:
+        top[k] = max(top.get(k, 0), g)
     lines = ["# %s (rocprofv3 kernel trace)" % title, "",
              "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
              "rocprofv3 --kernel-trace --stats --output-format csv -d %s -o run -- \\" % trace_dir,
@@ -193,16 +216,16 @@ def stats_summary(trace_dir, net=False):
              "python3 bench.py --%s %s > profiles/%s" % ("net-stats-summary" if net else "stats-summary",
                                                         trace_dir, out_file),
              "```", "",
-             "Durations in microseconds over every dispatch of the run (warmup included). The bench's",
-             "own per-launch event timings of the same run are printed in its JSON line.", "",
-             "| kernel | %s | calls | avg us | min us | max us |" % ("layer" if net else "bench case"),
-             "|---|---|---|---|---|---|"]
-    with open(files[0]) as fh:
-        for r in csv.DictReader(fh):
-            k = _short_kernel(r["Name"])
-            lines.append("| `%s` | %s | %s | %.1f | %.1f | %.1f |" % (
-                k[:70], cases.get(k, ""), r["Calls"], float(r["AverageNs"]) / 1e3,
-                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+             "Durations in microseconds (end minus start of each dispatch in the kernel trace) over every",
+             "dispatch of the run, warmup included, one row per kernel and launch size (grid threads). The",
+             "bench's own per-launch event timings of the same run are printed in its JSON line.", "",
+             "| kernel | grid threads | %s | calls | avg us | min us | max us |" % ("layer" if net else "bench case"),
+             "|---|---|---|---|---|---|---|"]
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    for (k, g), ns in rows:
+        case = cases.get(k, "") if g == top[k] else ""
+        lines.append("| `%s` | %d | %s | %d | %.1f | %.1f | %.1f |" % (
+            k[:70], g, case, len(ns), sum(ns) / len(ns) / 1e3, min(ns) / 1e3, max(ns) / 1e3))
     return "\n".join(lines) + "\n"
 
 
