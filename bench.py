@@ -42,13 +42,13 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0
 # source changes, the case reports traffic null until the counters are re-taken.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 TRAFFIC_KERNELS = {   # bench case -> (kernel as the profiler names it, its source files)
-    "8192x8192 3x3": ("is_k1_single<3, 3, true, false, false>", ("k1_single.hip",)),
-    "8192x8192 5x5": ("is_k1_single<5, 5, true, false, false>", ("k1_single.hip",)),
-    "8192x8192 7x7": ("is_k1_single<7, 7, true, false, false>", ("k1_single.hip",)),
+    "8192x8192 3x3": ("is_k1_single<3, 3, true, false, false, 1>", ("k1_single.hip",)),
+    "8192x8192 5x5": ("is_k1_single<5, 5, true, false, false, 1>", ("k1_single.hip",)),
+    "8192x8192 7x7": ("is_k1_single<7, 7, true, false, false, 1>", ("k1_single.hip",)),
     "fp32 layer 1x32x720x1280 -> 32, 3x3": ("is_k5_mfma_f32", ("k5_mfma_f32.hip",)),
     "fp16 NHWC layer 8x256x256x64 -> 64, 3x3": ("is_k4_mfma<128, 64, 64, 0, 0>", ("k4_mfma.hip",)),
     "upscaling chain 1280x720 (fused)": ("is_k3_chain", ("k3_chain.hip",)),
-    "separable 7x7 filter, 8192x8192 fp32": ("is_k1_single<7, 7, true, false, true>", ("k1_single.hip",)),
+    "separable 7x7 filter, 8192x8192 fp32": ("is_k1_single<7, 7, true, false, true, 1>", ("k1_single.hip",)),
     "1 channel -> 8 filters 3x3, 4096x4096 fp32": ("is_k2_multi<3, 8, 1, false, false>", ("k2_multi.hip",)),
     "stencil pipeline 3x3 x3, 8192x8192 fp32 (auto)": ("is_k7_fused_stencil<3, 3, 3>", ("k7_fused_stencil.hip",)),
 }
@@ -605,7 +605,9 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
                   (1, 1, 8192, 8192, 1, 1, 1), False),
                  ("separable_7x7_8192", "separable 7x7 filter, 8192x8192 fp32", (1, 1, 8192, 8192, 1, 7, 7), True),
                  ("one_channel_8_filters_3x3_4096", "1 channel -> 8 filters 3x3, 4096x4096 fp32",
-                  (1, 1, 4096, 4096, 8, 3, 3), False)]
+                  (1, 1, 4096, 4096, 8, 3, 3), False),
+                 ("one_channel_4_filters_3x3_4096", "1 channel -> 4 filters 3x3, 4096x4096 fp32",
+                  (1, 1, 4096, 4096, 4, 3, 3), False)]
         for key, name, (n_, c_, h_, w_, k_, r_, s_), sep in specs:
             plan = isa.Plan(isa.make_desc(n_, c_, h_, w_, k_, r_, s_, "f32", False, separable=sep))
             info = plan.info()

@@ -8,7 +8,7 @@ namespace is {
 enum KernelId {
   kGenericNchwF32 = 0,   // one thread per output, any shape (fallback)
   kGenericNhwcF16 = 1,   // one thread per output, any shape (fallback)
-  kSingleChannel = 2,    // C = K = 1, fp32 NCHW, r, s <= 7
+  kSingleChannel = 2,    // C = 1, fp32 NCHW: K = 1 with r, s <= 7, or K = 2, 4, 8 filters
   kMultiChannel = 3,     // fp32 NCHW register-blocked, C, K multiples of the block
   kMfmaNhwcF16 = 4,      // fp16 NHWC implicit GEMM on MFMA
   kMfmaNchwF32 = 5,      // fp32 NCHW 32 -> 32 3x3 implicit GEMM on the fp32 MFMA

@@ -24,7 +24,11 @@
 //  * separable filters w[u][v] = col[u] * row[v] (SEP): each input row is
 //    filtered once along the row (S FMAs per pixel) and that row result enters
 //    the R rolling output rows with the column taps (R FMAs), R + S FMAs per
-//    pixel instead of R * S.
+//    pixel instead of R * S;
+//  * F filters on the one channel (the page's general case with a single input
+//    channel): each input row, fetched once, feeds F rings of rolling output
+//    rows, and every step stores one row of each of the F output planes. The
+//    F * R * S taps stay in scalar registers, so F * R * S is kept <= 72.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -39,9 +43,11 @@ constexpr int kSegCols = 4 * kWave;   // 256 output columns per wave
 // rows that neighbouring strips read from L2). Measured 2-4% faster.
 constexpr int kNonTemporal = 2;
 
-template <int R>
+template <int R, int F>
 struct Unroll {   // rows per unrolled step: a multiple of R (ring slots are static)
-  static constexpr int value = R == 1 ? 4 : (R == 3 ? 6 : R);
+  // With F filters the F rings take the registers that a deeper prefetch
+  // would use.
+  static constexpr int value = R == 1 ? 4 : (R == 3 && F == 1 ? 6 : R);
 };
 
 struct Row4 {
@@ -94,7 +100,7 @@ __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, int off_m, i
     h.v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off_h + 4 * i, 0, 0));
 }
 
-template <int R, int S, bool VEC, bool RELU, bool SEP>
+template <int R, int S, bool VEC, bool RELU, bool SEP, int F>
 __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ x,
                                                      const float *__restrict__ w,
                                                      const float *__restrict__ bias,
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
                                                      int strip_rows, int nseg, int nstrip,
                                                      int ntiles) {
   constexpr int P = (R - 1) / 2, Q = (S - 1) / 2;
-  constexpr int U = Unroll<R>::value;
+  constexpr int U = Unroll<R, F>::value;
   constexpr int NW = 4 + 2 * Q;   // window: 4 own columns plus Q each side
 
   const int lane = threadIdx.x;
@@ -118,19 +124,22 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
 
   const size_t plane = (size_t)H * (size_t)W;
   const float *xp = x + (size_t)n * plane;
-  float *yp = y + (size_t)n * plane;
+  float *yp = y + (size_t)n * F * plane;   // output plane f of image n at yp + f * plane
 
   // Byte offsets inside a row. Lanes other than 0 and 63 aim their halo load
   // past any row so that it reads nothing.
   const int off_m = 4 * col;
   const int off_h = lane == 0 ? 4 * (x0 - Q) : (lane == kWave - 1 ? 4 * (x0 + kSegCols) : INT_MIN);
 
-  // Taps: R*S filter values, or (SEP) R column taps then S row taps.
-  constexpr int NTAPS = SEP ? R + S : R * S;
+  // Taps: F*R*S filter values (filter f's at f*R*S), or (SEP) R column taps
+  // then S row taps.
+  constexpr int NTAPS = SEP ? R + S : F * R * S;
   float wr[NTAPS];
 #pragma unroll
   for (int i = 0; i < NTAPS; ++i) wr[i] = w[i];
-  const float bv = bias ? bias[0] : 0.f;
+  float bv[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) bv[f] = bias ? bias[f] : 0.f;
 
   // Input rows this strip needs: y0-P .. y0+rows_out-1+P, clipped to the image.
   const int in_hi = min(H, y0 + rows_out + P);
@@ -146,13 +155,16 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // acc[slot]: ring of the R output rows that the current input row touches;
-  // output row o (relative ro = o - y0) lives in slot (ro + 2P) mod R.
-  float acc[R][4];
+  // acc[f][slot]: filter f's ring of the R output rows that the current input
+  // row touches; output row o (relative ro = o - y0) lives in slot
+  // (ro + 2P) mod R.
+  float acc[F][R][4];
 #pragma unroll
-  for (int s = 0; s < R; ++s)
+  for (int f = 0; f < F; ++f)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[s][i] = 0.f;
+    for (int s = 0; s < R; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[f][s][i] = 0.f;
 
   // No branch inside the loop: the rounds past NT read zero rows and store
   // nothing (their rows are outside both buffer ranges), so the loads, the
@@ -207,38 +219,44 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
         if constexpr (SEP) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc[slot][i] = j == R - 1 ? __builtin_fmaf(wr[u], hrow[i], bv)
-                                      : __builtin_fmaf(wr[u], hrow[i], acc[slot][i]);
+            acc[0][slot][i] = j == R - 1 ? __builtin_fmaf(wr[u], hrow[i], bv[0])
+                                         : __builtin_fmaf(wr[u], hrow[i], acc[0][slot][i]);
           continue;
         }
 #pragma unroll
-        for (int v = 0; v < S; ++v)
+        for (int f = 0; f < F; ++f)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[slot][i] = (j == R - 1 && v == 0)
-                               ? __builtin_fmaf(wr[u * S + v], win[i + v], bv)
-                               : __builtin_fmaf(wr[u * S + v], win[i + v], acc[slot][i]);
+          for (int v = 0; v < S; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[f][slot][i] = (j == R - 1 && v == 0)
+                                    ? __builtin_fmaf(wr[(f * R + u) * S + v], win[i + v], bv[f])
+                                    : __builtin_fmaf(wr[(f * R + u) * S + v], win[i + v], acc[f][slot][i]);
       }
 
       // Output row r-2P (slot p mod R) is complete (the bias entered with its
-      // first product); it is stored only when it lies inside the strip.
-      float o[4];
+      // first product); it is stored, in each of the F planes, only when it
+      // lies inside the strip.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[i] = acc[p % R][i];
-        if constexpr (RELU) o[i] = fmaxf(o[i], 0.f);
-      }
-      const __amdgpu_buffer_rsrc_t rs_o = row_rsrc(yp, y0 + r - 2 * P, y0, y0 + rows_out, W);
-      if constexpr (VEC) {
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
-                               make_float4(o[0], o[1], o[2], o[3])),
-            rs_o, off_m, 0, kNonTemporal);
-      } else {
+      for (int f = 0; f < F; ++f) {
+        float o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, o[i]), rs_o,
-                                                off_m + 4 * i, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          o[i] = acc[f][p % R][i];
+          if constexpr (RELU) o[i] = fmaxf(o[i], 0.f);
+        }
+        const __amdgpu_buffer_rsrc_t rs_o = row_rsrc(yp + (size_t)f * plane, y0 + r - 2 * P, y0, y0 + rows_out, W);
+        if constexpr (VEC) {
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
+                                 make_float4(o[0], o[1], o[2], o[3])),
+              rs_o, off_m, 0, kNonTemporal);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, o[i]), rs_o,
+                                                  off_m + 4 * i, 0, 0);
+        }
       }
       // Prefetch U rows ahead into the registers this row has just released
       // (the scheduling barrier keeps the load after the row's last FMA, so
@@ -264,7 +282,7 @@ using K1Fn = void (*)(const float *, const float *, const float *, float *, int,
 template <bool VEC, bool RELU>
 K1Fn pick(int r, int s) {
 #define IS_K1_CASE(RR, SS) \
-  if (r == RR && s == SS) return is_k1_single<RR, SS, VEC, RELU, false>;
+  if (r == RR && s == SS) return is_k1_single<RR, SS, VEC, RELU, false, 1>;
 #define IS_K1_ROW(RR) IS_K1_CASE(RR, 1) IS_K1_CASE(RR, 3) IS_K1_CASE(RR, 5) IS_K1_CASE(RR, 7)
   IS_K1_ROW(1) IS_K1_ROW(3) IS_K1_ROW(5) IS_K1_ROW(7)
 #undef IS_K1_ROW
@@ -276,14 +294,28 @@ K1Fn pick(int r, int s) {
 template <bool VEC, bool RELU>
 K1Fn pick_sep(int r, int s) {
   if (r != s) return nullptr;
-  if (r == 3) return is_k1_single<3, 3, VEC, RELU, true>;
-  if (r == 5) return is_k1_single<5, 5, VEC, RELU, true>;
-  if (r == 7) return is_k1_single<7, 7, VEC, RELU, true>;
+  if (r == 3) return is_k1_single<3, 3, VEC, RELU, true, 1>;
+  if (r == 5) return is_k1_single<5, 5, VEC, RELU, true, 1>;
+  if (r == 7) return is_k1_single<7, 7, VEC, RELU, true, 1>;
+  return nullptr;
+}
+
+// F filters on one channel, square sizes with F * R * R <= 72 taps.
+template <bool VEC, bool RELU>
+K1Fn pick_fanout(int f, int r, int s) {
+  if (r != s) return nullptr;
+#define IS_K1_FAN(FF, RR) \
+  if (f == FF && r == RR) return is_k1_single<RR, RR, VEC, RELU, false, FF>;
+  IS_K1_FAN(2, 1) IS_K1_FAN(2, 3) IS_K1_FAN(2, 5)
+  IS_K1_FAN(4, 1) IS_K1_FAN(4, 3)
+  IS_K1_FAN(8, 1) IS_K1_FAN(8, 3)
+#undef IS_K1_FAN
   return nullptr;
 }
 
 template <bool VEC, bool RELU>
 K1Fn pick_any(const conv2d_desc &d) {
+  if (d.k > 1) return d.separable ? nullptr : pick_fanout<VEC, RELU>(d.k, d.r, d.s);
   return d.separable ? pick_sep<VEC, RELU>(d.r, d.s) : pick<VEC, RELU>(d.r, d.s);
 }
 
@@ -291,7 +323,7 @@ K1Fn pick_any(const conv2d_desc &d) {
 
 bool configure_single(Plan &p, int param) {
   const conv2d_desc &d = p.d;
-  if (d.c != 1 || d.k != 1 || d.layout != IS_NCHW || d.in_dtype != IS_F32) return false;
+  if (d.c != 1 || d.layout != IS_NCHW || d.in_dtype != IS_F32) return false;
   if (d.r > 7 || d.s > 7) return false;
   if (pick_any<true, false>(d) == nullptr) return false;
   const int nseg = (d.w + kSegCols - 1) / kSegCols;
@@ -303,13 +335,25 @@ bool configure_single(Plan &p, int param) {
   // measured slower (128 rows: -15% on the 3x3), shorter ones no faster.
   int rows = 64;
   while (rows > 8 && (long long)nseg * ((d.h + rows - 1) / rows) * d.n < 4096) rows >>= 1;
+  if (d.k > 1) {
+    // F filters: 32-row strips (2048 waves on a 4096x4096 image). Measured
+    // against the multi-channel kernel, which stages the tile in LDS and
+    // spreads the F planes' stores over the waves of a workgroup: this one is
+    // 7-31% faster with 2 or 4 filters on large images, 10% slower with 8
+    // (eight stores per row step, and the 72 taps no longer fit the scalar
+    // registers), and slower on small images, which give it too few waves.
+    // Those shapes stay with the multi-channel kernel unless a tuning variant
+    // asks for this one.
+    rows = 32;
+    if (param == 0 && (d.k > 4 || (long long)nseg * ((d.h + rows - 1) / rows) * d.n < 2048)) return false;
+  }
   if (param != 0) {   // a tuning variant: 8 to 256 rows
     if (param < 8 || param > 256) return false;
     rows = param;
   }
   const int nstrip = (d.h + rows - 1) / rows;
   p.kid = kSingleChannel;
-  p.name = d.separable ? "is_k1_single_separable" : "is_k1_single";
+  p.name = d.separable ? "is_k1_single_separable" : (d.k > 1 ? "is_k1_single_fanout" : "is_k1_single");
   p.nseg = nseg;
   p.nstrip = nstrip;
   p.strip_rows = rows;

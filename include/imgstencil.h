@@ -139,7 +139,8 @@ is_status conv2d_get_plan_info(conv2d_plan plan, conv2d_plan_info *info);
  * the host without a GPU.
  *  kernel     : kernel family, as in conv2d_plan_info
  *  param      : the family's tuning parameter: output rows per strip
- *               (is_k1_single, is_k1_single_separable), output channels per
+ *               (is_k1_single, is_k1_single_separable, is_k1_single_fanout: one
+ *               channel, 2, 4 or 8 filters), output channels per
  *               workgroup (is_k2_multi), LDS swizzle row bytes, 0 = none
  *               (is_k4_mfma); 0 for the others
  *  is_default : 1 for the variant conv2d_create chooses (always index 0)

@@ -37,6 +37,14 @@ def _case(name):
         x, w, b = synth.cnn_layer_f32(N=2, C=1, K=8, H=40, W=136, R=5, seed=5)
         d = isa.make_desc(2, 1, 40, 136, 8, 5, 5, "f32", False)
         return d, x, w, b, False, "NCHW", w, oracle.conv2d(x, w, b, False)
+    if name.startswith("fanout_"):
+        # one channel, F filters: every strip height of the single-channel
+        # kernel's F-filter form next to the multi-channel kernel's groups
+        N, H, W, K, R, relu = {"fanout_2x5x5": (2, 70, 300, 2, 5, True), "fanout_4x3x3_odd": (1, 45, 301, 4, 3, False),
+                               "fanout_8x3x3": (1, 67, 520, 8, 3, True), "fanout_4x1x1": (2, 33, 260, 4, 1, False)}[name]
+        x, w, b = synth.cnn_layer_f32(N=N, C=1, K=K, H=H, W=W, R=R, seed=K + R + H)
+        d = isa.make_desc(N, 1, H, W, K, R, R, "f32", relu)
+        return d, x, w, b, relu, "NCHW", w, oracle.conv2d(x, w, b, relu)
     if name == "pointwise_8to16":
         x, w, b = synth.cnn_layer_f32(N=2, C=8, K=16, H=33, W=132, R=1, seed=7)
         d = isa.make_desc(2, 8, 33, 132, 16, 1, 1, "f32", True)
@@ -60,7 +68,8 @@ def _run(plan, x, wk, b, d):
     return host(y), (xd, wd, bd, y)
 
 
-CASES = ["single_3x3", "separable_5x5", "fp32_32to32", "one_channel_8_filters", "pointwise_8to16", "fp16_64to64"]
+CASES = ["single_3x3", "separable_5x5", "fp32_32to32", "one_channel_8_filters", "pointwise_8to16", "fp16_64to64",
+         "fanout_2x5x5", "fanout_4x3x3_odd", "fanout_8x3x3", "fanout_4x1x1"]
 
 
 @pytest.mark.parametrize("name", CASES)
@@ -69,6 +78,8 @@ def test_every_variant_matches_oracle(name):
     tau = TAU_F16 if layout == "NHWC" else TAU_F32
     variants = isa.conv2d_list_variants(d)
     assert len(variants) >= 2, variants
+    if name.startswith("fanout_"):
+        assert sum(v["kernel"] == "is_k1_single_fanout" for v in variants) == 4, variants
     for i, v in enumerate(variants):
         say("variant", name, i, v["kernel"], v["param"])
         plan = isa.Plan(d, variant=i)
@@ -119,3 +130,22 @@ def test_autotune_on_the_8192_image():
     ref, m = oracle.conv2d_points(x, w, None, False, pts)
     got = host(y)[pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]]
     check(got, ref, m, TAU_F32, "8192^2 after autotune")
+
+
+def test_fanout_default_on_a_4096_image():
+    """One channel, 2 filters 3x3 with bias and ReLU on 4096x4096: the default
+    plan is the single-channel kernel's F-filter form; both output planes are
+    checked on whole rows at strip boundaries and at the image edges."""
+    import torch
+    x, w, b = synth.cnn_layer_f32(N=1, C=1, K=2, H=4096, W=4096, R=3, seed=11)
+    d = isa.make_desc(1, 1, 4096, 4096, 2, 3, 3, "f32", True)
+    plan = isa.Plan(d)
+    assert plan.info()["kernel"] == "is_k1_single_fanout"
+    y = torch.full((1, 2, 4096, 4096), float("nan"), device="cuda")
+    say("fanout 4096^2 default")
+    plan.forward(dev(x), dev(w), dev(b), y)
+    rows = [0, 1, 31, 32, 33, 2047, 2048, 4094, 4095]
+    pts = np.array([(0, k, i, j) for k in range(2) for i in rows for j in range(4096)], np.int64)
+    ref, m = oracle.conv2d_points(x, w, b, True, pts)
+    got = host(y)[pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]]
+    check(got, ref, m, TAU_F32, "fanout 4096^2")

@@ -238,8 +238,24 @@ def test_separable_and_special_case_plans():
     weird.separable = 2
     with pytest.raises(isa.ImgStencilError):
         isa.Plan(weird)
+    # One channel with F filters: on small images (too few waves for the
+    # single-channel sweep), with 8 filters, or with F outside {2, 4, 8}, the
+    # multi-channel kernel; with 2 or 4 filters on a large image the
+    # single-channel kernel's F-filter form, 32-row strips. Either way the
+    # other family is among the tuning variants when it takes the shape.
     for (c, k, r) in ((1, 4, 3), (1, 8, 5), (1, 2, 1), (1, 6, 3)):
         assert isa.Plan(isa.make_desc(1, c, 64, 128, k, r, r)).info()["kernel"] == "is_k2_multi", (c, k, r)
+    for (k, r) in ((8, 3), (8, 1), (6, 3), (4, 5)):
+        assert isa.Plan(isa.make_desc(1, 1, 4096, 4096, k, r, r)).info()["kernel"] == "is_k2_multi", (k, r)
+    for (k, r) in ((2, 1), (2, 3), (2, 5), (4, 1), (4, 3)):
+        info = isa.Plan(isa.make_desc(1, 1, 4096, 4096, k, r, r)).info()
+        assert (info["kernel"], info["tile"], info["grid"]) == ("is_k1_single_fanout", (256, 32), (2048, 1, 1)), (k, r)
+    vs = [(v["kernel"], v["param"]) for v in isa.conv2d_list_variants(isa.make_desc(1, 1, 4096, 4096, 8, 3, 3))]
+    assert vs[0] == ("is_k2_multi", 8) and ("is_k1_single_fanout", 64) in vs
+    vs = [(v["kernel"], v["param"]) for v in isa.conv2d_list_variants(isa.make_desc(1, 1, 4096, 4096, 2, 3, 3))]
+    assert vs[0] == ("is_k1_single_fanout", 32) and ("is_k2_multi", 2) in vs
+    assert "is_k1_single_fanout" not in [v["kernel"] for v in
+                                         isa.conv2d_list_variants(isa.make_desc(1, 1, 4096, 4096, 4, 5, 5))]
     # 1x1 layers over several channels: the pointwise kernel when the planes
     # are whole 16-byte vectors (with the register-blocked kernel among the
     # tuning variants), else the multi-channel or fallback kernel
@@ -282,12 +298,18 @@ def test_tile_variants():
     assert {k for (k, _, _) in sep} == {"is_k1_single_separable"} and len(sep) == 5
     d = isa.make_desc(1, 1, 4096, 4096, 8, 3, 3)
     vs = isa.conv2d_list_variants(d)
-    assert [(v["kernel"], v["param"]) for v in vs] == [("is_k2_multi", 8), ("is_k2_multi", 4), ("is_k2_multi", 2)]
+    assert [(v["kernel"], v["param"]) for v in vs] == [("is_k2_multi", 8), ("is_k1_single_fanout", 16),
+                                                       ("is_k1_single_fanout", 32), ("is_k1_single_fanout", 64),
+                                                       ("is_k1_single_fanout", 128), ("is_k2_multi", 4),
+                                                       ("is_k2_multi", 2)]
     for i, v in enumerate(vs):
         p = isa.Plan(d, variant=i)
         info = p.info()
         assert info["kernel"] == v["kernel"]
-        assert info["grid"][0] == 64 * 256 * (8 // v["param"])   # 64x16 tiles x channel groups
+        if v["kernel"] == "is_k2_multi":
+            assert info["grid"][0] == 64 * 256 * (8 // v["param"])   # 64x16 tiles x channel groups
+        else:
+            assert info["grid"][0] == 16 * (4096 // v["param"])      # 256-column segments x strips
     with pytest.raises(isa.ImgStencilError):
         isa.Plan(d, variant=len(vs))
     with pytest.raises(isa.ImgStencilError):
