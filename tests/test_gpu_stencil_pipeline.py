@@ -106,12 +106,15 @@ def test_auto_without_workspace_runs_one_fused_group():
     check(host(y), ref, m, TAU_F32, "auto without workspace")
 
 
-def test_pipeline_8192_sampled():
-    """Two 3x3 filters on 8192^2 (the fused group the bench times): rows around
-    strip edges and random rows, every column."""
-    x, layers = _pipeline(1, 8192, 8192, [(3, True, True), (3, False, True)], seed=5)
-    say("pipeline 8192^2")
-    y = _run(x, layers, isa.IS_CHAIN_AUTO, [2])
+@pytest.mark.parametrize("spec,groups", [([(3, True, True), (3, False, True)], [2]),
+                                         ([(3, True, False)] * 3, [3])])
+def test_pipeline_8192_sampled(spec, groups):
+    """Two and three 3x3 filters on 8192^2 (the three with ReLU and no bias are
+    the group the bench times, one fused launch): rows around strip edges and
+    random rows, every column."""
+    x, layers = _pipeline(1, 8192, 8192, spec, seed=5)
+    say("pipeline 8192^2", len(spec))
+    y = _run(x, layers, isa.IS_CHAIN_AUTO, groups)
     rows = sorted({0, 1, 2, 62, 63, 64, 65, 4095, 4096, 8189, 8190, 8191} |
                   set(int(r) for r in np.random.default_rng(6).integers(0, 8192, 8)))
     for i in rows:
