@@ -338,14 +338,16 @@ bool configure_single(Plan &p, int param) {
   if (d.k > 1) {
     // F filters: 64-row strips (1024 waves on a 4096x4096 image; 32 rows
     // measured 1-5% slower, 16 and 128 rows 5-30% slower). Measured against
-    // the multi-channel kernel, which stages the tile in LDS and spreads the F
-    // planes' stores over the waves of a workgroup: this one is 7-31% faster
-    // with 2 or 4 filters on large images, 10% slower with 8 (eight stores per
-    // row step, and the 72 taps no longer fit the scalar registers), and
-    // slower on small images, which give it too few waves. Those shapes stay
-    // with the multi-channel kernel unless a tuning variant asks for this one.
+    // the multi-channel kernel (LDS-staged tile, the F planes' stores spread
+    // over a workgroup's waves, streaming stores) on 4096x4096: this one is
+    // faster only with two 5x5 filters (40 against 52 us); it ties with two
+    // 3x3 filters and is 14-42% slower with two 1x1 or four filters, and
+    // slower with eight and on small images, which give it too few waves.
+    // So the plan takes it for two 5x5 filters on large images; every other
+    // one-channel shape it can run lists it among the tuning variants.
     rows = 64;
-    if (param == 0 && (d.k > 4 || (long long)nseg * ((d.h + rows - 1) / rows) * d.n < 1024)) return false;
+    if (param == 0 && (d.k != 2 || d.r != 5 || (long long)nseg * ((d.h + rows - 1) / rows) * d.n < 1024))
+      return false;
   }
   if (param != 0) {   // a tuning variant: 8 to 256 rows
     if (param < 8 || param > 256) return false;

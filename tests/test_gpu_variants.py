@@ -133,12 +133,12 @@ def test_autotune_on_the_8192_image():
 
 
 def test_fanout_default_on_a_4096_image():
-    """One channel, 2 filters 3x3 with bias and ReLU on 4096x4096: the default
+    """One channel, 2 filters 5x5 with bias and ReLU on 4096x4096: the default
     plan is the single-channel kernel's F-filter form; both output planes are
     checked on whole rows at strip boundaries and at the image edges."""
     import torch
-    x, w, b = synth.cnn_layer_f32(N=1, C=1, K=2, H=4096, W=4096, R=3, seed=11)
-    d = isa.make_desc(1, 1, 4096, 4096, 2, 3, 3, "f32", True)
+    x, w, b = synth.cnn_layer_f32(N=1, C=1, K=2, H=4096, W=4096, R=5, seed=11)
+    d = isa.make_desc(1, 1, 4096, 4096, 2, 5, 5, "f32", True)
     plan = isa.Plan(d)
     assert plan.info()["kernel"] == "is_k1_single_fanout"
     y = torch.full((1, 2, 4096, 4096), float("nan"), device="cuda")

@@ -238,21 +238,19 @@ def test_separable_and_special_case_plans():
     weird.separable = 2
     with pytest.raises(isa.ImgStencilError):
         isa.Plan(weird)
-    # One channel with F filters: on small images (too few waves for the
-    # single-channel sweep), with 8 filters, or with F outside {2, 4, 8}, the
-    # multi-channel kernel; with 2 or 4 filters on a large image the
-    # single-channel kernel's F-filter form, 64-row strips. Either way the
-    # other family is among the tuning variants when it takes the shape.
-    for (c, k, r) in ((1, 4, 3), (1, 8, 5), (1, 2, 1), (1, 6, 3)):
+    # One channel with F filters: the multi-channel kernel, except two 5x5
+    # filters on a large image, which take the single-channel kernel's
+    # F-filter form with 64-row strips. Either way the other family is among
+    # the tuning variants when it takes the shape.
+    for (c, k, r) in ((1, 4, 3), (1, 8, 5), (1, 2, 1), (1, 6, 3), (1, 2, 5)):
         assert isa.Plan(isa.make_desc(1, c, 64, 128, k, r, r)).info()["kernel"] == "is_k2_multi", (c, k, r)
-    for (k, r) in ((8, 3), (8, 1), (6, 3), (4, 5)):
+    for (k, r) in ((8, 3), (8, 1), (6, 3), (4, 5), (2, 1), (2, 3), (4, 1), (4, 3)):
         assert isa.Plan(isa.make_desc(1, 1, 4096, 4096, k, r, r)).info()["kernel"] == "is_k2_multi", (k, r)
-    for (k, r) in ((2, 1), (2, 3), (2, 5), (4, 1), (4, 3)):
-        info = isa.Plan(isa.make_desc(1, 1, 4096, 4096, k, r, r)).info()
-        assert (info["kernel"], info["tile"], info["grid"]) == ("is_k1_single_fanout", (256, 64), (1024, 1, 1)), (k, r)
+    info = isa.Plan(isa.make_desc(1, 1, 4096, 4096, 2, 5, 5)).info()
+    assert (info["kernel"], info["tile"], info["grid"]) == ("is_k1_single_fanout", (256, 64), (1024, 1, 1))
     vs = [(v["kernel"], v["param"]) for v in isa.conv2d_list_variants(isa.make_desc(1, 1, 4096, 4096, 8, 3, 3))]
     assert vs[0] == ("is_k2_multi", 8) and ("is_k1_single_fanout", 64) in vs
-    vs = [(v["kernel"], v["param"]) for v in isa.conv2d_list_variants(isa.make_desc(1, 1, 4096, 4096, 2, 3, 3))]
+    vs = [(v["kernel"], v["param"]) for v in isa.conv2d_list_variants(isa.make_desc(1, 1, 4096, 4096, 2, 5, 5))]
     assert vs[0] == ("is_k1_single_fanout", 64) and ("is_k2_multi", 2) in vs
     assert "is_k1_single_fanout" not in [v["kernel"] for v in
                                          isa.conv2d_list_variants(isa.make_desc(1, 1, 4096, 4096, 4, 5, 5))]
