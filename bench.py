@@ -234,17 +234,18 @@ LDS_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ
 
 def lds_study(torch, isa, synth, stream, stream_obj, steps, warmup):
     """The LDS-staged kernels for a counter run of their bank conflicts: the fp16
-    layer under each swizzle of its input tile (IMGSTENCIL_K4_SWIZZLE, read at
-    plan creation; the kernel is instantiated per swizzle, so the profiler sees
+    layer under each swizzle of its input tile (tuning variants of its plan; the
+    kernel is instantiated per swizzle, so the profiler sees
     is_k4_mfma<0, 64, 64, 0, 0>, <128, 64, 64, 0, 0> and <256, 64, 64, 0, 0>), the fp32 layer and the fused chain."""
     out = []
     x, w, b = synth.cnn_layer_f16_nhwc()
     xd, wd, bd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
     yd = torch.empty((8, 256, 256, 64), dtype=torch.float16, device="cuda")
+    desc = isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16", False)
+    variants = isa.conv2d_list_variants(desc)
     for swz in (0, 128, 256):
-        os.environ["IMGSTENCIL_K4_SWIZZLE"] = str(swz)
-        plan = isa.Plan(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16", False))
-        del os.environ["IMGSTENCIL_K4_SWIZZLE"]
+        idx = [i for i, v in enumerate(variants) if v["kernel"] == "is_k4_mfma" and v["param"] == swz]
+        plan = isa.Plan(desc, variant=idx[0])
         c = Case("fp16 layer, swizzle %d" % swz,
                  lambda plan=plan: isa.conv2d_forward(plan.handle, xd.data_ptr(), wd.data_ptr(), bd.data_ptr(),
                                                       yd.data_ptr(), stream),

@@ -3,7 +3,8 @@
 The functions with the C names (conv2d_create, conv2d_forward, conv2d_destroy,
 conv2d_get_plan_info, conv2d_list_variants, conv2d_create_variant,
 conv2d_autotune, conv_chain_workspace_size, conv_chain_forward,
-conv_chain_kernel_name, conv_chain_groups, is_lds_tile_bytes, is_swizzle_col) marshal arguments to
+conv_chain_kernel_name, conv_chain_groups, is_lds_tile_bytes, is_swizzle_col,
+is_persistent_grid) marshal arguments to
 the C ABI of include/imgstencil.h and nothing else. conv2d() and conv_chain()
 are conveniences on torch tensors: torch only allocates device memory and
 supplies the current HIP stream.
@@ -17,7 +18,7 @@ from ._abi import (IS_F16, IS_F32, IS_NCHW, IS_NHWC, IS_CHAIN_AUTO, IS_CHAIN_FUS
 __all__ = ["conv2d_create", "conv2d_forward", "conv2d_destroy", "conv2d_get_plan_info",
            "conv2d_list_variants", "conv2d_create_variant", "conv2d_autotune",
            "conv_chain_workspace_size", "conv_chain_forward", "conv_chain_kernel_name", "conv_chain_groups",
-           "is_lds_tile_bytes", "is_swizzle_col", "is_version", "make_desc", "make_chain_desc",
+           "is_lds_tile_bytes", "is_swizzle_col", "is_persistent_grid", "is_version", "make_desc", "make_chain_desc",
            "conv2d", "conv2d_separable", "conv_chain", "Plan", "ImgStencilError"]
 
 
@@ -155,6 +156,10 @@ def is_swizzle_col(y, x, nx, elem_bytes, chunk_bytes):
     return load().is_swizzle_col(y, x, nx, elem_bytes, chunk_bytes)
 
 
+def is_persistent_grid(units, cus):
+    return load().is_persistent_grid(units, cus)
+
+
 def is_version():
     return load().is_version()
 
@@ -209,23 +214,57 @@ def _check_dev(t, dtype, name):
         raise ValueError("%s must be contiguous" % name)
 
 
+# The shape and dtype checks come before the device checks, so that every
+# rejected argument is reported the same way with or without a GPU.
+def _check_float_input(x):
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dtype not in (torch.float32, torch.float16):
+        raise TypeError("x must be a float32 (NCHW) or float16 (NHWC) tensor")
+    if x.dim() != 4:
+        raise ValueError("x must have 4 dimensions, got shape %s" % (tuple(x.shape),))
+
+
+def _check_weights(w, dtype, cin, name):
+    import torch
+    if not isinstance(w, torch.Tensor) or w.dtype != dtype:
+        raise TypeError("%s must be a %s tensor" % (name, dtype))
+    if w.dim() != 4:
+        raise ValueError("%s must be K,C,R,S, got shape %s" % (name, tuple(w.shape)))
+    if w.shape[1] != cin:
+        raise ValueError("%s expects %d input channels, the layer receives %d" % (name, w.shape[1], cin))
+
+
+def _check_bias(b, K, name="b"):
+    """b: None or K fp32 values."""
+    import torch
+    if b is None:
+        return
+    if not isinstance(b, torch.Tensor) or b.dtype != torch.float32:
+        raise TypeError("%s must be a float32 tensor" % name)
+    if b.numel() != K:
+        raise ValueError("%s must hold one value per output channel (%d), got %d" % (name, K, b.numel()))
+
+
 def conv2d(x, w, b=None, relu=False):
     """y = act(conv(x, w) + b). fp32: x is N,C,H,W. fp16: x is N,H,W,C. w is K,C,R,S."""
     import torch
+    _check_float_input(x)
     f16 = x.dtype == torch.float16
+    if f16:
+        N, H, W, C = x.shape
+    else:
+        N, C, H, W = x.shape
+    _check_weights(w, x.dtype, C, "w")
+    K, _, R, S = w.shape
+    _check_bias(b, K)
     _check_dev(x, x.dtype, "x")
     _check_dev(w, x.dtype, "w")
     if b is not None:
         _check_dev(b, torch.float32, "b")
-    K, C, R, S = w.shape
     if f16:
-        N, H, W, Cx = x.shape
         y = torch.empty((N, H, W, K), dtype=x.dtype, device=x.device)
     else:
-        N, Cx, H, W = x.shape
         y = torch.empty((N, K, H, W), dtype=x.dtype, device=x.device)
-    if Cx != C:
-        raise ValueError("channel mismatch")
     p = Plan(make_desc(N, C, H, W, K, R, S, "f16" if f16 else "f32", relu))
     return p.forward(x, w, b, y)
 
@@ -234,6 +273,10 @@ def conv2d_separable(x, col, row, b=None, relu=False):
     """Single-channel fp32 filtering with the separable filter w[i][j] =
     col[i] * row[j]: x N,1,H,W; col R taps, row S taps (device tensors)."""
     import torch
+    _check_float_input(x)
+    if x.dtype != torch.float32 or x.shape[1] != 1:
+        raise ValueError("separable filtering takes one fp32 channel, x is %s %s" % (x.dtype, tuple(x.shape)))
+    _check_bias(b, 1)
     _check_dev(x, torch.float32, "x")
     _check_dev(col, torch.float32, "col")
     _check_dev(row, torch.float32, "row")
@@ -251,18 +294,26 @@ def conv_chain(x, layers, depth_to_space=1, mode=IS_CHAIN_AUTO):
     """layers: list of (w, b, relu) device tensors. x fp32 NCHW with fp32 weights,
     or x fp16 NHWC with fp16 weights (fp32 biases). Returns the chain output."""
     import torch
+    _check_float_input(x)
     f16 = x.dtype == torch.float16
-    _check_dev(x, torch.float16 if f16 else torch.float32, "x")
     if f16:
         N, H, W, C = x.shape
     else:
         N, C, H, W = x.shape
+    if not 1 <= len(layers) <= _abi.IS_MAX_CHAIN:
+        raise ValueError("1 to %d layers" % _abi.IS_MAX_CHAIN)
     spec = []
-    for (w, b, relu) in layers:
-        _check_dev(w, torch.float16 if f16 else torch.float32, "w")
-        if b is not None:
-            _check_dev(b, torch.float32, "b")
+    for i, (w, b, relu) in enumerate(layers):
+        _check_weights(w, x.dtype, C if i == 0 else spec[-1][1], "w[%d]" % i)
+        if w.shape[2] != w.shape[3]:
+            raise ValueError("w[%d]: chain layers take square filters, got %dx%d" % (i, w.shape[2], w.shape[3]))
+        _check_bias(b, w.shape[0], "b[%d]" % i)
         spec.append((w.shape[1], w.shape[0], w.shape[2], relu))
+    _check_dev(x, x.dtype, "x")
+    for i, (w, b, _) in enumerate(layers):
+        _check_dev(w, x.dtype, "w[%d]" % i)
+        if b is not None:
+            _check_dev(b, torch.float32, "b[%d]" % i)
     d = make_chain_desc(N, H, W, spec, depth_to_space, mode, "f16" if f16 else "f32")
     f = depth_to_space
     if f16:

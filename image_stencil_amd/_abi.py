@@ -69,6 +69,7 @@ SIGNATURES = [
                                          ctypes.POINTER(ctypes.c_int)]),
     ("is_lds_tile_bytes", ctypes.c_size_t, [ctypes.c_int] * 6),
     ("is_swizzle_col", ctypes.c_int, [ctypes.c_int] * 5),
+    ("is_persistent_grid", ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     ("is_status_str", ctypes.c_char_p, [ctypes.c_int]),
     ("is_last_hip_error", ctypes.c_int, []),
     ("is_version", ctypes.c_int, []),

@@ -30,6 +30,9 @@ bool log_enabled() {
   return on;
 }
 
+constexpr int kMaxDevices = 64;
+int g_device_cus[kMaxDevices];   // 0 = not read yet
+
 size_t elem_size(is_dtype t) { return t == IS_F16 ? 2 : 4; }
 
 is_status validate(const conv2d_desc *d) {
@@ -418,77 +421,31 @@ bool runs_fused(const conv_chain_desc *d, const conv2d_desc *ld, const void *wor
 
 }  // namespace
 
-extern "C" {
+namespace is {
 
-is_status conv_chain_workspace_size(const conv_chain_desc *d, size_t *bytes) {
-  if (!bytes) return IS_ERR_INVALID_ARG;
-  conv2d_desc ld[IS_MAX_CHAIN];
-  const is_status st = chain_layers(d, ld);
-  if (st != IS_OK) return st;
-  return chain_workspace(d, ld, bytes);
+int persistent_grid(int units, int cus) {
+  const int g = cus < 8 ? 8 : cus / 8 * 8;
+  const long long need = ((long long)(units < 1 ? 1 : units) + 7) / 8 * 8;   // every group busy
+  return need < g ? (int)need : g;
 }
 
-is_status conv_chain_kernel_name(const conv_chain_desc *d, char *name, size_t len) {
-  if (!name || len == 0) return IS_ERR_INVALID_ARG;
-  conv2d_desc ld[IS_MAX_CHAIN];
-  const is_status st = chain_layers(d, ld);
-  if (st != IS_OK) return st;
-  size_t ws = 0;
-  const is_status st2 = chain_workspace(d, ld, &ws);
-  if (st2 != IS_OK) return st2;
-  // the path taken when the caller passes the workspace reported above
-  if (stencil_chain(d)) {
-    int size[IS_MAX_CHAIN];
-    const int groups = stencil_groups(d, size);
-    bool all_single = true;
-    for (int g = 0; g < groups; ++g) all_single = all_single && size[g] == 1;
-    if (all_single) {
-      snprintf(name, len, "%s", "layer_by_layer");
-    } else if (groups == 1) {
-      snprintf(name, len, "%s", "is_k7_fused_stencil");
-    } else {
-      char buf[64] = "fused_groups:";
-      for (int g = 0; g < groups; ++g) {
-        char part[8];
-        snprintf(part, sizeof(part), g ? "+%d" : "%d", size[g]);
-        strncat(buf, part, sizeof(buf) - strlen(buf) - 1);
-      }
-      snprintf(name, len, "%s", buf);
-    }
-    return IS_OK;
-  }
-  const bool fused = d->mode == IS_CHAIN_FUSED;
-  snprintf(name, len, "%s", fused ? "is_k3_chain" : "layer_by_layer");
-  return IS_OK;
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = __atomic_load_n(&g_device_cus[dev], __ATOMIC_RELAXED);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  __atomic_store_n(&g_device_cus[dev], cus, __ATOMIC_RELAXED);
+  return cus;
 }
 
-is_status conv_chain_groups(const conv_chain_desc *d, int *sizes, int max, int *count) {
-  if (!count || max < 0 || (max > 0 && !sizes)) return IS_ERR_INVALID_ARG;
-  conv2d_desc ld[IS_MAX_CHAIN];
-  const is_status st = chain_layers(d, ld);
-  if (st != IS_OK) return st;
-  size_t ws = 0;
-  const is_status st2 = chain_workspace(d, ld, &ws);
-  if (st2 != IS_OK) return st2;
-  int size[IS_MAX_CHAIN];
-  int groups;
-  if (stencil_chain(d)) {
-    groups = stencil_groups(d, size);
-  } else if (d->mode == IS_CHAIN_FUSED) {
-    groups = 1;
-    size[0] = d->n_layers;
-  } else {
-    groups = d->n_layers;
-    for (int l = 0; l < groups; ++l) size[l] = 1;
-  }
-  *count = groups;
-  for (int g = 0; g < groups && g < max; ++g) sizes[g] = size[g];
-  return IS_OK;
-}
+is_status report_hip(hipError_t e) { return hip_status(e); }
 
-is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void *const *w,
-                             const float *const *b, void *y, void *workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
+is_status chain_forward(const conv_chain_desc *d, const void *x, const void *const *w,
+                        const float *const *b, void *y, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   try {
     conv2d_desc ld[IS_MAX_CHAIN];
     is_status st = chain_layers(d, ld);
@@ -594,6 +551,87 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void
   }
 }
 
+
+}  // namespace is
+
+extern "C" {
+
+int is_persistent_grid(int units, int cus) {
+  if (units < 1 || cus < 1) return 0;
+  return is::persistent_grid(units, cus);
+}
+
+is_status conv_chain_workspace_size(const conv_chain_desc *d, size_t *bytes) {
+  if (!bytes) return IS_ERR_INVALID_ARG;
+  conv2d_desc ld[IS_MAX_CHAIN];
+  const is_status st = chain_layers(d, ld);
+  if (st != IS_OK) return st;
+  return chain_workspace(d, ld, bytes);
+}
+
+is_status conv_chain_kernel_name(const conv_chain_desc *d, char *name, size_t len) {
+  if (!name || len == 0) return IS_ERR_INVALID_ARG;
+  conv2d_desc ld[IS_MAX_CHAIN];
+  const is_status st = chain_layers(d, ld);
+  if (st != IS_OK) return st;
+  size_t ws = 0;
+  const is_status st2 = chain_workspace(d, ld, &ws);
+  if (st2 != IS_OK) return st2;
+  // the path taken when the caller passes the workspace reported above
+  if (stencil_chain(d)) {
+    int size[IS_MAX_CHAIN];
+    const int groups = stencil_groups(d, size);
+    bool all_single = true;
+    for (int g = 0; g < groups; ++g) all_single = all_single && size[g] == 1;
+    if (all_single) {
+      snprintf(name, len, "%s", "layer_by_layer");
+    } else if (groups == 1) {
+      snprintf(name, len, "%s", "is_k7_fused_stencil");
+    } else {
+      char buf[64] = "fused_groups:";
+      for (int g = 0; g < groups; ++g) {
+        char part[8];
+        snprintf(part, sizeof(part), g ? "+%d" : "%d", size[g]);
+        strncat(buf, part, sizeof(buf) - strlen(buf) - 1);
+      }
+      snprintf(name, len, "%s", buf);
+    }
+    return IS_OK;
+  }
+  const bool fused = d->mode == IS_CHAIN_FUSED;
+  snprintf(name, len, "%s", fused ? "is_k3_chain" : "layer_by_layer");
+  return IS_OK;
+}
+
+is_status conv_chain_groups(const conv_chain_desc *d, int *sizes, int max, int *count) {
+  if (!count || max < 0 || (max > 0 && !sizes)) return IS_ERR_INVALID_ARG;
+  conv2d_desc ld[IS_MAX_CHAIN];
+  const is_status st = chain_layers(d, ld);
+  if (st != IS_OK) return st;
+  size_t ws = 0;
+  const is_status st2 = chain_workspace(d, ld, &ws);
+  if (st2 != IS_OK) return st2;
+  int size[IS_MAX_CHAIN];
+  int groups;
+  if (stencil_chain(d)) {
+    groups = stencil_groups(d, size);
+  } else if (d->mode == IS_CHAIN_FUSED) {
+    groups = 1;
+    size[0] = d->n_layers;
+  } else {
+    groups = d->n_layers;
+    for (int l = 0; l < groups; ++l) size[l] = 1;
+  }
+  *count = groups;
+  for (int g = 0; g < groups && g < max; ++g) sizes[g] = size[g];
+  return IS_OK;
+}
+
+is_status conv_chain_forward(const conv_chain_desc *d, const void *x, const void *const *w,
+                             const float *const *b, void *y, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  return is::chain_forward(d, x, w, b, y, workspace, workspace_bytes, stream);
+}
 
 is_status conv2d_create(const conv2d_desc *d, conv2d_plan *out) {
   if (!out) return IS_ERR_INVALID_ARG;

@@ -31,6 +31,24 @@ struct Plan {
   int kvalid;                 // fp16 MFMA layer: output channels with weights (the rest are 0)
 };
 
+// Workgroups of a persistent kernel that walks `units` work units with one
+// workgroup per CU: the CU count rounded down to a multiple of 8 (the kernels
+// deal their units to 8 groups of workgroups, one group per XCD on a whole
+// MI355X, so the grid must stay a multiple of 8), or fewer when the units
+// need fewer: units rounded up to a multiple of 8; at least 8. Plans record it
+// for 256 CUs; the launchers recompute it for the current device.
+int persistent_grid(int units, int cus);
+// Compute units of the current device, cached per device (256 when the runtime
+// cannot tell).
+int device_cu_count();
+
+// conv_chain_forward with the caller's workspace (the whole entry point: checks
+// and launches); shared by the entry points that bring their own workspace.
+is_status chain_forward(const conv_chain_desc *d, const void *x, const void *const *w, const float *const *b,
+                        void *y, void *workspace, size_t workspace_bytes, hipStream_t stream);
+// IS_OK for hipSuccess, else IS_ERR_HIP with the error kept for is_last_hip_error.
+is_status report_hip(hipError_t e);
+
 // Each kernel family fills the launch geometry of a plan it accepts and
 // launches it. configure_* return false when the family cannot run the desc.
 // `param` selects one of the family's tile variants (0: the default choice):

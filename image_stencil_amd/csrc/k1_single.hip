@@ -325,6 +325,9 @@ bool configure_single(Plan &p, int param) {
   const conv2d_desc &d = p.d;
   if (d.c != 1 || d.layout != IS_NCHW || d.in_dtype != IS_F32) return false;
   if (d.r > 7 || d.s > 7) return false;
+  // Byte offsets inside a row are 32-bit: the row range 4 W and the halo
+  // offset 4 (x0 + 256) of the last segment must stay below 2^31.
+  if (4.0 * ((double)d.w + kSegCols) >= 2147483648.0) return false;
   if (pick_any<true, false>(d) == nullptr) return false;
   const int nseg = (d.w + kSegCols - 1) / kSegCols;
   // Strip height: a wave keeps about one prefetch window of rows in flight, so

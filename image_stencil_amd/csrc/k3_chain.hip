@@ -400,9 +400,10 @@ hipError_t launch_chain_fused(const conv_chain_desc *d, const float *x, const fl
   for (int l = 0; l < 4; ++l) a.relu_mask |= (d->layer[l].relu ? 1 : 0) << l;
   a.nstrip = (d->w + kKeep - 1) / kKeep;
   // About one workgroup per CU: split each strip into blocks of rows so that
-  // strips x blocks x images fills the 256 CUs once.
+  // strips x blocks x images fills the device's CUs once.
+  const int cus = device_cu_count();
   const int per_img = a.nstrip * d->n;
-  int nb = per_img >= 256 ? 1 : 256 / per_img;
+  int nb = per_img >= cus ? 1 : cus / per_img;
   if (nb < 1) nb = 1;
   int rows = (d->h + nb - 1) / nb;
   rows = (rows + kRows - 1) / kRows * kRows;

@@ -46,7 +46,6 @@
 #include "common.hpp"
 #include "internal.hpp"
 
-#include <stdlib.h>
 
 namespace is {
 namespace {
@@ -583,23 +582,14 @@ bool configure_mfma(Plan &p, int param) {
   p.name = "is_k4_mfma";
   p.ntiles = (int)units;
   p.kvalid = d.k;
-  // Persistent: one workgroup per CU (its LDS and registers fill the CU),
-  // 8 XCDs x 32 CUs; fewer when there are fewer units (kept a multiple of 8).
-  int g = 256;
-  while (g > 8 && g / 2 >= p.ntiles) g /= 2;
-  p.grid_x = g;
+  // Persistent: one workgroup per CU (its LDS and registers fill the CU);
+  // fewer when there are fewer units.
+  p.grid_x = persistent_grid(p.ntiles, 256);
   p.grid_y = p.grid_z = 1;
   p.block = kThreads;
   // Swizzle row bytes: 128 gives the fewest SQ_LDS_BANK_CONFLICT cycles of 0,
-  // 128 and 256 on the 64 -> 64 layer. IMGSTENCIL_K4_SWIZZLE=0|128|256
-  // overrides it for that layer (read when the plan is created) so that the
-  // three layouts can be measured.
+  // 128 and 256 on the 64 -> 64 layer; the other two are tuning variants.
   p.vec = 128;
-  if (d.c == 64 && d.k == 64)
-    if (const char *e = getenv("IMGSTENCIL_K4_SWIZZLE")) {
-      const int v = atoi(e);
-      if (v == 0 || v == 128 || v == 256) p.vec = v;
-    }
   if (param != 0) {   // a tuning variant: swizzle row bytes (-1 = none); 64 -> 64 only has all three
     const int v = param < 0 ? 0 : param;
     if (v != 128 && !(d.c == 64 && d.k == 64 && (v == 0 || v == 256))) return false;
@@ -611,9 +601,7 @@ bool configure_mfma(Plan &p, int param) {
     else fill_geometry<64, 32>(p);
     const long long u64 = (long long)p.nseg * p.nstrip * d.n;
     p.ntiles = (int)u64;
-    int g2 = 256;
-    while (g2 > 8 && g2 / 2 >= p.ntiles) g2 /= 2;
-    p.grid_x = g2;
+    p.grid_x = persistent_grid(p.ntiles, 256);
   }
   return true;
 }
@@ -640,7 +628,8 @@ hipError_t launch_mfma_d2s3(const Plan &p, const _Float16 *x, const _Float16 *w,
   a.units_x = p.nseg;
   a.units_y = p.nstrip;
   a.nunits = p.ntiles;
-  return launch_kernel(is_k4_mfma<128, 32, 16, 3>, dim3(p.grid_x), dim3(p.block), 0, s, a);
+  return launch_kernel(is_k4_mfma<128, 32, 16, 3>, dim3(persistent_grid(p.ntiles, device_cu_count())),
+                       dim3(p.block), 0, s, a);
 }
 
 hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
@@ -658,7 +647,7 @@ hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, cons
   a.units_x = p.nseg;
   a.units_y = p.nstrip;
   a.nunits = p.ntiles;
-  const dim3 grid(p.grid_x), block(p.block);
+  const dim3 grid(persistent_grid(p.ntiles, device_cu_count())), block(p.block);
   if (p.d.c == 64 && p.d.k == 64) {
     if (p.tile_h == 60) return launch_kernel(is_k4_mfma<128, 64, 64, 0, 60>, grid, block, 0, s, a);
     switch (p.vec) {

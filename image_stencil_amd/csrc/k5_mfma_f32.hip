@@ -301,11 +301,9 @@ bool configure_mfma_f32(Plan &p) {
   p.nseg = (d.w + kTC - 1) / kTC;
   p.nstrip = (d.h + kTR - 1) / kTR;
   p.ntiles = (int)tiles;
-  // Persistent: one workgroup per CU (its LDS fills the CU), 8 XCDs x 32 CUs;
-  // fewer when there are fewer tiles (kept a multiple of 8).
-  int g = 256;
-  while (g > 8 && g / 2 >= p.ntiles) g /= 2;
-  p.grid_x = g;
+  // Persistent: one workgroup per CU (its LDS fills the CU); fewer when there
+  // are fewer tiles.
+  p.grid_x = persistent_grid(p.ntiles, 256);
   p.grid_y = p.grid_z = 1;
   p.block = kThreads;
   p.lds = 2 * kBufFloats * 4;
@@ -328,7 +326,8 @@ hipError_t launch_mfma_f32(const Plan &p, const float *x, const float *w, const 
   a.tiles_x = p.nseg;
   a.tiles_y = p.nstrip;
   a.ntiles = p.ntiles;
-  return launch_kernel(is_k5_mfma_f32, dim3(p.grid_x), dim3(p.block), 0, s, a);
+  return launch_kernel(is_k5_mfma_f32, dim3(persistent_grid(p.ntiles, device_cu_count())), dim3(p.block), 0,
+                       s, a);
 }
 
 }  // namespace is

@@ -38,7 +38,7 @@ constexpr int kTH = 32;                 // tile rows
 constexpr int kTW = 64;                 // tile columns (4 waves x 16)
 constexpr int kThreads = 256;
 constexpr int kWgPerCu = 1;
-constexpr int kCus = 256;
+constexpr int kCus = 256;   // CUs the plan's grid is recorded for; launches use the device's
 constexpr unsigned kOob = 0xFFFFFFF0u;
 
 struct HeadArgs {
@@ -271,7 +271,10 @@ hipError_t launch_head_f16(const Plan &p, const _Float16 *x, const _Float16 *w, 
   a.tiles_x = p.nseg;
   a.tiles_y = p.nstrip;
   a.ntiles = p.ntiles;
-  return launch_kernel(fn, dim3(p.grid_x), dim3(p.block), 0, s, a);
+  // Persistent over the tiles: kWgPerCu workgroups per CU of this device.
+  const long long cap = (long long)device_cu_count() * kWgPerCu;
+  const int grid = (int)(p.ntiles < cap ? p.ntiles : cap);
+  return launch_kernel(fn, dim3(grid), dim3(p.block), 0, s, a);
 }
 
 }  // namespace is

@@ -94,7 +94,10 @@ typedef struct conv2d_plan_s *conv2d_plan;
 /* What a plan will launch (read-only, for tests and measurement). */
 typedef struct {
   char kernel[64];        /* device kernel family name, e.g. "is_k1_single" */
-  int grid_x, grid_y, grid_z;
+  int grid_x, grid_y, grid_z;   /* persistent kernels record their grid for 256 CUs; a
+                                   launch sizes it for the device: is_k4_mfma and
+                                   is_k5_mfma_f32 is_persistent_grid(units, CUs),
+                                   is_k6_head_f16 min(tiles, CUs) */
   int block;              /* threads per workgroup */
   int lds_bytes;          /* LDS per workgroup */
   int tile_w, tile_h;     /* output pixels per wave or workgroup tile */
@@ -267,6 +270,14 @@ size_t is_lds_tile_bytes(int tile_w, int tile_h, int r, int s, int channels, int
  * at column x_swz of row y. The same function the device code uses.
  * Returns -1 for arguments outside those rules. */
 int is_swizzle_col(int y, int x, int nx, int elem_bytes, int chunk_bytes);
+
+/* Workgroups a persistent kernel launches for `units` work units (tiles or
+ * strips that the workgroups take in turn) on a device of `cus` compute units:
+ * one per CU, the CU count rounded down to a multiple of 8 (units are dealt to
+ * 8 groups of workgroups, one group per XCD of a whole MI355X, so the grid
+ * stays a multiple of 8), or units rounded up to a multiple of 8 when that is
+ * fewer; at least 8. Host only; 0 for non-positive arguments. */
+int is_persistent_grid(int units, int cus);
 
 const char *is_status_str(is_status st);
 int is_last_hip_error(void);   /* hipError_t of this thread's most recent IS_ERR_HIP */

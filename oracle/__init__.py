@@ -90,11 +90,12 @@ def _dims(x, w, layout):
     return N, C, H, W, K, R, S
 
 
-def conv2d(x, w, b=None, relu=False, layout="NCHW", lib=None):
+def conv2d(x, w, b=None, relu=False, layout="NCHW", lib=None, scale=True):
     """Full output y and error scale m, both float64, in the input's layout.
 
     x: N,C,H,W (NCHW) or N,H,W,C (NHWC); w: K,C,R,S (odd R, S); b: K or None.
     lib: another build of oracle.c opened with load_library (default: this one).
+    scale=False skips the error scale (m is returned as None); y is the same.
     """
     x, w = _f64(x), _f64(w)
     b = None if b is None else _f64(b)
@@ -103,7 +104,7 @@ def conv2d(x, w, b=None, relu=False, layout="NCHW", lib=None):
         raise ValueError("bias must have shape (K,)")
     shape = (N, K, H, W) if layout == "NCHW" else (N, H, W, K)
     y = np.empty(shape, np.float64)
-    m = np.empty(shape, np.float64)
+    m = np.empty(shape, np.float64) if scale else None
     rc = (lib or _load()).oracle_conv2d(_LAYOUT[layout], N, C, H, W, K, R, S, _ptr(x),
                                         _ptr(w), _ptr(b), int(bool(relu)), _ptr(y), _ptr(m))
     if rc != 0:
@@ -159,8 +160,8 @@ def chain(x, layers, d2s=1):
     for w, b, relu in layers:
         w = _f64(w)
         b = None if b is None else _f64(b)
-        z, _ = conv2d(z, w, b, relu)
-        m, _ = conv2d(m, np.abs(w), None if b is None else np.abs(b), False)
+        z, _ = conv2d(z, w, b, relu, scale=False)
+        m, _ = conv2d(m, np.abs(w), None if b is None else np.abs(b), False, scale=False)
     if d2s > 1:
         z = depth_to_space(z, d2s)
         m = depth_to_space(m, d2s)
@@ -238,9 +239,9 @@ def chain_f16(x, layers, d2s=1):
     for w, b, relu in layers:
         w = _f64(w)
         b = None if b is None else _f64(b)
-        z, _ = conv2d(z, w, b, relu)
+        z, _ = conv2d(z, w, b, relu, scale=False)
         z = _to_f16(z)
-        m, _ = conv2d(m, np.abs(w), None if b is None else np.abs(b), False)
+        m, _ = conv2d(m, np.abs(w), None if b is None else np.abs(b), False, scale=False)
     if d2s > 1:
         z = depth_to_space(z, d2s)
         m = depth_to_space(m, d2s)

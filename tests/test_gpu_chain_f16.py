@@ -4,9 +4,10 @@ first-layer kernel against the oracle.
 The net of the StreamHPC CNN page ("Reducing memory traffic" table): 1 -> 64
 (5x5), 64 -> 64, 64 -> 32, 32 -> 9 (3x3), ReLU after the first three layers,
 data and weights stored as fp16, the 9 output channels as a 3x3 sub-pixel
-upscale. Every layer's output is rounded to fp16 on both sides; tolerance
-L * 2e-3 * m for L layers (see tolerance.py). The 1280x720 frame is compared on
-windows the oracle evaluates exactly (chain_f16_window).
+upscale. Every layer's output is rounded to fp16 on both sides; the tolerance
+of L layers is derived in tolerance.py (about L * 1.05e-3 * m). The 1280x720
+frame is compared in full and on windows the oracle evaluates exactly
+(chain_f16_window).
 """
 import numpy as np
 import pytest
@@ -80,6 +81,17 @@ def test_pages_net_1280x720_windows():
         mref = np.transpose(oracle.depth_to_space(mt, 3), (0, 2, 3, 1))
         got = y[:, 3 * i0:3 * i1, 3 * j0:3 * j1, :]
         check(got, ref, mref, tau, "pages net window %s" % ((i0, i1, j0, j1),))
+
+
+def test_pages_net_1280x720_full():
+    """The full frame: every pixel of the 3840x2160 output against the oracle's
+    fp16-storage chain."""
+    x, layers = synth.chain_f16_nhwc()
+    say("pages net 1280x720 full")
+    y = _chain(x, layers, 3)
+    ref, m = oracle.chain_f16(x, layers, d2s=3)
+    ratio = check(y, ref, m, tau_f16_chain(len(layers)), "pages net 1280x720 full")
+    say("max err/bound %.3g" % ratio)
 
 
 def test_f16_chain_other_shapes():

@@ -5,7 +5,7 @@ nearest even: |y - y_ref| <= 2e-3 * m per element, m = sum |w*x| + |b|. The
 oracle consumes the same fp16 values, widened exactly. Shapes cover exact and
 ragged 64-row x 32-column units (and the 4-row stages inside them), single
 pixels, batches, more units than workgroups, and the full 8x256x256x64 layer
-on whole sampled rows.
+(every output).
 """
 import numpy as np
 import pytest
@@ -70,20 +70,15 @@ def test_f16_other_channel_counts_use_generic_kernel():
     check(y, ref, m, TAU_F16, "generic f16")
 
 
-def test_mfma_layer_8x256x256_sampled():
-    """8 x 256 x 256 x 64 -> 64: rows on tile edges in every image, all columns
-    and channels."""
+def test_mfma_layer_8x256x256_full():
+    """8 x 256 x 256 x 64 -> 64, the launch the benchmark times: every output
+    against the oracle."""
     x, w, b = synth.cnn_layer_f16_nhwc()
     say("mfma full layer")
     y = _run(x, w, b, False, "is_k4_mfma")
-    assert np.isfinite(y.astype(np.float32)).all()
-    rows = [0, 7, 8, 127, 128, 248, 255]
-    pts = np.array([(n, k, i, j) for n in range(8) for i in rows[n % 3::3] + [rows[n % 7]]
-                    for j in range(256) for k in range(64)], np.int64)
-    ref, m = oracle.conv2d_points(x, w, b, False, pts, "NHWC")
-    got = y[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
-    ratio = check(got, ref, m, TAU_F16, "8x256x256 layer")
-    say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))
+    ref, m = oracle.conv2d(x, w, b, False, "NHWC")
+    ratio = check(y, ref, m, TAU_F16, "8x256x256x64 fp16 layer full")
+    say("max err/bound %.3g" % ratio)
 
 
 def test_mfma_layer_more_units_than_workgroups():
@@ -115,17 +110,12 @@ def test_mfma_other_channel_counts(C, K, N, H, W):
 
 
 @pytest.mark.parametrize("C,K", [(64, 32), (32, 16)])
-def test_mfma_other_channel_counts_1280x720_sampled(C, K):
-    """Two 1280x720 frames (more units than workgroups): rows on unit and
-    stage edges, columns on unit edges, every channel."""
+def test_mfma_other_channel_counts_1280x720_full(C, K):
+    """Two 1280x720 frames (more units than workgroups, 60-row units for the
+    64-channel input): every output against the oracle."""
     x, w, b = synth.cnn_layer_f16_nhwc(N=2, C=C, K=K, H=720, W=1280, seed=C * 3 + K)
-    say("mfma 2x720x1280", C, K)
+    say("mfma 2x720x1280 full", C, K)
     y = _run(x, w, b, True, "is_k4_mfma")
-    assert np.isfinite(y.astype(np.float32)).all()
-    rows = [0, 1, 3, 4, 31, 32, 33, 63, 64, 65, 703, 704, 719]
-    cols = list(range(0, 1280, 13)) + [63, 64, 127, 128, 1279]
-    pts = np.array([(n, k, i, j) for n in range(2) for i in rows for j in cols for k in range(K)], np.int64)
-    ref, m = oracle.conv2d_points(x, w, b, True, pts, "NHWC")
-    got = y[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
-    ratio = check(got, ref, m, TAU_F16, "2x720x1280 %d->%d" % (C, K))
-    say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))
+    ref, m = oracle.conv2d(x, w, b, True, "NHWC")
+    ratio = check(y, ref, m, TAU_F16, "2x720x1280 fp16 %d->%d full" % (C, K))
+    say("max err/bound %.3g" % ratio)

@@ -1,10 +1,10 @@
 """GPU parity of multi-channel fp32 NCHW layers against the oracle.
 
 Calls go through the C ABI. Shapes span several tiles with ragged edges (64x16
-for the register-blocked kernel, 32x16 for the fp32 MFMA kernel that takes the
-32 -> 32 3x3 layers), channel counts that fill one or several LDS slabs, every
-output-channel group size, and the full 1x32x720x1280 layer (sampled rows, all
-columns and channels).
+for the register-blocked kernel, 32 columns x 13 rows for the fp32 MFMA kernel
+that takes the 32 -> 32 3x3 layers), channel counts that fill one or several
+LDS slabs, every output-channel group size, and the full 1x32x720x1280 layer
+(every output, so every 13-row tile seam).
 """
 import numpy as np
 import pytest
@@ -119,17 +119,12 @@ def test_mfma_f32_no_bias_and_delta_weights():
     np.testing.assert_array_equal(y.astype(np.float64), ref)
 
 
-def test_cnn_layer_720p_sampled():
-    """1x32x720x1280 -> 32, 3x3, bias, ReLU: rows on tile edges and random rows,
-    every column and output channel."""
+def test_cnn_layer_720p_full():
+    """1x32x720x1280 -> 32, 3x3, bias, ReLU, the launch the benchmark times:
+    every output channel of every pixel against the oracle."""
     x, w, b = synth.cnn_layer_f32()
-    say("cnn layer 720p")
+    say("cnn layer 720p full")
     y = _run(x, w, b, True, "is_k5_mfma_f32")
-    assert np.isfinite(y).all()
-    rows = sorted({0, 1, 15, 16, 17, 31, 32, 47, 359, 360, 703, 704, 718, 719} |
-                  set(int(r) for r in np.random.default_rng(5).integers(0, 720, 6)))
-    pts = np.array([(0, k, i, j) for k in range(32) for i in rows for j in range(1280)], np.int64)
-    ref, m = oracle.conv2d_points(x, w, b, True, pts)
-    got = y[pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]]
-    ratio = check(got, ref, m, TAU_F32, "720p layer")
-    say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))
+    ref, m = oracle.conv2d(x, w, b, True)
+    ratio = check(y, ref, m, TAU_F32, "720p fp32 layer full")
+    say("max err/bound %.3g" % ratio)

@@ -1,10 +1,9 @@
 """GPU parity of single-channel filtering (C = K = 1, fp32 NCHW) against the oracle.
 
 Every call goes through the C ABI (conv2d_create / conv2d_forward) on the
-current HIP stream. Full comparisons at sizes the oracle finishes in seconds
-(several 256-column wave segments and 128-row strips, ragged tails, widths that
-are not multiples of 4); at 8192x8192 the comparison covers sampled rows and
-columns chosen on strip and segment boundaries.
+current HIP stream. Every output is compared, from ragged small images (several 256-column wave
+segments and 64-row strips, ragged tails, widths that are not multiples of 4)
+up to the full 8192x8192 image with each of the three filters.
 """
 import numpy as np
 import pytest
@@ -91,31 +90,13 @@ def test_empty_image_launches_nothing():
     torch.cuda.synchronize()
 
 
-def _boundary_rows(H, strip):
-    rows = {0, 1, 2, 3, H - 4, H - 3, H - 2, H - 1}
-    for s in range(strip, H, strip * 7):
-        rows |= {s - 3, s - 1, s, s + 2}
-    rng = np.random.default_rng(1)
-    rows |= set(int(r) for r in rng.integers(0, H, 12))
-    return sorted(r for r in rows if 0 <= r < H)
-
-
 @pytest.mark.parametrize("R", [3, 5, 7])
-def test_large_image_sampled(R):
-    """8192x8192 with an RxR normal(0, 1/(R*R)) filter: the launch the benchmark
-    times, checked on whole rows and columns around strip and segment edges."""
+def test_large_image_full(R):
+    """8192x8192 with an RxR normal(0, 1/(R*R)) filter, the launch the
+    benchmark times: every output against the oracle."""
     x, w = synth.large_image(R)
-    say("large image", R)
-    plan = isa.Plan(isa.make_desc(1, 1, 8192, 8192, 1, R, R))
-    strip = plan.info()["tile"][1]
+    say("large image full", R)
     y = _run(x, w)
-    assert np.isfinite(y).all()
-    rows = _boundary_rows(8192, strip)
-    cols = [0, 1, 2, 255, 256, 257, 4095, 4096, 8189, 8190, 8191]
-    pts = [(0, 0, i, j) for i in rows for j in range(8192)]
-    pts += [(0, 0, i, j) for j in cols for i in range(8192)]
-    pts = np.array(pts, np.int64)
-    ref, m = oracle.conv2d_points(x, w, None, False, pts)
-    got = y[pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]]
-    ratio = check(got, ref, m, TAU_F32, "8192^2 R=%d" % R)
-    say("sampled %d outputs, max err/bound %.3g" % (len(pts), ratio))
+    ref, m = oracle.conv2d(x, w)
+    ratio = check(y, ref, m, TAU_F32, "8192^2 %dx%d full" % (R, R))
+    say("max err/bound %.3g" % ratio)

@@ -423,3 +423,91 @@ def test_f16_chain_descriptor_checks():
         assert info["kernel"] == "is_k6_head_f16"
         assert info["tile"] == (64, 32)
     assert isa.Plan(isa.make_desc(1, 1, 72, 128, 8, 3, 3, "f16", True)).info()["kernel"] != "is_k6_head_f16"
+
+
+def test_persistent_grid_sizing():
+    """Persistent kernels launch one workgroup per CU of the device, in a
+    multiple of 8 (their units are dealt to 8 groups, one per XCD), fewer when
+    the units need fewer."""
+    g = isa.is_persistent_grid
+    assert g(256, 256) == 256 and g(2240, 256) == 256      # 8x256x256 fp16 layer; 1280x720 fp32 layer
+    assert g(100, 256) == 104 and g(3, 256) == 8 and g(1, 256) == 8
+    assert g(1000, 80) == 80 and g(1000, 84) == 80 and g(1000, 32) == 32   # partitioned devices
+    assert g(1000, 4) == 8 and g(9, 80) == 16
+    assert g(0, 256) == 0 and g(5, 0) == 0
+    for cus in (8, 32, 38, 80, 256, 304):
+        for units in range(1, 400, 7):
+            v = g(units, cus)
+            assert v % 8 == 0 and 8 <= v <= max(8, cus // 8 * 8)
+            assert v >= min(units, cus // 8 * 8) or v == 8
+    # plans record the grid for 256 CUs
+    p = isa.Plan(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16"))
+    assert p.info()["kernel"] == "is_k4_mfma" and p.info()["grid"][0] == 256
+    p = isa.Plan(isa.make_desc(1, 64, 20, 40, 64, 3, 3, "f16"))
+    assert p.info()["grid"][0] == g(p.info()["grid"][0], 256) == 8
+
+
+def test_single_channel_kernel_keeps_32_bit_row_offsets():
+    """The single-channel kernel's row offsets are 32-bit: its plans stop where
+    4 (W + 256) reaches 2^31, and wider rows go to another kernel."""
+    edge = (1 << 29) - 256
+    assert isa.Plan(isa.make_desc(1, 1, 2, edge - 4, 1, 3, 3)).info()["kernel"] == "is_k1_single"
+    for W in (edge, 1 << 29, 1 << 30):
+        d = isa.make_desc(1, 1, 2, W, 1, 3, 3)
+        assert isa.Plan(d).info()["kernel"] != "is_k1_single"
+        assert all(not v["kernel"].startswith("is_k1_single") for v in isa.conv2d_list_variants(d))
+
+
+def test_no_environment_variable_changes_a_plan():
+    """Only IMGSTENCIL_LOG is read from the environment (logging); layouts and
+    tiles come from the descriptor or a tuning variant."""
+    srcs = [os.path.join(ROOT, "image_stencil_amd", "csrc", f)
+            for f in os.listdir(os.path.join(ROOT, "image_stencil_amd", "csrc"))]
+    names = set()
+    for f in srcs:
+        names |= set(re.findall(r'getenv\("([A-Z_0-9]+)"\)', open(f).read()))
+    assert names <= {"IMGSTENCIL_LOG"}
+
+
+def test_binding_rejects_mismatched_arguments():
+    """conv2d / conv_chain check dtypes, channel counts, bias lengths and square
+    chain filters before anything reaches the library (CPU tensors suffice:
+    these checks come before the device check)."""
+    import torch
+    x = torch.zeros(1, 4, 8, 8)
+    w = torch.zeros(4, 4, 3, 3)
+    with pytest.raises(TypeError):
+        isa.conv2d(x.double(), w.double())
+    with pytest.raises(TypeError):
+        isa.conv2d(x.bfloat16(), w.bfloat16())
+    with pytest.raises(TypeError):
+        isa.conv2d(x, w.half())
+    with pytest.raises(ValueError):
+        isa.conv2d(x[:, :3].contiguous(), w)               # 3 channels, weights for 4
+    with pytest.raises(ValueError):
+        isa.conv2d(x, w, torch.zeros(3))                   # bias for 3 of 4 outputs
+    with pytest.raises(TypeError):
+        isa.conv2d(x, w, torch.zeros(4, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        isa.conv2d(x[0], w)                                # not 4-D
+    with pytest.raises(TypeError, match="device tensor"):
+        isa.conv2d(x, w)                                   # well formed: only the device check fails
+    xc = torch.zeros(1, 1, 8, 8)
+    l1 = (torch.zeros(8, 1, 5, 5), torch.zeros(8), True)
+    l2 = (torch.zeros(4, 8, 3, 3), torch.zeros(4), False)
+    with pytest.raises(ValueError):
+        isa.conv_chain(torch.zeros(1, 2, 8, 8), [l1, l2])  # 2 input channels, layer 1 takes 1
+    with pytest.raises(ValueError):
+        isa.conv_chain(xc, [l1, (torch.zeros(4, 6, 3, 3), None, False)])   # 8 channels into a 6-channel layer
+    with pytest.raises(ValueError):
+        isa.conv_chain(xc, [(torch.zeros(8, 1, 5, 3), None, True)])       # not square
+    with pytest.raises(ValueError):
+        isa.conv_chain(xc, [(l1[0], torch.zeros(7), True), l2])          # short bias
+    with pytest.raises(ValueError):
+        isa.conv_chain(xc, [])
+    with pytest.raises(TypeError):
+        isa.conv_chain(xc.half(), [l1, l2])                 # fp16 input, fp32 weights
+    with pytest.raises(TypeError, match="device tensor"):
+        isa.conv_chain(xc, [l1, l2], depth_to_space=2)
+    with pytest.raises(ValueError):
+        isa.conv2d_separable(x, torch.zeros(3), torch.zeros(3))   # 4 channels

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import synth
+from tolerance import f16_chain_bound
 
 
 def test_depth_to_space_by_3_is_pixel_shuffle():
@@ -70,14 +71,32 @@ def test_window_matches_full(win):
 
 def test_rounding_stays_within_the_chain_bound():
     """Against the exact chain (no rounding), the fp16-storage chain stays
-    within L * 2^-10 * m after L layers (each rounding is at most half an fp16
-    ulp, 2^-11 of the value, and ReLU and the convolutions propagate earlier
-    errors into m); this is the bound under the GPU tolerance."""
+    within ((1 + 2^-11)^L - 1) * m after L layers (each rounding is at most half
+    an fp16 ulp, 2^-11 of the value, and ReLU and the convolutions carry earlier
+    errors into m): about L * 2^-11, the oracle's share of the GPU tolerance
+    (tolerance.f16_chain_bound). The slack 1e-12 m covers the fp64 sums."""
     spec = ((1, 8, 5, True), (8, 8, 3, True), (8, 4, 3, True), (4, 9, 3, False))
     x, layers = synth.chain_f16_nhwc(N=1, H=10, W=11, spec=spec, seed=24)
     got, m = oracle.chain_f16(x, layers)
     exact, mx = oracle.chain(np.transpose(x, (0, 3, 1, 2)), layers)
     exact = np.transpose(exact, (0, 2, 3, 1))
     np.testing.assert_array_equal(m, np.transpose(mx, (0, 2, 3, 1)))
-    assert np.all(np.abs(got - exact) <= len(spec) * 2.0 ** -10 * m)
+    bound = f16_chain_bound(len(spec), gpu=False)
+    assert abs(bound - ((1 + 2.0 ** -11) ** len(spec) - 1)) < 1e-15
+    err = np.abs(got - exact)
+    assert np.all(err <= (bound + 1e-12) * m)
     assert np.any(got != exact)   # the rounding is visible
+
+
+def test_chain_bound_is_reached_by_a_tie():
+    """The one-layer bound 2^-11 m is attained up to a factor 1 - 2^-9: x = 1 +
+    2^-10, w = 1, b = 2^-11 lies halfway between the fp16 neighbours 1 + 2^-10
+    and 1 + 2^-9; nearest-even rounds up, by exactly 2^-11."""
+    x = np.full((1, 1, 1, 1), 1.0 + 2.0 ** -10, np.float16)
+    w = np.ones((1, 1, 1, 1), np.float16)
+    b = np.array([2.0 ** -11], np.float32)
+    got, m = oracle.chain_f16(x, [(w, b, False)])
+    assert got[0, 0, 0, 0] == 1.0 + 2.0 ** -9
+    err = got[0, 0, 0, 0] - (1.0 + 2.0 ** -10 + 2.0 ** -11)
+    assert err == 2.0 ** -11
+    assert 1 - 2.0 ** -9 < err / (f16_chain_bound(1, gpu=False) * m[0, 0, 0, 0]) <= 1.0

@@ -50,7 +50,11 @@ def test_tolerance_check():
     assert check(np.zeros(2), np.zeros(2), np.zeros(2), TAU_F32) == 0.0
     with pytest.raises(AssertionError):
         check(np.array([1e-30, 0.0]), np.zeros(2), np.zeros(2), TAU_F32)
-    assert tau_f16_chain(4) == pytest.approx(8e-3)
+    # the derived fp16-chain tolerance: per layer twice half an fp16 ulp plus
+    # the fp32 sum's bound, about 1.05e-3; four layers under the old 4 * 2e-3
+    assert tau_f16_chain(1) == pytest.approx(2 * 2.0 ** -11 + 577 * 2.0 ** -23, rel=1e-3)
+    assert 4 * 1.04e-3 < tau_f16_chain(4) < 4 * 1.05e-3
+    assert tau_f16_chain(4) < 4 * 2e-3
 
 
 def _im2col_conv(x, w, b, relu):
