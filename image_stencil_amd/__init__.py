@@ -2,7 +2,7 @@
 
 The functions with the C names (conv2d_create, conv2d_forward, conv2d_destroy,
 conv2d_get_plan_info, conv2d_list_variants, conv2d_create_variant,
-conv2d_autotune, conv_chain_workspace_size, conv_chain_forward,
+conv2d_autotune, conv_chain_workspace_size, conv_chain_forward, conv_chain_forward_noalloc,
 conv_chain_kernel_name, conv_chain_groups, is_lds_tile_bytes, is_swizzle_col,
 is_persistent_grid) marshal arguments to
 the C ABI of include/imgstencil.h and nothing else. conv2d() and conv_chain()
@@ -17,7 +17,8 @@ from ._abi import (IS_F16, IS_F32, IS_NCHW, IS_NHWC, IS_CHAIN_AUTO, IS_CHAIN_FUS
 
 __all__ = ["conv2d_create", "conv2d_forward", "conv2d_destroy", "conv2d_get_plan_info",
            "conv2d_list_variants", "conv2d_create_variant", "conv2d_autotune",
-           "conv_chain_workspace_size", "conv_chain_forward", "conv_chain_kernel_name", "conv_chain_groups",
+           "conv_chain_workspace_size", "conv_chain_forward", "conv_chain_forward_noalloc",
+           "conv_chain_kernel_name", "conv_chain_groups",
            "is_lds_tile_bytes", "is_swizzle_col", "is_persistent_grid", "is_version", "make_desc", "make_chain_desc",
            "conv2d", "conv2d_separable", "conv_chain", "Plan", "ImgStencilError"]
 
@@ -146,6 +147,15 @@ def conv_chain_forward(desc, x_ptr, w_ptrs, b_ptrs, y_ptr, ws_ptr, ws_bytes, str
     B = (ctypes.c_void_p * n)(*[p or None for p in b_ptrs]) if b_ptrs is not None else None
     _abi.check(load().conv_chain_forward(ctypes.byref(desc), x_ptr, W, B, y_ptr, ws_ptr or None,
                                          ws_bytes, stream or None), "conv_chain_forward")
+
+
+def conv_chain_forward_noalloc(desc, x_ptr, w_ptrs, b_ptrs, y_ptr, stream):
+    """conv_chain_forward with the library's own workspace (no allocation)."""
+    n = desc.n_layers
+    W = (ctypes.c_void_p * n)(*w_ptrs)
+    B = (ctypes.c_void_p * n)(*[p or None for p in b_ptrs]) if b_ptrs is not None else None
+    _abi.check(load().conv_chain_forward_noalloc(ctypes.byref(desc), x_ptr, W, B, y_ptr, stream or None),
+               "conv_chain_forward_noalloc")
 
 
 def is_lds_tile_bytes(tile_w, tile_h, r, s, channels, elem_bytes):

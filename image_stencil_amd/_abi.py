@@ -15,6 +15,7 @@ IS_F32, IS_F16 = 0, 1
 IS_NCHW, IS_NHWC = 0, 1
 IS_CHAIN_AUTO, IS_CHAIN_FUSED, IS_CHAIN_UNFUSED = 0, 1, 2
 IS_MAX_CHAIN = 8
+IS_NOALLOC_MAX_WORKSPACE = 256 << 20
 
 STATUS_NAMES = {0: "IS_OK", 1: "IS_ERR_INVALID_ARG", 2: "IS_ERR_UNSUPPORTED", 3: "IS_ERR_MISALIGNED",
                 4: "IS_ERR_HIP", 5: "IS_ERR_NO_MEMORY", 6: "IS_ERR_WORKSPACE"}
@@ -64,6 +65,8 @@ SIGNATURES = [
     ("conv_chain_workspace_size", ctypes.c_int, [ctypes.POINTER(conv_chain_desc), ctypes.POINTER(ctypes.c_size_t)]),
     ("conv_chain_forward", ctypes.c_int, [ctypes.POINTER(conv_chain_desc), _vp, ctypes.POINTER(_vp),
                                           ctypes.POINTER(_vp), _vp, _vp, ctypes.c_size_t, _vp]),
+    ("conv_chain_forward_noalloc", ctypes.c_int, [ctypes.POINTER(conv_chain_desc), _vp, ctypes.POINTER(_vp),
+                                                  ctypes.POINTER(_vp), _vp, _vp]),
     ("conv_chain_kernel_name", ctypes.c_int, [ctypes.POINTER(conv_chain_desc), ctypes.c_char_p, ctypes.c_size_t]),
     ("conv_chain_groups", ctypes.c_int, [ctypes.POINTER(conv_chain_desc), ctypes.POINTER(ctypes.c_int), ctypes.c_int,
                                          ctypes.POINTER(ctypes.c_int)]),

@@ -251,6 +251,35 @@ is_status conv_chain_forward(const conv_chain_desc *d, const void *x,
                              void *y, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Bytes of device workspace the library owns for conv_chain_forward_noalloc:
+ * one array of this size on every device the library runs on, held until the
+ * process ends (256 MiB, under 0.1% of an MI355X's 288 GB). */
+#define IS_NOALLOC_MAX_WORKSPACE ((size_t)256 << 20)
+
+/* conv_chain_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same chain and the same kernels, with the layer-by-layer
+ * intermediates in the library's own workspace of IS_NOALLOC_MAX_WORKSPACE
+ * bytes instead of the caller's. Arguments and results as conv_chain_forward
+ * without the workspace arguments. It allocates nothing: no hipMalloc, hipFree
+ * or allocating library call.
+ *  - A chain whose conv_chain_workspace_size exceeds IS_NOALLOC_MAX_WORKSPACE
+ *    is rejected with IS_ERR_WORKSPACE, before any GPU call (a 1280x720 frame
+ *    through the upscaling chain, fp32 or fp16, needs 225 MiB).
+ *  - `stream` must belong to the current device (else IS_ERR_INVALID_ARG): the
+ *    workspace's address on a device is looked up once, by the first call on
+ *    that device (hipGetSymbolAddress); make that first call outside a stream
+ *    capture.
+ *  - Every call on one device shares that device's workspace, which keeps the
+ *    last call's intermediates; nothing in it needs clearing (each layer writes
+ *    its whole output before the next layer reads it). Calls that overlap in
+ *    time on one device (on different streams, or from different host
+ *    threads) race on it: serialise them, e.g. on one stream.
+ * Errors: those of conv_chain_forward, and IS_ERR_WORKSPACE as above. */
+is_status conv_chain_forward_noalloc(const conv_chain_desc *d, const void *x,
+                                     const void *const *w, const float *const *b,
+                                     void *y, hipStream_t stream);
+
 /* Name of the kernel family conv_chain_forward launches for this chain when
  * given the workspace conv_chain_workspace_size reports ("is_k3_chain" when
  * fused, "layer_by_layer" otherwise), copied into name[0..len-1]. */
