@@ -27,6 +27,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+sys.path.insert(1, os.path.join(ROOT, "tests"))   # tolerance.py: the parity tests' bounds
 
 METRIC = "conv GFLOP/s and HBM GB/s as % of MI355X peak; ms per 1280x720 frame"
 HBM_PEAK_GBS = 8000.0
@@ -130,9 +131,9 @@ def _counter_means(d, counter):
 # the bench workloads leave out the pages' net (its 64 -> 64 layer runs the same
 # kernel instance as the fp16 layer workload and would mix into that row); the
 # net has a kernel-trace run of its own.
-PROFILE_ARGS = "--no-cpu-baseline --secondary fp32_layer,fp16_layer,upscale_chain,special_cases"
+PROFILE_ARGS = "--no-cpu-baseline --no-check --secondary fp32_layer,fp16_layer,upscale_chain,special_cases"
 PMC_ARGS = "--steps 2 --warmup 1 --min-warm-s 0 " + PROFILE_ARGS
-NET_PROFILE_ARGS = "--no-cpu-baseline --secondary pages_net"
+NET_PROFILE_ARGS = "--no-cpu-baseline --no-check --secondary pages_net"
 NET_KERNELS = {
     "is_k6_head_f16<5, 64>": "layer 1: 1 -> 64, 5x5",
     "is_k4_mfma<128, 64, 64, 0, 60>": "layer 2: 64 -> 64, 3x3 (60-row units)",
@@ -256,6 +257,58 @@ def lds_study(torch, isa, synth, stream, stream_obj, steps, warmup):
     c = _layer_cases(torch, isa, stream, x, w, b, True, 1, "fp32 layer")[0]
     _, per, _ = _time_cases(torch, [c], steps, warmup, stream_obj)
     out.append({"case": c.name, "kernel": c.kernel, "ms": round(per[0], 4)})
+
+    def variant_case(name, desc, kernel, param, xd, wd, bd, yd):
+        """The plan variant of `desc` running `kernel` with tuning parameter `param`."""
+        vs = isa.conv2d_list_variants(desc)
+        idx = [i for i, v in enumerate(vs) if v["kernel"] == kernel and (param is None or v["param"] == param)]
+        if not idx:
+            raise SystemExit("no %s variant (param %s) for %s" % (kernel, param, name))
+        plan = isa.Plan(desc, variant=idx[0])
+        cc = Case(name, lambda: isa.conv2d_forward(plan.handle, xd.data_ptr(), wd.data_ptr(),
+                                                     bd.data_ptr() if bd is not None else None, yd.data_ptr(),
+                                                     stream), 0, 1, kernel)
+        cc.keep = plan
+        return cc
+
+    # The register-blocked multi-channel kernel on the same fp32 layer (a
+    # tuning variant: 32 output channels per workgroup), and on one channel
+    # filtered by 8 3x3 filters (its default plan there).
+    xd, wd, bd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
+    yd = torch.empty((1, 32, 720, 1280), device="cuda")
+    more = [variant_case("multi-channel kernel, fp32 32->32 3x3 layer", isa.make_desc(1, 32, 720, 1280, 32, 3, 3,
+                                                                                       "f32", True),
+                         "is_k2_multi", 32, xd, wd, bd, yd)]
+    x1 = torch.rand((1, 1, 4096, 4096), device="cuda")
+    w8 = torch.randn((8, 1, 3, 3), device="cuda") / 3
+    y8 = torch.empty((1, 8, 4096, 4096), device="cuda")
+    more.append(variant_case("multi-channel kernel, 1 channel -> 8 filters 3x3", isa.make_desc(1, 1, 4096, 4096, 8,
+                                                                                                3, 3),
+                             "is_k2_multi", None, x1, w8, None, y8))
+    # The pointwise kernel (1x1, 32 -> 32 on a 1280x720 frame).
+    wp = torch.randn((32, 32, 1, 1), device="cuda") / 6
+    more.append(variant_case("pointwise kernel, 1x1 32->32", isa.make_desc(1, 32, 720, 1280, 32, 1, 1), "is_k8_pointwise",
+                             None, xd, wp, None, yd))
+    # The fp16 first-layer kernel (1 -> 64, 5x5, the pages' net's first layer)
+    # and the fp16 MFMA kernel's other instances (64 -> 32, 32 -> 16).
+    xh = torch.rand((1, 720, 1280, 1), device="cuda").half()
+    wh = (torch.randn((64, 1, 5, 5), device="cuda") / 5).half()
+    bh = torch.zeros(64, device="cuda")
+    yh = torch.empty((1, 720, 1280, 64), device="cuda", dtype=torch.float16)
+    more.append(variant_case("fp16 first layer 1->64 5x5", isa.make_desc(1, 1, 720, 1280, 64, 5, 5, "f16", True),
+                             "is_k6_head_f16", None, xh, wh, bh, yh))
+    w32 = (torch.randn((32, 64, 3, 3), device="cuda") / 24).half()
+    y32 = torch.empty((1, 720, 1280, 32), device="cuda", dtype=torch.float16)
+    more.append(variant_case("fp16 layer 64->32", isa.make_desc(1, 64, 720, 1280, 32, 3, 3, "f16", True),
+                             "is_k4_mfma", 128, yh, w32, bh[:32].contiguous(), y32))
+    w16 = (torch.randn((16, 32, 3, 3), device="cuda") / 17).half()
+    y16 = torch.empty((1, 720, 1280, 16), device="cuda", dtype=torch.float16)
+    more.append(variant_case("fp16 layer 32->16", isa.make_desc(1, 32, 720, 1280, 16, 3, 3, "f16", True),
+                             "is_k4_mfma", 128, y32, w16, bh[:16].contiguous(), y16))
+    for cc in more:
+        _, per, _ = _time_cases(torch, [cc], steps, warmup, stream_obj)
+        out.append({"case": cc.name, "kernel": cc.kernel, "ms": round(per[0], 4)})
+        cc.keep = None
     x, layers = synth.chain_f32()
     spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
     d = isa.make_chain_desc(1, 720, 1280, spec, 2, isa.IS_CHAIN_FUSED)
@@ -283,8 +336,11 @@ def pmc_lds_summary(pmc_dir):
              "```", "",
              "Counter values per dispatch (cycles or instructions summed over the chip), averaged over the",
              "dispatches of each kernel. The fp16 layer runs once per swizzle of its input tile (row bytes",
-             "0 = plain, 128, 256; the plan picks 128). conflict share = SQ_LDS_BANK_CONFLICT /",
-             "SQ_LDS_IDX_ACTIVE.", "",
+             "0 = plain, 128, 256; the plan picks 128), and its 64 -> 32 and 32 -> 16 instances on a",
+             "1280x720 frame; the register-blocked multi-channel kernel on the fp32 32 -> 32 layer (a tuning",
+             "variant there) and on one channel with 8 3x3 filters (4096x4096); the pointwise kernel on a",
+             "1x1 32 -> 32 layer; the fp16 first-layer kernel on 1 -> 64 5x5. conflict share =",
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
              "| kernel | dispatches | " + " | ".join(LDS_COUNTERS) + " | conflict share |",
              "|---|---|" + "---|" * len(LDS_COUNTERS) + "---|"]
     for k in kernels:
@@ -376,6 +432,55 @@ def _spread(cases):
     return {"median_ms": round(meds[len(meds) // 2], 4), "min_ms": round(min(c.min_ms for c in cases), 4)}
 
 
+def _oracle_check(y, ref, m, tau):
+    """Outside the timed region: the largest |y - ref| / (tau * m) of one timed
+    output against the oracle (at most 1 passes), with the element count."""
+    import numpy as np
+    y = np.asarray(y, dtype=np.float64)
+    err = np.abs(y - ref)
+    bound = tau * m
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    worst = float(np.max(ratio)) if ratio.size else 0.0
+    if not np.isfinite(y).all():
+        worst = float("inf")
+    return {"max_err_over_bound": float("%.3g" % worst), "tau": tau, "elements": int(y.size), "passed": worst <= 1.0}
+
+
+def _host_info(oracle=None):
+    """The host the CPU leg runs on: logical CPUs, those this process may use,
+    the CPU model, and the oracle's OpenMP threads."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    info = {"nproc": os.cpu_count(), "cpus_allowed": len(os.sched_getaffinity(0)), "cpu_model": model}
+    if oracle is not None:
+        info["omp_threads"] = oracle.threads()
+    return info
+
+
+def _warm_ms(torch, case, steps, stream_obj):
+    """Mean time per launch of one buffer set launched back to back (its data
+    partly or wholly in the 256 MB last-level cache), beside the rotating-set
+    (cold) figures."""
+    for _ in range(3):
+        case.launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream_obj)
+    for _ in range(steps):
+        case.launch()
+    e1.record(stream_obj)
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) / steps, 4)
+
+
 class Case:
     """One kernel launch of a workload: callable, counted work, kernel name."""
 
@@ -430,9 +535,13 @@ def _layer_cases(torch, isa, stream, x, w, b, relu, sets, label):
 SECONDARY_GROUPS = ("fp32_layer", "fp16_layer", "upscale_chain", "pages_net", "special_cases")
 
 
-def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECONDARY_GROUPS):
+def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECONDARY_GROUPS, check=True):
     """Other workloads, each timed on its own (not part of the headline step); `groups` names
-    which of SECONDARY_GROUPS to run."""
+    which of SECONDARY_GROUPS to run. check: after timing, compare one timed
+    output of each workload with the oracle (the full tensor)."""
+    if check:
+        import oracle
+        from tolerance import TAU_F16, TAU_F32, tau_f16_chain
     out = {}
     if "fp32_layer" in groups:
         x, w, b = synth.cnn_layer_f32()
@@ -441,11 +550,16 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
         ms = sum(per) / len(per)
         c = cases[0]
         out["cnn_layer_f32"] = {"workload": c.name + ", bias, ReLU", "kernel": c.kernel, "ms_per_frame": round(ms, 4),
-                                **_spread(cases),
+                                **_spread(cases), "warm_ms": _warm_ms(torch, c, steps, stream_obj),
                                 "gflops": round(c.flops / ms / 1e6, 1),
                                 "frac_fp32_valu": round(c.flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
                                 "frac_fp32_packed_peak": round(c.flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
                                 "roofline": _roofline(c, ms)}
+        if check:
+            y = c.keep[4].cpu().numpy()
+            ref, m = oracle.conv2d(x, w, b, True)
+            out["cnn_layer_f32"]["check"] = _oracle_check(y, ref, m, TAU_F32)
+            del y, ref, m
         for c in cases:
             c.keep = None
 
@@ -471,12 +585,18 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
         c = mcases[0]
         ach = c.flops / ms / 1e9
         out["mfma_layer_f16"] = {"workload": c.name + ", fp32 accumulate, fp16 out", "kernel": c.kernel,
-                                 "ms": round(ms, 4), **_spread(mcases), "gflops": round(c.flops / ms / 1e6, 1),
+                                 "ms": round(ms, 4), **_spread(mcases), "warm_ms": _warm_ms(torch, c, steps, stream_obj),
+                                 "gflops": round(c.flops / ms / 1e6, 1),
                                  "gbs": round(c.bytes / ms / 1e6, 1),
                                  "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                                               "unit": "TFLOP/s", "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4),
                                               "hbm_frac": round(c.bytes / ms / 1e6 / HBM_PEAK_GBS, 4),
                                               "traffic": _traffic(c.name)}}
+        if check:
+            y = c.keep[1].cpu().numpy()
+            ref, m = oracle.conv2d(x, w, b, False, "NHWC")
+            out["mfma_layer_f16"]["check"] = _oracle_check(y, ref, m, TAU_F16)
+            del y, ref, m
         for c in mcases:
             c.keep = None
         del plan
@@ -488,6 +608,7 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
         flops = sum(2.0 * 720 * 1280 * k * c * r * r for (c, k, r, _) in spec)
         nbytes = 4.0 * (720 * 1280 * 5) + sum(4.0 * (k * c * r * r + k) for (c, k, r, _) in spec)
         wl = [(torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()) for (w, b, _) in layers]
+        chain_ref = oracle.chain(x, layers, d2s=2) if check else None
         for mode_name, mode in (("fused", isa.IS_CHAIN_FUSED), ("unfused", isa.IS_CHAIN_UNFUSED)):
             d = isa.make_chain_desc(1, 720, 1280, spec, 2, mode)
             kname = isa.conv_chain_kernel_name(d)
@@ -510,15 +631,20 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
             ms = sum(per) / len(per)
             out["upscale_chain_" + mode_name] = {
                 "workload": ccases[0].name + ": 5x5 1->32, 3x3 32->32 x2, 3x3 32->4, depth-to-space x2",
-                "kernel": kname, "ms_per_frame": round(ms, 4), **_spread(ccases), "gflops": round(flops / ms / 1e6, 1),
+                "kernel": kname, "ms_per_frame": round(ms, 4), **_spread(ccases),
+                "warm_ms": _warm_ms(torch, ccases[0], steps, stream_obj), "gflops": round(flops / ms / 1e6, 1),
                 "frac_fp32_valu": round(flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
                 "frac_fp32_packed_peak": round(flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
                 # both paths run the two 32 -> 32 layers (90% of the FLOPs) on the
                 # fp32 matrix cores
                 "roofline": _roofline(ccases[0], ms, mfma_f32=True)}
+            if check:
+                out["upscale_chain_" + mode_name]["check"] = _oracle_check(ccases[0].keep[1].cpu().numpy(),
+                                                                           chain_ref[0], chain_ref[1], TAU_F32)
             for c in ccases:
                 c.keep = None
             del ws
+        del chain_ref
 
     if "pages_net" in groups:
         # The pages' own net in fp16 storage, layer by layer on the matrix cores.
@@ -549,9 +675,15 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
             "workload": ncases[0].name + ": 5x5 1->64, 3x3 64->64, 64->32, 32->9, depth-to-space x3, "
                         "fp16 storage, fp32 accumulate",
             "kernel": "layer_by_layer", "ms_per_frame": round(ms, 4), **_spread(ncases),
+            "warm_ms": _warm_ms(torch, ncases[0], steps, stream_obj),
             "gflops": round(flops / ms / 1e6, 1),
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None}}
+        if check:
+            ref, m = oracle.chain_f16(x, layers, d2s=3)
+            out["pages_net_f16"]["check"] = _oracle_check(ncases[0].keep[1].cpu().numpy(), ref, m,
+                                                          tau_f16_chain(len(layers)))
+            del ref, m
         for c in ncases:
             c.keep = None
         del ws
@@ -592,6 +724,9 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
                                       "us": round(ms * 1e3, 2), "us_back_to_back": round(b2b * 1e3, 2),
                                       "gbs": round(info["bytes"] / ms / 1e6, 1),
                                       "frac_hbm": round(info["bytes"] / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        if check:
+            ref, m = oracle.conv2d(x, w)
+            out["small_image_3x3_256"]["check"] = _oracle_check(tcases[0].keep[1].cpu().numpy(), ref, m, TAU_F32)
         for c in tcases:
             c.keep = None
         del plan
@@ -761,27 +896,292 @@ def _copy_reference(torch, stream_obj, mib=256, reps=5):
     return out
 
 
-def _cpu_baseline(synth, oracle, min_s=10.0):
+PROBES_LIB = os.path.join(ROOT, "image_stencil_amd", "libimgstencil_probes.so")
+
+
+def _probes(ctypes_mod):
+    if not os.path.exists(PROBES_LIB):
+        raise SystemExit("%s is not built (run __graft_entry__.build())" % PROBES_LIB)
+    lib = ctypes_mod.CDLL(PROBES_LIB)
+    vp = ctypes_mod.c_void_p
+    lib.isp_mfma_rate.argtypes = [ctypes_mod.c_int, ctypes_mod.c_int, ctypes_mod.c_int, vp, vp, vp]
+    lib.isp_lds_probe.argtypes = [ctypes_mod.c_int, ctypes_mod.c_int, ctypes_mod.c_int, ctypes_mod.c_int, vp, vp]
+    return lib
+
+
+def _mfma_reference(torch, stream_obj, min_s=0.3):
+    """The rate back-to-back matrix-core instructions sustain on this chip, the
+    attainable ceiling beside the nominal peaks: 8 waves per CU (as the fp16
+    layer) each issuing independent v_mfma_f32_16x16x32_f16 (or
+    v_mfma_f32_16x16x4_f32) on varying random operands, with the shader clock
+    over the loop from each wave's cycle counter against the 100 MHz real-time
+    counter."""
+    import ctypes
+    lib = _probes(ctypes)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = 2 * cus
+    waves = grid * 4
+    out = {"cus": cus, "waves": waves}
+    for kind, name, flop, iters, peak in ((0, "f16_16x16x32", 16384, 2048, FP16_MFMA_PEAK_TFLOPS),
+                                          (1, "f32_16x16x4", 2048, 1024, FP32_MFMA_PEAK_TFLOPS)):
+        stamps = torch.zeros(2 * waves, dtype=torch.int64, device="cuda")
+        sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+        stream = stream_obj.cuda_stream
+
+        def launch():
+            rc = lib.isp_mfma_rate(kind, grid, iters, stamps.data_ptr(), sink.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError("isp_mfma_rate: hipError_t %d" % rc)
+
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < min_s:   # the clock ramps up under load
+            launch()
+            torch.cuda.synchronize()
+        reps = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream_obj)
+        for _ in range(reps):
+            launch()
+        e1.record(stream_obj)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        st = stamps.cpu().view(-1, 2).double()
+        clock_ghz = float(st[:, 0].sum() / st[:, 1].sum()) * 0.1   # ticks at 100 MHz
+        tflops = waves * iters * 8 * flop / (ms / 1e3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tflops, 1), "peak": peak,
+                     "frac_of_peak": round(tflops / peak, 4), "shader_clock_ghz": round(clock_ghz, 3)}
+    return out
+
+
+def lds_bank_probe(torch, stream_obj, iters=4096):
+    """Launch every LDS probe (access width x address pattern) once, one wave
+    per CU, for a counter run of their bank conflicts (see probes.hip)."""
+    import ctypes
+    lib = _probes(ctypes)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 64, dtype=torch.float32, device="cuda")
+    for op in range(4):
+        for pat in range(5):
+            rc = lib.isp_lds_probe(op, pat, cus, iters, sink.data_ptr(), stream_obj.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("isp_lds_probe: hipError_t %d" % rc)
+            torch.cuda.synchronize()
+    return {"probes": 20, "waves_per_probe": cus, "accesses_per_wave": iters}
+
+
+LDS_PAIR_OFFSETS = (1024, 4096)
+
+
+def lds_pair_probe(torch, stream_obj, iters=1024):
+    """For each access width, every lane-pair probe (lane 0 and one partner on
+    the same bank position, at two row offsets), in a fixed order: width, then
+    offset, then partner 1 .. 63 (see probes.hip)."""
+    import ctypes
+    lib = _probes(ctypes)
+    lib.isp_lds_pair_probe.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 64, dtype=torch.float32, device="cuda")
+    n = 0
+    for op in range(4):
+        for off in LDS_PAIR_OFFSETS:
+            for partner in range(1, 64):
+                rc = lib.isp_lds_pair_probe(op, partner, off, cus, iters, sink.data_ptr(), stream_obj.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError("isp_lds_pair_probe: hipError_t %d" % rc)
+                n += 1
+        torch.cuda.synchronize()
+    return {"probes": n, "waves_per_probe": cus, "accesses_per_wave": iters}
+
+
+LDS_STRIDE_GROUPS = (4, 8, 16)
+LDS_STRIDES = (256, 512, 1024, 2048, 4096)
+
+
+def _stride_cases():
+    """(group, stride) pairs whose highest address fits the probe's 32 KB half."""
+    return [(g, st) for g in LDS_STRIDE_GROUPS for st in LDS_STRIDES if (63 // g) * st + g * 16 <= 32768]
+
+
+def lds_stride_probe(torch, stream_obj, iters=1024):
+    """For each access width, group size and stride, one stride probe, in that
+    order (see probes.hip)."""
+    import ctypes
+    lib = _probes(ctypes)
+    lib.isp_lds_stride_probe.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 64, dtype=torch.float32, device="cuda")
+    n = 0
+    for op in range(4):
+        for g, st in _stride_cases():
+            rc = lib.isp_lds_stride_probe(op, g, st, cus, iters, sink.data_ptr(), stream_obj.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("isp_lds_stride_probe: hipError_t %d" % rc)
+            n += 1
+        torch.cuda.synchronize()
+    return {"probes": n, "waves_per_probe": cus, "accesses_per_wave": iters}
+
+
+def pmc_lds_stride_summary(pmc_dir):
+    """Markdown summary of a counter run of --lds-stride-probe: conflict cycles
+    per instruction by access width, lane group and stride."""
+    import csv
+    import glob
+    import re
+    per = {}
+    for f in sorted(glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                m = re.search(r"isp_lds_stride_probe(?:ILi|<)(\d+)", r["Kernel_Name"])
+                if not m:
+                    continue
+                d = per.setdefault((int(m.group(1)), int(r["Dispatch_Id"])), {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = ["# LDS bank conflicts against the distance between lane groups (gfx950, probe kernels)", "",
+             "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
+             "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS --output-format csv -d %s -o run -- \\" % pmc_dir,
+             "    python3 bench.py --lds-stride-probe",
+             "python3 bench.py --pmc-lds-stride-summary %s > profiles/lds_bank_strides.md" % pmc_dir,
+             "```", "",
+             "Lane l accesses (l mod G) x width + (l / G) x stride bytes: groups of G consecutive lanes",
+             "cover contiguous bytes, the groups lie `stride` apart (`image_stencil_amd/probes/probes.hip`).",
+             "Conflict cycles per wave instruction (SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS).", "",
+             "| access | G | " + " | ".join("stride %d" % st for st in LDS_STRIDES) + " |",
+             "|---|---|" + "---|" * len(LDS_STRIDES)]
+    for op in range(4):
+        disp = sorted(d for (o, d) in per if o == op)
+        order = _stride_cases()
+        if len(disp) != len(order):
+            lines.append("| `%s` | %d dispatches found, %d expected |" % (LDS_PROBE_OPS[op], len(disp), len(order)))
+            continue
+        vals = {}
+        for d, key in zip(disp, order):
+            v = per[(op, d)]
+            vals[key] = v.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(v.get("SQ_INSTS_LDS", 1.0), 1.0)
+        for g in LDS_STRIDE_GROUPS:
+            lines.append("| `%s` | %d | %s |" % (LDS_PROBE_OPS[op], g, " | ".join(
+                "%.2f" % vals[(g, st)] if (g, st) in vals else "-" for st in LDS_STRIDES)))
+    return "\n".join(lines) + "\n"
+
+
+def pmc_lds_pair_summary(pmc_dir):
+    """Markdown summary of a counter run of --lds-pair-probe: for each access
+    width, the lanes served in the same LDS pass as lane 0."""
+    import csv
+    import glob
+    import re
+    per = {}   # (op, dispatch id) -> {counter: value}
+    for f in sorted(glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                m = re.search(r"isp_lds_pair_probe(?:ILi|<)(\d+)", name)
+                if not m:
+                    continue
+                key = (int(m.group(1)), int(r["Dispatch_Id"]))
+                d = per.setdefault(key, {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = ["# Which lanes share an LDS pass with lane 0 (gfx950, probe kernels)", "",
+             "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
+             "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS --output-format csv -d %s -o run -- \\" % pmc_dir,
+             "    python3 bench.py --lds-pair-probe",
+             "python3 bench.py --pmc-lds-pair-summary %s > profiles/lds_lane_groups.md" % pmc_dir,
+             "```", "",
+             "Each probe: every lane of a wave accesses its own contiguous slot (lane x width, no",
+             "conflict), except one partner lane, which accesses lane 0's bank position one row offset",
+             "higher. The probe conflicts exactly when lane 0 and the partner are served in the same",
+             "pass. Listed: the partners whose probe counted at least 0.5 conflict cycles per",
+             "instruction (`image_stencil_amd/probes/probes.hip`).", "",
+             "| access | row offset (bytes) | partners of lane 0 in its pass | conflict cycles / instr of those |",
+             "|---|---|---|---|"]
+    for op in range(4):
+        disp = sorted(d for (o, d) in per if o == op)
+        order = [(off, p) for off in LDS_PAIR_OFFSETS for p in range(1, 64)]
+        if len(disp) != len(order):
+            lines.append("| `%s` | | %d dispatches found, %d expected | |" % (LDS_PROBE_OPS[op], len(disp), len(order)))
+            continue
+        for off in LDS_PAIR_OFFSETS:
+            hits = []
+            for d, (o2, p) in zip(disp, order):
+                if o2 != off:
+                    continue
+                v = per[(op, d)]
+                c = v.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(v.get("SQ_INSTS_LDS", 1.0), 1.0)
+                if c >= 0.5:
+                    hits.append((p, c))
+            lines.append("| `%s` | %d | %s | %s |" % (LDS_PROBE_OPS[op], off, " ".join(str(p) for p, _ in hits) or "none",
+                                                    " ".join("%.2f" % c for _, c in hits)))
+    return "\n".join(lines) + "\n"
+
+
+LDS_PROBE_OPS = {0: "ds_read_b128", 1: "ds_write_b128", 2: "ds_read_b64", 3: "ds_write_b64"}
+LDS_PROBE_PATS = {0: "contiguous (lane x width)",
+                  1: "all lanes in one 16-byte bank group, rows 128 B apart",
+                  2: "8 consecutive lanes cover one 128-byte row; rows 256 B apart",
+                  3: "16 consecutive lanes cover 256 bytes; lane pairs share a 16-byte group mod 128",
+                  4: "fp16 layer operand pattern: 16 pixels x chunk, 128-byte XOR swizzle"}
+
+
+def pmc_lds_probe_summary(pmc_dir):
+    """Markdown summary of a counter run of --lds-bank-probe: conflict and
+    active LDS cycles per wave instruction of each access width and pattern."""
+    import re
+    tabs = {c: _counter_means(pmc_dir, c) for c in LDS_COUNTERS[:3]}
+    rows = []
+    for k, (v, n, full) in tabs["SQ_LDS_BANK_CONFLICT"].items():
+        m = re.search(r"isp_lds_probe(?:ILi|<)(\d+)(?:ELi|, )(\d+)", full) or re.search(r"isp_lds_probe<(\d+), (\d+)>", k)
+        if not m:
+            continue
+        op, pat = int(m.group(1)), int(m.group(2))
+        insts = tabs["SQ_INSTS_LDS"].get(k, (0.0, 0, ""))[0]
+        active = tabs["SQ_LDS_IDX_ACTIVE"].get(k, (0.0, 0, ""))[0]
+        rows.append((op, pat, v / insts if insts else 0.0, active / insts if insts else 0.0, insts))
+    lines = ["# LDS bank behaviour of gfx950, measured with probe kernels", "",
+             "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
+             "rocprofv3 --pmc %s --output-format csv -d %s -o run -- \\" % (" ".join(LDS_COUNTERS[:3]), pmc_dir),
+             "    python3 bench.py --lds-bank-probe",
+             "python3 bench.py --pmc-lds-probe-summary %s > profiles/lds_bank_probe.md" % pmc_dir,
+             "```", "",
+             "One wave per CU repeats one LDS access 4096 times at a fixed address per lane",
+             "(`image_stencil_amd/probes/probes.hip`). Per wave instruction, averaged over the chip:",
+             "conflict = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS, active = SQ_LDS_IDX_ACTIVE / SQ_INSTS_LDS",
+             "(the LDS set-up writes and the final read are included in the counts, about 3% of the",
+             "instructions).", "",
+             "| access | address pattern | conflict cycles / instr | active cycles / instr |",
+             "|---|---|---|---|"]
+    for op, pat, c, a, _ in sorted(rows):
+        lines.append("| `%s` | %s | %.2f | %.2f |" % (LDS_PROBE_OPS[op], LDS_PROBE_PATS[pat], c, a))
+    return "\n".join(lines) + "\n"
+
+
+def _cpu_baseline(synth, oracle, min_s=10.0, gpu_out=None, tau=None):
     """The oracle on full headline steps (3x3, 5x5 and 7x7 over 8192x8192),
-    repeated until at least `min_s` seconds of oracle compute have run."""
+    repeated until at least `min_s` seconds of oracle compute have run. With
+    gpu_out ({R: the GPU's timed output}), the first step's oracle results
+    also check those outputs (returned as the second value)."""
     import numpy as np
     data = []
     for R in (3, 5, 7):
         x, w = synth.large_image(R)
         data.append((R, x.astype(np.float64), w.astype(np.float64)))
         del x
+    checks = {}
     total_bytes, secs, reps = 0.0, 0.0, 0
     while reps == 0 or secs < min_s:
         for R, xd, wd in data:
             t = time.perf_counter()
-            oracle.conv2d(xd, wd)
+            ref, m = oracle.conv2d(xd, wd)
             secs += time.perf_counter() - t
             total_bytes += 4.0 * (2 * 8192 * 8192 + R * R)
+            if reps == 0 and gpu_out is not None:
+                checks["8192x8192 %dx%d" % (R, R)] = _oracle_check(gpu_out[R], ref, m, tau)
+            del ref, m
         reps += 1
-    return {"value": round(total_bytes / secs / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+    base = {"value": round(total_bytes / secs / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
             "kind": "oracle", "seconds": round(secs, 2), "steps": reps,
             "sample": "%d full steps: 8192x8192 fp32 image with 3x3, 5x5 and 7x7 filters, fp64 oracle "
                       "with error scale (compute only; input widening not timed)" % reps}
+    base.update(_host_info(oracle))
+    return base, checks
 
 
 def main():
@@ -792,6 +1192,8 @@ def main():
     ap.add_argument("--min-warm-s", type=float, default=0.3,
                     help="least warmup time per timed group, seconds (default %(default)s)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the oracle check of the timed outputs (profiler runs)")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--secondary", default=",".join(SECONDARY_GROUPS),
                     help="comma-separated secondary workloads to run (default: all of %(default)s); "
@@ -812,6 +1214,18 @@ def main():
                          "chain), for a counter run of their bank conflicts")
     ap.add_argument("--pmc-lds-summary", metavar="PMC_DIR",
                     help="print the LDS counter summary of a rocprofv3 --pmc run of --lds-study and exit")
+    ap.add_argument("--lds-bank-probe", action="store_true",
+                    help="launch only the LDS bank probes (for a counter run) and exit")
+    ap.add_argument("--pmc-lds-probe-summary", metavar="PMC_DIR",
+                    help="print the summary of a rocprofv3 --pmc run of --lds-bank-probe and exit")
+    ap.add_argument("--lds-stride-probe", action="store_true",
+                    help="launch only the LDS stride probes (for a counter run) and exit")
+    ap.add_argument("--pmc-lds-stride-summary", metavar="PMC_DIR",
+                    help="print the summary of a rocprofv3 --pmc run of --lds-stride-probe and exit")
+    ap.add_argument("--lds-pair-probe", action="store_true",
+                    help="launch only the LDS lane-pair probes (for a counter run) and exit")
+    ap.add_argument("--pmc-lds-pair-summary", metavar="PMC_DIR",
+                    help="print the summary of a rocprofv3 --pmc run of --lds-pair-probe and exit")
     args = ap.parse_args()
     globals()["MIN_WARM_S"] = args.min_warm_s
     if args.pmc_summary:
@@ -829,6 +1243,15 @@ def main():
     if args.pmc_lds_summary:
         sys.stdout.write(pmc_lds_summary(args.pmc_lds_summary))
         return
+    if args.pmc_lds_probe_summary:
+        sys.stdout.write(pmc_lds_probe_summary(args.pmc_lds_probe_summary))
+        return
+    if args.pmc_lds_stride_summary:
+        sys.stdout.write(pmc_lds_stride_summary(args.pmc_lds_stride_summary))
+        return
+    if args.pmc_lds_pair_summary:
+        sys.stdout.write(pmc_lds_pair_summary(args.pmc_lds_pair_summary))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -843,6 +1266,15 @@ def main():
     stream_obj = torch.cuda.current_stream()
     stream = stream_obj.cuda_stream
 
+    if args.lds_stride_probe:
+        print(json.dumps({"study": "lds_stride_probe", **lds_stride_probe(torch, stream_obj)}), flush=True)
+        return
+    if args.lds_pair_probe:
+        print(json.dumps({"study": "lds_pair_probe", **lds_pair_probe(torch, stream_obj)}), flush=True)
+        return
+    if args.lds_bank_probe:
+        print(json.dumps({"study": "lds_bank_probe", **lds_bank_probe(torch, stream_obj)}), flush=True)
+        return
     if args.lds_study:
         print(json.dumps({"study": "lds", "results": lds_study(torch, isa, synth, stream, stream_obj, args.steps,
                                                                 args.warmup)}), flush=True)
@@ -850,13 +1282,17 @@ def main():
 
     cases = _single_large_cases(torch, isa, synth, stream)
     ms_step, per, wall = _time_cases(torch, cases, args.steps, args.warmup, stream_obj)
+    # After the timed region: one buffer set launched back to back (warm), and
+    # the timed outputs copied to the host for the oracle check.
+    warm = [_warm_ms(torch, c, args.steps, stream_obj) for c in cases]
+    gpu_out = {c.R: c.keep[3].cpu().numpy() for c in cases} if not args.no_check else None
     step_bytes = sum(c.bytes for c in cases)
     step_flops = sum(c.flops for c in cases)
     value = step_bytes / (ms_step / 1e3) / 1e9
     kernels = []
-    for c, ms in zip(cases, per):
+    for c, ms, wms in zip(cases, per, warm):
         kernels.append({"case": c.name, "kernel": c.kernel, "ms": round(ms, 4),
-                        "median_ms": round(c.median_ms, 4), "min_ms": round(c.min_ms, 4),
+                        "median_ms": round(c.median_ms, 4), "min_ms": round(c.min_ms, 4), "warm_ms": wms,
                         "gflops": round(c.flops / ms / 1e6, 1), "gbs": round(c.bytes / ms / 1e6, 1),
                         "roofline": _roofline(c, ms)})
     dom = max(range(len(cases)), key=lambda i: per[i])
@@ -880,14 +1316,37 @@ def main():
         for g in groups:
             if g not in SECONDARY_GROUPS:
                 raise SystemExit("unknown secondary workload %r (choose from %s)" % (g, ", ".join(SECONDARY_GROUPS)))
-        out["secondary"] = _secondary(torch, isa, synth, stream, stream_obj, args.steps, args.warmup, groups)
+        out["secondary"] = _secondary(torch, isa, synth, stream, stream_obj, args.steps, args.warmup, groups,
+                                      check=not args.no_check)
         torch.cuda.empty_cache()
 
     out["copy_reference"] = _copy_reference(torch, stream_obj)
-    if not args.no_cpu_baseline:
+    out["mfma_reference"] = _mfma_reference(torch, stream_obj)
+    if not args.no_cpu_baseline or not args.no_check:
         import oracle
-        out["cpu_baseline"] = _cpu_baseline(synth, oracle)
+        from tolerance import TAU_F32
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"], checks = _cpu_baseline(synth, oracle, gpu_out=gpu_out, tau=TAU_F32)
+        else:
+            _, checks = _cpu_baseline(synth, oracle, min_s=0.0, gpu_out=gpu_out, tau=TAU_F32)
+        if gpu_out is not None:
+            for k in out["kernels"]:
+                k["check"] = checks[k["case"]]
+            out["check"] = _check_summary(out)
     print(json.dumps(out), flush=True)
+
+
+def _check_summary(out):
+    """Every oracle check of the run: the worst max err / bound and whether all passed."""
+    found = [k["check"] for k in out.get("kernels", []) if "check" in k]
+    for v in out.get("secondary", {}).values():
+        if isinstance(v, dict) and "check" in v:
+            found.append(v["check"])
+    worst = max((c["max_err_over_bound"] for c in found), default=0.0)
+    return {"outputs_checked": len(found), "worst_max_err_over_bound": worst,
+            "all_passed": all(c["passed"] for c in found),
+            "how": "after timing, one timed output of each workload is copied back and compared element by "
+                   "element with the fp64 oracle: |y - y_oracle| <= tau * m"}
 
 
 if __name__ == "__main__":

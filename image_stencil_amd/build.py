@@ -16,6 +16,10 @@ LIB = os.path.join(HERE, "libimgstencil.so")
 # with NaN (IMGSTENCIL_LDS_POISON), so that reading LDS that was never written
 # shows up in the results. Never loaded by the binding.
 LIB_LDS_POISON = os.path.join(HERE, "libimgstencil_ldspoison.so")
+# Measurement kernels of the benchmark (matrix-core rate and shader clock, LDS
+# bank probes): a library of their own, never loaded by the binding.
+PROBES_SRC = os.path.join(HERE, "probes", "probes.hip")
+LIB_PROBES = os.path.join(HERE, "libimgstencil_probes.so")
 ROOT = os.path.dirname(HERE)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -33,7 +37,20 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     """Build the library and its LDS-poison debug variant; returns the library's path."""
     variants = [(LIB, "_build", []), (LIB_LDS_POISON, "_build_ldspoison", ["-DIMGSTENCIL_LDS_POISON"])]
     _compile_and_link(variants, verbose, jobs)
+    _build_probes(verbose)
     return LIB
+
+
+def _build_probes(verbose):
+    tmp = LIB_PROBES + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-shared", PROBES_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        print(r.stdout.decode(errors="replace"), file=sys.stderr)
+        raise RuntimeError("hipcc failed for " + PROBES_SRC)
+    os.replace(tmp, LIB_PROBES)
 
 
 def _compile_and_link(variants, verbose, jobs):

@@ -82,7 +82,7 @@ struct K4Cfg {
   // (the 4-byte halo DMA writes 64 lanes x 4 bytes; with 32 channels its
   // second half holds zeros).
   static constexpr int ROW_SLOTS = TC * CPP + 16;
-  static constexpr int HALO_SLOT = TC * CPP;    // left halo pixel; the right one follows
+  static constexpr int HALO_SLOT = TC * CPP;    // the 16 slots of the two halo pixels (halo_rel)
   static constexpr int ROW_BYTES = ROW_SLOTS * 16;
   static constexpr int STAGE_BYTES = S * ROW_BYTES;
   static constexpr int OUT_ROW_BYTES = TC * K * 2;       // one output row of the unit, fp16
@@ -97,7 +97,6 @@ struct K4Cfg {
   static constexpr int READS_PER_STAGE = S * READS_PER_ROW;
   static constexpr int KS = 9 * NH;             // A fragments (k steps)
   static constexpr int MAIN_OPS = TC * CPP / 2 / 64;     // 16-byte DMA operations per row half
-  static constexpr int HALO_LANES = C / 2;      // lanes of the 4-byte halo DMA per halo pixel
   static constexpr int DMA_OPS = MAIN_OPS + 1;  // DMA operations per wave and stage
   // Weights are staged once, in ring slots PRE.. and the staging area, while
   // the DMA of the first unit's first PRE stages fills the slots before them.
@@ -105,6 +104,7 @@ struct K4Cfg {
   static constexpr int WROW = C * 9 * 2 + 16;   // bytes per padded weight row
   static constexpr int WSTAGE = PRE * STAGE_BYTES;
 
+  static_assert(HALO_SLOT % 16 == 0 && TC % 16 == 0, "halo slots keep the 256-byte bank period");
   static_assert(kWaves == 2 * S, "each wave moves half of one row of a stage");
   static_assert(S * OUT_ROW_BYTES == kWaves * 2 * 1024, "each wave stores two 1 KB pieces of a stage");
   static_assert(MAIN_OPS * 64 * 2 == TC * CPP, "whole DMA operations per row half");
@@ -146,7 +146,7 @@ constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 
 // "CUDA shared memory swizzling" with 16-byte elements and chunks. SWZ = 0
 // keeps the plain layout.
 template <int SWZ, int CPP>
-__device__ __forceinline__ int slot_in_row(int px, int c) {
+__host__ __device__ constexpr int slot_in_row(int px, int c) {
   if constexpr (SWZ == 0) {
     return px * CPP + c;
   } else {
@@ -156,6 +156,39 @@ __device__ __forceinline__ int slot_in_row(int px, int c) {
     const int x = (px % PPR) * CPP + c;
     return y * NX + swizzle_col(y, x, NX, 16, 16);
   }
+}
+
+// Slot (0..15, after HALO_SLOT) of chunk c of the left (side 0, column x0 - 1)
+// or right (side 1, column x0 + TC) halo pixel. A B read takes 16
+// consecutive pixels of a row, and a read of the whole wave runs at full rate
+// when every one of the LDS's 64 banks (4 bytes each, 16 slots of 16 bytes per
+// 256 bytes) receives the same number of accesses. The row's pixels achieve
+// that by the swizzle; a halo pixel takes the place modulo 16 slots of the
+// pixel one swizzle period away (pixel 15 for the left halo, 16 for the right,
+// TC being a multiple of 16), so that reads which include it stay balanced.
+// Where those two places coincide (the 256-byte swizzle), the halo pixels
+// keep plain positions: left chunks at 0 .. CPP-1, right ones after them.
+template <int SWZ, int CPP>
+__host__ __device__ constexpr bool halo_balanced() {
+  for (int a = 0; a < CPP; ++a)
+    for (int b = 0; b < CPP; ++b)
+      if ((slot_in_row<SWZ, CPP>(15, a) & 15) == (slot_in_row<SWZ, CPP>(16, b) & 15)) return false;
+  return true;
+}
+template <int SWZ, int CPP>
+__host__ __device__ constexpr int halo_rel(int side, int c) {
+  if constexpr (halo_balanced<SWZ, CPP>()) return slot_in_row<SWZ, CPP>(side ? 16 : 15, c) & 15;
+  return side * CPP + c;
+}
+// Every halo chunk has a slot of its own among the 16.
+template <int SWZ, int CPP>
+__host__ __device__ constexpr bool halo_slots_distinct() {
+  for (int i = 0; i < 2 * CPP; ++i)
+    for (int j = i + 1; j < 2 * CPP; ++j)
+      if (halo_rel<SWZ, CPP>(i / CPP, i % CPP) == halo_rel<SWZ, CPP>(j / CPP, j % CPP)) return false;
+  for (int i = 0; i < 2 * CPP; ++i)
+    if (halo_rel<SWZ, CPP>(i / CPP, i % CPP) < 0 || halo_rel<SWZ, CPP>(i / CPP, i % CPP) > 15) return false;
+  return true;
 }
 
 // Inverse: pixel and chunk stored at slot si of a row's pixel part. The XOR
@@ -204,6 +237,7 @@ template <int SWZ, int C, int K, int D2S = 0, int URX = 0>
 __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   using G = K4Cfg<C, K, URX>;
   static_assert(D2S == 0 || (D2S == 3 && K == 16), "depth-to-space by 3 of the first 9 of 16 channels");
+  static_assert(halo_slots_distinct<SWZ, G::CPP>(), "halo chunks need slots of their own");
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
   lds_poison(lds, sizeof(lds));
 
@@ -243,7 +277,18 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
 #pragma unroll
   for (int j = 0; j < G::MAIN_OPS; ++j)
     chunk_at<SWZ, G::CPP>(dhalf * (G::TC * G::CPP / 2) + 64 * j + lane, dpx[j], dc[j]);
-  const int hside = lane / G::HALO_LANES;      // halo DMA: 0 left pixel, 1 right, 2-3 none
+  // Halo DMA: lane l writes bytes 4l .. 4l + 3 of the 16 halo slots, i.e.
+  // dword l % 4 of slot l / 4, so it loads that dword of the chunk stored
+  // there (halo_rel), or nothing (the slot is unused and gets zeros).
+  int hside = 2, hchunk = 0;
+#pragma unroll
+  for (int side = 0; side < 2; ++side)
+#pragma unroll
+    for (int c = 0; c < G::CPP; ++c)
+      if (halo_rel<SWZ, G::CPP>(side, c) == (lane >> 2)) {
+        hside = side;
+        hchunk = c;
+      }
   const int hpx = hside ? G::TC : -1;
   // Stores: the stage's staged rows are 2 pieces of 1 KB per wave, piece
   // 2w + j covering bytes [1024 (2w + j), +1024) of the 4 rows in row-major
@@ -301,9 +346,8 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
       }
     }
     const int hx = q.x0 + hpx;
-    q.hcol = (hside < 2 && (unsigned)hx < (unsigned)a.W)
-                 ? (unsigned)(hx * C * 2 + 4 * (lane % G::HALO_LANES))
-                 : kOob;
+    q.hcol = (hside < 2 && (unsigned)hx < (unsigned)a.W) ? (unsigned)(hx * C * 2 + hchunk * 16 + 4 * (lane & 3))
+                                                          : kOob;
     return q;
   };
   auto issue_stage = [&](const UnitGeo &q, int t) {
@@ -395,21 +439,34 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     for (int h = 0; h < G::NH; ++h) {
       const int px = 16 * ch + n16 + v - 1;
       const int c = 4 * h + g;
-      const int slot = px < 0 ? G::HALO_SLOT + c
-                              : (px >= G::TC ? G::HALO_SLOT + G::CPP + c : slot_in_row<SWZ, G::CPP>(px, c));
+      const int slot = px < 0 ? G::HALO_SLOT + halo_rel<SWZ, G::CPP>(0, c)
+                              : (px >= G::TC ? G::HALO_SLOT + halo_rel<SWZ, G::CPP>(1, c)
+                                             : slot_in_row<SWZ, G::CPP>(px, c));
       boff[v][h] = slot * 16;
     }
-  // Staging: output row r of a stage holds pixel px's K channels as K/8 chunks,
-  // chunk c at position c ^ (px mod K/8) so that both the fragment writes and
-  // the line reads spread over the banks. This lane writes channels
-  // 16*og + 4g .. +4 of pixel 16*ch + n16; it reads chunk sc[j] of pixel spx[j].
+  // Staging: output row r of a stage holds pixel px's K channels as K/8 chunks
+  // of 16 bytes, chunk c at position c ^ skey(px), its two 8-byte halves swapped
+  // when shalf(px). A fragment write (8 bytes per lane) is served 16 lanes at a
+  // time over 32 banks (128 bytes): its 16 lanes write 16 consecutive pixels,
+  // the same 4 channels of each, and skey (which 16-byte position within the
+  // pixel's 128-byte window) with shalf (which half) give the 16 pixels 16
+  // distinct 8-byte places in that window. A line read (16 bytes per lane)
+  // takes whole pixels, so it keeps all 64 banks equally loaded; the halves
+  // are swapped back in registers. This lane writes channels 16*og + 4g .. +4
+  // of pixel 16*ch + n16; it reads chunk sc[j] of pixel spx[j].
+  constexpr int kPixPerWin = 64 / K;   // pixels per 128-byte window
+  auto skey = [](int px) { return (px / kPixPerWin) & (G::KPP - 1); };
+  auto shalf = [](int px) { return (px >> 3) & 1; };
   const int wpx = 16 * ch + n16;
-  const int soff_w =
-      G::RING_BYTES + wpx * 2 * K + (((2 * og + (g >> 1)) ^ (wpx & (G::KPP - 1))) * 16) + (g & 1) * 8;
+  const int soff_w = G::RING_BYTES + wpx * 2 * K + (((2 * og + (g >> 1)) ^ skey(wpx)) * 16) +
+                     (((g & 1) ^ shalf(wpx)) * 8);
   int soff_r[2];
+  bool sswap[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    soff_r[j] = G::RING_BYTES + sr * G::OUT_ROW_BYTES + spx[j] * 2 * K + ((sc[j] ^ (spx[j] & (G::KPP - 1))) * 16);
+  for (int j = 0; j < 2; ++j) {
+    soff_r[j] = G::RING_BYTES + sr * G::OUT_ROW_BYTES + spx[j] * 2 * K + ((sc[j] ^ skey(spx[j])) * 16);
+    sswap[j] = shalf(spx[j]) != 0;
+  }
   // D2S: staging offsets of the 6 values a lane stores per segment.
   int doff[2][6];
 #pragma unroll
@@ -418,8 +475,8 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     for (int e = 0; e < 6; ++e) {
       const int px = 2 * lane + e / 3;
       const int c = 3 * (ddy[j] < 0 ? 0 : ddy[j]) + e % 3;
-      doff[j][e] = G::RING_BYTES + drow_s[j] * G::OUT_ROW_BYTES + px * 2 * K +
-                   (((c >> 3) ^ (px & (G::KPP - 1))) * 16) + (c & 7) * 2;
+      doff[j][e] = G::RING_BYTES + drow_s[j] * G::OUT_ROW_BYTES + px * 2 * K + (((c >> 3) ^ skey(px)) * 16) +
+                   (((c & 7) * 2) ^ (shalf(px) * 8));
     }
   const unsigned out3_row_bytes = (unsigned)a.W * 6u;   // D2S output row: 3W fp16
 
@@ -446,7 +503,8 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
           for (int e = 0; e < 6; ++e) hw[e] = *reinterpret_cast<const unsigned short *>(base + doff[j][e]);
           sv[j] = uint4v{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16), 0u};
         } else {
-          sv[j] = *reinterpret_cast<const uint4v *>(lds + soff_r[j] + (t & 1) * G::S * G::OUT_ROW_BYTES);
+          const uint4v v = *reinterpret_cast<const uint4v *>(lds + soff_r[j] + (t & 1) * G::S * G::OUT_ROW_BYTES);
+          sv[j] = sswap[j] ? uint4v{v.z, v.w, v.x, v.y} : v;
         }
       }
     };

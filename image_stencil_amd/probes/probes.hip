@@ -1,0 +1,277 @@
+// probes.hip -- measurement kernels for the benchmark (not part of the
+// convolution library): the rate that back-to-back matrix-core instructions
+// sustain on this chip, with the shader clock during the run, and the LDS
+// bank behaviour of the access widths the convolution kernels use.
+//
+// Every kernel stays inside its own buffers: `stamps` holds two values per
+// wave, `sink` one per thread, and LDS addresses stay below kLdsBytes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
+typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;   // 4 waves: one per SIMD of a CU
+constexpr int kChains = 8;      // independent accumulators per wave
+
+__device__ __forceinline__ unsigned hash32(unsigned v) {
+  v ^= v >> 16;
+  v *= 0x7feb352dU;
+  v ^= v >> 15;
+  v *= 0x846ca68bU;
+  v ^= v >> 16;
+  return v;
+}
+
+// Back-to-back MFMAs: every wave issues kChains independent accumulations per
+// step (so no instruction waits for the previous one's result) for `iters`
+// steps, on operands that differ from one instruction to the next (random
+// values in [-1, 1), as the convolution's data would). F16: the fp16 layer's
+// v_mfma_f32_16x16x32_f16 (16384 FLOP each); else v_mfma_f32_16x16x4_f32
+// (2048 FLOP each). Each wave's lane 0 records its shader-clock cycles
+// (s_memtime) and 100 MHz real-time ticks (s_memrealtime) over the loop.
+template <bool F16>
+__global__ __launch_bounds__(kThreads) void isp_mfma_rate(int iters, unsigned long long *stamps, float *sink) {
+  const int tid = threadIdx.x;
+  const unsigned gid = blockIdx.x * kThreads + tid;
+  float4v acc[kChains];
+#pragma unroll
+  for (int j = 0; j < kChains; ++j) acc[j] = float4v{0.f, 0.f, 0.f, 0.f};
+  unsigned long long c0 = 0, r0 = 0;
+  if constexpr (F16) {
+    half8 a[kChains], b[kChains];
+#pragma unroll
+    for (int j = 0; j < kChains; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[j][e] = (_Float16)((int)(hash32(gid * 64 + j * 8 + e) & 0xFFFF) / 32768.f - 1.f);
+        b[j][e] = (_Float16)((int)(hash32(gid * 64 + j * 8 + e + 0x9E3779B9u) & 0xFFFF) / 32768.f - 1.f);
+      }
+    c0 = clock64();
+    r0 = wall_clock64();
+    for (int i = 0; i < iters; i += kChains) {   // the host rounds iters to a multiple of kChains
+#pragma unroll
+      for (int ii = 0; ii < kChains; ++ii)
+#pragma unroll
+        for (int j = 0; j < kChains; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], b[(j + ii) % kChains], acc[j], 0, 0, 0);
+    }
+  } else {
+    float a[kChains], b[kChains];
+#pragma unroll
+    for (int j = 0; j < kChains; ++j) {
+      a[j] = (int)(hash32(gid * 16 + j) & 0xFFFF) / 32768.f - 1.f;
+      b[j] = (int)(hash32(gid * 16 + j + 0x9E3779B9u) & 0xFFFF) / 32768.f - 1.f;
+    }
+    c0 = clock64();
+    r0 = wall_clock64();
+    for (int i = 0; i < iters; i += kChains) {
+#pragma unroll
+      for (int ii = 0; ii < kChains; ++ii)
+#pragma unroll
+        for (int j = 0; j < kChains; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[(j + ii) % kChains], acc[j], 0, 0, 0);
+    }
+  }
+  const unsigned long long c1 = clock64(), r1 = wall_clock64();
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kChains; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  sink[gid] = s;
+  if ((tid & 63) == 0) {
+    const unsigned wave = gid >> 6;
+    stamps[2 * wave] = c1 - c0;
+    stamps[2 * wave + 1] = r1 - r0;
+  }
+}
+
+// LDS bank probe: one wave per workgroup repeats one LDS access `iters`
+// times, every lane at the byte address pattern(lane) (alternating with a copy
+// of the pattern 8 KB higher, which keeps the banks and stops the compiler from
+// merging the accesses). OP: 0 read 16 B, 1 write 16 B, 2 read 8 B, 3 write
+// 8 B. PAT: 0 contiguous (lane x width); 1 every lane in one 16-byte bank
+// group, rows 128 B apart; 2 groups of 8 consecutive lanes each covering the
+// 128 bytes of one row (rows 256 B apart); 3 groups of 16 consecutive lanes
+// covering 256 bytes, but lanes l and l + 1 of an even pair share a 16-byte
+// bank group in the 128-byte view; 4 pixel-row reads of the fp16 layer: lane
+// l reads 16-byte chunk c = l / 16 of pixel l mod 16 under the 128-byte XOR
+// swizzle (chunk position c ^ (pixel mod 8)).
+constexpr int kLdsBytes = 32 * 1024;
+
+template <int PAT, int WIDTH>
+__device__ __forceinline__ int probe_addr(int lane) {
+  if constexpr (PAT == 0) return lane * WIDTH;
+  if constexpr (PAT == 1) return lane * 128;
+  if constexpr (PAT == 2) return (lane % 8) * 16 + (lane / 8) * 256;
+  if constexpr (PAT == 3) return ((lane % 16) % 2 * 8 + (lane % 16) / 2) * 16 + (lane / 16) * 256;
+  const int px = lane % 16, c = lane / 16;
+  return px * 128 + ((c ^ (px % 8)) * 16);
+}
+
+template <int OP, int PAT>
+__global__ __launch_bounds__(64) void isp_lds_probe(int iters, float *sink) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int lane = threadIdx.x;
+  constexpr int WIDTH = (OP <= 1) ? 16 : 8;
+  const int base = probe_addr<PAT, WIDTH>(lane);
+  for (int i = lane; i < kLdsBytes / 4; i += 64) reinterpret_cast<float *>(lds)[i] = (float)i;
+  __syncthreads();
+  uint4v acc = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < iters; ++i) {
+    const int addr = base + (i & 1) * 8192;
+    if constexpr (OP == 0) {
+      const uint4v v = *reinterpret_cast<const uint4v *>(lds + addr);
+      acc ^= v;
+    } else if constexpr (OP == 1) {
+      *reinterpret_cast<uint4v *>(lds + addr) = uint4v{(unsigned)i, (unsigned)lane, acc.x, 1u};
+    } else if constexpr (OP == 2) {
+      const uint2v v = *reinterpret_cast<const uint2v *>(lds + addr);
+      acc.x ^= v.x;
+      acc.y ^= v.y;
+    } else {
+      *reinterpret_cast<uint2v *>(lds + addr) = uint2v{(unsigned)i, (unsigned)lane};
+    }
+    __asm__ volatile("" ::: "memory");
+  }
+  __syncthreads();
+  sink[blockIdx.x * 64 + lane] = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w) + lds[(lane * 16) % kLdsBytes];
+}
+
+// Lane-pair probe: every lane accesses lane x width (contiguous, conflict-
+// free) except lane `partner`, which accesses lane 0's bank position
+// `offset` bytes higher (offset a multiple of 256, past the contiguous block).
+// A conflict then means that lane 0 and `partner` are served in the same LDS
+// pass. OP as above.
+template <int OP>
+__global__ __launch_bounds__(64) void isp_lds_pair_probe(int partner, int offset, int iters, float *sink) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int lane = threadIdx.x;
+  constexpr int WIDTH = (OP <= 1) ? 16 : 8;
+  const int base = lane == partner ? offset : lane * WIDTH;
+  for (int i = lane; i < kLdsBytes / 4; i += 64) reinterpret_cast<float *>(lds)[i] = (float)i;
+  __syncthreads();
+  uint4v acc = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < iters; ++i) {
+    const int addr = base + (i & 1) * 8192;
+    if constexpr (OP == 0) {
+      acc ^= *reinterpret_cast<const uint4v *>(lds + addr);
+    } else if constexpr (OP == 1) {
+      *reinterpret_cast<uint4v *>(lds + addr) = uint4v{(unsigned)i, (unsigned)lane, acc.x, 1u};
+    } else if constexpr (OP == 2) {
+      const uint2v v = *reinterpret_cast<const uint2v *>(lds + addr);
+      acc.x ^= v.x;
+      acc.y ^= v.y;
+    } else {
+      *reinterpret_cast<uint2v *>(lds + addr) = uint2v{(unsigned)i, (unsigned)lane};
+    }
+    __asm__ volatile("" ::: "memory");
+  }
+  __syncthreads();
+  sink[blockIdx.x * 64 + lane] = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w) + lds[(lane * 16) % kLdsBytes];
+}
+
+// Stride probe: lane l accesses (l mod group) x width + (l / group) x stride,
+// so groups of `group` consecutive lanes cover contiguous bytes and the groups
+// lie `stride` bytes apart. Whether two groups served in the same pass
+// conflict at a given stride shows how the bank index depends on the address.
+constexpr int kStrideLdsBytes = 64 * 1024;
+
+template <int OP>
+__global__ __launch_bounds__(64) void isp_lds_stride_probe(int group, int stride, int iters, float *sink) {
+  __shared__ __attribute__((aligned(16))) char lds[kStrideLdsBytes];
+  const int lane = threadIdx.x;
+  constexpr int WIDTH = (OP <= 1) ? 16 : 8;
+  const int base = (lane % group) * WIDTH + (lane / group) * stride;
+  for (int i = lane; i < kStrideLdsBytes / 4; i += 64) reinterpret_cast<float *>(lds)[i] = (float)i;
+  __syncthreads();
+  uint4v acc = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < iters; ++i) {
+    const int addr = base + (i & 1) * (kStrideLdsBytes / 2);
+    if constexpr (OP == 0) {
+      acc ^= *reinterpret_cast<const uint4v *>(lds + addr);
+    } else if constexpr (OP == 1) {
+      *reinterpret_cast<uint4v *>(lds + addr) = uint4v{(unsigned)i, (unsigned)lane, acc.x, 1u};
+    } else if constexpr (OP == 2) {
+      const uint2v v = *reinterpret_cast<const uint2v *>(lds + addr);
+      acc.x ^= v.x;
+      acc.y ^= v.y;
+    } else {
+      *reinterpret_cast<uint2v *>(lds + addr) = uint2v{(unsigned)i, (unsigned)lane};
+    }
+    __asm__ volatile("" ::: "memory");
+  }
+  __syncthreads();
+  sink[blockIdx.x * 64 + lane] = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w) + lds[(lane * 16) % kStrideLdsBytes];
+}
+
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*k)(KArgs...), int grid, int block, hipStream_t s, Args... args) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k, dim3(grid), dim3(block), 0, s, static_cast<KArgs>(args)...);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+// Back-to-back MFMA rate: `grid` workgroups of 256 threads; stamps holds
+// 2 x (grid x 4) values, sink grid x 256 floats. kind 0: fp16 16x16x32, 1: fp32
+// 16x16x4. iters is rounded up to a multiple of 8 (steps of 8 MFMAs per wave
+// each). Returns a hipError_t.
+int isp_mfma_rate(int kind, int grid, int iters, unsigned long long *stamps, float *sink, hipStream_t s) {
+  if (grid < 1 || iters < 1 || !stamps || !sink) return (int)hipErrorInvalidValue;
+  iters = (iters + kChains - 1) / kChains * kChains;
+  if (kind == 0) return (int)launch(isp_mfma_rate<true>, grid, kThreads, s, iters, stamps, sink);
+  if (kind == 1) return (int)launch(isp_mfma_rate<false>, grid, kThreads, s, iters, stamps, sink);
+  return (int)hipErrorInvalidValue;
+}
+
+// LDS probe of access `op` and address pattern `pat` (see above): `grid`
+// one-wave workgroups; sink holds grid x 64 floats.
+int isp_lds_probe(int op, int pat, int grid, int iters, float *sink, hipStream_t s) {
+  if (grid < 1 || iters < 1 || !sink) return (int)hipErrorInvalidValue;
+#define ISP_CASE(O, P) \
+  if (op == O && pat == P) return (int)launch(isp_lds_probe<O, P>, grid, 64, s, iters, sink);
+#define ISP_OP(O) ISP_CASE(O, 0) ISP_CASE(O, 1) ISP_CASE(O, 2) ISP_CASE(O, 3) ISP_CASE(O, 4)
+  ISP_OP(0) ISP_OP(1) ISP_OP(2) ISP_OP(3)
+#undef ISP_OP
+#undef ISP_CASE
+  return (int)hipErrorInvalidValue;
+}
+
+// Stride probe (see above): group in {4, 8, 16, 32}; the highest address,
+// (63 / group) x stride + group x width, must stay within half the 64 KB.
+int isp_lds_stride_probe(int op, int group, int stride, int grid, int iters, float *sink, hipStream_t s) {
+  if (grid < 1 || iters < 1 || !sink || (group != 4 && group != 8 && group != 16 && group != 32) || stride < 0 ||
+      stride % 16 != 0 || (63 / group) * stride + group * 16 > kStrideLdsBytes / 2)
+    return (int)hipErrorInvalidValue;
+  switch (op) {
+    case 0: return (int)launch(isp_lds_stride_probe<0>, grid, 64, s, group, stride, iters, sink);
+    case 1: return (int)launch(isp_lds_stride_probe<1>, grid, 64, s, group, stride, iters, sink);
+    case 2: return (int)launch(isp_lds_stride_probe<2>, grid, 64, s, group, stride, iters, sink);
+    case 3: return (int)launch(isp_lds_stride_probe<3>, grid, 64, s, group, stride, iters, sink);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+// Lane-pair probe (see above): offset must be a multiple of 256 in
+// [1024, 8192]; `grid` one-wave workgroups; sink holds grid x 64 floats.
+int isp_lds_pair_probe(int op, int partner, int offset, int grid, int iters, float *sink, hipStream_t s) {
+  if (grid < 1 || iters < 1 || !sink || partner < 0 || partner > 63 || offset < 1024 || offset > 8192 ||
+      offset % 256 != 0)
+    return (int)hipErrorInvalidValue;
+  switch (op) {
+    case 0: return (int)launch(isp_lds_pair_probe<0>, grid, 64, s, partner, offset, iters, sink);
+    case 1: return (int)launch(isp_lds_pair_probe<1>, grid, 64, s, partner, offset, iters, sink);
+    case 2: return (int)launch(isp_lds_pair_probe<2>, grid, 64, s, partner, offset, iters, sink);
+    case 3: return (int)launch(isp_lds_pair_probe<3>, grid, 64, s, partner, offset, iters, sink);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+}  // extern "C"

@@ -25,6 +25,9 @@ def pytest_terminal_summary(terminalreporter):
         r, n = worst.get(base, (0.0, 0))
         worst[base] = (max(r, ratio), n + count)
     terminalreporter.write_sep("-", "parity: max |err| / (tau * m) per check (%d checks)" % len(RATIOS))
-    for base in sorted(worst, key=lambda b: -worst[b][0])[:40]:
+    ranked = sorted(worst, key=lambda b: -worst[b][0])
+    # the 20 closest to their bound, then every full-size comparison
+    shown = ranked[:20] + [b for b in ranked[20:] if "full" in b]
+    for base in shown:
         r, n = worst[base]
         terminalreporter.write_line("  %-60s %.3g  (%d elements)" % (base[:60], r, n))
