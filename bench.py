@@ -961,12 +961,100 @@ def lds_bank_probe(torch, stream_obj, iters=4096):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(cus * 64, dtype=torch.float32, device="cuda")
     for op in range(4):
-        for pat in range(5):
+        for pat in range(len(LDS_PROBE_PATS)):
             rc = lib.isp_lds_probe(op, pat, cus, iters, sink.data_ptr(), stream_obj.cuda_stream)
             if rc != 0:
                 raise RuntimeError("isp_lds_probe: hipError_t %d" % rc)
             torch.cuda.synchronize()
-    return {"probes": 20, "waves_per_probe": cus, "accesses_per_wave": iters}
+    return {"probes": 4 * len(LDS_PROBE_PATS), "waves_per_probe": cus, "accesses_per_wave": iters}
+
+
+CLOCK_COUNTERS = ("GRBM_GUI_ACTIVE", "GRBM_COUNT", "SQ_BUSY_CYCLES")
+
+
+def clock_study(torch, isa, synth, stream, stream_obj, out_json):
+    """The matrix-core kernels and the 8192^2 7x7 filter, 4 launches each, and
+    the back-to-back MFMA probes (which measure their own shader clock from the
+    cycle counter; written to out_json), for a counter run of the clock."""
+    cases = []
+    x, w, b = synth.cnn_layer_f16_nhwc()
+    xd, wd, bd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
+    yd = torch.empty((8, 256, 256, 64), dtype=torch.float16, device="cuda")
+    p16 = isa.Plan(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16"))
+    cases.append(lambda: p16.forward(xd, wd, bd, yd))
+    x, w, b = synth.cnn_layer_f32()
+    xf, wf, bf = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
+    yf = torch.empty((1, 32, 720, 1280), device="cuda")
+    p32 = isa.Plan(isa.make_desc(1, 32, 720, 1280, 32, 3, 3, "f32", True))
+    cases.append(lambda: p32.forward(xf, wf, bf, yf))
+    x, layers = synth.chain_f32()
+    xc = torch.from_numpy(x).cuda()
+    lc = [(torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda(), r) for (w, b, r) in layers]
+    cases.append(lambda: isa.conv_chain(xc, lc, depth_to_space=2, mode=isa.IS_CHAIN_FUSED))
+    x, w = synth.large_image(7)
+    xs, ws = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+    ys = torch.empty_like(xs)
+    p7 = isa.Plan(isa.make_desc(1, 1, 8192, 8192, 1, 7, 7))
+    cases.append(lambda: p7.forward(xs, ws, None, ys))
+    for c in cases:
+        for _ in range(4):
+            c()
+        torch.cuda.synchronize()
+    ref = _mfma_reference(torch, stream_obj, min_s=0.1)
+    with open(out_json, "w") as fh:
+        json.dump(ref, fh)
+    return ref
+
+
+def pmc_clock_summary(pmc_dir):
+    """Markdown summary of a counter run of --clock-study: the average shader
+    clock of each dispatch, GRBM_GUI_ACTIVE (read per XCD: the counter sums
+    the 8 XCDs) over the dispatch's duration, against the clock the MFMA probes
+    measure themselves with the cycle counter."""
+    import csv
+    import glob
+    per = {}
+    for f in sorted(glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = (_short_kernel(r["Kernel_Name"]), f, r["Dispatch_Id"])
+                d = per.setdefault(key, {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    acc = {}
+    for (k, _, _), d in per.items():
+        if d["ns"] <= 0 or "GRBM_GUI_ACTIVE" not in d:
+            continue
+        a = acc.setdefault(k, [])
+        a.append((d["ns"], d["GRBM_GUI_ACTIVE"], d.get("GRBM_COUNT", 0.0), d.get("SQ_BUSY_CYCLES", 0.0)))
+    probe = {}
+    pj = os.path.join(pmc_dir, "probe_clock.json")
+    if os.path.exists(pj):
+        with open(pj) as fh:
+            probe = json.load(fh)
+    lines = ["# Shader clock per dispatch (GRBM_GUI_ACTIVE over the dispatch time)", "",
+             "Commands (from the repository root, one MI355X; then the summary, on any machine):", "", "```",
+             "rocprofv3 --pmc %s --output-format csv -d %s -o run -- \\" % (" ".join(CLOCK_COUNTERS), pmc_dir),
+             "    python3 bench.py --clock-study %s/probe_clock.json" % pmc_dir,
+             "python3 bench.py --pmc-clock-summary %s > profiles/shader_clock.md" % pmc_dir,
+             "```", "",
+             "clock = GRBM_GUI_ACTIVE / 8 / dispatch time (the counter is read as the sum of the 8 XCDs'",
+             "own). The MFMA probes measure their own clock over their loop from the cycle counter",
+             "(s_memtime) against the 100 MHz real-time counter; their rows check the counter reading.", "",
+             "| kernel | dispatches | avg us | GHz (GRBM_GUI_ACTIVE / 8) | GHz (GRBM_COUNT / 8) |",
+             "|---|---|---|---|---|"]
+    for k in sorted(acc, key=lambda kk: -sum(a[0] for a in acc[kk])):
+        if not (k.startswith("is_k") or k.startswith("isp_mfma")):
+            continue
+        a = acc[k]
+        ns = sum(v[0] for v in a)
+        gui = sum(v[1] for v in a) / 8.0 / ns
+        cnt = sum(v[2] for v in a) / 8.0 / ns
+        lines.append("| `%s` | %d | %.1f | %.3f | %.3f |" % (k[:60], len(a), ns / len(a) / 1e3, gui, cnt))
+    if probe:
+        lines += ["", "The probes' own clocks over their loops (cycle counter): fp16 %.3f GHz, fp32 %.3f GHz." % (
+            probe.get("f16_16x16x32", {}).get("shader_clock_ghz", 0.0),
+            probe.get("f32_16x16x4", {}).get("shader_clock_ghz", 0.0))]
+    return "\n".join(lines) + "\n"
 
 
 LDS_PAIR_OFFSETS = (1024, 4096)
@@ -995,6 +1083,9 @@ def lds_pair_probe(torch, stream_obj, iters=1024):
 
 LDS_STRIDE_GROUPS = (4, 8, 16)
 LDS_STRIDES = (256, 512, 1024, 2048, 4096)
+# Rows of 16 lanes at strides that are not multiples of 256 bytes, and
+# shifted starts: (stride, offset) of the 16-lane groups, 16-byte reads.
+LDS_ROW_CASES = [(st, off) for st in (256, 272, 288, 304, 320, 384, 512) for off in (0, 16, 128, 240)]
 
 
 def _stride_cases():
@@ -1007,17 +1098,25 @@ def lds_stride_probe(torch, stream_obj, iters=1024):
     order (see probes.hip)."""
     import ctypes
     lib = _probes(ctypes)
-    lib.isp_lds_stride_probe.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.isp_lds_stride_probe.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p, ctypes.c_void_p]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(cus * 64, dtype=torch.float32, device="cuda")
     n = 0
+
+    def one(op, g, st, off):
+        rc = lib.isp_lds_stride_probe(op, g, st, off, cus, iters, sink.data_ptr(), stream_obj.cuda_stream)
+        if rc != 0:
+            raise RuntimeError("isp_lds_stride_probe: hipError_t %d" % rc)
+
     for op in range(4):
         for g, st in _stride_cases():
-            rc = lib.isp_lds_stride_probe(op, g, st, cus, iters, sink.data_ptr(), stream_obj.cuda_stream)
-            if rc != 0:
-                raise RuntimeError("isp_lds_stride_probe: hipError_t %d" % rc)
+            one(op, g, st, 0)
             n += 1
         torch.cuda.synchronize()
+    for st, off in LDS_ROW_CASES:   # 16-byte reads of rows of 16 lanes, after the grid above
+        one(0, 16, st, off)
+        n += 1
+    torch.cuda.synchronize()
     return {"probes": n, "waves_per_probe": cus, "accesses_per_wave": iters}
 
 
@@ -1047,8 +1146,9 @@ def pmc_lds_stride_summary(pmc_dir):
              "Conflict cycles per wave instruction (SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS).", "",
              "| access | G | " + " | ".join("stride %d" % st for st in LDS_STRIDES) + " |",
              "|---|---|" + "---|" * len(LDS_STRIDES)]
+    rows_disp = sorted(d for (o, d) in per if o == 0)[len(_stride_cases()):]
     for op in range(4):
-        disp = sorted(d for (o, d) in per if o == op)
+        disp = sorted(d for (o, d) in per if o == op)[:len(_stride_cases())]
         order = _stride_cases()
         if len(disp) != len(order):
             lines.append("| `%s` | %d dispatches found, %d expected |" % (LDS_PROBE_OPS[op], len(disp), len(order)))
@@ -1060,6 +1160,18 @@ def pmc_lds_stride_summary(pmc_dir):
         for g in LDS_STRIDE_GROUPS:
             lines.append("| `%s` | %d | %s |" % (LDS_PROBE_OPS[op], g, " | ".join(
                 "%.2f" % vals[(g, st)] if (g, st) in vals else "-" for st in LDS_STRIDES)))
+    if len(rows_disp) == len(LDS_ROW_CASES):
+        offs = sorted({o for _, o in LDS_ROW_CASES})
+        lines += ["", "16-byte reads by rows of 16 lanes (G = 16) at strides that are not multiples of 256",
+                  "bytes, all addresses moved up by an offset: conflict cycles per wave instruction.", "",
+                  "| row stride (bytes) | " + " | ".join("offset %d" % o for o in offs) + " |",
+                  "|---|" + "---|" * len(offs)]
+        vals = {}
+        for d, key in zip(rows_disp, LDS_ROW_CASES):
+            v = per[(0, d)]
+            vals[key] = v.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(v.get("SQ_INSTS_LDS", 1.0), 1.0)
+        for st in sorted({s_ for s_, _ in LDS_ROW_CASES}):
+            lines.append("| %d | %s |" % (st, " | ".join("%.2f" % vals[(st, o)] for o in offs)))
     return "\n".join(lines) + "\n"
 
 
@@ -1118,7 +1230,10 @@ LDS_PROBE_PATS = {0: "contiguous (lane x width)",
                   1: "all lanes in one 16-byte bank group, rows 128 B apart",
                   2: "8 consecutive lanes cover one 128-byte row; rows 256 B apart",
                   3: "16 consecutive lanes cover 256 bytes; lane pairs share a 16-byte group mod 128",
-                  4: "fp16 layer operand pattern: 16 pixels x chunk, 128-byte XOR swizzle"}
+                  4: "fp16 layer operand pattern: 16 pixels x chunk, 128-byte XOR swizzle",
+                  5: "every lane at one address (broadcast)",
+                  6: "per 16 lanes: 15 on one address, 1 on another (rows 288 B apart)",
+                  7: "per 16 lanes: 16 consecutive vectors (rows 288 B apart)"}
 
 
 def pmc_lds_probe_summary(pmc_dir):
@@ -1218,6 +1333,10 @@ def main():
                     help="launch only the LDS bank probes (for a counter run) and exit")
     ap.add_argument("--pmc-lds-probe-summary", metavar="PMC_DIR",
                     help="print the summary of a rocprofv3 --pmc run of --lds-bank-probe and exit")
+    ap.add_argument("--clock-study", metavar="OUT_JSON",
+                    help="launch only the clock study kernels (for a counter run) and exit")
+    ap.add_argument("--pmc-clock-summary", metavar="PMC_DIR",
+                    help="print the summary of a rocprofv3 --pmc run of --clock-study and exit")
     ap.add_argument("--lds-stride-probe", action="store_true",
                     help="launch only the LDS stride probes (for a counter run) and exit")
     ap.add_argument("--pmc-lds-stride-summary", metavar="PMC_DIR",
@@ -1246,6 +1365,9 @@ def main():
     if args.pmc_lds_probe_summary:
         sys.stdout.write(pmc_lds_probe_summary(args.pmc_lds_probe_summary))
         return
+    if args.pmc_clock_summary:
+        sys.stdout.write(pmc_clock_summary(args.pmc_clock_summary))
+        return
     if args.pmc_lds_stride_summary:
         sys.stdout.write(pmc_lds_stride_summary(args.pmc_lds_stride_summary))
         return
@@ -1266,6 +1388,10 @@ def main():
     stream_obj = torch.cuda.current_stream()
     stream = stream_obj.cuda_stream
 
+    if args.clock_study:
+        print(json.dumps({"study": "clock", **clock_study(torch, isa, synth, stream, stream_obj,
+                                                           args.clock_study)}), flush=True)
+        return
     if args.lds_stride_probe:
         print(json.dumps({"study": "lds_stride_probe", **lds_stride_probe(torch, stream_obj)}), flush=True)
         return

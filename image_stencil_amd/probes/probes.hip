@@ -99,7 +99,11 @@ __global__ __launch_bounds__(kThreads) void isp_mfma_rate(int iters, unsigned lo
 // covering 256 bytes, but lanes l and l + 1 of an even pair share a 16-byte
 // bank group in the 128-byte view; 4 pixel-row reads of the fp16 layer: lane
 // l reads 16-byte chunk c = l / 16 of pixel l mod 16 under the 128-byte XOR
-// swizzle (chunk position c ^ (pixel mod 8)).
+// swizzle (chunk position c ^ (pixel mod 8)); 5 every lane at one address
+// (broadcast); 6 in each group of 16 lanes, lanes 0-14 share one address and
+// lane 15 reads another (a row's left and right halo vectors, rows 288 bytes
+// apart, as the multi-channel kernel reads them); 7 the same rows, every lane
+// its own vector (that kernel's main read).
 constexpr int kLdsBytes = 32 * 1024;
 
 template <int PAT, int WIDTH>
@@ -108,6 +112,9 @@ __device__ __forceinline__ int probe_addr(int lane) {
   if constexpr (PAT == 1) return lane * 128;
   if constexpr (PAT == 2) return (lane % 8) * 16 + (lane / 8) * 256;
   if constexpr (PAT == 3) return ((lane % 16) % 2 * 8 + (lane % 16) / 2) * 16 + (lane / 16) * 256;
+  if constexpr (PAT == 5) return 0;
+  if constexpr (PAT == 6) return (lane / 16) * 288 + ((lane % 16) == 15 ? 17 * 16 : 0);
+  if constexpr (PAT == 7) return (lane / 16) * 288 + ((lane % 16) + 1) * 16;
   const int px = lane % 16, c = lane / 16;
   return px * 128 + ((c ^ (px % 8)) * 16);
 }
@@ -181,11 +188,12 @@ __global__ __launch_bounds__(64) void isp_lds_pair_probe(int partner, int offset
 constexpr int kStrideLdsBytes = 64 * 1024;
 
 template <int OP>
-__global__ __launch_bounds__(64) void isp_lds_stride_probe(int group, int stride, int iters, float *sink) {
+__global__ __launch_bounds__(64) void isp_lds_stride_probe(int group, int stride, int offset, int iters,
+                                                           float *sink) {
   __shared__ __attribute__((aligned(16))) char lds[kStrideLdsBytes];
   const int lane = threadIdx.x;
   constexpr int WIDTH = (OP <= 1) ? 16 : 8;
-  const int base = (lane % group) * WIDTH + (lane / group) * stride;
+  const int base = offset + (lane % group) * WIDTH + (lane / group) * stride;
   for (int i = lane; i < kStrideLdsBytes / 4; i += 64) reinterpret_cast<float *>(lds)[i] = (float)i;
   __syncthreads();
   uint4v acc = {0u, 0u, 0u, 0u};
@@ -237,24 +245,29 @@ int isp_lds_probe(int op, int pat, int grid, int iters, float *sink, hipStream_t
   if (grid < 1 || iters < 1 || !sink) return (int)hipErrorInvalidValue;
 #define ISP_CASE(O, P) \
   if (op == O && pat == P) return (int)launch(isp_lds_probe<O, P>, grid, 64, s, iters, sink);
-#define ISP_OP(O) ISP_CASE(O, 0) ISP_CASE(O, 1) ISP_CASE(O, 2) ISP_CASE(O, 3) ISP_CASE(O, 4)
+#define ISP_OP(O) \
+  ISP_CASE(O, 0) ISP_CASE(O, 1) ISP_CASE(O, 2) ISP_CASE(O, 3) ISP_CASE(O, 4) ISP_CASE(O, 5) ISP_CASE(O, 6) ISP_CASE(O, 7)
   ISP_OP(0) ISP_OP(1) ISP_OP(2) ISP_OP(3)
 #undef ISP_OP
 #undef ISP_CASE
   return (int)hipErrorInvalidValue;
 }
 
-// Stride probe (see above): group in {4, 8, 16, 32}; the highest address,
-// (63 / group) x stride + group x width, must stay within half the 64 KB.
-int isp_lds_stride_probe(int op, int group, int stride, int grid, int iters, float *sink, hipStream_t s) {
+// Stride probe (see above), every address moved up by `offset` bytes: group
+// in {4, 8, 16, 32}; stride and offset multiples of 16; the highest address,
+// offset + (63 / group) x stride + group x width, must stay within half the
+// 64 KB.
+int isp_lds_stride_probe(int op, int group, int stride, int offset, int grid, int iters, float *sink,
+                         hipStream_t s) {
   if (grid < 1 || iters < 1 || !sink || (group != 4 && group != 8 && group != 16 && group != 32) || stride < 0 ||
-      stride % 16 != 0 || (63 / group) * stride + group * 16 > kStrideLdsBytes / 2)
+      stride % 16 != 0 || offset < 0 || offset % 16 != 0 ||
+      offset + (63 / group) * stride + group * 16 > kStrideLdsBytes / 2)
     return (int)hipErrorInvalidValue;
   switch (op) {
-    case 0: return (int)launch(isp_lds_stride_probe<0>, grid, 64, s, group, stride, iters, sink);
-    case 1: return (int)launch(isp_lds_stride_probe<1>, grid, 64, s, group, stride, iters, sink);
-    case 2: return (int)launch(isp_lds_stride_probe<2>, grid, 64, s, group, stride, iters, sink);
-    case 3: return (int)launch(isp_lds_stride_probe<3>, grid, 64, s, group, stride, iters, sink);
+    case 0: return (int)launch(isp_lds_stride_probe<0>, grid, 64, s, group, stride, offset, iters, sink);
+    case 1: return (int)launch(isp_lds_stride_probe<1>, grid, 64, s, group, stride, offset, iters, sink);
+    case 2: return (int)launch(isp_lds_stride_probe<2>, grid, 64, s, group, stride, offset, iters, sink);
+    case 3: return (int)launch(isp_lds_stride_probe<3>, grid, 64, s, group, stride, offset, iters, sink);
     default: return (int)hipErrorInvalidValue;
   }
 }
