@@ -91,7 +91,7 @@ def _short_kernel(name):
         targs = re.findall(r"Li(-?\d+)E", name[i:name.find("EE", i) + 1]) if name[i:i + 1] == "I" else []
         if parts:
             return parts[-1] + ("<%s>" % ", ".join(targs) if targs else "")
-    name = name.replace("void ", "").replace("is::(anonymous namespace)::", "")
+    name = name.replace("void ", "").replace("is::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
     m = re.match(r"([^(<]+(<[^>]*>)?)", name)
     return m.group(1).strip() if m else name
 
@@ -1040,20 +1040,32 @@ def pmc_clock_summary(pmc_dir):
              "clock = GRBM_GUI_ACTIVE / 8 / dispatch time (the counter is read as the sum of the 8 XCDs'",
              "own). The MFMA probes measure their own clock over their loop from the cycle counter",
              "(s_memtime) against the 100 MHz real-time counter; their rows check the counter reading.", "",
-             "| kernel | dispatches | avg us | GHz (GRBM_GUI_ACTIVE / 8) | GHz (GRBM_COUNT / 8) |",
-             "|---|---|---|---|---|"]
+             "| kernel | dispatches | avg us | GHz (GRBM_GUI_ACTIVE / 8) | GHz (GRBM_COUNT / 8) | GHz calibrated |",
+             "|---|---|---|---|---|---|"]
+
+    def ghz(k):
+        a = acc[k]
+        ns = sum(v[0] for v in a)
+        return ns, sum(v[1] for v in a) / 8.0 / ns, sum(v[2] for v in a) / 8.0 / ns
+
+    # Calibration: the probes' cycle-counter clocks over the counter reading of the same dispatches.
+    ratios = []
+    for name, key in (("isp_mfma_rate<true>", "f16_16x16x32"), ("isp_mfma_rate<false>", "f32_16x16x4")):
+        own = probe.get(key, {}).get("shader_clock_ghz", 0.0)
+        if name in acc and own > 0:
+            ratios.append(own / ghz(name)[1])
+    cal = sum(ratios) / len(ratios) if ratios else 1.0
     for k in sorted(acc, key=lambda kk: -sum(a[0] for a in acc[kk])):
         if not (k.startswith("is_k") or k.startswith("isp_mfma")):
             continue
-        a = acc[k]
-        ns = sum(v[0] for v in a)
-        gui = sum(v[1] for v in a) / 8.0 / ns
-        cnt = sum(v[2] for v in a) / 8.0 / ns
-        lines.append("| `%s` | %d | %.1f | %.3f | %.3f |" % (k[:60], len(a), ns / len(a) / 1e3, gui, cnt))
+        ns, gui, cnt = ghz(k)
+        lines.append("| `%s` | %d | %.1f | %.3f | %.3f | %.3f |" % (k[:60], len(acc[k]), ns / len(acc[k]) / 1e3,
+                                                                 gui, cnt, gui * cal))
     if probe:
-        lines += ["", "The probes' own clocks over their loops (cycle counter): fp16 %.3f GHz, fp32 %.3f GHz." % (
-            probe.get("f16_16x16x32", {}).get("shader_clock_ghz", 0.0),
-            probe.get("f32_16x16x4", {}).get("shader_clock_ghz", 0.0))]
+        lines += ["", "The probes' own clocks over their loops (cycle counter): fp16 %.3f GHz, fp32 %.3f GHz; "
+                      "calibrated = the counter reading x %.3f, their mean ratio." % (
+                          probe.get("f16_16x16x32", {}).get("shader_clock_ghz", 0.0),
+                          probe.get("f32_16x16x4", {}).get("shader_clock_ghz", 0.0), cal)]
     return "\n".join(lines) + "\n"
 
 
