@@ -653,32 +653,40 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
         flops = sum(2.0 * 720 * 1280 * k * c * r * r for (c, k, r, _) in spec)
         nbytes = 2.0 * 720 * 1280 * (1 + 9) + sum(2.0 * k * c * r * r + 4.0 * k for (c, k, r, _) in spec)
         wl = [(torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()) for (w, b, _) in layers]
-        d = isa.make_chain_desc(1, 720, 1280, spec, 3, isa.IS_CHAIN_AUTO, "f16")
-        ws_bytes = isa.conv_chain_workspace_size(d)
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-        ncases = []
-        for _ in range(16):
-            xd = torch.from_numpy(x).cuda()
-            yd = torch.empty((1, 2160, 3840, 1), dtype=torch.float16, device="cuda")
+        res = {}
+        for mname, mode in (("auto", isa.IS_CHAIN_AUTO), ("unfused", isa.IS_CHAIN_UNFUSED)):
+            d = isa.make_chain_desc(1, 720, 1280, spec, 3, mode, "f16")
+            kname = isa.conv_chain_kernel_name(d)
+            ws_bytes = isa.conv_chain_workspace_size(d)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+            ncases = []
+            for _ in range(16):
+                xd = torch.from_numpy(x).cuda()
+                yd = torch.empty((1, 2160, 3840, 1), dtype=torch.float16, device="cuda")
 
-            def launch(xd=xd, yd=yd):
-                isa.conv_chain_forward(d, xd.data_ptr(), [w.data_ptr() for (w, _) in wl],
-                                       [b.data_ptr() for (_, b) in wl], yd.data_ptr(), ws.data_ptr(), ws_bytes, stream)
+                def launch(d=d, xd=xd, yd=yd, ws=ws, ws_bytes=ws_bytes):
+                    isa.conv_chain_forward(d, xd.data_ptr(), [w.data_ptr() for (w, _) in wl],
+                                           [b.data_ptr() for (_, b) in wl], yd.data_ptr(), ws.data_ptr(), ws_bytes,
+                                           stream)
 
-            c = Case("pages' net fp16 1280x720", launch, flops, nbytes, "layer_by_layer")
-            c.keep = (xd, yd)
-            ncases.append(c)
-        _, per, _ = _time_cases(torch, ncases, steps, warmup, stream_obj)
-        ms = sum(per) / len(per)
+                c = Case("pages' net fp16 1280x720", launch, flops, nbytes, kname)
+                c.keep = (xd, yd)
+                ncases.append(c)
+            _, per, _ = _time_cases(torch, ncases, steps, warmup, stream_obj)
+            res[mname] = (sum(per) / len(per), ncases, kname, isa.conv_chain_groups(d), ws)
+        ms, ncases, kname, groups, ws = res["auto"]
         ach = flops / ms / 1e9
         out["pages_net_f16"] = {
             "workload": ncases[0].name + ": 5x5 1->64, 3x3 64->64, 64->32, 32->9, depth-to-space x3, "
                         "fp16 storage, fp32 accumulate",
-            "kernel": "layer_by_layer", "ms_per_frame": round(ms, 4), **_spread(ncases),
+            "kernel": kname, "groups": groups, "ms_per_frame": round(ms, 4), **_spread(ncases),
             "warm_ms": _warm_ms(torch, ncases[0], steps, stream_obj),
+            "ms_per_frame_one_launch_per_layer": round(res["unfused"][0], 4),
             "gflops": round(flops / ms / 1e6, 1),
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None}}
+        for c in res["unfused"][1]:
+            c.keep = None
         if check:
             ref, m = oracle.chain_f16(x, layers, d2s=3)
             out["pages_net_f16"]["check"] = _oracle_check(ncases[0].keep[1].cpu().numpy(), ref, m,

@@ -279,6 +279,22 @@ bool pad_last_f16(const conv_chain_desc *d, const conv2d_desc &last) {
   return is::configure_mfma(p);
 }
 
+// fp16 chains in IS_CHAIN_AUTO whose first layer is 1 -> 64 (3x3 or 5x5) and
+// second 64 -> 64 (3x3) on the MFMA kernel run those two layers as one launch:
+// the first layer is computed inside the second layer's units ("Optimizing
+// convolution kernels - CNNs in Vulkan Part 2/3", section "Reducing memory
+// traffic": its first intermediate never goes to memory).
+bool f16_head_fused(const conv_chain_desc *d, const conv2d_desc *ld) {
+  if (d->dtype != IS_F16 || d->mode != IS_CHAIN_AUTO || d->n_layers < 2) return false;
+  const conv_layer_desc &a = d->layer[0], &b = d->layer[1];
+  if (a.c != 1 || a.k != 64 || a.r != a.s || (a.r != 3 && a.r != 5)) return false;
+  if (b.c != 64 || b.k != 64 || b.r != 3 || b.s != 3) return false;
+  is::Plan p;
+  memset(&p, 0, sizeof(p));
+  p.d = ld[1];
+  return is::configure_mfma(p) && is::mfma_head_supported(p, a.r);
+}
+
 size_t chain_buffer_bytes(const conv_chain_desc *d, const conv2d_desc *ld) {
   const size_t es = d->dtype == IS_F16 ? 2 : 4;
   const int last = d->n_layers - 1;
@@ -507,7 +523,21 @@ is_status chain_forward(const conv_chain_desc *d, const void *x, const void *con
       return IS_OK;
     }
     const void *src = x;
-    for (int l = 0; l < d->n_layers; ++l) {
+    int l0 = 0;
+    if (f16_head_fused(d, ld)) {   // layers 0 and 1 in one launch, into layer 1's buffer
+      is::Plan p;
+      st = make_plan(&ld[1], p);
+      if (st != IS_OK) return st;
+      void *dst = (d->n_layers == 2 && d->depth_to_space == 1) ? y : (void *)(ws + half);
+      st = hip_status(is::launch_mfma_head(
+          p, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(w[0]), b ? b[0] : nullptr,
+          d->layer[0].relu, d->layer[0].r, static_cast<const _Float16 *>(w[1]), b ? b[1] : nullptr,
+          static_cast<_Float16 *>(dst), stream));
+      if (st != IS_OK) return st;
+      src = dst;
+      l0 = 2;
+    }
+    for (int l = l0; l < d->n_layers; ++l) {
       const bool last = l == d->n_layers - 1;
       void *dst = (last && d->depth_to_space == 1) ? y : (void *)(ws + (l % 2) * half);
       is::Plan p;
@@ -599,7 +629,7 @@ is_status conv_chain_kernel_name(const conv_chain_desc *d, char *name, size_t le
     return IS_OK;
   }
   const bool fused = d->mode == IS_CHAIN_FUSED;
-  snprintf(name, len, "%s", fused ? "is_k3_chain" : "layer_by_layer");
+  snprintf(name, len, "%s", fused ? "is_k3_chain" : (f16_head_fused(d, ld) ? "head_fused" : "layer_by_layer"));
   return IS_OK;
 }
 
@@ -618,6 +648,10 @@ is_status conv_chain_groups(const conv_chain_desc *d, int *sizes, int max, int *
   } else if (d->mode == IS_CHAIN_FUSED) {
     groups = 1;
     size[0] = d->n_layers;
+  } else if (f16_head_fused(d, ld)) {
+    groups = d->n_layers - 1;
+    size[0] = 2;
+    for (int l = 1; l < groups; ++l) size[l] = 1;
   } else {
     groups = d->n_layers;
     for (int l = 0; l < groups; ++l) size[l] = 1;

@@ -82,6 +82,15 @@ bool mfma_d2s3_supported(const Plan &p);
 hipError_t launch_mfma_d2s3(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
                             hipStream_t s);
 
+// The fp16 MFMA layer (plan p: 64 -> 64, 3x3) fed by a first layer
+// 1 -> 64 with an r x r filter (r = 3 or 5) computed inside the same launch
+// from the one-channel image x1 (N x H x W fp16): its weights wh (64 x 1 x r x r
+// fp16), bias bh (64 fp32 or null) and ReLU flag. The first layer's output is
+// rounded to fp16 as if it were stored, and never leaves the chip.
+bool mfma_head_supported(const Plan &p, int head_r);
+hipError_t launch_mfma_head(const Plan &p, const _Float16 *x1, const _Float16 *wh, const float *bh, int relu_h,
+                            int head_r, const _Float16 *w, const float *b, _Float16 *y, hipStream_t s);
+
 bool configure_head_f16(Plan &p);
 hipError_t launch_head_f16(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
                            hipStream_t s);

@@ -65,8 +65,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kLdsMax = 160 * 1024;
 constexpr int kMaxMainOps = 4;   // 16-byte DMA operations per row half, at most
 
-// Geometry of the layer with C input and K output channels.
-template <int C, int K, int URX = 0>
+// Geometry of the layer with C input and K output channels. HEAD = r > 0:
+// the layer's input is not read from HBM but computed in the unit, as the
+// output of a first layer 1 -> C with an r x r filter (the "head"), from the
+// one-channel image.
+template <int C, int K, int URX = 0, int HEAD = 0>
 struct K4Cfg {
   static constexpr int NH = C / 32;             // k steps (32 channels) per tap
   static constexpr int CPP = C / 8;             // 16-byte chunks per input pixel
@@ -88,10 +91,25 @@ struct K4Cfg {
   static constexpr int OUT_ROW_BYTES = TC * K * 2;       // one output row of the unit, fp16
   static constexpr int STAGING_BYTES = 2 * S * OUT_ROW_BYTES;
   static constexpr int FIT = (kLdsMax - STAGING_BYTES) / STAGE_BYTES;   // ring slots that fit
-  static constexpr int D = FIT - 1 < 5 ? FIT - 1 : 5;    // stages in flight ahead of the one read
-  static constexpr int NST = D + 1;             // ring slots
+  // Stages in flight ahead of the one read: D DMA stages, or (HEAD) 2 stages
+  // of head rows computed ahead.
+  static constexpr int D = HEAD ? 2 : (FIT - 1 < 5 ? FIT - 1 : 5);
+  static constexpr int NST = HEAD ? 3 : D + 1;  // ring slots
   static constexpr int RING_BYTES = NST * STAGE_BYTES;
-  static constexpr int LDS_BYTES = RING_BYTES + STAGING_BYTES;
+  // HEAD: the unit's one-channel image strip, STRIP_ROWS rows from y0-1-HP and
+  // 52 columns from x0-1-HP (the head's windows over the halo pixels and the
+  // three 16-pixel blocks it is computed in), fp16, after the ring and staging
+  // (or after the weights' pass through LDS, whichever is larger).
+  static constexpr int HP = HEAD ? (HEAD - 1) / 2 : 0;
+  static constexpr int STRIP_COLS = 52;
+  static constexpr int STRIP_ROWS = HEAD ? IN_ROWS + 2 * HP : 0;
+  static constexpr int STRIP_ROW_BYTES = STRIP_COLS * 2;
+  static constexpr int STRIP_OFF_RAW = RING_BYTES + STAGING_BYTES > K * (C * 9 * 2 + 16)
+                                           ? RING_BYTES + STAGING_BYTES
+                                           : K * (C * 9 * 2 + 16);
+  static constexpr int STRIP_OFF = (STRIP_OFF_RAW + 15) / 16 * 16;
+  static constexpr int STRIP_BYTES = STRIP_ROWS * STRIP_ROW_BYTES;
+  static constexpr int LDS_BYTES = HEAD ? STRIP_OFF + STRIP_BYTES : RING_BYTES + STAGING_BYTES;
   static constexpr int READS_PER_ROW = 3 * NH;  // B reads per input row: tap column x channel half
   static constexpr int READS = IN_ROWS * READS_PER_ROW;
   static constexpr int READS_PER_STAGE = S * READS_PER_ROW;
@@ -99,10 +117,16 @@ struct K4Cfg {
   static constexpr int MAIN_OPS = TC * CPP / 2 / 64;     // 16-byte DMA operations per row half
   static constexpr int DMA_OPS = MAIN_OPS + 1;  // DMA operations per wave and stage
   // Weights are staged once, in ring slots PRE.. and the staging area, while
-  // the DMA of the first unit's first PRE stages fills the slots before them.
-  static constexpr int PRE = D < 3 ? D : 3;
+  // the DMA of the first unit's first PRE stages fills the slots before them
+  // (HEAD: from the start of LDS, before any head row is computed).
+  static constexpr int PRE = HEAD ? 0 : (D < 3 ? D : 3);
   static constexpr int WROW = C * 9 * 2 + 16;   // bytes per padded weight row
   static constexpr int WSTAGE = PRE * STAGE_BYTES;
+  // HEAD: head rows are computed for a stage by all 8 waves, wave w taking row
+  // w / 2 of the stage and output-channel blocks 2 (w % 2) and 2 (w % 2) + 1,
+  // in three 16-pixel blocks (pixels -1 .. 46 of the row; -1 .. TC used), at
+  // read steps HEAD_STEP + 7 p (gather) and + 3 (products, writes).
+  static constexpr int HEAD_STEP = 1;
 
   static_assert(HALO_SLOT % 16 == 0 && TC % 16 == 0, "halo slots keep the 256-byte bank period");
   static_assert(kWaves == 2 * S, "each wave moves half of one row of a stage");
@@ -113,6 +137,10 @@ struct K4Cfg {
   static_assert(LDS_BYTES <= kLdsMax, "LDS");
   static_assert(WSTAGE + K * WROW <= LDS_BYTES, "weights fit beside the first stages");
   static_assert(READS_PER_STAGE > 3, "stores and DMA sit at read steps 0, 2 and 3 of a stage");
+  static_assert(HEAD == 0 || (C == 64 && (HEAD == 3 || HEAD == 5) && TC == 32),
+                "the head feeds a 64-channel layer of 32-pixel units");
+  static_assert(HEAD == 0 || HEAD_STEP + 7 * 2 + 3 < READS_PER_STAGE, "head steps inside a stage");
+  static_assert(HEAD == 0 || 16 * 3 + 2 * HP + 2 - HP <= STRIP_COLS, "strip covers the head windows");
 };
 
 // ---- VMEM operations of one wave, in program order, per unit:
@@ -216,6 +244,11 @@ struct MfmaArgs {
   int N, H, W, relu;
   int kvalid;   // output channels in w and bias; the rest of K computes zeros
   int units_x, units_y, nunits;
+  // HEAD: x is the one-channel image (N x H x W fp16); the head's C x 1 x r x r
+  // fp16 weights, its fp32 bias (or null) and ReLU flag.
+  const _Float16 *wh;
+  const float *bh;
+  int relu_h;
 };
 
 // Where one unit's bytes live: the image's buffer resources, the unit origin,
@@ -233,9 +266,9 @@ struct UnitGeo {
 // the way out (y is N x 3H x 3W fp16, out[3i+dy][3j+dx] = z[i][j][3dy+dx]),
 // in place of the staged rows' 16-channel pixel lines; 16 output channels only.
 // URX: unit height other than the default 64 rows (60 divides a 720-row frame).
-template <int SWZ, int C, int K, int D2S = 0, int URX = 0>
+template <int SWZ, int C, int K, int D2S = 0, int URX = 0, int HEAD = 0>
 __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
-  using G = K4Cfg<C, K, URX>;
+  using G = K4Cfg<C, K, URX, HEAD>;
   static_assert(D2S == 0 || (D2S == 3 && K == 16), "depth-to-space by 3 of the first 9 of 16 channels");
   static_assert(halo_slots_distinct<SWZ, G::CPP>(), "halo chunks need slots of their own");
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
@@ -370,6 +403,115 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     }
   };
 
+  // ---- HEAD: the layer's input rows are computed here from the one-channel
+  // image: z[px][c] = f16(act_h(bh[c] + sum_{u,v} wh[c][u][v] x[gy-HP+u][gx-HP+v]))
+  // for the unit's input row gy and pixel gx, 0 outside the image (the zero
+  // padding of this layer's input). One v_mfma_f32_16x16x32_f16 per 16
+  // channels x 16 pixels: A = 16 channels x 32 taps (taps past HEAD^2 have
+  // zero weights), B = 32 taps x 16 pixels gathered from the image strip in
+  // LDS, D = 4 consecutive channels of one pixel per lane, which go to the
+  // pixel's place in the ring row exactly as the DMA of an input row puts them
+  // (same swizzle, same halo slots).
+  constexpr int kHeadTaps = HEAD * HEAD;
+  constexpr int kStripElems = G::STRIP_ROWS * G::STRIP_COLS;
+  constexpr int kStripPerThread = HEAD ? (kStripElems + kThreads - 1) / kThreads : 1;
+  half8 ha[2];            // head weights of channel blocks 2 (wave % 2) and + 1
+  float hb[2][4];         // their biases for this lane's 4 channels
+  int toff[8];            // byte offsets in the strip of this lane's taps 8g .. 8g+7
+  const int hrow = wave >> 1;             // stage row this wave computes
+  const int hob = 2 * (wave & 1);         // first of its two channel blocks
+  if constexpr (HEAD) {
+    const __amdgpu_buffer_rsrc_t rwh = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<_Float16 *>(a.wh), (short)0, C * kHeadTaps * 2, kBufferFlags);
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      const int o = 16 * (hob + b2) + n16;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tap = 8 * g + j;
+        const unsigned off = tap < kHeadTaps ? (unsigned)((o * kHeadTaps + tap) * 2) : kOob;
+        ha[b2][j] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rwh, off, 0, 0));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hb[b2][e] = a.bh ? a.bh[16 * (hob + b2) + 4 * g + e] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tap = 8 * g + j;
+      toff[j] = tap < kHeadTaps ? (tap / HEAD) * G::STRIP_ROW_BYTES + (tap % HEAD) * 2 : 0;
+    }
+  }
+  // The image strip of unit geometry q: STRIP_ROWS x 52 fp16 values from
+  // (q.y0 - 1 - HP, q.x0 - 1 - HP), 0 outside the image; loaded into registers
+  // (strip_load) and then written to LDS (strip_store).
+  auto strip_load = [&](int u, unsigned short (&sv)[kStripPerThread]) {
+    const int tx = u % a.units_x;
+    const int ty = (u / a.units_x) % a.units_y;
+    const int n = u / (a.units_x * a.units_y);
+    const int sy0 = ty * G::UR - 1 - G::HP, sx0 = tx * G::TC - 1 - G::HP;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<_Float16 *>(a.x + (size_t)n * a.H * a.W), (short)0, (int)((size_t)a.H * a.W * 2), kBufferFlags);
+#pragma unroll
+    for (int e = 0; e < kStripPerThread; ++e) {
+      const int idx = e * kThreads + tid;
+      const int gy = sy0 + idx / G::STRIP_COLS, gx = sx0 + idx % G::STRIP_COLS;
+      const bool in = idx < kStripElems && (unsigned)gy < (unsigned)a.H && (unsigned)gx < (unsigned)a.W;
+      sv[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, in ? (unsigned)((gy * a.W + gx) * 2) : kOob, 0, 0);
+    }
+  };
+  auto strip_store = [&](const unsigned short (&sv)[kStripPerThread]) {
+#pragma unroll
+    for (int e = 0; e < kStripPerThread; ++e) {
+      const int idx = e * kThreads + tid;
+      if (kStripElems % kThreads == 0 || idx < kStripElems)
+        *reinterpret_cast<unsigned short *>(lds + G::STRIP_OFF + idx * 2) = sv[e];
+    }
+  };
+  // B fragment of pixel block p (pixels 16p - 1 + n16 of the row) for unit
+  // input row li: image rows li .. li + 2 HP of the strip.
+  auto head_gather = [&](int li, int p) -> half8 {
+    half8 b;
+    const char *base = lds + G::STRIP_OFF + li * G::STRIP_ROW_BYTES + (16 * p + n16) * 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const _Float16 v = *reinterpret_cast<const _Float16 *>(base + toff[j]);
+      b[j] = 8 * g + j < kHeadTaps ? v : (_Float16)0.f;   // as the weights past HEAD^2
+    }
+    return b;
+  };
+  // Products of pixel block p of input row li and its two channel blocks, and
+  // their place in ring slot `slot` (row hrow of that stage).
+  auto head_finish = [&](const UnitGeo &q, int slot, int li, int p, const half8 &bfrag) {
+    const int px = 16 * p - 1 + n16;
+    const int gy = q.y0 - 1 + li, gx = q.x0 + px;
+    const bool inside = (unsigned)gy < (unsigned)a.H && (unsigned)gx < (unsigned)a.W;
+    char *row = lds + slot * G::STAGE_BYTES + hrow * G::ROW_BYTES;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      const float4v d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[b2], bfrag, float4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      _Float16 hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float r = d[e] + hb[b2][e];
+        if (a.relu_h) r = fmaxf(r, 0.f);
+        hv[e] = inside ? (_Float16)r : (_Float16)0.f;
+      }
+      const int c = 2 * (hob + b2) + (g >> 1);
+      const int sl = px < 0 ? G::HALO_SLOT + halo_rel<SWZ, G::CPP>(0, c)
+                            : (px >= G::TC ? G::HALO_SLOT + halo_rel<SWZ, G::CPP>(1, c)
+                                           : slot_in_row<SWZ, G::CPP>(px, c));
+      if (px <= G::TC) *reinterpret_cast<uint2v *>(row + sl * 16 + (g & 1) * 8) = __builtin_bit_cast(uint2v, hv);
+    }
+  };
+  // Head rows of stage t of the unit (all of them: the prologue's stages).
+  auto head_stage = [&](const UnitGeo &q, int t) {
+    const int li = t * G::S + hrow;
+    if (li < G::IN_ROWS) {
+#pragma unroll
+      for (int p = 0; p < 3; ++p) head_finish(q, t % G::NST, li, p, head_gather(li, p));
+    }
+  };
+
   // ---- Weights and bias: bias and coalesced weight loads first, then the DMA
   // of the first unit's first PRE stages, then the weights' trip through LDS,
   // so that the DMA latency overlaps it. Each output channel's 9C halves go on
@@ -399,8 +541,10 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j)
       t[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, (j * kThreads + tid) * 16, 0, 0);
+    if constexpr (!HEAD) {
 #pragma unroll
-    for (int st = 0; st < G::PRE; ++st) issue_stage(geo, st);
+      for (int st = 0; st < G::PRE; ++st) issue_stage(geo, st);
+    }
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j) {
       const int v = j * kThreads + tid;
@@ -427,8 +571,22 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     }
   }
   lds_barrier();   // the weights' LDS is ring space from here on
+  // The first unit's first D stages: DMA, or (HEAD) the image strip and the
+  // head rows of stages 0 and 1.
+  auto unit_start = [&](const UnitGeo &q, int u, int from) {
+    if constexpr (HEAD) {
+      unsigned short sv[kStripPerThread];
+      strip_load(u, sv);
+      strip_store(sv);
+      lds_barrier();
 #pragma unroll
-  for (int st = G::PRE; st < G::D; ++st) issue_stage(geo, st);
+      for (int st = 0; st < G::D; ++st) head_stage(q, st);
+    } else {
+#pragma unroll
+      for (int st = from; st < G::D; ++st) issue_stage(q, st);
+    }
+  };
+  unit_start(geo, unit, G::PRE);
 
   // Byte offsets (inside a row) of this lane's B reads for filter column v and
   // channel half h: pixel 16*ch + n16 + v - 1 of the row, chunk 4h + g.
@@ -483,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   while (true) {
     // ---- Unit prologue: stages 0 .. D-1 are in flight; the first two must
     // have landed before the first read.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(vm_after<G>(1, -1)));
+    if constexpr (!HEAD) __builtin_amdgcn_s_waitcnt(waitcnt_vm(vm_after<G>(1, -1)));
     lds_barrier();
 
     auto read_b = [&](int q) -> half8 {
@@ -533,6 +691,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
 
     constexpr int kAhead = 8;
     half8 ring[kAhead];
+    half8 hfrag = {};   // HEAD: the pixel block gathered for the next head products
 #pragma unroll
     for (int q = 0; q < kAhead; ++q) ring[q] = read_b(q);
     float4v acc[4];
@@ -545,8 +704,22 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
       // Stage t - 1's rows leave for HBM; stage t + D's rows start their DMA.
       if constexpr (t >= 1 && qs == 0) read_staged(t - 1, sv);
       if constexpr (t >= 1 && qs == 2) store_stage(t - 1, sv);
-      if constexpr (t + G::D < G::STAGES && qs == 3) issue_stage(geo, t + G::D);
-      if constexpr (qs == 0 || qs == 2 || qs == 3) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!HEAD && t + G::D < G::STAGES && qs == 3) issue_stage(geo, t + G::D);
+      // HEAD: the head rows of stage t + 2, pixel block p gathered at step
+      // HEAD_STEP + 7p and finished three steps later.
+      constexpr bool kHeadStep = HEAD && t + 2 < G::STAGES && qs >= G::HEAD_STEP &&
+                                 qs <= G::HEAD_STEP + 14 + 3 && (qs - G::HEAD_STEP) % 7 <= 3 &&
+                                 ((qs - G::HEAD_STEP) % 7 == 0 || (qs - G::HEAD_STEP) % 7 == 3);
+      if constexpr (kHeadStep) {
+        constexpr int p = (qs - G::HEAD_STEP) / 7;
+        const int li = (t + 2) * G::S + hrow;
+        if constexpr ((qs - G::HEAD_STEP) % 7 == 0) {
+          if (li < G::IN_ROWS) hfrag = head_gather(li, p);
+        } else {
+          if (li < G::IN_ROWS) head_finish(geo, (t + 2) % G::NST, li, p, hfrag);
+        }
+      }
+      if constexpr (qs == 0 || qs == 2 || qs == 3 || kHeadStep) __builtin_amdgcn_sched_barrier(0);
 
       const half8 b = ring[q % kAhead];
       if constexpr (q + kAhead < G::READS) ring[q % kAhead] = read_b(q + kAhead);
@@ -577,7 +750,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
       // through the read-ahead ring) must have landed; the barrier publishes it,
       // frees stage t's ring slot and completes stage t's staged rows.
       if constexpr (qs == G::READS_PER_STAGE - 1 || q == G::READS - 1) {
-        if constexpr (t + 2 < G::STAGES) __builtin_amdgcn_s_waitcnt(waitcnt_vm(vm_after<G>(t + 2, t)));
+        if constexpr (!HEAD && t + 2 < G::STAGES) __builtin_amdgcn_s_waitcnt(waitcnt_vm(vm_after<G>(t + 2, t)));
         lds_barrier();
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -591,8 +764,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     // by this unit's last barrier, and the next unit's first barrier comes
     // after this unit's last staging reads.
     geo = unit_geo(unit);
-#pragma unroll
-    for (int t = 0; t < G::D; ++t) issue_stage(geo, t);
+    unit_start(geo, unit, 0);
   }
 }
 
@@ -686,8 +858,45 @@ hipError_t launch_mfma_d2s3(const Plan &p, const _Float16 *x, const _Float16 *w,
   a.units_x = p.nseg;
   a.units_y = p.nstrip;
   a.nunits = p.ntiles;
+  a.wh = nullptr;
+  a.bh = nullptr;
+  a.relu_h = 0;
   return launch_kernel(is_k4_mfma<128, 32, 16, 3>, dim3(persistent_grid(p.ntiles, device_cu_count())),
                        dim3(p.block), 0, s, a);
+}
+
+bool mfma_head_supported(const Plan &p, int head_r) {
+  const conv2d_desc &d = p.d;
+  return p.kid == kMfmaNhwcF16 && d.c == 64 && d.k == 64 && p.vec == 128 && p.kvalid == d.k &&
+         (head_r == 3 || head_r == 5) && (p.tile_h == 64 || p.tile_h == 60);
+}
+
+hipError_t launch_mfma_head(const Plan &p, const _Float16 *x1, const _Float16 *wh, const float *bh, int relu_h,
+                            int head_r, const _Float16 *w, const float *b, _Float16 *y, hipStream_t s) {
+  if (!mfma_head_supported(p, head_r)) return hipErrorInvalidValue;
+  MfmaArgs a;
+  a.x = x1;
+  a.w = w;
+  a.bias = b;
+  a.y = y;
+  a.N = p.d.n;
+  a.H = p.d.h;
+  a.W = p.d.w;
+  a.relu = p.d.relu;
+  a.kvalid = p.kvalid;
+  a.units_x = p.nseg;
+  a.units_y = p.nstrip;
+  a.nunits = p.ntiles;
+  a.wh = wh;
+  a.bh = bh;
+  a.relu_h = relu_h;
+  const dim3 grid(persistent_grid(p.ntiles, device_cu_count())), block(p.block);
+  const bool u60 = p.tile_h == 60;
+  if (head_r == 5)
+    return u60 ? launch_kernel(is_k4_mfma<128, 64, 64, 0, 60, 5>, grid, block, 0, s, a)
+               : launch_kernel(is_k4_mfma<128, 64, 64, 0, 0, 5>, grid, block, 0, s, a);
+  return u60 ? launch_kernel(is_k4_mfma<128, 64, 64, 0, 60, 3>, grid, block, 0, s, a)
+             : launch_kernel(is_k4_mfma<128, 64, 64, 0, 0, 3>, grid, block, 0, s, a);
 }
 
 hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
@@ -705,6 +914,9 @@ hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, cons
   a.units_x = p.nseg;
   a.units_y = p.nstrip;
   a.nunits = p.ntiles;
+  a.wh = nullptr;
+  a.bh = nullptr;
+  a.relu_h = 0;
   const dim3 grid(persistent_grid(p.ntiles, device_cu_count())), block(p.block);
   if (p.d.c == 64 && p.d.k == 64) {
     if (p.tile_h == 60) return launch_kernel(is_k4_mfma<128, 64, 64, 0, 60>, grid, block, 0, s, a);

@@ -193,8 +193,12 @@ is_status conv2d_autotune(conv2d_plan plan, const void *x, const void *w, const 
  *  Layer l reads layer[l].c channels (layer[0].c = input channels, layer[l].c
  *  = layer[l-1].k), has layer[l].k outputs, odd r == s, and ReLU if relu != 0.
  *  dtype: IS_F32 (NCHW tensors, fp32 weights and biases) or IS_F16 (NHWC
- *  tensors, fp16 weights, fp32 biases; every layer's output is stored as fp16,
- *  the page's "Reducing memory traffic" step; layer by layer only).
+ *  tensors, fp16 weights, fp32 biases; every layer's output is rounded to fp16
+ *  as the page's "Reducing memory traffic" step stores it). IS_F16 chains run
+ *  layer by layer, except that in IS_CHAIN_AUTO a first layer 1 -> 64 (3x3 or
+ *  5x5) followed by a 64 -> 64 3x3 layer runs as one launch in which the first
+ *  layer's fp16 output is computed where the second layer reads it and never
+ *  written to memory (IS_CHAIN_UNFUSED keeps one launch per layer).
  * Stencil pipelines: a fp32 chain whose layers all map one channel to one
  * (c = k = 1) and has no depth-to-space is an image-processing pipeline of
  * filters, the programs of the same arXiv 1909.07190. It runs in groups of 1
@@ -282,7 +286,9 @@ is_status conv_chain_forward_noalloc(const conv_chain_desc *d, const void *x,
 
 /* Name of the kernel family conv_chain_forward launches for this chain when
  * given the workspace conv_chain_workspace_size reports ("is_k3_chain" when
- * fused, "layer_by_layer" otherwise), copied into name[0..len-1]. */
+ * fused, "head_fused" for an fp16 chain whose first two layers run as one
+ * launch, "layer_by_layer" otherwise; stencil pipelines: see
+ * conv_chain_groups), copied into name[0..len-1]. */
 is_status conv_chain_kernel_name(const conv_chain_desc *d, char *name, size_t len);
 
 /* LDS bytes of an input tile that covers tile_w x tile_h outputs of a filter

@@ -9,6 +9,8 @@ of L layers is derived in tolerance.py (about L * 1.05e-3 * m). The 1280x720
 frame is compared in full and on windows the oracle evaluates exactly
 (chain_f16_window).
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -49,17 +51,48 @@ def _chain(x, layers, d2s, mode=isa.IS_CHAIN_AUTO):
 
 
 @pytest.mark.parametrize("N,H,W", [(1, 37, 70), (2, 20, 130), (1, 1, 1), (1, 66, 200), (1, 19, 77), (2, 35, 258),
-                                   (1, 70, 2)])
+                                   (1, 70, 2), (1, 120, 64)])
 def test_pages_net_small_frames(N, H, W):
+    """AUTO (the first two layers in one launch) and UNFUSED (one launch per
+    layer) against the oracle, and against each other bit for bit: both compute
+    the first layer with the same products and round it to fp16 the same way."""
     x, layers = synth.chain_f16_nhwc(N=N, H=H, W=W, seed=N * 1000 + H + W)
     spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
     d = isa.make_chain_desc(N, H, W, spec, 3, isa.IS_CHAIN_AUTO, "f16")
-    assert isa.conv_chain_kernel_name(d) == "layer_by_layer"
+    assert isa.conv_chain_kernel_name(d) == "head_fused"
     say("pages net", N, H, W)
     y = _chain(x, layers, 3)
+    yu = _chain(x, layers, 3, isa.IS_CHAIN_UNFUSED)
     ref, m = oracle.chain_f16(x, layers, d2s=3)
     assert y.shape == (N, 3 * H, 3 * W, 1)
     ratio = check(y, ref, m, tau_f16_chain(len(layers)), "pages net %dx%dx%d" % (N, H, W))
+    check(yu, ref, m, tau_f16_chain(len(layers)), "pages net unfused %dx%dx%d" % (N, H, W))
+    np.testing.assert_array_equal(y.view(np.uint16), yu.view(np.uint16))
+    say("max err/bound %.3g" % ratio)
+
+
+@pytest.mark.parametrize("r", [3, 5])
+@pytest.mark.parametrize("N,H,W,relu1,relu2,bias", [(1, 64, 32, True, True, True), (2, 37, 70, False, True, True),
+                                                    (1, 1, 1, True, False, False), (1, 120, 33, True, True, False),
+                                                    (1, 130, 96, False, False, True), (3, 9, 100, True, True, True)])
+def test_head_fused_pair(r, N, H, W, relu1, relu2, bias):
+    """Two layers, 1 -> 64 (r x r) and 64 -> 64 (3x3), in one launch: ragged
+    32-column and 64-row (and 60-row, H = 120) units, single pixels, batches,
+    either ReLU flag and no biases; against the oracle and against the two
+    launches of the unfused path."""
+    spec = ((1, 64, r, relu1), (64, 64, 3, relu2))
+    x, layers = synth.chain_f16_nhwc(N=N, H=H, W=W, spec=spec, seed=r * 100 + H + W)
+    if not bias:
+        layers = [(w, None, rl) for (w, _, rl) in layers]
+    d = isa.make_chain_desc(N, H, W, [(w.shape[1], w.shape[0], w.shape[2], rl) for (w, _, rl) in layers], 1,
+                            isa.IS_CHAIN_AUTO, "f16")
+    assert isa.conv_chain_kernel_name(d) == "head_fused"
+    say("head fused pair", r, N, H, W, relu1, relu2, bias)
+    y = _chain(x, layers, 1)
+    yu = _chain(x, layers, 1, isa.IS_CHAIN_UNFUSED)
+    ref, m = oracle.chain_f16(x, layers, d2s=1)
+    ratio = check(y, ref, m, tau_f16_chain(2), "head fused r%d %dx%dx%d" % (r, N, H, W))
+    np.testing.assert_array_equal(y.view(np.uint16), yu.view(np.uint16))
     say("max err/bound %.3g" % ratio)
 
 
@@ -83,15 +116,23 @@ def test_pages_net_1280x720_windows():
         check(got, ref, mref, tau, "pages net window %s" % ((i0, i1, j0, j1),))
 
 
-def test_pages_net_1280x720_full():
-    """The full frame: every pixel of the 3840x2160 output against the oracle's
+@pytest.mark.parametrize("mode", ["auto", "unfused"])
+def test_pages_net_1280x720_full(mode):
+    """The full frame, the first two layers in one launch (AUTO) and one launch
+    per layer: every pixel of the 3840x2160 output against the oracle's
     fp16-storage chain."""
     x, layers = synth.chain_f16_nhwc()
-    say("pages net 1280x720 full")
-    y = _chain(x, layers, 3)
-    ref, m = oracle.chain_f16(x, layers, d2s=3)
-    ratio = check(y, ref, m, tau_f16_chain(len(layers)), "pages net 1280x720 full")
+    say("pages net 1280x720 full", mode)
+    y = _chain(x, layers, 3, isa.IS_CHAIN_AUTO if mode == "auto" else isa.IS_CHAIN_UNFUSED)
+    ref, m = _pages_net_frame_oracle()
+    ratio = check(y, ref, m, tau_f16_chain(len(layers)), "pages net 1280x720 %s full" % mode)
     say("max err/bound %.3g" % ratio)
+
+
+@functools.lru_cache(maxsize=1)
+def _pages_net_frame_oracle():
+    x, layers = synth.chain_f16_nhwc()
+    return oracle.chain_f16(x, layers, d2s=3)
 
 
 def test_f16_chain_other_shapes():

@@ -111,13 +111,16 @@ def test_fused_fp32_chain_in_the_poison_build():
     check(got, ref, m, TAU_F32, "poison fused chain")
 
 
-def test_fp16_net_in_the_poison_build():
-    """The pages' net: first-layer kernel, three MFMA layers, the last with the
+@pytest.mark.parametrize("mode", ["auto", "unfused"])
+def test_fp16_net_in_the_poison_build(mode):
+    """The pages' net: the first two layers in one launch (AUTO: the first
+    layer's rows computed into the LDS ring) or the first-layer kernel and an
+    MFMA layer (UNFUSED), then two MFMA layers, the last with the
     depth-to-space in its stores."""
     import torch
     x, layers = synth.chain_f16_nhwc(N=1, H=33, W=70, seed=6)
     spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
-    d = isa.make_chain_desc(1, 33, 70, spec, 3, isa.IS_CHAIN_AUTO, "f16")
+    d = isa.make_chain_desc(1, 33, 70, spec, 3, isa.IS_CHAIN_AUTO if mode == "auto" else isa.IS_CHAIN_UNFUSED, "f16")
     ws_bytes = isa.conv_chain_workspace_size(d)
     y = torch.full((1, 99, 210, 1), float("nan"), dtype=torch.float16, device="cuda")
     got = _chain(d, x, layers, y, ws_bytes)

@@ -401,7 +401,21 @@ def test_f16_chain_descriptor_checks():
     spec = [(1, 64, 5, True), (64, 64, 3, True), (64, 32, 3, True), (32, 9, 3, False)]
     d = isa.make_chain_desc(1, 720, 1280, spec, 3, isa.IS_CHAIN_AUTO, "f16")
     assert isa.conv_chain_workspace_size(d) == 2 * 2 * 64 * 720 * 1280
-    assert isa.conv_chain_kernel_name(d) == "layer_by_layer"
+    # AUTO: the first two layers in one launch; UNFUSED: one launch per layer
+    assert isa.conv_chain_kernel_name(d) == "head_fused"
+    assert isa.conv_chain_groups(d) == [2, 1, 1]
+    du = isa.make_chain_desc(1, 720, 1280, spec, 3, isa.IS_CHAIN_UNFUSED, "f16")
+    assert isa.conv_chain_kernel_name(du) == "layer_by_layer"
+    assert isa.conv_chain_groups(du) == [1, 1, 1, 1]
+    assert isa.conv_chain_workspace_size(du) == isa.conv_chain_workspace_size(d)
+    # only a 1 -> 64 3x3 or 5x5 layer followed by 64 -> 64 3x3 is fused
+    for first, second in (((1, 64, 3, True), (64, 64, 3, True)), ((1, 64, 5, False), (64, 64, 3, False))):
+        assert isa.conv_chain_kernel_name(isa.make_chain_desc(1, 40, 64, [first, second], 1, isa.IS_CHAIN_AUTO,
+                                                              "f16")) == "head_fused"
+    for first, second in (((1, 32, 5, True), (32, 32, 3, True)), ((1, 64, 7, True), (64, 64, 3, True)),
+                          ((1, 64, 5, True), (64, 32, 3, True))):
+        assert isa.conv_chain_kernel_name(isa.make_chain_desc(1, 40, 64, [first, second], 1, isa.IS_CHAIN_AUTO,
+                                                              "f16")) == "layer_by_layer"
     assert round(traffic.chain_flops(1, 720, 1280, [t[:3] for t in spec]) / 1e9, 2) == 109.65
     for mode in (isa.IS_CHAIN_FUSED,):
         with pytest.raises(isa.ImgStencilError):
