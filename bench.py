@@ -961,6 +961,51 @@ def _mfma_reference(torch, stream_obj, min_s=0.3):
     return out
 
 
+def mfma_chain_study(torch, stream_obj, min_s=0.1):
+    """Sustained fp16 MFMA rate against the number of independent accumulators
+    per wave (1 .. 8) and waves per SIMD (1 or 2): how far apart dependent
+    matrix products must be to keep the matrix unit busy."""
+    import ctypes
+    lib = _probes(ctypes)
+    lib.isp_mfma_chain_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = []
+    for per_simd in (1, 2):
+        grid = per_simd * cus
+        waves = grid * 4
+        stamps = torch.zeros(2 * waves, dtype=torch.int64, device="cuda")
+        sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+        for chains in (1, 2, 3, 4, 6, 8):
+            iters = 2048 // per_simd
+
+            def launch():
+                rc = lib.isp_mfma_chain_rate(chains, grid, iters, stamps.data_ptr(), sink.data_ptr(),
+                                             stream_obj.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError("isp_mfma_chain_rate: hipError_t %d" % rc)
+
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < min_s:
+                launch()
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream_obj)
+            for _ in range(5):
+                launch()
+            e1.record(stream_obj)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 5
+            st = stamps.cpu().view(-1, 2).double()
+            clock = float(st[:, 0].sum() / st[:, 1].sum()) * 0.1
+            mfmas = waves * iters * 8
+            tflops = mfmas * 16384 / (ms / 1e3) / 1e12
+            out.append({"waves_per_simd": per_simd, "chains": chains, "tflops": round(tflops, 1),
+                        "clock_ghz": round(clock, 3),
+                        "cycles_per_mfma_per_simd": round(clock * 1e9 * ms / 1e3 / (mfmas / (cus * 4)), 2)})
+    return out
+
+
 def lds_bank_probe(torch, stream_obj, iters=4096):
     """Launch every LDS probe (access width x address pattern) once, one wave
     per CU, for a counter run of their bank conflicts (see probes.hip)."""
@@ -1353,6 +1398,8 @@ def main():
                     help="launch only the LDS bank probes (for a counter run) and exit")
     ap.add_argument("--pmc-lds-probe-summary", metavar="PMC_DIR",
                     help="print the summary of a rocprofv3 --pmc run of --lds-bank-probe and exit")
+    ap.add_argument("--mfma-chain-study", action="store_true",
+                    help="time back-to-back fp16 MFMAs against accumulator chains per wave and exit")
     ap.add_argument("--clock-study", metavar="OUT_JSON",
                     help="launch only the clock study kernels (for a counter run) and exit")
     ap.add_argument("--pmc-clock-summary", metavar="PMC_DIR",
@@ -1408,6 +1455,9 @@ def main():
     stream_obj = torch.cuda.current_stream()
     stream = stream_obj.cuda_stream
 
+    if args.mfma_chain_study:
+        print(json.dumps({"study": "mfma_chains", "results": mfma_chain_study(torch, stream_obj)}), flush=True)
+        return
     if args.clock_study:
         print(json.dumps({"study": "clock", **clock_study(torch, isa, synth, stream, stream_obj,
                                                            args.clock_study)}), flush=True)

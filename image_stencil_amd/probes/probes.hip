@@ -16,7 +16,7 @@ typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;   // 4 waves: one per SIMD of a CU
-constexpr int kChains = 8;      // independent accumulators per wave
+constexpr int kMaxChains = 8;   // independent accumulators per wave (at most)
 
 __device__ __forceinline__ unsigned hash32(unsigned v) {
   v ^= v >> 16;
@@ -34,7 +34,7 @@ __device__ __forceinline__ unsigned hash32(unsigned v) {
 // v_mfma_f32_16x16x32_f16 (16384 FLOP each); else v_mfma_f32_16x16x4_f32
 // (2048 FLOP each). Each wave's lane 0 records its shader-clock cycles
 // (s_memtime) and 100 MHz real-time ticks (s_memrealtime) over the loop.
-template <bool F16>
+template <bool F16, int kChains = 8>
 __global__ __launch_bounds__(kThreads) void isp_mfma_rate(int iters, unsigned long long *stamps, float *sink) {
   const int tid = threadIdx.x;
   const unsigned gid = blockIdx.x * kThreads + tid;
@@ -43,9 +43,9 @@ __global__ __launch_bounds__(kThreads) void isp_mfma_rate(int iters, unsigned lo
   for (int j = 0; j < kChains; ++j) acc[j] = float4v{0.f, 0.f, 0.f, 0.f};
   unsigned long long c0 = 0, r0 = 0;
   if constexpr (F16) {
-    half8 a[kChains], b[kChains];
+    half8 a[kMaxChains], b[kMaxChains];
 #pragma unroll
-    for (int j = 0; j < kChains; ++j)
+    for (int j = 0; j < kMaxChains; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         a[j][e] = (_Float16)((int)(hash32(gid * 64 + j * 8 + e) & 0xFFFF) / 32768.f - 1.f);
@@ -53,28 +53,33 @@ __global__ __launch_bounds__(kThreads) void isp_mfma_rate(int iters, unsigned lo
       }
     c0 = clock64();
     r0 = wall_clock64();
-    for (int i = 0; i < iters; i += kChains) {   // the host rounds iters to a multiple of kChains
+    // kMaxChains MFMAs per step in any case (the host's count), spread over
+    // kChains accumulators: each accumulator's next product depends on its
+    // previous one kChains instructions earlier.
+    for (int i = 0; i < iters; i += kMaxChains) {   // the host rounds iters to a multiple of 8
 #pragma unroll
-      for (int ii = 0; ii < kChains; ++ii)
+      for (int ii = 0; ii < kMaxChains; ++ii)
 #pragma unroll
-        for (int j = 0; j < kChains; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], b[(j + ii) % kChains], acc[j], 0, 0, 0);
+        for (int j = 0; j < kMaxChains; ++j)
+          acc[j % kChains] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], b[(j + ii) % kMaxChains],
+                                                                     acc[j % kChains], 0, 0, 0);
     }
   } else {
-    float a[kChains], b[kChains];
+    float a[kMaxChains], b[kMaxChains];
 #pragma unroll
-    for (int j = 0; j < kChains; ++j) {
+    for (int j = 0; j < kMaxChains; ++j) {
       a[j] = (int)(hash32(gid * 16 + j) & 0xFFFF) / 32768.f - 1.f;
       b[j] = (int)(hash32(gid * 16 + j + 0x9E3779B9u) & 0xFFFF) / 32768.f - 1.f;
     }
     c0 = clock64();
     r0 = wall_clock64();
-    for (int i = 0; i < iters; i += kChains) {
+    for (int i = 0; i < iters; i += kMaxChains) {
 #pragma unroll
-      for (int ii = 0; ii < kChains; ++ii)
+      for (int ii = 0; ii < kMaxChains; ++ii)
 #pragma unroll
-        for (int j = 0; j < kChains; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[(j + ii) % kChains], acc[j], 0, 0, 0);
+        for (int j = 0; j < kMaxChains; ++j)
+          acc[j % kChains] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[(j + ii) % kMaxChains],
+                                                                  acc[j % kChains], 0, 0, 0);
     }
   }
   const unsigned long long c1 = clock64(), r1 = wall_clock64();
@@ -233,10 +238,27 @@ extern "C" {
 // each). Returns a hipError_t.
 int isp_mfma_rate(int kind, int grid, int iters, unsigned long long *stamps, float *sink, hipStream_t s) {
   if (grid < 1 || iters < 1 || !stamps || !sink) return (int)hipErrorInvalidValue;
-  iters = (iters + kChains - 1) / kChains * kChains;
+  iters = (iters + kMaxChains - 1) / kMaxChains * kMaxChains;
   if (kind == 0) return (int)launch(isp_mfma_rate<true>, grid, kThreads, s, iters, stamps, sink);
   if (kind == 1) return (int)launch(isp_mfma_rate<false>, grid, kThreads, s, iters, stamps, sink);
   return (int)hipErrorInvalidValue;
+}
+
+// The fp16 rate with `chains` independent accumulators per wave (1, 2, 3, 4,
+// 6 or 8; 8 MFMAs per step in every case): how far apart dependent products
+// must be to keep the matrix unit busy.
+int isp_mfma_chain_rate(int chains, int grid, int iters, unsigned long long *stamps, float *sink, hipStream_t s) {
+  if (grid < 1 || iters < 1 || !stamps || !sink) return (int)hipErrorInvalidValue;
+  iters = (iters + kMaxChains - 1) / kMaxChains * kMaxChains;
+  switch (chains) {
+    case 1: return (int)launch(isp_mfma_rate<true, 1>, grid, kThreads, s, iters, stamps, sink);
+    case 2: return (int)launch(isp_mfma_rate<true, 2>, grid, kThreads, s, iters, stamps, sink);
+    case 3: return (int)launch(isp_mfma_rate<true, 3>, grid, kThreads, s, iters, stamps, sink);
+    case 4: return (int)launch(isp_mfma_rate<true, 4>, grid, kThreads, s, iters, stamps, sink);
+    case 6: return (int)launch(isp_mfma_rate<true, 6>, grid, kThreads, s, iters, stamps, sink);
+    case 8: return (int)launch(isp_mfma_rate<true, 8>, grid, kThreads, s, iters, stamps, sink);
+    default: return (int)hipErrorInvalidValue;
+  }
 }
 
 // LDS probe of access `op` and address pattern `pat` (see above): `grid`
