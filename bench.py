@@ -1006,6 +1006,90 @@ def mfma_chain_study(torch, stream_obj, min_s=0.1):
     return out
 
 
+def lds_rate_study(torch, stream_obj, iters=4096):
+    """LDS throughput per CU: conflict-free 16-byte reads, 16-byte writes and
+    8-byte reads by 4, 8 and 16 waves per CU (one workgroup per CU), in bytes
+    per shader clock from each wave's own cycle counter (the slowest wave of
+    the launch) and in TB/s over the whole chip from the launch time."""
+    import ctypes
+    lib = _probes(ctypes)
+    lib.isp_lds_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = []
+    for op, name, width in ((0, "read 16 B", 16), (1, "write 16 B", 16), (2, "read 8 B", 8)):
+        for waves in (4, 8, 16):
+            stamps = torch.zeros(2 * cus * waves, dtype=torch.int64, device="cuda")
+            sink = torch.empty(cus * waves * 64, dtype=torch.float32, device="cuda")
+
+            def launch():
+                rc = lib.isp_lds_rate(op, waves, cus, iters, stamps.data_ptr(), sink.data_ptr(),
+                                      stream_obj.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError("isp_lds_rate: hipError_t %d" % rc)
+
+            for _ in range(3):
+                launch()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream_obj)
+            for _ in range(5):
+                launch()
+            e1.record(stream_obj)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 5
+            st = stamps.cpu().view(-1, 2).double()
+            per_cu = waves * iters * 8 * 64 * width
+            clock = float(st[:, 0].sum() / st[:, 1].sum()) * 0.1
+            out.append({"access": name, "waves_per_cu": waves,
+                        "bytes_per_clock_per_cu": round(per_cu / float(st[:, 0].max()), 1),
+                        "clock_ghz": round(clock, 3),
+                        "chip_tb_s": round(per_cu * cus / (ms / 1e3) / 1e12, 2)})
+    return out
+
+
+MIX_PARTS = ((1, "lds_reads"), (2, "mfma"), (4, "row_writes"), (8, "barrier"), (16, "stores"), (32, "dma"))
+MIX_CASES = (2, 3, 7, 15, 10, 11, 31, 47, 63, 5, 61)
+
+
+def mix_study(torch, stream_obj, iters=512):
+    """The fp16 layer's instruction mix taken apart (probes.hip isp_mix_rate):
+    per combination of operand reads, MFMAs, finished-row writes, a barrier per
+    4-row stage, global stores and global-to-LDS loads, the launch time and the
+    matrix-core rate."""
+    import ctypes
+    lib = _probes(ctypes)
+    lib.isp_mix_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    gbuf = torch.zeros(cus * 65536, dtype=torch.uint8, device="cuda")
+    stamps = torch.zeros(2 * cus * 8, dtype=torch.int64, device="cuda")
+    sink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    out = []
+    for mix in MIX_CASES:
+        def launch():
+            rc = lib.isp_mix_rate(mix, cus, iters, stamps.data_ptr(), sink.data_ptr(), gbuf.data_ptr(),
+                                  stream_obj.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("isp_mix_rate: hipError_t %d" % rc)
+
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream_obj)
+        for _ in range(5):
+            launch()
+        e1.record(stream_obj)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        row = {"parts": "+".join(n for (b, n) in MIX_PARTS if mix & b), "ms": round(ms, 4)}
+        if mix & 2:
+            row["pflops"] = round(cus * 8 * iters * 72 * 16384 / (ms / 1e3) / 1e15, 3)
+        out.append(row)
+    return out
+
+
 def lds_bank_probe(torch, stream_obj, iters=4096):
     """Launch every LDS probe (access width x address pattern) once, one wave
     per CU, for a counter run of their bank conflicts (see probes.hip)."""
@@ -1398,6 +1482,10 @@ def main():
                     help="launch only the LDS bank probes (for a counter run) and exit")
     ap.add_argument("--pmc-lds-probe-summary", metavar="PMC_DIR",
                     help="print the summary of a rocprofv3 --pmc run of --lds-bank-probe and exit")
+    ap.add_argument("--mix-study", action="store_true",
+                    help="time the fp16 layer's instruction mix part by part and exit")
+    ap.add_argument("--lds-rate-study", action="store_true",
+                    help="time conflict-free LDS reads and writes per CU and exit")
     ap.add_argument("--mfma-chain-study", action="store_true",
                     help="time back-to-back fp16 MFMAs against accumulator chains per wave and exit")
     ap.add_argument("--clock-study", metavar="OUT_JSON",
@@ -1455,6 +1543,12 @@ def main():
     stream_obj = torch.cuda.current_stream()
     stream = stream_obj.cuda_stream
 
+    if args.mix_study:
+        print(json.dumps({"study": "mix", "results": mix_study(torch, stream_obj)}), flush=True)
+        return
+    if args.lds_rate_study:
+        print(json.dumps({"study": "lds_rate", "results": lds_rate_study(torch, stream_obj)}), flush=True)
+        return
     if args.mfma_chain_study:
         print(json.dumps({"study": "mfma_chains", "results": mfma_chain_study(torch, stream_obj)}), flush=True)
         return

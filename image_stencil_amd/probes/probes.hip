@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -25,6 +27,15 @@ __device__ __forceinline__ unsigned hash32(unsigned v) {
   v *= 0x846ca68bU;
   v ^= v >> 16;
   return v;
+}
+
+template <typename Fn, int... I>
+__device__ __forceinline__ void static_for_seq(Fn &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <typename Fn>
+__device__ __forceinline__ void static_for_steps(Fn &&f) {
+  static_for_seq(f, std::make_integer_sequence<int, 24>{});
 }
 
 // Back-to-back MFMAs: every wave issues kChains independent accumulations per
@@ -228,6 +239,153 @@ hipError_t launch(void (*k)(KArgs...), int grid, int block, hipStream_t s, Args.
   return hipGetLastError();
 }
 
+// LDS throughput: one workgroup of `waves` waves per CU; every wave issues
+// steps of 8 independent, conflict-free accesses (each wave 8 whole 64-lane
+// blocks of its own; OP 0 read 16 B, 1 write 16 B, 2 read 8 B) for `iters`
+// steps. Lane 0 of each wave records its cycles and real-time ticks over the
+// loop, as the MFMA probe does.
+constexpr int kRateLdsBytes = 64 * 1024;
+
+template <int OP>
+__global__ __launch_bounds__(1024) void isp_lds_rate(int iters, unsigned long long *stamps, float *sink) {
+  __shared__ __attribute__((aligned(16))) char lds[kRateLdsBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  constexpr int WIDTH = (OP == 2) ? 8 : 16;
+  for (int i = tid; i < kRateLdsBytes / 4; i += blockDim.x) reinterpret_cast<float *>(lds)[i] = (float)i;
+  __syncthreads();
+  uint4v acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = uint4v{0u, 0u, 0u, 0u};
+  const unsigned long long c0 = clock64(), r0 = wall_clock64();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // 64 x WIDTH bytes per block; blocks wrap within the 64 KB array
+      const int addr = ((wave * 8 + j) * 64 * WIDTH + lane * WIDTH) & (kRateLdsBytes - 1);
+      if constexpr (OP == 0) {
+        acc[j] ^= *reinterpret_cast<const uint4v *>(lds + addr);
+      } else if constexpr (OP == 1) {
+        *reinterpret_cast<uint4v *>(lds + addr) = uint4v{(unsigned)i, (unsigned)lane, (unsigned)j, 1u};
+      } else {
+        const uint2v v = *reinterpret_cast<const uint2v *>(lds + addr);
+        acc[j].x ^= v.x;
+        acc[j].y ^= v.y;
+      }
+    }
+    __asm__ volatile("" ::: "memory");
+  }
+  const unsigned long long c1 = clock64(), r1 = wall_clock64();
+  __syncthreads();
+  unsigned x = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x ^= acc[j].x ^ acc[j].y ^ acc[j].z ^ acc[j].w;
+  sink[blockIdx.x * blockDim.x + tid] = (float)x + lds[(tid * 16) % kRateLdsBytes];
+  if (lane == 0) {
+    const unsigned gw = blockIdx.x * (blockDim.x >> 6) + wave;
+    stamps[2 * gw] = c1 - c0;
+    stamps[2 * gw + 1] = r1 - r0;
+  }
+}
+
+// The fp16 layer's instruction mix, piece by piece: 8 waves per CU (2 per
+// SIMD), each holding 18 A fragments in registers and stepping through 24
+// operand slots of 1 KB per round (a stage of 4 input rows x 3 tap columns x
+// 2 channel halves): every step reads the operand 8 steps ahead from LDS into a
+// register ring and issues 3 v_mfma_f32_16x16x32_f16 that use the current one,
+// into 3 of 4 rotating accumulators; every 6 steps one accumulator is finished
+// (fp16, 8 bytes per lane). MIX bits switch the parts on: 1 the LDS operand
+// reads (else the ring keeps its first values), 2 the MFMAs (else one VALU add
+// per product), 4 the finished rows' LDS writes, 8 a workgroup barrier (LDS
+// drained) per round, 16 two 16-byte global stores per wave per round, 32 three
+// 16-byte global-to-LDS loads per wave per round (waited for before the
+// barrier). gbuf holds 64 KB per workgroup; LDS addresses stay below 128 KB.
+constexpr int kMixLdsBytes = 128 * 1024;
+constexpr int kMixSteps = 24;
+
+template <int MIX>
+__global__ __launch_bounds__(512, 1) void isp_mix_rate(int iters, unsigned long long *stamps, float *sink,
+                                                       char *gbuf) {
+  __shared__ __attribute__((aligned(16))) char lds[kMixLdsBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(gbuf + (size_t)blockIdx.x * 65536, (short)0, 65536, 0x00020000);
+  for (int i = tid; i < kMixLdsBytes / 4; i += blockDim.x)
+    reinterpret_cast<float *>(lds)[i] = (float)(i & 255) * (1.f / 256);
+  __syncthreads();
+  half8 wa[18];
+#pragma unroll
+  for (int k = 0; k < 18; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wa[k][e] = (_Float16)((int)(hash32(tid * 256 + k * 8 + e) & 255) / 256.f);
+  // Waves 0, 2, 4, 6 and 1, 3, 5, 7 read the same 24 KB (the four output-channel
+  // waves of a pixel block share their operand rows in the layer).
+  const int rbase = (wave & 1) * kMixSteps * 1024 + lane * 16;   // < 48 KB + 24 KB
+  const int wbase = 64 * 1024 + wave * 4096 + lane * 8;          // < 96 KB
+  half8 ring[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) ring[q] = *reinterpret_cast<const half8 *>(lds + rbase + q * 1024);
+  float4v acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = float4v{0.f, 0.f, 0.f, 0.f};
+  const unsigned long long c0 = clock64(), r0 = wall_clock64();
+  for (int it = 0; it < iters; ++it) {
+    static_for_steps([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      if constexpr ((MIX & 16) && (q == 2 || q == 14))
+        __builtin_amdgcn_raw_buffer_store_b128(uint4v{(unsigned)it, (unsigned)lane, (unsigned)q, 1u}, rs,
+                                               (wave * 2 + q / 12) * 1024 + lane * 16, 0, 2);
+      if constexpr ((MIX & 32) && (q == 3 || q == 11 || q == 19))
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void *)(lds + 96 * 1024 + (wave * 3 + q / 8) * 1024), 16,
+            32768 + (wave * 3 + q / 8) * 1024 + lane * 16, 0, 0, 2);
+      const half8 b = ring[q % 8];
+      if constexpr (MIX & 1)   // moving by 16 bytes a round keeps the reads conflict-free and live
+        ring[q % 8] = *reinterpret_cast<const half8 *>(lds + rbase + ((q + 8) % kMixSteps) * 1024 + (it & 7) * 16);
+      constexpr int i = q / 6, v = (q % 6) / 2, h = q % 2;
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int ks = 2 * (3 * u + v) + h;
+        if constexpr (MIX & 2)
+          acc[(i - u) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[ks], b, acc[(i - u) & 3], 0, 0, 0);
+        else
+          acc[(i - u) & 3][0] += (float)b[0];
+      }
+      if constexpr (q % 6 == 5) {
+        _Float16 hv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(acc[(i - 2) & 3][e] + 0.5f);
+        acc[(i - 2) & 3] = float4v{0.f, 0.f, 0.f, 0.f};
+        if constexpr (MIX & 4)
+          *reinterpret_cast<uint2v *>(lds + wbase + i * 512 + (it & 1) * 2048) = __builtin_bit_cast(uint2v, hv);
+        else
+          acc[(i + 1) & 3][1] += (float)hv[0] + (float)hv[3];
+      }
+    });
+    __asm__ volatile("" ::: "memory");
+    if constexpr (MIX & 8) {
+      if constexpr (MIX & 32) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: the loads have landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);                            // lgkmcnt 0
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+    }
+  }
+  const unsigned long long c1 = clock64(), r1 = wall_clock64();
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s += (float)ring[q][0];
+  __syncthreads();
+  sink[blockIdx.x * blockDim.x + tid] = s + lds[(tid * 16) % kMixLdsBytes];
+  if (lane == 0) {
+    const unsigned gw = blockIdx.x * 8 + wave;
+    stamps[2 * gw] = c1 - c0;
+    stamps[2 * gw + 1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -290,6 +448,34 @@ int isp_lds_stride_probe(int op, int group, int stride, int offset, int grid, in
     case 1: return (int)launch(isp_lds_stride_probe<1>, grid, 64, s, group, stride, offset, iters, sink);
     case 2: return (int)launch(isp_lds_stride_probe<2>, grid, 64, s, group, stride, offset, iters, sink);
     case 3: return (int)launch(isp_lds_stride_probe<3>, grid, 64, s, group, stride, offset, iters, sink);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+// LDS throughput probe (see above): `grid` workgroups of `waves` waves (4, 8
+// or 16); stamps holds 2 x grid x waves values, sink grid x waves x 64 floats.
+int isp_lds_rate(int op, int waves, int grid, int iters, unsigned long long *stamps, float *sink, hipStream_t s) {
+  if (grid < 1 || iters < 1 || !stamps || !sink || (waves != 4 && waves != 8 && waves != 16))
+    return (int)hipErrorInvalidValue;
+  switch (op) {
+    case 0: return (int)launch(isp_lds_rate<0>, grid, 64 * waves, s, iters, stamps, sink);
+    case 1: return (int)launch(isp_lds_rate<1>, grid, 64 * waves, s, iters, stamps, sink);
+    case 2: return (int)launch(isp_lds_rate<2>, grid, 64 * waves, s, iters, stamps, sink);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+// Instruction-mix probe (see above): `grid` workgroups of 8 waves; mix is an
+// OR of the part bits (1 .. 63); stamps holds 2 x grid x 8 values, sink
+// grid x 512 floats, gbuf grid x 64 KB.
+int isp_mix_rate(int mix, int grid, int iters, unsigned long long *stamps, float *sink, char *gbuf, hipStream_t s) {
+  if (grid < 1 || iters < 1 || !stamps || !sink || !gbuf) return (int)hipErrorInvalidValue;
+  switch (mix) {
+#define ISP_MIX(M) \
+  case M: return (int)launch(isp_mix_rate<M>, grid, 512, s, iters, stamps, sink, gbuf);
+    ISP_MIX(2) ISP_MIX(3) ISP_MIX(7) ISP_MIX(10) ISP_MIX(11) ISP_MIX(15) ISP_MIX(31) ISP_MIX(47) ISP_MIX(63)
+    ISP_MIX(5) ISP_MIX(61)
+#undef ISP_MIX
     default: return (int)hipErrorInvalidValue;
   }
 }
