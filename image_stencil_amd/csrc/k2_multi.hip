@@ -36,7 +36,8 @@ constexpr int kNonTemporalStore = 2;
 constexpr int kTW = 64;              // output columns per tile (16 lanes x 4)
 constexpr int kTH = 16;              // output rows per tile (4 waves x 4 rows)
 constexpr int kThreads = 256;
-constexpr int kG = kTW / 4 + 2;      // 16-byte groups per LDS row: x0-4 .. x0+TW+3
+constexpr int kG = kTW / 4 + 2;      // 16-byte groups per staged row: x0-4 .. x0+TW+3
+constexpr int kMainG = kTW / 4;      // the tile's own groups, x0 .. x0+TW-1 (256 bytes)
 constexpr unsigned kOob = 0xFFFFFFF0u;   // byte offset past any buffer: reads 0
 
 constexpr int kDppRowShr1 = 0x111;   // lane reads lane-1 inside its row of 16
@@ -56,6 +57,12 @@ struct Geo {
   static constexpr int P = (R - 1) / 2;
   static constexpr int LH = kTH + R - 1;                 // staged rows
   static constexpr int V4 = CS * LH * kG;                // 16-byte vectors per slab
+  // Slab layout in LDS: first every staged row's 16 own groups (rows 256 bytes
+  // apart), then every row's 2 halo groups (left, right). A read takes 4 rows x
+  // 16 lanes of consecutive groups; gfx950 serves such a read without bank
+  // conflicts only when its rows lie a multiple of 256 bytes apart (rows of
+  // 18 groups, 288 bytes apart, measured 2-way conflicts).
+  static constexpr int MAINV4 = CS * LH * kMainG;
   static constexpr int CHUNKS = (V4 + 63) / 64;          // wave-sized DMA chunks
   static constexpr int ROUNDS = (CHUNKS + 3) / 4;        // chunks per wave (4 waves)
   static constexpr int PADV4 = ROUNDS * 4 * 64;          // LDS vectors per buffer
@@ -111,10 +118,19 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi(const float *__restrict_
 #pragma unroll
   for (int j = 0; j < G::ROUNDS; ++j) {
     const int q = (j * 4 + wave) * 64 + lane;
-    const int c = q / (G::LH * kG);
-    const int rem = q - c * (G::LH * kG);
-    const int lrow = rem / kG;
-    const int g = rem - lrow * kG;
+    int c, lrow, g;
+    if (q < G::MAINV4) {
+      c = q / (G::LH * kMainG);
+      const int rem = q - c * (G::LH * kMainG);
+      lrow = rem / kMainG;
+      g = 1 + rem - lrow * kMainG;
+    } else {
+      const int h = q - G::MAINV4;
+      c = h / (G::LH * 2);
+      const int rem = h - c * (G::LH * 2);
+      lrow = rem / 2;
+      g = (rem & 1) ? kG - 1 : 0;
+    }
     const int gy = y0 - P + lrow;
     const int gx = x0 - 4 + 4 * g;
     const bool in = q < G::V4 && gy >= 0 && gy < H && gx >= 0 && gx < W;
@@ -142,8 +158,7 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi(const float *__restrict_
   // LDS vector indices of this lane's 16-byte input vector and of the halo
   // vector it may need (lc 0: left of the tile; lc 15: right; others share
   // lane 0's address so the read is a broadcast).
-  const int own_g = lc + 1;
-  const int halo_g = lc == 15 ? kG - 1 : 0;
+  const int halo_g = lc == 15 ? 1 : 0;
 
   // One input channel: its R row windows in VGPRs, then every output channel f
   // in turn with its R*R taps in SGPRs. The taps of channel f+2 are requested
@@ -157,9 +172,9 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi(const float *__restrict_
     auto read_raw = [&](int c, int b) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < R; ++u) {
-        const int base = (c * G::LH + row0 + u) * kG;
-        raw_o[b][u] = bf[base + own_g];
-        if constexpr (P > 0) raw_h[b][u] = bf[base + halo_g];
+        const int crow = c * G::LH + row0 + u;
+        raw_o[b][u] = bf[crow * kMainG + lc];
+        if constexpr (P > 0) raw_h[b][u] = bf[G::MAINV4 + crow * 2 + halo_g];
       }
     };
     read_raw(0, 0);

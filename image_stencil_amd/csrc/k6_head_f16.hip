@@ -62,14 +62,25 @@ __device__ constexpr int a_row_channel(int ob, int m) {
   }
 }
 
+// LDS row pitch (fp16 elements) of the staged tile. A B-fragment gather reads,
+// for one tap slot j, 16 consecutive pixels of each of the 4 lane groups g at
+// taps 8g + j, i.e. 4 rows of the tile; with rows LW = 64 + R - 1 apart those 4
+// runs of 8 banks overlap (up to 3 distinct dwords per bank for R = 5, 2 for
+// R = 3, counting 64 banks of 4 bytes). Pitches of 136 (R = 3) and 142 (R = 5)
+// elements put the 4 runs on disjoint banks for every j and every wave.
+constexpr int tile_pitch(int R) { return R == 3 ? 136 : (R == 5 ? 142 : kTW + R - 1); }
+
 template <int R>
 struct TileGeo {
   static constexpr int P = (R - 1) / 2;
-  static constexpr int LW = kTW + R - 1;
-  static constexpr int LH = kTH + R - 1;
+  static constexpr int LW = kTW + R - 1;          // staged columns
+  static constexpr int LH = kTH + R - 1;          // staged rows
+  static constexpr int LWP = tile_pitch(R);       // LDS row pitch
+  static_assert(LWP >= LW, "rows fit their pitch");
   static constexpr int ELEMS = LH * LW;
   static constexpr int NLD = (ELEMS + kThreads - 1) / kThreads;
-  static constexpr int SLOTS = NLD * kThreads;   // LDS elements per buffer
+  static constexpr int DUMMY = LH * LWP;          // where the past-the-tile load slots write
+  static constexpr int SLOTS = DUMMY + 2;         // LDS elements per buffer
 };
 
 // Issues the loads of tile t's input (with halo) into v; out-of-image and
@@ -152,14 +163,23 @@ __global__ __launch_bounds__(kThreads) void is_k6_head_f16(HeadArgs a) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int k = 8 * g + j;
-    toff[j] = k < R * R ? (k / R) * G::LW + 16 * wave + n16 + k % R : 0;
+    toff[j] = k < R * R ? (k / R) * G::LWP + 16 * wave + n16 + k % R : 0;
+  }
+  // LDS position of each of this thread's load slots (element e of the tile,
+  // row-major with LW columns, at its row's pitch; slots past the tile write a
+  // spare element).
+  int spos[G::NLD];
+#pragma unroll
+  for (int q = 0; q < G::NLD; ++q) {
+    const int e = tid + q * kThreads;
+    spos[q] = e < G::ELEMS ? (e / G::LW) * G::LWP + e % G::LW : G::DUMMY;
   }
   const size_t plane = (size_t)a.H * a.W;
 
   for (int buf = 0; t < a.ntiles; t += gridDim.x, buf ^= 1) {
 #pragma unroll
     for (int q = 0; q < G::NLD; ++q)
-      tile[buf][tid + q * kThreads] = __builtin_bit_cast(_Float16, (unsigned short)ld[q]);
+      tile[buf][spos[q]] = __builtin_bit_cast(_Float16, (unsigned short)ld[q]);
     __syncthreads();
     load_tile<R>(a, t + (int)gridDim.x, tid, ld);
 
@@ -179,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void is_k6_head_f16(HeadArgs a) {
       half8 b;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const _Float16 v = tb[toff[j] + r * G::LW];
+        const _Float16 v = tb[toff[j] + r * G::LWP];
         b[j] = (8 * g + j < R * R) ? v : (_Float16)0.f;
       }
       const int gy = ty * kTH + r;
@@ -247,8 +267,7 @@ bool configure_head_f16(Plan &p) {
   p.grid_x = (int)(tiles < kCus * kWgPerCu ? tiles : kCus * kWgPerCu);
   p.grid_y = p.grid_z = 1;
   p.block = kThreads;
-  const int elems = (kTH + d.r - 1) * (kTW + d.r - 1);
-  p.lds = 2 * ((elems + kThreads - 1) / kThreads) * kThreads * 2;
+  p.lds = 2 * ((kTH + d.r - 1) * tile_pitch(d.r) + 2) * 2;
   p.tile_w = kTW;
   p.tile_h = kTH;
   return true;
