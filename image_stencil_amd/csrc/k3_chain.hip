@@ -59,10 +59,22 @@ __device__ __forceinline__ float row_next(float src, float old) {
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 // Intermediate rings hold, per row slot and channel, the 64 window columns as
-// 16 float4 vectors; odd channels are stored rotated by 4 vectors (16 floats)
-// so that the two channels read by one 32-lane half of an MFMA operand load
-// land on disjoint halves of the 32 LDS banks. Vector lc of channel c:
-__device__ __forceinline__ int rot4(int c, int lc) { return (lc + 4 * (c & 1)) & 15; }
+// 16 float4 vectors (one channel row = 256 bytes = the 64 LDS banks of 4
+// bytes); channel c is stored rotated by 4 * (c mod 4) vectors (16 floats) so
+// that the four channels of a quad, which one MFMA operand load reads 16
+// floats each, land on four disjoint quarters of the banks. Vector lc of
+// channel c:
+__device__ __forceinline__ int rot4(int c, int lc) { return (lc + 4 * (c & 3)) & 15; }
+
+// The input ring: per row slot, the window's own 16 vectors (x0 .. x0+63,
+// rows 256 bytes apart, so that the 4 rows of a read are served without bank
+// conflicts) and, after all of those, the slot's 2 halo vectors (x0-4 .. x0-1
+// and x0+64 .. x0+67). Vector g of slot s, g = 0 .. kInG-1 counting from x0-4:
+constexpr int kInMain = kWin / 4;
+constexpr int kInHaloBase = kInRing * kInMain;
+__device__ __forceinline__ int in_idx(int s, int g) {
+  return (g >= 1 && g <= kInMain) ? s * kInMain + g - 1 : kInHaloBase + 2 * s + (g != 0);
+}
 
 struct ChainArgs {
   const float *x;
@@ -157,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void is_k3_chain(ChainArgs a) {
   auto in_slot = [&](int r) { return (r - t0 - 1) % kInRing; };
 
   // Input rows t0+1 .. t0+8 before the first step.
-  for (int q = tid; q < 8 * kInG; q += kThreads) in_ring[q] = ld4(rx, in_off(t0 + 1, q));
+  for (int q = tid; q < 8 * kInG; q += kThreads) in_ring[in_idx(q / kInG, q % kInG)] = ld4(rx, in_off(t0 + 1, q));
 
   // MFMA layers: lane (g4, n16) holds, for filter tap t and channel quad cq,
   // the weight of output channel 16*mob + n16 and input channel 4*cq + g4.
@@ -198,9 +210,9 @@ __global__ __launch_bounds__(kThreads) void is_k3_chain(ChainArgs a) {
         for (int p = 0; p < 4; ++p) acc[f][p] = 0.f;
 #pragma unroll
       for (int u = 0; u < 5; ++u) {
-        const float4 *rp = in_ring + in_slot(row + u - 2) * kInG;
-        const float4 o = rp[lc + 1];
-        const float4 h = rp[lc == 15 ? kInG - 1 : 0];
+        const int rs = in_slot(row + u - 2);
+        const float4 o = in_ring[in_idx(rs, lc + 1)];
+        const float4 h = in_ring[in_idx(rs, lc == 15 ? kInG - 1 : 0)];
         float win[8];
         win[2] = o.x; win[3] = o.y; win[4] = o.z; win[5] = o.w;
         win[1] = row_prev(o.w, h.w);
@@ -270,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void is_k3_chain(ChainArgs a) {
 #pragma unroll
           for (int v = 0; v < 3; ++v)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) aoff[u][v][cb] = base + ((16 * cb + n16 + v - 1 + 16 * (g4 & 1)) & 63);
+            for (int cb = 0; cb < 4; ++cb) aoff[u][v][cb] = base + ((16 * cb + n16 + v - 1 + 16 * g4) & 63);
         }
         constexpr int kSteps = 9 * (kCh / 4) * 4;   // (tap, channel quad, column block)
         constexpr int kAhead = 16;
@@ -365,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void is_k3_chain(ChainArgs a) {
       }
     }
 
-    if (do_pre) in_ring[in_slot(t + 9) * kInG + tid] = pre;
+    if (do_pre) in_ring[in_idx(in_slot(t + 9) + tid / kInG, tid % kInG)] = pre;
     __syncthreads();
   }
 }
