@@ -4,12 +4,9 @@
 // Kernels on Kepler GPUs" (arXiv 1705.10591), sections "thread layout" (3.1) and
 // "memory access schedule" with its Algorithm 1, rebuilt for a CDNA wave64:
 //  * a wave owns a strip of 256 columns x `strip_rows` rows (the page's H x W
-//    image block; its best block was 256 wide) and sweeps it one input row per
-//    step, so every input pixel is fetched from HBM once plus a thin halo (the
-//    page's communication-optimal global reads). Even strips sweep top to
-//    bottom, odd strips bottom to top: two strips that share halo rows then
-//    read them at the same time (both at their start, or both at their end),
-//    so the second read hits in L2 instead of going back to HBM;
+//    image block; its best block was 256 wide) and sweeps it top to bottom, one
+//    input row per step, so every input pixel is fetched from HBM once plus a
+//    thin halo (the page's communication-optimal global reads);
 //  * each lane keeps 4 contiguous columns, read and written as one 16-byte
 //    access (the page's n pixels per thread, with n matched to the access width);
 //  * horizontal sharing: the page stages each row in shared memory so that
@@ -41,14 +38,18 @@ namespace is {
 namespace {
 
 constexpr int kSegCols = 4 * kWave;   // 256 output columns per wave
-// Cache policy: the output is written once, so its stores are non-temporal.
-// The image loads are not: the lines a wave loads hold the halo columns that
-// the neighbouring segments' waves fetch soon after, and a non-temporal load
-// lets L2 drop them first. Measured by FETCH_SIZE on 8192x8192: 276-278 MiB
-// for the 256 MiB image with non-temporal loads, 258-260 MiB without, and
-// 3-5% less time.
+// Cache policy. The output is written once: non-temporal stores. The image
+// loads of a filter with halo columns (S > 1) keep their lines: those lines
+// hold the halo columns that the waves of the neighbouring segments load soon
+// after, and a non-temporal load lets L2 drop them first. Measured on
+// 8192x8192, the five filter cases launched in turn in one process (two
+// builds interleaved): FETCH_SIZE 276-278 MiB for the 256 MiB image with
+// non-temporal loads and 258-275 MiB without; 3x3 101.5 -> 96.0 us, 5x5
+// 110.7 -> 100.1, 7x7 124.1 -> 105.9, separable 7x7 113.8 -> 98.0. A 1x1
+// filter has no halo: its loads stay non-temporal (97.3 against 99.6 us).
 constexpr int kNonTemporal = 2;
-constexpr int kLoadPolicy = 0;
+template <int Q>
+constexpr int load_policy() { return Q > 0 ? 0 : kNonTemporal; }
 
 template <int R, int F>
 struct Unroll {   // rows per unrolled step: a multiple of R (ring slots are static)
@@ -92,7 +93,7 @@ __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, int off_m, i
                                          Halo<Q> &h) {
   if constexpr (VEC) {
     const float4 a =
-        __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off_m, 0, kLoadPolicy));
+        __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off_m, 0, load_policy<Q>()));
     m.v[0] = a.x; m.v[1] = a.y; m.v[2] = a.z; m.v[3] = a.w;
   } else {
 #pragma unroll
@@ -104,7 +105,7 @@ __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, int off_m, i
   // wider load leaves a dead destination register.
 #pragma unroll
   for (int i = 0; i < Q; ++i)
-    h.v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off_h + 4 * i, 0, kLoadPolicy));
+    h.v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off_h + 4 * i, 0, load_policy<Q>()));
 }
 
 template <int R, int S, bool VEC, bool RELU, bool SEP, int F>
@@ -138,37 +139,17 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
   const int off_m = 4 * col;
   const int off_h = lane == 0 ? 4 * (x0 - Q) : (lane == kWave - 1 ? 4 * (x0 + kSegCols) : INT_MIN);
 
-  // Sweep direction: step r reads input row t_first + t_step * r and completes
-  // output row o_first + t_step * (r - 2P). A bottom-up sweep is the top-down
-  // one on the vertically mirrored image with the mirrored filter, so it loads
-  // the filter rows in reverse order and runs the same loop.
-  const bool up = (strip & 1) != 0;
-  const int t_step = up ? -1 : 1;
-  const int t_first = up ? y0 + rows_out - 1 + P : y0 - P;
-  const int o_first = up ? y0 + rows_out - 1 : y0;
-
   // Taps: F*R*S filter values (filter f's at f*R*S), or (SEP) R column taps
-  // then S row taps; filter rows (column taps) reversed when sweeping up.
+  // then S row taps.
   constexpr int NTAPS = SEP ? R + S : F * R * S;
   float wr[NTAPS];
 #pragma unroll
-  for (int i = 0; i < NTAPS; ++i) {
-    int src = i;
-    if constexpr (SEP) {
-      if (i < R) src = up ? R - 1 - i : i;
-    } else {
-      const int f = i / (R * S), u = (i / S) % R, v = i % S;
-      src = (f * R + (up ? R - 1 - u : u)) * S + v;
-    }
-    wr[i] = w[src];
-  }
+  for (int i = 0; i < NTAPS; ++i) wr[i] = w[i];
   float bv[F];
 #pragma unroll
   for (int f = 0; f < F; ++f) bv[f] = bias ? bias[f] : 0.f;
 
-  // Input rows this strip needs: y0-P .. y0+rows_out-1+P, clipped to the image;
-  // steps past the strip's rows (the last block's tail) read zeros.
-  const int in_lo = max(0, y0 - P);
+  // Input rows this strip needs: y0-P .. y0+rows_out-1+P, clipped to the image.
   const int in_hi = min(H, y0 + rows_out + P);
 
   // Prologue loads in row order (kept so by the scheduling barriers): the row
@@ -178,12 +159,13 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
   Halo<Q> ph[U];
 #pragma unroll
   for (int i = 0; i < U; ++i) {
-    load_row<VEC, Q>(row_rsrc(xp, t_first + t_step * i, in_lo, in_hi, W), off_m, off_h, pf[i], ph[i]);
+    load_row<VEC, Q>(row_rsrc(xp, y0 - P + i, 0, in_hi, W), off_m, off_h, pf[i], ph[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
 
   // acc[f][slot]: filter f's ring of the R output rows that the current input
-  // row touches; the output row completed at step r' lives in slot r' mod R.
+  // row touches; output row o (relative ro = o - y0) lives in slot
+  // (ro + 2P) mod R.
   float acc[F][R][4];
 #pragma unroll
   for (int f = 0; f < F; ++f)
@@ -232,15 +214,13 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
         }
       }
 
-      // The input row of step r feeds the output rows of steps r-2P+j (output
-      // rows counted in the sweep direction from the strip's first), j = 0..R-1,
-      // with filter row R-1-j of the (direction-ordered) taps. j = R-1 is the
-      // first contribution to its output row: it starts that slot with
-      // product + bias instead of clearing it.
+      // Input row r feeds relative output rows r-2P+j, j = 0..R-1, with
+      // filter row R-1-j. j = R-1 is the first contribution to output row r:
+      // it starts that slot with product + bias instead of clearing it.
 #pragma unroll
       for (int j = 0; j < R; ++j) {
-        // Output row r-2P+j lies before the strip's first when FIRST and
-        // p + j < 2P, past its last when LAST (r = NT-U+p) and p + j >= U.
+        // Output row r-2P+j: above the strip when FIRST and p + j < 2P, below
+        // it when LAST (r = NT-U+p) and p + j >= U.
         if ((FIRST && p + j < 2 * P) || (LAST && p + j >= U)) continue;
         const int slot = (p + j) % R;
         const int u = R - 1 - j;
@@ -262,7 +242,7 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
                                     : __builtin_fmaf(wr[(f * R + u) * S + v], win[i + v], acc[f][slot][i]);
       }
 
-      // Output row r-2P of the sweep (slot p mod R) is complete (the bias entered with its
+      // Output row r-2P (slot p mod R) is complete (the bias entered with its
       // first product); it is stored, in each of the F planes, only when it
       // lies inside the strip.
 #pragma unroll
@@ -273,8 +253,7 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
           o[i] = acc[f][p % R][i];
           if constexpr (RELU) o[i] = fmaxf(o[i], 0.f);
         }
-        const __amdgpu_buffer_rsrc_t rs_o =
-            row_rsrc(yp + (size_t)f * plane, o_first + t_step * (r - 2 * P), y0, y0 + rows_out, W);
+        const __amdgpu_buffer_rsrc_t rs_o = row_rsrc(yp + (size_t)f * plane, y0 + r - 2 * P, y0, y0 + rows_out, W);
         if constexpr (VEC) {
           __builtin_amdgcn_raw_buffer_store_b128(
               __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
@@ -291,7 +270,7 @@ __global__ __launch_bounds__(kWave) void is_k1_single(const float *__restrict__ 
       // (the scheduling barrier keeps the load after the row's last FMA, so
       // that it can reuse them instead of holding U + 1 rows live).
       __builtin_amdgcn_sched_barrier(0);
-      load_row<VEC, Q>(row_rsrc(xp, t_first + t_step * (r + U), in_lo, in_hi, W), off_m, off_h, pf[p], ph[p]);
+      load_row<VEC, Q>(row_rsrc(xp, y0 - P + r + U, 0, in_hi, W), off_m, off_h, pf[p], ph[p]);
     }
   };
   using yes = std::integral_constant<bool, true>;
@@ -360,15 +339,17 @@ bool configure_single(Plan &p, int param) {
   if (pick_any<true, false>(d) == nullptr) return false;
   const int nseg = (d.w + kSegCols - 1) / kSegCols;
   // Strip height: a wave keeps about one prefetch window of rows in flight, so
-  // the bytes in flight per CU grow with the number of waves. The halo rows
-  // that adjacent strips both read come from L2 (the two sweep toward or away
-  // from each other at the same time, and the loads keep their lines):
-  // FETCH_SIZE reads 258-260 MiB for the 256 MiB 8192x8192 image at 64 rows.
-  // 64 rows give 4096 waves (16 per CU) there. Measured with the three filters
-  // launched in turn: 16-row strips make the 3x3 and 5x5 3-5% faster but the
-  // 7x7 that follows them 20% slower (at the same shader clock), 64 rows give
-  // the shortest sum; heights that are not powers of two (22 .. 66 rows) were
-  // 2-10% slower than the neighbouring powers of two.
+  // the bytes in flight per CU grow with the number of resident waves. 64 rows
+  // give 4096 waves (16 per CU) on an 8192x8192 image. Each strip also reads
+  // the 2P halo rows it shares with its neighbours, which L2 seldom still holds
+  // (the neighbour reads them at the other end of its sweep): FETCH_SIZE reads
+  // 266-280 MiB for the 256 MiB image (3x3 .. 7x7). Sweeping odd strips upward,
+  // so that both reads of a halo row coincide, brought that to 258-260 MiB but
+  // was 2-3% slower on the 3x3 and 5x5 (builds interleaved in one process).
+  // 16-row strips made the 3x3 and 5x5 3-5% faster but the 7x7 launched after
+  // them 20% slower at the same shader clock; 128 rows were 7-15% slower, and
+  // heights that are not powers of two (22 .. 66 rows) 2-10% slower than the
+  // neighbouring powers of two.
   int rows = 64;
   while (rows > 8 && (long long)nseg * ((d.h + rows - 1) / rows) * d.n < 4096) rows >>= 1;
   if (d.k > 1) {

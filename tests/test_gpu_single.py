@@ -2,8 +2,7 @@
 
 Every call goes through the C ABI (conv2d_create / conv2d_forward) on the
 current HIP stream. Every output is compared, from ragged small images (several 256-column wave
-segments and strips of 8 to 64 rows swept down (even strips) and up (odd
-strips), ragged tails, widths that are not multiples of 4)
+segments and 64-row strips, ragged tails, widths that are not multiples of 4)
 up to the full 8192x8192 image with each of the three filters.
 """
 import numpy as np
