@@ -47,7 +47,7 @@ TRAFFIC_KERNELS = {   # bench case -> (kernel as the profiler names it, its sour
     "8192x8192 5x5": ("is_k1_single<5, 5, true, false, false, 1>", ("k1_single.hip",)),
     "8192x8192 7x7": ("is_k1_single<7, 7, true, false, false, 1>", ("k1_single.hip",)),
     "fp32 layer 1x32x720x1280 -> 32, 3x3": ("is_k5_mfma_f32", ("k5_mfma_f32.hip",)),
-    "fp16 NHWC layer 8x256x256x64 -> 64, 3x3": ("is_k4_mfma<128, 64, 64, 0, 0, 0>", ("k4_mfma.hip",)),
+    "fp16 NHWC layer 8x256x256x64 -> 64, 3x3": ("is_k4_mfma<128, 64, 64, 0, 0, 0, false>", ("k4_mfma.hip",)),
     "upscaling chain 1280x720 (fused)": ("is_k3_chain", ("k3_chain.hip",)),
     "separable 7x7 filter, 8192x8192 fp32": ("is_k1_single<7, 7, true, false, true, 1>", ("k1_single.hip",)),
     "1 channel -> 8 filters 3x3, 4096x4096 fp32": ("is_k2_multi<3, 8, 1, false, false>", ("k2_multi.hip",)),
@@ -135,11 +135,11 @@ PROFILE_ARGS = "--no-cpu-baseline --no-check --secondary fp32_layer,fp16_layer,u
 PMC_ARGS = "--steps 2 --warmup 1 --min-warm-s 0 " + PROFILE_ARGS
 NET_PROFILE_ARGS = "--no-cpu-baseline --no-check --secondary pages_net"
 NET_KERNELS = {
-    "is_k4_mfma<128, 64, 64, 0, 60, 5>": "layers 1 + 2: the 1 -> 64 5x5 computed inside the 64 -> 64 3x3 (60-row units)",
-    "is_k4_mfma<128, 64, 32, 0, 60, 0>": "layer 3: 64 -> 32, 3x3 (60-row units)",
-    "is_k4_mfma<128, 32, 16, 3, 0, 0>": "layer 4: 32 -> 9 (as 16), 3x3, with the depth-to-space x3 in its stores",
+    "is_k4_mfma<128, 64, 64, 0, 60, 5, true>": "layers 1 + 2: the 1 -> 64 5x5 computed inside the 64 -> 64 3x3 (60-row units)",
+    "is_k4_mfma<128, 64, 32, 0, 60, 0, true>": "layer 3: 64 -> 32, 3x3 (60-row units)",
+    "is_k4_mfma<128, 32, 16, 3, 0, 0, false>": "layer 4: 32 -> 9 (as 16), 3x3, with the depth-to-space x3 in its stores",
     "is_k6_head_f16<5, 64>": "layer 1 alone: 1 -> 64, 5x5 (one-launch-per-layer run)",
-    "is_k4_mfma<128, 64, 64, 0, 60, 0>": "layer 2 alone: 64 -> 64, 3x3 (one-launch-per-layer run)",
+    "is_k4_mfma<128, 64, 64, 0, 60, 0, true>": "layer 2 alone: 64 -> 64, 3x3 (one-launch-per-layer run)",
 }
 
 
@@ -238,7 +238,7 @@ def lds_study(torch, isa, synth, stream, stream_obj, steps, warmup):
     """The LDS-staged kernels for a counter run of their bank conflicts: the fp16
     layer under each swizzle of its input tile (tuning variants of its plan; the
     kernel is instantiated per swizzle, so the profiler sees
-    is_k4_mfma<0, 64, 64, 0, 0, 0>, <128, ...> and <256, ...>), the other LDS-staging kernels
+    is_k4_mfma<0, 64, 64, 0, 0, 0, false>, <128, ...> and <256, ...>), the other LDS-staging kernels
     and the fp32 layer and the fused chain."""
     out = []
     x, w, b = synth.cnn_layer_f16_nhwc()

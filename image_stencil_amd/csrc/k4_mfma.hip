@@ -241,7 +241,7 @@ struct MfmaArgs {
   const _Float16 *w;
   const float *bias;
   _Float16 *y;
-  int N, H, W, relu;
+  int N, H, W, relu;   // relu: which instance the launch picks (not read by the kernel)
   int kvalid;   // output channels in w and bias; the rest of K computes zeros
   int units_x, units_y, nunits;
   // HEAD: x is the one-channel image (N x H x W fp16); the head's C x 1 x r x r
@@ -266,7 +266,7 @@ struct UnitGeo {
 // the way out (y is N x 3H x 3W fp16, out[3i+dy][3j+dx] = z[i][j][3dy+dx]),
 // in place of the staged rows' 16-channel pixel lines; 16 output channels only.
 // URX: unit height other than the default 64 rows (60 divides a 720-row frame).
-template <int SWZ, int C, int K, int D2S = 0, int URX = 0, int HEAD = 0>
+template <int SWZ, int C, int K, int D2S = 0, int URX = 0, int HEAD = 0, bool RELU = false>
 __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
   using G = K4Cfg<C, K, URX, HEAD>;
   static_assert(D2S == 0 || (D2S == 3 && K == 16), "depth-to-space by 3 of the first 9 of 16 channels");
@@ -740,7 +740,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float r = acc[o & 3][e] + bias[e];
-          if (a.relu) r = fmaxf(r, 0.f);
+          if constexpr (RELU) r = fmaxf(r, 0.f);
           hv[e] = (_Float16)r;
         }
         *reinterpret_cast<uint2v *>(lds + soff_w + ((t & 1) * G::S + (i % G::S)) * G::OUT_ROW_BYTES) =
@@ -781,6 +781,14 @@ void fill_geometry(Plan &p) {
   p.lds = G::LDS_BYTES;
   p.tile_w = G::TC;
   p.tile_h = G::UR;
+}
+
+// The layer's ReLU is a compile-time choice: a run-time flag costs a select
+// per output value in the row epilogue (1.5% of the 64 -> 64 layer's time).
+template <int SWZ, int C, int K, int D2S = 0, int URX = 0, int HEAD = 0>
+hipError_t launch_k4(const MfmaArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  return a.relu ? launch_kernel(is_k4_mfma<SWZ, C, K, D2S, URX, HEAD, true>, grid, block, 0, s, a)
+                : launch_kernel(is_k4_mfma<SWZ, C, K, D2S, URX, HEAD, false>, grid, block, 0, s, a);
 }
 
 }  // namespace
@@ -861,8 +869,7 @@ hipError_t launch_mfma_d2s3(const Plan &p, const _Float16 *x, const _Float16 *w,
   a.wh = nullptr;
   a.bh = nullptr;
   a.relu_h = 0;
-  return launch_kernel(is_k4_mfma<128, 32, 16, 3>, dim3(persistent_grid(p.ntiles, device_cu_count())),
-                       dim3(p.block), 0, s, a);
+  return launch_k4<128, 32, 16, 3>(a, dim3(persistent_grid(p.ntiles, device_cu_count())), dim3(p.block), s);
 }
 
 bool mfma_head_supported(const Plan &p, int head_r) {
@@ -893,10 +900,10 @@ hipError_t launch_mfma_head(const Plan &p, const _Float16 *x1, const _Float16 *w
   const dim3 grid(persistent_grid(p.ntiles, device_cu_count())), block(p.block);
   const bool u60 = p.tile_h == 60;
   if (head_r == 5)
-    return u60 ? launch_kernel(is_k4_mfma<128, 64, 64, 0, 60, 5>, grid, block, 0, s, a)
-               : launch_kernel(is_k4_mfma<128, 64, 64, 0, 0, 5>, grid, block, 0, s, a);
-  return u60 ? launch_kernel(is_k4_mfma<128, 64, 64, 0, 60, 3>, grid, block, 0, s, a)
-             : launch_kernel(is_k4_mfma<128, 64, 64, 0, 0, 3>, grid, block, 0, s, a);
+    return u60 ? launch_k4<128, 64, 64, 0, 60, 5>(a, grid, block, s)
+               : launch_k4<128, 64, 64, 0, 0, 5>(a, grid, block, s);
+  return u60 ? launch_k4<128, 64, 64, 0, 60, 3>(a, grid, block, s)
+             : launch_k4<128, 64, 64, 0, 0, 3>(a, grid, block, s);
 }
 
 hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
@@ -919,19 +926,19 @@ hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, cons
   a.relu_h = 0;
   const dim3 grid(persistent_grid(p.ntiles, device_cu_count())), block(p.block);
   if (p.d.c == 64 && p.d.k == 64) {
-    if (p.tile_h == 60) return launch_kernel(is_k4_mfma<128, 64, 64, 0, 60>, grid, block, 0, s, a);
+    if (p.tile_h == 60) return launch_k4<128, 64, 64, 0, 60>(a, grid, block, s);
     switch (p.vec) {
-      case 0: return launch_kernel(is_k4_mfma<0, 64, 64>, grid, block, 0, s, a);
-      case 128: return launch_kernel(is_k4_mfma<128, 64, 64>, grid, block, 0, s, a);
-      default: return launch_kernel(is_k4_mfma<256, 64, 64>, grid, block, 0, s, a);
+      case 0: return launch_k4<0, 64, 64>(a, grid, block, s);
+      case 128: return launch_k4<128, 64, 64>(a, grid, block, s);
+      default: return launch_k4<256, 64, 64>(a, grid, block, s);
     }
   }
   if (p.d.c == 64 && p.d.k == 32) {
-    if (p.tile_h == 60) return launch_kernel(is_k4_mfma<128, 64, 32, 0, 60>, grid, block, 0, s, a);
-    return launch_kernel(is_k4_mfma<128, 64, 32>, grid, block, 0, s, a);
+    if (p.tile_h == 60) return launch_k4<128, 64, 32, 0, 60>(a, grid, block, s);
+    return launch_k4<128, 64, 32>(a, grid, block, s);
   }
-  if (p.d.c == 32 && p.d.k == 32) return launch_kernel(is_k4_mfma<128, 32, 32>, grid, block, 0, s, a);
-  if (p.d.c == 32 && p.d.k == 16) return launch_kernel(is_k4_mfma<128, 32, 16>, grid, block, 0, s, a);
+  if (p.d.c == 32 && p.d.k == 32) return launch_k4<128, 32, 32>(a, grid, block, s);
+  if (p.d.c == 32 && p.d.k == 16) return launch_k4<128, 32, 16>(a, grid, block, s);
   return hipErrorInvalidValue;
 }
 
