@@ -510,12 +510,13 @@ def _single_large_cases(torch, isa, synth, stream):
     return cases
 
 
-def _layer_cases(torch, isa, stream, x, w, b, relu, sets, label):
+def _layer_cases(torch, isa, stream, x, w, b, relu, sets, label, variant=None):
     """One case per rotating buffer set (same values, distinct memory), so that
-    consecutive launches do not find their inputs in the 256 MB last-level cache."""
+    consecutive launches do not find their inputs in the 256 MB last-level cache.
+    variant: a tuning variant's index (None: the plan's choice)."""
     N, C, H, W = x.shape
     K, _, R, S = w.shape
-    plan = isa.Plan(isa.make_desc(N, C, H, W, K, R, S, "f32", relu))
+    plan = isa.Plan(isa.make_desc(N, C, H, W, K, R, S, "f32", relu), variant=variant)
     info = plan.info()
     wd = torch.from_numpy(w).cuda()
     bd = torch.from_numpy(b).cuda() if b is not None else None
@@ -557,13 +558,53 @@ def _secondary(torch, isa, synth, stream, stream_obj, steps, warmup, groups=SECO
                                 "frac_fp32_valu": round(c.flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
                                 "frac_fp32_packed_peak": round(c.flops / ms / 1e9 / FP32_PACKED_PEAK_TFLOPS, 4),
                                 "roofline": _roofline(c, ms)}
+        ref = m = None
         if check:
             y = c.keep[4].cpu().numpy()
             ref, m = oracle.conv2d(x, w, b, True)
             out["cnn_layer_f32"]["check"] = _oracle_check(y, ref, m, TAU_F32)
-            del y, ref, m
+            del y
         for c in cases:
             c.keep = None
+        # The same layer on the vector ALUs: every variant of the register-blocked
+        # multi-channel kernel (output channels per workgroup), the fastest reported
+        # against the fp32 vector peak.
+        d = isa.make_desc(1, 32, 720, 1280, 32, 3, 3, "f32", True)
+        per_variant = {}
+        best = None
+        for i, v in enumerate(isa.conv2d_list_variants(d)):
+            if v["kernel"] != "is_k2_multi":
+                continue
+            vc = _layer_cases(torch, isa, stream, x, w, b, True, 4, "fp32 layer 1x32x720x1280 -> 32, 3x3", i)
+            _, vper, _ = _time_cases(torch, vc, steps, warmup, stream_obj)
+            vms = sum(vper) / len(vper)
+            per_variant[v["param"]] = round(vms, 4)
+            if best is None or vms < best[0]:
+                if best is not None:
+                    for oc in best[2]:
+                        oc.keep = None
+                best = (vms, v["param"], vc)
+            else:
+                for oc in vc:
+                    oc.keep = None
+        if best is not None:
+            vms, param, vc = best
+            c = vc[0]
+            out["cnn_layer_f32_valu"] = {
+                "workload": c.name + ", bias, ReLU, on the vector ALUs", "kernel": c.kernel,
+                "channels_per_workgroup": param, "ms_per_frame": round(vms, 4), **_spread(vc),
+                "gflops": round(c.flops / vms / 1e6, 1),
+                "variants_ms": per_variant,
+                "roofline": {"bound": "alu", "achieved": round(c.flops / vms / 1e9, 3),
+                             "peak": round(FP32_VALU_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+                             "frac": round(c.flops / vms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4)}}
+            if check:
+                y = c.keep[4].cpu().numpy()
+                out["cnn_layer_f32_valu"]["check"] = _oracle_check(y, ref, m, TAU_F32)
+                del y
+            for oc in vc:
+                oc.keep = None
+        del ref, m
 
     if "fp16_layer" in groups:
         # fp16 NHWC layer on the matrix cores.
