@@ -8,8 +8,8 @@
 // direct fp32 kernel is bound by the vector ALUs; v_mfma_f32_16x16x4_f32 does
 // the same fp32 products and sums at twice that ceiling (157.3 vs 78.6 TFLOP/s
 // without packed FP32). Design:
-//  * persistent workgroups of 4 waves, one per CU, looping over 13 x 32 pixel
-//    tiles (2240 on a 1280x720 frame: 9 rounds of 256 CUs, the last 75% full;
+//  * persistent workgroups of 8 waves (2 per SIMD), one per CU, looping over
+//    13 x 32 pixel tiles (2240 on a 1280x720 frame: 9 rounds of 256 CUs, the last 75% full;
 //    12-row tiles needed 10 rounds, 120 rows per CU against 117); tiles of one
 //    XCD are neighbours so halo re-reads hit its L2;
 //  * the input tile with its halo (32 channels x 15 rows x 40 columns, aligned
@@ -18,11 +18,15 @@
 //    through the range check;
 //  * LDS keeps the NCHW order; the channel-plane pitch of 624 floats (600 used)
 //    is an odd multiple of 16 banks: the 16 lanes of one channel read 16
-//    consecutive floats, and the two channels of a 32-lane half land on
-//    disjoint bank halves; the two tile buffers fill the 160 KB of LDS;
-//  * wave w computes output channels 16*(w&1) .. +16 for columns 16*(w>>1) ..
-//    +16 of all 13 tile rows; its 72 weight fragments (all 288 k) stay in
-//    registers;
+//    consecutive floats, and the 4 channels of a read sit 16 banks apart; the
+//    two tile buffers fill the 160 KB of LDS;
+//  * wave w computes output channels 16*(w&1) .. +16 for columns
+//    16*((w>>1)&1) .. +16 of tile rows 0..6 (w < 4) or 7..12 (w >= 4); its 72
+//    weight fragments (all 288 k) stay in registers. Two waves per SIMD hide
+//    each other's operand-read and epilogue stalls: with 4 waves (one per SIMD,
+//    each taking all 13 rows) the layer took 149.8 us against 142.6 us with 8
+//    (interleaved in one process, the same results bit for bit); the two row
+//    halves read 17 input rows per tile instead of 15;
 //  * MFMA operands: A = 16 pixels x 4 channels of one tap (one LDS float per
 //    lane), B = 4 channels x 16 output channels (weights), D = 4 consecutive
 //    pixels of one output channel per lane, stored as one 16-byte NCHW vector;
@@ -50,34 +54,23 @@ constexpr int kIC = 4 * kChunksRow;           // LDS floats per input row
 constexpr int kPlaneChunks = 156;             // 16-byte slots per channel plane, 150 used
 constexpr int kPlane = 4 * kPlaneChunks;      // LDS floats per channel plane (624)
 constexpr int kChunks = kC * kPlaneChunks;    // 16-byte slots per input tile, padding included
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;                     // 2 per SIMD
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRounds = (kChunks + kThreads - 1) / kThreads;   // 16-byte DMA rounds per thread and tile
 constexpr int kBufFloats = kRounds * kThreads * 4;   // floats per LDS tile buffer (whole rounds)
 constexpr int kCQ = kC / 4;                   // channel quads (k steps per tap)
 constexpr int kKS = 9 * kCQ;                  // k steps of 4
-constexpr int kReadSteps = kIR * 3 * kCQ;     // A reads per wave and tile
-// The next tile's DMA rounds are issued during the first kIssueSteps read
-// steps (round j at step j * kIssueSteps / kRounds), so that the last one has
-// the rest of the tile's MFMAs to arrive.
-constexpr int kIssueSteps = kReadSteps * 3 / 5;
-// Output stores issued after the last DMA round of a tile: row o is stored at
-// read step (o + 2) * 3 * kCQ + 3 * kCQ - 1.
-constexpr int stores_after_last_round() {
-  const int q_last = ((kRounds - 1) * kIssueSteps) / kRounds;
-  int n = 0;
-  for (int o = 0; o < kTR; ++o)
-    if ((o + 2) * 3 * kCQ + 3 * kCQ - 1 >= q_last) ++n;
-  return n;
-}
-constexpr int kStores = stores_after_last_round();
+// Output rows of a wave: waves 0-3 take tile rows 0..6 and waves 4-7 rows
+// 7..12 of the same columns and channels.
+template <int RH>
+struct Rows {
+  static constexpr int O0 = RH ? 7 : 0;
+  static constexpr int O1 = RH ? kTR : 7;
+};
 constexpr unsigned kOob = 0xFFFFFFF0u;
-// s_waitcnt immediate (gfx9 encoding): vmcnt <= kStores (bits 3:0 and 15:14),
-// expcnt and lgkmcnt not waited for (all ones).
-constexpr int kWaitDmaNotStores = (kStores & 0xF) | ((kStores >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 static_assert(kPlane % 32 == 16, "plane pitch: 16 banks apart");
 static_assert(kIR * kChunksRow <= kPlaneChunks, "the tile rows fit the plane");
 static_assert(kC * kPlane <= kBufFloats, "the tile fits its buffer");
-static_assert(kStores < 64, "vmcnt field");
 
 struct MfmaF32Args {
   const float *x;
@@ -98,7 +91,8 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
   const int n16 = lane & 15;   // pixel of A, output channel of B and D
   const int g = lane >> 4;     // channel of A and B inside a quad; pixel group of D
   const int ob = wave & 1;     // output channels 16*ob .. +16
-  const int ch = wave >> 1;    // tile columns 16*ch .. +16
+  const int ch = (wave >> 1) & 1;   // tile columns 16*ch .. +16
+  const int rh = wave >> 2;    // row half (8 waves)
 
   // ---- Tile schedule: XCD x (= blockIdx mod 8) walks its own contiguous range.
   const int G = gridDim.x;
@@ -143,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
   // break the instruction stream.
   const int plane_i = H * W;
   auto issue_round = [&](const Dma &d, float *buf, int j) {
-    const unsigned s = (unsigned)((j * 4 + wave) * 64 + lane);
+    const unsigned s = (unsigned)((j * kWaves + wave) * 64 + lane);
     const unsigned c = s / kPlaneChunks;
     const unsigned r = s - c * kPlaneChunks;
     const unsigned row = r / kChunksRow;
@@ -153,7 +147,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
                     ((unsigned)gx < (unsigned)W);
     const unsigned off = in ? (unsigned)((int)c * plane_i + gy * W + gx) * 4u : kOob;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        d.rx, (__attribute__((address_space(3))) void *)(buf + (j * 4 + wave) * 64 * 4), 16, off, 0, 0, 0);
+        d.rx, (__attribute__((address_space(3))) void *)(buf + (j * kWaves + wave) * 64 * 4), 16, off, 0, 0, 0);
   };
 
   // ---- Weights: coalesced 16-byte loads of the KCRS tensor, then the first
@@ -168,14 +162,14 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(a.bias), (short)0, a.bias ? kK * 4 : 0, kBufferFlags);
     constexpr int kVecRow = kC * 9 / 4;        // 72 vectors per output channel
-    constexpr int kVecPerThread = kK * kVecRow / kThreads;
-    static_assert(kVecPerThread * kThreads == kK * kVecRow, "whole vectors per thread");
+    constexpr int kVecs = kK * kVecRow;
+    constexpr int kVecPerThread = (kVecs + kThreads - 1) / kThreads;
     constexpr int kWPitch = kC * 9 + 4;        // 16-byte aligned rows
     static_assert(kK * kWPitch <= kBufFloats, "the weights fit one tile buffer");
     uint4v t[kVecPerThread];
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j)
-      t[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, (j * kThreads + tid) * 16, 0, 0);
+      t[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, (j * kThreads + tid) * 16, 0, 0);   // past the end: 0
     {
       const Dma d0 = dma_for(tile);
 #pragma unroll
@@ -190,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
     for (int j = 0; j < kVecPerThread; ++j) {
       const int v = j * kThreads + tid;
       const int o = v / kVecRow, r = v - o * kVecRow;
-      *reinterpret_cast<uint4v *>(wl + o * kWPitch + 4 * r) = t[j];
+      if (kVecs % kThreads == 0 || v < kVecs) *reinterpret_cast<uint4v *>(wl + o * kWPitch + 4 * r) = t[j];
     }
     lds_barrier();
     const float *wp = wl + (16 * ob + n16) * kWPitch + g * 9;
@@ -209,24 +203,24 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
   // The next tile's DMA rounds are spread over the first 3/5 of the MFMA
   // loop, between the reads: spread to the very end, the last round's latency
   // would be exposed at every tile boundary.
-  auto compute_store = [&](int tl, const float *buf, const Dma &dn, float *nbuf) {
+  auto compute_store = [&](auto rh_c, int tl, const float *buf, const Dma &dn, float *nbuf) {
+    using RW = Rows<decltype(rh_c)::value>;
+    constexpr int O0 = RW::O0, O1 = RW::O1;
+    constexpr int kReads = (O1 + 2 - O0) * 3 * kCQ;
+    constexpr int kIssue = kReads * 3 / 5;
     int n, y0, x0;
     tile_origin(tl, n, y0, x0);
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
         a.y + (size_t)n * kK * plane, (short)0, (int)(kK * plane * 4), kBufferFlags);
-    // This lane's output: channel 16*ob + n16, columns x0 + 16*ch + 4g .. +4.
     const int gx = x0 + 16 * ch + 4 * g;
     const bool col_in = gx < W;
     const unsigned col_off = (unsigned)(((size_t)(16 * ob + n16) * plane + gx) * 4);
-    float4v acc[kTR];
+    float4v acc[O1 - O0];
 #pragma unroll
-    for (int o = 0; o < kTR; ++o) acc[o] = float4v{0.f, 0.f, 0.f, 0.f};
-    // Reads in (input row i, tap column v, channel quad cq) order, each issued
-    // kAhead reads early into a ring of registers.
-    constexpr int kReads = kReadSteps;
+    for (int o = 0; o < O1 - O0; ++o) acc[o] = float4v{0.f, 0.f, 0.f, 0.f};
     constexpr int kAhead = 16;
     auto read_a = [&](int q) -> float {
-      const int i = q / (3 * kCQ), v = (q / kCQ) % 3, cq = q % kCQ;
+      const int i = O0 + q / (3 * kCQ), v = (q / kCQ) % 3, cq = q % kCQ;
       return buf[aoff + cq * 4 * kPlane + i * kIC + v];
     };
     float ring[kAhead];
@@ -234,32 +228,29 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
     for (int q = 0; q < kAhead; ++q) ring[q] = read_a(q);
     static_for<kReads>([&](auto qc) __attribute__((always_inline)) {
       constexpr int q = decltype(qc)::value;
-      // rounds issued at this step: j with j * kIssueSteps / kRounds == q
-      constexpr int j0 = q < kIssueSteps ? (q * kRounds + kIssueSteps - 1) / kIssueSteps : kRounds;
-      constexpr int j1 = q < kIssueSteps ? ((q + 1) * kRounds + kIssueSteps - 1) / kIssueSteps : kRounds;
+      constexpr int j0 = q < kIssue ? (q * kRounds + kIssue - 1) / kIssue : kRounds;
+      constexpr int j1 = q < kIssue ? ((q + 1) * kRounds + kIssue - 1) / kIssue : kRounds;
       if constexpr (j1 > j0) {
 #pragma unroll
         for (int j = j0; j < j1; ++j) issue_round(dn, nbuf, j);
-        // keeps the round ahead of this step's store (the tile-end wait counts
-        // the stores issued after the last round)
         __builtin_amdgcn_sched_barrier(0);
       }
       const float av = ring[q % kAhead];
       if constexpr (q + kAhead < kReads) ring[q % kAhead] = read_a(q + kAhead);
-      constexpr int i = q / (3 * kCQ), v = (q / kCQ) % 3, cq = q % kCQ;
+      constexpr int i = O0 + q / (3 * kCQ), v = (q / kCQ) % 3, cq = q % kCQ;
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
         const int o = i - u;
-        if (o >= 0 && o < kTR)
-          acc[o] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wb[(3 * u + v) * kCQ + cq], acc[o], 0, 0, 0);
+        if (o >= O0 && o < O1)
+          acc[o - O0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wb[(3 * u + v) * kCQ + cq], acc[o - O0], 0, 0, 0);
       }
-      if constexpr (v == 2 && cq == kCQ - 1 && i >= 2) {
+      if constexpr (v == 2 && cq == kCQ - 1 && i - 2 >= O0 && i - 2 < O1) {
         constexpr int o = i - 2;
         const int gy = y0 + o;
         float r[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          r[e] = acc[o][e] + bv;
+          r[e] = acc[o - O0][e] + bv;
           if (a.relu) r[e] = fmaxf(r[e], 0.f);
         }
         const unsigned off = ((gy < H) & col_in) ? col_off + (unsigned)gy * (unsigned)W * 4u : kOob;
@@ -268,6 +259,17 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    // Wait for the next tile's DMA but not for the output stores issued after
+    // its last round: vector-memory operations retire in issue order on gfx9.
+    constexpr int q_last = ((kRounds - 1) * kIssue) / kRounds;
+    constexpr int stores = [] {
+      int c = 0;
+      for (int o = O0; o < O1; ++o)
+        if ((o + 2 - O0) * 3 * kCQ + 3 * kCQ - 1 >= q_last) ++c;
+      return c;
+    }();
+    static_assert(stores < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((stores & 0xF) | ((stores >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   };
 
   __builtin_amdgcn_s_waitcnt(0);
@@ -275,10 +277,12 @@ __global__ __launch_bounds__(kThreads, 1) void is_k5_mfma_f32(MfmaF32Args a) {
   int cur = 0;
   while (tile < hi) {
     const int next = tile + step;
-    compute_store(tile, lds + cur * kBufFloats, dma_for(next), lds + (cur ^ 1) * kBufFloats);
-    // Wait for the next tile's DMA but not for the output stores issued after
-    // its last round: vector-memory operations retire in issue order on gfx9.
-    __builtin_amdgcn_s_waitcnt(kWaitDmaNotStores);
+    if (rh == 0)
+      compute_store(std::integral_constant<int, 0>{}, tile, lds + cur * kBufFloats, dma_for(next),
+                    lds + (cur ^ 1) * kBufFloats);
+    else
+      compute_store(std::integral_constant<int, 1>{}, tile, lds + cur * kBufFloats, dma_for(next),
+                    lds + (cur ^ 1) * kBufFloats);
     __syncthreads();
     tile = next;
     cur ^= 1;
