@@ -299,6 +299,11 @@ def lds_study(torch, isa, synth, stream, stream_obj, steps, warmup):
     yh = torch.empty((1, 720, 1280, 64), device="cuda", dtype=torch.float16)
     more.append(variant_case("fp16 first layer 1->64 5x5", isa.make_desc(1, 1, 720, 1280, 64, 5, 5, "f16", True),
                              "is_k6_head_f16", None, xh, wh, bh, yh))
+    # The fp32 first-layer kernel (1 -> 32, 5x5, the upscaling chain's first layer).
+    x1f = torch.rand((1, 1, 720, 1280), device="cuda")
+    w1f = torch.randn((32, 1, 5, 5), device="cuda") / 5
+    more.append(variant_case("fp32 first layer 1->32 5x5", isa.make_desc(1, 1, 720, 1280, 32, 5, 5, "f32", True),
+                             "is_k9_head_f32", None, x1f, w1f, bd, yd))
     w32 = (torch.randn((32, 64, 3, 3), device="cuda") / 24).half()
     y32 = torch.empty((1, 720, 1280, 32), device="cuda", dtype=torch.float16)
     more.append(variant_case("fp16 layer 64->32", isa.make_desc(1, 64, 720, 1280, 32, 3, 3, "f16", True),
@@ -341,7 +346,8 @@ def pmc_lds_summary(pmc_dir):
              "0 = plain, 128, 256; the plan picks 128), and its 64 -> 32 and 32 -> 16 instances on a",
              "1280x720 frame; the register-blocked multi-channel kernel on the fp32 32 -> 32 layer (a tuning",
              "variant there) and on one channel with 8 3x3 filters (4096x4096); the pointwise kernel on a",
-             "1x1 32 -> 32 layer; the fp16 first-layer kernel on 1 -> 64 5x5. conflict share =",
+             "1x1 32 -> 32 layer; the fp16 first-layer kernel on 1 -> 64 5x5; the fp32 first-layer kernel",
+             "on 1 -> 32 5x5. conflict share =",
              "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
              "| kernel | dispatches | " + " | ".join(LDS_COUNTERS) + " | conflict share |",
              "|---|---|" + "---|" * len(LDS_COUNTERS) + "---|"]

@@ -92,7 +92,8 @@ is_status make_plan(const conv2d_desc *d, is::Plan &p) {
   if (d->separable) {
     // Only the single-channel kernel evaluates separable filters.
     if (!is::configure_single(p)) return IS_ERR_UNSUPPORTED;
-  } else if (!is::configure_single(p) && !is::configure_mfma_f32(p) && !is::configure_pointwise(p) &&
+  } else if (!is::configure_single(p) && !is::configure_head_f32(p) && !is::configure_mfma_f32(p) &&
+             !is::configure_pointwise(p) &&
              !is::configure_multi(p) && !is::configure_mfma(p) && !is::configure_head_f16(p)) {
     is::configure_generic(p);
   }
@@ -132,6 +133,7 @@ bool configure_variant(is::Plan &p, const conv2d_desc &d, const Variant &v) {
     case is::kMfmaNchwF32: return !d.separable && is::configure_mfma_f32(p);
     case is::kPointwise: return is::configure_pointwise(p, v.param);
     case is::kHeadNhwcF16: return !d.separable && is::configure_head_f16(p);
+    case is::kHeadNchwF32: return is::configure_head_f32(p);
     default:
       if (d.separable) return false;
       is::configure_generic(p);
@@ -160,7 +162,7 @@ int collect_variants(const conv2d_desc &d, const is::Plan &def, Variant *out, in
       {is::kMultiChannel, 32}, {is::kMultiChannel, 16}, {is::kMultiChannel, 8}, {is::kMultiChannel, 4},
       {is::kMultiChannel, 2},
       {is::kMfmaNhwcF16, 128}, {is::kMfmaNhwcF16, 0}, {is::kMfmaNhwcF16, 256},
-      {is::kHeadNhwcF16, 0}};
+      {is::kHeadNhwcF16, 0}, {is::kHeadNchwF32, 0}};
   for (const Variant &v : tries)
     if (configure_variant(p, d, v)) add(p);
   return n;
@@ -223,6 +225,10 @@ is_status run_plan(const is::Plan &p, const void *x, const void *w, const float 
     case is::kHeadNhwcF16:
       e = is::launch_head_f16(p, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(w), bias,
                               static_cast<_Float16 *>(y), stream);
+      break;
+    case is::kHeadNchwF32:
+      e = is::launch_head_f32(p, static_cast<const float *>(x), static_cast<const float *>(w), bias,
+                              static_cast<float *>(y), stream);
       break;
     default:
       e = is::launch_generic(p, x, w, bias, y, stream);

@@ -13,7 +13,8 @@ enum KernelId {
   kMfmaNhwcF16 = 4,      // fp16 NHWC implicit GEMM on MFMA
   kMfmaNchwF32 = 5,      // fp32 NCHW 32 -> 32 3x3 implicit GEMM on the fp32 MFMA
   kHeadNhwcF16 = 6,      // fp16 NHWC first layer, 1 -> K, one MFMA k step over the taps
-  kPointwise = 7         // fp32 NCHW 1x1 filters over several channels
+  kPointwise = 7,        // fp32 NCHW 1x1 filters over several channels
+  kHeadNchwF32 = 8       // fp32 NCHW first layer, 1 -> K, fp32 MFMA k steps over the taps
 };
 
 struct Plan {
@@ -91,6 +92,9 @@ bool mfma_head_supported(const Plan &p, int head_r);
 hipError_t launch_mfma_head(const Plan &p, const _Float16 *x1, const _Float16 *wh, const float *bh, int relu_h,
                             int head_r, const _Float16 *w, const float *b, _Float16 *y, hipStream_t s);
 
+bool configure_head_f32(Plan &p);
+hipError_t launch_head_f32(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                           hipStream_t s);
 bool configure_head_f16(Plan &p);
 hipError_t launch_head_f16(const Plan &p, const _Float16 *x, const _Float16 *w, const float *b, _Float16 *y,
                            hipStream_t s);

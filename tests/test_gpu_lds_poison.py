@@ -65,6 +65,8 @@ LAYERS = [
     (1, 64, 32, 125, 96, 3, "f16", True, "is_k4_mfma"),
     (1, 32, 16, 21, 150, 3, "f16", False, "is_k4_mfma"),
     (1, 1, 64, 67, 129, 5, "f16", True, "is_k6_head_f16"),
+    (2, 1, 32, 37, 132, 5, "f32", True, "is_k9_head_f32"),
+    (1, 1, 16, 19, 68, 3, "f32", False, "is_k9_head_f32"),
 ]
 
 

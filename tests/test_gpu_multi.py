@@ -2,9 +2,10 @@
 
 Calls go through the C ABI. Shapes span several tiles with ragged edges (64x16
 for the register-blocked kernel, 32 columns x 13 rows for the fp32 MFMA kernel
-that takes the 32 -> 32 3x3 layers), channel counts that fill one or several
-LDS slabs, every output-channel group size, and the full 1x32x720x1280 layer
-(every output, so every 13-row tile seam).
+that takes the 32 -> 32 3x3 layers, 64 columns x 16 rows for the fp32 MFMA
+first layer that takes one input channel to 16, 32 or 64), channel counts that
+fill one or several LDS slabs, every output-channel group size, and the full
+1x32x720x1280 layer (every output, so every 13-row tile seam).
 """
 import numpy as np
 import pytest
@@ -42,9 +43,9 @@ CASES = [
     (2, 8, 16, 37, 132, 3, False, "is_k2_multi"),
     (1, 4, 8, 17, 68, 3, True, "is_k2_multi"),
     (1, 4, 4, 33, 64, 3, False, "is_k2_multi"),
-    (1, 1, 32, 40, 136, 5, True, "is_k2_multi"),
+    (1, 1, 32, 40, 136, 5, True, "is_k9_head_f32"),
     (1, 8, 32, 21, 72, 5, False, "is_k2_multi"),
-    (1, 1, 32, 19, 68, 3, True, "is_k2_multi"),
+    (1, 1, 32, 19, 68, 3, True, "is_k9_head_f32"),
     (1, 12, 32, 16, 64, 1, False, "is_k8_pointwise"),
     (1, 32, 4, 45, 140, 3, False, "is_k2_multi"),
     (3, 3, 8, 9, 20, 3, True, "is_k2_multi"),
@@ -56,6 +57,15 @@ CASES = [
     (1, 1, 6, 16, 64, 5, False, "is_k2_multi"),
     (1, 1, 16, 21, 72, 1, True, "is_k2_multi"),
     (1, 1, 3, 21, 72, 3, False, "is_k0_generic_nchw_f32"),
+    # one input channel to 16, 32 or 64 outputs, 3x3 or 5x5: the fp32 MFMA first
+    # layer (16 x 64 tiles: ragged rows and columns, several tiles, images)
+    (2, 1, 16, 37, 132, 3, False, "is_k9_head_f32"),
+    (1, 1, 16, 1, 4, 5, True, "is_k9_head_f32"),
+    (3, 1, 32, 17, 68, 5, False, "is_k9_head_f32"),
+    (1, 1, 64, 33, 260, 5, True, "is_k9_head_f32"),
+    (2, 1, 64, 16, 64, 3, False, "is_k9_head_f32"),
+    (1, 1, 32, 45, 196, 5, True, "is_k9_head_f32"),
+    (1, 1, 32, 21, 70, 5, True, "is_k0_generic_nchw_f32"),
     # 1x1 filters over several channels: the pointwise kernel (planes of whole
     # 16-byte vectors, ragged last workgroup), else the fallback
     (1, 8, 16, 21, 72, 1, False, "is_k8_pointwise"),
@@ -115,6 +125,23 @@ def test_mfma_f32_no_bias_and_delta_weights():
     for k in range(32):
         wd[k, rng.integers(0, 32), rng.integers(0, 3), rng.integers(0, 3)] = 1.0
     y = _run(x, wd, None, False, "is_k5_mfma_f32")
+    ref, _ = oracle.conv2d(x, wd)
+    np.testing.assert_array_equal(y.astype(np.float64), ref)
+
+
+def test_head_f32_no_bias_and_delta_weights():
+    """The fp32 first-layer kernel without bias, and with one-hot 5x5 filters
+    (each output channel copies the image shifted by its tap): products by 0
+    and 1 and their sums are exact, so the result must be too; the taps past
+    the 25th, which the kernel pads with zeros, must not leak in."""
+    x, w, _ = synth.cnn_layer_f32(N=1, C=1, K=32, H=35, W=72, R=5, seed=8)
+    y = _run(x, w, None, False, "is_k9_head_f32")
+    ref, m = oracle.conv2d(x, w, None, False)
+    check(y, ref, m, TAU_F32, "head f32 no bias")
+    wd = np.zeros((32, 1, 5, 5), np.float32)
+    for k in range(32):
+        wd[k, 0, (k % 25) // 5, (k % 25) % 5] = 1.0
+    y = _run(x, wd, None, False, "is_k9_head_f32")
     ref, _ = oracle.conv2d(x, wd)
     np.testing.assert_array_equal(y.astype(np.float64), ref)
 

@@ -291,6 +291,14 @@ def test_tile_variants():
     d720 = isa.make_desc(1, 64, 720, 1280, 64, 3, 3, "f16")
     assert [isa.Plan(d720, variant=i).info()["tile"][1] for i in range(3)] == [60, 64, 64]
     assert names(isa.make_desc(1, 1, 720, 1280, 64, 5, 5, "f16", True)) == [("is_k6_head_f16", 0, True)]
+    # one channel to 16/32/64 fp32 outputs, 3x3 or 5x5: the fp32 MFMA first layer, the
+    # register-blocked kernel's groups as variants; not for widths that are not whole vectors
+    assert names(isa.make_desc(1, 1, 720, 1280, 32, 5, 5, "f32", True)) == [
+        ("is_k9_head_f32", 0, True), ("is_k2_multi", 32, False), ("is_k2_multi", 16, False),
+        ("is_k2_multi", 8, False), ("is_k2_multi", 4, False), ("is_k2_multi", 2, False)]
+    assert isa.Plan(isa.make_desc(1, 1, 720, 1282, 32, 5, 5)).info()["kernel"] != "is_k9_head_f32"
+    assert isa.Plan(isa.make_desc(1, 1, 720, 1280, 32, 7, 7)).info()["kernel"] != "is_k9_head_f32"
+    assert isa.Plan(isa.make_desc(1, 1, 720, 1280, 8, 5, 5)).info()["kernel"] == "is_k2_multi"
     assert names(isa.make_desc(1, 3, 16, 30, 5, 3, 3)) == [("is_k0_generic_nchw_f32", 0, True)]
     sep = names(isa.make_desc(1, 1, 512, 512, 1, 7, 7, separable=True))
     assert {k for (k, _, _) in sep} == {"is_k1_single_separable"} and len(sep) == 5
