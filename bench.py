@@ -304,6 +304,11 @@ def lds_study(torch, isa, synth, stream, stream_obj, steps, warmup):
     w1f = torch.randn((32, 1, 5, 5), device="cuda") / 5
     more.append(variant_case("fp32 first layer 1->32 5x5", isa.make_desc(1, 1, 720, 1280, 32, 5, 5, "f32", True),
                              "is_k9_head_f32", None, x1f, w1f, bd, yd))
+    # The 4-filter matrix-core layer (32 -> 4 3x3, the upscaling chain's last layer).
+    w4 = torch.randn((4, 32, 3, 3), device="cuda") / 17
+    y4 = torch.empty((1, 4, 720, 1280), device="cuda")
+    more.append(variant_case("4-filter matrix-core layer 32->4 3x3", isa.make_desc(1, 32, 720, 1280, 4, 3, 3, "f32"),
+                             "is_k2_multi_mfma", None, xd, w4, bd[:4].contiguous(), y4))
     w32 = (torch.randn((32, 64, 3, 3), device="cuda") / 24).half()
     y32 = torch.empty((1, 720, 1280, 32), device="cuda", dtype=torch.float16)
     more.append(variant_case("fp16 layer 64->32", isa.make_desc(1, 64, 720, 1280, 32, 3, 3, "f16", True),
@@ -347,7 +352,8 @@ def pmc_lds_summary(pmc_dir):
              "1280x720 frame; the register-blocked multi-channel kernel on the fp32 32 -> 32 layer (a tuning",
              "variant there) and on one channel with 8 3x3 filters (4096x4096); the pointwise kernel on a",
              "1x1 32 -> 32 layer; the fp16 first-layer kernel on 1 -> 64 5x5; the fp32 first-layer kernel",
-             "on 1 -> 32 5x5. conflict share =",
+             "on 1 -> 32 5x5; the 4-filter matrix-core form of the multi-channel kernel on the upscaling",
+             "chain's last layer (32 -> 4 3x3, 1280x720). conflict share =",
              "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
              "| kernel | dispatches | " + " | ".join(LDS_COUNTERS) + " | conflict share |",
              "|---|---|" + "---|" * len(LDS_COUNTERS) + "---|"]

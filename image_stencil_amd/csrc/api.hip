@@ -93,7 +93,7 @@ is_status make_plan(const conv2d_desc *d, is::Plan &p) {
     // Only the single-channel kernel evaluates separable filters.
     if (!is::configure_single(p)) return IS_ERR_UNSUPPORTED;
   } else if (!is::configure_single(p) && !is::configure_head_f32(p) && !is::configure_mfma_f32(p) &&
-             !is::configure_pointwise(p) &&
+             !is::configure_pointwise(p) && !is::configure_multi_mf(p) &&
              !is::configure_multi(p) && !is::configure_mfma(p) && !is::configure_head_f16(p)) {
     is::configure_generic(p);
   }
@@ -134,6 +134,7 @@ bool configure_variant(is::Plan &p, const conv2d_desc &d, const Variant &v) {
     case is::kPointwise: return is::configure_pointwise(p, v.param);
     case is::kHeadNhwcF16: return !d.separable && is::configure_head_f16(p);
     case is::kHeadNchwF32: return is::configure_head_f32(p);
+    case is::kMultiMfmaF32: return is::configure_multi_mf(p, true);
     default:
       if (d.separable) return false;
       is::configure_generic(p);
@@ -162,7 +163,7 @@ int collect_variants(const conv2d_desc &d, const is::Plan &def, Variant *out, in
       {is::kMultiChannel, 32}, {is::kMultiChannel, 16}, {is::kMultiChannel, 8}, {is::kMultiChannel, 4},
       {is::kMultiChannel, 2},
       {is::kMfmaNhwcF16, 128}, {is::kMfmaNhwcF16, 0}, {is::kMfmaNhwcF16, 256},
-      {is::kHeadNhwcF16, 0}, {is::kHeadNchwF32, 0}};
+      {is::kHeadNhwcF16, 0}, {is::kHeadNchwF32, 0}, {is::kMultiMfmaF32, 0}};
   for (const Variant &v : tries)
     if (configure_variant(p, d, v)) add(p);
   return n;
@@ -228,6 +229,10 @@ is_status run_plan(const is::Plan &p, const void *x, const void *w, const float 
       break;
     case is::kHeadNchwF32:
       e = is::launch_head_f32(p, static_cast<const float *>(x), static_cast<const float *>(w), bias,
+                              static_cast<float *>(y), stream);
+      break;
+    case is::kMultiMfmaF32:
+      e = is::launch_multi_mf(p, static_cast<const float *>(x), static_cast<const float *>(w), bias,
                               static_cast<float *>(y), stream);
       break;
     default:

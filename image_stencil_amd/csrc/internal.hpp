@@ -14,7 +14,8 @@ enum KernelId {
   kMfmaNchwF32 = 5,      // fp32 NCHW 32 -> 32 3x3 implicit GEMM on the fp32 MFMA
   kHeadNhwcF16 = 6,      // fp16 NHWC first layer, 1 -> K, one MFMA k step over the taps
   kPointwise = 7,        // fp32 NCHW 1x1 filters over several channels
-  kHeadNchwF32 = 8       // fp32 NCHW first layer, 1 -> K, fp32 MFMA k steps over the taps
+  kHeadNchwF32 = 8,      // fp32 NCHW first layer, 1 -> K, fp32 MFMA k steps over the taps
+  kMultiMfmaF32 = 9      // fp32 NCHW, 4 filters per workgroup on the fp32 4x4x1 MFMA
 };
 
 struct Plan {
@@ -67,8 +68,14 @@ hipError_t launch_single(const Plan &p, const float *x, const float *w, const fl
 bool configure_multi(Plan &p, int param = 0);
 hipError_t launch_multi(const Plan &p, const float *x, const float *w, const float *b, float *y,
                         hipStream_t s);
-// The multi-channel layer with 4 output channels followed by a 2x depth-to-space
-// (y: N x 1 x 2H x 2W), in one launch.
+// The multi-channel layer's products on the matrix cores, 4 filters per
+// workgroup (C even, K a multiple of 4, 3x3 or 5x5). The default plan takes it for
+// K = 4 only (any_k false); the tuning variants list it for any such K.
+bool configure_multi_mf(Plan &p, bool any_k = false);
+hipError_t launch_multi_mf(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                           hipStream_t s);
+// The multi-channel layer (either path) with 4 output channels followed by a
+// 2x depth-to-space (y: N x 1 x 2H x 2W), in one launch.
 bool multi_d2s_supported(const Plan &p);
 hipError_t launch_multi_d2s(const Plan &p, const float *x, const float *w, const float *b, float *y,
                             hipStream_t s);

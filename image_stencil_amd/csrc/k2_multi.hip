@@ -40,6 +40,12 @@ constexpr int kG = kTW / 4 + 2;      // 16-byte groups per staged row: x0-4 .. x
 constexpr int kMainG = kTW / 4;      // the tile's own groups, x0 .. x0+TW-1 (256 bytes)
 constexpr unsigned kOob = 0xFFFFFFF0u;   // byte offset past any buffer: reads 0
 
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (and nothing else).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 constexpr int kDppRowShr1 = 0x111;   // lane reads lane-1 inside its row of 16
 constexpr int kDppRowShl1 = 0x101;   // lane reads lane+1 inside its row of 16
 
@@ -82,6 +88,95 @@ __device__ __forceinline__ void issue_slab(__amdgpu_buffer_rsrc_t rs, float4 *bu
   }
 }
 
+// Per-lane byte offsets of this lane's DMA vectors inside a slab (the same
+// for every slab: the resource base moves instead). Vectors outside the image
+// and the padding past the slab read 0.
+template <int R, int CS>
+__device__ __forceinline__ void slab_offsets(unsigned *voff, int wave, int lane, int x0, int y0, int H, int W,
+                                             size_t HW) {
+  using G = Geo<R, CS>;
+#pragma unroll
+  for (int j = 0; j < G::ROUNDS; ++j) {
+    const int q = (j * 4 + wave) * 64 + lane;
+    int c, lrow, g;
+    if (q < G::MAINV4) {
+      c = q / (G::LH * kMainG);
+      const int rem = q - c * (G::LH * kMainG);
+      lrow = rem / kMainG;
+      g = 1 + rem - lrow * kMainG;
+    } else {
+      const int h = q - G::MAINV4;
+      c = h / (G::LH * 2);
+      const int rem = h - c * (G::LH * 2);
+      lrow = rem / 2;
+      g = (rem & 1) ? kG - 1 : 0;
+    }
+    const int gy = y0 - G::P + lrow;
+    const int gx = x0 - 4 + 4 * g;
+    const bool in = q < G::V4 && gy >= 0 && gy < H && gx >= 0 && gx < W;
+    voff[j] = in ? (unsigned)(((size_t)c * HW + (size_t)gy * W + gx) * 4) : kOob;
+  }
+}
+
+// Epilogue: bias, ReLU, 16-byte stores (dropped outside the image). acc[f][p]
+// is this lane's sum for filter kg * FT + f at output pixel (oy, ox + p).
+template <int FT, bool RELU, bool D2S>
+__device__ __forceinline__ void store_tile(const float (&acc)[FT][4], const float *bias, float *y, int n,
+                                           int kg, int K, int H, int W, int oy, int ox) {
+  const size_t HW = (size_t)H * W;
+  const bool in = oy < H && ox < W;
+  if constexpr (D2S) {
+    static_assert(FT == 4, "depth-to-space takes 4 channels");
+    // This lane's 4 columns of the 4 channels become 8 columns of output rows
+    // 2*oy (channels 0, 1 interleaved) and 2*oy + 1 (channels 2, 3): two
+    // 16-byte stores per row; W % 4 == 0 keeps them whole.
+    float o[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const float b = bias ? bias[f] : 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        o[f][p] = acc[f][p] + b;
+        if constexpr (RELU) o[f][p] = fmaxf(o[f][p], 0.f);
+      }
+    }
+    float *yn = y + (size_t)n * 4 * HW;
+    const __amdgpu_buffer_rsrc_t rs_o =
+        __builtin_amdgcn_make_buffer_rsrc(yn, (short)0, (int)(4 * HW * 4), kBufferFlags);
+#pragma unroll
+    for (int dy = 0; dy < 2; ++dy) {
+      const int c0 = 2 * dy;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned off =
+            in ? (unsigned)((((size_t)(2 * oy + dy) * (2 * W)) + 2 * ox + 4 * h) * 4) : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
+                               make_float4(o[c0][2 * h], o[c0 + 1][2 * h], o[c0][2 * h + 1], o[c0 + 1][2 * h + 1])),
+            rs_o, off, 0, 0);
+      }
+    }
+    return;
+  }
+  float *yn = y + ((size_t)n * K + (size_t)kg * FT) * HW;
+  const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
+      yn, (short)0, (int)(FT * HW * 4), kBufferFlags);
+#pragma unroll
+  for (int f = 0; f < FT; ++f) {
+    const float b = bias ? bias[kg * FT + f] : 0.f;
+    float o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      o[p] = acc[f][p] + b;
+      if constexpr (RELU) o[p] = fmaxf(o[p], 0.f);
+    }
+    const unsigned off = in ? (unsigned)(((size_t)f * HW + (size_t)oy * W + ox) * 4) : kOob;
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, make_float4(o[0], o[1], o[2], o[3])),
+        rs_o, off, 0, kNonTemporalStore);
+  }
+}
+
 // D2S: the layer has 4 output channels and its output goes through a 2x
 // depth-to-space, out[n][0][2i+dy][2j+dx] = z[n][2dy+dx][i][j] (y is then
 // N x 1 x 2H x 2W), done in the epilogue instead of a pass of its own.
@@ -112,30 +207,8 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi(const float *__restrict_
   const int x0 = tx * kTW, y0 = ty * kTH;
   const size_t HW = (size_t)H * W;
 
-  // Per-lane byte offsets of this lane's DMA vectors inside a slab (same for
-  // every slab: the resource base moves instead).
   unsigned voff[G::ROUNDS];
-#pragma unroll
-  for (int j = 0; j < G::ROUNDS; ++j) {
-    const int q = (j * 4 + wave) * 64 + lane;
-    int c, lrow, g;
-    if (q < G::MAINV4) {
-      c = q / (G::LH * kMainG);
-      const int rem = q - c * (G::LH * kMainG);
-      lrow = rem / kMainG;
-      g = 1 + rem - lrow * kMainG;
-    } else {
-      const int h = q - G::MAINV4;
-      c = h / (G::LH * 2);
-      const int rem = h - c * (G::LH * 2);
-      lrow = rem / 2;
-      g = (rem & 1) ? kG - 1 : 0;
-    }
-    const int gy = y0 - P + lrow;
-    const int gx = x0 - 4 + 4 * g;
-    const bool in = q < G::V4 && gy >= 0 && gy < H && gx >= 0 && gx < W;
-    voff[j] = in ? (unsigned)(((size_t)c * HW + (size_t)gy * W + gx) * 4) : kOob;
-  }
+  slab_offsets<R, CS>(voff, wave, lane, x0, y0, H, W, HW);
 
   const float *xn = x + (size_t)n * C * HW;
   const unsigned slab_bytes = (unsigned)(CS * HW * 4);
@@ -241,60 +314,227 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi(const float *__restrict_
     __syncthreads();
   }
 
-  // Epilogue: bias, ReLU, 16-byte stores (dropped outside the image).
-  const int oy = y0 + row0;
-  const int ox = x0 + 4 * lc;
-  const bool in = oy < H && ox < W;
-  if constexpr (D2S) {
-    static_assert(FT == 4, "depth-to-space takes 4 channels");
-    // This lane's 4 columns of the 4 channels become 8 columns of output rows
-    // 2*oy (channels 0, 1 interleaved) and 2*oy + 1 (channels 2, 3): two
-    // 16-byte stores per row; W % 4 == 0 keeps them whole.
-    float o[4][4];
+  store_tile<FT, RELU, D2S>(acc, bias, y, n, kg, K, H, W, y0 + row0, x0 + 4 * lc);
+}
+
+// ---- The matrix-core path --------------------------------------------------
+//
+// The same tiles, slabs and row windows with the products on the fp32 matrix
+// cores, for 4 filters per workgroup. v_mfma_f32_4x4x1_16b_f32 multiplies, in
+// each of 16 blocks of 4 lanes, a 4-vector A by a 4-vector B into a 4 x 4
+// accumulator: lane 4b + i gives A[b][i] and B[b][i] and holds D[b][0..3][i].
+// A is one tap of the 4 filters (lane i gives filter i mod 4's tap) and B the
+// pixel the lane owns, so every lane accumulates its own pixel for all 4
+// filters: one instruction per input channel, tap and pixel column of the
+// lane's 4, each accumulation a single-rounding fma, in the vector path's
+// order (channel, then filter row, then column), so both paths give the same
+// bits. Per tap it issues at the matrix cores' full fp32 rate, twice the
+// vector ALUs' fma rate.
+//
+// The layer moves 36 bytes per output pixel for 288 fmas, so once the products
+// are this cheap the input stream decides the time, and one slab in flight per
+// workgroup (the vector path's double buffer) leaves HBM idle between slabs.
+// Here slabs of CS channels go through a ring of NB LDS buffers with NB - 1
+// slabs in flight and one workgroup barrier per slab. Each slab brings its taps
+// after its pixels ([channel][filter][tap], rows of TP taps padded with zeros
+// to 16 bytes), by dword DMA. Every wave issues the same number of DMA
+// instructions per slab (chunks past the data write zeros into the padding),
+// so a slab's arrival is a fixed count of outstanding vector-memory operations.
+template <int R, int CS>
+struct MGeo {
+  using G = Geo<R, CS>;
+  static constexpr int TP = (R * R + 3) / 4 * 4;        // taps per (channel, filter)
+  static constexpr int WUSED = CS * 4 * TP;             // tap dwords of a slab
+  static constexpr int WROUNDS = (WUSED + 255) / 256;   // dword chunks per wave
+  static constexpr int PIXV4 = G::PADV4;                // pixel vectors per buffer
+  static constexpr int BUFV4 = PIXV4 + WROUNDS * 64;    // + WROUNDS x 4 x 64 dwords
+  static constexpr int IPW = G::ROUNDS + WROUNDS;       // DMA instructions per wave per slab
+};
+
+// One slab into one ring buffer: every wave issues G::ROUNDS pixel chunks and
+// WROUNDS tap chunks.
+template <int R, int CS>
+__device__ __forceinline__ void issue_ring_slab(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rw, float4 *buf,
+                                                int wave, const unsigned *voff, const unsigned *wvoff) {
+  using G = Geo<R, CS>;
+  using M = MGeo<R, CS>;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const float b = bias ? bias[f] : 0.f;
+  for (int j = 0; j < G::ROUNDS; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(buf + (j * 4 + wave) * 64),
+                                             16, voff[j], 0, 0, 0);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        o[f][p] = acc[f][p] + b;
-        if constexpr (RELU) o[f][p] = fmaxf(o[f][p], 0.f);
-      }
-    }
-    float *yn = y + (size_t)n * 4 * HW;
-    const __amdgpu_buffer_rsrc_t rs_o =
-        __builtin_amdgcn_make_buffer_rsrc(yn, (short)0, (int)(4 * HW * 4), kBufferFlags);
+  for (int j = 0; j < M::WROUNDS; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rw, (__attribute__((address_space(3))) void *)((float *)(buf + M::PIXV4) + (j * 4 + wave) * 64), 4,
+        wvoff[j], 0, 0, 0);
+}
+
+// NSL: the slab count C / CS when known at compile time (0: any).
+template <int R, int CS, int NB, int NSL, bool RELU, bool D2S>
+__global__ __launch_bounds__(kThreads) void is_k2_multi_mfma(const float *__restrict__ x,
+                                                             const float *__restrict__ w,
+                                                             const float *__restrict__ bias,
+                                                             float *__restrict__ y, int C, int H, int W, int K,
+                                                             int ntx, int nty, int nkg, int ntiles) {
+  using G = Geo<R, CS>;
+  using M = MGeo<R, CS>;
+  constexpr int P = G::P;
+  constexpr int TQ = M::TP / 4;
+  constexpr int PD = NB - 1;   // slabs in flight ahead of the one computed
+  static_assert((PD - 1) * M::IPW < 64, "vmcnt field");
+  // The ring's buffers are separate arrays so that the compiler can tell a
+  // slab's LDS reads from the DMA still writing the other buffers (one array
+  // indexed by slab would make every LDS read wait for all DMA in flight).
+  static_assert(NB == 4, "four ring buffers");
+  __shared__ float4 ring0[M::BUFV4], ring1[M::BUFV4], ring2[M::BUFV4], ring3[M::BUFV4];
+  lds_poison(ring0, sizeof(ring0));
+  lds_poison(ring1, sizeof(ring1));
+  lds_poison(ring2, sizeof(ring2));
+  lds_poison(ring3, sizeof(ring3));
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lr = lane >> 4;
+  const int lc = lane & 15;
+
+  const int tile = xcd_remap(blockIdx.x, ntiles);
+  const int tx = tile % ntx;
+  const int ty = (tile / ntx) % nty;
+  const int kg = (tile / (ntx * nty)) % nkg;
+  const int n = tile / (ntx * nty * nkg);
+  const int x0 = tx * kTW, y0 = ty * kTH;
+  const size_t HW = (size_t)H * W;
+
+  unsigned voff[G::ROUNDS];
+  slab_offsets<R, CS>(voff, wave, lane, x0, y0, H, W, HW);
+  // This lane's tap dwords in a slab: filter f of the group, channel c of the
+  // slab, tap t; relative to the slab's first channel of the group's first
+  // filter. Padding taps and chunks read 0.
+  unsigned wvoff[M::WROUNDS];
 #pragma unroll
-    for (int dy = 0; dy < 2; ++dy) {
-      const int c0 = 2 * dy;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const unsigned off =
-            in ? (unsigned)((((size_t)(2 * oy + dy) * (2 * W)) + 2 * ox + 4 * h) * 4) : kOob;
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
-                               make_float4(o[c0][2 * h], o[c0 + 1][2 * h], o[c0][2 * h + 1], o[c0 + 1][2 * h + 1])),
-            rs_o, off, 0, 0);
-      }
-    }
-    return;
+  for (int j = 0; j < M::WROUNDS; ++j) {
+    const int e = (j * 4 + wave) * 64 + lane;
+    const int c = e / (4 * M::TP), f = (e / M::TP) % 4, t = e % M::TP;
+    wvoff[j] = (e < M::WUSED && t < R * R) ? (unsigned)((((size_t)f * C + c) * R * R + t) * 4) : kOob;
   }
-  float *yn = y + ((size_t)n * K + (size_t)kg * FT) * HW;
-  const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
-      yn, (short)0, (int)(FT * HW * 4), kBufferFlags);
+
+  const float *xn = x + (size_t)n * C * HW;
+  const float *wg = w + (size_t)kg * 4 * C * R * R;
+  const size_t w_left = (size_t)(K - kg * 4) * C * R * R;   // dwords from wg to the end of w
+  auto issue = [&](int s, float4 *buf) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(xn + (size_t)s * CS * HW), (short)0, (int)(CS * HW * 4), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(wg + (size_t)s * CS * R * R), (short)0,
+        (int)((w_left - (size_t)s * CS * R * R) * 4), kBufferFlags);
+    issue_ring_slab<R, CS>(rs, rw, buf, wave, voff, wvoff);
+  };
+
+  const int row0 = wave * 4 + lr;
+  const int halo_g = lc == 15 ? 1 : 0;
+  float4v macc[4];   // macc[p][f]: pixel column p, filter f
 #pragma unroll
-  for (int f = 0; f < FT; ++f) {
-    const float b = bias ? bias[kg * FT + f] : 0.f;
-    float o[4];
+  for (int p = 0; p < 4; ++p) macc[p] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // One slab: per channel, the R row windows as on the vector path and the
+  // taps of filter lane mod 4 (16-byte reads); the next channel's LDS reads
+  // are issued before this channel's products.
+  auto compute = [&](const float4 *bf) __attribute__((always_inline)) {
+    const float4 *wl = bf + M::PIXV4 + (lane & 3) * TQ;
+    float4 raw_o[2][R], raw_h[2][R], raw_w[2][TQ];
+    auto read_raw = [&](int c, int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      o[p] = acc[f][p] + b;
-      if constexpr (RELU) o[p] = fmaxf(o[p], 0.f);
+      for (int u = 0; u < R; ++u) {
+        const int crow = c * G::LH + row0 + u;
+        raw_o[b][u] = bf[crow * kMainG + lc];
+        if constexpr (P > 0) raw_h[b][u] = bf[G::MAINV4 + crow * 2 + halo_g];
+      }
+#pragma unroll
+      for (int q = 0; q < TQ; ++q) raw_w[b][q] = wl[c * 4 * TQ + q];
+    };
+    read_raw(0, 0);
+#pragma unroll
+    for (int c = 0; c < CS; ++c) {
+      float win[R][4 + 2 * P];
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const float4 o4 = raw_o[c & 1][u];
+        win[u][P + 0] = o4.x; win[u][P + 1] = o4.y; win[u][P + 2] = o4.z; win[u][P + 3] = o4.w;
+        if constexpr (P > 0) {
+          const float4 h4 = raw_h[c & 1][u];
+          const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
+          const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+          for (int q = 1; q <= P; ++q) {
+            win[u][P - q] = row_prev(ov[4 - q], hv[4 - q]);
+            win[u][P + 3 + q] = row_next(ov[q - 1], hv[q - 1]);
+          }
+        }
+      }
+      float tap[4 * TQ];
+#pragma unroll
+      for (int q = 0; q < TQ; ++q) {
+        const float4 t4 = raw_w[c & 1][q];
+        tap[4 * q] = t4.x; tap[4 * q + 1] = t4.y; tap[4 * q + 2] = t4.z; tap[4 * q + 3] = t4.w;
+      }
+      if (c + 1 < CS) read_raw(c + 1, (c + 1) & 1);
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+#pragma unroll
+        for (int v = 0; v < R; ++v)
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            macc[p] = __builtin_amdgcn_mfma_f32_4x4x1f32(tap[u * R + v], win[u][p + v], macc[p], 0, 0, 0);
     }
-    const unsigned off = in ? (unsigned)(((size_t)f * HW + (size_t)oy * W + ox) * 4) : kOob;
-    __builtin_amdgcn_raw_buffer_store_b128(
-        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, make_float4(o[0], o[1], o[2], o[3])),
-        rs_o, off, 0, kNonTemporalStore);
+  };
+
+  // Wait until this wave's part of slab s has landed, with `ahead` later slabs
+  // still allowed in flight.
+  static_assert(PD <= 4, "wait_slab's cases");
+  auto wait_slab = [&](int ahead) __attribute__((always_inline)) {
+    if (ahead == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if constexpr (PD > 1) if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(1 * M::IPW));
+    if constexpr (PD > 2) if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * M::IPW));
+    if constexpr (PD > 3) if (ahead == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * M::IPW));
+  };
+
+  const int nslab = NSL > 0 ? NSL : C / CS;
+  float4 *const bufs[4] = {ring0, ring1, ring2, ring3};
+  if (nslab > 0) issue(0, ring0);
+  if (nslab > 1) issue(1, ring1);
+  if (nslab > 2) issue(2, ring2);
+  // Slab s sits in buffer s mod 4; slab s + 3 goes into the buffer of slab s - 1.
+  auto step = [&](int s, float4 *cur, float4 *next) __attribute__((always_inline)) {
+    wait_slab(min(PD - 1, nslab - 1 - s));
+    // Every wave's part of slab s is in LDS, and every wave is done with slab
+    // s - 1, whose buffer slab s + PD takes next; the later slabs' DMA stays
+    // in flight across the barrier.
+    lds_barrier();
+    if (s + PD < nslab) issue(s + PD, next);
+    compute(cur);
+  };
+  if constexpr (NSL > 0) {
+    // A known slab count unrolls the whole channel loop. The compiler then sees
+    // which buffer every LDS read and DMA touches and waits only for the slab a
+    // read needs; around a loop's back edge it would wait for all DMA in flight.
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) step(s, bufs[s & 3], bufs[(s + 3) & 3]);
+  } else {
+    for (int s = 0; s < nslab; s += 4) {
+      step(s, ring0, ring3);
+      if (s + 1 < nslab) step(s + 1, ring1, ring0);
+      if (s + 2 < nslab) step(s + 2, ring2, ring1);
+      if (s + 3 < nslab) step(s + 3, ring3, ring2);
+    }
   }
+
+  float acc[4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc[f][p] = macc[p][f];
+  store_tile<4, RELU, D2S>(acc, bias, y, n, kg, K, H, W, y0 + row0, x0 + 4 * lc);
 }
 
 using K2Fn = void (*)(const float *, const float *, const float *, float *, int, int, int, int, int, int, int,
@@ -322,6 +562,21 @@ K2Fn pick(int r, int ft, int cs) {
 template <bool RELU>
 K2Fn pick_d2s(int r, int ft, int cs) {
   if (r == 3 && ft == 4 && cs == 4) return is_k2_multi<3, 4, 4, RELU, true>;
+  return nullptr;
+}
+
+// The matrix-core path: slabs of 2 channels in a ring of 4 buffers (3 slabs in
+// flight; 53 KB of LDS, so 3 workgroups per CU).
+constexpr int kMfCS = 2;
+constexpr int kMfNB = 4;
+template <bool RELU, bool D2S>
+K2Fn pick_mf(int r, int c) {
+  if (r == 3) {
+    if (c == 32) return is_k2_multi_mfma<3, kMfCS, kMfNB, 32 / kMfCS, RELU, D2S>;
+    return is_k2_multi_mfma<3, kMfCS, kMfNB, 0, RELU, D2S>;
+  }
+  if constexpr (!D2S)
+    if (r == 5) return is_k2_multi_mfma<5, kMfCS, kMfNB, 0, RELU, D2S>;
   return nullptr;
 }
 
@@ -372,8 +627,47 @@ bool configure_multi(Plan &p, int param) {
   return true;
 }
 
+bool configure_multi_mf(Plan &p, bool any_k) {
+  const conv2d_desc &d = p.d;
+  if (d.layout != IS_NCHW || d.in_dtype != IS_F32 || d.r != d.s || d.separable) return false;
+  if (d.w % 4 != 0 || d.c % kMfCS != 0 || d.k % 4 != 0 || (!any_k && d.k != 4)) return false;
+  if (pick_mf<false, false>(d.r, d.c) == nullptr) return false;
+  // 32-bit buffer offsets: one image's input and output planes, and the weights.
+  const double img_bytes = 4.0 * d.c * (double)d.h * d.w;
+  const double out_bytes = 4.0 * d.k * (double)d.h * d.w;
+  const double w_bytes = 4.0 * d.k * d.c * d.r * d.s;
+  if (img_bytes >= 4.0e9 || out_bytes >= 4.0e9 || w_bytes >= 2.0e9) return false;
+  p.kid = kMultiMfmaF32;
+  p.name = "is_k2_multi_mfma";
+  p.nseg = (d.w + kTW - 1) / kTW;
+  p.nstrip = (d.h + kTH - 1) / kTH;
+  p.strip_rows = 4;      // output channels per workgroup
+  p.vec = kMfCS;         // input channels per LDS slab
+  const long long tiles = (long long)p.nseg * p.nstrip * (d.k / 4) * d.n;
+  if (tiles > (1LL << 31) - 1) return false;
+  p.ntiles = (int)tiles;
+  p.grid_x = p.ntiles;
+  p.grid_y = p.grid_z = 1;
+  p.block = kThreads;
+  p.lds = kMfNB * 16 * (d.r == 3 ? MGeo<3, kMfCS>::BUFV4 : MGeo<5, kMfCS>::BUFV4);
+  p.tile_w = kTW;
+  p.tile_h = kTH;
+  return true;
+}
+
+hipError_t launch_multi_mf(const Plan &p, const float *x, const float *w, const float *b, float *y,
+                           hipStream_t s) {
+  const conv2d_desc &d = p.d;
+  const K2Fn fn = d.relu ? pick_mf<true, false>(d.r, d.c) : pick_mf<false, false>(d.r, d.c);
+  if (p.kid != kMultiMfmaF32 || !fn) return hipErrorInvalidValue;
+  return launch_kernel(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, d.c, d.h, d.w, d.k, p.nseg,
+                       p.nstrip, d.k / 4, p.ntiles);
+}
+
 bool multi_d2s_supported(const Plan &p) {
-  return p.kid == kMultiChannel && p.d.k == 4 && pick_d2s<false>(p.d.r, p.strip_rows, p.vec) != nullptr;
+  if (p.d.k != 4) return false;
+  if (p.kid == kMultiMfmaF32) return pick_mf<false, true>(p.d.r, p.d.c) != nullptr;
+  return p.kid == kMultiChannel && pick_d2s<false>(p.d.r, p.strip_rows, p.vec) != nullptr;
 }
 
 hipError_t launch_multi_d2s(const Plan &p, const float *x, const float *w, const float *b, float *y,
@@ -381,7 +675,11 @@ hipError_t launch_multi_d2s(const Plan &p, const float *x, const float *w, const
   const conv2d_desc &d = p.d;
   if (!multi_d2s_supported(p)) return hipErrorInvalidValue;
   const int ft = p.strip_rows, cs = p.vec;
-  const K2Fn fn = d.relu ? pick_d2s<true>(d.r, ft, cs) : pick_d2s<false>(d.r, ft, cs);
+  K2Fn fn;
+  if (p.kid == kMultiMfmaF32)
+    fn = d.relu ? pick_mf<true, true>(d.r, d.c) : pick_mf<false, true>(d.r, d.c);
+  else
+    fn = d.relu ? pick_d2s<true>(d.r, ft, cs) : pick_d2s<false>(d.r, ft, cs);
   return launch_kernel(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, d.c, d.h, d.w, d.k, p.nseg,
                        p.nstrip, d.k / ft, p.ntiles);
 }

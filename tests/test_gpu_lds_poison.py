@@ -67,6 +67,8 @@ LAYERS = [
     (1, 1, 64, 67, 129, 5, "f16", True, "is_k6_head_f16"),
     (2, 1, 32, 37, 132, 5, "f32", True, "is_k9_head_f32"),
     (1, 1, 16, 19, 68, 3, "f32", False, "is_k9_head_f32"),
+    (1, 32, 4, 37, 132, 3, "f32", True, "is_k2_multi_mfma"),
+    (2, 6, 4, 21, 72, 5, "f32", False, "is_k2_multi_mfma"),
 ]
 
 
@@ -102,15 +104,20 @@ def _chain(d, x, layers, y, ws_bytes):
     return host(y)
 
 
-def test_fused_fp32_chain_in_the_poison_build():
+@pytest.mark.parametrize("mode", ["fused", "unfused"])
+def test_fp32_chain_in_the_poison_build(mode):
+    """The upscaling chain in one launch (FUSED), or layer by layer (UNFUSED:
+    the first-layer kernel, two 32 -> 32 MFMA layers and the 4-filter
+    matrix-core layer with the depth-to-space in its stores)."""
     import torch
     x, layers = synth.chain_f32(N=1, H=37, W=120, seed=5)
     spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
-    d = isa.make_chain_desc(1, 37, 120, spec, 2, isa.IS_CHAIN_FUSED)
+    d = isa.make_chain_desc(1, 37, 120, spec, 2, isa.IS_CHAIN_FUSED if mode == "fused" else isa.IS_CHAIN_UNFUSED)
+    ws_bytes = 0 if mode == "fused" else isa.conv_chain_workspace_size(d)
     y = torch.full((1, 1, 74, 240), float("nan"), device="cuda")
-    got = _chain(d, x, layers, y, 0)
+    got = _chain(d, x, layers, y, ws_bytes)
     ref, m = oracle.chain(x, layers, d2s=2)
-    check(got, ref, m, TAU_F32, "poison fused chain")
+    check(got, ref, m, TAU_F32, "poison %s chain" % mode)
 
 
 @pytest.mark.parametrize("mode", ["auto", "unfused"])

@@ -1,11 +1,12 @@
 """GPU parity of multi-channel fp32 NCHW layers against the oracle.
 
 Calls go through the C ABI. Shapes span several tiles with ragged edges (64x16
-for the register-blocked kernel, 32 columns x 13 rows for the fp32 MFMA kernel
-that takes the 32 -> 32 3x3 layers, 64 columns x 16 rows for the fp32 MFMA
-first layer that takes one input channel to 16, 32 or 64), channel counts that
-fill one or several LDS slabs, every output-channel group size, and the full
-1x32x720x1280 layer (every output, so every 13-row tile seam).
+for the register-blocked kernel and its 4-filter matrix-core form, 32 columns x
+13 rows for the fp32 MFMA kernel that takes the 32 -> 32 3x3 layers, 64 columns
+x 16 rows for the fp32 MFMA first layer that takes one input channel to 16, 32
+or 64), channel counts that fill one or several LDS slabs, every output-channel
+group size, and the full 1x32x720x1280 layer (every output, so every 13-row tile
+seam). The 4-filter matrix-core form must also reproduce the vector form's bits.
 """
 import numpy as np
 import pytest
@@ -42,13 +43,24 @@ CASES = [
     (1, 32, 32, 9, 30, 3, False, "is_k0_generic_nchw_f32"),
     (2, 8, 16, 37, 132, 3, False, "is_k2_multi"),
     (1, 4, 8, 17, 68, 3, True, "is_k2_multi"),
-    (1, 4, 4, 33, 64, 3, False, "is_k2_multi"),
+    (1, 4, 4, 33, 64, 3, False, "is_k2_multi_mfma"),
     (1, 1, 32, 40, 136, 5, True, "is_k9_head_f32"),
     (1, 8, 32, 21, 72, 5, False, "is_k2_multi"),
     (1, 1, 32, 19, 68, 3, True, "is_k9_head_f32"),
     (1, 12, 32, 16, 64, 1, False, "is_k8_pointwise"),
-    (1, 32, 4, 45, 140, 3, False, "is_k2_multi"),
+    (1, 32, 4, 45, 140, 3, False, "is_k2_multi_mfma"),
     (3, 3, 8, 9, 20, 3, True, "is_k2_multi"),
+    # 4 filters on the fp32 matrix cores: slabs of 2 channels through a ring of 4
+    # LDS buffers (the 32-channel layer's unrolled form and the general loop:
+    # 1, 3, 4, 5 and 17 slabs), 3x3 and 5x5, ragged tiles, several images
+    (2, 32, 4, 37, 132, 3, True, "is_k2_multi_mfma"),
+    (1, 32, 4, 16, 64, 3, False, "is_k2_multi_mfma"),
+    (3, 32, 4, 1, 4, 3, True, "is_k2_multi_mfma"),
+    (1, 2, 4, 21, 72, 3, True, "is_k2_multi_mfma"),
+    (2, 6, 4, 40, 136, 5, False, "is_k2_multi_mfma"),
+    (1, 8, 4, 33, 260, 5, True, "is_k2_multi_mfma"),
+    (1, 10, 4, 19, 68, 3, False, "is_k2_multi_mfma"),
+    (1, 34, 4, 17, 196, 3, True, "is_k2_multi_mfma"),
     # one input channel, F filters (F = 2 .. 12; 1x1, 3x3, 5x5)
     (1, 1, 4, 40, 136, 3, True, "is_k2_multi"),
     (2, 1, 8, 37, 132, 5, False, "is_k2_multi"),
@@ -144,6 +156,30 @@ def test_head_f32_no_bias_and_delta_weights():
     y = _run(x, wd, None, False, "is_k9_head_f32")
     ref, _ = oracle.conv2d(x, wd)
     np.testing.assert_array_equal(y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("N,C,H,W,R,relu", [(1, 32, 720, 1280, 3, False), (2, 32, 45, 140, 3, True),
+                                              (1, 6, 40, 136, 5, True), (1, 34, 17, 196, 3, False)])
+def test_mfma_four_filters_bits_of_vector_path(N, C, H, W, R, relu):
+    """The 4-filter layer's matrix-core form rounds every accumulation once, in
+    the vector form's order (channel, filter row, filter column), so the two
+    give the same bits; the 1280x720 case is the chain's last layer. Both are
+    also checked against the oracle."""
+    import torch
+    x, w, b = synth.cnn_layer_f32(N=N, C=C, K=4, H=H, W=W, R=R, seed=C + H)
+    d = isa.make_desc(N, C, H, W, 4, R, R, "f32", relu)
+    names = [(v["kernel"], v["param"]) for v in isa.conv2d_list_variants(d)]
+    assert names[0] == ("is_k2_multi_mfma", 0) and ("is_k2_multi", 4) in names, names
+    say("mfma vs vector", N, C, H, W, R, relu)
+    ys = []
+    for i in (0, names.index(("is_k2_multi", 4))):
+        y = torch.full((N, 4, H, W), float("nan"), dtype=torch.float32, device="cuda")
+        isa.Plan(d, variant=i).forward(dev(x), dev(w), dev(b), y)
+        ys.append(host(y))
+    np.testing.assert_array_equal(ys[0], ys[1])
+    ref, m = oracle.conv2d(x, w, b, relu)
+    ratio = check(ys[0], ref, m, TAU_F32, "mfma 4 filters N%d C%d %dx%d R%d" % (N, C, H, W, R))
+    say("max err/bound %.3g" % ratio)
 
 
 def test_cnn_layer_720p_full():

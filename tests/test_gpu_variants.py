@@ -33,6 +33,11 @@ def _case(name):
         x, w, b = synth.cnn_layer_f32(N=1, C=32, K=32, H=50, W=200, seed=4)
         d = isa.make_desc(1, 32, 50, 200, 32, 3, 3, "f32", True)
         return d, x, w, b, True, "NCHW", w, oracle.conv2d(x, w, b, True)
+    if name == "fp32_32to4":
+        # the matrix-core and vector forms of the 4-filter layer (ragged tiles, 2 images)
+        x, w, b = synth.cnn_layer_f32(N=2, C=32, K=4, H=45, W=140, seed=9)
+        d = isa.make_desc(2, 32, 45, 140, 4, 3, 3, "f32", True)
+        return d, x, w, b, True, "NCHW", w, oracle.conv2d(x, w, b, True)
     if name == "one_channel_8_filters":
         x, w, b = synth.cnn_layer_f32(N=2, C=1, K=8, H=40, W=136, R=5, seed=5)
         d = isa.make_desc(2, 1, 40, 136, 8, 5, 5, "f32", False)
@@ -68,8 +73,8 @@ def _run(plan, x, wk, b, d):
     return host(y), (xd, wd, bd, y)
 
 
-CASES = ["single_3x3", "separable_5x5", "fp32_32to32", "one_channel_8_filters", "pointwise_8to16", "fp16_64to64",
-         "fanout_2x5x5", "fanout_4x3x3_odd", "fanout_8x3x3", "fanout_4x1x1"]
+CASES = ["single_3x3", "separable_5x5", "fp32_32to32", "fp32_32to4", "one_channel_8_filters", "pointwise_8to16",
+         "fp16_64to64", "fanout_2x5x5", "fanout_4x3x3_odd", "fanout_8x3x3", "fanout_4x1x1"]
 
 
 @pytest.mark.parametrize("name", CASES)
