@@ -178,7 +178,8 @@ def test_mfma_four_filters_bits_of_vector_path(N, C, H, W, R, relu):
         ys.append(host(y))
     np.testing.assert_array_equal(ys[0], ys[1])
     ref, m = oracle.conv2d(x, w, b, relu)
-    ratio = check(ys[0], ref, m, TAU_F32, "mfma 4 filters N%d C%d %dx%d R%d" % (N, C, H, W, R))
+    ratio = check(ys[0], ref, m, TAU_F32, "mfma 4 filters N%d C%d %dx%d R%d%s"
+                  % (N, C, H, W, R, " (chain's last layer) full" if (H, W) == (720, 1280) else ""))
     say("max err/bound %.3g" % ratio)
 
 
