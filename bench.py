@@ -1141,6 +1141,25 @@ def mix_study(torch, stream_obj, iters=512):
         row = {"parts": "+".join(n for (b, n) in MIX_PARTS if mix & b), "ms": round(ms, 4)}
         if mix & 2:
             row["pflops"] = round(cus * 8 * iters * 72 * 16384 / (ms / 1e3) / 1e15, 3)
+        # The same stage on the 4-wave data flow (isp_mix4_rate: a wave holds 64
+        # output channels x half the k range; 12 products per operand read; the
+        # k halves summed through LDS), the same products per CU and round.
+        lib.isp_mix4_rate.argtypes = lib.isp_mix_rate.argtypes
+        rc = lib.isp_mix4_rate(mix, cus, iters, stamps.data_ptr(), sink.data_ptr(), gbuf.data_ptr(),
+                               stream_obj.cuda_stream)
+        if rc != 0:
+            raise RuntimeError("isp_mix4_rate: hipError_t %d" % rc)
+        torch.cuda.synchronize()
+        e0.record(stream_obj)
+        for _ in range(5):
+            lib.isp_mix4_rate(mix, cus, iters, stamps.data_ptr(), sink.data_ptr(), gbuf.data_ptr(),
+                              stream_obj.cuda_stream)
+        e1.record(stream_obj)
+        torch.cuda.synchronize()
+        ms4 = e0.elapsed_time(e1) / 5
+        row["ms_4wave"] = round(ms4, 4)
+        if mix & 2:
+            row["pflops_4wave"] = round(cus * 4 * iters * 144 * 16384 / (ms4 / 1e3) / 1e15, 3)
         out.append(row)
     return out
 

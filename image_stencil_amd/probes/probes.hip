@@ -386,6 +386,121 @@ __global__ __launch_bounds__(512, 1) void isp_mix_rate(int iters, unsigned long 
   }
 }
 
+// The same stage on another data flow, for comparison: 4 waves per CU (one per
+// SIMD), each holding 64 output channels x half the k range (input channels
+// 32*kh .. +32 of all 9 taps: 36 A fragments), so one 16-byte operand read
+// feeds 12 MFMAs (4 channel blocks x 3 accumulating rows) instead of 3. The two
+// k halves of an output row are summed through LDS: when a row is final the
+// kh = 1 waves write their fp32 partial sums (4 x 16 bytes per lane) and the
+// kh = 0 waves read and add them before rounding to fp16 and staging the row.
+// MIX bits as above (4: the partial-sum exchange with the staging writes); per
+// round (4 input rows) each wave makes 12 operand reads and 144 MFMAs, so a
+// CU does 576 MFMAs per round as in isp_mix_rate. gbuf holds 64 KB per
+// workgroup; LDS addresses stay below 128 KB.
+template <int MIX>
+__global__ __launch_bounds__(256, 1) void isp_mix4_rate(int iters, unsigned long long *stamps, float *sink,
+                                                        char *gbuf) {
+  constexpr int kSteps4 = 12;   // 4 input rows x 3 filter columns
+  __shared__ __attribute__((aligned(16))) char lds[kMixLdsBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int kh = wave >> 1;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(gbuf + (size_t)blockIdx.x * 65536, (short)0, 65536, 0x00020000);
+  for (int i = tid; i < kMixLdsBytes / 4; i += blockDim.x)
+    reinterpret_cast<float *>(lds)[i] = (float)(i & 255) * (1.f / 256);
+  __syncthreads();
+  half8 wa[36];
+#pragma unroll
+  for (int k = 0; k < 36; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wa[k][e] = (_Float16)((int)(hash32(tid * 512 + k * 8 + e) & 255) / 256.f);
+  const int rbase = wave * kSteps4 * 1024 + lane * 16;            // reads below 48 KB + 1.1 KB
+  const int pbase = 50 * 1024 + (wave & 1) * 4096 + lane * 16;    // partial sums below 68 KB
+  const int sbase = 72 * 1024 + wave * 2048 + lane * 8;           // staging below 80 KB
+  half8 ring[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ring[q] = *reinterpret_cast<const half8 *>(lds + rbase + q * 1024);
+  float4v acc[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[b][j] = float4v{0.f, 0.f, 0.f, 0.f};
+  const unsigned long long c0 = clock64(), r0 = wall_clock64();
+  for (int it = 0; it < iters; ++it) {
+    static_for_seq([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      if constexpr ((MIX & 16) && q % 3 == 1)
+        __builtin_amdgcn_raw_buffer_store_b128(uint4v{(unsigned)it, (unsigned)lane, (unsigned)q, 1u}, rs,
+                                               (wave * 4 + q / 3) * 1024 + lane * 16, 0, 2);
+      if constexpr ((MIX & 32) && q % 3 == 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void *)(lds + 96 * 1024 + (wave * 4 + q / 3) * 1024), 16,
+            32768 + (wave * 4 + q / 3) * 1024 + lane * 16, 0, 0, 2);
+      const half8 b = ring[q % 4];
+      if constexpr (MIX & 1)
+        ring[q % 4] = *reinterpret_cast<const half8 *>(lds + rbase + ((q + 4) % kSteps4) * 1024 + (it & 7) * 16);
+      constexpr int i = q / 3, v = q % 3;
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          if constexpr (MIX & 2)
+            acc[blk][(i - u) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[blk * 9 + 3 * u + v], b,
+                                                                            acc[blk][(i - u) & 3], 0, 0, 0);
+          else
+            acc[blk][(i - u) & 3][0] += (float)b[0];
+        }
+      if constexpr (v == 2) {   // output row i - 2 is final in every block
+        constexpr int o = (i - 2) & 3;
+        if constexpr (MIX & 4) {
+          char *pp = lds + pbase + (it & 1) * 8192;
+          if (kh) {
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) *reinterpret_cast<float4v *>(pp + blk * 1024) = acc[blk][o];
+          } else {
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+              const float4v pv = *reinterpret_cast<const float4v *>(pp + blk * 1024 + 2048);
+              _Float16 hv[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(acc[blk][o][e] + pv[e]);
+              *reinterpret_cast<uint2v *>(lds + sbase + blk * 512 + (it & 1) * 256) = __builtin_bit_cast(uint2v, hv);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) acc[blk][(o + 1) & 3][1] += acc[blk][o][2];
+        }
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) acc[blk][o] = float4v{0.f, 0.f, 0.f, 0.f};
+      }
+    }, std::make_integer_sequence<int, kSteps4>{});
+    __asm__ volatile("" ::: "memory");
+    if constexpr (MIX & 8) {
+      if constexpr (MIX & 32) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: the loads have landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);                            // lgkmcnt 0
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+    }
+  }
+  const unsigned long long c1 = clock64(), r1 = wall_clock64();
+  float s = 0.f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += acc[b][j][0] + acc[b][j][1] + acc[b][j][2] + acc[b][j][3];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s += (float)ring[q][0];
+  __syncthreads();
+  sink[blockIdx.x * blockDim.x + tid] = s + lds[(tid * 16) % kMixLdsBytes];
+  if (lane == 0) {
+    const unsigned gw = blockIdx.x * 4 + wave;
+    stamps[2 * gw] = c1 - c0;
+    stamps[2 * gw + 1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -476,6 +591,20 @@ int isp_mix_rate(int mix, int grid, int iters, unsigned long long *stamps, float
     ISP_MIX(2) ISP_MIX(3) ISP_MIX(7) ISP_MIX(10) ISP_MIX(11) ISP_MIX(15) ISP_MIX(31) ISP_MIX(47) ISP_MIX(63)
     ISP_MIX(5) ISP_MIX(61)
 #undef ISP_MIX
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+// The 4-wave data flow (isp_mix4_rate): `grid` workgroups of 256 threads;
+// stamps 2 x (grid x 4) values, sink grid x 256 floats, gbuf grid x 64 KB.
+int isp_mix4_rate(int mix, int grid, int iters, unsigned long long *stamps, float *sink, char *gbuf, hipStream_t s) {
+  if (grid < 1 || iters < 1 || !stamps || !sink || !gbuf) return (int)hipErrorInvalidValue;
+  switch (mix) {
+#define IS_MIX4_CASE(M) \
+  case M: return (int)launch(isp_mix4_rate<M>, grid, 256, s, iters, stamps, sink, gbuf);
+    IS_MIX4_CASE(2) IS_MIX4_CASE(3) IS_MIX4_CASE(7) IS_MIX4_CASE(15) IS_MIX4_CASE(10) IS_MIX4_CASE(11)
+    IS_MIX4_CASE(31) IS_MIX4_CASE(47) IS_MIX4_CASE(63) IS_MIX4_CASE(5) IS_MIX4_CASE(61)
+#undef IS_MIX4_CASE
     default: return (int)hipErrorInvalidValue;
   }
 }
