@@ -69,9 +69,9 @@ bool configure_multi(Plan &p, int param = 0);
 hipError_t launch_multi(const Plan &p, const float *x, const float *w, const float *b, float *y,
                         hipStream_t s);
 // The multi-channel layer's products on the matrix cores, 4 filters per
-// workgroup (C even, K a multiple of 4, 3x3 or 5x5). The default plan takes it for
-// K = 4 only (any_k false); the tuning variants list it for any such K.
-bool configure_multi_mf(Plan &p, bool any_k = false);
+// workgroup (C even, K a multiple of 4, 3x3 or 5x5). The default plan takes it
+// from 4 input channels on (variant false); the tuning variants list it from 2.
+bool configure_multi_mf(Plan &p, bool variant = false);
 hipError_t launch_multi_mf(const Plan &p, const float *x, const float *w, const float *b, float *y,
                            hipStream_t s);
 // The multi-channel layer (either path) with 4 output channels followed by a

@@ -41,11 +41,16 @@ def _poison_lib():
     return _lib
 
 
-def _forward(d, x, w, b, y):
+def _forward(d, x, w, b, y, variant=None):
+    """variant: (kernel, param) of a tuning variant to run instead of the plan."""
     import torch
     lib = _poison_lib()
     plan = ctypes.c_void_p()
-    assert lib.conv2d_create(ctypes.byref(d), ctypes.byref(plan)) == 0
+    if variant is None:
+        assert lib.conv2d_create(ctypes.byref(d), ctypes.byref(plan)) == 0
+    else:
+        vs = [(v["kernel"], v["param"]) for v in isa.conv2d_list_variants(d)]
+        assert lib.conv2d_create_variant(ctypes.byref(d), vs.index(variant), ctypes.byref(plan)) == 0
     info = _abi.conv2d_plan_info()
     assert lib.conv2d_get_plan_info(plan, ctypes.byref(info)) == 0
     st = lib.conv2d_forward(plan, x.data_ptr(), w.data_ptr(), b.data_ptr() if b is not None else None,
@@ -57,7 +62,7 @@ def _forward(d, x, w, b, y):
 
 LAYERS = [
     # (N, C, K, H, W, R, dtype, relu, expected kernel)
-    (1, 8, 16, 37, 132, 3, "f32", True, "is_k2_multi"),
+    (1, 8, 16, 37, 132, 3, "f32", True, "is_k2_multi_mfma"),
     (2, 1, 8, 40, 136, 5, "f32", False, "is_k2_multi"),
     (1, 32, 32, 50, 200, 3, "f32", True, "is_k5_mfma_f32"),
     (1, 16, 8, 33, 132, 1, "f32", False, "is_k8_pointwise"),
@@ -86,6 +91,24 @@ def test_layer_in_the_poison_build(N, C, K, H, W, R, dtype, relu, kernel):
     assert _forward(d, dev(x), dev(w), dev(b), y) == kernel
     ref, m = oracle.conv2d(x, w, b, relu, "NHWC" if dtype == "f16" else "NCHW")
     check(host(y), ref, m, TAU_F16 if dtype == "f16" else TAU_F32, "poison %s" % kernel)
+
+
+@pytest.mark.parametrize("N,C,K,H,W,R,relu,variant", [
+    (1, 32, 32, 37, 132, 3, True, ("is_k2_multi", 32)),   # 4-channel slabs, 32 filters per workgroup
+    (2, 8, 8, 21, 72, 3, False, ("is_k2_multi", 8)),
+    (1, 12, 4, 19, 68, 3, True, ("is_k2_multi", 4)),
+])
+def test_vector_multichannel_variants_in_the_poison_build(N, C, K, H, W, R, relu, variant):
+    """The register-blocked kernel's vector form over 4-channel slabs, which the
+    plans now leave to its matrix-core form, run as a tuning variant."""
+    import torch
+    say("lds poison variant", N, C, K, H, W, R, variant)
+    x, w, b = synth.cnn_layer_f32(N=N, C=C, K=K, H=H, W=W, R=R, seed=C + K + H)
+    y = torch.full((N, K, H, W), float("nan"), dtype=torch.float32, device="cuda")
+    d = isa.make_desc(N, C, H, W, K, R, R, "f32", relu)
+    assert _forward(d, dev(x), dev(w), dev(b), y, variant) == variant[0]
+    ref, m = oracle.conv2d(x, w, b, relu)
+    check(host(y), ref, m, TAU_F32, "poison %s/%d" % variant)
 
 
 def _chain(d, x, layers, y, ws_bytes):

@@ -41,22 +41,24 @@ CASES = [
     (1, 32, 32, 1, 4, 3, True, "is_k5_mfma_f32"),
     (1, 32, 32, 33, 260, 3, False, "is_k5_mfma_f32"),
     (1, 32, 32, 9, 30, 3, False, "is_k0_generic_nchw_f32"),
-    (2, 8, 16, 37, 132, 3, False, "is_k2_multi"),
-    (1, 4, 8, 17, 68, 3, True, "is_k2_multi"),
+    (2, 8, 16, 37, 132, 3, False, "is_k2_multi_mfma"),
+    (1, 4, 8, 17, 68, 3, True, "is_k2_multi_mfma"),
     (1, 4, 4, 33, 64, 3, False, "is_k2_multi_mfma"),
     (1, 1, 32, 40, 136, 5, True, "is_k9_head_f32"),
-    (1, 8, 32, 21, 72, 5, False, "is_k2_multi"),
+    (1, 8, 32, 21, 72, 5, False, "is_k2_multi_mfma"),
     (1, 1, 32, 19, 68, 3, True, "is_k9_head_f32"),
     (1, 12, 32, 16, 64, 1, False, "is_k8_pointwise"),
     (1, 32, 4, 45, 140, 3, False, "is_k2_multi_mfma"),
     (3, 3, 8, 9, 20, 3, True, "is_k2_multi"),
+    (2, 2, 8, 21, 72, 3, False, "is_k2_multi"),
+    (1, 12, 8, 19, 68, 5, False, "is_k2_multi_mfma"),
     # 4 filters on the fp32 matrix cores: slabs of 2 channels through a ring of 4
     # LDS buffers (the 32-channel layer's unrolled form and the general loop:
     # 1, 3, 4, 5 and 17 slabs), 3x3 and 5x5, ragged tiles, several images
     (2, 32, 4, 37, 132, 3, True, "is_k2_multi_mfma"),
     (1, 32, 4, 16, 64, 3, False, "is_k2_multi_mfma"),
     (3, 32, 4, 1, 4, 3, True, "is_k2_multi_mfma"),
-    (1, 2, 4, 21, 72, 3, True, "is_k2_multi_mfma"),
+    (1, 2, 4, 21, 72, 3, True, "is_k2_multi"),
     (2, 6, 4, 40, 136, 5, False, "is_k2_multi_mfma"),
     (1, 8, 4, 33, 260, 5, True, "is_k2_multi_mfma"),
     (1, 10, 4, 19, 68, 3, False, "is_k2_multi_mfma"),
@@ -107,7 +109,7 @@ def test_multichannel_shapes(N, C, K, H, W, R, relu, kernel):
 
 def test_no_bias():
     x, w, _ = synth.cnn_layer_f32(N=1, C=8, K=8, H=20, W=64, seed=2)
-    y = _run(x, w, None, False, "is_k2_multi")
+    y = _run(x, w, None, False, "is_k2_multi_mfma")
     ref, m = oracle.conv2d(x, w, None, False)
     check(y, ref, m, TAU_F32, "no bias")
 
@@ -119,7 +121,7 @@ def test_delta_weights_bit_exact():
     rng = np.random.default_rng(4)
     for k in range(8):
         w[k, rng.integers(0, 8), rng.integers(0, 3), rng.integers(0, 3)] = 1.0
-    y = _run(x, w, None, False, "is_k2_multi")
+    y = _run(x, w, None, False, "is_k2_multi_mfma")
     ref, _ = oracle.conv2d(x, w)
     np.testing.assert_array_equal(y.astype(np.float64), ref)
 
@@ -158,28 +160,34 @@ def test_head_f32_no_bias_and_delta_weights():
     np.testing.assert_array_equal(y.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("N,C,H,W,R,relu", [(1, 32, 720, 1280, 3, False), (2, 32, 45, 140, 3, True),
-                                              (1, 6, 40, 136, 5, True), (1, 34, 17, 196, 3, False)])
-def test_mfma_four_filters_bits_of_vector_path(N, C, H, W, R, relu):
-    """The 4-filter layer's matrix-core form rounds every accumulation once, in
-    the vector form's order (channel, filter row, filter column), so the two
-    give the same bits; the 1280x720 case is the chain's last layer. Both are
-    also checked against the oracle."""
+@pytest.mark.parametrize("N,C,K,H,W,R,relu", [(1, 32, 4, 720, 1280, 3, False), (2, 32, 4, 45, 140, 3, True),
+                                                (1, 6, 4, 40, 136, 5, True), (1, 34, 4, 17, 196, 3, False),
+                                                (1, 8, 8, 33, 132, 3, True), (2, 16, 16, 21, 72, 3, False),
+                                                (1, 64, 32, 19, 68, 3, True), (1, 12, 8, 17, 68, 5, False)])
+def test_mfma_four_filters_bits_of_vector_path(N, C, K, H, W, R, relu):
+    """The matrix-core form (4 filters per workgroup) rounds every accumulation
+    once, in the vector form's order (channel, filter row, filter column), so
+    it gives the same bits as every vector variant (any channels per
+    workgroup); the 1280x720 case is the chain's last layer. The matrix-core
+    result is also checked against the oracle."""
     import torch
-    x, w, b = synth.cnn_layer_f32(N=N, C=C, K=4, H=H, W=W, R=R, seed=C + H)
-    d = isa.make_desc(N, C, H, W, 4, R, R, "f32", relu)
+    x, w, b = synth.cnn_layer_f32(N=N, C=C, K=K, H=H, W=W, R=R, seed=C + H + K)
+    d = isa.make_desc(N, C, H, W, K, R, R, "f32", relu)
     names = [(v["kernel"], v["param"]) for v in isa.conv2d_list_variants(d)]
-    assert names[0] == ("is_k2_multi_mfma", 0) and ("is_k2_multi", 4) in names, names
-    say("mfma vs vector", N, C, H, W, R, relu)
+    assert names[0] == ("is_k2_multi_mfma", 0), names
+    vec = [i for i, (k, _) in enumerate(names) if k == "is_k2_multi"]
+    assert vec or (R == 5 and K % 32 != 0 and C % 4 == 0), names
+    say("mfma vs vector", N, C, K, H, W, R, relu, [names[i] for i in vec])
     ys = []
-    for i in (0, names.index(("is_k2_multi", 4))):
-        y = torch.full((N, 4, H, W), float("nan"), dtype=torch.float32, device="cuda")
+    for i in [0] + vec:
+        y = torch.full((N, K, H, W), float("nan"), dtype=torch.float32, device="cuda")
         isa.Plan(d, variant=i).forward(dev(x), dev(w), dev(b), y)
         ys.append(host(y))
-    np.testing.assert_array_equal(ys[0], ys[1])
+    for j in range(1, len(ys)):
+        np.testing.assert_array_equal(ys[0], ys[j], err_msg=str(names[vec[j - 1]]))
     ref, m = oracle.conv2d(x, w, b, relu)
-    ratio = check(ys[0], ref, m, TAU_F32, "mfma 4 filters N%d C%d %dx%d R%d%s"
-                  % (N, C, H, W, R, " (chain's last layer) full" if (H, W) == (720, 1280) else ""))
+    ratio = check(ys[0], ref, m, TAU_F32, "mfma %d filters N%d C%d %dx%d R%d%s"
+                  % (K, N, C, H, W, R, " (chain's last layer) full" if (H, W) == (720, 1280) else ""))
     say("max err/bound %.3g" % ratio)
 
 

@@ -280,16 +280,25 @@ def test_tile_variants():
     assert names(isa.make_desc(1, 32, 720, 1280, 32, 3, 3, "f32", True)) == [
         ("is_k5_mfma_f32", 0, True), ("is_k2_multi", 32, False), ("is_k2_multi", 16, False),
         ("is_k2_multi", 8, False), ("is_k2_multi", 4, False), ("is_k2_multi_mfma", 0, False)]
-    # 4 output channels over an even channel count, 3x3 or 5x5: the register-blocked
-    # kernel's products on the fp32 matrix cores, the vector form as a variant; for
-    # other K that are multiples of 4 the matrix-core form is a variant only
+    # K a multiple of 4 over an even channel count from 4 on, 3x3 or 5x5: the
+    # register-blocked kernel's products on the fp32 matrix cores (4 filters per
+    # workgroup), its vector form among the variants; with 2 channels the vector
+    # form is the plan and the matrix-core form a variant
     assert names(isa.make_desc(1, 32, 720, 1280, 4, 3, 3, "f32")) == [
         ("is_k2_multi_mfma", 0, True), ("is_k2_multi", 4, False)]
     assert names(isa.make_desc(2, 6, 40, 136, 4, 5, 5, "f32", True)) == [
         ("is_k2_multi_mfma", 0, True), ("is_k2_multi", 4, False), ("is_k2_multi", 2, False)]
     assert names(isa.make_desc(1, 8, 64, 128, 8, 3, 3, "f32")) == [
-        ("is_k2_multi", 8, True), ("is_k2_multi", 4, False), ("is_k2_multi_mfma", 0, False)]
-    for (c, k, r, w) in ((3, 4, 3, 128), (32, 4, 7, 128), (32, 4, 3, 130), (32, 6, 3, 128)):
+        ("is_k2_multi_mfma", 0, True), ("is_k2_multi", 8, False), ("is_k2_multi", 4, False)]
+    assert names(isa.make_desc(1, 64, 64, 128, 32, 3, 3, "f32")) == [
+        ("is_k2_multi_mfma", 0, True), ("is_k2_multi", 32, False), ("is_k2_multi", 16, False),
+        ("is_k2_multi", 8, False), ("is_k2_multi", 4, False)]
+    # 5x5 with 8 filters per group, which the vector form does not instantiate
+    # over 4-channel slabs: the matrix-core form instead of the fallback
+    assert names(isa.make_desc(1, 32, 64, 128, 8, 5, 5, "f32")) == [("is_k2_multi_mfma", 0, True)]
+    assert names(isa.make_desc(1, 2, 64, 128, 8, 3, 3, "f32"))[0] == ("is_k2_multi", 8, True)
+    assert ("is_k2_multi_mfma", 0, False) in names(isa.make_desc(1, 2, 64, 128, 8, 3, 3, "f32"))
+    for (c, k, r, w) in ((3, 4, 3, 128), (32, 4, 7, 128), (32, 4, 3, 130), (32, 6, 3, 128), (2, 4, 3, 128)):
         assert isa.Plan(isa.make_desc(1, c, 64, w, k, r, r)).info()["kernel"] != "is_k2_multi_mfma", (c, k, r, w)
     assert isa.Plan(isa.make_desc(1, 32, 720, 1280, 4, 3, 3, "f32")).info()["lds_bytes"] == 53248
     assert names(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16")) == [
