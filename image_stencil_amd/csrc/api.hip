@@ -94,7 +94,8 @@ is_status make_plan(const conv2d_desc *d, is::Plan &p) {
     if (!is::configure_single(p)) return IS_ERR_UNSUPPORTED;
   } else if (!is::configure_single(p) && !is::configure_head_f32(p) && !is::configure_mfma_f32(p) &&
              !is::configure_pointwise(p) && !is::configure_multi_mf(p) &&
-             !is::configure_multi(p) && !is::configure_mfma(p) && !is::configure_head_f16(p)) {
+             !is::configure_multi(p) && !is::configure_mfma(p) && !is::configure_head_f16(p) &&
+             !is::configure_multi_mf(p, is::kMfLastResort)) {
     is::configure_generic(p);
   }
   if (log_enabled())
@@ -134,7 +135,7 @@ bool configure_variant(is::Plan &p, const conv2d_desc &d, const Variant &v) {
     case is::kPointwise: return is::configure_pointwise(p, v.param);
     case is::kHeadNhwcF16: return !d.separable && is::configure_head_f16(p);
     case is::kHeadNchwF32: return is::configure_head_f32(p);
-    case is::kMultiMfmaF32: return is::configure_multi_mf(p, true);
+    case is::kMultiMfmaF32: return is::configure_multi_mf(p, is::kMfVariant);
     default:
       if (d.separable) return false;
       is::configure_generic(p);

@@ -69,9 +69,12 @@ bool configure_multi(Plan &p, int param = 0);
 hipError_t launch_multi(const Plan &p, const float *x, const float *w, const float *b, float *y,
                         hipStream_t s);
 // The multi-channel layer's products on the matrix cores, 4 filters per
-// workgroup (C even, K a multiple of 4, 3x3 or 5x5). The default plan takes it
-// from 4 input channels on (variant false); the tuning variants list it from 2.
-bool configure_multi_mf(Plan &p, bool variant = false);
+// workgroup (any C and K, 3x3 or 5x5, W a multiple of 4). use: kMfPlan where it
+// is the plan's first choice (an even channel count from 4 on), kMfVariant for
+// the tuning variants (2 channels or more), kMfLastResort for the plan of
+// shapes that no other kernel but the one-thread-per-output fallback takes.
+enum { kMfPlan = 0, kMfVariant = 1, kMfLastResort = 2 };
+bool configure_multi_mf(Plan &p, int use = kMfPlan);
 hipError_t launch_multi_mf(const Plan &p, const float *x, const float *w, const float *b, float *y,
                            hipStream_t s);
 // The multi-channel layer (either path) with 4 output channels followed by a

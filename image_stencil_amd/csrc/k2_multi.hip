@@ -119,12 +119,15 @@ __device__ __forceinline__ void slab_offsets(unsigned *voff, int wave, int lane,
 }
 
 // Epilogue: bias, ReLU, 16-byte stores (dropped outside the image). acc[f][p]
-// is this lane's sum for filter kg * FT + f at output pixel (oy, ox + p).
+// is this lane's sum for filter kg * FT + f at output pixel (oy, ox + p);
+// filters from K on (a last group of the matrix-core form that K does not
+// fill) have no bias and their stores fall outside the output's range.
 template <int FT, bool RELU, bool D2S>
 __device__ __forceinline__ void store_tile(const float (&acc)[FT][4], const float *bias, float *y, int n,
                                            int kg, int K, int H, int W, int oy, int ox) {
   const size_t HW = (size_t)H * W;
   const bool in = oy < H && ox < W;
+  const int kv = min(FT, K - kg * FT);   // filters of this group that exist
   if constexpr (D2S) {
     static_assert(FT == 4, "depth-to-space takes 4 channels");
     // This lane's 4 columns of the 4 channels become 8 columns of output rows
@@ -160,10 +163,10 @@ __device__ __forceinline__ void store_tile(const float (&acc)[FT][4], const floa
   }
   float *yn = y + ((size_t)n * K + (size_t)kg * FT) * HW;
   const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
-      yn, (short)0, (int)(FT * HW * 4), kBufferFlags);
+      yn, (short)0, (int)(kv * HW * 4), kBufferFlags);
 #pragma unroll
   for (int f = 0; f < FT; ++f) {
-    const float b = bias ? bias[kg * FT + f] : 0.f;
+    const float b = (bias && f < kv) ? bias[kg * FT + f] : 0.f;
     float o[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -566,17 +569,24 @@ K2Fn pick_d2s(int r, int ft, int cs) {
 }
 
 // The matrix-core path: slabs of 2 channels in a ring of 4 buffers (3 slabs in
-// flight; 53 KB of LDS, so 3 workgroups per CU).
+// flight; 53 KB of LDS, so 3 workgroups per CU), or of 1 channel for odd
+// channel counts (37 KB).
 constexpr int kMfCS = 2;
 constexpr int kMfNB = 4;
 template <bool RELU, bool D2S>
 K2Fn pick_mf(int r, int c) {
-  if (r == 3) {
-    if (c == 32) return is_k2_multi_mfma<3, kMfCS, kMfNB, 32 / kMfCS, RELU, D2S>;
-    return is_k2_multi_mfma<3, kMfCS, kMfNB, 0, RELU, D2S>;
+  if (c % kMfCS == 0) {
+    if (r == 3) {
+      if (c == 32) return is_k2_multi_mfma<3, kMfCS, kMfNB, 32 / kMfCS, RELU, D2S>;
+      return is_k2_multi_mfma<3, kMfCS, kMfNB, 0, RELU, D2S>;
+    }
+    if constexpr (!D2S)
+      if (r == 5) return is_k2_multi_mfma<5, kMfCS, kMfNB, 0, RELU, D2S>;
+    return nullptr;
   }
+  if (r == 3) return is_k2_multi_mfma<3, 1, kMfNB, 0, RELU, D2S>;
   if constexpr (!D2S)
-    if (r == 5) return is_k2_multi_mfma<5, kMfCS, kMfNB, 0, RELU, D2S>;
+    if (r == 5) return is_k2_multi_mfma<5, 1, kMfNB, 0, RELU, D2S>;
   return nullptr;
 }
 
@@ -627,16 +637,21 @@ bool configure_multi(Plan &p, int param) {
   return true;
 }
 
-bool configure_multi_mf(Plan &p, bool variant) {
+bool configure_multi_mf(Plan &p, int use) {
   const conv2d_desc &d = p.d;
   if (d.layout != IS_NCHW || d.in_dtype != IS_F32 || d.r != d.s || d.separable) return false;
-  if (d.w % 4 != 0 || d.c % kMfCS != 0 || d.k % 4 != 0) return false;
-  // The default plan for 4 or more channels: measured on 1280x720 it beats the
-  // vector form at every such shape tried (32 -> 8 3x3: 61 against 84 us;
-  // 64 -> 16: 228 against 284-344; 32 -> 64: 432 against 505-635; 5x5 layers,
-  // which the vector form takes only for some channel groups, 144-146 us), and
-  // loses only with 2 channels, one slab per tile (11.5 against 9.2 us).
-  if (!variant && d.c < 4) return false;
+  if (d.w % 4 != 0) return false;
+  // The default plan for an even channel count from 4 on: measured on 1280x720
+  // it beats the vector form at every such shape tried (32 -> 8 3x3: 61 against
+  // 84 us; 64 -> 16: 228 against 284-344; 32 -> 64: 432 against 505-635; 5x5
+  // layers, which the vector form takes only for some channel groups, 144-146
+  // us), and loses only with 2 channels, one slab per tile (11.5 against 9.2
+  // us). Odd and smaller channel counts keep the vector form (which reads the
+  // input once for all its filters), with this form among the variants from 2
+  // channels on; the plan falls back to it for the shapes that no other kernel
+  // but the one-thread-per-output fallback takes.
+  if (use == kMfPlan && (d.c < 4 || d.c % kMfCS != 0)) return false;
+  if (use == kMfVariant && d.c < 2) return false;
   if (pick_mf<false, false>(d.r, d.c) == nullptr) return false;
   // 32-bit buffer offsets: one image's input and output planes, and the weights.
   const double img_bytes = 4.0 * d.c * (double)d.h * d.w;
@@ -648,14 +663,16 @@ bool configure_multi_mf(Plan &p, bool variant) {
   p.nseg = (d.w + kTW - 1) / kTW;
   p.nstrip = (d.h + kTH - 1) / kTH;
   p.strip_rows = 4;      // output channels per workgroup
-  p.vec = kMfCS;         // input channels per LDS slab
-  const long long tiles = (long long)p.nseg * p.nstrip * (d.k / 4) * d.n;
+  const int cs = d.c % kMfCS == 0 ? kMfCS : 1;
+  p.vec = cs;            // input channels per LDS slab
+  const long long tiles = (long long)p.nseg * p.nstrip * ((d.k + 3) / 4) * d.n;
   if (tiles > (1LL << 31) - 1) return false;
   p.ntiles = (int)tiles;
   p.grid_x = p.ntiles;
   p.grid_y = p.grid_z = 1;
   p.block = kThreads;
-  p.lds = kMfNB * 16 * (d.r == 3 ? MGeo<3, kMfCS>::BUFV4 : MGeo<5, kMfCS>::BUFV4);
+  p.lds = kMfNB * 16 * (cs == kMfCS ? (d.r == 3 ? MGeo<3, kMfCS>::BUFV4 : MGeo<5, kMfCS>::BUFV4)
+                                    : (d.r == 3 ? MGeo<3, 1>::BUFV4 : MGeo<5, 1>::BUFV4));
   p.tile_w = kTW;
   p.tile_h = kTH;
   return true;
@@ -667,7 +684,7 @@ hipError_t launch_multi_mf(const Plan &p, const float *x, const float *w, const 
   const K2Fn fn = d.relu ? pick_mf<true, false>(d.r, d.c) : pick_mf<false, false>(d.r, d.c);
   if (p.kid != kMultiMfmaF32 || !fn) return hipErrorInvalidValue;
   return launch_kernel(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, d.c, d.h, d.w, d.k, p.nseg,
-                       p.nstrip, d.k / 4, p.ntiles);
+                       p.nstrip, (d.k + 3) / 4, p.ntiles);
 }
 
 bool multi_d2s_supported(const Plan &p) {

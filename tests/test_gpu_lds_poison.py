@@ -74,6 +74,8 @@ LAYERS = [
     (1, 1, 16, 19, 68, 3, "f32", False, "is_k9_head_f32"),
     (1, 32, 4, 37, 132, 3, "f32", True, "is_k2_multi_mfma"),
     (2, 6, 4, 21, 72, 5, "f32", False, "is_k2_multi_mfma"),
+    (1, 32, 3, 37, 132, 3, "f32", True, "is_k2_multi_mfma"),
+    (2, 5, 3, 21, 72, 5, "f32", False, "is_k2_multi_mfma"),
 ]
 
 
