@@ -172,6 +172,16 @@ int collect_variants(const conv2d_desc &d, const is::Plan &def, Variant *out, in
 
 constexpr int kMaxVariants = 32;
 
+// Plan of variant i: the default plan itself for i = 0 (a kernel family can
+// take a shape as the plan's last resort that its variant listing leaves out),
+// else the family's configuration.
+void variant_plan(is::Plan &p, const conv2d_desc &d, const is::Plan &def, const Variant *v, int i) {
+  if (i == 0)
+    p = def;
+  else
+    configure_variant(p, d, v[i]);
+}
+
 void fill_variant(const is::Plan &p, bool is_default, float ms, conv2d_variant *out) {
   memset(out, 0, sizeof(*out));
   snprintf(out->kernel, sizeof(out->kernel), "%s", p.name);
@@ -719,7 +729,7 @@ is_status conv2d_list_variants(const conv2d_desc *d, conv2d_variant *out, int ma
     *count = n;
     for (int i = 0; i < n && i < max; ++i) {
       is::Plan p;
-      configure_variant(p, *d, v[i]);
+      variant_plan(p, *d, def, v, i);
       fill_variant(p, i == 0, 0.f, &out[i]);
     }
     return IS_OK;
@@ -740,7 +750,7 @@ is_status conv2d_create_variant(const conv2d_desc *d, int index, conv2d_plan *ou
     if (index < 0 || index >= n) return IS_ERR_INVALID_ARG;
     conv2d_plan_s *h = new (std::nothrow) conv2d_plan_s;
     if (!h) return IS_ERR_NO_MEMORY;
-    configure_variant(h->p, *d, v[index]);
+    variant_plan(h->p, *d, def, v, index);
     *out = h;
     return IS_OK;
   } catch (...) {
@@ -770,7 +780,7 @@ is_status conv2d_autotune(conv2d_plan plan, const void *x, const void *w, const 
     is::Plan best_plan;
     for (int i = 0; i < n && st == IS_OK; ++i) {
       is::Plan p;
-      configure_variant(p, d, v[i]);
+      variant_plan(p, d, def, v, i);
       st = run_plan(p, x, w, bias, y, stream);   // warm-up; also checks the arguments
       if (st != IS_OK) break;
       hipError_t e = hipEventRecord(e0, stream);

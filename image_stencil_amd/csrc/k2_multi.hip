@@ -1,4 +1,5 @@
-// k2_multi.hip -- multi-channel fp32 NCHW layer, square odd filters r = s in {1, 3, 5}.
+// k2_multi.hip -- multi-channel fp32 NCHW layer, square odd filters r = s in {1, 3, 5}
+// (and 7 in the matrix-core form at the end of the file).
 //
 // The "general case" kernel of "Optimizing Memory Efficiency for Convolution
 // Kernels on Kepler GPUs" (arXiv 1705.10591; its Algorithm 2 and the sections
@@ -573,9 +574,12 @@ K2Fn pick_d2s(int r, int ft, int cs) {
 // channel counts (37 KB).
 constexpr int kMfCS = 2;
 constexpr int kMfNB = 4;
+// Channels per slab: 2, or 1 for odd channel counts and for 7x7 filters (whose
+// 2-channel slabs need 181 VGPRs and 72 KB of LDS: 2 workgroups per CU against 4).
+int mf_slab_channels(int r, int c) { return (c % kMfCS == 0 && r != 7) ? kMfCS : 1; }
 template <bool RELU, bool D2S>
 K2Fn pick_mf(int r, int c) {
-  if (c % kMfCS == 0) {
+  if (mf_slab_channels(r, c) == kMfCS) {
     if (r == 3) {
       if (c == 32) return is_k2_multi_mfma<3, kMfCS, kMfNB, 32 / kMfCS, RELU, D2S>;
       return is_k2_multi_mfma<3, kMfCS, kMfNB, 0, RELU, D2S>;
@@ -585,8 +589,10 @@ K2Fn pick_mf(int r, int c) {
     return nullptr;
   }
   if (r == 3) return is_k2_multi_mfma<3, 1, kMfNB, 0, RELU, D2S>;
-  if constexpr (!D2S)
+  if constexpr (!D2S) {
     if (r == 5) return is_k2_multi_mfma<5, 1, kMfNB, 0, RELU, D2S>;
+    if (r == 7) return is_k2_multi_mfma<7, 1, kMfNB, 0, RELU, D2S>;
+  }
   return nullptr;
 }
 
@@ -650,7 +656,7 @@ bool configure_multi_mf(Plan &p, int use) {
   // input once for all its filters), with this form among the variants from 2
   // channels on; the plan falls back to it for the shapes that no other kernel
   // but the one-thread-per-output fallback takes.
-  if (use == kMfPlan && (d.c < 4 || d.c % kMfCS != 0)) return false;
+  if (use == kMfPlan && (d.c < 4 || d.c % kMfCS != 0) && !(d.r == 7 && d.c >= 2)) return false;
   if (use == kMfVariant && d.c < 2) return false;
   if (pick_mf<false, false>(d.r, d.c) == nullptr) return false;
   // 32-bit buffer offsets: one image's input and output planes, and the weights.
@@ -663,7 +669,7 @@ bool configure_multi_mf(Plan &p, int use) {
   p.nseg = (d.w + kTW - 1) / kTW;
   p.nstrip = (d.h + kTH - 1) / kTH;
   p.strip_rows = 4;      // output channels per workgroup
-  const int cs = d.c % kMfCS == 0 ? kMfCS : 1;
+  const int cs = mf_slab_channels(d.r, d.c);
   p.vec = cs;            // input channels per LDS slab
   const long long tiles = (long long)p.nseg * p.nstrip * ((d.k + 3) / 4) * d.n;
   if (tiles > (1LL << 31) - 1) return false;
@@ -672,7 +678,8 @@ bool configure_multi_mf(Plan &p, int use) {
   p.grid_y = p.grid_z = 1;
   p.block = kThreads;
   p.lds = kMfNB * 16 * (cs == kMfCS ? (d.r == 3 ? MGeo<3, kMfCS>::BUFV4 : MGeo<5, kMfCS>::BUFV4)
-                                    : (d.r == 3 ? MGeo<3, 1>::BUFV4 : MGeo<5, 1>::BUFV4));
+                                    : (d.r == 3 ? MGeo<3, 1>::BUFV4
+                                                : (d.r == 5 ? MGeo<5, 1>::BUFV4 : MGeo<7, 1>::BUFV4)));
   p.tile_w = kTW;
   p.tile_h = kTH;
   return true;

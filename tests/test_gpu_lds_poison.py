@@ -76,6 +76,7 @@ LAYERS = [
     (2, 6, 4, 21, 72, 5, "f32", False, "is_k2_multi_mfma"),
     (1, 32, 3, 37, 132, 3, "f32", True, "is_k2_multi_mfma"),
     (2, 5, 3, 21, 72, 5, "f32", False, "is_k2_multi_mfma"),
+    (1, 6, 5, 21, 72, 7, "f32", True, "is_k2_multi_mfma"),
 ]
 
 

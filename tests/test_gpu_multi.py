@@ -63,6 +63,12 @@ CASES = [
     (2, 5, 3, 37, 132, 3, True, "is_k2_multi_mfma"),
     (1, 3, 7, 21, 72, 5, False, "is_k2_multi_mfma"),
     (1, 7, 3, 17, 68, 5, True, "is_k2_multi_mfma"),
+    # 7x7 over 1-channel slabs (the vector form has no 7x7)
+    (1, 8, 8, 37, 132, 7, True, "is_k2_multi_mfma"),
+    (2, 3, 5, 21, 72, 7, False, "is_k2_multi_mfma"),
+    (1, 2, 16, 19, 68, 7, True, "is_k2_multi_mfma"),
+    (1, 1, 4, 33, 136, 7, False, "is_k2_multi_mfma"),
+    (1, 32, 4, 17, 196, 7, True, "is_k2_multi_mfma"),
     # 4 filters on the fp32 matrix cores: slabs of 2 channels through a ring of 4
     # LDS buffers (the 32-channel layer's unrolled form and the general loop:
     # 1, 3, 4, 5 and 17 slabs), 3x3 and 5x5, ragged tiles, several images

@@ -301,19 +301,24 @@ def test_tile_variants():
     assert names(isa.make_desc(1, 32, 64, 128, 8, 5, 5, "f32")) == [("is_k2_multi_mfma", 0, True)]
     assert names(isa.make_desc(1, 2, 64, 128, 8, 3, 3, "f32"))[0] == ("is_k2_multi", 8, True)
     assert ("is_k2_multi_mfma", 0, False) in names(isa.make_desc(1, 2, 64, 128, 8, 3, 3, "f32"))
-    for (c, k, r, w) in ((3, 4, 3, 128), (32, 4, 7, 128), (32, 4, 3, 130), (2, 4, 3, 128), (5, 3, 3, 126)):
+    for (c, k, r, w) in ((3, 4, 3, 128), (32, 4, 3, 130), (2, 4, 3, 128), (5, 3, 3, 126), (8, 4, 9, 128)):
         assert isa.Plan(isa.make_desc(1, c, 64, w, k, r, r)).info()["kernel"] != "is_k2_multi_mfma", (c, k, r, w)
     # any K: the last group of 4 filters masks the ones past K (an RGB output
     # layer 32 -> 3 took the one-thread-per-output fallback before); odd
     # channel counts that the vector form does not take (K = 3, 5x5 with 4
     # filters per group) get it over 1-channel slabs
-    for (c, k, r) in ((32, 3, 3), (32, 1, 3), (6, 6, 3), (8, 7, 5), (4, 2, 3), (5, 3, 3), (3, 7, 5)):
+    for (c, k, r) in ((32, 3, 3), (32, 1, 3), (6, 6, 3), (8, 7, 5), (4, 2, 3), (5, 3, 3), (3, 7, 5), (8, 8, 7),
+                      (2, 16, 7), (3, 5, 7), (1, 4, 7)):
         info = isa.Plan(isa.make_desc(2, c, 40, 136, k, r, r)).info()
         assert info["kernel"] == "is_k2_multi_mfma" and info["grid"][0] == 2 * 3 * 3 * ((k + 3) // 4), (c, k, r, info)
     assert names(isa.make_desc(1, 3, 720, 1280, 32, 3, 3, "f32"))[0] == ("is_k2_multi", 32, True)
     assert ("is_k2_multi_mfma", 0, False) in names(isa.make_desc(1, 3, 720, 1280, 32, 3, 3, "f32"))
     assert "is_k2_multi_mfma" not in [n[0] for n in names(isa.make_desc(1, 1, 8192, 8192, 1, 3, 3))]
     assert isa.Plan(isa.make_desc(1, 5, 40, 136, 3, 3, 3)).info()["lds_bytes"] == 4 * 576 * 16
+    assert isa.Plan(isa.make_desc(1, 8, 40, 136, 8, 7, 7)).info()["lds_bytes"] == 4 * 576 * 16   # 1-channel slabs
+    # a plan that only the last resort takes is variant 0 and re-creates as itself
+    assert names(isa.make_desc(1, 1, 64, 128, 4, 7, 7)) == [("is_k2_multi_mfma", 0, True)]
+    assert isa.Plan(isa.make_desc(1, 1, 64, 128, 4, 7, 7), variant=0).info()["kernel"] == "is_k2_multi_mfma"
     assert isa.Plan(isa.make_desc(1, 32, 720, 1280, 4, 3, 3, "f32")).info()["lds_bytes"] == 53248
     assert names(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16")) == [
         ("is_k4_mfma", 128, True), ("is_k4_mfma", 0, False), ("is_k4_mfma", 256, False)]
