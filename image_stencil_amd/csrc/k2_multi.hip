@@ -603,13 +603,17 @@ bool configure_multi(Plan &p, int param) {
   if (d.layout != IS_NCHW || d.in_dtype != IS_F32 || d.r != d.s) return false;
   if (d.w % 4 != 0) return false;
   const int cs = (d.c % 4 == 0) ? 4 : 1;
-  // Output channels per workgroup: as many as divide K, up to 32. With one
-  // input channel there is a single slab, so a workgroup loads, computes and
-  // stores in sequence; 16 channels give twice the workgroups to overlap those
-  // phases (the 1 -> 32 5x5 layer of a 1280x720 frame: 35.5 against 38.5 us).
+  // Output channels per workgroup: as many as divide K, up to 16 (up to 32 for
+  // one channel with K not a multiple of 16). With one input channel there is a
+  // single slab, so a workgroup loads, computes and stores in sequence; 16
+  // channels give twice the workgroups to overlap those phases (the 1 -> 32 5x5
+  // layer of a 1280x720 frame: 35.5 against 38.5 us). With more channels 32 per
+  // workgroup was the slowest choice but one at every shape the tuner timed
+  // (3 -> 32 3x3: 40.2 us against 36.4 with 16; 3 -> 64: 72.5 against 64.0-65.2
+  // with 8 or 16; 2 -> 32: 32.8 against 27.8-28.1).
   int ft = 0;
   for (int f : {32, 16, 8, 4, 2})
-    if (d.k % f == 0 && !(d.c == 1 && f == 32 && d.k % 16 == 0 && pick<false>(d.r, 16, cs))) {
+    if (d.k % f == 0 && !(f == 32 && d.k % 16 == 0 && pick<false>(d.r, 16, cs))) {
       ft = f;
       break;
     }
@@ -656,7 +660,10 @@ bool configure_multi_mf(Plan &p, int use) {
   // input once for all its filters), with this form among the variants from 2
   // channels on; the plan falls back to it for the shapes that no other kernel
   // but the one-thread-per-output fallback takes.
-  if (use == kMfPlan && (d.c < 4 || d.c % kMfCS != 0) && !(d.r == 7 && d.c >= 2)) return false;
+  // 5x5 and 7x7 layers take it from 2 channels on whatever their parity (3 -> 32
+  // 5x5: 59.6 against 74-87 us; 7 -> 16: 64 against 88-94; 2 -> 16: 28.2
+  // against 30-35; the vector form has no 7x7).
+  if (use == kMfPlan && (d.c < 4 || d.c % kMfCS != 0) && !(d.r >= 5 && d.c >= 2)) return false;
   if (use == kMfVariant && d.c < 2) return false;
   if (pick_mf<false, false>(d.r, d.c) == nullptr) return false;
   // 32-bit buffer offsets: one image's input and output planes, and the weights.

@@ -51,6 +51,9 @@ CASES = [
     (1, 32, 4, 45, 140, 3, False, "is_k2_multi_mfma"),
     (3, 3, 8, 9, 20, 3, True, "is_k2_multi"),
     (2, 2, 8, 21, 72, 3, False, "is_k2_multi"),
+    (1, 3, 32, 21, 72, 3, False, "is_k2_multi"),      # 16 filters per workgroup
+    (1, 3, 32, 37, 132, 5, True, "is_k2_multi_mfma"),
+    (2, 2, 16, 19, 68, 5, False, "is_k2_multi_mfma"),
     (1, 12, 8, 19, 68, 5, False, "is_k2_multi_mfma"),
     # K not a multiple of 4: the last group's missing filters are masked
     (1, 32, 3, 37, 132, 3, True, "is_k2_multi_mfma"),

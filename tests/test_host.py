@@ -311,8 +311,13 @@ def test_tile_variants():
                       (2, 16, 7), (3, 5, 7), (1, 4, 7)):
         info = isa.Plan(isa.make_desc(2, c, 40, 136, k, r, r)).info()
         assert info["kernel"] == "is_k2_multi_mfma" and info["grid"][0] == 2 * 3 * 3 * ((k + 3) // 4), (c, k, r, info)
-    assert names(isa.make_desc(1, 3, 720, 1280, 32, 3, 3, "f32"))[0] == ("is_k2_multi", 32, True)
+    # odd channel counts, 3x3: the vector form with at most 16 filters per workgroup
+    assert names(isa.make_desc(1, 3, 720, 1280, 32, 3, 3, "f32"))[0] == ("is_k2_multi", 16, True)
     assert ("is_k2_multi_mfma", 0, False) in names(isa.make_desc(1, 3, 720, 1280, 32, 3, 3, "f32"))
+    assert names(isa.make_desc(1, 2, 720, 1280, 32, 3, 3, "f32"))[0] == ("is_k2_multi", 16, True)
+    # 5x5 from 2 channels whatever the parity: the matrix-core form
+    for c in (2, 3, 7):
+        assert names(isa.make_desc(1, c, 720, 1280, 16, 5, 5, "f32"))[0] == ("is_k2_multi_mfma", 0, True), c
     assert "is_k2_multi_mfma" not in [n[0] for n in names(isa.make_desc(1, 1, 8192, 8192, 1, 3, 3))]
     assert isa.Plan(isa.make_desc(1, 5, 40, 136, 3, 3, 3)).info()["lds_bytes"] == 4 * 576 * 16
     assert isa.Plan(isa.make_desc(1, 8, 40, 136, 8, 7, 7)).info()["lds_bytes"] == 4 * 576 * 16   # 1-channel slabs
