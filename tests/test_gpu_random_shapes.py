@@ -56,7 +56,23 @@ def _draw_cases(n=80, seed=1234):
     return cases
 
 
-CASES = _draw_cases()
+def _draw_multi_cases(n=24, seed=4321):
+    """Multi-channel fp32 layers of any channel and filter count with 3x3, 5x5
+    or 7x7 filters (the register-blocked kernel in either form, its masked last
+    filter group, 1-channel slabs, the fallback for widths that are not whole
+    16-byte vectors)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        N = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 60))
+        W = int(rng.integers(1, 40)) * 4 if rng.random() < 0.85 else int(rng.integers(1, 120))
+        C, K, R = int(rng.integers(1, 40)), int(rng.integers(1, 13)), int(rng.choice([3, 5, 7]))
+        cases.append((100 + i, "multi_any", N, C, K, H, W, R, R, bool(rng.random() < 0.5), bool(rng.random() < 0.7)))
+    return cases
+
+
+CASES = _draw_cases() + _draw_multi_cases()
 
 
 @pytest.mark.parametrize("i,kind,N,C,K,H,W,R,S,relu,bias", CASES, ids=[str(c[0]) for c in CASES])
