@@ -69,7 +69,7 @@ bool configure_multi(Plan &p, int param = 0);
 hipError_t launch_multi(const Plan &p, const float *x, const float *w, const float *b, float *y,
                         hipStream_t s);
 // The multi-channel layer's products on the matrix cores, 4 filters per
-// workgroup (any C and K, 3x3, 5x5 or 7x7, W a multiple of 4). use: kMfPlan
+// workgroup (any C, K and W; 3x3, 5x5 or 7x7). use: kMfPlan
 // where it is the plan's first choice (an even channel count from 4 on, or 7x7
 // from 2 channels: the vector form has no 7x7), kMfVariant for
 // the tuning variants (2 channels or more), kMfLastResort for the plan of

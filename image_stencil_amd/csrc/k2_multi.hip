@@ -123,7 +123,7 @@ __device__ __forceinline__ void slab_offsets(unsigned *voff, int wave, int lane,
 // is this lane's sum for filter kg * FT + f at output pixel (oy, ox + p);
 // filters from K on (a last group of the matrix-core form that K does not
 // fill) have no bias and their stores fall outside the output's range.
-template <int FT, bool RELU, bool D2S>
+template <int FT, bool RELU, bool D2S, bool VEC = true>
 __device__ __forceinline__ void store_tile(const float (&acc)[FT][4], const float *bias, float *y, int n,
                                            int kg, int K, int H, int W, int oy, int ox) {
   const size_t HW = (size_t)H * W;
@@ -174,10 +174,21 @@ __device__ __forceinline__ void store_tile(const float (&acc)[FT][4], const floa
       o[p] = acc[f][p] + b;
       if constexpr (RELU) o[p] = fmaxf(o[p], 0.f);
     }
-    const unsigned off = in ? (unsigned)(((size_t)f * HW + (size_t)oy * W + ox) * 4) : kOob;
-    __builtin_amdgcn_raw_buffer_store_b128(
-        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, make_float4(o[0], o[1], o[2], o[3])),
-        rs_o, off, 0, kNonTemporalStore);
+    if constexpr (VEC) {
+      const unsigned off = in ? (unsigned)(((size_t)f * HW + (size_t)oy * W + ox) * 4) : kOob;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, make_float4(o[0], o[1], o[2], o[3])),
+          rs_o, off, 0, kNonTemporalStore);
+    } else {
+      // Rows that are not whole vectors: one dword per pixel inside the row.
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const unsigned off =
+            (oy < H && ox + p < W) ? (unsigned)(((size_t)f * HW + (size_t)oy * W + ox + p) * 4) : kOob;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, o[p]), rs_o, off, 0,
+                                              kNonTemporalStore);
+      }
+    }
   }
 }
 
@@ -353,6 +364,16 @@ struct MGeo {
   static constexpr int PIXV4 = G::PADV4;                // pixel vectors per buffer
   static constexpr int BUFV4 = PIXV4 + WROUNDS * 64;    // + WROUNDS x 4 x 64 dwords
   static constexpr int IPW = G::ROUNDS + WROUNDS;       // DMA instructions per wave per slab
+  // Rows that are not whole 16-byte vectors (W % 4 != 0): the pixels move one
+  // dword per lane, so that each pixel outside the image reads 0 on its own.
+  // Instruction i writes LDS floats 64 i .. 64 i + 63: first one per staged
+  // row (its 64 own columns), then the halo area (8 floats per row) in pieces
+  // of 64; every wave issues DROUNDS of them (the last ones into padding).
+  static constexpr int DMAIN = CS * G::LH;                       // one per staged row
+  static constexpr int DHALO = (CS * G::LH * 8 + 63) / 64;
+  static constexpr int DROUNDS = (DMAIN + DHALO + 3) / 4;
+  static constexpr int IPW_D = DROUNDS + WROUNDS;
+  static_assert(DROUNDS * 4 * 16 <= PIXV4, "the dword DMA stays in the pixel area");
 };
 
 // One slab into one ring buffer: every wave issues G::ROUNDS pixel chunks and
@@ -374,7 +395,25 @@ __device__ __forceinline__ void issue_ring_slab(__amdgpu_buffer_rsrc_t rs, __amd
 }
 
 // NSL: the slab count C / CS when known at compile time (0: any).
-template <int R, int CS, int NB, int NSL, bool RELU, bool D2S>
+// The same with the pixels as dwords (rows that are not whole vectors).
+template <int R, int CS>
+__device__ __forceinline__ void issue_ring_slab_d(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rw,
+                                                  float4 *buf, int wave, const unsigned *doff,
+                                                  const unsigned *wvoff) {
+  using M = MGeo<R, CS>;
+#pragma unroll
+  for (int j = 0; j < M::DROUNDS; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void *)((float *)buf + (j * 4 + wave) * 64), 4, doff[j], 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < M::WROUNDS; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rw, (__attribute__((address_space(3))) void *)((float *)(buf + M::PIXV4) + (j * 4 + wave) * 64), 4,
+        wvoff[j], 0, 0, 0);
+}
+
+// VEC: W % 4 == 0 (16-byte pixel groups and stores); else dwords.
+template <int R, int CS, int NB, int NSL, bool RELU, bool D2S, bool VEC = true>
 __global__ __launch_bounds__(kThreads) void is_k2_multi_mfma(const float *__restrict__ x,
                                                              const float *__restrict__ w,
                                                              const float *__restrict__ bias,
@@ -385,7 +424,6 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi_mfma(const float *__rest
   constexpr int P = G::P;
   constexpr int TQ = M::TP / 4;
   constexpr int PD = NB - 1;   // slabs in flight ahead of the one computed
-  static_assert((PD - 1) * M::IPW < 64, "vmcnt field");
   // The ring's buffers are separate arrays so that the compiler can tell a
   // slab's LDS reads from the DMA still writing the other buffers (one array
   // indexed by slab would make every LDS read wait for all DMA in flight).
@@ -410,8 +448,35 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi_mfma(const float *__rest
   const int x0 = tx * kTW, y0 = ty * kTH;
   const size_t HW = (size_t)H * W;
 
-  unsigned voff[G::ROUNDS];
-  slab_offsets<R, CS>(voff, wave, lane, x0, y0, H, W, HW);
+  static_assert(VEC || !D2S, "the depth-to-space stores are 16-byte vectors");
+  constexpr int IPW = VEC ? M::IPW : M::IPW_D;   // DMA operations per wave and slab
+  static_assert((PD - 1) * IPW < 64, "vmcnt field");
+  unsigned voff[VEC ? G::ROUNDS : M::DROUNDS];
+  if constexpr (VEC) {
+    slab_offsets<R, CS>(voff, wave, lane, x0, y0, H, W, HW);
+  } else {
+#pragma unroll
+    for (int j = 0; j < M::DROUNDS; ++j) {
+      const int ins = j * 4 + wave;
+      int c = 0, lrow = 0, gx = -1;
+      if (ins < M::DMAIN) {
+        c = ins / G::LH;
+        lrow = ins - c * G::LH;
+        gx = x0 + lane;
+      } else {
+        const int h = (ins - M::DMAIN) * 64 + lane;   // float of the halo area
+        if (h < CS * G::LH * 8) {
+          const int crow = h >> 3, j8 = h & 7;
+          c = crow / G::LH;
+          lrow = crow - c * G::LH;
+          gx = j8 < 4 ? x0 - 4 + j8 : x0 + kTW + j8 - 4;
+        }
+      }
+      const int gy = y0 - P + lrow;
+      const bool in = gx >= 0 && gx < W && gy >= 0 && gy < H;
+      voff[j] = in ? (unsigned)(((size_t)c * HW + (size_t)gy * W + gx) * 4) : kOob;
+    }
+  }
   // This lane's tap dwords in a slab: filter f of the group, channel c of the
   // slab, tap t; relative to the slab's first channel of the group's first
   // filter. Padding taps and chunks read 0.
@@ -432,7 +497,10 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi_mfma(const float *__rest
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(wg + (size_t)s * CS * R * R), (short)0,
         (int)((w_left - (size_t)s * CS * R * R) * 4), kBufferFlags);
-    issue_ring_slab<R, CS>(rs, rw, buf, wave, voff, wvoff);
+    if constexpr (VEC)
+      issue_ring_slab<R, CS>(rs, rw, buf, wave, voff, wvoff);
+    else
+      issue_ring_slab_d<R, CS>(rs, rw, buf, wave, voff, wvoff);
   };
 
   const int row0 = wave * 4 + lr;
@@ -498,9 +566,9 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi_mfma(const float *__rest
   static_assert(PD <= 4, "wait_slab's cases");
   auto wait_slab = [&](int ahead) __attribute__((always_inline)) {
     if (ahead == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    if constexpr (PD > 1) if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(1 * M::IPW));
-    if constexpr (PD > 2) if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * M::IPW));
-    if constexpr (PD > 3) if (ahead == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * M::IPW));
+    if constexpr (PD > 1) if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(1 * IPW));
+    if constexpr (PD > 2) if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * IPW));
+    if constexpr (PD > 3) if (ahead == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * IPW));
   };
 
   const int nslab = NSL > 0 ? NSL : C / CS;
@@ -538,7 +606,7 @@ __global__ __launch_bounds__(kThreads) void is_k2_multi_mfma(const float *__rest
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc[f][p] = macc[p][f];
-  store_tile<4, RELU, D2S>(acc, bias, y, n, kg, K, H, W, y0 + row0, x0 + 4 * lc);
+  store_tile<4, RELU, D2S, VEC>(acc, bias, y, n, kg, K, H, W, y0 + row0, x0 + 4 * lc);
 }
 
 using K2Fn = void (*)(const float *, const float *, const float *, float *, int, int, int, int, int, int, int,
@@ -577,23 +645,31 @@ constexpr int kMfNB = 4;
 // Channels per slab: 2, or 1 for odd channel counts and for 7x7 filters (whose
 // 2-channel slabs need 181 VGPRs and 72 KB of LDS: 2 workgroups per CU against 4).
 int mf_slab_channels(int r, int c) { return (c % kMfCS == 0 && r != 7) ? kMfCS : 1; }
-template <bool RELU, bool D2S>
-K2Fn pick_mf(int r, int c) {
+template <bool RELU, bool D2S, bool VEC>
+K2Fn pick_mf_v(int r, int c) {
   if (mf_slab_channels(r, c) == kMfCS) {
     if (r == 3) {
-      if (c == 32) return is_k2_multi_mfma<3, kMfCS, kMfNB, 32 / kMfCS, RELU, D2S>;
-      return is_k2_multi_mfma<3, kMfCS, kMfNB, 0, RELU, D2S>;
+      if constexpr (VEC)
+        if (c == 32) return is_k2_multi_mfma<3, kMfCS, kMfNB, 32 / kMfCS, RELU, D2S, VEC>;
+      return is_k2_multi_mfma<3, kMfCS, kMfNB, 0, RELU, D2S, VEC>;
     }
     if constexpr (!D2S)
-      if (r == 5) return is_k2_multi_mfma<5, kMfCS, kMfNB, 0, RELU, D2S>;
+      if (r == 5) return is_k2_multi_mfma<5, kMfCS, kMfNB, 0, RELU, D2S, VEC>;
     return nullptr;
   }
-  if (r == 3) return is_k2_multi_mfma<3, 1, kMfNB, 0, RELU, D2S>;
+  if (r == 3) return is_k2_multi_mfma<3, 1, kMfNB, 0, RELU, D2S, VEC>;
   if constexpr (!D2S) {
-    if (r == 5) return is_k2_multi_mfma<5, 1, kMfNB, 0, RELU, D2S>;
-    if (r == 7) return is_k2_multi_mfma<7, 1, kMfNB, 0, RELU, D2S>;
+    if (r == 5) return is_k2_multi_mfma<5, 1, kMfNB, 0, RELU, D2S, VEC>;
+    if (r == 7) return is_k2_multi_mfma<7, 1, kMfNB, 0, RELU, D2S, VEC>;
   }
   return nullptr;
+}
+// w % 4 == 0: 16-byte pixel groups and stores; else dwords (no depth-to-space).
+template <bool RELU, bool D2S>
+K2Fn pick_mf(int r, int c, int w) {
+  if (w % 4 == 0) return pick_mf_v<RELU, D2S, true>(r, c);
+  if constexpr (D2S) return nullptr;
+  return pick_mf_v<RELU, false, false>(r, c);
 }
 
 }  // namespace
@@ -650,7 +726,6 @@ bool configure_multi(Plan &p, int param) {
 bool configure_multi_mf(Plan &p, int use) {
   const conv2d_desc &d = p.d;
   if (d.layout != IS_NCHW || d.in_dtype != IS_F32 || d.r != d.s || d.separable) return false;
-  if (d.w % 4 != 0) return false;
   // The default plan for an even channel count from 4 on: measured on 1280x720
   // it beats the vector form at every such shape tried (32 -> 8 3x3: 61 against
   // 84 us; 64 -> 16: 228 against 284-344; 32 -> 64: 432 against 505-635; 5x5
@@ -665,7 +740,7 @@ bool configure_multi_mf(Plan &p, int use) {
   // against 30-35; the vector form has no 7x7).
   if (use == kMfPlan && (d.c < 4 || d.c % kMfCS != 0) && !(d.r >= 5 && d.c >= 2)) return false;
   if (use == kMfVariant && d.c < 2) return false;
-  if (pick_mf<false, false>(d.r, d.c) == nullptr) return false;
+  if (pick_mf<false, false>(d.r, d.c, d.w) == nullptr) return false;
   // 32-bit buffer offsets: one image's input and output planes, and the weights.
   const double img_bytes = 4.0 * d.c * (double)d.h * d.w;
   const double out_bytes = 4.0 * d.k * (double)d.h * d.w;
@@ -695,7 +770,7 @@ bool configure_multi_mf(Plan &p, int use) {
 hipError_t launch_multi_mf(const Plan &p, const float *x, const float *w, const float *b, float *y,
                            hipStream_t s) {
   const conv2d_desc &d = p.d;
-  const K2Fn fn = d.relu ? pick_mf<true, false>(d.r, d.c) : pick_mf<false, false>(d.r, d.c);
+  const K2Fn fn = d.relu ? pick_mf<true, false>(d.r, d.c, d.w) : pick_mf<false, false>(d.r, d.c, d.w);
   if (p.kid != kMultiMfmaF32 || !fn) return hipErrorInvalidValue;
   return launch_kernel(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, d.c, d.h, d.w, d.k, p.nseg,
                        p.nstrip, (d.k + 3) / 4, p.ntiles);
@@ -703,7 +778,7 @@ hipError_t launch_multi_mf(const Plan &p, const float *x, const float *w, const 
 
 bool multi_d2s_supported(const Plan &p) {
   if (p.d.k != 4) return false;
-  if (p.kid == kMultiMfmaF32) return pick_mf<false, true>(p.d.r, p.d.c) != nullptr;
+  if (p.kid == kMultiMfmaF32) return pick_mf<false, true>(p.d.r, p.d.c, p.d.w) != nullptr;
   return p.kid == kMultiChannel && pick_d2s<false>(p.d.r, p.strip_rows, p.vec) != nullptr;
 }
 
@@ -714,7 +789,7 @@ hipError_t launch_multi_d2s(const Plan &p, const float *x, const float *w, const
   const int ft = p.strip_rows, cs = p.vec;
   K2Fn fn;
   if (p.kid == kMultiMfmaF32)
-    fn = d.relu ? pick_mf<true, true>(d.r, d.c) : pick_mf<false, true>(d.r, d.c);
+    fn = d.relu ? pick_mf<true, true>(d.r, d.c, d.w) : pick_mf<false, true>(d.r, d.c, d.w);
   else
     fn = d.relu ? pick_d2s<true>(d.r, ft, cs) : pick_d2s<false>(d.r, ft, cs);
   return launch_kernel(fn, dim3(p.grid_x), dim3(p.block), 0, s, x, w, b, y, d.c, d.h, d.w, d.k, p.nseg,

@@ -77,6 +77,8 @@ LAYERS = [
     (1, 32, 3, 37, 132, 3, "f32", True, "is_k2_multi_mfma"),
     (2, 5, 3, 21, 72, 5, "f32", False, "is_k2_multi_mfma"),
     (1, 6, 5, 21, 72, 7, "f32", True, "is_k2_multi_mfma"),
+    (2, 8, 6, 19, 70, 3, "f32", False, "is_k2_multi_mfma"),   # dword pixels (rows of 70)
+    (1, 3, 4, 17, 133, 5, "f32", True, "is_k2_multi_mfma"),
 ]
 
 

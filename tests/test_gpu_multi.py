@@ -40,7 +40,7 @@ CASES = [
     (1, 32, 32, 16, 32, 3, False, "is_k5_mfma_f32"),
     (1, 32, 32, 1, 4, 3, True, "is_k5_mfma_f32"),
     (1, 32, 32, 33, 260, 3, False, "is_k5_mfma_f32"),
-    (1, 32, 32, 9, 30, 3, False, "is_k0_generic_nchw_f32"),
+    (1, 32, 32, 9, 30, 3, False, "is_k2_multi_mfma"),   # rows of 30: dword pixels
     (2, 8, 16, 37, 132, 3, False, "is_k2_multi_mfma"),
     (1, 4, 8, 17, 68, 3, True, "is_k2_multi_mfma"),
     (1, 4, 4, 33, 64, 3, False, "is_k2_multi_mfma"),
@@ -91,7 +91,7 @@ CASES = [
     (1, 1, 6, 16, 64, 5, False, "is_k2_multi"),
     (1, 1, 16, 21, 72, 1, True, "is_k2_multi"),
     (1, 1, 3, 21, 72, 3, False, "is_k2_multi_mfma"),
-    (1, 1, 3, 21, 70, 3, False, "is_k0_generic_nchw_f32"),
+    (1, 1, 3, 21, 70, 3, False, "is_k2_multi_mfma"),
     # one input channel to 16, 32 or 64 outputs, 3x3 or 5x5: the fp32 MFMA first
     # layer (16 x 64 tiles: ragged rows and columns, several tiles, images)
     (2, 1, 16, 37, 132, 3, False, "is_k9_head_f32"),
@@ -100,7 +100,7 @@ CASES = [
     (1, 1, 64, 33, 260, 5, True, "is_k9_head_f32"),
     (2, 1, 64, 16, 64, 3, False, "is_k9_head_f32"),
     (1, 1, 32, 45, 196, 5, True, "is_k9_head_f32"),
-    (1, 1, 32, 21, 70, 5, True, "is_k0_generic_nchw_f32"),
+    (1, 1, 32, 21, 70, 5, True, "is_k2_multi_mfma"),
     # 1x1 filters over several channels: the pointwise kernel (planes of whole
     # 16-byte vectors, ragged last workgroup), else the fallback
     (1, 8, 16, 21, 72, 1, False, "is_k8_pointwise"),
@@ -113,8 +113,14 @@ CASES = [
     (1, 384, 32, 9, 64, 1, False, "is_k8_pointwise"),   # staged weights exactly 48 KB
     (1, 385, 32, 5, 64, 1, False, "is_k8_pointwise"),   # 16 channels per workgroup instead
     (1, 8, 16, 9, 30, 1, False, "is_k0_generic_nchw_f32"),
-    (1, 5, 6, 11, 30, 5, False, "is_k0_generic_nchw_f32"),
-    (1, 8, 8, 10, 13, 3, True, "is_k0_generic_nchw_f32"),
+    (1, 5, 6, 11, 30, 5, False, "is_k2_multi_mfma"),
+    (1, 8, 8, 10, 13, 3, True, "is_k2_multi_mfma"),
+    # widths that are not whole 16-byte vectors, several tiles and images
+    (2, 32, 4, 37, 130, 3, True, "is_k2_multi_mfma"),
+    (1, 6, 9, 19, 197, 7, False, "is_k2_multi_mfma"),
+    (3, 3, 16, 17, 67, 5, True, "is_k2_multi_mfma"),
+    (1, 2, 8, 33, 1, 3, False, "is_k2_multi_mfma"),
+    (1, 4, 4, 9, 30, 1, True, "is_k0_generic_nchw_f32"),
 ]
 
 

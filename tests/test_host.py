@@ -266,9 +266,10 @@ def test_separable_and_special_case_plans():
     assert isa.Plan(isa.make_desc(1, 4000, 64, 128, 8, 1, 1)).info()["kernel"] == "is_k2_multi"
     assert isa.Plan(isa.make_desc(1, 8, 9, 30, 16, 1, 1)).info()["kernel"] == "is_k0_generic_nchw_f32"
     # one channel with 3 filters: no fan-out or register-blocked instance takes
-    # it; the matrix-core form's 1-channel slabs do (W a multiple of 4)
+    # it; the matrix-core form's 1-channel slabs do (16-byte or dword pixels)
     assert isa.Plan(isa.make_desc(1, 1, 64, 128, 3, 3, 3)).info()["kernel"] == "is_k2_multi_mfma"
-    assert isa.Plan(isa.make_desc(1, 1, 64, 126, 3, 3, 3)).info()["kernel"] == "is_k0_generic_nchw_f32"
+    assert isa.Plan(isa.make_desc(1, 1, 64, 126, 3, 3, 3)).info()["kernel"] == "is_k2_multi_mfma"
+    assert isa.Plan(isa.make_desc(1, 1, 64, 126, 3, 1, 1)).info()["kernel"] == "is_k0_generic_nchw_f32"
 
 
 def test_tile_variants():
@@ -301,8 +302,11 @@ def test_tile_variants():
     assert names(isa.make_desc(1, 32, 64, 128, 8, 5, 5, "f32")) == [("is_k2_multi_mfma", 0, True)]
     assert names(isa.make_desc(1, 2, 64, 128, 8, 3, 3, "f32"))[0] == ("is_k2_multi", 8, True)
     assert ("is_k2_multi_mfma", 0, False) in names(isa.make_desc(1, 2, 64, 128, 8, 3, 3, "f32"))
-    for (c, k, r, w) in ((3, 4, 3, 128), (32, 4, 3, 130), (2, 4, 3, 128), (5, 3, 3, 126), (8, 4, 9, 128)):
+    for (c, k, r, w) in ((3, 4, 3, 128), (2, 4, 3, 128), (8, 4, 9, 128), (8, 4, 1, 130)):
         assert isa.Plan(isa.make_desc(1, c, 64, w, k, r, r)).info()["kernel"] != "is_k2_multi_mfma", (c, k, r, w)
+    # widths that are not whole 16-byte vectors: the matrix-core form's dword path
+    for (c, k, r, w) in ((32, 4, 3, 130), (5, 3, 3, 126), (32, 32, 3, 30), (1, 32, 5, 70), (8, 8, 3, 13)):
+        assert isa.Plan(isa.make_desc(1, c, 64, w, k, r, r)).info()["kernel"] == "is_k2_multi_mfma", (c, k, r, w)
     # any K: the last group of 4 filters masks the ones past K (an RGB output
     # layer 32 -> 3 took the one-thread-per-output fallback before); odd
     # channel counts that the vector form does not take (K = 3, 5x5 with 4
@@ -344,7 +348,8 @@ def test_tile_variants():
     assert isa.Plan(isa.make_desc(1, 1, 720, 1282, 32, 5, 5)).info()["kernel"] != "is_k9_head_f32"
     assert isa.Plan(isa.make_desc(1, 1, 720, 1280, 32, 7, 7)).info()["kernel"] != "is_k9_head_f32"
     assert isa.Plan(isa.make_desc(1, 1, 720, 1280, 8, 5, 5)).info()["kernel"] == "is_k2_multi"
-    assert names(isa.make_desc(1, 3, 16, 30, 5, 3, 3)) == [("is_k0_generic_nchw_f32", 0, True)]
+    assert names(isa.make_desc(1, 3, 16, 30, 5, 3, 3)) == [("is_k2_multi_mfma", 0, True)]
+    assert names(isa.make_desc(1, 3, 16, 30, 5, 1, 1)) == [("is_k0_generic_nchw_f32", 0, True)]
     sep = names(isa.make_desc(1, 1, 512, 512, 1, 7, 7, separable=True))
     assert {k for (k, _, _) in sep} == {"is_k1_single_separable"} and len(sep) == 5
     d = isa.make_desc(1, 1, 4096, 4096, 8, 3, 3)
