@@ -137,7 +137,7 @@ NET_PROFILE_ARGS = "--no-cpu-baseline --no-check --secondary pages_net"
 NET_KERNELS = {
     "is_k4_mfma<128, 64, 64, 0, 60, 5, true>": "layers 1 + 2: the 1 -> 64 5x5 computed inside the 64 -> 64 3x3 (60-row units)",
     "is_k4_mfma<128, 64, 32, 0, 60, 0, true>": "layer 3: 64 -> 32, 3x3 (60-row units)",
-    "is_k4_mfma<128, 32, 16, 3, 0, 0, false>": "layer 4: 32 -> 9 (as 16), 3x3, with the depth-to-space x3 in its stores",
+    "is_k4_mfma<128, 32, 16, 3, 30, 0, false>": "layer 4: 32 -> 9 (as 16), 3x3, with the depth-to-space x3 in its stores (30-row units)",
     "is_k6_head_f16<5, 64>": "layer 1 alone: 1 -> 64, 5x5 (one-launch-per-layer run)",
     "is_k4_mfma<128, 64, 64, 0, 60, 0, true>": "layer 2 alone: 64 -> 64, 3x3 (one-launch-per-layer run)",
 }

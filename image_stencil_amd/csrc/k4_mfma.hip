@@ -799,10 +799,14 @@ bool configure_mfma(Plan &p, int param) {
   if (!shape_supported(d.c, d.k) || d.r != 3 || d.s != 3) return false;
   if (2.0 * d.h * (double)d.w * d.c >= 4.0e9 || 2.0 * d.h * (double)d.w * d.k >= 4.0e9)
     return false;   // 32-bit offsets per image
-  // Unit height: 64 rows, or 60 when that computes fewer rows past the
-  // image's last one (a 720-row frame: 12 units of 60 rows against 12 of 64,
-  // a twelfth of them below the image), for the 64-channel inputs.
+  // Unit height: 64 rows (32 for 16 output channels), or 60 (30) when that
+  // computes fewer rows past the image's last one. A 720-row frame: 12 units
+  // of 60 rows against 12 of 64, a twelfth of them below the image; with 16
+  // output channels 24 units of 30 rows, 32 input rows = 8 whole stages each,
+  // against 23 units of 32 rows, 34 input rows = 9 stages, the last one half
+  // used, and 16 rows below the image.
   const bool ur60 = (d.h + 59) / 60 * 60 < (d.h + 63) / 64 * 64;
+  const bool ur30 = (d.h + 29) / 30 * 30 < (d.h + 31) / 32 * 32;
   if (d.c == 64 && d.k == 64) {
     if (ur60) fill_geometry<64, 64, 60>(p);
     else fill_geometry<64, 64>(p);
@@ -810,9 +814,11 @@ bool configure_mfma(Plan &p, int param) {
     if (ur60) fill_geometry<64, 32, 60>(p);
     else fill_geometry<64, 32>(p);
   } else if (d.k == 32) {
-    fill_geometry<32, 32>(p);
+    if (ur60) fill_geometry<32, 32, 60>(p);
+    else fill_geometry<32, 32>(p);
   } else {
-    fill_geometry<32, 16>(p);
+    if (ur30) fill_geometry<32, 16, 30>(p);
+    else fill_geometry<32, 16>(p);
   }
   const long long units = (long long)p.nseg * p.nstrip * d.n;
   if (units > (1LL << 31) - 1) return false;
@@ -869,7 +875,9 @@ hipError_t launch_mfma_d2s3(const Plan &p, const _Float16 *x, const _Float16 *w,
   a.wh = nullptr;
   a.bh = nullptr;
   a.relu_h = 0;
-  return launch_k4<128, 32, 16, 3>(a, dim3(persistent_grid(p.ntiles, device_cu_count())), dim3(p.block), s);
+  const dim3 grid(persistent_grid(p.ntiles, device_cu_count())), block(p.block);
+  return p.tile_h == 30 ? launch_k4<128, 32, 16, 3, 30>(a, grid, block, s)
+                        : launch_k4<128, 32, 16, 3>(a, grid, block, s);
 }
 
 bool mfma_head_supported(const Plan &p, int head_r) {
@@ -937,8 +945,14 @@ hipError_t launch_mfma(const Plan &p, const _Float16 *x, const _Float16 *w, cons
     if (p.tile_h == 60) return launch_k4<128, 64, 32, 0, 60>(a, grid, block, s);
     return launch_k4<128, 64, 32>(a, grid, block, s);
   }
-  if (p.d.c == 32 && p.d.k == 32) return launch_k4<128, 32, 32>(a, grid, block, s);
-  if (p.d.c == 32 && p.d.k == 16) return launch_k4<128, 32, 16>(a, grid, block, s);
+  if (p.d.c == 32 && p.d.k == 32) {
+    if (p.tile_h == 60) return launch_k4<128, 32, 32, 0, 60>(a, grid, block, s);
+    return launch_k4<128, 32, 32>(a, grid, block, s);
+  }
+  if (p.d.c == 32 && p.d.k == 16) {
+    if (p.tile_h == 30) return launch_k4<128, 32, 16, 0, 30>(a, grid, block, s);
+    return launch_k4<128, 32, 16>(a, grid, block, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -51,7 +51,7 @@ def _chain(x, layers, d2s, mode=isa.IS_CHAIN_AUTO):
 
 
 @pytest.mark.parametrize("N,H,W", [(1, 37, 70), (2, 20, 130), (1, 1, 1), (1, 66, 200), (1, 19, 77), (2, 35, 258),
-                                   (1, 70, 2), (1, 120, 64)])
+                                   (1, 70, 2), (1, 120, 64), (1, 64, 100)])
 def test_pages_net_small_frames(N, H, W):
     """AUTO (the first two layers in one launch) and UNFUSED (one launch per
     layer) against the oracle, and against each other bit for bit: both compute

@@ -98,10 +98,11 @@ def test_mfma_layer_more_units_than_workgroups():
 
 
 @pytest.mark.parametrize("C,K", [(64, 32), (32, 32), (32, 16)])
-@pytest.mark.parametrize("N,H,W", [(1, 8, 32), (2, 37, 70), (1, 66, 130), (1, 1, 1), (1, 40, 257)])
+@pytest.mark.parametrize("N,H,W", [(1, 8, 32), (2, 37, 70), (1, 66, 130), (1, 1, 1), (1, 40, 257), (1, 64, 96)])
 def test_mfma_other_channel_counts(C, K, N, H, W):
     """The upscaling network's other fp16 layers (64 -> 32, 32 -> 32, 32 -> 16):
-    wider units (64 and 128 pixels), shorter ones for 16 outputs, ragged edges."""
+    wider units (64 and 128 pixels), shorter ones for 16 outputs, ragged edges;
+    60- and 30-row units where they compute fewer rows, 64 and 32 rows at H = 64."""
     x, w, b = synth.cnn_layer_f16_nhwc(N=N, C=C, K=K, H=H, W=W, seed=C + K + H + W)
     say("mfma", C, K, N, H, W)
     y = _run(x, w, b, True, "is_k4_mfma")

@@ -332,8 +332,9 @@ def test_tile_variants():
     assert names(isa.make_desc(8, 64, 256, 256, 64, 3, 3, "f16")) == [
         ("is_k4_mfma", 128, True), ("is_k4_mfma", 0, False), ("is_k4_mfma", 256, False)]
     assert names(isa.make_desc(1, 64, 72, 128, 32, 3, 3, "f16")) == [("is_k4_mfma", 128, True)]
-    # fp16 MFMA units are 64 rows, or 60 where that computes fewer rows (720)
-    for (h, c, k, th) in ((256, 64, 64, 64), (720, 64, 64, 60), (720, 64, 32, 60), (720, 32, 16, 32),
+    # fp16 MFMA units are 64 rows (32 for 16 outputs), or 60 (30) where that computes fewer rows (720)
+    for (h, c, k, th) in ((256, 64, 64, 64), (720, 64, 64, 60), (720, 64, 32, 60), (720, 32, 16, 30),
+                          (720, 32, 32, 60), (256, 32, 16, 32), (256, 32, 32, 64), (90, 32, 16, 30),
                           (1080, 64, 64, 60), (64, 64, 64, 64)):
         assert isa.Plan(isa.make_desc(1, c, h, 1280, k, 3, 3, "f16")).info()["tile"][1] == th, (h, c, k)
     # other swizzles keep 64-row units
