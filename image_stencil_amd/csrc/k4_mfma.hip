@@ -89,7 +89,14 @@ struct K4Cfg {
   static constexpr int ROW_BYTES = ROW_SLOTS * 16;
   static constexpr int STAGE_BYTES = S * ROW_BYTES;
   static constexpr int OUT_ROW_BYTES = TC * K * 2;       // one output row of the unit, fp16
-  static constexpr int STAGING_BYTES = 2 * S * OUT_ROW_BYTES;
+  // Output staging: two stage buffers (a stage's rows are copied out while the
+  // next stage's are written), or one where two would leave fewer than 4 ring
+  // slots, i.e. fewer than 3 stages of DMA in flight (the 64- and 128-pixel
+  // units of 64 -> 32 and 32 -> 16); one buffer costs a second barrier per
+  // stage, between the copy-out reads and the stage's first row write.
+  static constexpr int FIT2 = (kLdsMax - 2 * S * OUT_ROW_BYTES) / STAGE_BYTES;
+  static constexpr int SBUF = (HEAD == 0 && FIT2 < 4) ? 1 : 2;
+  static constexpr int STAGING_BYTES = SBUF * S * OUT_ROW_BYTES;
   static constexpr int FIT = (kLdsMax - STAGING_BYTES) / STAGE_BYTES;   // ring slots that fit
   // Stages in flight ahead of the one read: D DMA stages, or (HEAD) 2 stages
   // of head rows computed ahead.
@@ -137,6 +144,8 @@ struct K4Cfg {
   static_assert(LDS_BYTES <= kLdsMax, "LDS");
   static_assert(WSTAGE + K * WROW <= LDS_BYTES, "weights fit beside the first stages");
   static_assert(READS_PER_STAGE > 3, "stores and DMA sit at read steps 0, 2 and 3 of a stage");
+  static_assert(SBUF == 2 || READS_PER_ROW - 1 >= 2, "one staging buffer: no row write before read step 2");
+  static_assert(SBUF == 2 || FIT - 1 >= 3, "one staging buffer buys a third stage of DMA in flight");
   static_assert(HEAD == 0 || (C == 64 && (HEAD == 3 || HEAD == 5) && TC == 32),
                 "the head feeds a 64-channel layer of 32-pixel units");
   static_assert(HEAD == 0 || HEAD_STEP + 7 * 2 + 3 < READS_PER_STAGE, "head steps inside a stage");
@@ -655,13 +664,13 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if constexpr (D2S) {
-          const char *base = lds + (t & 1) * G::S * G::OUT_ROW_BYTES;
+          const char *base = lds + (t % G::SBUF) * G::S * G::OUT_ROW_BYTES;
           unsigned hw[6];
 #pragma unroll
           for (int e = 0; e < 6; ++e) hw[e] = *reinterpret_cast<const unsigned short *>(base + doff[j][e]);
           sv[j] = uint4v{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16), 0u};
         } else {
-          const uint4v v = *reinterpret_cast<const uint4v *>(lds + soff_r[j] + (t & 1) * G::S * G::OUT_ROW_BYTES);
+          const uint4v v = *reinterpret_cast<const uint4v *>(lds + soff_r[j] + (t % G::SBUF) * G::S * G::OUT_ROW_BYTES);
           sv[j] = sswap[j] ? uint4v{v.z, v.w, v.x, v.y} : v;
         }
       }
@@ -703,6 +712,9 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
       constexpr int qs = q % G::READS_PER_STAGE;           // read step inside the stage
       // Stage t - 1's rows leave for HBM; stage t + D's rows start their DMA.
       if constexpr (t >= 1 && qs == 0) read_staged(t - 1, sv);
+      // One staging buffer: every wave's copy-out reads are done before any
+      // wave writes this stage's first row (read step 2 or later).
+      if constexpr (G::SBUF == 1 && t >= 1 && qs == 1) lds_barrier();
       if constexpr (t >= 1 && qs == 2) store_stage(t - 1, sv);
       if constexpr (!HEAD && t + G::D < G::STAGES && qs == 3) issue_stage(geo, t + G::D);
       // HEAD: the head rows of stage t + 2, pixel block p gathered at step
@@ -719,7 +731,8 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
           if (li < G::IN_ROWS) head_finish(geo, (t + 2) % G::NST, li, p, hfrag);
         }
       }
-      if constexpr (qs == 0 || qs == 2 || qs == 3 || kHeadStep) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (qs == 0 || (G::SBUF == 1 && qs == 1) || qs == 2 || qs == 3 || kHeadStep)
+        __builtin_amdgcn_sched_barrier(0);
 
       const half8 b = ring[q % kAhead];
       if constexpr (q + kAhead < G::READS) ring[q % kAhead] = read_b(q + kAhead);
@@ -743,7 +756,7 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
           if constexpr (RELU) r = fmaxf(r, 0.f);
           hv[e] = (_Float16)r;
         }
-        *reinterpret_cast<uint2v *>(lds + soff_w + ((t & 1) * G::S + (i % G::S)) * G::OUT_ROW_BYTES) =
+        *reinterpret_cast<uint2v *>(lds + soff_w + ((t % G::SBUF) * G::S + (i % G::S)) * G::OUT_ROW_BYTES) =
             __builtin_bit_cast(uint2v, hv);
       }
       // End of stage t: stage t + 2 (read from the next stage's last steps on,
