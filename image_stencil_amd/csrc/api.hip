@@ -158,7 +158,8 @@ int collect_variants(const conv2d_desc &d, const is::Plan &def, Variant *out, in
   add(def);
   is::Plan p;
   const Variant tries[] = {
-      {is::kSingleChannel, 16}, {is::kSingleChannel, 32}, {is::kSingleChannel, 64}, {is::kSingleChannel, 128},
+      {is::kSingleChannel, 4}, {is::kSingleChannel, 8}, {is::kSingleChannel, 16},
+      {is::kSingleChannel, 32}, {is::kSingleChannel, 64}, {is::kSingleChannel, 128},
       {is::kMfmaNchwF32, 0},
       {is::kPointwise, 32}, {is::kPointwise, 16}, {is::kPointwise, 8}, {is::kPointwise, 4},
       {is::kMultiChannel, 32}, {is::kMultiChannel, 16}, {is::kMultiChannel, 8}, {is::kMultiChannel, 4},

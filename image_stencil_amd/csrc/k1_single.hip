@@ -366,8 +366,8 @@ bool configure_single(Plan &p, int param) {
     if (param == 0 && (d.k != 2 || d.r != 5 || (long long)nseg * ((d.h + rows - 1) / rows) * d.n < 1024))
       return false;
   }
-  if (param != 0) {   // a tuning variant: 8 to 256 rows
-    if (param < 8 || param > 256) return false;
+  if (param != 0) {   // a tuning variant: 4 to 256 rows
+    if (param < 4 || param > 256) return false;
     rows = param;
   }
   const int nstrip = (d.h + rows - 1) / rows;

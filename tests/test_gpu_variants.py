@@ -84,7 +84,7 @@ def test_every_variant_matches_oracle(name):
     variants = isa.conv2d_list_variants(d)
     assert len(variants) >= 2, variants
     if name.startswith("fanout_"):
-        assert sum(v["kernel"] == "is_k1_single_fanout" for v in variants) == 4, variants
+        assert sum(v["kernel"] == "is_k1_single_fanout" for v in variants) == 6, variants
     for i, v in enumerate(variants):
         say("variant", name, i, v["kernel"], v["param"])
         plan = isa.Plan(d, variant=i)

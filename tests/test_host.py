@@ -279,8 +279,8 @@ def test_tile_variants():
     def names(d):
         return [(v["kernel"], v["param"], v["is_default"]) for v in isa.conv2d_list_variants(d)]
     assert names(isa.make_desc(1, 1, 8192, 8192, 1, 3, 3)) == [
-        ("is_k1_single", 64, True), ("is_k1_single", 16, False), ("is_k1_single", 32, False),
-        ("is_k1_single", 128, False)]
+        ("is_k1_single", 64, True), ("is_k1_single", 4, False), ("is_k1_single", 8, False),
+        ("is_k1_single", 16, False), ("is_k1_single", 32, False), ("is_k1_single", 128, False)]
     assert names(isa.make_desc(1, 32, 720, 1280, 32, 3, 3, "f32", True)) == [
         ("is_k5_mfma_f32", 0, True), ("is_k2_multi", 32, False), ("is_k2_multi", 16, False),
         ("is_k2_multi", 8, False), ("is_k2_multi", 4, False), ("is_k2_multi_mfma", 0, False)]
@@ -352,10 +352,11 @@ def test_tile_variants():
     assert names(isa.make_desc(1, 3, 16, 30, 5, 3, 3)) == [("is_k2_multi_mfma", 0, True)]
     assert names(isa.make_desc(1, 3, 16, 30, 5, 1, 1)) == [("is_k0_generic_nchw_f32", 0, True)]
     sep = names(isa.make_desc(1, 1, 512, 512, 1, 7, 7, separable=True))
-    assert {k for (k, _, _) in sep} == {"is_k1_single_separable"} and len(sep) == 5
+    assert {k for (k, _, _) in sep} == {"is_k1_single_separable"} and len(sep) == 6
     d = isa.make_desc(1, 1, 4096, 4096, 8, 3, 3)
     vs = isa.conv2d_list_variants(d)
-    assert [(v["kernel"], v["param"]) for v in vs] == [("is_k2_multi", 8), ("is_k1_single_fanout", 16),
+    assert [(v["kernel"], v["param"]) for v in vs] == [("is_k2_multi", 8), ("is_k1_single_fanout", 4),
+                                                       ("is_k1_single_fanout", 8), ("is_k1_single_fanout", 16),
                                                        ("is_k1_single_fanout", 32), ("is_k1_single_fanout", 64),
                                                        ("is_k1_single_fanout", 128), ("is_k2_multi", 4),
                                                        ("is_k2_multi", 2)]
