@@ -298,9 +298,13 @@ __global__ __launch_bounds__(1024) void isp_lds_rate(int iters, unsigned long lo
 // reads (else the ring keeps its first values), 2 the MFMAs (else one VALU add
 // per product), 4 the finished rows' LDS writes, 8 a workgroup barrier (LDS
 // drained) per round, 16 two 16-byte global stores per wave per round, 32 three
-// 16-byte global-to-LDS loads per wave per round (waited for before the
-// barrier). gbuf holds 64 KB per workgroup; LDS addresses stay below 128 KB.
+// 16-byte global-to-LDS loads per wave per round (each round's waited for at
+// the barrier 3 rounds later, as the layer waits for its row DMA). gbuf holds
+// 64 KB per workgroup; LDS addresses stay below 128 KB.
 constexpr int kMixLdsBytes = 128 * 1024;
+// s_waitcnt immediate: at most n vector memory operations outstanding (expcnt
+// and lgkmcnt not waited for).
+constexpr int mix_vm_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kMixSteps = 24;
 
 template <int MIX>
@@ -365,7 +369,10 @@ __global__ __launch_bounds__(512, 1) void isp_mix_rate(int iters, unsigned long 
     });
     __asm__ volatile("" ::: "memory");
     if constexpr (MIX & 8) {
-      if constexpr (MIX & 32) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: the loads have landed
+      // As in the layer (5 stages of DMA ahead, each waited for 3 stages
+      // after it was issued): the loads of the round 3 rounds back have
+      // landed; this round's and the 2 before it may still be in flight.
+      if constexpr (MIX & 32) __builtin_amdgcn_s_waitcnt(mix_vm_wait(3 * ((MIX & 16 ? 2 : 0) + 3)));
       __builtin_amdgcn_s_waitcnt(0xC07F);                            // lgkmcnt 0
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(256, 1) void isp_mix4_rate(int iters, unsigned long
     }, std::make_integer_sequence<int, kSteps4>{});
     __asm__ volatile("" ::: "memory");
     if constexpr (MIX & 8) {
-      if constexpr (MIX & 32) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: the loads have landed
+      if constexpr (MIX & 32) __builtin_amdgcn_s_waitcnt(mix_vm_wait(3 * ((MIX & 16 ? 4 : 0) + 4)));   // as above
       __builtin_amdgcn_s_waitcnt(0xC07F);                            // lgkmcnt 0
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
