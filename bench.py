@@ -1103,8 +1103,9 @@ def lds_rate_study(torch, stream_obj, iters=4096):
     return out
 
 
-MIX_PARTS = ((1, "lds_reads"), (2, "mfma"), (4, "row_writes"), (8, "barrier"), (16, "stores"), (32, "dma"))
-MIX_CASES = (2, 3, 7, 15, 10, 11, 31, 47, 63, 5, 61)
+MIX_PARTS = ((1, "lds_reads"), (2, "mfma"), (4, "row_writes"), (8, "barrier"), (16, "stores"), (32, "dma"),
+             (64, "split_by_wave"))
+MIX_CASES = (2, 3, 7, 15, 10, 11, 31, 47, 63, 5, 61, 127, 125)   # 64: the 8-wave flow only
 
 
 def mix_study(torch, stream_obj, iters=512):
@@ -1144,6 +1145,9 @@ def mix_study(torch, stream_obj, iters=512):
         # The same stage on the 4-wave data flow (isp_mix4_rate: a wave holds 64
         # output channels x half the k range; 12 products per operand read; the
         # k halves summed through LDS), the same products per CU and round.
+        if mix & 64:
+            out.append(row)
+            continue
         lib.isp_mix4_rate.argtypes = lib.isp_mix_rate.argtypes
         rc = lib.isp_mix4_rate(mix, cus, iters, stamps.data_ptr(), sink.data_ptr(), gbuf.data_ptr(),
                                stream_obj.cuda_stream)

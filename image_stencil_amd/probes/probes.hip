@@ -299,7 +299,8 @@ __global__ __launch_bounds__(1024) void isp_lds_rate(int iters, unsigned long lo
 // per product), 4 the finished rows' LDS writes, 8 a workgroup barrier (LDS
 // drained) per round, 16 two 16-byte global stores per wave per round, 32 three
 // 16-byte global-to-LDS loads per wave per round (each round's waited for at
-// the barrier 3 rounds later, as the layer waits for its row DMA). gbuf holds
+// the barrier 3 rounds later, as the layer waits for its row DMA), 64 the
+// stores and loads split by wave (even waves store, odd waves load). gbuf holds
 // 64 KB per workgroup; LDS addresses stay below 128 KB.
 constexpr int kMixLdsBytes = 128 * 1024;
 // s_waitcnt immediate: at most n vector memory operations outstanding (expcnt
@@ -337,13 +338,24 @@ __global__ __launch_bounds__(512, 1) void isp_mix_rate(int iters, unsigned long 
   for (int it = 0; it < iters; ++it) {
     static_for_steps([&](auto qc) {
       constexpr int q = decltype(qc)::value;
-      if constexpr ((MIX & 16) && (q == 2 || q == 14))
+      if constexpr ((MIX & 16) && !(MIX & 64) && (q == 2 || q == 14))
         __builtin_amdgcn_raw_buffer_store_b128(uint4v{(unsigned)it, (unsigned)lane, (unsigned)q, 1u}, rs,
                                                (wave * 2 + q / 12) * 1024 + lane * 16, 0, 2);
-      if constexpr ((MIX & 32) && (q == 3 || q == 11 || q == 19))
+      if constexpr ((MIX & 32) && !(MIX & 64) && (q == 3 || q == 11 || q == 19))
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (__attribute__((address_space(3))) void *)(lds + 96 * 1024 + (wave * 3 + q / 8) * 1024), 16,
             32768 + (wave * 3 + q / 8) * 1024 + lane * 16, 0, 0, 2);
+      // 64: the same stores and loads per workgroup, split by wave: the even
+      // waves issue all the stores (4 each), the odd ones all the loads (6 each).
+      if constexpr ((MIX & 16) && (MIX & 64) && q % 6 == 2)
+        if ((wave & 1) == 0)
+          __builtin_amdgcn_raw_buffer_store_b128(uint4v{(unsigned)it, (unsigned)lane, (unsigned)q, 1u}, rs,
+                                                 (wave * 4 + q / 6) * 1024 + lane * 16, 0, 2);
+      if constexpr ((MIX & 32) && (MIX & 64) && q % 4 == 3)
+        if (wave & 1)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void *)(lds + 96 * 1024 + ((wave * 6 + q / 4) % 32) * 1024),
+              16, 32768 + ((wave * 6 + q / 4) % 32) * 1024 + lane * 16, 0, 0, 2);
       const half8 b = ring[q % 8];
       if constexpr (MIX & 1)   // moving by 16 bytes a round keeps the reads conflict-free and live
         ring[q % 8] = *reinterpret_cast<const half8 *>(lds + rbase + ((q + 8) % kMixSteps) * 1024 + (it & 7) * 16);
@@ -372,7 +384,11 @@ __global__ __launch_bounds__(512, 1) void isp_mix_rate(int iters, unsigned long 
       // As in the layer (5 stages of DMA ahead, each waited for 3 stages
       // after it was issued): the loads of the round 3 rounds back have
       // landed; this round's and the 2 before it may still be in flight.
-      if constexpr (MIX & 32) __builtin_amdgcn_s_waitcnt(mix_vm_wait(3 * ((MIX & 16 ? 2 : 0) + 3)));
+      if constexpr ((MIX & 32) && !(MIX & 64)) __builtin_amdgcn_s_waitcnt(mix_vm_wait(3 * ((MIX & 16 ? 2 : 0) + 3)));
+      if constexpr ((MIX & 32) && (MIX & 64)) {
+        if (wave & 1) __builtin_amdgcn_s_waitcnt(mix_vm_wait(3 * 6));
+        else __builtin_amdgcn_s_waitcnt(mix_vm_wait(3 * 4));
+      }
       __builtin_amdgcn_s_waitcnt(0xC07F);                            // lgkmcnt 0
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
@@ -596,7 +612,7 @@ int isp_mix_rate(int mix, int grid, int iters, unsigned long long *stamps, float
 #define ISP_MIX(M) \
   case M: return (int)launch(isp_mix_rate<M>, grid, 512, s, iters, stamps, sink, gbuf);
     ISP_MIX(2) ISP_MIX(3) ISP_MIX(7) ISP_MIX(10) ISP_MIX(11) ISP_MIX(15) ISP_MIX(31) ISP_MIX(47) ISP_MIX(63)
-    ISP_MIX(5) ISP_MIX(61)
+    ISP_MIX(5) ISP_MIX(61) ISP_MIX(127) ISP_MIX(125)
 #undef ISP_MIX
     default: return (int)hipErrorInvalidValue;
   }
