@@ -149,9 +149,16 @@ __global__ __launch_bounds__(kThreads) void is_k9_head_f32(HeadF32Args a) {
   }
   const size_t plane = (size_t)a.H * a.W;
 
-  for (int buf = 0; t < a.ntiles; t += gridDim.x, buf ^= 1) {
+  // The tile's values go to LDS at the end of the previous iteration (the
+  // first tile's here): written at the top of the loop body, the wait for
+  // the prefetch loads would also cover the previous tile's output stores,
+  // which went out after them (vector memory operations retire in issue
+  // order), and the compiler's count for the first iteration, with no stores
+  // in flight, is the one it keeps for every iteration.
 #pragma unroll
-    for (int q = 0; q < G::NLD; ++q) tile[buf][spos[q]] = ld[q];
+  for (int q = 0; q < G::NLD; ++q) tile[0][spos[q]] = ld[q];
+  for (int buf = 0; t < a.ntiles; t += gridDim.x, buf ^= 1) {
+    // tile[buf] is complete, and every wave has finished reading tile[buf ^ 1].
     __syncthreads();
     load_tile<R>(a, t + (int)gridDim.x, tid, ld);
 
@@ -193,6 +200,9 @@ __global__ __launch_bounds__(kThreads) void is_k9_head_f32(HeadF32Args a) {
                                                off, 0, 0);
       }
     }
+    // The next tile's values into the other buffer (past the last tile: zeros).
+#pragma unroll
+    for (int q = 0; q < G::NLD; ++q) tile[buf ^ 1][spos[q]] = ld[q];
   }
 }
 
