@@ -332,6 +332,22 @@ def lds_study(torch, isa, synth, stream, stream_obj, steps, warmup):
                                                            stream), 0, 1, "is_k3_chain")
     _, per, _ = _time_cases(torch, [c], steps, warmup, stream_obj)
     out.append({"case": c.name, "kernel": c.kernel, "ms": round(per[0], 4)})
+    # The pages' fp16 net (AUTO): the first layer computed inside the 64 -> 64
+    # layer, then 64 -> 32 and 32 -> 9 with the x3 depth-to-space in its stores.
+    x, layers = synth.chain_f16_nhwc()
+    spec = [(w.shape[1], w.shape[0], w.shape[2], relu) for (w, b, relu) in layers]
+    d = isa.make_chain_desc(1, 720, 1280, spec, 3, isa.IS_CHAIN_AUTO, "f16")
+    ws_bytes = isa.conv_chain_workspace_size(d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    xd = torch.from_numpy(x).cuda()
+    wl = [(torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()) for (w, b, _) in layers]
+    yn = torch.empty((1, 2160, 3840, 1), dtype=torch.float16, device="cuda")
+    c = Case("pages' net fp16", lambda: isa.conv_chain_forward(d, xd.data_ptr(), [w.data_ptr() for (w, _) in wl],
+                                                               [b.data_ptr() for (_, b) in wl], yn.data_ptr(),
+                                                               ws.data_ptr(), ws_bytes, stream),
+             0, 1, isa.conv_chain_kernel_name(d))
+    _, per, _ = _time_cases(torch, [c], steps, warmup, stream_obj)
+    out.append({"case": c.name, "kernel": c.kernel, "ms": round(per[0], 4)})
     return out
 
 
@@ -353,7 +369,9 @@ def pmc_lds_summary(pmc_dir):
              "variant there) and on one channel with 8 3x3 filters (4096x4096); the pointwise kernel on a",
              "1x1 32 -> 32 layer; the fp16 first-layer kernel on 1 -> 64 5x5; the fp32 first-layer kernel",
              "on 1 -> 32 5x5; the 4-filter matrix-core form of the multi-channel kernel on the upscaling",
-             "chain's last layer (32 -> 4 3x3, 1280x720). conflict share =",
+             "chain's last layer (32 -> 4 3x3, 1280x720); the pages' fp16 net on a 1280x720 frame (its first",
+             "layer computed inside the 64 -> 64 layer, then 64 -> 32, then 32 -> 9 with the x3",
+             "depth-to-space in its stores). conflict share =",
              "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
              "| kernel | dispatches | " + " | ".join(LDS_COUNTERS) + " | conflict share |",
              "|---|---|" + "---|" * len(LDS_COUNTERS) + "---|"]

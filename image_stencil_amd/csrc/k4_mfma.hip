@@ -634,17 +634,22 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
     soff_r[j] = G::RING_BYTES + sr * G::OUT_ROW_BYTES + spx[j] * 2 * K + ((sc[j] ^ skey(spx[j])) * 16);
     sswap[j] = shalf(spx[j]) != 0;
   }
-  // D2S: staging offsets of the 6 values a lane stores per segment.
-  int doff[2][6];
+  // D2S staging: a staged row holds the first 9 channels as 9 planes of TC
+  // fp16 values, plane c = 3 dy + dx at c * kD2sPlane bytes. A fragment write
+  // puts each of its (up to) 4 channels into its plane: 16 lanes write 32
+  // consecutive bytes, and the plane pitch of 68 dwords puts the planes that
+  // one instruction writes (c, c + 4, c + 8) 16 dwords apart on the banks. A
+  // copy-out read takes one dword (pixels 2 lane, 2 lane + 1) from each of a
+  // segment's 3 planes: 64 consecutive dwords, one per bank. (With the
+  // pixel-major layout of the other layers, those reads were 2-byte loads of
+  // pixels 64 bytes apart: 54% of the LDS cycles were bank conflicts.)
+  constexpr int kD2sPlane = 272;
+  static_assert(!D2S || (9 * kD2sPlane <= G::OUT_ROW_BYTES && 2 * G::TC <= kD2sPlane), "D2S planes fit a staged row");
+  int doff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int e = 0; e < 6; ++e) {
-      const int px = 2 * lane + e / 3;
-      const int c = 3 * (ddy[j] < 0 ? 0 : ddy[j]) + e % 3;
-      doff[j][e] = G::RING_BYTES + drow_s[j] * G::OUT_ROW_BYTES + px * 2 * K + (((c >> 3) ^ skey(px)) * 16) +
-                   (((c & 7) * 2) ^ (shalf(px) * 8));
-    }
+    doff[j] = G::RING_BYTES + drow_s[j] * G::OUT_ROW_BYTES + 3 * (ddy[j] < 0 ? 0 : ddy[j]) * kD2sPlane + 4 * lane;
+  const int d2s_w = G::RING_BYTES + 2 * wpx;   // + row + plane c * kD2sPlane
   const unsigned out3_row_bytes = (unsigned)a.W * 6u;   // D2S output row: 3W fp16
 
   while (true) {
@@ -664,11 +669,14 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if constexpr (D2S) {
-          const char *base = lds + (t % G::SBUF) * G::S * G::OUT_ROW_BYTES;
-          unsigned hw[6];
-#pragma unroll
-          for (int e = 0; e < 6; ++e) hw[e] = *reinterpret_cast<const unsigned short *>(base + doff[j][e]);
-          sv[j] = uint4v{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16), 0u};
+          // Planes dx = 0, 1, 2 of the segment: (pixel 2 lane, pixel 2 lane + 1)
+          // each; the output takes both pixels' 3 values in turn.
+          const char *base = lds + (t % G::SBUF) * G::S * G::OUT_ROW_BYTES + doff[j];
+          const unsigned d0 = *reinterpret_cast<const unsigned *>(base);
+          const unsigned d1 = *reinterpret_cast<const unsigned *>(base + kD2sPlane);
+          const unsigned d2 = *reinterpret_cast<const unsigned *>(base + 2 * kD2sPlane);
+          sv[j] = uint4v{(d0 & 0xFFFFu) | (d1 << 16), (d2 & 0xFFFFu) | (d0 & 0xFFFF0000u),
+                         (d1 >> 16) | (d2 & 0xFFFF0000u), 0u};
         } else {
           const uint4v v = *reinterpret_cast<const uint4v *>(lds + soff_r[j] + (t % G::SBUF) * G::S * G::OUT_ROW_BYTES);
           sv[j] = sswap[j] ? uint4v{v.z, v.w, v.x, v.y} : v;
@@ -756,8 +764,16 @@ __global__ __launch_bounds__(kThreads, 1) void is_k4_mfma(MfmaArgs a) {
           if constexpr (RELU) r = fmaxf(r, 0.f);
           hv[e] = (_Float16)r;
         }
-        *reinterpret_cast<uint2v *>(lds + soff_w + ((t % G::SBUF) * G::S + (i % G::S)) * G::OUT_ROW_BYTES) =
-            __builtin_bit_cast(uint2v, hv);
+        if constexpr (D2S) {
+          // Channels 4g .. 4g + 3 of pixel wpx into their planes (the first 9).
+          char *row = lds + d2s_w + ((t % G::SBUF) * G::S + (i % G::S)) * G::OUT_ROW_BYTES;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * g + e < 9) *reinterpret_cast<_Float16 *>(row + (4 * g + e) * kD2sPlane) = hv[e];
+        } else {
+          *reinterpret_cast<uint2v *>(lds + soff_w + ((t % G::SBUF) * G::S + (i % G::S)) * G::OUT_ROW_BYTES) =
+              __builtin_bit_cast(uint2v, hv);
+        }
       }
       // End of stage t: stage t + 2 (read from the next stage's last steps on,
       // through the read-ahead ring) must have landed; the barrier publishes it,
