@@ -120,3 +120,30 @@ def test_mfma_other_channel_counts_1280x720_full(C, K):
     ref, m = oracle.conv2d(x, w, b, True, "NHWC")
     ratio = check(y, ref, m, TAU_F16, "2x720x1280 fp16 %d->%d full" % (C, K))
     say("max err/bound %.3g" % ratio)
+
+
+def test_mfma_largest_image():
+    """The fp16 layer at the plan's 32-bit offset limit (2 H W C bytes just
+    under 4e9: one 5000 x 6248 x 64 image). Windows in the first and last units
+    and across unit seams in the middle are compared with the oracle run on
+    those windows plus a one-pixel border of input (a window's own border
+    outputs are compared only where they are the image's)."""
+    import torch
+    H, W = 5000, 6248
+    x, w, b = synth.cnn_layer_f16_nhwc(N=1, H=H, W=W, seed=22)
+    plan = isa.Plan(isa.make_desc(1, 64, H, W, 64, 3, 3, "f16", False))
+    assert plan.info()["kernel"] == "is_k4_mfma"
+    say("fp16 mfma largest image", H, W)
+    xd = dev(x)
+    y = torch.full((1, H, W, 64), float("nan"), dtype=torch.float16, device="cuda")
+    plan.forward(xd, dev(w), dev(b), y)
+    for r0, r1, c0, c1 in [(0, 70, 0, 40), (2530, 2600, 3100, 3140), (H - 70, H, W - 40, W)]:
+        lr, hr, lc, hc = max(0, r0 - 1), min(H, r1 + 1), max(0, c0 - 1), min(W, c1 + 1)
+        ref, m = oracle.conv2d(x[:, lr:hr, lc:hc, :], w, b, False, "NHWC")
+        got = host(y[:, lr:hr, lc:hc, :].contiguous())
+        ar, br = (0 if lr == 0 else 1), (hr - lr if hr == H else hr - lr - 1)
+        ac, bc = (0 if lc == 0 else 1), (hc - lc if hc == W else hc - lc - 1)
+        sl = (slice(None), slice(ar, br), slice(ac, bc), slice(None))
+        ratio = check(got[sl], ref[sl], m[sl], TAU_F16, "fp16 mfma %dx%d rows %d..%d cols %d..%d" % (
+            H, W, lr + ar, lr + br, lc + ac, lc + bc))
+        say("max err/bound %.3g" % ratio)

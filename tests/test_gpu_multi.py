@@ -228,3 +228,29 @@ def test_cnn_layer_720p_full():
     ref, m = oracle.conv2d(x, w, b, True)
     ratio = check(y, ref, m, TAU_F32, "720p fp32 layer full")
     say("max err/bound %.3g" % ratio)
+
+
+def test_mfma_f32_largest_image():
+    """The fp32 MFMA layer at the plan's 32-bit offset limit (4 C H W bytes just
+    under 2e9: 32 x 3840 x 4064 fp32, bias, ReLU). Windows in the first and
+    last tiles and across tile seams in the middle are compared with the
+    oracle run on those windows plus a one-pixel border of input (a window's own
+    border outputs are compared only where they are the image's)."""
+    import torch
+    H, W = 3840, 4064
+    x, w, b = synth.cnn_layer_f32(N=1, H=H, W=W, seed=21)
+    plan = isa.Plan(isa.make_desc(1, 32, H, W, 32, 3, 3, "f32", True))
+    assert plan.info()["kernel"] == "is_k5_mfma_f32"
+    say("fp32 mfma largest image", H, W)
+    y = torch.full((1, 32, H, W), float("nan"), dtype=torch.float32, device="cuda")
+    plan.forward(dev(x), dev(w), dev(b), y)
+    for r0, r1, c0, c1 in [(0, 30, 0, 70), (1940, 1972, 2010, 2080), (H - 30, H, W - 70, W)]:
+        lr, hr, lc, hc = max(0, r0 - 1), min(H, r1 + 1), max(0, c0 - 1), min(W, c1 + 1)
+        ref, m = oracle.conv2d(x[:, :, lr:hr, lc:hc], w, b, True)
+        got = host(y[:, :, lr:hr, lc:hc].contiguous())
+        ar, br = (0 if lr == 0 else 1), (hr - lr if hr == H else hr - lr - 1)
+        ac, bc = (0 if lc == 0 else 1), (hc - lc if hc == W else hc - lc - 1)
+        sl = (slice(None), slice(None), slice(ar, br), slice(ac, bc))
+        ratio = check(got[sl], ref[sl], m[sl], TAU_F32, "fp32 mfma %dx%d rows %d..%d cols %d..%d" % (
+            H, W, lr + ar, lr + br, lc + ac, lc + bc))
+        say("max err/bound %.3g" % ratio)

@@ -100,3 +100,32 @@ def test_large_image_full(R):
     ref, m = oracle.conv2d(x, w)
     ratio = check(y, ref, m, TAU_F32, "8192^2 %dx%d full" % (R, R))
     say("max err/bound %.3g" % ratio)
+
+
+def test_widest_row_at_the_offset_limit():
+    """Rows as wide as the kernel's 32-bit byte offsets allow (4 (W + 256) just
+    under 2^31, the plan's limit): two rows of 2^29 - 260 columns with a 3x3
+    filter. The first and last 600 columns and 600 columns around a wave
+    segment boundary in the middle of the row are compared with the oracle run
+    on those windows (with their neighbouring columns; a window's own edge
+    columns are compared only where they are the image's)."""
+    W = (1 << 29) - 260
+    x, w = synth.single_channel(H=2, W=W, R=3, seed=11)
+    plan = isa.Plan(isa.make_desc(1, 1, 2, W, 1, 3, 3))
+    assert plan.info()["kernel"] == "is_k1_single"
+    say("widest row", W)
+    import torch
+    xd = dev(x)
+    del x
+    y = torch.full((1, 1, 2, W), float("nan"), dtype=torch.float32, device="cuda")
+    plan.forward(xd, dev(w), None, y)
+    mid = (W // 512) * 256
+    for c0, c1 in [(0, 600), (mid - 300, mid + 300), (W - 600, W)]:
+        lo, hi = max(0, c0 - 1), min(W, c1 + 1)
+        xs = host(xd[..., lo:hi].contiguous())
+        ref, m = oracle.conv2d(xs, w)
+        got = host(y[..., lo:hi].contiguous())
+        a = 0 if lo == 0 else 1
+        b = hi - lo if hi == W else hi - lo - 1
+        ratio = check(got[..., a:b], ref[..., a:b], m[..., a:b], TAU_F32, "row of %d, columns %d..%d" % (W, lo + a, lo + b))
+        say("columns %d..%d max err/bound %.3g" % (lo + a, lo + b, ratio))
