@@ -585,3 +585,29 @@ def test_binding_rejects_mismatched_arguments():
         isa.conv_chain(xc, [l1, l2], depth_to_space=2)
     with pytest.raises(ValueError):
         isa.conv2d_separable(x, torch.zeros(3), torch.zeros(3))   # 4 channels
+
+
+def test_offset_limits_of_every_kernel():
+    """Each kernel's plan takes the largest image its 32-bit buffer offsets
+    allow and gives the next larger width to another kernel (the GPU tests run
+    the widths that are taken)."""
+    def kernel(*desc):
+        return isa.Plan(isa.make_desc(*desc)).info()["kernel"]
+    cases = [  # (desc at the limit, desc one step wider, kernel)
+        ((1, 32, 3840, 4068, 32, 3, 3, "f32", True), (1, 32, 3840, 4072, 32, 3, 3, "f32", True), "is_k5_mfma_f32"),
+        ((1, 64, 5000, 6248, 64, 3, 3, "f16"), (1, 64, 5000, 6252, 64, 3, 3, "f16"), "is_k4_mfma"),
+        ((1, 1, 3840, 4068, 32, 5, 5, "f32", True), (1, 1, 3840, 4072, 32, 5, 5, "f32", True), "is_k9_head_f32"),
+        ((1, 32, 5000, 6248, 4, 3, 3, "f32", True), (1, 32, 5000, 6252, 4, 3, 3, "f32", True), "is_k2_multi_mfma"),
+        ((1, 1, 5000, 6248, 64, 5, 5, "f16", True), (1, 1, 5000, 6252, 64, 5, 5, "f16", True), "is_k6_head_f16"),
+    ]
+    for at, past, name in cases:
+        assert kernel(*at) == name, (at, kernel(*at))
+        assert kernel(*past) != name, (past, kernel(*past))
+    pipe = [(1, 1, 3, True), (1, 1, 3, True), (1, 1, 3, False)]
+    assert isa.conv_chain_kernel_name(isa.make_chain_desc(1, 20000, 24996, pipe, 1, isa.IS_CHAIN_AUTO)) == \
+        "is_k7_fused_stencil"
+    assert isa.conv_chain_groups(isa.make_chain_desc(1, 20000, 25000, pipe, 1, isa.IS_CHAIN_AUTO)) == [1, 1, 1]
+    up = [(1, 32, 5, True), (32, 32, 3, True), (32, 32, 3, True), (32, 4, 3, False)]
+    assert isa.conv_chain_kernel_name(isa.make_chain_desc(1, 15000, 16664, up, 2, isa.IS_CHAIN_FUSED)) == "is_k3_chain"
+    with pytest.raises(isa.ImgStencilError):
+        isa.conv_chain_kernel_name(isa.make_chain_desc(1, 15000, 16668, up, 2, isa.IS_CHAIN_FUSED))
